@@ -1,0 +1,329 @@
+"""Float64 CPU oracle for the ZeroS (zero-sum linear attention) forward pass.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the library's product path may import, call or execute
+this module; only the tests, the smoke check and the benchmark's CPU-baseline leg use it. It
+shares no code with the HIP library and the library never falls back to it.
+
+Sources (cited by page title and section; the pages are web summaries of arXiv 2602.05230):
+  [Notes/zero-sum]  Paper-Notes page "ZeroS: Zero-Sum Linear Attention for Efficient
+                    Transformers", section 关键设计, item "Softmax 零阶移除与零和权重构建":
+                    softmax is split into a 1/t term, a first-order offset delta/t and a
+                    higher-order residual eps; the 1/t term is dropped and the weight is
+                    w_{t,i} = sigma1_t * delta_{t,i} / t + sigmah_t * eps_{t,i}, with sigmoid
+                    gates that depend on the query step t. The weights sum to zero over i.
+  [Notes/radial]    same page, item "径向-角向解耦": o_t = sum_{i<=t} r_{t,i} cos(theta) v_i
+                    with cos(theta) the inner product of the L2-normalised q_t and k_i;
+                    with RoPE the angular factor becomes q^_t R_{t-i} k^_i^T.
+  [Notes/logits]    same page, item "偏差 logits 设计": s_i = -(1/sqrt(d)) u_i . ubar_i with
+                    ubar_i = (e^tau mu + sum_{j<=i} u_j) / (e^tau + i).
+  [Notes/scan]      same page, item "线性时间前缀扫描": the prefix states E, P, F, G, H and
+                    o_t = q^_t (alpha_t F_t + beta_t G_t + gamma_t H_t).
+  [Notes/training]  same page, section "损失函数 / 训练策略": causal (decoder) and
+                    non-causal (encoder) modes.
+  [Summary/plain]   ai.info page "ZeroS: Zero-Sum Linear Attention for Efficient Transformers",
+                    section "Methodology in Plain English" (same method in English).
+
+Readings taken where the pages leave a step open (each is listed in the design notes):
+  * delta_{t,i} = s_i - (1/t) sum_{j<=t} s_j, the first-order Taylor term of softmax about equal
+    logits; eps_{t,i} = softmax_{t,i} - 1/t - delta_{t,i}/t.
+  * Expanding w over the prefix sums gives w_{t,i} = alpha_t e^{s_i} + beta_t s_i + gamma_t with
+    alpha_t = sigmah_t / E_t, beta_t = (sigma1_t - sigmah_t)/t,
+    gamma_t = -(sigma1_t - sigmah_t) P_t / t^2 - sigmah_t / t  (see ``coefficients``).
+  * Positions are 1-based in the formulas; the sum for ubar_i includes u_i; the causal sum over
+    i <= t includes i = t.
+  * The 1/sqrt(d) of the logit uses d_u, the length of the dot product.
+  * mu (d_u vector) and tau (scalar) are per head; gates arrive as pre-activations and the
+    logistic sigmoid is applied here.
+  * L2 normalisation divides by max(||x||, 1e-12).
+  * RoPE: interleaved pairs (2j, 2j+1), theta_j = base^(-2j/d), 0-based position p = t-1,
+    applied after normalisation to both q^ and k^.
+  * Encoder mode: one global prior-smoothed mean ubar over all N tokens, and every query uses
+    the full-sequence sums with t replaced by N and its own gates.
+  * A running maximum m_t of the logits rescales e^{s}: the state stores
+    Et = sum e^{s_i - m_t} and Ft = sum e^{s_i - m_t} k^_i^T v_i (this leaves o unchanged).
+
+Array conventions: leading dimensions [B, H] (any number of leading dims works), then tokens,
+then features. All arithmetic is float64.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F64 = np.float64
+
+
+def _f64(x):
+    return np.asarray(x, dtype=F64)
+
+
+def sigmoid(x):
+    """Logistic sigmoid, evaluated without overflow for large |x|."""
+    x = _f64(x)
+    out = np.empty_like(x)
+    pos = x >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-x[pos]))
+    ex = np.exp(x[~pos])
+    out[~pos] = ex / (1.0 + ex)
+    return out
+
+
+def l2_normalize(x):
+    """Unit vectors along the last axis [Notes/radial]."""
+    x = _f64(x)
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    return x / np.maximum(n, 1e-12)
+
+
+def rope_theta(d, base):
+    """Per-pair frequencies theta_j = base^(-2j/d), j = 0 .. d/2-1."""
+    j = np.arange(d // 2, dtype=F64)
+    return np.power(F64(base), -2.0 * j / d)
+
+
+def rope_rotate(x, positions, base):
+    """Rotate interleaved pairs (2j, 2j+1) of x[..., n, d] by angle positions[n] * theta_j.
+
+    [Notes/radial] (RoPE compatibility): q^_t R_t and k^_i R_i, so that their inner product
+    depends on t - i only.
+    """
+    x = _f64(x)
+    d = x.shape[-1]
+    ang = _f64(positions)[:, None] * rope_theta(d, base)[None, :]      # [n, d/2]
+    c, s = np.cos(ang), np.sin(ang)
+    x0, x1 = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = x0 * c - x1 * s
+    out[..., 1::2] = x0 * s + x1 * c
+    return out
+
+
+def angular_vectors(q, k, rope=False, rope_base=10000.0, pos0=0):
+    """Return (q^, k^): L2-normalised and, optionally, RoPE-rotated at positions pos0 + 0..n-1."""
+    qh, kh = l2_normalize(q), l2_normalize(k)
+    if rope:
+        pos = pos0 + np.arange(qh.shape[-2], dtype=F64)
+        qh = rope_rotate(qh, pos, rope_base)
+        kh = rope_rotate(kh, pos, rope_base)
+    return qh, kh
+
+
+def _prior(mu, tau):
+    """(e^tau * mu, e^tau) with mu [..., d_u] and tau [...] broadcast to the leading dims."""
+    et = np.exp(_f64(tau))
+    return et[..., None] * _f64(mu), et
+
+
+def deviation_logits_causal(u, mu, tau):
+    """s_i = -(u_i . ubar_i)/sqrt(d_u), ubar_i = (e^tau mu + sum_{j<=i} u_j)/(e^tau + i).
+
+    [Notes/logits]. u [..., N, d_u]; mu [..., d_u] and tau [...] broadcast over the leading
+    dims (per head). Returns s [..., N].
+    """
+    u = _f64(u)
+    N, du = u.shape[-2], u.shape[-1]
+    emu, et = _prior(mu, tau)
+    S = np.cumsum(u, axis=-2)
+    i = np.arange(1, N + 1, dtype=F64)
+    ubar = (emu[..., None, :] + S) / (et[..., None, None] + i[:, None])
+    return -np.sum(u * ubar, axis=-1) / np.sqrt(F64(du))
+
+
+def deviation_logits_encoder(u, mu, tau):
+    """Encoder reading: one global ubar = (e^tau mu + sum_{all j} u_j)/(e^tau + N)."""
+    u = _f64(u)
+    N, du = u.shape[-2], u.shape[-1]
+    emu, et = _prior(mu, tau)
+    ubar = (emu + np.sum(u, axis=-2)) / (et[..., None] + N)
+    return -np.einsum("...nc,...c->...n", u, ubar) / np.sqrt(F64(du))
+
+
+def coefficients(t, Et, Pt, sig1, sigh):
+    """alpha, beta, gamma of o_t = q^_t(alpha F + beta G + gamma H).
+
+    Derivation from [Notes/zero-sum] with the readings above:
+      w_{t,i} = sig1 (s_i - P_t/t)/t + sigh (e^{s_i}/E_t - 1/t - (s_i - P_t/t)/t)
+              = (sigh/E_t) e^{s_i} + ((sig1 - sigh)/t) s_i + (-(sig1 - sigh) P_t/t^2 - sigh/t).
+    Summing over i <= t gives alpha E_t + beta P_t + gamma t = 0 (the zero-sum property).
+    ``Et`` may be the max-rescaled sum; alpha then multiplies the equally rescaled F.
+    """
+    t = _f64(t)
+    d1 = _f64(sig1) - _f64(sigh)
+    alpha = _f64(sigh) / _f64(Et)
+    beta = d1 / t
+    gamma = -d1 * _f64(Pt) / (t * t) - _f64(sigh) / t
+    return alpha, beta, gamma
+
+
+# --------------------------------------------------------------------------------------------
+# Recurrent (five-state) form: the oracle used at every size.
+# --------------------------------------------------------------------------------------------
+
+def empty_state(lead, d, d_u):
+    """State before any token: t = 0, m = -inf, all sums zero. ``lead`` = leading shape."""
+    lead = tuple(lead)
+    return {
+        "t": np.zeros(lead, dtype=np.int64),
+        "m": np.full(lead, -np.inf, dtype=F64),
+        "E": np.zeros(lead, dtype=F64),
+        "P": np.zeros(lead, dtype=F64),
+        "Su": np.zeros(lead + (d_u,), dtype=F64),
+        "F": np.zeros(lead + (d, d), dtype=F64),
+        "G": np.zeros(lead + (d, d), dtype=F64),
+        "H": np.zeros(lead + (d, d), dtype=F64),
+    }
+
+
+def decode_step(state, q, k, v, u, mu, tau, g1, gh, rope=False, rope_base=10000.0):
+    """Advance the state by one token and return (o, new_state); ``state`` is not modified.
+
+    q, k, v [..., d]; u [..., d_u]; mu [..., d_u]; tau, g1, gh [...]. The token is at 1-based
+    position t = state["t"] + 1 (RoPE position t - 1). States follow [Notes/scan]; the logit uses
+    the running u-sum of [Notes/logits]; coefficients as in ``coefficients``.
+    """
+    st = {key: np.array(val, copy=True) for key, val in state.items()}
+    o = _step_inplace(st, q, k, v, u, mu, tau, g1, gh, rope, rope_base)
+    return o, st
+
+
+def _step_inplace(st, q, k, v, u, mu, tau, g1, gh, rope, rope_base):
+    t = st["t"] + 1
+    tf = t.astype(F64)
+    d_u = st["Su"].shape[-1]
+    qh, kh = l2_normalize(q), l2_normalize(k)
+    if rope:
+        pos = (t - 1).astype(F64)
+        qh, kh = _rope_per_item(qh, pos, rope_base), _rope_per_item(kh, pos, rope_base)
+    u = _f64(u)
+    emu, et = _prior(mu, tau)
+    st["Su"] += u
+    ubar = (emu + st["Su"]) / (et + tf)[..., None]
+    s = -np.sum(u * ubar, axis=-1) / np.sqrt(F64(d_u))
+    m_new = np.maximum(st["m"], s)
+    with np.errstate(invalid="ignore"):
+        c = np.exp(st["m"] - m_new)        # exp(-inf) = 0 for the empty state
+    e = np.exp(s - m_new)
+    st["E"] = c * st["E"] + e
+    st["P"] = st["P"] + s
+    kv = kh[..., :, None] * _f64(v)[..., None, :]
+    F, G, H = st["F"], st["G"], st["H"]
+    F *= c[..., None, None]
+    F += e[..., None, None] * kv
+    G += s[..., None, None] * kv
+    H += kv
+    st["m"] = m_new
+    st["t"] = t
+    a, b, g = coefficients(tf, st["E"], st["P"], sigmoid(g1), sigmoid(gh))
+    M = a[..., None, None] * F + b[..., None, None] * G + g[..., None, None] * H
+    return np.einsum("...j,...jm->...m", qh, M)
+
+
+def _rope_per_item(x, pos, base):
+    d = x.shape[-1]
+    ang = pos[..., None] * rope_theta(d, base)
+    c, s = np.cos(ang), np.sin(ang)
+    out = np.empty_like(x)
+    out[..., 0::2] = x[..., 0::2] * c - x[..., 1::2] * s
+    out[..., 1::2] = x[..., 0::2] * s + x[..., 1::2] * c
+    return out
+
+
+def causal_forward(q, k, v, u, mu, tau, g1, gh, rope=False, rope_base=10000.0,
+                   return_state=False, state=None):
+    """Causal ZeroS forward as the sequential five-state recurrence (one step per token).
+
+    q, k, v [..., N, d]; u [..., N, d_u]; mu [..., d_u] (per head, broadcast over batch);
+    tau [...]; g1, gh [..., N]. Returns o [..., N, d] (float64), and the final state if asked.
+    ``state`` continues from a previous state instead of the empty one.
+    """
+    q, k, v, u = _f64(q), _f64(k), _f64(v), _f64(u)
+    g1, gh = _f64(g1), _f64(gh)
+    lead = q.shape[:-2]
+    N, d = q.shape[-2], q.shape[-1]
+    d_u = u.shape[-1]
+    mu_b = np.broadcast_to(_f64(mu), lead + (d_u,))
+    tau_b = np.broadcast_to(_f64(tau), lead)
+    if state is None:
+        st = empty_state(lead, d, d_u)
+    else:
+        st = {key: np.array(val, copy=True) for key, val in state.items()}
+    o = np.empty(lead + (N, v.shape[-1]), dtype=F64)
+    for n in range(N):
+        o[..., n, :] = _step_inplace(st, q[..., n, :], k[..., n, :], v[..., n, :], u[..., n, :],
+                                     mu_b, tau_b, g1[..., n], gh[..., n], rope, rope_base)
+    return (o, st) if return_state else o
+
+
+def encoder_forward(q, k, v, u, mu, tau, g1, gh, rope=False, rope_base=10000.0):
+    """Non-causal ZeroS forward [Notes/training]: every query uses the full-sequence sums.
+
+    With t = N for every query: m = max s, E = sum e^{s-m}, P = sum s, F = sum e^{s-m} k^T v,
+    G = sum s k^T v, H = sum k^T v, and o_t = q^_t(alpha_t F + beta_t G + gamma_t H) with the
+    gates of token t.
+    """
+    v = _f64(v)
+    qh, kh = angular_vectors(q, k, rope, rope_base)
+    N = qh.shape[-2]
+    s = deviation_logits_encoder(u, mu, tau)                          # [..., N]
+    m = np.max(s, axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    E = np.sum(e, axis=-1)
+    P = np.sum(s, axis=-1)
+    F = np.einsum("...nj,...n,...nm->...jm", kh, e, v)
+    G = np.einsum("...nj,...n,...nm->...jm", kh, s, v)
+    H = np.einsum("...nj,...nm->...jm", kh, v)
+    a, b, g = coefficients(F64(N), E[..., None], P[..., None], sigmoid(g1), sigmoid(gh))
+    return (a[..., None] * (qh @ F) + b[..., None] * (qh @ G) + g[..., None] * (qh @ H))
+
+
+# --------------------------------------------------------------------------------------------
+# Explicit O(N^2) weights: the plain definition, used to pin the recurrence on small inputs.
+# --------------------------------------------------------------------------------------------
+
+def explicit_weights_causal(s, g1, gh):
+    """W[..., t, i] = w_{t,i} for i <= t, 0 above the diagonal [Notes/zero-sum].
+
+    Row t (1-based) takes a softmax over s_1..s_t, its mean, delta = s_i - mean,
+    eps = softmax - 1/t - delta/t, w = sigma1_t delta/t + sigmah_t eps.
+    """
+    s = _f64(s)
+    N = s.shape[-1]
+    s1, sh = sigmoid(g1), sigmoid(gh)
+    W = np.zeros(s.shape + (N,), dtype=F64)
+    for ti in range(N):
+        t = ti + 1
+        row = s[..., :t]
+        ex = np.exp(row - np.max(row, axis=-1, keepdims=True))
+        sm = ex / np.sum(ex, axis=-1, keepdims=True)
+        delta = row - np.mean(row, axis=-1, keepdims=True)
+        eps = sm - 1.0 / t - delta / t
+        W[..., ti, :t] = s1[..., ti, None] * delta / t + sh[..., ti, None] * eps
+    return W
+
+
+def explicit_weights_encoder(s, g1, gh):
+    """Encoder weights: the same construction with the softmax and mean over all N tokens."""
+    s = _f64(s)
+    N = s.shape[-1]
+    ex = np.exp(s - np.max(s, axis=-1, keepdims=True))
+    sm = ex / np.sum(ex, axis=-1, keepdims=True)
+    delta = s - np.mean(s, axis=-1, keepdims=True)
+    eps = sm - 1.0 / N - delta / N
+    s1, sh = sigmoid(g1)[..., :, None], sigmoid(gh)[..., :, None]
+    return s1 * delta[..., None, :] / N + sh * eps[..., None, :]
+
+
+def causal_brute_force(q, k, v, u, mu, tau, g1, gh, rope=False, rope_base=10000.0):
+    """o_t = sum_{i<=t} w_{t,i} (q^_t . k^_i) v_i with the explicit weights [Notes/radial]."""
+    qh, kh = angular_vectors(q, k, rope, rope_base)
+    s = deviation_logits_causal(u, mu, tau)
+    W = explicit_weights_causal(s, g1, gh)
+    cos = qh @ np.swapaxes(kh, -1, -2)
+    return (W * cos) @ _f64(v)
+
+
+def encoder_brute_force(q, k, v, u, mu, tau, g1, gh, rope=False, rope_base=10000.0):
+    qh, kh = angular_vectors(q, k, rope, rope_base)
+    s = deviation_logits_encoder(u, mu, tau)
+    W = explicit_weights_encoder(s, g1, gh)
+    cos = qh @ np.swapaxes(kh, -1, -2)
+    return (W * cos) @ _f64(v)

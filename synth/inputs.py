@@ -1,0 +1,108 @@
+"""Workload table and seeded input generator.
+
+Every tensor is drawn with ``numpy.random.default_rng(seed)`` (PCG64) in float32, in the fixed
+order q, k, v, u, mu, tau, g1, gh, and then rounded to the workload's storage dtype. The
+rounded values are returned as float32 arrays; whoever consumes them (the float64 oracle or the
+GPU library) sees exactly the same numbers.
+
+Distributions: q, k, v, u ~ N(0, 1) iid; mu ~ N(0, 0.1^2) per head; tau is either 0 or
+U(-1, 1) per head; the gate pre-activations g1, gh ~ N(0, 1) per token.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, replace
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    d_u: int
+    dtype: str          # "f32" or "bf16": storage type of q, k, v, u, g1, gh and o
+    mode: str           # "causal", "encoder" or "decode"
+    rope: bool = False
+    rope_base: float = 10000.0
+    tau_uniform: bool = False   # tau ~ U(-1, 1) per head when True, else tau = 0
+    seed: int = 0
+    prefill: int = 0    # decode only: tokens already folded into the state
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+    @property
+    def tokens(self) -> int:
+        return self.B * self.N
+
+    def summary(self) -> dict:
+        out = {"workload": self.name, "mode": self.mode, "B": self.B, "H": self.H,
+               "N": self.N, "d": self.d, "d_u": self.d_u, "dtype": self.dtype,
+               "rope": self.rope, "seed": self.seed}
+        if self.mode == "decode":
+            out["prefill"] = self.prefill
+        return out
+
+
+CONFIGS = {
+    1: Workload("tiny-causal-B1H1N64d16", 1, 1, 64, 16, 16, "f32", "causal", seed=1),
+    2: Workload("lm-layer-causal-B8H8N512d64", 8, 8, 512, 64, 64, "f32", "causal",
+                tau_uniform=True, seed=2),
+    3: Workload("vit-tiny-encoder-B64H3N197d64", 64, 3, 197, 64, 64, "bf16", "encoder", seed=3),
+    4: Workload("long-causal-rope-B2H16N16384d128", 2, 16, 16384, 128, 128, "bf16", "causal",
+                rope=True, tau_uniform=True, seed=4),
+    5: Workload("decode-S256H32d128-t8192", 256, 32, 1, 128, 128, "bf16", "decode",
+                tau_uniform=True, seed=5, prefill=8192),
+}
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 (ties to even); returned as float32."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    bits = x.view(np.uint32).astype(np.uint64)
+    lsb = (bits >> 16) & 1
+    rounded = ((bits + 0x7FFF + lsb) >> 16) << 16
+    out = rounded.astype(np.uint32).view(np.float32)
+    # NaN stays NaN (the add above could carry a NaN payload into the exponent of an inf).
+    return np.where(np.isnan(x), x, out)
+
+
+def round_to_dtype(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "f32":
+        return np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == "bf16":
+        return bf16_round(x)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def make_inputs(wl: Workload, *, u_scale: float = 1.0) -> dict:
+    """Draw one batch of inputs for ``wl``.
+
+    Shapes: q, k, v [B, H, N, d]; u [B, H, N, d_u]; mu [H, d_u]; tau [H]; g1, gh [B, H, N].
+    For decode workloads N is 1 (one new token per sequence). ``u_scale`` multiplies u before
+    rounding (logit stress cases).
+    """
+    rng = np.random.default_rng(wl.seed)
+    B, H, N, d, du = wl.B, wl.H, wl.N, wl.d, wl.d_u
+    q = rng.standard_normal((B, H, N, d), dtype=np.float32)
+    k = rng.standard_normal((B, H, N, d), dtype=np.float32)
+    v = rng.standard_normal((B, H, N, d), dtype=np.float32)
+    u = rng.standard_normal((B, H, N, du), dtype=np.float32)
+    mu = (0.1 * rng.standard_normal((H, du), dtype=np.float32)).astype(np.float32)
+    if wl.tau_uniform:
+        tau = rng.uniform(-1.0, 1.0, size=(H,)).astype(np.float32)
+    else:
+        tau = np.zeros((H,), dtype=np.float32)
+    g1 = rng.standard_normal((B, H, N), dtype=np.float32)
+    gh = rng.standard_normal((B, H, N), dtype=np.float32)
+    if u_scale != 1.0:
+        u = (u * np.float32(u_scale)).astype(np.float32)
+    dt = wl.dtype
+    return {
+        "q": round_to_dtype(q, dt), "k": round_to_dtype(k, dt), "v": round_to_dtype(v, dt),
+        "u": round_to_dtype(u, dt), "mu": mu, "tau": tau,
+        "g1": round_to_dtype(g1, dt), "gh": round_to_dtype(gh, dt),
+    }

@@ -1,0 +1,145 @@
+/*
+ * libzeros: ZeroS (zero-sum linear attention) forward pass for AMD Instinct MI355X (gfx950).
+ *
+ * The method (arXiv 2602.05230) is described on the Paper-Notes page "ZeroS: Zero-Sum Linear
+ * Attention for Efficient Transformers" (section 关键设计) and on the ai.info summary of the same
+ * title (section "Methodology in Plain English"). Per head, with 1-based positions t and i:
+ *
+ *   deviation logits      s_i  = -(u_i . ubar_i) / sqrt(d_u),
+ *                         ubar_i = (e^tau mu + sum_{j<=i} u_j) / (e^tau + i)
+ *   zero-sum weights      w_{t,i} = sigma1_t (s_i - P_t/t)/t
+ *                                 + sigmah_t (softmax_{t,i} - 1/t - (s_i - P_t/t)/t)
+ *   angular factor        cos_{t,i} = q^_t . k^_i  (L2-normalised, optionally RoPE-rotated)
+ *   output                o_t = sum_{i<=t} w_{t,i} cos_{t,i} v_i
+ *                             = q^_t (alpha_t F_t + beta_t G_t + gamma_t H_t)
+ *
+ * with E_t = sum e^{s_i}, P_t = sum s_i, F_t = sum e^{s_i} k^_i^T v_i, G_t = sum s_i k^_i^T v_i,
+ * H_t = sum k^_i^T v_i (the prefix scan of 关键设计 / 线性时间前缀扫描), alpha_t = sigmah_t/E_t,
+ * beta_t = (sigma1_t - sigmah_t)/t, gamma_t = -(sigma1_t - sigmah_t) P_t/t^2 - sigmah_t/t, and
+ * sigma = logistic sigmoid of the gate pre-activations g1, gh.
+ *
+ * Conventions shared by every entry point
+ *   Memory:    every pointer is DEVICE memory owned by the caller; the library allocates
+ *              nothing and keeps no state between calls (an error message is kept per thread).
+ *              Token tensors (q, k, v, u, g1, gh, o) may be NULL when N = 0; mu and tau never.
+ *   Layout:    contiguous row-major, feature dimension innermost:
+ *              q, k, v, o [B, H, N, d]; u [B, H, N, d_u]; g1, gh [B, H, N];
+ *              mu [H, d_u] float32; tau [H] float32 (per head, shared across the batch).
+ *   Types:     q, k, v, u, g1, gh and o share `dtype` (float32 or bfloat16); arithmetic is
+ *              float32 (states, sums and accumulation); o is written in `dtype`.
+ *   Streams:   work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the call
+ *              returns without synchronising.
+ *   Errors:    the return value only; nothing throws or aborts. Arguments are validated on the
+ *              host before any launch; a failed launch returns ZEROS_ERR_HIP. NaN/Inf in the
+ *              inputs propagate to the outputs they influence and are not checked.
+ *   Aliasing:  o must not overlap any input. Decode updates its state in place.
+ *   Shapes:    d in {16, 32, 64, 128}, d_u == d, B, H >= 1, N >= 0 (N = 0 is a no-op),
+ *              B*H*N*d < 2^31 elements per tensor; anything else is ZEROS_ERR_UNSUPPORTED or
+ *              ZEROS_ERR_SHAPE.
+ *   Threads:   calls are thread-safe; calls that write the same buffers race.
+ */
+#ifndef ZEROS_H
+#define ZEROS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ZEROS_ABI_VERSION 1
+
+typedef enum {
+    ZEROS_OK = 0,
+    ZEROS_ERR_NULL = 1,         /* a required pointer is NULL                         */
+    ZEROS_ERR_SHAPE = 2,        /* non-positive or overflowing sizes, d_u != d        */
+    ZEROS_ERR_DTYPE = 3,        /* dtype is not a zeros_dtype value                   */
+    ZEROS_ERR_UNSUPPORTED = 4,  /* valid but not implemented (e.g. d = 96)             */
+    ZEROS_ERR_HIP = 5,          /* the HIP runtime reported an error                  */
+    ZEROS_ERR_ALIAS = 6         /* o overlaps an input                                 */
+} zeros_status;
+
+typedef enum { ZEROS_F32 = 0, ZEROS_BF16 = 1 } zeros_dtype;
+
+typedef struct {
+    int32_t B, H, N;      /* batch (or decode sequences), heads, tokens                 */
+    int32_t d, d_u;       /* head dim of q/k/v/o, logit dim of u and mu                  */
+    int32_t dtype;        /* zeros_dtype                                                  */
+    int32_t rope;         /* 0: off; 1: RoPE on interleaved pairs (2j, 2j+1), applied to  */
+                          /*    q^ and k^ after normalisation at 0-based position t-1     */
+    float rope_base;      /* theta_j = rope_base^(-2j/d); 10000 is the usual value        */
+} zeros_shape;
+
+/*
+ * Recurrent state of S sequences x H heads, all float32 except t. F is kept rescaled by the
+ * running maximum of the logits: F = sum_i e^{s_i - m} k^_i^T v_i and E = sum_i e^{s_i - m};
+ * G, Hs, P, Su are plain sums. Matrices are [S, H, d, d] with the k^ index as rows and the v
+ * index as columns. The state at t = 0 is m = -inf and everything else zero. F, G and Hs must be
+ * 16-byte aligned and the other fields 4-byte aligned (ZEROS_ERR_SHAPE otherwise).
+ */
+typedef struct {
+    float *F, *G, *Hs;    /* [S, H, d, d]                                                 */
+    float *Su;            /* [S, H, d_u]  running sum of u                                 */
+    float *m, *E, *P;     /* [S, H]       running max, sum e^{s-m}, sum s                  */
+    int32_t *t;           /* [S, H]       tokens consumed                                  */
+} zeros_state;
+
+/*
+ * Causal forward (Paper-Notes 关键设计: zero-sum weights, radial-angular decoupling, deviation
+ * logits and the linear-time prefix scan; decoder mode per 损失函数 / 训练策略).
+ * Inputs as in the conventions above; writes o [B, H, N, d].
+ * state_out (nullable): receives the state after token N for every (b, h) (S = B); its
+ * buffers must not overlap the inputs or o.
+ */
+zeros_status zeros_fwd_causal(const zeros_shape *shape,
+                              const void *q, const void *k, const void *v, const void *u,
+                              const float *mu, const float *tau,
+                              const void *g1, const void *gh,
+                              void *o, const zeros_state *state_out, void *stream);
+
+/*
+ * Encoder (non-causal) forward (Paper-Notes 损失函数 / 训练策略: both modes are supported).
+ * Every query t uses the sums over all N tokens, ubar is the single prior-smoothed mean of all
+ * N u's, and the coefficients use t = N with the gates of token t. Writes o [B, H, N, d].
+ */
+zeros_status zeros_fwd_encoder(const zeros_shape *shape,
+                               const void *q, const void *k, const void *v, const void *u,
+                               const float *mu, const float *tau,
+                               const void *g1, const void *gh,
+                               void *o, void *stream);
+
+/*
+ * One recurrent step (the O(d^2)-per-token update of 关键设计 / 线性时间前缀扫描):
+ * shape->B = S sequences, shape->N must be 1. q, k, v, o [S, H, d]; u [S, H, d_u];
+ * g1, gh [S, H]. Each (sequence, head) consumes one token at position state.t + 1 and its state
+ * is updated in place.
+ */
+zeros_status zeros_decode_step(const zeros_shape *shape,
+                               const void *q, const void *k, const void *v, const void *u,
+                               const float *mu, const float *tau,
+                               const void *g1, const void *gh,
+                               void *o, const zeros_state *state, void *stream);
+
+/* Bytes of one state for S x H heads when packed by zeros_state_from_buffer (256-B aligned
+ * fields, order F, G, Hs, Su, m, E, P, t). Returns 0 for invalid sizes. */
+size_t zeros_state_bytes(int32_t S, int32_t H, int32_t d, int32_t d_u);
+
+/* Point the fields of *out into one buffer of zeros_state_bytes() bytes (no device access). */
+zeros_status zeros_state_from_buffer(void *base, int32_t S, int32_t H, int32_t d, int32_t d_u,
+                                     zeros_state *out);
+
+/* Static description of a status code. */
+const char *zeros_status_str(int32_t status);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char *zeros_last_error(void);
+
+/* ZEROS_ABI_VERSION of the built library. */
+int32_t zeros_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZEROS_H */

@@ -62,12 +62,14 @@ CONFIGS = {
 def bf16_round(x: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bfloat16 (ties to even); returned as float32."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    bits = x.view(np.uint32).astype(np.uint64)
-    lsb = (bits >> 16) & 1
-    rounded = ((bits + 0x7FFF + lsb) >> 16) << 16
-    out = rounded.astype(np.uint32).view(np.float32)
-    # NaN stays NaN (the add above could carry a NaN payload into the exponent of an inf).
-    return np.where(np.isnan(x), x, out)
+    bits = x.view(np.uint32)
+    # finite inputs stay below 2^32 after the rounding add; NaN is passed through unchanged
+    rounded = (bits + (np.uint32(0x7FFF) + ((bits >> np.uint32(16)) & np.uint32(1)))) & np.uint32(0xFFFF0000)
+    out = rounded.view(np.float32)
+    nan = np.isnan(x)
+    if nan.any():
+        out = np.where(nan, x, out)
+    return out
 
 
 def round_to_dtype(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -106,3 +108,26 @@ def make_inputs(wl: Workload, *, u_scale: float = 1.0) -> dict:
         "u": round_to_dtype(u, dt), "mu": mu, "tau": tau,
         "g1": round_to_dtype(g1, dt), "gh": round_to_dtype(gh, dt),
     }
+
+
+def decode_prefill_batch(wl: Workload, s0: int, s1: int, device="cuda"):
+    """Prefix tokens 1..wl.prefill of decode sequences [s0, s1), drawn on the GPU.
+
+    The full prefix of a decode workload (256 x 32 x 8192 tokens x 4 tensors) is far too large to
+    draw on the host, so it comes from torch's device generator seeded with (wl.seed, s0): the
+    same batch always gets the same values on the same software stack. Returns torch tensors
+    q, k, v, u [s1-s0, H, prefill, d] and g1, gh [s1-s0, H, prefill] in the workload dtype.
+    """
+    import torch
+
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16}[wl.dtype]
+    g = torch.Generator(device=device)
+    g.manual_seed(wl.seed * 1_000_003 + s0)
+    S, H, T = s1 - s0, wl.H, wl.prefill
+    out = {}
+    for key in ("q", "k", "v", "u"):
+        feat = wl.d_u if key == "u" else wl.d
+        out[key] = torch.randn((S, H, T, feat), generator=g, device=device, dtype=torch.float32).to(dt)
+    for key in ("g1", "gh"):
+        out[key] = torch.randn((S, H, T), generator=g, device=device, dtype=torch.float32).to(dt)
+    return out

@@ -1,0 +1,169 @@
+"""C-ABI tests that need no GPU: the library loads, exports every function the header declares,
+and rejects bad arguments on the host before any HIP call.
+
+Every call here that passes placeholder pointers is one that validation rejects (or a no-op such
+as N = 0 without a state), so no kernel is ever launched with them.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from zero_sum_attention_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "zeros.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return L.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(zeros_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    for n in ("zeros_fwd_causal", "zeros_fwd_encoder", "zeros_decode_step", "zeros_state_bytes",
+              "zeros_state_from_buffer", "zeros_status_str", "zeros_last_error", "zeros_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"libzeros.so does not export {name}"
+
+
+def test_abi_version(lib):
+    text = open(HEADER).read()
+    ver = int(re.search(r"#define ZEROS_ABI_VERSION (\d+)", text).group(1))
+    assert lib.zeros_abi_version() == ver
+
+
+def test_status_strings(lib):
+    for code in range(7):
+        s = lib.zeros_status_str(code).decode()
+        assert s.startswith("ZEROS_"), s
+    assert "unknown" in lib.zeros_status_str(99).decode()
+
+
+def test_struct_layout_matches_header():
+    assert ctypes.sizeof(L.zeros_shape) == 32
+    assert ctypes.sizeof(L.zeros_state) == 8 * ctypes.sizeof(ctypes.c_void_p)
+
+
+# placeholder addresses, far apart so they never overlap unless a test wants them to
+P = {name: 0x10000000 * (i + 1) for i, name in enumerate(("q", "k", "v", "u", "mu", "tau", "g1", "gh", "o"))}
+
+
+def shape(B=1, H=2, N=8, d=16, d_u=16, dtype=0, rope=0, base=10000.0):
+    return L.zeros_shape(B, H, N, d, d_u, dtype, rope, base)
+
+
+def call_causal(lib, shp, ptrs=None, state=None):
+    p = dict(P, **(ptrs or {}))
+    return lib.zeros_fwd_causal(ctypes.byref(shp) if shp is not None else None, p["q"], p["k"], p["v"],
+                                p["u"], p["mu"], p["tau"], p["g1"], p["gh"], p["o"], state, None)
+
+
+def call_encoder(lib, shp, ptrs=None):
+    p = dict(P, **(ptrs or {}))
+    return lib.zeros_fwd_encoder(ctypes.byref(shp), p["q"], p["k"], p["v"], p["u"], p["mu"], p["tau"],
+                                 p["g1"], p["gh"], p["o"], None)
+
+
+def call_decode(lib, shp, state, ptrs=None):
+    p = dict(P, **(ptrs or {}))
+    return lib.zeros_decode_step(ctypes.byref(shp), p["q"], p["k"], p["v"], p["u"], p["mu"], p["tau"],
+                                 p["g1"], p["gh"], p["o"], state, None)
+
+
+def test_null_shape(lib):
+    assert call_causal(lib, None) == L.ZEROS_ERR_NULL
+    assert "shape" in lib.zeros_last_error().decode()
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "u", "mu", "tau", "g1", "gh", "o"])
+def test_null_tensor(lib, name):
+    assert call_causal(lib, shape(), {name: None}) == L.ZEROS_ERR_NULL
+    assert call_encoder(lib, shape(), {name: None}) == L.ZEROS_ERR_NULL
+
+
+def test_bad_dtype(lib):
+    assert call_causal(lib, shape(dtype=7)) == L.ZEROS_ERR_DTYPE
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=-1), dict(d=0), dict(d_u=0),
+                                dict(B=1 << 20, H=1 << 10, N=1 << 10, d=128, d_u=128)])
+def test_bad_sizes(lib, kw):
+    assert call_causal(lib, shape(**kw)) == L.ZEROS_ERR_SHAPE
+
+
+@pytest.mark.parametrize("kw", [dict(d=96, d_u=96), dict(d=256, d_u=256), dict(d=64, d_u=32),
+                                dict(rope=2)])
+def test_unsupported(lib, kw):
+    assert call_causal(lib, shape(**kw)) == L.ZEROS_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("base", [0.5, float("inf"), float("nan")])
+def test_bad_rope_base(lib, base):
+    assert call_causal(lib, shape(rope=1, base=base)) == L.ZEROS_ERR_SHAPE
+
+
+def test_output_alias(lib):
+    # o starts inside q's byte range: [B,H,N,d] = 1*2*8*16 f32 = 1024 bytes
+    assert call_causal(lib, shape(), {"o": P["q"] + 512}) == L.ZEROS_ERR_ALIAS
+    assert call_encoder(lib, shape(), {"o": P["gh"]}) == L.ZEROS_ERR_ALIAS
+
+
+def test_partial_state_rejected(lib):
+    st = L.zeros_state(1, 2, 3, 4, 5, 6, 7, None)
+    assert call_causal(lib, shape(), state=ctypes.byref(st)) == L.ZEROS_ERR_NULL
+
+
+def test_decode_validation(lib):
+    st = L.zeros_state(1, 2, 3, 4, 5, 6, 7, 8)
+    assert call_decode(lib, shape(N=2), ctypes.byref(st)) == L.ZEROS_ERR_SHAPE
+    assert call_decode(lib, shape(N=1), None) == L.ZEROS_ERR_NULL
+    bad = L.zeros_state(1, 2, 3, None, 5, 6, 7, 8)
+    assert call_decode(lib, shape(N=1), ctypes.byref(bad)) == L.ZEROS_ERR_NULL
+    assert call_decode(lib, shape(N=1, d=48, d_u=48), ctypes.byref(st)) == L.ZEROS_ERR_UNSUPPORTED
+
+
+def test_misaligned_state_rejected(lib):
+    st = L.zeros_state(0x1000008, 0x2000000, 0x3000000, 0x4000000, 0x5000000, 0x6000000, 0x7000000, 0x8000000)
+    assert call_decode(lib, shape(N=1), ctypes.byref(st)) == L.ZEROS_ERR_SHAPE
+    assert call_causal(lib, shape(), state=ctypes.byref(st)) == L.ZEROS_ERR_SHAPE
+
+
+def test_empty_sequence_is_a_noop(lib):
+    none = {k: None for k in ("q", "k", "v", "u", "g1", "gh", "o")}
+    assert call_causal(lib, shape(N=0), none) == L.ZEROS_OK
+    assert call_encoder(lib, shape(N=0), none) == L.ZEROS_OK
+    assert call_causal(lib, shape(N=0), {"mu": None}) == L.ZEROS_ERR_NULL
+    assert call_causal(lib, shape(N=0)) == L.ZEROS_OK
+    assert call_encoder(lib, shape(N=0)) == L.ZEROS_OK
+    assert lib.zeros_last_error().decode() == ""
+
+
+def test_state_bytes_and_packing(lib):
+    S, H, d, du = 3, 5, 64, 64
+    n = S * H
+    a256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    expect = 3 * a256(n * d * d * 4) + a256(n * du * 4) + 4 * a256(n * 4)
+    assert lib.zeros_state_bytes(S, H, d, du) == expect
+    assert lib.zeros_state_bytes(0, H, d, du) == 0
+    st = L.zeros_state()
+    base = 0x40000000
+    assert lib.zeros_state_from_buffer(base, S, H, d, du, ctypes.byref(st)) == L.ZEROS_OK
+    fields = [st.F, st.G, st.Hs, st.Su, st.m, st.E, st.P, st.t]
+    assert fields[0] == base
+    assert all(f % 256 == 0 for f in fields)
+    assert fields == sorted(fields)
+    assert st.t + n * 4 <= base + expect
+    assert lib.zeros_state_from_buffer(None, S, H, d, du, ctypes.byref(st)) == L.ZEROS_ERR_NULL

@@ -1,0 +1,277 @@
+"""GPU parity: libzeros (through its C ABI) against the float64 oracle on the same seeded inputs.
+
+Bar: relative L2 error of the whole output <= 1e-4 for float32 inputs and <= 2e-2 for bfloat16
+inputs with float32 accumulation. Sizes span several 32-token chunks and a ragged tail; the
+full-size workloads are compared on sampled heads, which the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import zeros_ref as R
+from synth import CONFIGS, make_inputs
+from synth.inputs import decode_prefill_batch
+from tests.gpu_helpers import TOL, rel_l2, slice_heads, tail_rel_l2, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+# Where the exact output is zero (a single token, u = 0) float32 rounding leaves residues of
+# order eps32 * |v|: bound them absolutely.
+ZERO_ABS = 1e-6
+
+import zero_sum_attention_amd as Z  # noqa: E402
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    print(f"\n[gpu-case] {request.node.nodeid}", flush=True)
+    yield
+    torch.cuda.synchronize()
+
+
+def run_causal(x, dtype, rope=False, state_out=None):
+    t = to_device(x, dtype)
+    o = Z.zeros_fwd_causal(t["q"], t["k"], t["v"], t["u"], t["mu"], t["tau"], t["g1"], t["gh"],
+                           rope=rope, state_out=state_out)
+    torch.cuda.synchronize()
+    return o
+
+
+def run_encoder(x, dtype, rope=False):
+    t = to_device(x, dtype)
+    o = Z.zeros_fwd_encoder(t["q"], t["k"], t["v"], t["u"], t["mu"], t["tau"], t["g1"], t["gh"], rope=rope)
+    torch.cuda.synchronize()
+    return o
+
+
+def test_library_is_native():
+    lib = Z.load_library()
+    assert lib.zeros_abi_version() == 1
+    assert torch.cuda.is_available()
+
+
+# ------------------------------------------------------------------ the configured workloads
+
+def test_config1_tiny_causal():
+    wl = CONFIGS[1]
+    x = make_inputs(wl)
+    o = to_f64(run_causal(x, wl.dtype))
+    ref = R.causal_forward(**x)
+    assert rel_l2(o, ref) <= TOL["f32"]
+    assert rel_l2(o, R.causal_brute_force(**x)) <= TOL["f32"]
+
+
+def test_config2_lm_layer_causal():
+    wl = CONFIGS[2]
+    x = make_inputs(wl)
+    o = to_f64(run_causal(x, wl.dtype))
+    ref = R.causal_forward(**x)
+    err = rel_l2(o, ref)
+    print(f"config2 rel_l2={err:.3e}", flush=True)
+    assert err <= TOL["f32"]
+
+
+def test_config3_vit_encoder():
+    wl = CONFIGS[3]
+    x = make_inputs(wl)
+    o = to_f64(run_encoder(x, wl.dtype))
+    ref = R.encoder_forward(**x)
+    err = rel_l2(o, ref)
+    print(f"config3 rel_l2={err:.3e}", flush=True)
+    assert err <= TOL["bf16"]
+
+
+def test_config4_long_rope_sampled_heads():
+    wl = CONFIGS[4]
+    x = make_inputs(wl)
+    o = run_causal(x, wl.dtype, rope=True)
+    pairs = [(0, 0), (1, 15), (0, 9)]
+    xs = slice_heads(x, pairs)
+    ref = R.causal_forward(**xs, rope=True)
+    got = np.stack([to_f64(o[b, h]) for b, h in pairs])[None]
+    err, tail = rel_l2(got, ref), tail_rel_l2(got, ref, 1024)
+    print(f"config4 sampled rel_l2={err:.3e} tail(t>1024)={tail:.3e}", flush=True)
+    assert err <= TOL["bf16"]
+    assert np.all(np.isfinite(to_f64(o)))
+
+
+# ------------------------------------------------------------------ shapes, tails, options
+
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("N", [1, 31, 33, 100])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rope", [False, True])
+def test_causal_shapes(d, N, dtype, rope):
+    wl = CONFIGS[2].with_(B=2, H=3, N=N, d=d, d_u=d, dtype=dtype, seed=1000 + d + N)
+    x = make_inputs(wl)
+    o = to_f64(run_causal(x, dtype, rope=rope))
+    ref = R.causal_forward(**x, rope=rope)
+    assert np.max(np.abs(o[..., 0, :])) <= ZERO_ABS      # o_1 = 0
+    if N > 1:
+        assert rel_l2(o, ref) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("d", [16, 64, 128])
+@pytest.mark.parametrize("N", [1, 2, 47, 197])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rope", [False, True])
+def test_encoder_shapes(d, N, dtype, rope):
+    wl = CONFIGS[3].with_(B=2, H=2, N=N, d=d, d_u=d, dtype=dtype, seed=2000 + d + N)
+    x = make_inputs(wl)
+    o = to_f64(run_encoder(x, dtype, rope=rope))
+    ref = R.encoder_forward(**x, rope=rope)
+    if N == 1:
+        assert np.max(np.abs(o)) <= ZERO_ABS    # one token: its weight is zero
+    else:
+        assert rel_l2(o, ref) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("scale,tol", [(10.0, 1e-4), (30.0, 1e-3)])
+def test_logit_stress_running_max(scale, tol):
+    wl = CONFIGS[2].with_(B=1, H=4, N=300, seed=77)
+    x = make_inputs(wl, u_scale=scale)
+    o = to_f64(run_causal(x, "f32"))
+    assert np.all(np.isfinite(o))
+    assert rel_l2(o, R.causal_forward(**x)) <= tol
+
+
+def test_first_row_zero_and_constant_logits():
+    wl = CONFIGS[2].with_(B=1, H=2, N=70, seed=78)
+    x = make_inputs(wl)
+    o = to_f64(run_causal(x, "f32"))
+    assert np.max(np.abs(o[..., 0, :])) <= ZERO_ABS
+    x["u"] = np.zeros_like(x["u"])
+    assert np.max(np.abs(to_f64(run_causal(x, "f32")))) <= ZERO_ABS
+
+
+def test_deterministic_and_causal():
+    wl = CONFIGS[2].with_(B=2, H=2, N=200, seed=79)
+    x = make_inputs(wl)
+    o1 = run_causal(x, "f32").cpu()
+    o2 = run_causal(x, "f32").cpu()
+    assert torch.equal(o1, o2)
+    y = {k: np.array(v, copy=True) for k, v in x.items()}
+    rng = np.random.default_rng(5)
+    for key in ("q", "k", "v", "u"):
+        y[key][..., 150:, :] = rng.standard_normal(y[key][..., 150:, :].shape).astype(np.float32)
+    o3 = run_causal(y, "f32").cpu()
+    assert torch.equal(o1[..., :150, :], o3[..., :150, :])
+    assert not torch.equal(o1[..., 150:, :], o3[..., 150:, :])
+
+
+# ------------------------------------------------------------------ state and decode
+
+def _state_np(st):
+    return {"F": to_f64(st.F), "G": to_f64(st.G), "H": to_f64(st.Hs), "Su": to_f64(st.Su),
+            "m": to_f64(st.m), "E": to_f64(st.E), "P": to_f64(st.P),
+            "t": st.t.cpu().numpy().astype(np.int64)}
+
+
+@pytest.mark.parametrize("rope", [False, True])
+def test_state_out_matches_oracle(rope):
+    wl = CONFIGS[2].with_(B=2, H=3, N=77, d=32, d_u=32, seed=80)
+    x = make_inputs(wl)
+    st = Z.DecodeState(2, 3, 32, 32).reset()
+    run_causal(x, "f32", rope=rope, state_out=st)
+    _, ref = R.causal_forward(**x, rope=rope, return_state=True)
+    got = _state_np(st)
+    assert np.all(got["t"] == 77)
+    for key in ("m", "E", "P", "Su", "F", "G", "H"):
+        assert rel_l2(got[key], ref[key]) <= 1e-5, key
+
+
+def test_state_out_empty_sequence():
+    wl = CONFIGS[2].with_(B=1, H=2, N=0, d=16, d_u=16, seed=81)
+    x = make_inputs(wl)
+    st = Z.DecodeState(1, 2, 16, 16)
+    st.buffer.fill_(0x7F)
+    run_causal(x, "f32", state_out=st)
+    assert torch.all(st.t == 0) and torch.all(torch.isneginf(st.m))
+    for key in ("F", "G", "Hs", "Su", "E", "P"):
+        assert torch.all(getattr(st, key) == 0), key
+
+
+@pytest.mark.parametrize("dtype,rope", [("f32", False), ("f32", True), ("bf16", True)])
+def test_decode_continues_forward(dtype, rope):
+    wl = CONFIGS[2].with_(B=3, H=2, N=65, d=64, d_u=64, dtype=dtype, seed=82)
+    x = make_inputs(wl)
+    cut = 64
+    head = {k: (v[..., :cut, :] if v.ndim == 4 else v[..., :cut] if v.ndim == 3 else v) for k, v in x.items()}
+    st = Z.DecodeState(3, 2, 64, 64).reset()
+    run_causal(head, dtype, rope=rope, state_out=st)
+    t = to_device(x, dtype)
+    o_step = Z.zeros_decode_step(t["q"][:, :, cut].contiguous(), t["k"][:, :, cut].contiguous(),
+                                 t["v"][:, :, cut].contiguous(), t["u"][:, :, cut].contiguous(),
+                                 t["mu"], t["tau"], t["g1"][:, :, cut].contiguous(),
+                                 t["gh"][:, :, cut].contiguous(), st, rope=rope)
+    torch.cuda.synchronize()
+    ref = R.causal_forward(**x, rope=rope)[..., cut, :]
+    assert rel_l2(to_f64(o_step), ref) <= TOL[dtype]
+    assert torch.all(st.t == cut + 1)
+
+
+def test_decode_from_empty_state_runs_the_recurrence():
+    wl = CONFIGS[2].with_(B=2, H=2, N=20, d=16, d_u=16, seed=83)
+    x = make_inputs(wl)
+    t = to_device(x, "f32")
+    st = Z.DecodeState(2, 2, 16, 16).reset()
+    outs = []
+    for n in range(20):
+        outs.append(Z.zeros_decode_step(*(t[k][:, :, n].contiguous() for k in ("q", "k", "v", "u")),
+                                        t["mu"], t["tau"], t["g1"][:, :, n].contiguous(),
+                                        t["gh"][:, :, n].contiguous(), st))
+    o = to_f64(torch.stack(outs, dim=2))
+    assert rel_l2(o, R.causal_forward(**x)) <= TOL["f32"]
+
+
+def test_config5_decode_full_size():
+    """256 sequences x 32 heads, prefilled to t = 8192 with the causal forward, then one step.
+
+    Parity: (a) the step from the GPU's own state, against the oracle step applied to that same
+    state in float64, over every head; (b) the prefilled state of sampled (sequence, head) pairs
+    against the oracle recurrence over their 8192 prefix tokens.
+    """
+    wl = CONFIGS[5]
+    S, H, d = wl.B, wl.H, wl.d
+    st = Z.DecodeState(S, H, d, d).reset()
+    step = make_inputs(wl)
+    t = to_device(step, wl.dtype)
+    mu, tau = t["mu"], t["tau"]
+    samples = [(0, 0), (200, 31)]
+    sampled_prefix = {}
+    batch = 16
+    for s0 in range(0, S, batch):
+        pre = decode_prefill_batch(wl, s0, s0 + batch)
+        Z.zeros_fwd_causal(pre["q"], pre["k"], pre["v"], pre["u"], mu, tau, pre["g1"], pre["gh"],
+                           state_out=st.sequences(s0, s0 + batch))
+        for (s, h) in samples:
+            if s0 <= s < s0 + batch:
+                sampled_prefix[(s, h)] = {k: to_f64(val[s - s0, h]) for k, val in pre.items()}
+        del pre
+    torch.cuda.synchronize()
+    assert torch.all(st.t == wl.prefill)
+    # (b) sampled prefill states
+    for (s, h), px in sampled_prefix.items():
+        _, ref = R.causal_forward(px["q"], px["k"], px["v"], px["u"], step["mu"][h], step["tau"][h],
+                                  px["g1"], px["gh"], return_state=True)
+        for key, gk in (("F", st.F), ("G", st.G), ("H", st.Hs)):
+            assert rel_l2(to_f64(gk[s, h]), ref[key]) <= 1e-3, (s, h, key)
+        assert abs(float(st.m[s, h]) - ref["m"]) <= 1e-4
+        assert rel_l2(to_f64(st.Su[s, h]), ref["Su"]) <= 1e-4
+    # (a) one step from the identical state
+    before = {k: getattr(st, a).cpu() for k, a in (("F", "F"), ("G", "G"), ("H", "Hs"), ("Su", "Su"),
+                                                 ("m", "m"), ("E", "E"), ("P", "P"), ("t", "t"))}
+    sq = {k: t[k][:, :, 0].contiguous() for k in ("q", "k", "v", "u", "g1", "gh")}
+    o = Z.zeros_decode_step(sq["q"], sq["k"], sq["v"], sq["u"], mu, tau, sq["g1"], sq["gh"], st)
+    torch.cuda.synchronize()
+    o = to_f64(o)
+    ref_o = np.empty_like(o)
+    for s0 in range(0, S, 32):
+        sl = slice(s0, s0 + 32)
+        state = {k: v[sl].numpy().astype(np.float64 if k != "t" else np.int64) for k, v in before.items()}
+        ref_o[sl], _ = R.decode_step(state, *(step[k][sl, :, 0] for k in ("q", "k", "v", "u")),
+                                     step["mu"], step["tau"], step["g1"][sl, :, 0], step["gh"][sl, :, 0])
+    err = rel_l2(o, ref_o)
+    print(f"config5 step rel_l2={err:.3e}", flush=True)
+    assert err <= TOL["bf16"]
+    assert torch.all(st.t == wl.prefill + 1)

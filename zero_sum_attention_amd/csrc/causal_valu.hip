@@ -1,0 +1,338 @@
+// Causal ZeroS forward, float32 VALU path (all d, both storage types).
+//
+// Method: Paper-Notes page "ZeroS: Zero-Sum Linear Attention for Efficient Transformers",
+// 关键设计 (zero-sum weights, radial-angular decoupling, deviation logits, linear-time prefix
+// scan). Per head the output is o_t = sum_{i<=t} (alpha_t e^{s_i} + beta_t s_i + gamma_t)
+// (q^_t . k^_i) v_i, which the prefix states turn into a recurrence.
+//
+// Work split: one workgroup per (batch, head, 16-column tile of v/o). The workgroup walks the
+// sequence in chunks of kC tokens. For a chunk covering (t0, t1]:
+//   o_t = sum_{t0<i<=t} W_{t,i} v_i + q^_t (a_t e^{m0-m_t} F + beta_t G + gamma_t H)   (states at t0)
+// with W_{t,i} = (q^_t.k^_i)(a_t e^{s_i-m_t} + beta_t s_i + gamma_t), a_t = sigmah_t / E_t, and
+// E, F rescaled by the running logit maximum m. The chunk then folds its keys into F, G, H.
+// The u running sum, logits and scalar scans are recomputed by every tile of a head (they are
+// O(C d) per chunk against O(C d^2) for the contractions).
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace zeros {
+namespace {
+
+constexpr int kC = 32;         // tokens per chunk
+constexpr int kThreads = 256;  // 4 waves
+constexpr int kTile = 16;      // value columns per workgroup
+constexpr int kTPR = 8;        // threads per token row in the load phase
+
+template <int D>
+struct CausalSmem {
+    float qh[kC][D + 1];   // normalised (and rotated) queries of the chunk
+    float kh[kC][D + 1];   // normalised (and rotated) keys
+    float ub[kC][D + 1];   // u, then u * ubar
+    float vt[kC][kTile];   // this workgroup's value columns
+    float W[kC][kC + 1];   // intra-chunk weights times cosines
+    float F[D][kTile], G[D][kTile], Hs[D][kTile];
+    float s[kC], sig1[kC], sigh[kC], invden[kC];
+    float a_in[kC];        // a_t e^{m0 - m_t}: multiplies the carried F
+    float a_loc[kC];       // a_t = sigmah_t / E_t (E relative to m_t)
+    float mrow[kC], brow[kC], grow[kC];
+    float estate[kC];      // e^{s_i - m1}: key weight of the F update
+    float carry[4];        // m1, E1, P1 at the chunk end and the decay e^{m0 - m1}
+};
+
+template <typename T>
+__device__ __forceinline__ float ld(const T *p, size_t i) { return to_f32(p[i]); }
+
+template <int D, typename T, bool ROPE>
+__global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p) {
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    CausalSmem<D> &sm = *reinterpret_cast<CausalSmem<D> *>(smem_raw);
+    constexpr int NTILE = D / kTile;
+    constexpr int EPT = D / kTPR;
+    const int tid = threadIdx.x;
+
+    // The NTILE workgroups of one head read the same q/k/u rows: keep them on one XCD
+    // (consecutive dispatch slots go round-robin over the 8 XCDs).
+    const int G = gridDim.x;
+    int L = blockIdx.x;
+    if ((G & 7) == 0) L = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+    const int tile = L % NTILE;
+    const int bh = L / NTILE;
+    const int h = bh % p.H;
+    const int N = p.N;
+    const size_t row0 = static_cast<size_t>(bh) * N;
+    const T *q = static_cast<const T *>(p.q) + row0 * D;
+    const T *k = static_cast<const T *>(p.k) + row0 * D;
+    const T *v = static_cast<const T *>(p.v) + row0 * D;
+    const T *u = static_cast<const T *>(p.u) + row0 * D;
+    const T *g1 = static_cast<const T *>(p.g1) + row0;
+    const T *gh = static_cast<const T *>(p.gh) + row0;
+    T *o = static_cast<T *>(p.o) + row0 * D;
+
+    const float et = expf(p.tau[h]);
+    const float rs_du = 1.f / sqrtf(static_cast<float>(D));
+
+    const int lr = tid / kTPR, lp = tid % kTPR, c0 = lp * EPT;
+    double rope_rev[ROPE ? EPT / 2 : 1];
+    if (ROPE) {
+#pragma unroll
+        for (int jj = 0; jj < EPT / 2; ++jj) rope_rev[jj] = rope_rev_per_pos(c0 / 2 + jj, D, p.rope_base);
+    }
+
+    float Su = 0.f;                                         // owned by thread tid < D
+    const float emu = (tid < D) ? et * p.mu[h * D + tid] : 0.f;
+    float m_c = kNegInf, E_c = 0.f, P_c = 0.f;
+
+    for (int x = tid; x < D * kTile; x += kThreads) {
+        (&sm.F[0][0])[x] = 0.f;
+        (&sm.G[0][0])[x] = 0.f;
+        (&sm.Hs[0][0])[x] = 0.f;
+    }
+
+    for (int t0 = 0; t0 < N; t0 += kC) {
+        const int nval = min(kC, N - t0);
+
+        // ---- load, normalise, rotate
+        {
+            const int tok = t0 + lr;
+            const bool valid = lr < nval;
+            float xq[EPT], xk[EPT], xu[EPT];
+            float ssq = 0.f, ssk = 0.f;
+#pragma unroll
+            for (int c = 0; c < EPT; ++c) {
+                const size_t idx = static_cast<size_t>(tok) * D + c0 + c;
+                xq[c] = valid ? ld(q, idx) : 0.f;
+                xk[c] = valid ? ld(k, idx) : 0.f;
+                xu[c] = valid ? ld(u, idx) : 0.f;
+                ssq += xq[c] * xq[c];
+                ssk += xk[c] * xk[c];
+            }
+            ssq = group_sum<kTPR>(ssq);
+            ssk = group_sum<kTPR>(ssk);
+            const float iq = 1.f / fmaxf(sqrtf(ssq), 1e-12f);
+            const float ik = 1.f / fmaxf(sqrtf(ssk), 1e-12f);
+#pragma unroll
+            for (int c = 0; c < EPT; ++c) {
+                xq[c] *= iq;
+                xk[c] *= ik;
+            }
+            if (ROPE) {
+#pragma unroll
+                for (int jj = 0; jj < EPT / 2; ++jj) {
+                    float cs, sn;
+                    rope_cos_sin(rope_rev[jj], tok, cs, sn);
+                    const float q0 = xq[2 * jj], q1 = xq[2 * jj + 1];
+                    const float k0 = xk[2 * jj], k1 = xk[2 * jj + 1];
+                    xq[2 * jj] = q0 * cs - q1 * sn;
+                    xq[2 * jj + 1] = q0 * sn + q1 * cs;
+                    xk[2 * jj] = k0 * cs - k1 * sn;
+                    xk[2 * jj + 1] = k0 * sn + k1 * cs;
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < EPT; ++c) {
+                sm.qh[lr][c0 + c] = xq[c];
+                sm.kh[lr][c0 + c] = xk[c];
+                sm.ub[lr][c0 + c] = xu[c];
+            }
+        }
+        {
+            const int r = tid / 8, mc = (tid % 8) * 2;
+            const bool valid = r < nval;
+            const size_t idx = static_cast<size_t>(t0 + r) * D + tile * kTile + mc;
+            sm.vt[r][mc] = valid ? ld(v, idx) : 0.f;
+            sm.vt[r][mc + 1] = valid ? ld(v, idx + 1) : 0.f;
+        }
+        if (tid < kC) {
+            const bool valid = tid < nval;
+            sm.sig1[tid] = valid ? sigmoidf(ld(g1, t0 + tid)) : 0.f;
+            sm.sigh[tid] = valid ? sigmoidf(ld(gh, t0 + tid)) : 0.f;
+            sm.invden[tid] = 1.f / (et + static_cast<float>(t0 + tid + 1));
+        }
+        __syncthreads();
+
+        // ---- running u-sum and ubar: products u_i * ubar_i in place
+        if (tid < D) {
+            for (int r = 0; r < nval; ++r) {
+                const float ur = sm.ub[r][tid];
+                Su += ur;
+                sm.ub[r][tid] = ur * ((emu + Su) * sm.invden[r]);
+            }
+        }
+        __syncthreads();
+        {
+            float acc = 0.f;
+#pragma unroll
+            for (int c = 0; c < EPT; ++c) acc += sm.ub[lr][c0 + c];
+            acc = group_sum<kTPR>(acc);
+            if (lp == 0) sm.s[lr] = -acc * rs_du;
+        }
+        __syncthreads();
+
+        // ---- scans of (max, sum e^{s-max}, sum s) over the chunk, joined with the carry
+        if (tid < 64) {
+            const int r = tid;
+            const bool valid = r < nval;
+            const float sr = valid ? sm.s[r] : 0.f;
+            float m = valid ? sr : kNegInf, e = valid ? 1.f : 0.f, ps = valid ? sr : 0.f;
+#pragma unroll
+            for (int off = 1; off < kC; off <<= 1) {
+                const float m2 = __shfl_up(m, off, 64);
+                const float e2 = __shfl_up(e, off, 64);
+                const float p2 = __shfl_up(ps, off, 64);
+                if (r >= off) {
+                    const float M = fmaxf(m, m2);
+                    e = e * exp_diff(m, M) + e2 * exp_diff(m2, M);
+                    ps += p2;
+                    m = M;
+                }
+            }
+            const float M = fmaxf(m_c, m);
+            const float E = E_c * exp_diff(m_c, M) + e * exp_diff(m, M);
+            const float P = P_c + ps;
+            if (valid) {
+                const float tt = static_cast<float>(t0 + r + 1);
+                const float s1 = sm.sig1[r], sh = sm.sigh[r];
+                const float a = sh / E;
+                const float d1 = s1 - sh;
+                sm.a_loc[r] = a;
+                sm.a_in[r] = a * exp_diff(m_c, M);
+                sm.mrow[r] = M;
+                sm.brow[r] = d1 / tt;
+                sm.grow[r] = -d1 * (P / tt) / tt - sh / tt;
+            }
+            if (r == nval - 1) {
+                sm.carry[0] = M;
+                sm.carry[1] = E;
+                sm.carry[2] = P;
+                sm.carry[3] = exp_diff(m_c, M);
+            }
+        }
+        __syncthreads();
+        const float m_new = sm.carry[0];
+        if (tid < kC) sm.estate[tid] = (tid < nval) ? expf(sm.s[tid] - m_new) : 0.f;
+
+        // ---- intra-chunk weights W_{t,i} (i <= t)
+        {
+            const int t = tid / 8, i0 = (tid % 8) * 4;
+            float acc[4] = {0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < D; ++j) {
+                const float qv = sm.qh[t][j];
+#pragma unroll
+                for (int x = 0; x < 4; ++x) acc[x] += qv * sm.kh[i0 + x][j];
+            }
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int i = i0 + x;
+                float w = 0.f;
+                if (i <= t && t < nval) {
+                    const float si = sm.s[i];
+                    w = acc[x] * (sm.a_loc[t] * expf(si - sm.mrow[t]) + sm.brow[t] * si + sm.grow[t]);
+                }
+                sm.W[t][i] = w;
+            }
+        }
+        __syncthreads();
+
+        // ---- outputs: intra-chunk part plus the carried states
+        {
+            const int t = tid / 8, m0 = (tid % 8) * 2;
+            float out[2];
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                const int mm = m0 + x;
+                float intra = 0.f;
+                for (int i = 0; i <= t; ++i) intra += sm.W[t][i] * sm.vt[i][mm];
+                float xF = 0.f, xG = 0.f, xH = 0.f;
+                for (int j = 0; j < D; ++j) {
+                    const float qv = sm.qh[t][j];
+                    xF += qv * sm.F[j][mm];
+                    xG += qv * sm.G[j][mm];
+                    xH += qv * sm.Hs[j][mm];
+                }
+                out[x] = intra + sm.a_in[t] * xF + sm.brow[t] * xG + sm.grow[t] * xH;
+            }
+            if (t < nval) {
+                const size_t idx = static_cast<size_t>(t0 + t) * D + tile * kTile + m0;
+                o[idx] = from_f32<T>(out[0]);
+                o[idx + 1] = from_f32<T>(out[1]);
+            }
+        }
+        __syncthreads();
+
+        // ---- fold the chunk's keys into the states
+        {
+            const int mm = tid % kTile;
+            const float decay = sm.carry[3];
+            for (int j = tid / kTile; j < D; j += kThreads / kTile) {
+                float f = 0.f, g = 0.f, hh = 0.f;
+                for (int i = 0; i < nval; ++i) {
+                    const float kv = sm.kh[i][j] * sm.vt[i][mm];
+                    f += sm.estate[i] * kv;
+                    g += sm.s[i] * kv;
+                    hh += kv;
+                }
+                sm.F[j][mm] = decay * sm.F[j][mm] + f;
+                sm.G[j][mm] += g;
+                sm.Hs[j][mm] += hh;
+            }
+        }
+        m_c = m_new;
+        E_c = sm.carry[1];
+        P_c = sm.carry[2];
+        __syncthreads();
+    }
+
+    // ---- final state
+    if (p.st.F != nullptr) {
+        const size_t mat0 = static_cast<size_t>(bh) * D * D;
+        for (int x = tid; x < D * kTile; x += kThreads) {
+            const int j = x / kTile, mm = x % kTile;
+            const size_t idx = mat0 + static_cast<size_t>(j) * D + tile * kTile + mm;
+            p.st.F[idx] = sm.F[j][mm];
+            p.st.G[idx] = sm.G[j][mm];
+            p.st.Hs[idx] = sm.Hs[j][mm];
+        }
+        if (tile == 0) {
+            if (tid < D) p.st.Su[static_cast<size_t>(bh) * D + tid] = Su;
+            if (tid == 0) {
+                p.st.m[bh] = m_c;
+                p.st.E[bh] = E_c;
+                p.st.P[bh] = P_c;
+                p.st.t[bh] = N;
+            }
+        }
+    }
+}
+
+template <int D, typename T, bool ROPE>
+hipError_t launch_one(const Problem &p, hipStream_t stream) {
+    const size_t smem = sizeof(CausalSmem<D>);
+    const void *fn = reinterpret_cast<const void *>(&causal_valu_kernel<D, T, ROPE>);
+    hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         static_cast<int>(smem));
+    if (err != hipSuccess) return err;
+    const int grid = p.B * p.H * (D / kTile);
+    hipLaunchKernelGGL((causal_valu_kernel<D, T, ROPE>), dim3(grid), dim3(kThreads), smem, stream, p);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const Problem &p, hipStream_t stream) {
+    if (p.dtype == ZEROS_BF16)
+        return p.rope ? launch_one<D, bf16, true>(p, stream) : launch_one<D, bf16, false>(p, stream);
+    return p.rope ? launch_one<D, float, true>(p, stream) : launch_one<D, float, false>(p, stream);
+}
+
+}  // namespace
+
+hipError_t launch_causal_valu(const Problem &p, hipStream_t stream) {
+    switch (p.d) {
+        case 16: return launch_d<16>(p, stream);
+        case 32: return launch_d<32>(p, stream);
+        case 64: return launch_d<64>(p, stream);
+        case 128: return launch_d<128>(p, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace zeros

@@ -1,0 +1,70 @@
+// Device helpers shared by the libzeros kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace zeros {
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// bfloat16 storage: the upper 16 bits of an IEEE float32.
+struct bf16 {
+    uint16_t bits;
+};
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) {
+    return __uint_as_float(static_cast<uint32_t>(x.bits) << 16);
+}
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) {
+    // round to nearest, ties to even; NaN stays a quiet NaN
+    uint32_t u = __float_as_uint(x);
+    bf16 r;
+    if ((u & 0x7fffffffu) > 0x7f800000u) {
+        r.bits = static_cast<uint16_t>((u >> 16) | 0x40u);
+    } else {
+        u += 0x7fffu + ((u >> 16) & 1u);
+        r.bits = static_cast<uint16_t>(u >> 16);
+    }
+    return r;
+}
+
+__device__ __forceinline__ float sigmoidf(float x) {
+    // 1/(1+e^-x) without overflow for large |x|
+    if (x >= 0.f) return 1.f / (1.f + expf(-x));
+    const float e = expf(x);
+    return e / (1.f + e);
+}
+
+// exp(a - b) that treats a = -inf as contributing zero (also when b = -inf).
+__device__ __forceinline__ float exp_diff(float a, float b) {
+    return (a == kNegInf) ? 0.f : expf(a - b);
+}
+
+// RoPE frequency of pair j expressed in revolutions per position: base^(-2j/d) / (2 pi).
+__device__ __forceinline__ double rope_rev_per_pos(int j, int d, float base) {
+    return pow(static_cast<double>(base), -2.0 * j / d) * 0.15915494309189535;  // 1/(2 pi)
+}
+
+// cos/sin of pos * theta_j with the angle reduced exactly enough in double precision:
+// rev = pos * theta_j / (2 pi) is formed in double, its integer part dropped, and the
+// remaining fraction of a turn converted to radians in [-pi, pi] before a float sincos.
+__device__ __forceinline__ void rope_cos_sin(double rev_per_pos, int pos, float &c, float &s) {
+    double r = static_cast<double>(pos) * rev_per_pos;
+    r -= rint(r);
+    const float ang = static_cast<float>(r * 6.283185307179586);
+    sincosf(ang, &s, &c);
+}
+
+// Sum over groups of G consecutive lanes (G a power of two <= 64); every lane gets the sum.
+template <int G> __device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+    for (int off = 1; off < G; off <<= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+}  // namespace zeros

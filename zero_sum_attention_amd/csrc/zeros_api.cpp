@@ -1,0 +1,193 @@
+// C-ABI front end of libzeros: argument validation, dispatch and error reporting.
+// Every check runs on the host before any HIP call, so invalid arguments never reach a kernel.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "launch.hpp"
+
+namespace zeros {
+hipError_t launch_causal_valu(const Problem &p, hipStream_t stream);
+}
+
+namespace {
+
+thread_local std::string g_last_error;
+
+zeros_status fail(zeros_status st, const std::string &msg) {
+    g_last_error = msg;
+    return st;
+}
+
+zeros_status ok() {
+    g_last_error.clear();
+    return ZEROS_OK;
+}
+
+size_t elem_bytes(int dtype) { return dtype == ZEROS_BF16 ? 2 : 4; }
+
+struct Range {
+    const void *p;
+    size_t bytes;
+};
+
+bool overlap(const Range &a, const Range &b) {
+    if (a.bytes == 0 || b.bytes == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// Common validation of the shape and the input/output pointers. `tokens` is the number of
+// token rows per (b, h) that the call reads (N for the forward calls, 1 for decode).
+zeros_status check_common(const zeros_shape *s, const void *q, const void *k, const void *v,
+                          const void *u, const float *mu, const float *tau, const void *g1,
+                          const void *gh, const void *o, const char *fn) {
+    const std::string f(fn);
+    if (!s) return fail(ZEROS_ERR_NULL, f + ": shape is NULL");
+    if (!mu || !tau) return fail(ZEROS_ERR_NULL, f + ": mu or tau is NULL");
+    // token tensors may be NULL only when there are no tokens (N = 0)
+    if ((!q || !k || !v || !u || !g1 || !gh || !o) && s->N != 0)
+        return fail(ZEROS_ERR_NULL, f + ": a tensor pointer is NULL");
+    if (s->dtype != ZEROS_F32 && s->dtype != ZEROS_BF16)
+        return fail(ZEROS_ERR_DTYPE, f + ": dtype must be ZEROS_F32 or ZEROS_BF16");
+    if (s->B < 1 || s->H < 1 || s->N < 0 || s->d < 1 || s->d_u < 1)
+        return fail(ZEROS_ERR_SHAPE, f + ": need B, H, d, d_u >= 1 and N >= 0");
+    if (s->d != 16 && s->d != 32 && s->d != 64 && s->d != 128)
+        return fail(ZEROS_ERR_UNSUPPORTED, f + ": d must be 16, 32, 64 or 128");
+    if (s->d_u != s->d) return fail(ZEROS_ERR_UNSUPPORTED, f + ": d_u must equal d");
+    if (s->rope != 0 && s->rope != 1) return fail(ZEROS_ERR_UNSUPPORTED, f + ": rope must be 0 or 1");
+    if (s->rope == 1 && !(std::isfinite(s->rope_base) && s->rope_base > 1.0f))
+        return fail(ZEROS_ERR_SHAPE, f + ": rope_base must be finite and > 1");
+    const long double elems = static_cast<long double>(s->B) * s->H * s->N * s->d;
+    if (elems >= 2147483648.0L) return fail(ZEROS_ERR_SHAPE, f + ": tensor has 2^31 elements or more");
+    const size_t eb = elem_bytes(s->dtype);
+    const size_t tens = static_cast<size_t>(s->B) * s->H * s->N * s->d * eb;
+    const size_t gate = static_cast<size_t>(s->B) * s->H * s->N * eb;
+    const Range out{o, tens};
+    const Range ins[] = {{q, tens}, {k, tens}, {v, tens}, {u, tens}, {g1, gate}, {gh, gate},
+                         {mu, static_cast<size_t>(s->H) * s->d_u * 4}, {tau, static_cast<size_t>(s->H) * 4}};
+    for (const Range &r : ins)
+        if (overlap(out, r)) return fail(ZEROS_ERR_ALIAS, f + ": o overlaps an input");
+    return ZEROS_OK;
+}
+
+bool state_complete(const zeros_state *st) {
+    return st->F && st->G && st->Hs && st->Su && st->m && st->E && st->P && st->t;
+}
+
+// The state matrices are streamed with 16-byte accesses; the scalars need 4-byte alignment.
+bool state_aligned(const zeros_state *st) {
+    auto al = [](const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; };
+    return al(st->F, 16) && al(st->G, 16) && al(st->Hs, 16) && al(st->Su, 4) && al(st->m, 4) &&
+           al(st->E, 4) && al(st->P, 4) && al(st->t, 4);
+}
+
+zeros::Problem make_problem(const zeros_shape *s, const void *q, const void *k, const void *v,
+                            const void *u, const float *mu, const float *tau, const void *g1,
+                            const void *gh, void *o, const zeros_state *st) {
+    zeros::Problem p{};
+    p.q = q; p.k = k; p.v = v; p.u = u; p.mu = mu; p.tau = tau; p.g1 = g1; p.gh = gh; p.o = o;
+    if (st) p.st = *st;
+    p.B = s->B; p.H = s->H; p.N = s->N; p.d = s->d; p.du = s->d_u;
+    p.dtype = s->dtype; p.rope = s->rope; p.rope_base = s->rope_base;
+    return p;
+}
+
+zeros_status hip_result(hipError_t err, const char *fn) {
+    if (err != hipSuccess)
+        return fail(ZEROS_ERR_HIP, std::string(fn) + ": " + hipGetErrorName(err) + ": " + hipGetErrorString(err));
+    return ok();
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+}  // namespace
+
+extern "C" {
+
+zeros_status zeros_fwd_causal(const zeros_shape *shape, const void *q, const void *k, const void *v,
+                              const void *u, const float *mu, const float *tau, const void *g1,
+                              const void *gh, void *o, const zeros_state *state_out, void *stream) {
+    zeros_status st = check_common(shape, q, k, v, u, mu, tau, g1, gh, o, "zeros_fwd_causal");
+    if (st != ZEROS_OK) return st;
+    if (state_out && !state_complete(state_out))
+        return fail(ZEROS_ERR_NULL, "zeros_fwd_causal: a state_out field is NULL");
+    if (state_out && !state_aligned(state_out))
+        return fail(ZEROS_ERR_SHAPE, "zeros_fwd_causal: state_out matrices must be 16-byte aligned");
+    if (shape->N == 0 && !state_out) return ok();
+    const zeros::Problem p = make_problem(shape, q, k, v, u, mu, tau, g1, gh, o, state_out);
+    return hip_result(zeros::launch_causal_valu(p, static_cast<hipStream_t>(stream)), "zeros_fwd_causal");
+}
+
+zeros_status zeros_fwd_encoder(const zeros_shape *shape, const void *q, const void *k, const void *v,
+                               const void *u, const float *mu, const float *tau, const void *g1,
+                               const void *gh, void *o, void *stream) {
+    zeros_status st = check_common(shape, q, k, v, u, mu, tau, g1, gh, o, "zeros_fwd_encoder");
+    if (st != ZEROS_OK) return st;
+    if (shape->N == 0) return ok();
+    const zeros::Problem p = make_problem(shape, q, k, v, u, mu, tau, g1, gh, o, nullptr);
+    return hip_result(zeros::launch_encoder(p, static_cast<hipStream_t>(stream)), "zeros_fwd_encoder");
+}
+
+zeros_status zeros_decode_step(const zeros_shape *shape, const void *q, const void *k, const void *v,
+                               const void *u, const float *mu, const float *tau, const void *g1,
+                               const void *gh, void *o, const zeros_state *state, void *stream) {
+    zeros_status st = check_common(shape, q, k, v, u, mu, tau, g1, gh, o, "zeros_decode_step");
+    if (st != ZEROS_OK) return st;
+    if (shape->N != 1) return fail(ZEROS_ERR_SHAPE, "zeros_decode_step: N must be 1");
+    if (!state) return fail(ZEROS_ERR_NULL, "zeros_decode_step: state is NULL");
+    if (!state_complete(state)) return fail(ZEROS_ERR_NULL, "zeros_decode_step: a state field is NULL");
+    if (!state_aligned(state))
+        return fail(ZEROS_ERR_SHAPE, "zeros_decode_step: state matrices must be 16-byte aligned");
+    const zeros::Problem p = make_problem(shape, q, k, v, u, mu, tau, g1, gh, o, state);
+    return hip_result(zeros::launch_decode(p, static_cast<hipStream_t>(stream)), "zeros_decode_step");
+}
+
+size_t zeros_state_bytes(int32_t S, int32_t H, int32_t d, int32_t d_u) {
+    if (S < 1 || H < 1 || d < 1 || d_u < 1) return 0;
+    const long double heads = static_cast<long double>(S) * H;
+    if (heads * (3.0L * d * d + d_u + 4.0L) * 4.0L >= 9.0e18L) return 0;
+    const size_t n = static_cast<size_t>(S) * H;
+    const size_t mat = align256(n * d * d * 4);
+    return 3 * mat + align256(n * d_u * 4) + 4 * align256(n * 4);
+}
+
+zeros_status zeros_state_from_buffer(void *base, int32_t S, int32_t H, int32_t d, int32_t d_u,
+                                     zeros_state *out) {
+    if (!base || !out) return fail(ZEROS_ERR_NULL, "zeros_state_from_buffer: NULL argument");
+    if (zeros_state_bytes(S, H, d, d_u) == 0) return fail(ZEROS_ERR_SHAPE, "zeros_state_from_buffer: bad sizes");
+    const size_t n = static_cast<size_t>(S) * H;
+    const size_t mat = align256(n * d * d * 4), vec = align256(n * d_u * 4), sc = align256(n * 4);
+    char *b = static_cast<char *>(base);
+    out->F = reinterpret_cast<float *>(b);
+    out->G = reinterpret_cast<float *>(b + mat);
+    out->Hs = reinterpret_cast<float *>(b + 2 * mat);
+    out->Su = reinterpret_cast<float *>(b + 3 * mat);
+    out->m = reinterpret_cast<float *>(b + 3 * mat + vec);
+    out->E = reinterpret_cast<float *>(b + 3 * mat + vec + sc);
+    out->P = reinterpret_cast<float *>(b + 3 * mat + vec + 2 * sc);
+    out->t = reinterpret_cast<int32_t *>(b + 3 * mat + vec + 3 * sc);
+    return ok();
+}
+
+const char *zeros_status_str(int32_t status) {
+    switch (status) {
+        case ZEROS_OK: return "ZEROS_OK: success";
+        case ZEROS_ERR_NULL: return "ZEROS_ERR_NULL: a required pointer is NULL";
+        case ZEROS_ERR_SHAPE: return "ZEROS_ERR_SHAPE: invalid sizes";
+        case ZEROS_ERR_DTYPE: return "ZEROS_ERR_DTYPE: unknown dtype";
+        case ZEROS_ERR_UNSUPPORTED: return "ZEROS_ERR_UNSUPPORTED: valid but not implemented";
+        case ZEROS_ERR_HIP: return "ZEROS_ERR_HIP: HIP runtime error";
+        case ZEROS_ERR_ALIAS: return "ZEROS_ERR_ALIAS: output overlaps an input";
+        default: return "unknown zeros_status";
+    }
+}
+
+const char *zeros_last_error(void) { return g_last_error.c_str(); }
+
+int32_t zeros_abi_version(void) { return ZEROS_ABI_VERSION; }
+
+}  // extern "C"

@@ -33,6 +33,22 @@ SAMPLE_HEADS = [(0, 0), (1, 5), (0, 10), (1, 15)]
 _X = None                       # inputs shared with forked oracle workers
 
 
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "causal_B2H16N16384d128_rope_traffic.json")
+
+
+def measured_traffic():
+    """HBM bytes per call from the rocprofv3 FETCH_SIZE/WRITE_SIZE record, or None when the
+    kernel sources changed since those counters were taken."""
+    import hashlib
+
+    try:
+        rec = json.load(open(TRAFFIC_RECORD))
+        h = hashlib.sha256(b"".join(open(os.path.join(ROOT, s), "rb").read() for s in rec["sources"]))
+    except (OSError, ValueError, KeyError):
+        return None
+    return rec["hbm_bytes_per_call"] if h.hexdigest() == rec["sources_sha256"] else None
+
+
 def algorithmic_bytes(wl) -> int:
     """q, k, v, u and the two gates read once, o written once, mu and tau read once."""
     eb = 2 if wl.dtype == "bf16" else 4
@@ -70,13 +86,32 @@ def cpu_baseline(x):
     return info, {r[0]: r[1] for r in results}
 
 
+def copy_probe(mib: int) -> None:
+    """A plain copy of `mib` MiB between two device buffers: it reads and writes exactly that many
+    bytes, so FETCH_SIZE / WRITE_SIZE of its kernel calibrate the counter scale."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n * 4}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (calibrates the HBM "
+                         "traffic counters) and exit")
     args = ap.parse_args()
+    if args.copy_probe_mb:
+        copy_probe(args.copy_probe_mb)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the ZeroS heads shard across GPUs with no communication; see the design notes)",
@@ -140,8 +175,8 @@ def main():
                    "rope": wl.rope, "rope_base": wl.rope_base, "seed": wl.seed,
                    "accumulate": "f32", "states": "f32"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "causal_valu_kernel<128,bf16,rope>",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
+                     "kernel": "zeros_fwd_causal call: useg_sum_kernel + logits_kernel + causal_mfma_kernel<128,rope>",
                      "algorithmic_bytes_per_launch": nbytes,
                      "avg_kernel_ms": avg_kernel_ms,
                      "min_kernel_ms": float(np.min(kernel_ms))},

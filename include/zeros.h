@@ -32,6 +32,7 @@
  *   Errors:    the return value only; nothing throws or aborts. Arguments are validated on the
  *              host before any launch; a failed launch returns ZEROS_ERR_HIP. NaN/Inf in the
  *              inputs propagate to the outputs they influence and are not checked.
+ *   Alignment: q, k, v, u and o must be 16-byte aligned (ZEROS_ERR_SHAPE otherwise).
  *   Aliasing:  o must not overlap any input. Decode updates its state in place.
  *   Shapes:    d in {16, 32, 64, 128}, d_u == d, B, H >= 1, N >= 0 (N = 0 is a no-op),
  *              B*H*N*d < 2^31 elements per tensor; anything else is ZEROS_ERR_UNSUPPORTED or
@@ -90,13 +91,22 @@ typedef struct {
  * logits and the linear-time prefix scan; decoder mode per 损失函数 / 训练策略).
  * Inputs as in the conventions above; writes o [B, H, N, d].
  * state_out (nullable): receives the state after token N for every (b, h) (S = B); its
- * buffers must not overlap the inputs or o.
+ *   buffers must not overlap the inputs or o.
+ * workspace (nullable): device scratch of at least zeros_fwd_causal_workspace_bytes(shape)
+ *   bytes, 256-byte aligned, used only while the call's work runs on `stream` (it holds the
+ *   logits s_i and per-segment u sums). When NULL and scratch is needed, the library takes it
+ *   from the stream-ordered allocator (hipMallocAsync / hipFreeAsync on `stream`).
+ *   A workspace smaller than required is ZEROS_ERR_SHAPE.
  */
 zeros_status zeros_fwd_causal(const zeros_shape *shape,
                               const void *q, const void *k, const void *v, const void *u,
                               const float *mu, const float *tau,
                               const void *g1, const void *gh,
-                              void *o, const zeros_state *state_out, void *stream);
+                              void *o, const zeros_state *state_out,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/* Scratch bytes zeros_fwd_causal needs for `shape` (0 if none, or if shape is invalid). */
+size_t zeros_fwd_causal_workspace_bytes(const zeros_shape *shape);
 
 /*
  * Encoder (non-causal) forward (Paper-Notes 损失函数 / 训练策略: both modes are supported).

@@ -30,6 +30,7 @@ def declared_functions():
 def test_header_declares_entry_points():
     names = declared_functions()
     for n in ("zeros_fwd_causal", "zeros_fwd_encoder", "zeros_decode_step", "zeros_state_bytes",
+              "zeros_fwd_causal_workspace_bytes",
               "zeros_state_from_buffer", "zeros_status_str", "zeros_last_error", "zeros_abi_version"):
         assert n in names
 
@@ -68,7 +69,7 @@ def shape(B=1, H=2, N=8, d=16, d_u=16, dtype=0, rope=0, base=10000.0):
 def call_causal(lib, shp, ptrs=None, state=None):
     p = dict(P, **(ptrs or {}))
     return lib.zeros_fwd_causal(ctypes.byref(shp) if shp is not None else None, p["q"], p["k"], p["v"],
-                                p["u"], p["mu"], p["tau"], p["g1"], p["gh"], p["o"], state, None)
+                                p["u"], p["mu"], p["tau"], p["g1"], p["gh"], p["o"], state, None, 0, None)
 
 
 def call_encoder(lib, shp, ptrs=None):
@@ -119,6 +120,30 @@ def test_output_alias(lib):
     # o starts inside q's byte range: [B,H,N,d] = 1*2*8*16 f32 = 1024 bytes
     assert call_causal(lib, shape(), {"o": P["q"] + 512}) == L.ZEROS_ERR_ALIAS
     assert call_encoder(lib, shape(), {"o": P["gh"]}) == L.ZEROS_ERR_ALIAS
+
+
+def test_misaligned_tensors_rejected(lib):
+    assert call_causal(lib, shape(), {"q": P["q"] + 2}) == L.ZEROS_ERR_SHAPE
+    assert call_encoder(lib, shape(), {"o": P["o"] + 8}) == L.ZEROS_ERR_SHAPE
+
+
+def test_workspace_size_and_validation(lib):
+    bf = shape(B=2, H=16, N=16384, d=128, d_u=128, dtype=1)
+    n = lib.zeros_fwd_causal_workspace_bytes(ctypes.byref(bf))
+    logits = 2 * 16 * 16384 * 4
+    useg = 2 * 16 * (16384 // 512) * 128 * 4
+    assert n == logits + useg
+    assert lib.zeros_fwd_causal_workspace_bytes(ctypes.byref(shape(dtype=0))) == 0   # f32 path: none
+    assert lib.zeros_fwd_causal_workspace_bytes(None) == 0
+    small = shape(B=1, H=2, N=8, d=64, d_u=64, dtype=1)
+    need = lib.zeros_fwd_causal_workspace_bytes(ctypes.byref(small))
+    p = dict(P)
+    r = lib.zeros_fwd_causal(ctypes.byref(small), p["q"], p["k"], p["v"], p["u"], p["mu"], p["tau"], p["g1"],
+                             p["gh"], p["o"], None, 0x7000000, need - 1, None)
+    assert r == L.ZEROS_ERR_SHAPE
+    r = lib.zeros_fwd_causal(ctypes.byref(small), p["q"], p["k"], p["v"], p["u"], p["mu"], p["tau"], p["g1"],
+                             p["gh"], p["o"], None, 0x7000010, need, None)
+    assert r == L.ZEROS_ERR_SHAPE                                                       # misaligned
 
 
 def test_partial_state_rejected(lib):

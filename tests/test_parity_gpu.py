@@ -111,6 +111,50 @@ def test_causal_shapes(d, N, dtype, rope):
         assert rel_l2(o, ref) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [64, 65, 129, 300, 1000])
+@pytest.mark.parametrize("rope", [False, True])
+def test_causal_mfma_chunks(d, N, rope):
+    """bfloat16 d in {64, 128} runs on the matrix-core path: several 64-token chunks, ragged tails."""
+    wl = CONFIGS[4].with_(B=2, H=2, N=N, d=d, d_u=d, seed=3000 + d + N)
+    x = make_inputs(wl)
+    o = to_f64(run_causal(x, "bf16", rope=rope))
+    ref = R.causal_forward(**x, rope=rope)
+    err = rel_l2(o, ref)
+    print(f"mfma d={d} N={N} rope={rope} rel_l2={err:.3e}", flush=True)
+    assert err <= TOL["bf16"]
+    assert np.max(np.abs(o[..., 0, :])) <= 1e-3
+
+
+@pytest.mark.parametrize("rope", [False, True])
+def test_causal_mfma_state_out(rope):
+    wl = CONFIGS[4].with_(B=2, H=2, N=333, seed=3100)
+    x = make_inputs(wl)
+    st = Z.DecodeState(2, 2, 128, 128).reset()
+    run_causal(x, "bf16", rope=rope, state_out=st)
+    _, ref = R.causal_forward(**x, rope=rope, return_state=True)
+    got = _state_np(st)
+    assert np.all(got["t"] == 333)
+    for key in ("m", "E", "P", "Su"):
+        assert rel_l2(got[key], ref[key]) <= 1e-5, key
+    for key in ("F", "G", "H"):
+        assert rel_l2(got[key], ref[key]) <= 2e-2, key
+
+
+def test_causal_workspace_reuse():
+    wl = CONFIGS[4].with_(B=1, H=3, N=700, seed=3200)
+    x = make_inputs(wl)
+    t = to_device(x, "bf16")
+    n = Z.zeros_fwd_causal_workspace_bytes(1, 3, 700, 128, 128, torch.bfloat16)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    args = [t[k] for k in ("q", "k", "v", "u", "mu", "tau", "g1", "gh")]
+    o1 = Z.zeros_fwd_causal(*args, rope=True, workspace=ws)
+    o2 = Z.zeros_fwd_causal(*args, rope=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert rel_l2(to_f64(o1), R.causal_forward(**x, rope=True)) <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("d", [16, 64, 128])
 @pytest.mark.parametrize("N", [1, 2, 47, 197])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -255,7 +299,7 @@ def test_config5_decode_full_size():
         _, ref = R.causal_forward(px["q"], px["k"], px["v"], px["u"], step["mu"][h], step["tau"][h],
                                   px["g1"], px["gh"], return_state=True)
         for key, gk in (("F", st.F), ("G", st.G), ("H", st.Hs)):
-            assert rel_l2(to_f64(gk[s, h]), ref[key]) <= 1e-3, (s, h, key)
+            assert rel_l2(to_f64(gk[s, h]), ref[key]) <= TOL["bf16"], (s, h, key)
         assert abs(float(st.m[s, h]) - ref["m"]) <= 1e-4
         assert rel_l2(to_f64(st.Su[s, h]), ref["Su"]) <= 1e-4
     # (a) one step from the identical state

@@ -52,8 +52,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     vp, i32, f32p = ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p
     fwd = [ctypes.POINTER(zeros_shape), vp, vp, vp, vp, f32p, f32p, vp, vp, vp]
-    lib.zeros_fwd_causal.argtypes = fwd + [ctypes.POINTER(zeros_state), vp]
+    lib.zeros_fwd_causal.argtypes = fwd + [ctypes.POINTER(zeros_state), vp, ctypes.c_size_t, vp]
     lib.zeros_fwd_causal.restype = i32
+    lib.zeros_fwd_causal_workspace_bytes.argtypes = [ctypes.POINTER(zeros_shape)]
+    lib.zeros_fwd_causal_workspace_bytes.restype = ctypes.c_size_t
     lib.zeros_fwd_encoder.argtypes = fwd + [vp]
     lib.zeros_fwd_encoder.restype = i32
     lib.zeros_decode_step.argtypes = fwd + [ctypes.POINTER(zeros_state), vp]
@@ -171,8 +173,11 @@ class DecodeState:
 
 def zeros_fwd_causal(q, k, v, u, mu, tau, g1, gh, *, rope: bool = False, rope_base: float = 10000.0,
                      out: torch.Tensor | None = None, state_out: DecodeState | None = None,
-                     stream=None) -> torch.Tensor:
-    """Causal forward over q, k, v [B, H, N, d], u [B, H, N, d_u], g1, gh [B, H, N]."""
+                     workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Causal forward over q, k, v [B, H, N, d], u [B, H, N, d_u], g1, gh [B, H, N].
+
+    ``workspace`` (optional uint8 tensor) is reused scratch; without it one is allocated per call
+    when the path needs it (see zeros_fwd_causal_workspace_bytes)."""
     _check_tensors(q, k, v, u, mu, tau, g1, gh, 1)
     o = torch.empty_like(v) if out is None else out
     _need(o.shape == v.shape and o.dtype == v.dtype and o.is_contiguous() and o.device == q.device,
@@ -183,10 +188,24 @@ def zeros_fwd_causal(q, k, v, u, mu, tau, g1, gh, *, rope: bool = False, rope_ba
     lib = load_library()
     shp = _shape(q, u, q.shape[2], rope, rope_base)
     st = ctypes.byref(state_out.c) if state_out is not None else None
+    nws = lib.zeros_fwd_causal_workspace_bytes(ctypes.byref(shp))
+    if workspace is None and nws > 0:
+        workspace = torch.empty(nws, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _need(workspace.dtype == torch.uint8 and workspace.device == q.device and workspace.is_contiguous(),
+              "workspace must be a contiguous uint8 tensor on q's device")
     _check(lib.zeros_fwd_causal(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(u), _ptr(mu),
                                 _ptr(tau), _ptr(g1), _ptr(gh), _ptr(o), st,
+                                _ptr(workspace), 0 if workspace is None else workspace.numel(),
                                 _stream(q.device, stream)))
     return o
+
+
+def zeros_fwd_causal_workspace_bytes(B: int, H: int, N: int, d: int, d_u: int, dtype, rope: bool = False) -> int:
+    """Scratch bytes zeros_fwd_causal needs for these sizes (0 when the path needs none)."""
+    lib = load_library()
+    shp = zeros_shape(B, H, N, d, d_u, _DT[dtype], 1 if rope else 0, 10000.0)
+    return int(lib.zeros_fwd_causal_workspace_bytes(ctypes.byref(shp)))
 
 
 def zeros_fwd_encoder(q, k, v, u, mu, tau, g1, gh, *, rope: bool = False, rope_base: float = 10000.0,

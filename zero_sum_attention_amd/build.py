@@ -22,6 +22,8 @@ ARCH = "gfx950"
 SOURCES = [
     "zeros_api.cpp",
     "causal_valu.hip",
+    "causal_mfma.hip",
+    "logits.hip",
     "encoder_valu.hip",
     "decode.hip",
 ]

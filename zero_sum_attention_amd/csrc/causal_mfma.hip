@@ -1,0 +1,546 @@
+// Causal ZeroS forward on the matrix cores: bfloat16 q/k/v with float32 states, d in {64, 128}.
+//
+// Method: Paper-Notes page "ZeroS: Zero-Sum Linear Attention for Efficient Transformers", 关键设计
+// (zero-sum weights w_{t,i} = alpha_t e^{s_i} + beta_t s_i + gamma_t after expanding the gated
+// first-order and residual terms; angular factor q^_t . k^_i with RoPE as a relative rotation;
+// the prefix states of the linear-time scan). The logits s_i come from logits.hip.
+//
+// Work split: one workgroup (4 waves) per (batch, head, 16-column tile of v/o); the 8 (d = 128)
+// tiles of a head are mapped onto one XCD so they share q/k through its L2. The sequence is
+// walked in chunks of kC = 64 tokens; wave w owns queries [16w, 16w+16) of the chunk and state
+// rows [w d/4, (w+1) d/4). Per chunk (t0, t1]:
+//   intra:  A^T = K Q^T (MFMA), W_{t,i} = A (q^,k^ norms folded in) (a_t e^{s_i-m_t} + b_t s_i + g_t)
+//           for i <= t, o^T += V^T W^T (MFMA; W stays in registers: its accumulator layout is the
+//           B-operand layout up to a permutation of the contraction index, mirrored in V^T).
+//   inter:  o_t += q^_t (cX_t X + b_t Y + kappa_t H) with the states at t0 (MFMA).
+//   update: X, Y, H advanced to t1 (elementwise rescale, then K^T V' on MFMA).
+// States are kept in a centred basis, X = F/E - H/t0 and Y = G - (P/t0) H. Both have zero-sum
+// weights, so they stay of the size of the output, and rounding them (and the update operands)
+// to bfloat16 for the MFMA is not amplified by the cancellation between alpha F, beta G and
+// gamma H. With RoPE, q and k are rotated by their offset inside the chunk and the states are
+// kept in the frame of the chunk start, re-based by a fixed rotation after every chunk.
+#include <hip/hip_bf16.h>
+
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace zeros {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+constexpr int kC = 64;          // tokens per chunk
+constexpr int kThreads = 256;   // 4 waves
+constexpr int kTile = 16;       // value columns per workgroup
+constexpr int kPad = 8;         // bf16 elements of row padding in LDS
+
+__device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    __hip_bfloat162 h = __float22bfloat162_rn(make_float2(lo, hi));
+    return *reinterpret_cast<uint32_t *>(&h);
+}
+__device__ __forceinline__ float lo_f(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_f(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    bf16x8 r;
+    r[0] = static_cast<short>(a & 0xffff); r[1] = static_cast<short>(a >> 16);
+    r[2] = static_cast<short>(b & 0xffff); r[3] = static_cast<short>(b >> 16);
+    r[4] = static_cast<short>(c & 0xffff); r[5] = static_cast<short>(c >> 16);
+    r[6] = static_cast<short>(d & 0xffff); r[7] = static_cast<short>(d >> 16);
+    return r;
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, float acc) {
+    typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+    const bf16x2v v = *reinterpret_cast<const bf16x2v *>(&a);
+    return __builtin_amdgcn_fdot2_f32_bf16(v, v, acc, false);
+}
+
+// Per-chunk coefficients, produced one chunk ahead by wave 0 (double-buffered).
+struct Coef {
+    float qa[kC], qm[kC], qb[kC], qg[kC], qcx[kC], qkap[kC];   // per query t
+    float wx[kC], wy[kC], s[kC];                                // per key i (w without 1/|k|)
+    float chunk[8];                                             // m1, E1, P1, rX, cHX, cHY
+};
+
+template <int D>
+struct alignas(16) MSmem {
+    alignas(16) uint16_t qh[kC][D + kPad];     // raw (rotated) q rows of the chunk, bf16
+    alignas(16) uint16_t kh[kC][D + kPad];     // raw (rotated) k rows
+    alignas(16) uint16_t vt[kTile][kC + kPad]; // v tile, transposed: vt[m][token]
+    alignas(16) uint16_t vx[kTile][kC + kPad]; // update operands: v * w_X / |k|, v * w_Y / |k|,
+    alignas(16) uint16_t vy[kTile][kC + kPad]; //   v / |k| (transposed like vt)
+    alignas(16) uint16_t vh[kTile][kC + kPad];
+    alignas(16) uint16_t st[3][kTile][D + kPad];  // X, Y, H transposed: st[s][m][j], bf16
+    alignas(16) float2 kinfo[kC];              // (s_i, 1/|k_i|)
+    float invq[kC];
+    Coef cf[2];
+};
+
+// (max, sum e^{s-max}) combine of two partial scans; a max of -inf marks an empty part.
+__device__ __forceinline__ void lse_combine(float &m, float &e, float m2, float e2) {
+    if (m2 == kNegInf) return;
+    if (m == kNegInf) { m = m2; e = e2; return; }
+    if (m >= m2) {
+        e += e2 * __expf(m2 - m);
+    } else {
+        e = e * __expf(m - m2) + e2;
+        m = m2;
+    }
+}
+
+// Scalar scan of one chunk (wave 0, lane r = token t0 + r + 1) and its coefficients.
+// Inputs: the chunk's logits and gate pre-activations in lanes; the carry (m0, E0, P0) at t0,
+// updated to the chunk end on return.
+__device__ __forceinline__ void chunk_scan(Coef &cf, int lane, int t0, int nval, float sr_in, float g1v,
+                                           float ghv, float &m0, float &E0, float &P0) {
+    const int r = lane;
+    const bool valid = r < nval;
+    const float t0f = static_cast<float>(t0);
+    const float sr = valid ? sr_in : 0.f;
+    float m = valid ? sr : kNegInf, e = valid ? 1.f : 0.f, pp = valid ? sr : 0.f;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float m2 = __shfl_up(m, off, 64);
+        const float e2 = __shfl_up(e, off, 64);
+        const float p2 = __shfl_up(pp, off, 64);
+        if (r >= off) {
+            lse_combine(m, e, m2, e2);
+            pp += p2;
+        }
+    }
+    const float M = fmaxf(m0, m);
+    const float E0p = (m0 == kNegInf) ? 0.f : E0 * __expf(m0 - M);   // earlier tokens, relative to m_t
+    const float dE = (m == kNegInf) ? 0.f : e * __expf(m - M);      // this chunk up to t
+    const float Et = E0p + dE;
+    const float Pt = P0 + pp;
+    const float s1 = __fdividef(1.f, 1.f + __expf(-g1v));
+    const float sh = __fdividef(1.f, 1.f + __expf(-ghv));
+    if (valid) {
+        const float tt = t0f + static_cast<float>(r + 1);
+        const float itt = __fdividef(1.f, tt);
+        const float d1 = s1 - sh;
+        const float a = __fdividef(sh, Et);
+        cf.qa[r] = a;
+        cf.qm[r] = M;
+        cf.qb[r] = d1 * itt;
+        cf.qg[r] = -d1 * (Pt * itt) * itt - sh * itt;
+        if (t0 > 0) {
+            const float dt = tt - t0f;
+            cf.qcx[r] = a * E0p;
+            cf.qkap[r] = sh * __fdividef(E0p * dt - t0f * dE, Et * tt * t0f) +
+                         d1 * __fdividef(P0 * dt - t0f * pp, tt * tt * t0f);
+        } else {
+            cf.qcx[r] = 0.f;
+            cf.qkap[r] = 0.f;
+        }
+    }
+    const int last = nval - 1;
+    const float M1 = __shfl(M, last, 64), E1 = __shfl(Et, last, 64), P1 = __shfl(Pt, last, 64);
+    const float dE1 = __shfl(dE, last, 64), dP1 = __shfl(pp, last, 64), E0p1 = __shfl(E0p, last, 64);
+    const float t1 = t0f + static_cast<float>(nval);
+    cf.wx[r] = valid ? __fdividef(__expf(sr - M1), E1) - __fdividef(1.f, t1) : 0.f;
+    cf.wy[r] = valid ? sr - __fdividef(P1, t1) : 0.f;
+    cf.s[r] = sr;
+    if (r == 0) {
+        cf.chunk[0] = M1;
+        cf.chunk[1] = E1;
+        cf.chunk[2] = P1;
+        if (t0 > 0) {
+            cf.chunk[3] = __fdividef(E0p1, E1);
+            cf.chunk[4] = __fdividef(E0p1 * (t1 - t0f) - t0f * dE1, E1 * t0f * t1);
+            cf.chunk[5] = __fdividef(P0 * (t1 - t0f) - t0f * dP1, t0f * t1);
+        } else {
+            cf.chunk[3] = cf.chunk[4] = cf.chunk[5] = 0.f;
+        }
+    }
+    m0 = M1;
+    E0 = E1;
+    P0 = P1;
+}
+
+template <int D, bool ROPE>
+__global__ __launch_bounds__(kThreads) void causal_mfma_kernel(Problem p, CausalWork work) {
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    MSmem<D> &sm = *reinterpret_cast<MSmem<D> *>(smem_raw);
+    constexpr int NTILE = D / kTile;
+    constexpr int KS = D / 32;          // MFMA k-steps over the feature dimension
+    constexpr int RT = D / 64;          // 16-row state tiles per wave
+    constexpr int QW = D / 4;           // features per thread in the load phase
+    constexpr int NV = QW / 8;          // 16-byte vectors per thread per row slice
+    constexpr int NP = QW / 2;          // rotation pairs per thread
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, g4 = lane >> 4;
+
+    const int G = gridDim.x;
+    int L = blockIdx.x;
+    if ((G & 7) == 0) L = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+    const int tile = L % NTILE;
+    const int bh = L / NTILE;
+    const int N = p.N;
+    const size_t row0 = static_cast<size_t>(bh) * N;
+    const uint16_t *qg = static_cast<const uint16_t *>(p.q) + row0 * D;
+    const uint16_t *kg = static_cast<const uint16_t *>(p.k) + row0 * D;
+    const uint16_t *vg = static_cast<const uint16_t *>(p.v) + row0 * D;
+    const uint16_t *g1g = static_cast<const uint16_t *>(p.g1) + row0;
+    const uint16_t *ghg = static_cast<const uint16_t *>(p.gh) + row0;
+    const float *slog = work.s + row0;
+    uint16_t *og = static_cast<uint16_t *>(p.o) + row0 * D;
+
+    // load-phase coordinates: row lr of the chunk, features [f0, f0 + QW)
+    const int lr = tid >> 2, f0 = (tid & 3) * QW;
+
+    // rotation of this thread's pairs by its offset lr inside the chunk
+    float rc[ROPE ? NP : 1], rs[ROPE ? NP : 1];
+    // rotation re-basing the state rows of this lane by -kC after each chunk
+    float fc[ROPE ? 2 * RT : 1], fs[ROPE ? 2 * RT : 1];
+    if (ROPE) {
+#pragma unroll
+        for (int a = 0; a < NP; ++a)
+            rope_cos_sin(rope_rev_per_pos(f0 / 2 + a, D, p.rope_base), lr, rc[a], rs[a]);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+                const int jp = 8 * (RT * wave + rt) + 2 * g4 + pp;
+                rope_cos_sin(rope_rev_per_pos(jp, D, p.rope_base), kC, fc[2 * rt + pp], fs[2 * rt + pp]);
+            }
+    }
+
+    f32x4 X[RT], Y[RT], Hm[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) X[rt][i] = Y[rt][i] = Hm[rt][i] = 0.f;
+    float m0 = kNegInf, E0 = 0.f, P0 = 0.f;    // scan carry (kept by wave 0)
+
+    // prefetch registers
+    uint4 pq[NV], pk[NV];
+    uint2 pv;
+    float ps = 0.f, pg1 = 0.f, pgh = 0.f;
+    auto load_chunk = [&](int tc) {
+        const bool valid = tc + lr < N;
+        const size_t base = static_cast<size_t>(tc + lr) * D + f0;
+#pragma unroll
+        for (int a = 0; a < NV; ++a) {
+            pq[a] = valid ? *reinterpret_cast<const uint4 *>(qg + base + 8 * a) : make_uint4(0, 0, 0, 0);
+            pk[a] = valid ? *reinterpret_cast<const uint4 *>(kg + base + 8 * a) : make_uint4(0, 0, 0, 0);
+        }
+        pv = valid ? *reinterpret_cast<const uint2 *>(vg + static_cast<size_t>(tc + lr) * D + tile * kTile +
+                                                      4 * (tid & 3))
+                   : make_uint2(0, 0);
+        if (tid < kC) {
+            const bool vs = tc + tid < N;
+            ps = vs ? slog[tc + tid] : 0.f;
+            pg1 = vs ? lo_f(g1g[tc + tid]) : 0.f;
+            pgh = vs ? lo_f(ghg[tc + tid]) : 0.f;
+        }
+    };
+    if (N > 0) {
+        load_chunk(0);
+        if (wave == 0) chunk_scan(sm.cf[0], lane, 0, min(kC, N), ps, pg1, pgh, m0, E0, P0);
+    }
+    __syncthreads();
+
+    for (int t0 = 0, ci = 0; t0 < N; t0 += kC, ++ci) {
+        const int nval = min(kC, N - t0);
+        const Coef &cf = sm.cf[ci & 1];
+
+        // ---- registers -> LDS: norms, rotation, v operands, per-key data
+        {
+            float ssq = 0.f, ssk = 0.f;
+#pragma unroll
+            for (int a = 0; a < NV; ++a) {
+                ssq = dot2_bf16(pq[a].x, ssq); ssq = dot2_bf16(pq[a].y, ssq);
+                ssq = dot2_bf16(pq[a].z, ssq); ssq = dot2_bf16(pq[a].w, ssq);
+                ssk = dot2_bf16(pk[a].x, ssk); ssk = dot2_bf16(pk[a].y, ssk);
+                ssk = dot2_bf16(pk[a].z, ssk); ssk = dot2_bf16(pk[a].w, ssk);
+            }
+            ssq = group_sum<4>(ssq);
+            ssk = group_sum<4>(ssk);
+            const bool valid = lr < nval;
+            const float iq = valid ? __frsqrt_rn(fmaxf(ssq, 1e-24f)) : 0.f;
+            const float ik = valid ? __frsqrt_rn(fmaxf(ssk, 1e-24f)) : 0.f;
+            if ((tid & 3) == 0) {
+                sm.invq[lr] = iq;
+                sm.kinfo[lr] = make_float2(cf.s[lr], ik);
+            }
+            if (ROPE) {
+#pragma unroll
+                for (int a = 0; a < NV; ++a) {
+                    uint32_t wq[4] = {pq[a].x, pq[a].y, pq[a].z, pq[a].w};
+                    uint32_t wk[4] = {pk[a].x, pk[a].y, pk[a].z, pk[a].w};
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        const float c = rc[4 * a + b], sn = rs[4 * a + b];
+                        const float q0 = lo_f(wq[b]), q1 = hi_f(wq[b]);
+                        const float k0 = lo_f(wk[b]), k1 = hi_f(wk[b]);
+                        wq[b] = pack2(q0 * c - q1 * sn, q0 * sn + q1 * c);
+                        wk[b] = pack2(k0 * c - k1 * sn, k0 * sn + k1 * c);
+                    }
+                    pq[a] = make_uint4(wq[0], wq[1], wq[2], wq[3]);
+                    pk[a] = make_uint4(wk[0], wk[1], wk[2], wk[3]);
+                }
+            }
+#pragma unroll
+            for (int a = 0; a < NV; ++a) {
+                *reinterpret_cast<uint4 *>(&sm.qh[lr][f0 + 8 * a]) = pq[a];
+                *reinterpret_cast<uint4 *>(&sm.kh[lr][f0 + 8 * a]) = pk[a];
+            }
+            const int mc = 4 * (tid & 3);
+            const float vv[4] = {lo_f(pv.x), hi_f(pv.x), lo_f(pv.y), hi_f(pv.y)};
+            const float wxk = cf.wx[lr] * ik, wyk = cf.wy[lr] * ik;
+            const uint32_t px0 = pack2(vv[0] * wxk, vv[1] * wxk), px1 = pack2(vv[2] * wxk, vv[3] * wxk);
+            const uint32_t py0 = pack2(vv[0] * wyk, vv[1] * wyk), py1 = pack2(vv[2] * wyk, vv[3] * wyk);
+            const uint32_t ph0 = pack2(vv[0] * ik, vv[1] * ik), ph1 = pack2(vv[2] * ik, vv[3] * ik);
+            const uint32_t pvw[2] = {pv.x, pv.y}, pxw[2] = {px0, px1}, pyw[2] = {py0, py1}, phw[2] = {ph0, ph1};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int sh = 16 * (c & 1);
+                sm.vt[mc + c][lr] = static_cast<uint16_t>(pvw[c >> 1] >> sh);
+                sm.vx[mc + c][lr] = static_cast<uint16_t>(pxw[c >> 1] >> sh);
+                sm.vy[mc + c][lr] = static_cast<uint16_t>(pyw[c >> 1] >> sh);
+                sm.vh[mc + c][lr] = static_cast<uint16_t>(phw[c >> 1] >> sh);
+            }
+        }
+        __syncthreads();
+        if (t0 + kC < N) load_chunk(t0 + kC);
+
+        // ---- A^T tiles for this wave's query block
+        const int tb = wave;
+        bf16x8 qop[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qop[ks] = *reinterpret_cast<const bf16x8 *>(&sm.qh[16 * tb + l16][32 * ks + 8 * g4]);
+        f32x4 at[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) at[kb][i] = 0.f;
+            if (kb <= tb) {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&sm.kh[16 * kb + l16][32 * ks + 8 * g4]);
+                    at[kb] = mfma(a, qop[ks], at[kb]);
+                }
+            }
+        }
+
+        // ---- intra-chunk weights and o^T = V^T W^T
+        const int tq = 16 * tb + l16;
+        const float iq = sm.invq[tq], qa = cf.qa[tq], qm = cf.qm[tq], qb = cf.qb[tq], qgm = cf.qg[tq];
+        f32x4 oacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int pi = 0; pi < 2; ++pi) {
+            if (2 * pi > tb) continue;
+            uint32_t wv[4] = {0u, 0u, 0u, 0u};
+            uint2 va[2] = {make_uint2(0, 0), make_uint2(0, 0)};
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const int kb = 2 * pi + h2;
+                if (kb > tb) continue;
+                const float4 ka = *reinterpret_cast<const float4 *>(&sm.kinfo[16 * kb + 4 * g4]);
+                const float4 kb4 = *reinterpret_cast<const float4 *>(&sm.kinfo[16 * kb + 4 * g4 + 2]);
+                const float ks_[4] = {ka.x, ka.z, kb4.x, kb4.z};
+                const float ki_[4] = {ka.y, ka.w, kb4.y, kb4.w};
+                float w[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int key = 16 * kb + 4 * g4 + i;
+                    const float sk = ks_[i];
+                    const float x = at[kb][i] * iq * ki_[i] * (qa * __expf(sk - qm) + qb * sk + qgm);
+                    w[i] = (key <= tq && tq < nval) ? x : 0.f;
+                }
+                wv[2 * h2] = pack2(w[0], w[1]);
+                wv[2 * h2 + 1] = pack2(w[2], w[3]);
+                va[h2] = *reinterpret_cast<const uint2 *>(&sm.vt[l16][16 * kb + 4 * g4]);
+            }
+            oacc = mfma(as_bf16x8(va[0].x, va[0].y, va[1].x, va[1].y), as_bf16x8(wv[0], wv[1], wv[2], wv[3]), oacc);
+        }
+
+        // ---- carried states
+        if (t0 > 0) {
+            f32x4 ax = {0.f, 0.f, 0.f, 0.f}, ay = ax, ah = ax;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                ax = mfma(*reinterpret_cast<const bf16x8 *>(&sm.st[0][l16][32 * ks + 8 * g4]), qop[ks], ax);
+                ay = mfma(*reinterpret_cast<const bf16x8 *>(&sm.st[1][l16][32 * ks + 8 * g4]), qop[ks], ay);
+                ah = mfma(*reinterpret_cast<const bf16x8 *>(&sm.st[2][l16][32 * ks + 8 * g4]), qop[ks], ah);
+            }
+            const float cx = cf.qcx[tq], kap = cf.qkap[tq];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) oacc[i] += iq * (cx * ax[i] + qb * ay[i] + kap * ah[i]);
+        }
+        if (tq < nval) {
+            const uint2 ov = make_uint2(pack2(oacc[0], oacc[1]), pack2(oacc[2], oacc[3]));
+            *reinterpret_cast<uint2 *>(og + static_cast<size_t>(t0 + tq) * D + tile * kTile + 4 * g4) = ov;
+        }
+
+        // ---- advance the states to t1
+        if (t0 > 0) {
+            const float rX = cf.chunk[3], cHX = cf.chunk[4], cHY = cf.chunk[5];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    X[rt][i] = rX * X[rt][i] + cHX * Hm[rt][i];
+                    Y[rt][i] = Y[rt][i] + cHY * Hm[rt][i];
+                }
+        }
+#pragma unroll
+        for (int ks2 = 0; ks2 < kC / 32; ++ks2) {
+            const int kk0 = 32 * ks2 + 8 * g4;
+            const bf16x8 BX = *reinterpret_cast<const bf16x8 *>(&sm.vx[l16][kk0]);
+            const bf16x8 BY = *reinterpret_cast<const bf16x8 *>(&sm.vy[l16][kk0]);
+            const bf16x8 BH = *reinterpret_cast<const bf16x8 *>(&sm.vh[l16][kk0]);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const int j = 16 * (RT * wave + rt) + l16;
+                bf16x8 a;
+#pragma unroll
+                for (int c = 0; c < 8; ++c) a[c] = static_cast<short>(sm.kh[kk0 + c][j]);
+                X[rt] = mfma(a, BX, X[rt]);
+                Y[rt] = mfma(a, BY, Y[rt]);
+                Hm[rt] = mfma(a, BH, Hm[rt]);
+            }
+        }
+        if (ROPE) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int pp = 0; pp < 2; ++pp) {
+                    const float c = fc[2 * rt + pp], sn = fs[2 * rt + pp];
+                    const int i0 = 2 * pp, i1 = i0 + 1;
+                    float x0 = X[rt][i0], x1 = X[rt][i1];
+                    X[rt][i0] = x0 * c + x1 * sn; X[rt][i1] = x1 * c - x0 * sn;
+                    x0 = Y[rt][i0]; x1 = Y[rt][i1];
+                    Y[rt][i0] = x0 * c + x1 * sn; Y[rt][i1] = x1 * c - x0 * sn;
+                    x0 = Hm[rt][i0]; x1 = Hm[rt][i1];
+                    Hm[rt][i0] = x0 * c + x1 * sn; Hm[rt][i1] = x1 * c - x0 * sn;
+                }
+        }
+        // ---- coefficients of the next chunk (wave 0; its logits and gates are in the prefetch)
+        if (wave == 0 && t0 + kC < N)
+            chunk_scan(sm.cf[(ci + 1) & 1], lane, t0 + kC, min(kC, N - t0 - kC), ps, pg1, pgh, m0, E0, P0);
+        __syncthreads();          // every wave is done with st, kh, v operands and this chunk's coefficients
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const int jc = 16 * (RT * wave + rt) + 4 * g4;
+            *reinterpret_cast<uint2 *>(&sm.st[0][l16][jc]) = make_uint2(pack2(X[rt][0], X[rt][1]), pack2(X[rt][2], X[rt][3]));
+            *reinterpret_cast<uint2 *>(&sm.st[1][l16][jc]) = make_uint2(pack2(Y[rt][0], Y[rt][1]), pack2(Y[rt][2], Y[rt][3]));
+            *reinterpret_cast<uint2 *>(&sm.st[2][l16][jc]) = make_uint2(pack2(Hm[rt][0], Hm[rt][1]), pack2(Hm[rt][2], Hm[rt][3]));
+        }
+    }
+
+    // ---- final state: back to F = E (X + H/t), G = Y + (P/t) H in the absolute RoPE frame
+    if (p.st.F != nullptr) {
+        // wave 0 holds the carry at t = N; the final chunk's coefficients hold the same values
+        if (N > 0) {
+            const Coef &cl = sm.cf[((N + kC - 1) / kC - 1) & 1];
+            m0 = cl.chunk[0];
+            E0 = cl.chunk[1];
+            P0 = cl.chunk[2];
+        }
+        const size_t mat0 = static_cast<size_t>(bh) * D * D;
+        const float tf = static_cast<float>(N);
+        const int nchunks = (N + kC - 1) / kC;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            float F[4], Gv[4], Hv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float hh = Hm[rt][i];
+                F[i] = N > 0 ? E0 * (X[rt][i] + hh / tf) : 0.f;
+                Gv[i] = N > 0 ? Y[rt][i] + (P0 / tf) * hh : 0.f;
+                Hv[i] = hh;
+            }
+            if (ROPE && N > 0) {
+#pragma unroll
+                for (int pp = 0; pp < 2; ++pp) {
+                    const int jp = 8 * (RT * wave + rt) + 2 * g4 + pp;
+                    float c, s;
+                    rope_cos_sin(rope_rev_per_pos(jp, D, p.rope_base), nchunks * kC, c, s);
+                    const int i0 = 2 * pp, i1 = i0 + 1;
+                    float x0 = F[i0], x1 = F[i1];
+                    F[i0] = x0 * c - x1 * s; F[i1] = x0 * s + x1 * c;
+                    x0 = Gv[i0]; x1 = Gv[i1];
+                    Gv[i0] = x0 * c - x1 * s; Gv[i1] = x0 * s + x1 * c;
+                    x0 = Hv[i0]; x1 = Hv[i1];
+                    Hv[i0] = x0 * c - x1 * s; Hv[i1] = x0 * s + x1 * c;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int j = 16 * (RT * wave + rt) + 4 * g4 + i;
+                const size_t idx = mat0 + static_cast<size_t>(j) * D + tile * kTile + l16;
+                p.st.F[idx] = F[i];
+                p.st.G[idx] = Gv[i];
+                p.st.Hs[idx] = Hv[i];
+            }
+        }
+        if (tile == 0) {
+            const int nseg = (N + kLogitSeg - 1) / kLogitSeg;
+            if (tid < D) {
+                float su = 0.f;
+                for (int sg = 0; sg < nseg; ++sg) su += work.useg[(static_cast<size_t>(bh) * nseg + sg) * D + tid];
+                p.st.Su[static_cast<size_t>(bh) * D + tid] = su;
+            }
+            if (tid == 0) {
+                p.st.m[bh] = m0;
+                p.st.E[bh] = E0;
+                p.st.P[bh] = P0;
+                p.st.t[bh] = N;
+            }
+        }
+    }
+}
+
+template <int D, bool ROPE>
+hipError_t launch_one(const Problem &p, const CausalWork &w, hipStream_t stream) {
+    const size_t smem = sizeof(MSmem<D>);
+    const void *fn = reinterpret_cast<const void *>(&causal_mfma_kernel<D, ROPE>);
+    static bool attr_set = false;   // idempotent; a race only repeats the same call
+    if (!attr_set) {
+        hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
+        if (err != hipSuccess) return err;
+        attr_set = true;
+    }
+    const int grid = p.B * p.H * (D / kTile);
+    hipLaunchKernelGGL((causal_mfma_kernel<D, ROPE>), dim3(grid), dim3(kThreads), smem, stream, p, w);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t causal_work_bytes(int B, int H, int N, int du) {
+    const size_t a = 256;
+    const size_t nseg = (static_cast<size_t>(N) + kLogitSeg - 1) / kLogitSeg;
+    const size_t s = (static_cast<size_t>(B) * H * N * 4 + a - 1) / a * a;
+    const size_t u = (static_cast<size_t>(B) * H * nseg * du * 4 + a - 1) / a * a;
+    return s + u;
+}
+
+CausalWork causal_work_carve(void *base, int B, int H, int N, int du) {
+    const size_t a = 256;
+    const size_t s = (static_cast<size_t>(B) * H * N * 4 + a - 1) / a * a;
+    CausalWork w;
+    w.s = static_cast<float *>(base);
+    w.useg = reinterpret_cast<float *>(static_cast<char *>(base) + s);
+    (void)du;
+    return w;
+}
+
+hipError_t launch_causal_mfma(const Problem &p, const CausalWork &w, hipStream_t stream) {
+    hipError_t err = launch_logits(p, w.useg, w.s, stream);
+    if (err != hipSuccess) return err;
+    if (p.d == 128) return p.rope ? launch_one<128, true>(p, w, stream) : launch_one<128, false>(p, w, stream);
+    if (p.d == 64) return p.rope ? launch_one<64, true>(p, w, stream) : launch_one<64, false>(p, w, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace zeros

@@ -20,6 +20,19 @@ struct Problem {
     float rope_base;
 };
 
+// Tokens per segment of the two-pass logit computation.
+constexpr int kLogitSeg = 512;
+
+// Workspace of the causal MFMA path, carved from one caller- or library-provided buffer.
+struct CausalWork {
+    float *s;       // [B*H, N] logits
+    float *useg;    // [B*H, nseg, d_u] per-segment u sums
+};
+size_t causal_work_bytes(int B, int H, int N, int du);
+CausalWork causal_work_carve(void *base, int B, int H, int N, int du);
+
+hipError_t launch_logits(const Problem &p, float *useg, float *s_out, hipStream_t stream);
+hipError_t launch_causal_mfma(const Problem &p, const CausalWork &w, hipStream_t stream);
 hipError_t launch_causal(const Problem &p, hipStream_t stream);
 hipError_t launch_encoder(const Problem &p, hipStream_t stream);
 hipError_t launch_decode(const Problem &p, hipStream_t stream);

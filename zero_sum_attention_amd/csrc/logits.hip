@@ -1,0 +1,194 @@
+// Deviation logits of the causal ZeroS forward, computed ahead of the chunked scan.
+//
+// Paper-Notes page "ZeroS: Zero-Sum Linear Attention for Efficient Transformers", 关键设计 /
+// 偏差 logits 设计: s_i = -(1/sqrt(d_u)) u_i . ubar_i with the prior-smoothed running mean
+// ubar_i = (e^tau mu + sum_{j<=i} u_j) / (e^tau + i). The logit depends on the step i only, so
+// all of them can be formed before the attention scan, in two passes over u:
+//   pass 1 (useg_sum_kernel): per (head, segment of kSeg tokens), the column sums of u;
+//   pass 2 (logits_kernel):   per (head, segment), the running sum starts from e^tau mu plus
+//                             the sums of the earlier segments, then a lane-parallel scan over
+//                             64-token blocks gives ubar_i and s_i.
+// Output: s [B*H, N] float32 and the per-segment sums [B*H, nseg, d_u] (their total is the
+// u-sum of the recurrent state).
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace zeros {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <typename T>
+__device__ __forceinline__ void load8(const T *p, float (&x)[8]);
+template <>
+__device__ __forceinline__ void load8<bf16>(const bf16 *p, float (&x)[8]) {
+    const uint4 w = *reinterpret_cast<const uint4 *>(p);
+    const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(a[i] << 16);
+        x[2 * i + 1] = __uint_as_float(a[i] & 0xffff0000u);
+    }
+}
+template <>
+__device__ __forceinline__ void load8<float>(const float *p, float (&x)[8]) {
+    const float4 a = *reinterpret_cast<const float4 *>(p);
+    const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+template <typename T>
+__device__ __forceinline__ void load4(const T *p, float (&x)[4]);
+template <>
+__device__ __forceinline__ void load4<bf16>(const bf16 *p, float (&x)[4]) {
+    const uint2 w = *reinterpret_cast<const uint2 *>(p);
+    x[0] = __uint_as_float(w.x << 16);
+    x[1] = __uint_as_float(w.x & 0xffff0000u);
+    x[2] = __uint_as_float(w.y << 16);
+    x[3] = __uint_as_float(w.y & 0xffff0000u);
+}
+template <>
+__device__ __forceinline__ void load4<float>(const float *p, float (&x)[4]) {
+    const float4 a = *reinterpret_cast<const float4 *>(p);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+}
+
+// NE contiguous features (NE a multiple of 4) into x, or zeros when !valid.
+template <int NE, typename T>
+__device__ __forceinline__ void load_feats(const T *p, bool valid, float (&x)[NE]) {
+#pragma unroll
+    for (int i = 0; i < NE; i += 4) {
+        float y[4] = {0.f, 0.f, 0.f, 0.f};
+        if (valid) load4(p + i, y);
+#pragma unroll
+        for (int a = 0; a < 4; ++a) x[i + a] = y[a];
+    }
+}
+
+// Column sums of u over one segment: 8 consecutive features per thread, rows strided.
+template <int D, typename T>
+__global__ __launch_bounds__(kThreads) void useg_sum_kernel(const T *u, float *useg, int N, int nseg) {
+    constexpr int VPR = D / 8;                 // threads per row
+    constexpr int RPI = kThreads / VPR;        // rows per iteration
+    __shared__ float part[RPI][D + 1];
+    const int seg = blockIdx.x % nseg;
+    const int bh = blockIdx.x / nseg;
+    const int tid = threadIdx.x;
+    const int c0 = (tid % VPR) * 8, rg = tid / VPR;
+    const int r0 = seg * kLogitSeg, r1 = min(N, r0 + kLogitSeg);
+    const T *ub = u + static_cast<size_t>(bh) * N * D;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int r = r0 + rg; r < r1; r += RPI) {
+        float x[8];
+        load8(ub + static_cast<size_t>(r) * D + c0, x);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += x[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) part[rg][c0 + i] = acc[i];
+    __syncthreads();
+    if (tid < D) {
+        float s = 0.f;
+        for (int g = 0; g < RPI; ++g) s += part[g][tid];
+        useg[(static_cast<size_t>(bh) * nseg + seg) * D + tid] = s;
+    }
+}
+
+// Logits of one segment. Lane = token within a 64-token block, wave w = features
+// [w*D/4, (w+1)*D/4). The running sum over the block is an inclusive lane scan per feature.
+template <int D, typename T>
+__global__ __launch_bounds__(kThreads) void logits_kernel(const T *u, const float *mu, const float *tau,
+                                                          const float *useg, float *s_out, int N, int H,
+                                                          int nseg) {
+    constexpr int DW = D / 4;                  // features per wave
+    __shared__ float c0s[D];
+    __shared__ float part[4][64];
+    const int seg = blockIdx.x % nseg;
+    const int bh = blockIdx.x / nseg;
+    const int h = bh % H;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const float et = expf(tau[h]);
+    if (tid < D) {
+        float s = et * mu[h * D + tid];
+        const float *us = useg + static_cast<size_t>(bh) * nseg * D + tid;
+        for (int p = 0; p < seg; ++p) s += us[static_cast<size_t>(p) * D];
+        c0s[tid] = s;
+    }
+    __syncthreads();
+    float c0[DW], carry[DW];
+#pragma unroll
+    for (int i = 0; i < DW; ++i) {
+        c0[i] = c0s[w * DW + i];
+        carry[i] = 0.f;
+    }
+    const float rs_du = 1.f / sqrtf(static_cast<float>(D));
+    const T *ub = u + static_cast<size_t>(bh) * N * D;
+    const int r0 = seg * kLogitSeg, r1 = min(N, r0 + kLogitSeg);
+    for (int b0 = r0; b0 < r1; b0 += 64) {
+        const int row = b0 + lane;
+        const bool valid = row < r1;
+        float x[DW], S[DW];
+        load_feats<DW>(ub + static_cast<size_t>(row) * D + w * DW, valid, x);
+#pragma unroll
+        for (int i = 0; i < DW; ++i) S[i] = x[i];
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+#pragma unroll
+            for (int i = 0; i < DW; ++i) {
+                const float y = __shfl_up(S[i], off, 64);
+                if (lane >= off) S[i] += y;
+            }
+        }
+        const float inv = 1.f / (et + static_cast<float>(row + 1));
+        float dot = 0.f;
+#pragma unroll
+        for (int i = 0; i < DW; ++i) {
+            S[i] += carry[i];
+            dot += x[i] * ((c0[i] + S[i]) * inv);
+        }
+        part[w][lane] = dot;
+#pragma unroll
+        for (int i = 0; i < DW; ++i) carry[i] = __shfl(S[i], 63, 64);   // rows past r1 add zeros
+        __syncthreads();
+        if (w == 0 && valid) {
+            const float tot = part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane];
+            s_out[static_cast<size_t>(bh) * N + row] = -tot * rs_du;
+        }
+        __syncthreads();
+    }
+}
+
+template <int D, typename T>
+hipError_t launch_t(const Problem &p, float *useg, float *s_out, hipStream_t stream) {
+    const int nseg = (p.N + kLogitSeg - 1) / kLogitSeg;
+    const int grid = p.B * p.H * nseg;
+    hipLaunchKernelGGL((useg_sum_kernel<D, T>), dim3(grid), dim3(kThreads), 0, stream,
+                       static_cast<const T *>(p.u), useg, p.N, nseg);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((logits_kernel<D, T>), dim3(grid), dim3(kThreads), 0, stream,
+                       static_cast<const T *>(p.u), p.mu, p.tau, useg, s_out, p.N, p.H, nseg);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const Problem &p, float *useg, float *s_out, hipStream_t stream) {
+    return p.dtype == ZEROS_BF16 ? launch_t<D, bf16>(p, useg, s_out, stream)
+                                 : launch_t<D, float>(p, useg, s_out, stream);
+}
+
+}  // namespace
+
+hipError_t launch_logits(const Problem &p, float *useg, float *s_out, hipStream_t stream) {
+    if (p.N == 0) return hipSuccess;
+    switch (p.d) {
+        case 16: return launch_d<16>(p, useg, s_out, stream);
+        case 32: return launch_d<32>(p, useg, s_out, stream);
+        case 64: return launch_d<64>(p, useg, s_out, stream);
+        case 128: return launch_d<128>(p, useg, s_out, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace zeros

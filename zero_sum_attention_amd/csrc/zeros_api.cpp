@@ -14,6 +14,14 @@ hipError_t launch_causal_valu(const Problem &p, hipStream_t stream);
 }
 
 namespace {
+// The matrix-core path covers bfloat16 inputs with d in {64, 128}; everything else (float32
+// inputs, small heads) runs on the float32 VALU kernel.
+bool causal_uses_mfma(const zeros_shape *s) {
+    return s->dtype == ZEROS_BF16 && (s->d == 64 || s->d == 128);
+}
+}  // namespace
+
+namespace {
 
 thread_local std::string g_last_error;
 
@@ -66,6 +74,9 @@ zeros_status check_common(const zeros_shape *s, const void *q, const void *k, co
     const size_t eb = elem_bytes(s->dtype);
     const size_t tens = static_cast<size_t>(s->B) * s->H * s->N * s->d * eb;
     const size_t gate = static_cast<size_t>(s->B) * s->H * s->N * eb;
+    auto al16 = [](const void *x) { return (reinterpret_cast<uintptr_t>(x) & 15u) == 0; };
+    if (s->N != 0 && !(al16(q) && al16(k) && al16(v) && al16(u) && al16(o)))
+        return fail(ZEROS_ERR_SHAPE, f + ": q, k, v, u and o must be 16-byte aligned");
     const Range out{o, tens};
     const Range ins[] = {{q, tens}, {k, tens}, {v, tens}, {u, tens}, {g1, gate}, {gh, gate},
                          {mu, static_cast<size_t>(s->H) * s->d_u * 4}, {tau, static_cast<size_t>(s->H) * 4}};
@@ -110,7 +121,8 @@ extern "C" {
 
 zeros_status zeros_fwd_causal(const zeros_shape *shape, const void *q, const void *k, const void *v,
                               const void *u, const float *mu, const float *tau, const void *g1,
-                              const void *gh, void *o, const zeros_state *state_out, void *stream) {
+                              const void *gh, void *o, const zeros_state *state_out,
+                              void *workspace, size_t workspace_bytes, void *stream) {
     zeros_status st = check_common(shape, q, k, v, u, mu, tau, g1, gh, o, "zeros_fwd_causal");
     if (st != ZEROS_OK) return st;
     if (state_out && !state_complete(state_out))
@@ -119,7 +131,35 @@ zeros_status zeros_fwd_causal(const zeros_shape *shape, const void *q, const voi
         return fail(ZEROS_ERR_SHAPE, "zeros_fwd_causal: state_out matrices must be 16-byte aligned");
     if (shape->N == 0 && !state_out) return ok();
     const zeros::Problem p = make_problem(shape, q, k, v, u, mu, tau, g1, gh, o, state_out);
-    return hip_result(zeros::launch_causal_valu(p, static_cast<hipStream_t>(stream)), "zeros_fwd_causal");
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (!causal_uses_mfma(shape))
+        return hip_result(zeros::launch_causal_valu(p, hs), "zeros_fwd_causal");
+    const size_t need = zeros::causal_work_bytes(shape->B, shape->H, shape->N, shape->d_u);
+    void *ws = workspace;
+    bool owned = false;
+    if (ws) {
+        if (workspace_bytes < need)
+            return fail(ZEROS_ERR_SHAPE, "zeros_fwd_causal: workspace smaller than zeros_fwd_causal_workspace_bytes()");
+        if (reinterpret_cast<uintptr_t>(ws) & 255u)
+            return fail(ZEROS_ERR_SHAPE, "zeros_fwd_causal: workspace must be 256-byte aligned");
+    } else {
+        hipError_t err = hipMallocAsync(&ws, need, hs);
+        if (err != hipSuccess) return hip_result(err, "zeros_fwd_causal (workspace)");
+        owned = true;
+    }
+    const zeros::CausalWork w = zeros::causal_work_carve(ws, shape->B, shape->H, shape->N, shape->d_u);
+    hipError_t err = zeros::launch_causal_mfma(p, w, hs);
+    if (owned) {
+        hipError_t e2 = hipFreeAsync(ws, hs);
+        if (err == hipSuccess) err = e2;
+    }
+    return hip_result(err, "zeros_fwd_causal");
+}
+
+size_t zeros_fwd_causal_workspace_bytes(const zeros_shape *shape) {
+    if (!shape || shape->B < 1 || shape->H < 1 || shape->N < 0 || shape->d_u < 1) return 0;
+    if (!causal_uses_mfma(shape)) return 0;
+    return zeros::causal_work_bytes(shape->B, shape->H, shape->N, shape->d_u);
 }
 
 zeros_status zeros_fwd_encoder(const zeros_shape *shape, const void *q, const void *k, const void *v,

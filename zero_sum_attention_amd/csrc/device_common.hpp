@@ -67,4 +67,39 @@ template <int G> __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
+// Workgroup barrier that only waits for this wave's LDS traffic. __syncthreads() also waits for
+// every outstanding global load, which would stall the prefetch of the next chunk at each barrier.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// DPP control codes: row_shr:n, row_ror:n, row_bcast:15, row_bcast:31.
+constexpr int kRowShr = 0x110, kRowRor = 0x120, kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f(float old, float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (rows of 16 by shifts, then row broadcasts).
+__device__ __forceinline__ float wave_scan_add(float v) {
+    v += dpp_f<kRowShr + 1, 0xf>(0.f, v);
+    v += dpp_f<kRowShr + 2, 0xf>(0.f, v);
+    v += dpp_f<kRowShr + 4, 0xf>(0.f, v);
+    v += dpp_f<kRowShr + 8, 0xf>(0.f, v);
+    v += dpp_f<kRowBcast15, 0xa>(0.f, v);
+    v += dpp_f<kRowBcast31, 0xc>(0.f, v);
+    return v;
+}
+// Inclusive prefix maximum over the 64 lanes of a wave.
+__device__ __forceinline__ float wave_scan_max(float v) {
+    v = fmaxf(v, dpp_f<kRowShr + 1, 0xf>(kNegInf, v));
+    v = fmaxf(v, dpp_f<kRowShr + 2, 0xf>(kNegInf, v));
+    v = fmaxf(v, dpp_f<kRowShr + 4, 0xf>(kNegInf, v));
+    v = fmaxf(v, dpp_f<kRowShr + 8, 0xf>(kNegInf, v));
+    v = fmaxf(v, dpp_f<kRowBcast15, 0xa>(kNegInf, v));
+    v = fmaxf(v, dpp_f<kRowBcast31, 0xc>(kNegInf, v));
+    return v;
+}
+__device__ __forceinline__ float lane_f(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
 }  // namespace zeros

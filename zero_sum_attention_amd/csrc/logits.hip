@@ -131,15 +131,7 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(const T *u, const floa
         float x[DW], S[DW];
         load_feats<DW>(ub + static_cast<size_t>(row) * D + w * DW, valid, x);
 #pragma unroll
-        for (int i = 0; i < DW; ++i) S[i] = x[i];
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-#pragma unroll
-            for (int i = 0; i < DW; ++i) {
-                const float y = __shfl_up(S[i], off, 64);
-                if (lane >= off) S[i] += y;
-            }
-        }
+        for (int i = 0; i < DW; ++i) S[i] = wave_scan_add(x[i]);
         const float inv = 1.f / (et + static_cast<float>(row + 1));
         float dot = 0.f;
 #pragma unroll
@@ -149,13 +141,13 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(const T *u, const floa
         }
         part[w][lane] = dot;
 #pragma unroll
-        for (int i = 0; i < DW; ++i) carry[i] = __shfl(S[i], 63, 64);   // rows past r1 add zeros
-        __syncthreads();
+        for (int i = 0; i < DW; ++i) carry[i] = lane_f(S[i], 63);   // rows past r1 add zeros
+        lds_barrier();
         if (w == 0 && valid) {
             const float tot = part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane];
             s_out[static_cast<size_t>(bh) * N + row] = -tot * rs_du;
         }
-        __syncthreads();
+        lds_barrier();
     }
 }
 

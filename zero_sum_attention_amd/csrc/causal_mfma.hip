@@ -67,8 +67,8 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, float acc) {
 // Per-chunk coefficients, produced one chunk ahead by wave 0 (double-buffered).
 struct Coef {
     float qa[kC], qm[kC], qb[kC], qg[kC], qcx[kC], qkap[kC];   // per query t
-    float wx[kC], wy[kC], s[kC];                                // per key i (w without 1/|k|)
-    float chunk[8];                                             // m1, E1, P1, rX, cHX, cHY
+    float wx[kC], wy[kC], s[kC], ek[kC];                        // per key i; ek = e^{s_i - m1}
+    float chunk[8];                      // m1, E1, P1, rX, cHX, cHY, exact-exp flag
 };
 
 template <int D>
@@ -115,8 +115,10 @@ __device__ __forceinline__ void chunk_scan(Coef &cf, int lane, int t0, int nval,
     const float M = fmaxf(m0, mloc);                                 // m_t
     const float M1 = fmaxf(m0, lane_f(mloc, 63));                    // chunk-end maximum
     const float mfirst = lane_f(M, 0);
+    // wave-uniform choice of the fixed-reference path
+    const bool fixed_ref = __builtin_amdgcn_readfirstlane((M1 - mfirst <= 60.f) ? 1 : 0) != 0;
     float Et, dE, E0p;
-    if (M1 - mfirst <= 60.f) {
+    if (fixed_ref) {
         const float E0r = (m0 == kNegInf) ? 0.f : E0 * __expf(m0 - M1);
         const float pe = wave_scan_add(valid ? __expf(sr - M1) : 0.f);
         const float up = __expf(M1 - M);                             // 1 at the chunk end
@@ -143,7 +145,8 @@ __device__ __forceinline__ void chunk_scan(Coef &cf, int lane, int t0, int nval,
         const float itt = __fdividef(1.f, tt);
         const float d1 = s1 - sh;
         const float a = __fdividef(sh, Et);
-        cf.qa[r] = a;
+        // with the fixed reference, W uses e^{s_i - M1} e^{M1 - m_t}: fold the second factor in
+        cf.qa[r] = fixed_ref ? a * __expf(M1 - M) : a;
         cf.qm[r] = M;
         cf.qb[r] = d1 * itt;
         cf.qg[r] = -d1 * (Pt * itt) * itt - sh * itt;
@@ -157,18 +160,21 @@ __device__ __forceinline__ void chunk_scan(Coef &cf, int lane, int t0, int nval,
             cf.qkap[r] = 0.f;
         }
     }
-    const int last = nval - 1;
+    const int last = __builtin_amdgcn_readfirstlane(nval - 1);
     const float E1 = lane_f(Et, last), P1 = lane_f(Pt, last);
     const float dE1 = lane_f(dE, last), dP1 = lane_f(pp, last), E0p1 = lane_f(E0p, last);
     const float t1 = t0f + static_cast<float>(nval);
     const float iE1 = __fdividef(1.f, E1), it1 = __fdividef(1.f, t1);
-    cf.wx[r] = valid ? __expf(sr - M1) * iE1 - it1 : 0.f;
+    const float ek = valid ? __expf(sr - M1) : 0.f;
+    cf.ek[r] = ek;
+    cf.wx[r] = valid ? ek * iE1 - it1 : 0.f;
     cf.wy[r] = valid ? sr - P1 * it1 : 0.f;
     cf.s[r] = sr;
     if (r == 0) {
         cf.chunk[0] = M1;
         cf.chunk[1] = E1;
         cf.chunk[2] = P1;
+        cf.chunk[6] = fixed_ref ? 0.f : 1.f;
         if (t0 > 0) {
             cf.chunk[3] = E0p1 * iE1;
             cf.chunk[4] = __fdividef(E0p1 * (t1 - t0f) - t0f * dE1, E1 * t0f * t1);
@@ -372,6 +378,7 @@ __global__ __launch_bounds__(kThreads) void causal_mfma_kernel(Problem p, Causal
             // ---- intra-chunk weights and o^T = V^T W^T
             const int tq = 16 * tb + l16;
             const float iq = sm.invq[tq], qa = cf.qa[tq], qm = cf.qm[tq], qb = cf.qb[tq], qgm = cf.qg[tq];
+            const bool exact_exp = cf.chunk[6] != 0.f;   // uniform: logits jumped by > e^60 in the chunk
             f32x4 oacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int pi = 0; pi < 2; ++pi) {
@@ -384,12 +391,19 @@ __global__ __launch_bounds__(kThreads) void causal_mfma_kernel(Problem p, Causal
                     if (kb > tb) continue;
                     const float4 s4 = *reinterpret_cast<const float4 *>(&cf.s[16 * kb + 4 * g4]);
                     const float ks_[4] = {s4.x, s4.y, s4.z, s4.w};
+                    float ke_[4];
+                    if (exact_exp) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) ke_[i] = __expf(ks_[i] - qm);
+                    } else {
+                        const float4 e4 = *reinterpret_cast<const float4 *>(&cf.ek[16 * kb + 4 * g4]);
+                        ke_[0] = e4.x; ke_[1] = e4.y; ke_[2] = e4.z; ke_[3] = e4.w;
+                    }
                     float w[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int key = 16 * kb + 4 * g4 + i;
-                        const float sk = ks_[i];
-                        const float x = at[kb][i] * iq * (qa * __expf(sk - qm) + qb * sk + qgm);
+                        const float x = at[kb][i] * iq * (qa * ke_[i] + qb * ks_[i] + qgm);
                         w[i] = (key <= tq && tq < nval) ? x : 0.f;
                     }
                     wv[2 * h2] = pack2(w[0], w[1]);

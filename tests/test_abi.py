@@ -130,9 +130,12 @@ def test_misaligned_tensors_rejected(lib):
 def test_workspace_size_and_validation(lib):
     bf = shape(B=2, H=16, N=16384, d=128, d_u=128, dtype=1)
     n = lib.zeros_fwd_causal_workspace_bytes(ctypes.byref(bf))
-    logits = 2 * 16 * 16384 * 4
-    useg = 2 * 16 * (16384 // 512) * 128 * 4
-    assert n == logits + useg
+    bh, nch = 2 * 16, 16384 // 64
+    logits = bh * 16384 * 4
+    useg = bh * (16384 // 512) * 128 * 4
+    agg = bh * nch * 16                                  # (max, sum e, sum s, pad) per 64-token chunk
+    rec = (4 * 4 + 8 * 2 + 4 * 2) * 1024 + 1536          # q^, k^T, W operand tiles + coefficients
+    assert n == logits + useg + agg + bh * nch * rec
     assert lib.zeros_fwd_causal_workspace_bytes(ctypes.byref(shape(dtype=0))) == 0   # f32 path: none
     assert lib.zeros_fwd_causal_workspace_bytes(None) == 0
     small = shape(B=1, H=2, N=8, d=64, d_u=64, dtype=1)

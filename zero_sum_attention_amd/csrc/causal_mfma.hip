@@ -3,20 +3,20 @@
 // Method: Paper-Notes page "ZeroS: Zero-Sum Linear Attention for Efficient Transformers", 关键设计
 // (zero-sum weights w_{t,i} = alpha_t e^{s_i} + beta_t s_i + gamma_t after expanding the gated
 // first-order and residual terms; angular factor q^_t . k^_i with RoPE as a relative rotation;
-// the prefix states of the linear-time scan). The logits s_i come from logits.hip.
+// the prefix states of the linear-time scan). The logits s_i and per-chunk logit aggregates come
+// from logits.hip. The sequence is cut into chunks of kC = 64 tokens.
 //
-// Work split: one workgroup of 8 waves per (batch, head, 16-column tile of v/o); the d/16 tiles of
-// a head are mapped onto one XCD so they share q/k through its L2. The sequence is walked in
-// chunks of kC = 64 tokens. After all 8 waves have staged a chunk in LDS, two groups run side by
-// side until the end-of-chunk barrier (each SIMD holds one wave of each group):
-//   waves 0-3, queries [16w, 16w+16) of the chunk:
-//     intra:  A^T = K Q^T (MFMA), W_{t,i} = A (norms folded in) (a_t e^{s_i-m_t} + b_t s_i + g_t)
-//             for i <= t, o^T += V^T W^T (MFMA; W stays in registers: its accumulator layout is
-//             the B-operand layout up to a permutation of the contraction index, mirrored in V^T);
-//     inter:  o_t += q^_t (cX_t X + b_t Y + kappa_t H) with the states at t0 (MFMA), then o.
-//   waves 4-7, state rows [(w-4) d/4, (w-3) d/4): X, Y, H advanced to t1 (elementwise rescale,
-//     then K^T V' on MFMA), written to the other LDS state buffer; wave 4 also runs the scalar
-//     scan of the next chunk.
+// causal_prep_kernel, one workgroup per (batch, head, chunk), all chunks in parallel: everything
+//   that depends on the tokens of a chunk but not on the value columns, done once per head:
+//   the logit carry at the chunk start (combining the aggregates of the earlier chunks), the
+//   chunk's scalar scan and coefficients, unit (RoPE-rotated) q^ and k^, A^T = K Q^T on MFMA and
+//   the intra-chunk weights W_{t,i} = A (a_t e^{s_i-m_t} + b_t s_i + g_t), i <= t. It writes them
+//   to a per-chunk record already laid out as MFMA operands (q^, k^T, W) plus the coefficients.
+// causal_main_kernel, one workgroup of 8 waves per (batch, head, 16-column tile of v/o), walks the
+//   chunks in order. Waves 0-3 (queries [16w, 16w+16)): o^T = V^T W^T + q^-weighted carried
+//   states, on MFMA. Waves 4-7 (state rows [(w-4) d/4, (w-3) d/4)): X, Y, H advanced to the chunk
+//   end, K^T V' on MFMA. The W accumulator layout of the prep kernel is the B-operand layout of
+//   V^T W^T up to a permutation of the contraction index, which V^T is read with.
 // States are kept in a centred basis, X = F/E - H/t0 and Y = G - (P/t0) H. Both have zero-sum
 // weights, so they stay of the size of the output, and rounding them (and the update operands)
 // to bfloat16 for the MFMA is not amplified by the cancellation between alpha F, beta G and
@@ -34,7 +34,6 @@ typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 constexpr int kC = 64;          // tokens per chunk
-constexpr int kThreads = 512;   // 8 waves: queries 0-3, state rows 4-7
 constexpr int kTile = 16;       // value columns per workgroup
 constexpr int kPad = 8;         // bf16 elements of row padding in LDS
 
@@ -71,20 +70,8 @@ struct Coef {
     float chunk[8];                      // m1, E1, P1, rX, cHX, cHY, exact-exp flag
 };
 
-template <int D>
-struct alignas(16) MSmem {
-    alignas(16) uint16_t qh[kC][D + kPad];     // raw (rotated) q rows of the chunk, bf16
-    alignas(16) uint16_t kh[kC][D + kPad];     // unit (rotated) k rows, 16-byte blocks swizzled (kswz)
-    alignas(16) uint16_t vt[kTile][kC + kPad]; // v tile, transposed: vt[m][token] (also the H update operand)
-    alignas(16) uint16_t vx[kTile][kC + kPad]; // update operands v * w_X and v * w_Y (transposed)
-    alignas(16) uint16_t vy[kTile][kC + kPad];
-    alignas(16) uint16_t st[2][3][kTile][D + kPad];  // X, Y, H transposed, bf16, double-buffered
-    float invq[kC];
-    Coef cf[2];
-};
-
-// Column-block swizzle of the k rows: 16-byte block b of row `key` is stored at b ^ kswz(key),
-// so the 8-key column gathers of the state update hit distinct LDS banks.
+// Column-block swizzle of the k rows in LDS: 16-byte block b of row `key` is stored at
+// b ^ kswz(key), so the 8-key column gathers hit distinct LDS banks.
 __device__ __forceinline__ int kswz(int key) { return ((key >> 3) & 3) << 1; }
 
 // (max, sum e^{s-max}) combine of two partial scans; a max of -inf marks an empty part.
@@ -188,21 +175,244 @@ __device__ __forceinline__ void chunk_scan(Coef &cf, int lane, int t0, int nval,
     P0 = P1;
 }
 
+
+// ---- per-chunk record written by the prep kernel and read by the main kernel ------------------
+// [ Q^ operands  : 4 query blocks x KS k-steps x 64 lanes x 16 B ]
+// [ K^T operands : d/16 row tiles x 2 key steps x 64 lanes x 16 B ]
+// [ W operands   : 4 query blocks x 2 key-block pairs x 64 lanes x 16 B ]
+// [ coefficients : cX, beta, kappa per query; w_X, w_Y per key; rX, cHX, cHY, m1, E1, P1 ]
+constexpr int kCoefFloats = 5 * kC + 8;
+template <int D> struct Rec {
+    static constexpr int KS = D / 32;
+    static constexpr size_t q_off = 0;
+    static constexpr size_t k_off = q_off + size_t(4) * KS * 1024;
+    static constexpr size_t w_off = k_off + size_t(D / 16) * 2 * 1024;
+    static constexpr size_t c_off = w_off + size_t(8) * 1024;
+    static constexpr size_t bytes = c_off + 1536;
+};
+enum { kCoCX = 0, kCoBeta = kC, kCoKap = 2 * kC, kCoWX = 3 * kC, kCoWY = 4 * kC, kCoChunk = 5 * kC };
+
+__device__ __forceinline__ void st16(unsigned char *p, const bf16x8 &v) { *reinterpret_cast<bf16x8 *>(p) = v; }
+__device__ __forceinline__ bf16x8 ld16(const unsigned char *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+
+constexpr int kPrepThreads = 256;
+constexpr int kMainThreads = 512;
+
+template <int D>
+struct alignas(16) PSmem {
+    alignas(16) uint16_t qh[kC][D + kPad];     // unit (rotated) q rows, bf16
+    alignas(16) uint16_t kh[kC][D + kPad];     // unit (rotated) k rows, 16-byte blocks swizzled
+    Coef cf;
+    double rev[D / 2];                         // RoPE frequency of each feature pair, turns per position
+};
+
 template <int D, bool ROPE>
-__global__ __launch_bounds__(kThreads) void causal_mfma_kernel(Problem p, CausalWork work) {
+__global__ __launch_bounds__(kPrepThreads) void causal_prep_kernel(Problem p, CausalWork work) {
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    PSmem<D> &sm = *reinterpret_cast<PSmem<D> *>(smem_raw);
+    using R = Rec<D>;
+    constexpr int KS = D / 32;
+    constexpr int RT = D / 64;
+    constexpr int QW = D / 4;           // features per thread in the load phase
+    constexpr int NV = QW / 8;
+    constexpr int NP = QW / 2;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int N = p.N;
+    const int nch = (N + kC - 1) / kC;
+    const int c = blockIdx.x % nch;
+    const int bh = blockIdx.x / nch;
+    const int t0 = c * kC, nval = min(kC, N - t0);
+    const size_t row0 = static_cast<size_t>(bh) * N;
+    unsigned char *rec = work.rec + (static_cast<size_t>(bh) * nch + c) * R::bytes;
+
+    if (ROPE) {
+        if (tid < D / 2) sm.rev[tid] = rope_rev_per_pos(tid, D, p.rope_base);
+        __syncthreads();
+    }
+
+    // ---- wave 0: logit carry at t0 from the earlier chunks, then this chunk's scan
+    if (wave == 0) {
+        float m = kNegInf, e = 0.f, ps = 0.f;
+        const float4 *ag = work.agg + static_cast<size_t>(bh) * nch;
+        for (int j = lane; j < c; j += 64) {
+            const float4 a = ag[j];
+            lse_combine(m, e, a.x, a.y);
+            ps += a.z;
+        }
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float m2 = __shfl_xor(m, off, 64), e2 = __shfl_xor(e, off, 64), p2 = __shfl_xor(ps, off, 64);
+            lse_combine(m, e, m2, e2);
+            ps += p2;
+        }
+        float m0 = lane_f(m, 0), E0 = lane_f(e, 0), P0 = lane_f(ps, 0);
+        const bool vs = lane < nval;
+        const float sv = vs ? work.s[row0 + t0 + lane] : 0.f;
+        const float g1v = vs ? lo_f(static_cast<const uint16_t *>(p.g1)[row0 + t0 + lane]) : 0.f;
+        const float ghv = vs ? lo_f(static_cast<const uint16_t *>(p.gh)[row0 + t0 + lane]) : 0.f;
+        chunk_scan(sm.cf, lane, t0, nval, sv, g1v, ghv, m0, E0, P0);
+    }
+
+    // ---- unit q^, k^ rows, rotated by their offset inside the chunk
+    {
+        const int lr = tid >> 2, f0 = (tid & 3) * QW;
+        const bool valid = lr < nval;
+        const size_t base = (row0 + t0 + lr) * D + f0;
+        const uint16_t *qg = static_cast<const uint16_t *>(p.q), *kg = static_cast<const uint16_t *>(p.k);
+        uint4 pq[NV], pk[NV];
+#pragma unroll
+        for (int a = 0; a < NV; ++a) {
+            pq[a] = valid ? *reinterpret_cast<const uint4 *>(qg + base + 8 * a) : make_uint4(0, 0, 0, 0);
+            pk[a] = valid ? *reinterpret_cast<const uint4 *>(kg + base + 8 * a) : make_uint4(0, 0, 0, 0);
+        }
+        float ssq = 0.f, ssk = 0.f;
+#pragma unroll
+        for (int a = 0; a < NV; ++a) {
+            ssq = dot2_bf16(pq[a].x, ssq); ssq = dot2_bf16(pq[a].y, ssq);
+            ssq = dot2_bf16(pq[a].z, ssq); ssq = dot2_bf16(pq[a].w, ssq);
+            ssk = dot2_bf16(pk[a].x, ssk); ssk = dot2_bf16(pk[a].y, ssk);
+            ssk = dot2_bf16(pk[a].z, ssk); ssk = dot2_bf16(pk[a].w, ssk);
+        }
+        ssq = group_sum<4>(ssq);
+        ssk = group_sum<4>(ssk);
+        const float iq = valid ? __frsqrt_rn(fmaxf(ssq, 1e-24f)) : 0.f;
+        const float ik = valid ? __frsqrt_rn(fmaxf(ssk, 1e-24f)) : 0.f;
+#pragma unroll
+        for (int a = 0; a < NV; ++a) {
+            uint32_t wq[4] = {pq[a].x, pq[a].y, pq[a].z, pq[a].w};
+            uint32_t wk[4] = {pk[a].x, pk[a].y, pk[a].z, pk[a].w};
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const float q0 = lo_f(wq[b]), q1 = hi_f(wq[b]);
+                const float k0 = lo_f(wk[b]), k1 = hi_f(wk[b]);
+                if (ROPE) {
+                    float cs, sn;
+                    rope_cos_sin(sm.rev[f0 / 2 + 4 * a + b], lr, cs, sn);
+                    const float cq = cs * iq, sq = sn * iq, ck = cs * ik, sk = sn * ik;
+                    wq[b] = pack2(q0 * cq - q1 * sq, q0 * sq + q1 * cq);
+                    wk[b] = pack2(k0 * ck - k1 * sk, k0 * sk + k1 * ck);
+                } else {
+                    wq[b] = pack2(q0 * iq, q1 * iq);
+                    wk[b] = pack2(k0 * ik, k1 * ik);
+                }
+            }
+            const int blk = f0 / 8 + a;
+            *reinterpret_cast<uint4 *>(&sm.qh[lr][8 * blk]) = make_uint4(wq[0], wq[1], wq[2], wq[3]);
+            *reinterpret_cast<uint4 *>(&sm.kh[lr][8 * (blk ^ kswz(lr))]) = make_uint4(wk[0], wk[1], wk[2], wk[3]);
+        }
+    }
+    __syncthreads();
+
+    // ---- query block tb = wave: q^ operands, A^T tiles, intra-chunk weights
+    {
+        const int tb = wave;
+        const Coef &cf = sm.cf;
+        bf16x8 qop[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            qop[ks] = *reinterpret_cast<const bf16x8 *>(&sm.qh[16 * tb + l16][32 * ks + 8 * g4]);
+            st16(rec + R::q_off + (size_t(tb * KS + ks) * 64 + lane) * 16, qop[ks]);
+        }
+        f32x4 at[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) at[kb][i] = 0.f;
+            if (kb <= tb) {
+                const int key = 16 * kb + l16;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&sm.kh[key][8 * ((4 * ks + g4) ^ kswz(key))]);
+                    at[kb] = mfma(a, qop[ks], at[kb]);
+                }
+            }
+        }
+        const int tq = 16 * tb + l16;
+        const float qa = cf.qa[tq], qm = cf.qm[tq], qb = cf.qb[tq], qgm = cf.qg[tq];
+        const bool exact_exp = cf.chunk[6] != 0.f;
+#pragma unroll
+        for (int pi = 0; pi < 2; ++pi) {
+            uint32_t wv[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const int kb = 2 * pi + h2;
+                if (kb > tb) continue;
+                const float4 s4 = *reinterpret_cast<const float4 *>(&cf.s[16 * kb + 4 * g4]);
+                const float ks_[4] = {s4.x, s4.y, s4.z, s4.w};
+                float ke_[4];
+                if (exact_exp) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) ke_[i] = __expf(ks_[i] - qm);
+                } else {
+                    const float4 e4 = *reinterpret_cast<const float4 *>(&cf.ek[16 * kb + 4 * g4]);
+                    ke_[0] = e4.x; ke_[1] = e4.y; ke_[2] = e4.z; ke_[3] = e4.w;
+                }
+                float w[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int key = 16 * kb + 4 * g4 + i;
+                    const float x = at[kb][i] * (qa * ke_[i] + qb * ks_[i] + qgm);
+                    w[i] = (key <= tq && tq < nval) ? x : 0.f;
+                }
+                wv[2 * h2] = pack2(w[0], w[1]);
+                wv[2 * h2 + 1] = pack2(w[2], w[3]);
+            }
+            st16(rec + R::w_off + (size_t(tb * 2 + pi) * 64 + lane) * 16, as_bf16x8(wv[0], wv[1], wv[2], wv[3]));
+        }
+    }
+
+    // ---- k^T operands of the state update: row tiles [RT*wave, RT*wave+RT), 2 key steps
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int jb = RT * wave + rt;
+        const int j = 16 * jb + l16;
+#pragma unroll
+        for (int ks2 = 0; ks2 < kC / 32; ++ks2) {
+            const int kk0 = 32 * ks2 + 8 * g4;
+            const int jc = (((j >> 3) ^ (2 * g4)) << 3) | (j & 7);   // kswz(kk0 + c) == 2 * g4
+            bf16x8 a;
+#pragma unroll
+            for (int cc = 0; cc < 8; ++cc) a[cc] = static_cast<short>(sm.kh[kk0 + cc][jc]);
+            st16(rec + R::k_off + (size_t(jb * 2 + ks2) * 64 + lane) * 16, a);
+        }
+    }
+
+    // ---- coefficients used by the main kernel
+    if (tid < kC) {
+        float *co = reinterpret_cast<float *>(rec + R::c_off);
+        co[kCoCX + tid] = sm.cf.qcx[tid];
+        co[kCoBeta + tid] = sm.cf.qb[tid];
+        co[kCoKap + tid] = sm.cf.qkap[tid];
+        co[kCoWX + tid] = sm.cf.wx[tid];
+        co[kCoWY + tid] = sm.cf.wy[tid];
+        if (tid < 6) {
+            const int src[6] = {3, 4, 5, 0, 1, 2};   // rX, cHX, cHY, m1, E1, P1
+            co[kCoChunk + tid] = sm.cf.chunk[src[tid]];
+        }
+    }
+}
+
+template <int D>
+struct alignas(16) MSmem {
+    alignas(16) uint16_t vt[kTile][kC + kPad]; // v tile, transposed: vt[m][token] (also the H update operand)
+    alignas(16) uint16_t vx[kTile][kC + kPad]; // update operands v * w_X and v * w_Y (transposed)
+    alignas(16) uint16_t vy[kTile][kC + kPad];
+    alignas(16) uint16_t st[2][3][kTile][D + kPad];  // X, Y, H transposed, bf16, double-buffered
+};
+
+template <int D, bool ROPE>
+__global__ __launch_bounds__(kMainThreads) void causal_main_kernel(Problem p, CausalWork work) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     MSmem<D> &sm = *reinterpret_cast<MSmem<D> *>(smem_raw);
+    using R = Rec<D>;
     constexpr int NTILE = D / kTile;
-    constexpr int KS = D / 32;          // MFMA k-steps over the feature dimension
-    constexpr int RT = D / 64;          // 16-row state tiles per update wave
-    constexpr int QW = D / 8;           // features per thread in the load phase
-    constexpr int NV = QW / 8;          // 16-byte vectors per thread per row slice
-    constexpr int NP = QW / 2;          // rotation pairs per thread
-    constexpr int kScanWave = 0;        // the query wave with the least intra-chunk work
+    constexpr int KS = D / 32;
+    constexpr int RT = D / 64;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, g4 = lane >> 4;
-    const bool qgroup = wave < 4;       // waves 0-3: queries; 4-7: state update
+    const bool qgroup = wave < 4;
     const int wb = wave & 3;
 
     const int G = gridDim.x;
@@ -211,36 +421,25 @@ __global__ __launch_bounds__(kThreads) void causal_mfma_kernel(Problem p, Causal
     const int tile = L % NTILE;
     const int bh = L / NTILE;
     const int N = p.N;
+    const int nch = (N + kC - 1) / kC;
     const size_t row0 = static_cast<size_t>(bh) * N;
-    const uint16_t *qg = static_cast<const uint16_t *>(p.q) + row0 * D;
-    const uint16_t *kg = static_cast<const uint16_t *>(p.k) + row0 * D;
     const uint16_t *vg = static_cast<const uint16_t *>(p.v) + row0 * D;
-    const uint16_t *g1g = static_cast<const uint16_t *>(p.g1) + row0;
-    const uint16_t *ghg = static_cast<const uint16_t *>(p.gh) + row0;
-    const float *slog = work.s + row0;
     uint16_t *og = static_cast<uint16_t *>(p.o) + row0 * D;
+    const unsigned char *rec0 = work.rec + static_cast<size_t>(bh) * nch * R::bytes;
 
-    // load-phase coordinates: row lr of the chunk, features [f0, f0 + QW), value columns 2*p8+{0,1}
-    const int lr = tid >> 3, p8 = tid & 7, f0 = p8 * QW;
-    const int sc_lane = tid - 64 * kScanWave;   // lane of the scan wave that loads logits/gates
+    // staging coordinates: token lr of the chunk, value columns 2*p8 + {0, 1}
+    const int lr = tid >> 3, p8 = tid & 7;
 
-    // rotation of this thread's pairs by its offset lr inside the chunk
-    float rc[ROPE ? NP : 1], rs[ROPE ? NP : 1];
     // rotation re-basing this update lane's state rows by -kC after each chunk
     float fc[ROPE ? 2 * RT : 1], fs[ROPE ? 2 * RT : 1];
-    if (ROPE) {
+    if (ROPE && !qgroup) {
 #pragma unroll
-        for (int a = 0; a < NP; ++a)
-            rope_cos_sin(rope_rev_per_pos(f0 / 2 + a, D, p.rope_base), lr, rc[a], rs[a]);
-        if (!qgroup) {
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-                for (int pp = 0; pp < 2; ++pp) {
-                    const int jp = 8 * (RT * wb + rt) + 2 * g4 + pp;
-                    rope_cos_sin(rope_rev_per_pos(jp, D, p.rope_base), kC, fc[2 * rt + pp], fs[2 * rt + pp]);
-                }
-        }
+            for (int pp = 0; pp < 2; ++pp) {
+                const int jp = 8 * (RT * wb + rt) + 2 * g4 + pp;
+                rope_cos_sin(rope_rev_per_pos(jp, D, p.rope_base), kC, fc[2 * rt + pp], fs[2 * rt + pp]);
+            }
     }
 
     f32x4 X[RT], Y[RT], Hm[RT];
@@ -248,202 +447,116 @@ __global__ __launch_bounds__(kThreads) void causal_mfma_kernel(Problem p, Causal
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) X[rt][i] = Y[rt][i] = Hm[rt][i] = 0.f;
-    float m0 = kNegInf, E0 = 0.f, P0 = 0.f;    // scan carry (kept by the scan wave)
 
-    // prefetch registers
-    uint4 pq[NV], pk[NV];
-    uint32_t pv;                               // v of token lr, columns 2*p8 (low half) and 2*p8+1
-    float ps = 0.f, pg1 = 0.f, pgh = 0.f;     // logits and gates of the chunk after the current one
-    auto load_scalars = [&](int tc) {
-        if (sc_lane >= 0 && sc_lane < kC) {
-            const bool vs = tc + sc_lane < N;
-            ps = vs ? slog[tc + sc_lane] : 0.f;
-            pg1 = vs ? lo_f(g1g[tc + sc_lane]) : 0.f;
-            pgh = vs ? lo_f(ghg[tc + sc_lane]) : 0.f;
-        }
-    };
-    auto load_chunk = [&](int tc) {
-        const bool valid = tc + lr < N;
-        const size_t base = static_cast<size_t>(tc + lr) * D + f0;
+    // operands of the current chunk (loaded one chunk ahead)
+    // MFMA operands of a chunk, NOP 16-byte slots per lane, loaded one chunk ahead. Waves 0-3:
+    // slots 0..KS-1 = q^ (query block wb), KS, KS+1 = W (key-block pairs); waves 4-7: slots
+    // 0..2RT-1 = k^T (row tiles of wave wb-4, two key steps), the rest repeat slot 0. The loads
+    // are the same code in every wave, only the addresses differ.
+    constexpr int NOP = KS + 2;
+    uint32_t opoff[NOP];
 #pragma unroll
-        for (int a = 0; a < NV; ++a) {
-            pq[a] = valid ? *reinterpret_cast<const uint4 *>(qg + base + 8 * a) : make_uint4(0, 0, 0, 0);
-            pk[a] = valid ? *reinterpret_cast<const uint4 *>(kg + base + 8 * a) : make_uint4(0, 0, 0, 0);
-        }
-        pv = valid ? *reinterpret_cast<const uint32_t *>(vg + static_cast<size_t>(tc + lr) * D + tile * kTile + 2 * p8)
-                   : 0u;
-    };
-    if (N > 0) {
-        load_chunk(0);
-        load_scalars(0);
-        if (wave == kScanWave) chunk_scan(sm.cf[0], lane, 0, min(kC, N), ps, pg1, pgh, m0, E0, P0);
-        load_scalars(kC);
+    for (int i = 0; i < NOP; ++i) {
+        size_t o;
+        if (qgroup) o = i < KS ? R::q_off + size_t(wb * KS + i) * 1024 : R::w_off + size_t(wb * 2 + i - KS) * 1024;
+        else { const int j = i < 2 * RT ? i : 0; o = R::k_off + size_t((RT * wb + j / 2) * 2 + (j & 1)) * 1024; }
+        opoff[i] = static_cast<uint32_t>(o + lane * 16);
     }
-    __syncthreads();
+    bf16x8 opn[NOP];
+    // three scalars per lane: (cX, beta, kappa) of the lane's query in waves 0-3,
+    // (rX, cHX, cHY) of the chunk in waves 4-7
+    const int tq_lane = 16 * wb + l16;
+    const int sc_off0 = qgroup ? kCoCX + tq_lane : kCoChunk + 0;
+    const int sc_off1 = qgroup ? kCoBeta + tq_lane : kCoChunk + 1;
+    const int sc_off2 = qgroup ? kCoKap + tq_lane : kCoChunk + 2;
+    float sc0 = 0.f, sc1 = 0.f, sc2 = 0.f;
+    uint32_t pv = 0;                            // v of token lr, columns 2*p8 (low) and 2*p8+1
+    bool pv_ok = false;                         // token lr exists (else pv is a stand-in row)
+    float2 wx2 = make_float2(0.f, 0.f), wy2 = wx2;  // w_X, w_Y of tokens (lr & ~1), (lr | 1)
+    const int tok_lane = lr & ~1;
+    const size_t vcol = static_cast<size_t>(tile) * kTile + 2 * p8;
+#define ZEROS_LOAD_CHUNK(c)                                                                              \
+    do {                                                                                                 \
+        const unsigned char *rec_ = rec0 + static_cast<size_t>(c) * R::bytes;                          \
+        const float *co_ = reinterpret_cast<const float *>(rec_ + R::c_off);                            \
+        _Pragma("unroll") for (int i = 0; i < NOP; ++i) opn[i] = ld16(rec_ + opoff[i]);                  \
+        sc0 = co_[sc_off0];                                                                              \
+        sc1 = co_[sc_off1];                                                                              \
+        sc2 = co_[sc_off2];                                                                              \
+        const int tok_ = (c) * kC + lr;     /* rows past N read row N-1 (in bounds), then zeroed */     \
+        const uint32_t raw_ = *reinterpret_cast<const uint32_t *>(vg + static_cast<size_t>(min(tok_, N - 1)) * D + vcol); \
+        pv = raw_;                                                                                       \
+        pv_ok = tok_ < N;                   /* applied when staging, so the load is not waited for */   \
+        wx2 = *reinterpret_cast<const float2 *>(co_ + kCoWX + tok_lane);                                 \
+        wy2 = *reinterpret_cast<const float2 *>(co_ + kCoWY + tok_lane);                                 \
+    } while (0)
 
+    if (N > 0) ZEROS_LOAD_CHUNK(0);
     for (int t0 = 0, ci = 0; t0 < N; t0 += kC, ++ci) {
         const int nval = min(kC, N - t0);
-        const Coef &cf = sm.cf[ci & 1];
 
-        // ---- registers -> LDS: norms, rotation, v operands, per-key data (all 8 waves)
+        // ---- stage the v tile (transposed token pairs) and its update operands
         {
-            float ssq = 0.f, ssk = 0.f;
-#pragma unroll
-            for (int a = 0; a < NV; ++a) {
-                ssq = dot2_bf16(pq[a].x, ssq); ssq = dot2_bf16(pq[a].y, ssq);
-                ssq = dot2_bf16(pq[a].z, ssq); ssq = dot2_bf16(pq[a].w, ssq);
-                ssk = dot2_bf16(pk[a].x, ssk); ssk = dot2_bf16(pk[a].y, ssk);
-                ssk = dot2_bf16(pk[a].z, ssk); ssk = dot2_bf16(pk[a].w, ssk);
-            }
-            ssq = group_sum<8>(ssq);
-            ssk = group_sum<8>(ssk);
-            const bool valid = lr < nval;
-            const float iq = valid ? __frsqrt_rn(fmaxf(ssq, 1e-24f)) : 0.f;
-            const float ik = valid ? __frsqrt_rn(fmaxf(ssk, 1e-24f)) : 0.f;
-            if (p8 == 0) sm.invq[lr] = iq;
-            // q keeps its norm (1/|q| is applied per query); k is stored as a unit vector
-#pragma unroll
-            for (int a = 0; a < NV; ++a) {
-                uint32_t wq[4] = {pq[a].x, pq[a].y, pq[a].z, pq[a].w};
-                uint32_t wk[4] = {pk[a].x, pk[a].y, pk[a].z, pk[a].w};
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const float k0 = lo_f(wk[b]), k1 = hi_f(wk[b]);
-                    if (ROPE) {
-                        const float c = rc[4 * a + b], sn = rs[4 * a + b];
-                        const float q0 = lo_f(wq[b]), q1 = hi_f(wq[b]);
-                        const float ck = c * ik, sk = sn * ik;
-                        wq[b] = pack2(q0 * c - q1 * sn, q0 * sn + q1 * c);
-                        wk[b] = pack2(k0 * ck - k1 * sk, k0 * sk + k1 * ck);
-                    } else {
-                        wk[b] = pack2(k0 * ik, k1 * ik);
-                    }
-                }
-                pq[a] = make_uint4(wq[0], wq[1], wq[2], wq[3]);
-                pk[a] = make_uint4(wk[0], wk[1], wk[2], wk[3]);
-            }
-            const int ksw = kswz(lr);
-#pragma unroll
-            for (int a = 0; a < NV; ++a) {
-                const int blk = f0 / 8 + a;
-                *reinterpret_cast<uint4 *>(&sm.qh[lr][8 * blk]) = pq[a];
-                *reinterpret_cast<uint4 *>(&sm.kh[lr][8 * (blk ^ ksw)]) = pk[a];
-            }
-            // v operands, stored transposed as token pairs: the lanes of rows 2a and 2a+1 (8 lanes
-            // apart, same DPP row) swap their column pairs, then row 2a writes column 2 p8 and
-            // row 2a+1 column 2 p8 + 1 for tokens (2a, 2a+1). Weights are zero past the chunk end.
+            const uint32_t pvv = pv_ok ? pv : 0u;
             const uint32_t other = static_cast<uint32_t>(
-                __builtin_amdgcn_update_dpp(0, static_cast<int>(pv), kRowRor + 8, 0xf, 0xf, false));
+                __builtin_amdgcn_update_dpp(0, static_cast<int>(pvv), kRowRor + 8, 0xf, 0xf, false));
             const bool odd = lr & 1;
-            const uint32_t pair = odd ? ((other >> 16) | (pv & 0xffff0000u)) : ((pv & 0xffffu) | (other << 16));
+            const uint32_t pair = odd ? ((other >> 16) | (pvv & 0xffff0000u)) : ((pvv & 0xffffu) | (other << 16));
             const int col = 2 * p8 + (odd ? 1 : 0), tok = lr & ~1;
-            const float2 wx2 = *reinterpret_cast<const float2 *>(&cf.wx[tok]);
-            const float2 wy2 = *reinterpret_cast<const float2 *>(&cf.wy[tok]);
             const float v0 = lo_f(pair), v1 = hi_f(pair);
             *reinterpret_cast<uint32_t *>(&sm.vt[col][tok]) = pair;
             *reinterpret_cast<uint32_t *>(&sm.vx[col][tok]) = pack2(v0 * wx2.x, v1 * wx2.y);
             *reinterpret_cast<uint32_t *>(&sm.vy[col][tok]) = pack2(v0 * wy2.x, v1 * wy2.y);
         }
+        // keep this chunk's operands, fetch the next chunk's
+        bf16x8 opc[NOP];
+#pragma unroll
+        for (int i = 0; i < NOP; ++i) opc[i] = opn[i];
+        const float s0c = sc0, s1c = sc1, s2c = sc2;
         lds_barrier();
-        if (t0 + kC < N) load_chunk(t0 + kC);
-        // ---- coefficients of the next chunk; then fetch the logits and gates of the one after
-        if (wave == kScanWave && t0 + kC < N) {
-            chunk_scan(sm.cf[(ci + 1) & 1], lane, t0 + kC, min(kC, N - t0 - kC), ps, pg1, pgh, m0, E0, P0);
-            load_scalars(t0 + 2 * kC);
-        }
+        if (t0 + kC < N) ZEROS_LOAD_CHUNK(ci + 1);
 
         if (qgroup) {
-            // ---- A^T tiles for this wave's query block
             const int tb = wb;
-            bf16x8 qop[KS];
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                qop[ks] = *reinterpret_cast<const bf16x8 *>(&sm.qh[16 * tb + l16][32 * ks + 8 * g4]);
-            f32x4 at[4];
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) at[kb][i] = 0.f;
-                if (kb <= tb) {
-                    const int key = 16 * kb + l16;
-                    const int ksw = kswz(key);
-#pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) {
-                        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&sm.kh[key][8 * ((4 * ks + g4) ^ ksw)]);
-                        at[kb] = mfma(a, qop[ks], at[kb]);
-                    }
-                }
-            }
-
-            // ---- intra-chunk weights and o^T = V^T W^T
             const int tq = 16 * tb + l16;
-            const float iq = sm.invq[tq], qa = cf.qa[tq], qm = cf.qm[tq], qb = cf.qb[tq], qgm = cf.qg[tq];
-            const bool exact_exp = cf.chunk[6] != 0.f;   // uniform: logits jumped by > e^60 in the chunk
             f32x4 oacc = {0.f, 0.f, 0.f, 0.f};
+            // intra-chunk: o^T += V^T W^T over key-block pairs (0,1) and (2,3)
 #pragma unroll
             for (int pi = 0; pi < 2; ++pi) {
                 if (2 * pi > tb) continue;
-                uint32_t wv[4] = {0u, 0u, 0u, 0u};
-                uint2 va[2] = {make_uint2(0, 0), make_uint2(0, 0)};
-#pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2) {
-                    const int kb = 2 * pi + h2;
-                    if (kb > tb) continue;
-                    const float4 s4 = *reinterpret_cast<const float4 *>(&cf.s[16 * kb + 4 * g4]);
-                    const float ks_[4] = {s4.x, s4.y, s4.z, s4.w};
-                    float ke_[4];
-                    if (exact_exp) {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) ke_[i] = __expf(ks_[i] - qm);
-                    } else {
-                        const float4 e4 = *reinterpret_cast<const float4 *>(&cf.ek[16 * kb + 4 * g4]);
-                        ke_[0] = e4.x; ke_[1] = e4.y; ke_[2] = e4.z; ke_[3] = e4.w;
-                    }
-                    float w[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int key = 16 * kb + 4 * g4 + i;
-                        const float x = at[kb][i] * iq * (qa * ke_[i] + qb * ks_[i] + qgm);
-                        w[i] = (key <= tq && tq < nval) ? x : 0.f;
-                    }
-                    wv[2 * h2] = pack2(w[0], w[1]);
-                    wv[2 * h2 + 1] = pack2(w[2], w[3]);
-                    va[h2] = *reinterpret_cast<const uint2 *>(&sm.vt[l16][16 * kb + 4 * g4]);
-                }
-                oacc = mfma(as_bf16x8(va[0].x, va[0].y, va[1].x, va[1].y), as_bf16x8(wv[0], wv[1], wv[2], wv[3]), oacc);
+                const int kb0 = 2 * pi, kb1 = 2 * pi + 1;
+                const uint2 va = *reinterpret_cast<const uint2 *>(&sm.vt[l16][16 * kb0 + 4 * g4]);
+                const uint2 vb = (kb1 <= tb) ? *reinterpret_cast<const uint2 *>(&sm.vt[l16][16 * kb1 + 4 * g4])
+                                             : make_uint2(0, 0);
+                oacc = mfma(as_bf16x8(va.x, va.y, vb.x, vb.y), opc[KS + pi], oacc);
             }
-
-            // ---- carried states
+            // carried states
             if (t0 > 0) {
                 const int sb = ci & 1;
                 f32x4 ax = {0.f, 0.f, 0.f, 0.f}, ay = ax, ah = ax;
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    ax = mfma(*reinterpret_cast<const bf16x8 *>(&sm.st[sb][0][l16][32 * ks + 8 * g4]), qop[ks], ax);
-                    ay = mfma(*reinterpret_cast<const bf16x8 *>(&sm.st[sb][1][l16][32 * ks + 8 * g4]), qop[ks], ay);
-                    ah = mfma(*reinterpret_cast<const bf16x8 *>(&sm.st[sb][2][l16][32 * ks + 8 * g4]), qop[ks], ah);
+                    ax = mfma(*reinterpret_cast<const bf16x8 *>(&sm.st[sb][0][l16][32 * ks + 8 * g4]), opc[ks], ax);
+                    ay = mfma(*reinterpret_cast<const bf16x8 *>(&sm.st[sb][1][l16][32 * ks + 8 * g4]), opc[ks], ay);
+                    ah = mfma(*reinterpret_cast<const bf16x8 *>(&sm.st[sb][2][l16][32 * ks + 8 * g4]), opc[ks], ah);
                 }
-                const float cx = cf.qcx[tq], kap = cf.qkap[tq];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) oacc[i] += iq * (cx * ax[i] + qb * ay[i] + kap * ah[i]);
+                for (int i = 0; i < 4; ++i) oacc[i] += s0c * ax[i] + s1c * ay[i] + s2c * ah[i];   // cX, beta, kappa
             }
             if (tq < nval) {
                 const uint2 ov = make_uint2(pack2(oacc[0], oacc[1]), pack2(oacc[2], oacc[3]));
                 *reinterpret_cast<uint2 *>(og + static_cast<size_t>(t0 + tq) * D + tile * kTile + 4 * g4) = ov;
             }
         } else {
-            // ---- advance the states to t1
             if (t0 > 0) {
-                const float rX = cf.chunk[3], cHX = cf.chunk[4], cHY = cf.chunk[5];
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        X[rt][i] = rX * X[rt][i] + cHX * Hm[rt][i];
-                        Y[rt][i] = Y[rt][i] + cHY * Hm[rt][i];
+                        X[rt][i] = s0c * X[rt][i] + s1c * Hm[rt][i];   // rX, cHX
+                        Y[rt][i] = Y[rt][i] + s2c * Hm[rt][i];           // cHY
                     }
             }
-            const int gsw = 2 * g4;             // kswz of every key this lane gathers
 #pragma unroll
             for (int ks2 = 0; ks2 < kC / 32; ++ks2) {
                 const int kk0 = 32 * ks2 + 8 * g4;
@@ -452,14 +565,9 @@ __global__ __launch_bounds__(kThreads) void causal_mfma_kernel(Problem p, Causal
                 const bf16x8 BH = *reinterpret_cast<const bf16x8 *>(&sm.vt[l16][kk0]);
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) {
-                    const int j = 16 * (RT * wb + rt) + l16;
-                    const int jc = (((j >> 3) ^ gsw) << 3) | (j & 7);
-                    bf16x8 a;
-#pragma unroll
-                    for (int c = 0; c < 8; ++c) a[c] = static_cast<short>(sm.kh[kk0 + c][jc]);
-                    X[rt] = mfma(a, BX, X[rt]);
-                    Y[rt] = mfma(a, BY, Y[rt]);
-                    Hm[rt] = mfma(a, BH, Hm[rt]);
+                    X[rt] = mfma(opc[2 * rt + ks2], BX, X[rt]);
+                    Y[rt] = mfma(opc[2 * rt + ks2], BY, Y[rt]);
+                    Hm[rt] = mfma(opc[2 * rt + ks2], BH, Hm[rt]);
                 }
             }
             if (ROPE) {
@@ -486,21 +594,23 @@ __global__ __launch_bounds__(kThreads) void causal_mfma_kernel(Problem p, Causal
                 *reinterpret_cast<uint2 *>(&sm.st[nb][2][l16][jc]) = make_uint2(pack2(Hm[rt][0], Hm[rt][1]), pack2(Hm[rt][2], Hm[rt][3]));
             }
         }
-        lds_barrier();            // chunk done: LDS staging, states and coefficients may be replaced
+        lds_barrier();            // chunk done: staging and the state buffer may be replaced
     }
+
+#undef ZEROS_LOAD_CHUNK
 
     // ---- final state (update waves): back to F = E (X + H/t), G = Y + (P/t) H, absolute RoPE frame
     if (p.st.F != nullptr) {
+        float m0 = kNegInf, E0 = 0.f, P0 = 0.f;
         if (N > 0) {
-            const Coef &cl = sm.cf[((N + kC - 1) / kC - 1) & 1];
-            m0 = cl.chunk[0];
-            E0 = cl.chunk[1];
-            P0 = cl.chunk[2];
+            const float *co = reinterpret_cast<const float *>(rec0 + static_cast<size_t>(nch - 1) * R::bytes + R::c_off);
+            m0 = co[kCoChunk + 3];
+            E0 = co[kCoChunk + 4];
+            P0 = co[kCoChunk + 5];
         }
         if (!qgroup) {
             const size_t mat0 = static_cast<size_t>(bh) * D * D;
             const float tf = static_cast<float>(N);
-            const int nchunks = (N + kC - 1) / kC;
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
                 float F[4], Gv[4], Hv[4];
@@ -516,7 +626,7 @@ __global__ __launch_bounds__(kThreads) void causal_mfma_kernel(Problem p, Causal
                     for (int pp = 0; pp < 2; ++pp) {
                         const int jp = 8 * (RT * wb + rt) + 2 * g4 + pp;
                         float c, sn;
-                        rope_cos_sin(rope_rev_per_pos(jp, D, p.rope_base), nchunks * kC, c, sn);
+                        rope_cos_sin(rope_rev_per_pos(jp, D, p.rope_base), nch * kC, c, sn);
                         const int i0 = 2 * pp, i1 = i0 + 1;
                         float x0 = F[i0], x1 = F[i1];
                         F[i0] = x0 * c - x1 * sn; F[i1] = x0 * sn + x1 * c;
@@ -553,43 +663,66 @@ __global__ __launch_bounds__(kThreads) void causal_mfma_kernel(Problem p, Causal
     }
 }
 
+template <typename K>
+hipError_t set_smem(K kernel, size_t bytes) {
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               static_cast<int>(bytes));
+}
+
 template <int D, bool ROPE>
 hipError_t launch_one(const Problem &p, const CausalWork &w, hipStream_t stream) {
-    const size_t smem = sizeof(MSmem<D>);
-    const void *fn = reinterpret_cast<const void *>(&causal_mfma_kernel<D, ROPE>);
-    static bool attr_set = false;   // idempotent; a race only repeats the same call
+    static bool attr_set = false;   // idempotent; a race only repeats the same calls
     if (!attr_set) {
-        hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
+        hipError_t err = set_smem(&causal_prep_kernel<D, ROPE>, sizeof(PSmem<D>));
+        if (err == hipSuccess) err = set_smem(&causal_main_kernel<D, ROPE>, sizeof(MSmem<D>));
         if (err != hipSuccess) return err;
         attr_set = true;
     }
-    const int grid = p.B * p.H * (D / kTile);
-    hipLaunchKernelGGL((causal_mfma_kernel<D, ROPE>), dim3(grid), dim3(kThreads), smem, stream, p, w);
+    const int nch = (p.N + kC - 1) / kC;
+    if (nch > 0) {
+        hipLaunchKernelGGL((causal_prep_kernel<D, ROPE>), dim3(p.B * p.H * nch), dim3(kPrepThreads),
+                           sizeof(PSmem<D>), stream, p, w);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    hipLaunchKernelGGL((causal_main_kernel<D, ROPE>), dim3(p.B * p.H * (D / kTile)), dim3(kMainThreads),
+                       sizeof(MSmem<D>), stream, p, w);
     return hipGetLastError();
 }
 
 }  // namespace
 
+size_t causal_rec_bytes(int d) { return d == 128 ? Rec<128>::bytes : Rec<64>::bytes; }
+
 size_t causal_work_bytes(int B, int H, int N, int du) {
     const size_t a = 256;
+    auto up = [a](size_t x) { return (x + a - 1) / a * a; };
     const size_t nseg = (static_cast<size_t>(N) + kLogitSeg - 1) / kLogitSeg;
-    const size_t s = (static_cast<size_t>(B) * H * N * 4 + a - 1) / a * a;
-    const size_t u = (static_cast<size_t>(B) * H * nseg * du * 4 + a - 1) / a * a;
-    return s + u;
+    const size_t nch = (static_cast<size_t>(N) + kC - 1) / kC;
+    const size_t bh = static_cast<size_t>(B) * H;
+    return up(bh * N * 4) + up(bh * nseg * du * 4) + up(bh * nch * 16) + bh * nch * causal_rec_bytes(du);
 }
 
 CausalWork causal_work_carve(void *base, int B, int H, int N, int du) {
     const size_t a = 256;
-    const size_t s = (static_cast<size_t>(B) * H * N * 4 + a - 1) / a * a;
+    auto up = [a](size_t x) { return (x + a - 1) / a * a; };
+    const size_t nseg = (static_cast<size_t>(N) + kLogitSeg - 1) / kLogitSeg;
+    const size_t nch = (static_cast<size_t>(N) + kC - 1) / kC;
+    const size_t bh = static_cast<size_t>(B) * H;
+    char *b = static_cast<char *>(base);
     CausalWork w;
-    w.s = static_cast<float *>(base);
-    w.useg = reinterpret_cast<float *>(static_cast<char *>(base) + s);
-    (void)du;
+    w.s = reinterpret_cast<float *>(b);
+    b += up(bh * N * 4);
+    w.useg = reinterpret_cast<float *>(b);
+    b += up(bh * nseg * du * 4);
+    w.agg = reinterpret_cast<float4 *>(b);
+    b += up(bh * nch * 16);
+    w.rec = reinterpret_cast<unsigned char *>(b);
     return w;
 }
 
 hipError_t launch_causal_mfma(const Problem &p, const CausalWork &w, hipStream_t stream) {
-    hipError_t err = launch_logits(p, w.useg, w.s, stream);
+    hipError_t err = launch_logits(p, w.useg, w.s, w.agg, stream);
     if (err != hipSuccess) return err;
     if (p.d == 128) return p.rope ? launch_one<128, true>(p, w, stream) : launch_one<128, false>(p, w, stream);
     if (p.d == 64) return p.rope ? launch_one<64, true>(p, w, stream) : launch_one<64, false>(p, w, stream);

@@ -20,18 +20,22 @@ struct Problem {
     float rope_base;
 };
 
-// Tokens per segment of the two-pass logit computation.
+// Tokens per segment of the two-pass logit computation, and per chunk of the causal scan.
 constexpr int kLogitSeg = 512;
+constexpr int kCausalChunk = 64;
 
 // Workspace of the causal MFMA path, carved from one caller- or library-provided buffer.
 struct CausalWork {
-    float *s;       // [B*H, N] logits
-    float *useg;    // [B*H, nseg, d_u] per-segment u sums
+    float *s;           // [B*H, N] logits
+    float *useg;        // [B*H, nseg, d_u] per-segment u sums
+    float4 *agg;        // [B*H, nchunk] per-chunk (max s, sum e^{s-max}, sum s, 0)
+    unsigned char *rec; // [B*H, nchunk, rec_bytes(d)] per-chunk operands prepared for the scan
 };
+size_t causal_rec_bytes(int d);
 size_t causal_work_bytes(int B, int H, int N, int du);
 CausalWork causal_work_carve(void *base, int B, int H, int N, int du);
 
-hipError_t launch_logits(const Problem &p, float *useg, float *s_out, hipStream_t stream);
+hipError_t launch_logits(const Problem &p, float *useg, float *s_out, float4 *agg, hipStream_t stream);
 hipError_t launch_causal_mfma(const Problem &p, const CausalWork &w, hipStream_t stream);
 hipError_t launch_causal(const Problem &p, hipStream_t stream);
 hipError_t launch_encoder(const Problem &p, hipStream_t stream);

@@ -8,8 +8,8 @@
 //   pass 2 (logits_kernel):   per (head, segment), the running sum starts from e^tau mu plus
 //                             the sums of the earlier segments, then a lane-parallel scan over
 //                             64-token blocks gives ubar_i and s_i.
-// Output: s [B*H, N] float32 and the per-segment sums [B*H, nseg, d_u] (their total is the
-// u-sum of the recurrent state).
+// Output: s [B*H, N] float32, the per-segment sums [B*H, nseg, d_u] (their total is the u-sum of
+// the recurrent state) and, per 64-token chunk, (max s, sum e^{s - max}, sum s) [B*H, nchunk, 4].
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -99,8 +99,8 @@ __global__ __launch_bounds__(kThreads) void useg_sum_kernel(const T *u, float *u
 // [w*D/4, (w+1)*D/4). The running sum over the block is an inclusive lane scan per feature.
 template <int D, typename T>
 __global__ __launch_bounds__(kThreads) void logits_kernel(const T *u, const float *mu, const float *tau,
-                                                          const float *useg, float *s_out, int N, int H,
-                                                          int nseg) {
+                                                          const float *useg, float *s_out, float4 *agg,
+                                                          int N, int H, int nseg) {
     constexpr int DW = D / 4;                  // features per wave
     __shared__ float c0s[D];
     __shared__ float part[4][64];
@@ -143,16 +143,22 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(const T *u, const floa
 #pragma unroll
         for (int i = 0; i < DW; ++i) carry[i] = lane_f(S[i], 63);   // rows past r1 add zeros
         lds_barrier();
-        if (w == 0 && valid) {
+        if (w == 0) {
             const float tot = part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane];
-            s_out[static_cast<size_t>(bh) * N + row] = -tot * rs_du;
+            const float sv = -tot * rs_du;
+            if (valid) s_out[static_cast<size_t>(bh) * N + row] = sv;
+            // aggregates of this 64-token chunk (segments are whole chunks)
+            const float mx = lane_f(wave_scan_max(valid ? sv : kNegInf), 63);
+            const float se = lane_f(wave_scan_add(valid ? __expf(sv - mx) : 0.f), 63);
+            const float ss = lane_f(wave_scan_add(valid ? sv : 0.f), 63);
+            if (lane == 0) agg[static_cast<size_t>(bh) * ((N + 63) / 64) + b0 / 64] = make_float4(mx, se, ss, 0.f);
         }
         lds_barrier();
     }
 }
 
 template <int D, typename T>
-hipError_t launch_t(const Problem &p, float *useg, float *s_out, hipStream_t stream) {
+hipError_t launch_t(const Problem &p, float *useg, float *s_out, float4 *agg, hipStream_t stream) {
     const int nseg = (p.N + kLogitSeg - 1) / kLogitSeg;
     const int grid = p.B * p.H * nseg;
     hipLaunchKernelGGL((useg_sum_kernel<D, T>), dim3(grid), dim3(kThreads), 0, stream,
@@ -160,25 +166,25 @@ hipError_t launch_t(const Problem &p, float *useg, float *s_out, hipStream_t str
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL((logits_kernel<D, T>), dim3(grid), dim3(kThreads), 0, stream,
-                       static_cast<const T *>(p.u), p.mu, p.tau, useg, s_out, p.N, p.H, nseg);
+                       static_cast<const T *>(p.u), p.mu, p.tau, useg, s_out, agg, p.N, p.H, nseg);
     return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_d(const Problem &p, float *useg, float *s_out, hipStream_t stream) {
-    return p.dtype == ZEROS_BF16 ? launch_t<D, bf16>(p, useg, s_out, stream)
-                                 : launch_t<D, float>(p, useg, s_out, stream);
+hipError_t launch_d(const Problem &p, float *useg, float *s_out, float4 *agg, hipStream_t stream) {
+    return p.dtype == ZEROS_BF16 ? launch_t<D, bf16>(p, useg, s_out, agg, stream)
+                                 : launch_t<D, float>(p, useg, s_out, agg, stream);
 }
 
 }  // namespace
 
-hipError_t launch_logits(const Problem &p, float *useg, float *s_out, hipStream_t stream) {
+hipError_t launch_logits(const Problem &p, float *useg, float *s_out, float4 *agg, hipStream_t stream) {
     if (p.N == 0) return hipSuccess;
     switch (p.d) {
-        case 16: return launch_d<16>(p, useg, s_out, stream);
-        case 32: return launch_d<32>(p, useg, s_out, stream);
-        case 64: return launch_d<64>(p, useg, s_out, stream);
-        case 128: return launch_d<128>(p, useg, s_out, stream);
+        case 16: return launch_d<16>(p, useg, s_out, agg, stream);
+        case 32: return launch_d<32>(p, useg, s_out, agg, stream);
+        case 64: return launch_d<64>(p, useg, s_out, agg, stream);
+        case 128: return launch_d<128>(p, useg, s_out, agg, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -20,8 +20,9 @@
 // States are kept in a centred basis, X = F/E - H/t0 and Y = G - (P/t0) H. Both have zero-sum
 // weights, so they stay of the size of the output, and rounding them (and the update operands)
 // to bfloat16 for the MFMA is not amplified by the cancellation between alpha F, beta G and
-// gamma H. With RoPE, q and k are rotated by their offset inside the chunk and the states are
-// kept in the frame of the chunk start, re-based by a fixed rotation after every chunk.
+// gamma H. With RoPE, q^ and k^ are rotated by their absolute position (the angle of the chunk
+// start composed with the tabulated angle of the offset inside the chunk), so the carried states
+// are in the absolute frame and need no re-basing between chunks.
 #include <hip/hip_bf16.h>
 
 #include "device_common.hpp"
@@ -36,14 +37,18 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 constexpr int kC = 64;          // tokens per chunk
 constexpr int kTile = 16;       // value columns per workgroup
 constexpr int kPad = 8;         // bf16 elements of row padding in LDS
+constexpr int kRing = 3;        // chunks whose operands are in flight in the scan kernel
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Two floats to a packed bfloat16 pair (round to nearest even): one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-    __hip_bfloat162 h = __float22bfloat162_rn(make_float2(lo, hi));
-    return *reinterpret_cast<uint32_t *>(&h);
+    typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+    typedef float f32x2v __attribute__((ext_vector_type(2)));
+    const f32x2v f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v));
 }
 __device__ __forceinline__ float lo_f(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_f(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -203,8 +208,20 @@ struct alignas(16) PSmem {
     alignas(16) uint16_t qh[kC][D + kPad];     // unit (rotated) q rows, bf16
     alignas(16) uint16_t kh[kC][D + kPad];     // unit (rotated) k rows, 16-byte blocks swizzled
     Coef cf;
-    double rev[D / 2];                         // RoPE frequency of each feature pair, turns per position
+    float2 rot0[D / 2];                        // cos, sin of t0 * theta_j (chunk start)
 };
+
+// cos, sin of r * theta_j for the in-chunk offsets r in [0, kC) and feature pairs j in [0, D/2):
+// the rotations the prep kernel applies to q and k (every chunk uses the same table).
+template <int D>
+__global__ __launch_bounds__(256) void rope_table_kernel(float2 *tab, float base) {
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= kC * (D / 2)) return;
+    const int r = idx / (D / 2), j = idx % (D / 2);
+    float c, s;
+    rope_cos_sin(rope_rev_per_pos(j, D, base), r, c, s);
+    tab[idx] = make_float2(c, s);
+}
 
 template <int D, bool ROPE>
 __global__ __launch_bounds__(kPrepThreads) void causal_prep_kernel(Problem p, CausalWork work) {
@@ -227,7 +244,11 @@ __global__ __launch_bounds__(kPrepThreads) void causal_prep_kernel(Problem p, Ca
     unsigned char *rec = work.rec + (static_cast<size_t>(bh) * nch + c) * R::bytes;
 
     if (ROPE) {
-        if (tid < D / 2) sm.rev[tid] = rope_rev_per_pos(tid, D, p.rope_base);
+        if (tid < D / 2) {
+            float c0, s0;
+            rope_cos_sin(rope_rev_per_pos(tid, D, p.rope_base), t0, c0, s0);
+            sm.rot0[tid] = make_float2(c0, s0);
+        }
         __syncthreads();
     }
 
@@ -287,8 +308,10 @@ __global__ __launch_bounds__(kPrepThreads) void causal_prep_kernel(Problem p, Ca
                 const float q0 = lo_f(wq[b]), q1 = hi_f(wq[b]);
                 const float k0 = lo_f(wk[b]), k1 = hi_f(wk[b]);
                 if (ROPE) {
-                    float cs, sn;
-                    rope_cos_sin(sm.rev[f0 / 2 + 4 * a + b], lr, cs, sn);
+                    // angle of position t0 + lr = angle of t0 + angle of lr
+                    const int jp = f0 / 2 + 4 * a + b;
+                    const float2 tr = work.rope[lr * (D / 2) + jp], t0r = sm.rot0[jp];
+                    const float cs = t0r.x * tr.x - t0r.y * tr.y, sn = t0r.y * tr.x + t0r.x * tr.y;
                     const float cq = cs * iq, sq = sn * iq, ck = cs * ik, sk = sn * ik;
                     wq[b] = pack2(q0 * cq - q1 * sq, q0 * sq + q1 * cq);
                     wk[b] = pack2(k0 * ck - k1 * sk, k0 * sk + k1 * ck);
@@ -395,9 +418,11 @@ __global__ __launch_bounds__(kPrepThreads) void causal_prep_kernel(Problem p, Ca
 
 template <int D>
 struct alignas(16) MSmem {
-    alignas(16) uint16_t vt[kTile][kC + kPad]; // v tile, transposed: vt[m][token] (also the H update operand)
-    alignas(16) uint16_t vx[kTile][kC + kPad]; // update operands v * w_X and v * w_Y (transposed)
-    alignas(16) uint16_t vy[kTile][kC + kPad];
+    // v tile, transposed: vt[m][token] (also the H update operand), and the update operands
+    // v * w_X, v * w_Y (transposed); double-buffered, the next chunk is staged during this one
+    alignas(16) uint16_t vt[2][kTile][kC + kPad];
+    alignas(16) uint16_t vx[2][kTile][kC + kPad];
+    alignas(16) uint16_t vy[2][kTile][kC + kPad];
     alignas(16) uint16_t st[2][3][kTile][D + kPad];  // X, Y, H transposed, bf16, double-buffered
 };
 
@@ -410,7 +435,8 @@ __global__ __launch_bounds__(kMainThreads) void causal_main_kernel(Problem p, Ca
     constexpr int KS = D / 32;
     constexpr int RT = D / 64;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar branches
     const int l16 = lane & 15, g4 = lane >> 4;
     const bool qgroup = wave < 4;
     const int wb = wave & 3;
@@ -430,29 +456,16 @@ __global__ __launch_bounds__(kMainThreads) void causal_main_kernel(Problem p, Ca
     // staging coordinates: token lr of the chunk, value columns 2*p8 + {0, 1}
     const int lr = tid >> 3, p8 = tid & 7;
 
-    // rotation re-basing this update lane's state rows by -kC after each chunk
-    float fc[ROPE ? 2 * RT : 1], fs[ROPE ? 2 * RT : 1];
-    if (ROPE && !qgroup) {
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-            for (int pp = 0; pp < 2; ++pp) {
-                const int jp = 8 * (RT * wb + rt) + 2 * g4 + pp;
-                rope_cos_sin(rope_rev_per_pos(jp, D, p.rope_base), kC, fc[2 * rt + pp], fs[2 * rt + pp]);
-            }
-    }
-
     f32x4 X[RT], Y[RT], Hm[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) X[rt][i] = Y[rt][i] = Hm[rt][i] = 0.f;
 
-    // operands of the current chunk (loaded one chunk ahead)
-    // MFMA operands of a chunk, NOP 16-byte slots per lane, loaded one chunk ahead. Waves 0-3:
-    // slots 0..KS-1 = q^ (query block wb), KS, KS+1 = W (key-block pairs); waves 4-7: slots
-    // 0..2RT-1 = k^T (row tiles of wave wb-4, two key steps), the rest repeat slot 0. The loads
-    // are the same code in every wave, only the addresses differ.
+    // MFMA operands of a chunk, NOP 16-byte slots per lane. Waves 0-3: slots 0..KS-1 = q^ (query
+    // block wb), KS, KS+1 = W (key-block pairs); waves 4-7: slots 0..2RT-1 = k^T (row tiles of
+    // wave wb-4, two key steps), the rest repeat slot 0. The loads are the same code in every wave,
+    // only the addresses differ.
     constexpr int NOP = KS + 2;
     uint32_t opoff[NOP];
 #pragma unroll
@@ -462,60 +475,63 @@ __global__ __launch_bounds__(kMainThreads) void causal_main_kernel(Problem p, Ca
         else { const int j = i < 2 * RT ? i : 0; o = R::k_off + size_t((RT * wb + j / 2) * 2 + (j & 1)) * 1024; }
         opoff[i] = static_cast<uint32_t>(o + lane * 16);
     }
-    bf16x8 opn[NOP];
     // three scalars per lane: (cX, beta, kappa) of the lane's query in waves 0-3,
     // (rX, cHX, cHY) of the chunk in waves 4-7
     const int tq_lane = 16 * wb + l16;
     const int sc_off0 = qgroup ? kCoCX + tq_lane : kCoChunk + 0;
     const int sc_off1 = qgroup ? kCoBeta + tq_lane : kCoChunk + 1;
     const int sc_off2 = qgroup ? kCoKap + tq_lane : kCoChunk + 2;
-    float sc0 = 0.f, sc1 = 0.f, sc2 = 0.f;
-    uint32_t pv = 0;                            // v of token lr, columns 2*p8 (low) and 2*p8+1
-    bool pv_ok = false;                         // token lr exists (else pv is a stand-in row)
-    float2 wx2 = make_float2(0.f, 0.f), wy2 = wx2;  // w_X, w_Y of tokens (lr & ~1), (lr | 1)
     const int tok_lane = lr & ~1;
     const size_t vcol = static_cast<size_t>(tile) * kTile + 2 * p8;
-#define ZEROS_LOAD_CHUNK(c)                                                                              \
-    do {                                                                                                 \
-        const unsigned char *rec_ = rec0 + static_cast<size_t>(c) * R::bytes;                          \
-        const float *co_ = reinterpret_cast<const float *>(rec_ + R::c_off);                            \
-        _Pragma("unroll") for (int i = 0; i < NOP; ++i) opn[i] = ld16(rec_ + opoff[i]);                  \
-        sc0 = co_[sc_off0];                                                                              \
-        sc1 = co_[sc_off1];                                                                              \
-        sc2 = co_[sc_off2];                                                                              \
-        const int tok_ = (c) * kC + lr;     /* rows past N read row N-1 (in bounds), then zeroed */     \
-        const uint32_t raw_ = *reinterpret_cast<const uint32_t *>(vg + static_cast<size_t>(min(tok_, N - 1)) * D + vcol); \
-        pv = raw_;                                                                                       \
-        pv_ok = tok_ < N;                   /* applied when staging, so the load is not waited for */   \
-        wx2 = *reinterpret_cast<const float2 *>(co_ + kCoWX + tok_lane);                                 \
-        wy2 = *reinterpret_cast<const float2 *>(co_ + kCoWY + tok_lane);                                 \
-    } while (0)
 
-    if (N > 0) ZEROS_LOAD_CHUNK(0);
-    for (int t0 = 0, ci = 0; t0 < N; t0 += kC, ++ci) {
-        const int nval = min(kC, N - t0);
-
-        // ---- stage the v tile (transposed token pairs) and its update operands
-        {
-            const uint32_t pvv = pv_ok ? pv : 0u;
-            const uint32_t other = static_cast<uint32_t>(
-                __builtin_amdgcn_update_dpp(0, static_cast<int>(pvv), kRowRor + 8, 0xf, 0xf, false));
-            const bool odd = lr & 1;
-            const uint32_t pair = odd ? ((other >> 16) | (pvv & 0xffff0000u)) : ((pvv & 0xffffu) | (other << 16));
-            const int col = 2 * p8 + (odd ? 1 : 0), tok = lr & ~1;
-            const float v0 = lo_f(pair), v1 = hi_f(pair);
-            *reinterpret_cast<uint32_t *>(&sm.vt[col][tok]) = pair;
-            *reinterpret_cast<uint32_t *>(&sm.vx[col][tok]) = pack2(v0 * wx2.x, v1 * wx2.y);
-            *reinterpret_cast<uint32_t *>(&sm.vy[col][tok]) = pack2(v0 * wy2.x, v1 * wy2.y);
-        }
-        // keep this chunk's operands, fetch the next chunk's
-        bf16x8 opc[NOP];
+    // Everything one chunk needs from memory, per lane. The record and v of chunk c are read
+    // kRing chunks before c is processed (a ring of register slots, the loop unrolled by kRing),
+    // so that the latency of the first touch of a record line is covered by the work of the
+    // chunks in between.
+    struct Slot {
+        bf16x8 op[NOP];
+        float sc0, sc1, sc2;
+        uint32_t pv;           // v of token lr, columns 2*p8 (low) and 2*p8+1
+        bool pv_ok;            // token lr exists (else pv is a stand-in row)
+        float2 wx2, wy2;       // w_X, w_Y of tokens (lr & ~1), (lr | 1)
+    };
+    auto load = [&](Slot &sl, const int c) __attribute__((always_inline)) {
+        const unsigned char *rec_ = rec0 + static_cast<size_t>(c) * R::bytes;
+        const float *co_ = reinterpret_cast<const float *>(rec_ + R::c_off);
 #pragma unroll
-        for (int i = 0; i < NOP; ++i) opc[i] = opn[i];
-        const float s0c = sc0, s1c = sc1, s2c = sc2;
-        lds_barrier();
-        if (t0 + kC < N) ZEROS_LOAD_CHUNK(ci + 1);
+        for (int i = 0; i < NOP; ++i) sl.op[i] = ld16(rec_ + opoff[i]);
+        sl.sc0 = co_[sc_off0];
+        sl.sc1 = co_[sc_off1];
+        sl.sc2 = co_[sc_off2];
+        const int tok_ = c * kC + lr;       // rows past N read row N-1 (in bounds), then zeroed
+        sl.pv = *reinterpret_cast<const uint32_t *>(vg + static_cast<size_t>(min(tok_, N - 1)) * D + vcol);
+        sl.pv_ok = tok_ < N;                // applied when staging, so the load is not waited for
+        sl.wx2 = *reinterpret_cast<const float2 *>(co_ + kCoWX + tok_lane);
+        sl.wy2 = *reinterpret_cast<const float2 *>(co_ + kCoWY + tok_lane);
+    };
 
+    // stage the v tile of a chunk (transposed token pairs) and its update operands into buffer b
+    auto stage = [&](const Slot &sl, const int b) __attribute__((always_inline)) {
+        const uint32_t pvv = sl.pv_ok ? sl.pv : 0u;
+        const uint32_t other = static_cast<uint32_t>(
+            __builtin_amdgcn_update_dpp(0, static_cast<int>(pvv), kRowRor + 8, 0xf, 0xf, false));
+        const bool odd = lr & 1;
+        const uint32_t pair = odd ? ((other >> 16) | (pvv & 0xffff0000u)) : ((pvv & 0xffffu) | (other << 16));
+        const int col = 2 * p8 + (odd ? 1 : 0), tok = lr & ~1;
+        const float v0 = lo_f(pair), v1 = hi_f(pair);
+        *reinterpret_cast<uint32_t *>(&sm.vt[b][col][tok]) = pair;
+        *reinterpret_cast<uint32_t *>(&sm.vx[b][col][tok]) = pack2(v0 * sl.wx2.x, v1 * sl.wx2.y);
+        *reinterpret_cast<uint32_t *>(&sm.vy[b][col][tok]) = pack2(v0 * sl.wy2.x, v1 * sl.wy2.y);
+    };
+
+    // One chunk: compute with slot sl (chunk ci, staged in buffer ci & 1), stage chunk ci + 1 from
+    // slot nx into the other buffer, refill sl, then a single barrier.
+    auto body = [&](Slot &sl, const Slot &nx, const int ci) __attribute__((always_inline)) {
+        const int t0 = ci * kC;
+        const int nval = min(kC, N - t0);
+        const int vb = ci & 1;
+
+        const float s0c = sl.sc0, s1c = sl.sc1, s2c = sl.sc2;
         if (qgroup) {
             const int tb = wb;
             const int tq = 16 * tb + l16;
@@ -525,10 +541,10 @@ __global__ __launch_bounds__(kMainThreads) void causal_main_kernel(Problem p, Ca
             for (int pi = 0; pi < 2; ++pi) {
                 if (2 * pi > tb) continue;
                 const int kb0 = 2 * pi, kb1 = 2 * pi + 1;
-                const uint2 va = *reinterpret_cast<const uint2 *>(&sm.vt[l16][16 * kb0 + 4 * g4]);
-                const uint2 vb = (kb1 <= tb) ? *reinterpret_cast<const uint2 *>(&sm.vt[l16][16 * kb1 + 4 * g4])
+                const uint2 va = *reinterpret_cast<const uint2 *>(&sm.vt[vb][l16][16 * kb0 + 4 * g4]);
+                const uint2 vc = (kb1 <= tb) ? *reinterpret_cast<const uint2 *>(&sm.vt[vb][l16][16 * kb1 + 4 * g4])
                                              : make_uint2(0, 0);
-                oacc = mfma(as_bf16x8(va.x, va.y, vb.x, vb.y), opc[KS + pi], oacc);
+                oacc = mfma(as_bf16x8(va.x, va.y, vc.x, vc.y), sl.op[KS + pi], oacc);
             }
             // carried states
             if (t0 > 0) {
@@ -536,9 +552,9 @@ __global__ __launch_bounds__(kMainThreads) void causal_main_kernel(Problem p, Ca
                 f32x4 ax = {0.f, 0.f, 0.f, 0.f}, ay = ax, ah = ax;
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    ax = mfma(*reinterpret_cast<const bf16x8 *>(&sm.st[sb][0][l16][32 * ks + 8 * g4]), opc[ks], ax);
-                    ay = mfma(*reinterpret_cast<const bf16x8 *>(&sm.st[sb][1][l16][32 * ks + 8 * g4]), opc[ks], ay);
-                    ah = mfma(*reinterpret_cast<const bf16x8 *>(&sm.st[sb][2][l16][32 * ks + 8 * g4]), opc[ks], ah);
+                    ax = mfma(*reinterpret_cast<const bf16x8 *>(&sm.st[sb][0][l16][32 * ks + 8 * g4]), sl.op[ks], ax);
+                    ay = mfma(*reinterpret_cast<const bf16x8 *>(&sm.st[sb][1][l16][32 * ks + 8 * g4]), sl.op[ks], ay);
+                    ah = mfma(*reinterpret_cast<const bf16x8 *>(&sm.st[sb][2][l16][32 * ks + 8 * g4]), sl.op[ks], ah);
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) oacc[i] += s0c * ax[i] + s1c * ay[i] + s2c * ah[i];   // cX, beta, kappa
@@ -547,7 +563,7 @@ __global__ __launch_bounds__(kMainThreads) void causal_main_kernel(Problem p, Ca
                 const uint2 ov = make_uint2(pack2(oacc[0], oacc[1]), pack2(oacc[2], oacc[3]));
                 *reinterpret_cast<uint2 *>(og + static_cast<size_t>(t0 + tq) * D + tile * kTile + 4 * g4) = ov;
             }
-        } else {
+        } else if (ci < nch) {              // padding chunks past the end leave the states alone
             if (t0 > 0) {
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
@@ -560,30 +576,15 @@ __global__ __launch_bounds__(kMainThreads) void causal_main_kernel(Problem p, Ca
 #pragma unroll
             for (int ks2 = 0; ks2 < kC / 32; ++ks2) {
                 const int kk0 = 32 * ks2 + 8 * g4;
-                const bf16x8 BX = *reinterpret_cast<const bf16x8 *>(&sm.vx[l16][kk0]);
-                const bf16x8 BY = *reinterpret_cast<const bf16x8 *>(&sm.vy[l16][kk0]);
-                const bf16x8 BH = *reinterpret_cast<const bf16x8 *>(&sm.vt[l16][kk0]);
+                const bf16x8 BX = *reinterpret_cast<const bf16x8 *>(&sm.vx[vb][l16][kk0]);
+                const bf16x8 BY = *reinterpret_cast<const bf16x8 *>(&sm.vy[vb][l16][kk0]);
+                const bf16x8 BH = *reinterpret_cast<const bf16x8 *>(&sm.vt[vb][l16][kk0]);
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) {
-                    X[rt] = mfma(opc[2 * rt + ks2], BX, X[rt]);
-                    Y[rt] = mfma(opc[2 * rt + ks2], BY, Y[rt]);
-                    Hm[rt] = mfma(opc[2 * rt + ks2], BH, Hm[rt]);
+                    X[rt] = mfma(sl.op[2 * rt + ks2], BX, X[rt]);
+                    Y[rt] = mfma(sl.op[2 * rt + ks2], BY, Y[rt]);
+                    Hm[rt] = mfma(sl.op[2 * rt + ks2], BH, Hm[rt]);
                 }
-            }
-            if (ROPE) {
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-                    for (int pp = 0; pp < 2; ++pp) {
-                        const float c = fc[2 * rt + pp], sn = fs[2 * rt + pp];
-                        const int i0 = 2 * pp, i1 = i0 + 1;
-                        float x0 = X[rt][i0], x1 = X[rt][i1];
-                        X[rt][i0] = x0 * c + x1 * sn; X[rt][i1] = x1 * c - x0 * sn;
-                        x0 = Y[rt][i0]; x1 = Y[rt][i1];
-                        Y[rt][i0] = x0 * c + x1 * sn; Y[rt][i1] = x1 * c - x0 * sn;
-                        x0 = Hm[rt][i0]; x1 = Hm[rt][i1];
-                        Hm[rt][i0] = x0 * c + x1 * sn; Hm[rt][i1] = x1 * c - x0 * sn;
-                    }
             }
             const int nb = (ci + 1) & 1;        // the query waves read st[ci & 1] meanwhile
 #pragma unroll
@@ -594,12 +595,36 @@ __global__ __launch_bounds__(kMainThreads) void causal_main_kernel(Problem p, Ca
                 *reinterpret_cast<uint2 *>(&sm.st[nb][2][l16][jc]) = make_uint2(pack2(Hm[rt][0], Hm[rt][1]), pack2(Hm[rt][2], Hm[rt][3]));
             }
         }
-        lds_barrier();            // chunk done: staging and the state buffer may be replaced
+        stage(nx, vb ^ 1);
+        // this slot is consumed: refill it with the chunk kRing ahead. The load is unconditional
+        // (past the end it repeats the last chunk) so that the wait before each use of a slot is
+        // a fixed count of younger loads and the other slots stay in flight.
+        load(sl, min(ci + kRing, nch - 1));
+        lds_barrier();            // chunk done: next staging and states visible, old buffers free
+    };
+
+    Slot s0, s1, s2;
+    static_assert(kRing == 3, "the loop below is unrolled for a ring of three slots");
+    if (nch > 0) {
+        // issued in slot order (the empty asm keeps the compiler from reordering them), so that
+        // slot 0 is the oldest at the loop entry as it is on every later iteration
+        load(s0, 0);
+        asm volatile("" ::: "memory");
+        load(s1, min(1, nch - 1));
+        asm volatile("" ::: "memory");
+        load(s2, min(2, nch - 1));
+        asm volatile("" ::: "memory");
+        stage(s0, 0);
+        lds_barrier();
+        // whole groups of kRing chunks; a chunk index past the end stores nothing (nval <= 0)
+        for (int ci = 0; ci < nch; ci += kRing) {
+            body(s0, s1, ci);
+            body(s1, s2, ci + 1);
+            body(s2, s0, ci + 2);
+        }
     }
 
-#undef ZEROS_LOAD_CHUNK
-
-    // ---- final state (update waves): back to F = E (X + H/t), G = Y + (P/t) H, absolute RoPE frame
+    // ---- final state (update waves): back to F = E (X + H/t), G = Y + (P/t) H
     if (p.st.F != nullptr) {
         float m0 = kNegInf, E0 = 0.f, P0 = 0.f;
         if (N > 0) {
@@ -620,21 +645,6 @@ __global__ __launch_bounds__(kMainThreads) void causal_main_kernel(Problem p, Ca
                     F[i] = N > 0 ? E0 * (X[rt][i] + hh / tf) : 0.f;
                     Gv[i] = N > 0 ? Y[rt][i] + (P0 / tf) * hh : 0.f;
                     Hv[i] = hh;
-                }
-                if (ROPE && N > 0) {
-#pragma unroll
-                    for (int pp = 0; pp < 2; ++pp) {
-                        const int jp = 8 * (RT * wb + rt) + 2 * g4 + pp;
-                        float c, sn;
-                        rope_cos_sin(rope_rev_per_pos(jp, D, p.rope_base), nch * kC, c, sn);
-                        const int i0 = 2 * pp, i1 = i0 + 1;
-                        float x0 = F[i0], x1 = F[i1];
-                        F[i0] = x0 * c - x1 * sn; F[i1] = x0 * sn + x1 * c;
-                        x0 = Gv[i0]; x1 = Gv[i1];
-                        Gv[i0] = x0 * c - x1 * sn; Gv[i1] = x0 * sn + x1 * c;
-                        x0 = Hv[i0]; x1 = Hv[i1];
-                        Hv[i0] = x0 * c - x1 * sn; Hv[i1] = x0 * sn + x1 * c;
-                    }
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -679,6 +689,12 @@ hipError_t launch_one(const Problem &p, const CausalWork &w, hipStream_t stream)
         attr_set = true;
     }
     const int nch = (p.N + kC - 1) / kC;
+    if (ROPE && nch > 0) {
+        hipLaunchKernelGGL((rope_table_kernel<D>), dim3((kC * (D / 2) + 255) / 256), dim3(256), 0, stream,
+                           w.rope, p.rope_base);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
     if (nch > 0) {
         hipLaunchKernelGGL((causal_prep_kernel<D, ROPE>), dim3(p.B * p.H * nch), dim3(kPrepThreads),
                            sizeof(PSmem<D>), stream, p, w);
@@ -700,7 +716,8 @@ size_t causal_work_bytes(int B, int H, int N, int du) {
     const size_t nseg = (static_cast<size_t>(N) + kLogitSeg - 1) / kLogitSeg;
     const size_t nch = (static_cast<size_t>(N) + kC - 1) / kC;
     const size_t bh = static_cast<size_t>(B) * H;
-    return up(bh * N * 4) + up(bh * nseg * du * 4) + up(bh * nch * 16) + bh * nch * causal_rec_bytes(du);
+    return up(bh * N * 4) + up(bh * nseg * du * 4) + up(bh * nch * 16) + up(size_t(kC) * (du / 2) * 8) +
+           bh * nch * causal_rec_bytes(du);
 }
 
 CausalWork causal_work_carve(void *base, int B, int H, int N, int du) {
@@ -717,6 +734,8 @@ CausalWork causal_work_carve(void *base, int B, int H, int N, int du) {
     b += up(bh * nseg * du * 4);
     w.agg = reinterpret_cast<float4 *>(b);
     b += up(bh * nch * 16);
+    w.rope = reinterpret_cast<float2 *>(b);
+    b += up(size_t(kC) * (du / 2) * 8);
     w.rec = reinterpret_cast<unsigned char *>(b);
     return w;
 }

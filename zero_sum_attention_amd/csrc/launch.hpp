@@ -29,6 +29,7 @@ struct CausalWork {
     float *s;           // [B*H, N] logits
     float *useg;        // [B*H, nseg, d_u] per-segment u sums
     float4 *agg;        // [B*H, nchunk] per-chunk (max s, sum e^{s-max}, sum s, 0)
+    float2 *rope;       // [kCausalChunk, d/2] cos, sin of r * theta_j (RoPE only)
     unsigned char *rec; // [B*H, nchunk, rec_bytes(d)] per-chunk operands prepared for the scan
 };
 size_t causal_rec_bytes(int d);

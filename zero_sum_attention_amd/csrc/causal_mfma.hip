@@ -12,11 +12,13 @@
 //   chunk's scalar scan and coefficients, unit (RoPE-rotated) q^ and k^, A^T = K Q^T on MFMA and
 //   the intra-chunk weights W_{t,i} = A (a_t e^{s_i-m_t} + b_t s_i + g_t), i <= t. It writes them
 //   to a per-chunk record already laid out as MFMA operands (q^, k^T, W) plus the coefficients.
-// causal_main_kernel, one workgroup of 8 waves per (batch, head, 16-column tile of v/o), walks the
-//   chunks in order. Waves 0-3 (queries [16w, 16w+16)): o^T = V^T W^T + q^-weighted carried
-//   states, on MFMA. Waves 4-7 (state rows [(w-4) d/4, (w-3) d/4)): X, Y, H advanced to the chunk
-//   end, K^T V' on MFMA. The W accumulator layout of the prep kernel is the B-operand layout of
-//   V^T W^T up to a permutation of the contraction index, which V^T is read with.
+// causal_seg_kernel, one workgroup of d/16 waves per (batch, head, segment of the chunks), walks
+//   its chunks in order; wave w owns value columns [16w, 16w+16) and all d rows of X, Y, H in
+//   float32 registers. Per chunk: o^T = S^T Q^T (carried states, S^T straight from the registers)
+//   + V^T W^T (intra-chunk), then the states advance to the chunk end with K^T V' on MFMA. The W
+//   accumulator layout of the prep kernel is the B-operand layout of V^T W^T up to a permutation
+//   of the contraction index, which V^T is read with. Segments are chained exactly by a pass over
+//   each segment from a zero state and a combine step (see the segment-parallel scan below).
 // States are kept in a centred basis, X = F/E - H/t0 and Y = G - (P/t0) H. Both have zero-sum
 // weights, so they stay of the size of the output, and rounding them (and the update operands)
 // to bfloat16 for the MFMA is not amplified by the cancellation between alpha F, beta G and
@@ -37,7 +39,6 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 constexpr int kC = 64;          // tokens per chunk
 constexpr int kTile = 16;       // value columns per workgroup
 constexpr int kPad = 8;         // bf16 elements of row padding in LDS
-constexpr int kRing = 3;        // chunks whose operands are in flight in the scan kernel
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -185,23 +186,21 @@ __device__ __forceinline__ void chunk_scan(Coef &cf, int lane, int t0, int nval,
 // [ Q^ operands  : 4 query blocks x KS k-steps x 64 lanes x 16 B ]
 // [ K^T operands : d/16 row tiles x 2 key steps x 64 lanes x 16 B ]
 // [ W operands   : 4 query blocks x 2 key-block pairs x 64 lanes x 16 B ]
-// [ coefficients : cX, beta, kappa per query; w_X, w_Y per key; rX, cHX, cHY, m1, E1, P1 ]
-constexpr int kCoefFloats = 5 * kC + 8;
+// [ coefficients : (cX, beta, kappa, 0) per query; (w_X, w_Y) per key; rX, cHX, cHY, m1, E1, P1 ]
 template <int D> struct Rec {
     static constexpr int KS = D / 32;
     static constexpr size_t q_off = 0;
     static constexpr size_t k_off = q_off + size_t(4) * KS * 1024;
     static constexpr size_t w_off = k_off + size_t(D / 16) * 2 * 1024;
     static constexpr size_t c_off = w_off + size_t(8) * 1024;
-    static constexpr size_t bytes = c_off + 1536;
+    static constexpr size_t bytes = c_off + (6 * kC + 8) * 4;
 };
-enum { kCoCX = 0, kCoBeta = kC, kCoKap = 2 * kC, kCoWX = 3 * kC, kCoWY = 4 * kC, kCoChunk = 5 * kC };
+enum { kCoQ = 0, kCoW = 4 * kC, kCoChunk = 6 * kC };   // float offsets in the coefficient block
 
 __device__ __forceinline__ void st16(unsigned char *p, const bf16x8 &v) { *reinterpret_cast<bf16x8 *>(p) = v; }
 __device__ __forceinline__ bf16x8 ld16(const unsigned char *p) { return *reinterpret_cast<const bf16x8 *>(p); }
 
 constexpr int kPrepThreads = 256;
-constexpr int kMainThreads = 512;
 
 template <int D>
 struct alignas(16) PSmem {
@@ -335,7 +334,11 @@ __global__ __launch_bounds__(kPrepThreads) void causal_prep_kernel(Problem p, Ca
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             qop[ks] = *reinterpret_cast<const bf16x8 *>(&sm.qh[16 * tb + l16][32 * ks + 8 * g4]);
-            st16(rec + R::q_off + (size_t(tb * KS + ks) * 64 + lane) * 16, qop[ks]);
+            // the record holds features {32ks + 4g4 + i, 32ks + 16 + 4g4 + i}, i < 4: the order in
+            // which a lane of the scan kernel holds the rows of two 16-row state accumulator tiles
+            const uint2 qa = *reinterpret_cast<const uint2 *>(&sm.qh[16 * tb + l16][32 * ks + 4 * g4]);
+            const uint2 qc = *reinterpret_cast<const uint2 *>(&sm.qh[16 * tb + l16][32 * ks + 16 + 4 * g4]);
+            st16(rec + R::q_off + (size_t(tb * KS + ks) * 64 + lane) * 16, as_bf16x8(qa.x, qa.y, qc.x, qc.y));
         }
         f32x4 at[4];
 #pragma unroll
@@ -404,228 +407,275 @@ __global__ __launch_bounds__(kPrepThreads) void causal_prep_kernel(Problem p, Ca
     // ---- coefficients used by the main kernel
     if (tid < kC) {
         float *co = reinterpret_cast<float *>(rec + R::c_off);
-        co[kCoCX + tid] = sm.cf.qcx[tid];
-        co[kCoBeta + tid] = sm.cf.qb[tid];
-        co[kCoKap + tid] = sm.cf.qkap[tid];
-        co[kCoWX + tid] = sm.cf.wx[tid];
-        co[kCoWY + tid] = sm.cf.wy[tid];
-        if (tid < 6) {
-            const int src[6] = {3, 4, 5, 0, 1, 2};   // rX, cHX, cHY, m1, E1, P1
-            co[kCoChunk + tid] = sm.cf.chunk[src[tid]];
+        *reinterpret_cast<float4 *>(co + kCoQ + 4 * tid) = make_float4(sm.cf.qcx[tid], sm.cf.qb[tid], sm.cf.qkap[tid], 0.f);
+        *reinterpret_cast<float2 *>(co + kCoW + 2 * tid) = make_float2(sm.cf.wx[tid], sm.cf.wy[tid]);
+        if (tid < 8) {
+            const int src[8] = {3, 4, 5, 0, 1, 2, 7, 7};   // rX, cHX, cHY, m1, E1, P1, 0, 0
+            co[kCoChunk + tid] = tid < 6 ? sm.cf.chunk[src[tid]] : 0.f;
         }
     }
 }
 
+// ---- segment-parallel scan ----------------------------------------------------------------
+//
+// The chunks of a head are cut into nseg segments of seg_chunks chunks. One workgroup of D/16 waves
+// owns a whole head (wave w: value columns [16w, 16w+16), all D state rows of X, Y, H in float32
+// registers) for one segment, so every record chunk is read once per head.
+//
+// Within a segment the per-chunk recurrence of the centred states is affine:
+//   X <- rX X + cHX H + dX,   Y <- Y + cHY H + dY,   H <- H + dH        (d: the chunk's K^T V')
+// so the state at the end of a segment is M (state at its start) + L, where L is the recurrence run
+// from zero over the segment and M composes the scalar maps: X <- Rs X + Hs H, Y <- Y + Ys H.
+//   pass 1 (PASS1 = true), segments 0 .. nseg-2: L and (Rs, Hs, Ys);
+//   combine: start states of segments 1 .. nseg-1, in order, in float32;
+//   main (PASS1 = false), every segment: from its start state, outputs of its chunks (and the final
+//   recurrent state in the last segment).
+// The float32 arithmetic is the sequential recurrence reassociated at segment boundaries.
+
+// Segment states are stored in accumulator order: float4 index ((s * D/16 + jb) * D/16 + w) * 64 +
+// lane holds rows 16 jb + 4 (lane >> 4) + i, i < 4, column 16 w + (lane & 15) of state s (X, Y, H).
+template <int D> constexpr size_t kSegFloats = size_t(3) * D * D;
+
 template <int D>
-struct alignas(16) MSmem {
-    // v tile, transposed: vt[m][token] (also the H update operand), and the update operands
-    // v * w_X, v * w_Y (transposed); double-buffered, the next chunk is staged during this one
-    alignas(16) uint16_t vt[2][kTile][kC + kPad];
-    alignas(16) uint16_t vx[2][kTile][kC + kPad];
-    alignas(16) uint16_t vy[2][kTile][kC + kPad];
-    alignas(16) uint16_t st[2][3][kTile][D + kPad];  // X, Y, H transposed, bf16, double-buffered
+struct alignas(16) SSmem {
+    alignas(16) unsigned char rec[2][Rec<D>::bytes];       // record of the current and next chunk
+    // per wave: its v tile transposed, vt[m][token] (also the H update operand), and the update
+    // operands v * w_X, v * w_Y, transposed
+    alignas(16) uint16_t vt[D / 16][kTile][kC + kPad];
+    alignas(16) uint16_t vx[D / 16][kTile][kC + kPad];
+    alignas(16) uint16_t vy[D / 16][kTile][kC + kPad];
 };
 
-template <int D, bool ROPE>
-__global__ __launch_bounds__(kMainThreads) void causal_main_kernel(Problem p, CausalWork work) {
+template <int D, bool ROPE, bool PASS1>
+__global__ __launch_bounds__(D * 4) void causal_seg_kernel(Problem p, CausalWork work) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
-    MSmem<D> &sm = *reinterpret_cast<MSmem<D> *>(smem_raw);
+    SSmem<D> &sm = *reinterpret_cast<SSmem<D> *>(smem_raw);
     using R = Rec<D>;
-    constexpr int NTILE = D / kTile;
-    constexpr int KS = D / 32;
-    constexpr int RT = D / 64;
+    constexpr int NW = D / 16;          // waves
+    constexpr int NT = NW * 64;
+    constexpr int KS = D / 32;          // 32-feature steps of the carried-state products
+    constexpr int JB = D / 16;          // 16-row state tiles
+    constexpr int NREC = (int(R::bytes / 16) + NT - 1) / NT;   // 16-byte record pieces per thread
 
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar branches
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g4 = lane >> 4;
-    const bool qgroup = wave < 4;
-    const int wb = wave & 3;
-
-    const int G = gridDim.x;
-    int L = blockIdx.x;
-    if ((G & 7) == 0) L = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
-    const int tile = L % NTILE;
-    const int bh = L / NTILE;
+    const int nseg = work.nseg;
+    const int seg = blockIdx.x % (PASS1 ? nseg - 1 : nseg);
+    const int bh = blockIdx.x / (PASS1 ? nseg - 1 : nseg);
     const int N = p.N;
     const int nch = (N + kC - 1) / kC;
+    const int c_begin = seg * work.seg_chunks;
+    const int c_end = min(nch, c_begin + work.seg_chunks);
     const size_t row0 = static_cast<size_t>(bh) * N;
     const uint16_t *vg = static_cast<const uint16_t *>(p.v) + row0 * D;
     uint16_t *og = static_cast<uint16_t *>(p.o) + row0 * D;
     const unsigned char *rec0 = work.rec + static_cast<size_t>(bh) * nch * R::bytes;
 
-    // staging coordinates: token lr of the chunk, value columns 2*p8 + {0, 1}
-    const int lr = tid >> 3, p8 = tid & 7;
-
-    f32x4 X[RT], Y[RT], Hm[RT];
+    // state of this wave's columns: X, Y, H rows 16 jb + 4 g4 + i, column 16 w + l16
+    f32x4 X[JB], Y[JB], Hm[JB];
+    const size_t sidx = static_cast<size_t>(w) * 64 + lane;       // float4 index inside a (s, jb) block
+    if (!PASS1 && seg > 0) {
+        const float4 *st0 = reinterpret_cast<const float4 *>(work.segst + (static_cast<size_t>(bh) * (nseg - 1) + seg - 1) * kSegFloats<D>);
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+        for (int jb = 0; jb < JB; ++jb) {
+            const float4 a = st0[(size_t(0 * JB + jb) * NW) * 64 + sidx];
+            const float4 b = st0[(size_t(1 * JB + jb) * NW) * 64 + sidx];
+            const float4 c = st0[(size_t(2 * JB + jb) * NW) * 64 + sidx];
+            X[jb] = f32x4{a.x, a.y, a.z, a.w};
+            Y[jb] = f32x4{b.x, b.y, b.z, b.w};
+            Hm[jb] = f32x4{c.x, c.y, c.z, c.w};
+        }
+    } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) X[rt][i] = Y[rt][i] = Hm[rt][i] = 0.f;
-
-    // MFMA operands of a chunk, NOP 16-byte slots per lane. Waves 0-3: slots 0..KS-1 = q^ (query
-    // block wb), KS, KS+1 = W (key-block pairs); waves 4-7: slots 0..2RT-1 = k^T (row tiles of
-    // wave wb-4, two key steps), the rest repeat slot 0. The loads are the same code in every wave,
-    // only the addresses differ.
-    constexpr int NOP = KS + 2;
-    uint32_t opoff[NOP];
+        for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
-    for (int i = 0; i < NOP; ++i) {
-        size_t o;
-        if (qgroup) o = i < KS ? R::q_off + size_t(wb * KS + i) * 1024 : R::w_off + size_t(wb * 2 + i - KS) * 1024;
-        else { const int j = i < 2 * RT ? i : 0; o = R::k_off + size_t((RT * wb + j / 2) * 2 + (j & 1)) * 1024; }
-        opoff[i] = static_cast<uint32_t>(o + lane * 16);
+            for (int i = 0; i < 4; ++i) X[jb][i] = Y[jb][i] = Hm[jb][i] = 0.f;
     }
-    // three scalars per lane: (cX, beta, kappa) of the lane's query in waves 0-3,
-    // (rX, cHX, cHY) of the chunk in waves 4-7
-    const int tq_lane = 16 * wb + l16;
-    const int sc_off0 = qgroup ? kCoCX + tq_lane : kCoChunk + 0;
-    const int sc_off1 = qgroup ? kCoBeta + tq_lane : kCoChunk + 1;
-    const int sc_off2 = qgroup ? kCoKap + tq_lane : kCoChunk + 2;
-    const int tok_lane = lr & ~1;
-    const size_t vcol = static_cast<size_t>(tile) * kTile + 2 * p8;
+    float Rs = 1.f, Hs = 0.f, Ys = 0.f;   // composed scalar map of the segment (pass 1)
 
-    // Everything one chunk needs from memory, per lane. The record and v of chunk c are read
-    // kRing chunks before c is processed (a ring of register slots, the loop unrolled by kRing),
-    // so that the latency of the first touch of a record line is covered by the work of the
-    // chunks in between.
-    struct Slot {
-        bf16x8 op[NOP];
-        float sc0, sc1, sc2;
-        uint32_t pv;           // v of token lr, columns 2*p8 (low) and 2*p8+1
-        bool pv_ok;            // token lr exists (else pv is a stand-in row)
-        float2 wx2, wy2;       // w_X, w_Y of tokens (lr & ~1), (lr | 1)
-    };
-    auto load = [&](Slot &sl, const int c) __attribute__((always_inline)) {
-        const unsigned char *rec_ = rec0 + static_cast<size_t>(c) * R::bytes;
-        const float *co_ = reinterpret_cast<const float *>(rec_ + R::c_off);
-#pragma unroll
-        for (int i = 0; i < NOP; ++i) sl.op[i] = ld16(rec_ + opoff[i]);
-        sl.sc0 = co_[sc_off0];
-        sl.sc1 = co_[sc_off1];
-        sl.sc2 = co_[sc_off2];
-        const int tok_ = c * kC + lr;       // rows past N read row N-1 (in bounds), then zeroed
-        sl.pv = *reinterpret_cast<const uint32_t *>(vg + static_cast<size_t>(min(tok_, N - 1)) * D + vcol);
-        sl.pv_ok = tok_ < N;                // applied when staging, so the load is not waited for
-        sl.wx2 = *reinterpret_cast<const float2 *>(co_ + kCoWX + tok_lane);
-        sl.wy2 = *reinterpret_cast<const float2 *>(co_ + kCoWY + tok_lane);
-    };
+    // v of this wave's columns: lane holds tokens 2 (lane & 31), +1 and columns 8 (lane >> 5) + [0, 8)
+    const int vtok = 2 * (lane & 31), vh = lane >> 5;
+    const size_t vcol = static_cast<size_t>(w) * kTile + 8 * vh;
+    // record pieces tid + i * NT of a chunk (clamped to the last piece, so every load is issued)
+    // and this wave's v rows, read one chunk ahead
+    uint4 rq0, rq1, rq2, rq3, rq4, rq5, rq6;
+    static_assert(NREC <= 7, "record larger than seven 16-byte pieces per thread");
+    uint4 va, vb;
+    constexpr int kPieces = int(R::bytes / 16);
+#define ZEROS_FETCH(c_)                                                                                   \
+    do {                                                                                                  \
+        const uint4 *src_ = reinterpret_cast<const uint4 *>(rec0 + static_cast<size_t>(c_) * R::bytes);  \
+        rq0 = src_[min(tid + 0 * NT, kPieces - 1)];                                                       \
+        if (NREC > 1) rq1 = src_[min(tid + 1 * NT, kPieces - 1)];                                         \
+        if (NREC > 2) rq2 = src_[min(tid + 2 * NT, kPieces - 1)];                                         \
+        if (NREC > 3) rq3 = src_[min(tid + 3 * NT, kPieces - 1)];                                         \
+        if (NREC > 4) rq4 = src_[min(tid + 4 * NT, kPieces - 1)];                                         \
+        if (NREC > 5) rq5 = src_[min(tid + 5 * NT, kPieces - 1)];                                         \
+        if (NREC > 6) rq6 = src_[min(tid + 6 * NT, kPieces - 1)];                                         \
+        const int t_ = (c_) * kC + vtok;   /* rows past N read row N-1 (in bounds), zeroed when staged */ \
+        va = *reinterpret_cast<const uint4 *>(vg + static_cast<size_t>(min(t_, N - 1)) * D + vcol);       \
+        vb = *reinterpret_cast<const uint4 *>(vg + static_cast<size_t>(min(t_ + 1, N - 1)) * D + vcol);   \
+    } while (0)
+#define ZEROS_PUT_REC(b_)                                                                                 \
+    do {                                                                                                  \
+        uint4 *dst_ = reinterpret_cast<uint4 *>(sm.rec[b_]);                                              \
+        if (tid + 0 * NT < kPieces) dst_[tid + 0 * NT] = rq0;                                             \
+        if (NREC > 1 && tid + 1 * NT < kPieces) dst_[tid + 1 * NT] = rq1;                                 \
+        if (NREC > 2 && tid + 2 * NT < kPieces) dst_[tid + 2 * NT] = rq2;                                 \
+        if (NREC > 3 && tid + 3 * NT < kPieces) dst_[tid + 3 * NT] = rq3;                                 \
+        if (NREC > 4 && tid + 4 * NT < kPieces) dst_[tid + 4 * NT] = rq4;                                 \
+        if (NREC > 5 && tid + 5 * NT < kPieces) dst_[tid + 5 * NT] = rq5;                                 \
+        if (NREC > 6 && tid + 6 * NT < kPieces) dst_[tid + 6 * NT] = rq6;                                 \
+    } while (0)
 
-    // stage the v tile of a chunk (transposed token pairs) and its update operands into buffer b
-    auto stage = [&](const Slot &sl, const int b) __attribute__((always_inline)) {
-        const uint32_t pvv = sl.pv_ok ? sl.pv : 0u;
-        const uint32_t other = static_cast<uint32_t>(
-            __builtin_amdgcn_update_dpp(0, static_cast<int>(pvv), kRowRor + 8, 0xf, 0xf, false));
-        const bool odd = lr & 1;
-        const uint32_t pair = odd ? ((other >> 16) | (pvv & 0xffff0000u)) : ((pvv & 0xffffu) | (other << 16));
-        const int col = 2 * p8 + (odd ? 1 : 0), tok = lr & ~1;
-        const float v0 = lo_f(pair), v1 = hi_f(pair);
-        *reinterpret_cast<uint32_t *>(&sm.vt[b][col][tok]) = pair;
-        *reinterpret_cast<uint32_t *>(&sm.vx[b][col][tok]) = pack2(v0 * sl.wx2.x, v1 * sl.wx2.y);
-        *reinterpret_cast<uint32_t *>(&sm.vy[b][col][tok]) = pack2(v0 * sl.wy2.x, v1 * sl.wy2.y);
-    };
-
-    // One chunk: compute with slot sl (chunk ci, staged in buffer ci & 1), stage chunk ci + 1 from
-    // slot nx into the other buffer, refill sl, then a single barrier.
-    auto body = [&](Slot &sl, const Slot &nx, const int ci) __attribute__((always_inline)) {
-        const int t0 = ci * kC;
+    if (c_begin < c_end) {
+        ZEROS_FETCH(c_begin);
+        ZEROS_PUT_REC(0);
+        lds_barrier();
+    }
+    for (int c = c_begin; c < c_end; ++c) {
+        const int b = (c - c_begin) & 1;
+        const int t0 = c * kC;
         const int nval = min(kC, N - t0);
-        const int vb = ci & 1;
+        const unsigned char *rb = sm.rec[b];
+        const float *co = reinterpret_cast<const float *>(rb + R::c_off);
 
-        const float s0c = sl.sc0, s1c = sl.sc1, s2c = sl.sc2;
-        if (qgroup) {
-            const int tb = wb;
-            const int tq = 16 * tb + l16;
-            f32x4 oacc = {0.f, 0.f, 0.f, 0.f};
-            // intra-chunk: o^T += V^T W^T over key-block pairs (0,1) and (2,3)
+        // ---- stage this wave's v tile (token pairs per column) and v * w_X, v * w_Y
+        {
+            const bool ok0 = t0 + vtok < N, ok1 = t0 + vtok + 1 < N;
+            const uint32_t a4[4] = {ok0 ? va.x : 0u, ok0 ? va.y : 0u, ok0 ? va.z : 0u, ok0 ? va.w : 0u};
+            const uint32_t b4[4] = {ok1 ? vb.x : 0u, ok1 ? vb.y : 0u, ok1 ? vb.z : 0u, ok1 ? vb.w : 0u};
+            const float4 wv = *reinterpret_cast<const float4 *>(co + kCoW + 2 * vtok);   // wX, wY of both tokens
 #pragma unroll
-            for (int pi = 0; pi < 2; ++pi) {
-                if (2 * pi > tb) continue;
-                const int kb0 = 2 * pi, kb1 = 2 * pi + 1;
-                const uint2 va = *reinterpret_cast<const uint2 *>(&sm.vt[vb][l16][16 * kb0 + 4 * g4]);
-                const uint2 vc = (kb1 <= tb) ? *reinterpret_cast<const uint2 *>(&sm.vt[vb][l16][16 * kb1 + 4 * g4])
-                                             : make_uint2(0, 0);
-                oacc = mfma(as_bf16x8(va.x, va.y, vc.x, vc.y), sl.op[KS + pi], oacc);
+            for (int i = 0; i < 4; ++i) {
+                // columns 8 vh + 2i (low halves) and 8 vh + 2i + 1 (high halves)
+                const uint32_t plo = (a4[i] & 0xffffu) | (b4[i] << 16);           // (a.lo, b.lo)
+                const uint32_t phi = (a4[i] >> 16) | (b4[i] & 0xffff0000u);       // (a.hi, b.hi)
+                const int m0 = 8 * vh + 2 * i;
+                *reinterpret_cast<uint32_t *>(&sm.vt[w][m0][vtok]) = plo;
+                *reinterpret_cast<uint32_t *>(&sm.vt[w][m0 + 1][vtok]) = phi;
+                const float x0 = lo_f(a4[i]), y0 = lo_f(b4[i]), x1 = hi_f(a4[i]), y1 = hi_f(b4[i]);
+                *reinterpret_cast<uint32_t *>(&sm.vx[w][m0][vtok]) = pack2(x0 * wv.x, y0 * wv.z);
+                *reinterpret_cast<uint32_t *>(&sm.vx[w][m0 + 1][vtok]) = pack2(x1 * wv.x, y1 * wv.z);
+                *reinterpret_cast<uint32_t *>(&sm.vy[w][m0][vtok]) = pack2(x0 * wv.y, y0 * wv.w);
+                *reinterpret_cast<uint32_t *>(&sm.vy[w][m0 + 1][vtok]) = pack2(x1 * wv.y, y1 * wv.w);
             }
-            // carried states
+        }
+        // next chunk's record and v, in flight during this chunk
+        ZEROS_FETCH(min(c + 1, c_end - 1));
+
+        if (!PASS1) {
+            f32x4 oacc[4];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) oacc[tb][i] = 0.f;
+            // carried states: o^T += S^T Q^T, S^T from this wave's float32 accumulators
             if (t0 > 0) {
-                const int sb = ci & 1;
-                f32x4 ax = {0.f, 0.f, 0.f, 0.f}, ay = ax, ah = ax;
+                f32x4 ax[4], ay[4], ah[4];
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) ax[tb][i] = ay[tb][i] = ah[tb][i] = 0.f;
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    ax = mfma(*reinterpret_cast<const bf16x8 *>(&sm.st[sb][0][l16][32 * ks + 8 * g4]), sl.op[ks], ax);
-                    ay = mfma(*reinterpret_cast<const bf16x8 *>(&sm.st[sb][1][l16][32 * ks + 8 * g4]), sl.op[ks], ay);
-                    ah = mfma(*reinterpret_cast<const bf16x8 *>(&sm.st[sb][2][l16][32 * ks + 8 * g4]), sl.op[ks], ah);
+                    const f32x4 &x0 = X[2 * ks], &x1 = X[2 * ks + 1];
+                    const f32x4 &y0 = Y[2 * ks], &y1 = Y[2 * ks + 1];
+                    const f32x4 &h0 = Hm[2 * ks], &h1 = Hm[2 * ks + 1];
+                    const bf16x8 AX = as_bf16x8(pack2(x0[0], x0[1]), pack2(x0[2], x0[3]), pack2(x1[0], x1[1]), pack2(x1[2], x1[3]));
+                    const bf16x8 AY = as_bf16x8(pack2(y0[0], y0[1]), pack2(y0[2], y0[3]), pack2(y1[0], y1[1]), pack2(y1[2], y1[3]));
+                    const bf16x8 AH = as_bf16x8(pack2(h0[0], h0[1]), pack2(h0[2], h0[3]), pack2(h1[0], h1[1]), pack2(h1[2], h1[3]));
+#pragma unroll
+                    for (int tb = 0; tb < 4; ++tb) {
+                        const bf16x8 Bq = ld16(rb + R::q_off + (size_t(tb * KS + ks) * 64 + lane) * 16);
+                        ax[tb] = mfma(AX, Bq, ax[tb]);
+                        ay[tb] = mfma(AY, Bq, ay[tb]);
+                        ah[tb] = mfma(AH, Bq, ah[tb]);
+                    }
                 }
 #pragma unroll
-                for (int i = 0; i < 4; ++i) oacc[i] += s0c * ax[i] + s1c * ay[i] + s2c * ah[i];   // cX, beta, kappa
+                for (int tb = 0; tb < 4; ++tb) {
+                    const float4 cq = *reinterpret_cast<const float4 *>(co + kCoQ + 4 * (16 * tb + l16));  // cX, beta, kappa
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) oacc[tb][i] = cq.x * ax[tb][i] + cq.y * ay[tb][i] + cq.z * ah[tb][i];
+                }
             }
-            if (tq < nval) {
-                const uint2 ov = make_uint2(pack2(oacc[0], oacc[1]), pack2(oacc[2], oacc[3]));
-                *reinterpret_cast<uint2 *>(og + static_cast<size_t>(t0 + tq) * D + tile * kTile + 4 * g4) = ov;
+            // intra-chunk: o^T += V^T W^T over key-block pairs (0,1) and (2,3)
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+                for (int pi = 0; pi < 2; ++pi) {
+                    if (2 * pi > tb) continue;
+                    const uint2 a = *reinterpret_cast<const uint2 *>(&sm.vt[w][l16][32 * pi + 4 * g4]);
+                    const uint2 e = (2 * pi + 1 <= tb) ? *reinterpret_cast<const uint2 *>(&sm.vt[w][l16][32 * pi + 16 + 4 * g4])
+                                                       : make_uint2(0, 0);
+                    const bf16x8 Bw = ld16(rb + R::w_off + (size_t(tb * 2 + pi) * 64 + lane) * 16);
+                    oacc[tb] = mfma(as_bf16x8(a.x, a.y, e.x, e.y), Bw, oacc[tb]);
+                }
+                const int tq = 16 * tb + l16;
+                if (tq < nval) {
+                    const uint2 ov = make_uint2(pack2(oacc[tb][0], oacc[tb][1]), pack2(oacc[tb][2], oacc[tb][3]));
+                    *reinterpret_cast<uint2 *>(og + static_cast<size_t>(t0 + tq) * D + w * kTile + 4 * g4) = ov;
+                }
             }
-        } else if (ci < nch) {              // padding chunks past the end leave the states alone
+        }
+
+        // ---- state update to the chunk end: rescale to the new basis, then K^T V' on MFMA
+        {
+            const float4 ch = *reinterpret_cast<const float4 *>(co + kCoChunk);   // rX, cHX, cHY, m1
             if (t0 > 0) {
 #pragma unroll
-                for (int rt = 0; rt < RT; ++rt)
+                for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        X[rt][i] = s0c * X[rt][i] + s1c * Hm[rt][i];   // rX, cHX
-                        Y[rt][i] = Y[rt][i] + s2c * Hm[rt][i];           // cHY
+                        X[jb][i] = ch.x * X[jb][i] + ch.y * Hm[jb][i];
+                        Y[jb][i] = Y[jb][i] + ch.z * Hm[jb][i];
                     }
+                Hs = ch.x * Hs + ch.y;
+                Rs = ch.x * Rs;
+                Ys = Ys + ch.z;
+            } else {
+                Rs = 0.f;                    // the first chunk of the sequence starts from nothing
+                Hs = 0.f;
             }
 #pragma unroll
             for (int ks2 = 0; ks2 < kC / 32; ++ks2) {
                 const int kk0 = 32 * ks2 + 8 * g4;
-                const bf16x8 BX = *reinterpret_cast<const bf16x8 *>(&sm.vx[vb][l16][kk0]);
-                const bf16x8 BY = *reinterpret_cast<const bf16x8 *>(&sm.vy[vb][l16][kk0]);
-                const bf16x8 BH = *reinterpret_cast<const bf16x8 *>(&sm.vt[vb][l16][kk0]);
+                const bf16x8 BX = *reinterpret_cast<const bf16x8 *>(&sm.vx[w][l16][kk0]);
+                const bf16x8 BY = *reinterpret_cast<const bf16x8 *>(&sm.vy[w][l16][kk0]);
+                const bf16x8 BH = *reinterpret_cast<const bf16x8 *>(&sm.vt[w][l16][kk0]);
 #pragma unroll
-                for (int rt = 0; rt < RT; ++rt) {
-                    X[rt] = mfma(sl.op[2 * rt + ks2], BX, X[rt]);
-                    Y[rt] = mfma(sl.op[2 * rt + ks2], BY, Y[rt]);
-                    Hm[rt] = mfma(sl.op[2 * rt + ks2], BH, Hm[rt]);
+                for (int jb = 0; jb < JB; ++jb) {
+                    const bf16x8 Ak = ld16(rb + R::k_off + (size_t(jb * 2 + ks2) * 64 + lane) * 16);
+                    X[jb] = mfma(Ak, BX, X[jb]);
+                    Y[jb] = mfma(Ak, BY, Y[jb]);
+                    Hm[jb] = mfma(Ak, BH, Hm[jb]);
                 }
             }
-            const int nb = (ci + 1) & 1;        // the query waves read st[ci & 1] meanwhile
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                const int jc = 16 * (RT * wb + rt) + 4 * g4;
-                *reinterpret_cast<uint2 *>(&sm.st[nb][0][l16][jc]) = make_uint2(pack2(X[rt][0], X[rt][1]), pack2(X[rt][2], X[rt][3]));
-                *reinterpret_cast<uint2 *>(&sm.st[nb][1][l16][jc]) = make_uint2(pack2(Y[rt][0], Y[rt][1]), pack2(Y[rt][2], Y[rt][3]));
-                *reinterpret_cast<uint2 *>(&sm.st[nb][2][l16][jc]) = make_uint2(pack2(Hm[rt][0], Hm[rt][1]), pack2(Hm[rt][2], Hm[rt][3]));
-            }
         }
-        stage(nx, vb ^ 1);
-        // this slot is consumed: refill it with the chunk kRing ahead. The load is unconditional
-        // (past the end it repeats the last chunk) so that the wait before each use of a slot is
-        // a fixed count of younger loads and the other slots stay in flight.
-        load(sl, min(ci + kRing, nch - 1));
-        lds_barrier();            // chunk done: next staging and states visible, old buffers free
-    };
-
-    Slot s0, s1, s2;
-    static_assert(kRing == 3, "the loop below is unrolled for a ring of three slots");
-    if (nch > 0) {
-        // issued in slot order (the empty asm keeps the compiler from reordering them), so that
-        // slot 0 is the oldest at the loop entry as it is on every later iteration
-        load(s0, 0);
-        asm volatile("" ::: "memory");
-        load(s1, min(1, nch - 1));
-        asm volatile("" ::: "memory");
-        load(s2, min(2, nch - 1));
-        asm volatile("" ::: "memory");
-        stage(s0, 0);
-        lds_barrier();
-        // whole groups of kRing chunks; a chunk index past the end stores nothing (nval <= 0)
-        for (int ci = 0; ci < nch; ci += kRing) {
-            body(s0, s1, ci);
-            body(s1, s2, ci + 1);
-            body(s2, s0, ci + 2);
-        }
+        ZEROS_PUT_REC(b ^ 1);     // the other buffer was last read before the previous barrier
+        lds_barrier();            // record of chunk c + 1 visible; this chunk's buffer free
     }
 
-    // ---- final state (update waves): back to F = E (X + H/t), G = Y + (P/t) H
-    if (p.st.F != nullptr) {
+#undef ZEROS_FETCH
+#undef ZEROS_PUT_REC
+
+    if (PASS1) {
+        // segment-local sums and the composed scalar map, for the combine step
+        float4 *dst = reinterpret_cast<float4 *>(work.segst + (static_cast<size_t>(bh) * (nseg - 1) + seg) * kSegFloats<D>);
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb) {
+            dst[(size_t(0 * JB + jb) * NW) * 64 + sidx] = make_float4(X[jb][0], X[jb][1], X[jb][2], X[jb][3]);
+            dst[(size_t(1 * JB + jb) * NW) * 64 + sidx] = make_float4(Y[jb][0], Y[jb][1], Y[jb][2], Y[jb][3]);
+            dst[(size_t(2 * JB + jb) * NW) * 64 + sidx] = make_float4(Hm[jb][0], Hm[jb][1], Hm[jb][2], Hm[jb][3]);
+        }
+        if (tid == 0) work.segsc[static_cast<size_t>(bh) * nseg + seg] = make_float4(Rs, Hs, Ys, 0.f);
+        return;
+    }
+
+    // ---- final recurrent state (last segment): back to F = E (X + H/t), G = Y + (P/t) H
+    if (p.st.F != nullptr && seg == nseg - 1) {
         float m0 = kNegInf, E0 = 0.f, P0 = 0.f;
         if (N > 0) {
             const float *co = reinterpret_cast<const float *>(rec0 + static_cast<size_t>(nch - 1) * R::bytes + R::c_off);
@@ -633,43 +683,59 @@ __global__ __launch_bounds__(kMainThreads) void causal_main_kernel(Problem p, Ca
             E0 = co[kCoChunk + 4];
             P0 = co[kCoChunk + 5];
         }
-        if (!qgroup) {
-            const size_t mat0 = static_cast<size_t>(bh) * D * D;
-            const float tf = static_cast<float>(N);
+        const size_t mat0 = static_cast<size_t>(bh) * D * D;
+        const float tf = static_cast<float>(N);
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                float F[4], Gv[4], Hv[4];
+        for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float hh = Hm[rt][i];
-                    F[i] = N > 0 ? E0 * (X[rt][i] + hh / tf) : 0.f;
-                    Gv[i] = N > 0 ? Y[rt][i] + (P0 / tf) * hh : 0.f;
-                    Hv[i] = hh;
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int j = 16 * (RT * wb + rt) + 4 * g4 + i;
-                    const size_t idx = mat0 + static_cast<size_t>(j) * D + tile * kTile + l16;
-                    p.st.F[idx] = F[i];
-                    p.st.G[idx] = Gv[i];
-                    p.st.Hs[idx] = Hv[i];
-                }
+            for (int i = 0; i < 4; ++i) {
+                const float hh = Hm[jb][i];
+                const int j = 16 * jb + 4 * g4 + i;
+                const size_t idx = mat0 + static_cast<size_t>(j) * D + w * kTile + l16;
+                p.st.F[idx] = N > 0 ? E0 * (X[jb][i] + hh / tf) : 0.f;
+                p.st.G[idx] = N > 0 ? Y[jb][i] + (P0 / tf) * hh : 0.f;
+                p.st.Hs[idx] = hh;
             }
+        const int nls = (N + kLogitSeg - 1) / kLogitSeg;
+        if (tid < D) {
+            float su = 0.f;
+            for (int sg = 0; sg < nls; ++sg) su += work.useg[(static_cast<size_t>(bh) * nls + sg) * D + tid];
+            p.st.Su[static_cast<size_t>(bh) * D + tid] = su;
         }
-        if (tile == 0) {
-            const int nseg = (N + kLogitSeg - 1) / kLogitSeg;
-            if (tid < D) {
-                float su = 0.f;
-                for (int sg = 0; sg < nseg; ++sg) su += work.useg[(static_cast<size_t>(bh) * nseg + sg) * D + tid];
-                p.st.Su[static_cast<size_t>(bh) * D + tid] = su;
-            }
-            if (tid == 0) {
-                p.st.m[bh] = m0;
-                p.st.E[bh] = E0;
-                p.st.P[bh] = P0;
-                p.st.t[bh] = N;
-            }
+        if (tid == 0) {
+            p.st.m[bh] = m0;
+            p.st.E[bh] = E0;
+            p.st.P[bh] = P0;
+            p.st.t[bh] = N;
         }
+    }
+}
+
+// Start states of segments 1 .. nseg-1 (in place over the segment-local sums), one float4 position
+// of the three state matrices per thread: S_{j+1} = M_j S_j + L_j with S_0 = 0.
+template <int D>
+__global__ __launch_bounds__(256) void causal_seg_combine_kernel(CausalWork work) {
+    constexpr size_t Q = size_t(D) * D / 4;              // float4 positions per state matrix
+    const size_t pos = static_cast<size_t>(blockIdx.y) * 256 + threadIdx.x;
+    if (pos >= Q) return;
+    const int bh = blockIdx.x;
+    const int nseg = work.nseg;
+    float4 x = make_float4(0.f, 0.f, 0.f, 0.f), y = x, h = x;
+    for (int j = 0; j + 1 < nseg; ++j) {
+        float4 *st = reinterpret_cast<float4 *>(work.segst + (static_cast<size_t>(bh) * (nseg - 1) + j) * kSegFloats<D>);
+        const float4 m = work.segsc[static_cast<size_t>(bh) * nseg + j];   // Rs, Hs, Ys
+        const float4 lx = st[pos], ly = st[Q + pos], lh = st[2 * Q + pos];
+        const float4 nx = make_float4(m.x * x.x + m.y * h.x + lx.x, m.x * x.y + m.y * h.y + lx.y,
+                                      m.x * x.z + m.y * h.z + lx.z, m.x * x.w + m.y * h.w + lx.w);
+        const float4 ny = make_float4(y.x + m.z * h.x + ly.x, y.y + m.z * h.y + ly.y,
+                                      y.z + m.z * h.z + ly.z, y.w + m.z * h.w + ly.w);
+        const float4 nh = make_float4(h.x + lh.x, h.y + lh.y, h.z + lh.z, h.w + lh.w);
+        st[pos] = nx;
+        st[Q + pos] = ny;
+        st[2 * Q + pos] = nh;
+        x = nx;
+        y = ny;
+        h = nh;
     }
 }
 
@@ -684,25 +750,34 @@ hipError_t launch_one(const Problem &p, const CausalWork &w, hipStream_t stream)
     static bool attr_set = false;   // idempotent; a race only repeats the same calls
     if (!attr_set) {
         hipError_t err = set_smem(&causal_prep_kernel<D, ROPE>, sizeof(PSmem<D>));
-        if (err == hipSuccess) err = set_smem(&causal_main_kernel<D, ROPE>, sizeof(MSmem<D>));
+        if (err == hipSuccess) err = set_smem(&causal_seg_kernel<D, ROPE, false>, sizeof(SSmem<D>));
+        if (err == hipSuccess) err = set_smem(&causal_seg_kernel<D, ROPE, true>, sizeof(SSmem<D>));
         if (err != hipSuccess) return err;
         attr_set = true;
     }
     const int nch = (p.N + kC - 1) / kC;
+    const int bh = p.B * p.H;
+    hipError_t err;
     if (ROPE && nch > 0) {
         hipLaunchKernelGGL((rope_table_kernel<D>), dim3((kC * (D / 2) + 255) / 256), dim3(256), 0, stream,
                            w.rope, p.rope_base);
-        hipError_t err = hipGetLastError();
-        if (err != hipSuccess) return err;
+        if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if (nch > 0) {
-        hipLaunchKernelGGL((causal_prep_kernel<D, ROPE>), dim3(p.B * p.H * nch), dim3(kPrepThreads),
+        hipLaunchKernelGGL((causal_prep_kernel<D, ROPE>), dim3(bh * nch), dim3(kPrepThreads),
                            sizeof(PSmem<D>), stream, p, w);
-        hipError_t err = hipGetLastError();
-        if (err != hipSuccess) return err;
+        if ((err = hipGetLastError()) != hipSuccess) return err;
     }
-    hipLaunchKernelGGL((causal_main_kernel<D, ROPE>), dim3(p.B * p.H * (D / kTile)), dim3(kMainThreads),
-                       sizeof(MSmem<D>), stream, p, w);
+    if (w.nseg > 1) {
+        hipLaunchKernelGGL((causal_seg_kernel<D, ROPE, true>), dim3(bh * (w.nseg - 1)), dim3(D * 4),
+                           sizeof(SSmem<D>), stream, p, w);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        hipLaunchKernelGGL((causal_seg_combine_kernel<D>), dim3(bh, (D * D / 4 + 255) / 256), dim3(256), 0,
+                           stream, w);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    hipLaunchKernelGGL((causal_seg_kernel<D, ROPE, false>), dim3(bh * w.nseg), dim3(D * 4), sizeof(SSmem<D>),
+                       stream, p, w);
     return hipGetLastError();
 }
 
@@ -710,32 +785,50 @@ hipError_t launch_one(const Problem &p, const CausalWork &w, hipStream_t stream)
 
 size_t causal_rec_bytes(int d) { return d == 128 ? Rec<128>::bytes : Rec<64>::bytes; }
 
+// Segments of the scan: enough (head, segment) workgroups to cover the chip, whole chunks each.
+static void seg_plan(int B, int H, int N, int &nseg, int &seg_chunks) {
+    const int nch = (N + kC - 1) / kC;
+    const int bh = B * H;
+    int want = (256 + bh - 1) / bh;
+    if (want > nch) want = nch;
+    if (want < 1) want = 1;
+    seg_chunks = nch > 0 ? (nch + want - 1) / want : 1;
+    nseg = nch > 0 ? (nch + seg_chunks - 1) / seg_chunks : 1;
+}
+
 size_t causal_work_bytes(int B, int H, int N, int du) {
     const size_t a = 256;
     auto up = [a](size_t x) { return (x + a - 1) / a * a; };
-    const size_t nseg = (static_cast<size_t>(N) + kLogitSeg - 1) / kLogitSeg;
+    const size_t nls = (static_cast<size_t>(N) + kLogitSeg - 1) / kLogitSeg;
     const size_t nch = (static_cast<size_t>(N) + kC - 1) / kC;
     const size_t bh = static_cast<size_t>(B) * H;
-    return up(bh * N * 4) + up(bh * nseg * du * 4) + up(bh * nch * 16) + up(size_t(kC) * (du / 2) * 8) +
-           bh * nch * causal_rec_bytes(du);
+    int nseg, seg_chunks;
+    seg_plan(B, H, N, nseg, seg_chunks);
+    return up(bh * N * 4) + up(bh * nls * du * 4) + up(bh * nch * 16) + up(size_t(kC) * (du / 2) * 8) +
+           up(bh * nseg * 16) + up(bh * (nseg - 1) * size_t(3) * du * du * 4) + bh * nch * causal_rec_bytes(du);
 }
 
 CausalWork causal_work_carve(void *base, int B, int H, int N, int du) {
     const size_t a = 256;
     auto up = [a](size_t x) { return (x + a - 1) / a * a; };
-    const size_t nseg = (static_cast<size_t>(N) + kLogitSeg - 1) / kLogitSeg;
+    const size_t nls = (static_cast<size_t>(N) + kLogitSeg - 1) / kLogitSeg;
     const size_t nch = (static_cast<size_t>(N) + kC - 1) / kC;
     const size_t bh = static_cast<size_t>(B) * H;
-    char *b = static_cast<char *>(base);
     CausalWork w;
+    seg_plan(B, H, N, w.nseg, w.seg_chunks);
+    char *b = static_cast<char *>(base);
     w.s = reinterpret_cast<float *>(b);
     b += up(bh * N * 4);
     w.useg = reinterpret_cast<float *>(b);
-    b += up(bh * nseg * du * 4);
+    b += up(bh * nls * du * 4);
     w.agg = reinterpret_cast<float4 *>(b);
     b += up(bh * nch * 16);
     w.rope = reinterpret_cast<float2 *>(b);
     b += up(size_t(kC) * (du / 2) * 8);
+    w.segsc = reinterpret_cast<float4 *>(b);
+    b += up(bh * w.nseg * 16);
+    w.segst = reinterpret_cast<float *>(b);
+    b += up(bh * (w.nseg - 1) * size_t(3) * du * du * 4);
     w.rec = reinterpret_cast<unsigned char *>(b);
     return w;
 }

@@ -30,6 +30,10 @@ struct CausalWork {
     float *useg;        // [B*H, nseg, d_u] per-segment u sums
     float4 *agg;        // [B*H, nchunk] per-chunk (max s, sum e^{s-max}, sum s, 0)
     float2 *rope;       // [kCausalChunk, d/2] cos, sin of r * theta_j (RoPE only)
+    float4 *segsc;      // [B*H, nseg] composed scalar map (Rs, Hs, Ys, 0) of each scan segment
+    float *segst;       // [B*H, nseg-1, 3, d, d] segment-local sums, then segment start states
+    int nseg;           // scan segments per head
+    int seg_chunks;     // chunks per segment (the last one may be shorter)
     unsigned char *rec; // [B*H, nchunk, rec_bytes(d)] per-chunk operands prepared for the scan
 };
 size_t causal_rec_bytes(int d);

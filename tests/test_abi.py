@@ -139,7 +139,8 @@ def test_workspace_size_and_validation(lib):
     segsc = bh * nseg * 16                               # composed scalar map per segment
     segst = bh * (nseg - 1) * 3 * 128 * 128 * 4          # float32 X, Y, H per segment boundary
     rec = (4 * 4 + 8 * 2 + 4 * 2) * 1024 + (6 * 64 + 8) * 4   # q^, k^T, W operand tiles + coefficients
-    assert n == logits + useg + agg + rope + segsc + segst + bh * nch * rec
+    sink = 64 * 128 * 2                                  # output rows past N of a last, partial chunk
+    assert n == logits + useg + agg + rope + segsc + segst + sink + bh * nch * rec
     assert lib.zeros_fwd_causal_workspace_bytes(ctypes.byref(shape(dtype=0))) == 0   # f32 path: none
     assert lib.zeros_fwd_causal_workspace_bytes(None) == 0
     small = shape(B=1, H=2, N=8, d=64, d_u=64, dtype=1)

@@ -436,26 +436,28 @@ __global__ __launch_bounds__(kPrepThreads) void causal_prep_kernel(Problem p, Ca
 // lane holds rows 16 jb + 4 (lane >> 4) + i, i < 4, column 16 w + (lane & 15) of state s (X, Y, H).
 template <int D> constexpr size_t kSegFloats = size_t(3) * D * D;
 
-template <int D>
-struct alignas(16) SSmem {
-    alignas(16) unsigned char rec[2][Rec<D>::bytes];       // record of the current and next chunk
-    // per wave: its v tile transposed, vt[m][token] (also the H update operand), and the update
-    // operands v * w_X, v * w_Y, transposed
-    alignas(16) uint16_t vt[D / 16][kTile][kC + kPad];
-    alignas(16) uint16_t vx[D / 16][kTile][kC + kPad];
-    alignas(16) uint16_t vy[D / 16][kTile][kC + kPad];
-};
+// LDS bytes of one staged record: whole 64-piece (1 KiB) wave copies
+template <int D> constexpr int kRecLds = int((Rec<D>::bytes / 16 + 63) / 64 * 64 * 16);
 
 template <int D, bool ROPE, bool PASS1>
 __global__ __launch_bounds__(D * 4) void causal_seg_kernel(Problem p, CausalWork work) {
-    extern __shared__ __align__(16) unsigned char smem_raw[];
-    SSmem<D> &sm = *reinterpret_cast<SSmem<D> *>(smem_raw);
+    // Two record buffers as separate objects: the next chunk is copied into one by direct
+    // global-to-LDS loads while the other is read, and the compiler can tell the two apart (so
+    // it does not wait for the copy before reading the current one).
+    __shared__ __align__(16) unsigned char recA[kRecLds<D>];
+    __shared__ __align__(16) unsigned char recB[kRecLds<D>];
+    // per wave: its v tile transposed, vt[m][token] (also the H update operand), and the update
+    // operands v * w_X, v * w_Y, transposed
+    __shared__ __align__(16) uint16_t svt[D / 16][kTile][kC + kPad];
+    __shared__ __align__(16) uint16_t svx[D / 16][kTile][kC + kPad];
+    __shared__ __align__(16) uint16_t svy[D / 16][kTile][kC + kPad];
     using R = Rec<D>;
     constexpr int NW = D / 16;          // waves
     constexpr int NT = NW * 64;
     constexpr int KS = D / 32;          // 32-feature steps of the carried-state products
     constexpr int JB = D / 16;          // 16-row state tiles
     constexpr int NREC = (int(R::bytes / 16) + NT - 1) / NT;   // 16-byte record pieces per thread
+    constexpr int kPieces = int(R::bytes / 16);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -497,48 +499,30 @@ __global__ __launch_bounds__(D * 4) void causal_seg_kernel(Problem p, CausalWork
     // v of this wave's columns: lane holds tokens 2 (lane & 31), +1 and columns 8 (lane >> 5) + [0, 8)
     const int vtok = 2 * (lane & 31), vh = lane >> 5;
     const size_t vcol = static_cast<size_t>(w) * kTile + 8 * vh;
-    // record pieces tid + i * NT of a chunk (clamped to the last piece, so every load is issued)
-    // and this wave's v rows, read one chunk ahead
-    uint4 rq0, rq1, rq2, rq3, rq4, rq5, rq6;
-    static_assert(NREC <= 7, "record larger than seven 16-byte pieces per thread");
     uint4 va, vb;
-    constexpr int kPieces = int(R::bytes / 16);
-#define ZEROS_FETCH(c_)                                                                                   \
-    do {                                                                                                  \
-        const uint4 *src_ = reinterpret_cast<const uint4 *>(rec0 + static_cast<size_t>(c_) * R::bytes);  \
-        rq0 = src_[min(tid + 0 * NT, kPieces - 1)];                                                       \
-        if (NREC > 1) rq1 = src_[min(tid + 1 * NT, kPieces - 1)];                                         \
-        if (NREC > 2) rq2 = src_[min(tid + 2 * NT, kPieces - 1)];                                         \
-        if (NREC > 3) rq3 = src_[min(tid + 3 * NT, kPieces - 1)];                                         \
-        if (NREC > 4) rq4 = src_[min(tid + 4 * NT, kPieces - 1)];                                         \
-        if (NREC > 5) rq5 = src_[min(tid + 5 * NT, kPieces - 1)];                                         \
-        if (NREC > 6) rq6 = src_[min(tid + 6 * NT, kPieces - 1)];                                         \
-        const int t_ = (c_) * kC + vtok;   /* rows past N read row N-1 (in bounds), zeroed when staged */ \
-        va = *reinterpret_cast<const uint4 *>(vg + static_cast<size_t>(min(t_, N - 1)) * D + vcol);       \
-        vb = *reinterpret_cast<const uint4 *>(vg + static_cast<size_t>(min(t_ + 1, N - 1)) * D + vcol);   \
-    } while (0)
-#define ZEROS_PUT_REC(b_)                                                                                 \
-    do {                                                                                                  \
-        uint4 *dst_ = reinterpret_cast<uint4 *>(sm.rec[b_]);                                              \
-        if (tid + 0 * NT < kPieces) dst_[tid + 0 * NT] = rq0;                                             \
-        if (NREC > 1 && tid + 1 * NT < kPieces) dst_[tid + 1 * NT] = rq1;                                 \
-        if (NREC > 2 && tid + 2 * NT < kPieces) dst_[tid + 2 * NT] = rq2;                                 \
-        if (NREC > 3 && tid + 3 * NT < kPieces) dst_[tid + 3 * NT] = rq3;                                 \
-        if (NREC > 4 && tid + 4 * NT < kPieces) dst_[tid + 4 * NT] = rq4;                                 \
-        if (NREC > 5 && tid + 5 * NT < kPieces) dst_[tid + 5 * NT] = rq5;                                 \
-        if (NREC > 6 && tid + 6 * NT < kPieces) dst_[tid + 6 * NT] = rq6;                                 \
-    } while (0)
+    // v rows of chunk c into registers, and record chunk c into LDS buffer dst (direct copies:
+    // wave w moves pieces [64 w + NT i, 64 w + NT i + 64) of the record; lanes past the end repeat
+    // the last piece into the padding of the buffer)
+    auto fetch = [&](const int c, unsigned char *dst) __attribute__((always_inline)) {
+        const int t_ = c * kC + vtok;      // rows past N read row N-1 (in bounds), zeroed when staged
+        va = *reinterpret_cast<const uint4 *>(vg + static_cast<size_t>(min(t_, N - 1)) * D + vcol);
+        vb = *reinterpret_cast<const uint4 *>(vg + static_cast<size_t>(min(t_ + 1, N - 1)) * D + vcol);
+        const uint4 *src = reinterpret_cast<const uint4 *>(rec0 + static_cast<size_t>(c) * R::bytes);
+#pragma unroll
+        for (int i = 0; i < NREC; ++i) {
+            const int base = w * 64 + i * NT;                    // wave-uniform
+            if (base < kPieces)
+                __builtin_amdgcn_global_load_lds(src + min(base + lane, kPieces - 1), dst + base * 16, 16, 0, 0);
+        }
+    };
 
-    if (c_begin < c_end) {
-        ZEROS_FETCH(c_begin);
-        ZEROS_PUT_REC(0);
-        lds_barrier();
-    }
-    for (int c = c_begin; c < c_end; ++c) {
-        const int b = (c - c_begin) & 1;
+    if (c_begin < c_end) fetch(c_begin, recA);
+    // unconditional: the start-state loads and the first copies are complete on every path into
+    // the loop, so no wait inside it has to cover them
+    __syncthreads();
+    auto chunk = [&](const int c, const unsigned char *rb, unsigned char *rn) __attribute__((always_inline)) {
         const int t0 = c * kC;
         const int nval = min(kC, N - t0);
-        const unsigned char *rb = sm.rec[b];
         const float *co = reinterpret_cast<const float *>(rb + R::c_off);
 
         // ---- stage this wave's v tile (token pairs per column) and v * w_X, v * w_Y
@@ -553,85 +537,85 @@ __global__ __launch_bounds__(D * 4) void causal_seg_kernel(Problem p, CausalWork
                 const uint32_t plo = (a4[i] & 0xffffu) | (b4[i] << 16);           // (a.lo, b.lo)
                 const uint32_t phi = (a4[i] >> 16) | (b4[i] & 0xffff0000u);       // (a.hi, b.hi)
                 const int m0 = 8 * vh + 2 * i;
-                *reinterpret_cast<uint32_t *>(&sm.vt[w][m0][vtok]) = plo;
-                *reinterpret_cast<uint32_t *>(&sm.vt[w][m0 + 1][vtok]) = phi;
+                *reinterpret_cast<uint32_t *>(&svt[w][m0][vtok]) = plo;
+                *reinterpret_cast<uint32_t *>(&svt[w][m0 + 1][vtok]) = phi;
                 const float x0 = lo_f(a4[i]), y0 = lo_f(b4[i]), x1 = hi_f(a4[i]), y1 = hi_f(b4[i]);
-                *reinterpret_cast<uint32_t *>(&sm.vx[w][m0][vtok]) = pack2(x0 * wv.x, y0 * wv.z);
-                *reinterpret_cast<uint32_t *>(&sm.vx[w][m0 + 1][vtok]) = pack2(x1 * wv.x, y1 * wv.z);
-                *reinterpret_cast<uint32_t *>(&sm.vy[w][m0][vtok]) = pack2(x0 * wv.y, y0 * wv.w);
-                *reinterpret_cast<uint32_t *>(&sm.vy[w][m0 + 1][vtok]) = pack2(x1 * wv.y, y1 * wv.w);
+                *reinterpret_cast<uint32_t *>(&svx[w][m0][vtok]) = pack2(x0 * wv.x, y0 * wv.z);
+                *reinterpret_cast<uint32_t *>(&svx[w][m0 + 1][vtok]) = pack2(x1 * wv.x, y1 * wv.z);
+                *reinterpret_cast<uint32_t *>(&svy[w][m0][vtok]) = pack2(x0 * wv.y, y0 * wv.w);
+                *reinterpret_cast<uint32_t *>(&svy[w][m0 + 1][vtok]) = pack2(x1 * wv.y, y1 * wv.w);
+            }
+        }
+
+        // ---- carried-state products and the state update, interleaved by pairs of row tiles:
+        // step ks reads rows 2ks, 2ks+1 of X, Y, H (as bf16 MFMA operands, the state at t0), after
+        // which those rows are rescaled to the chunk-end basis and advanced by K^T V' on MFMA.
+        const float4 ch = *reinterpret_cast<const float4 *>(co + kCoChunk);   // rX, cHX, cHY, m1
+        // every operand from this wave's staging area is read here, before the next record's
+        // copies are issued: afterwards the wave reads only the current record buffer, which the
+        // compiler can tell apart from the copy target (no wait for the copies inside the chunk)
+        bf16x8 BX[kC / 32], BY[kC / 32], BH[kC / 32];
+#pragma unroll
+        for (int ks2 = 0; ks2 < kC / 32; ++ks2) {
+            const int kk0 = 32 * ks2 + 8 * g4;
+            BX[ks2] = *reinterpret_cast<const bf16x8 *>(&svx[w][l16][kk0]);
+            BY[ks2] = *reinterpret_cast<const bf16x8 *>(&svy[w][l16][kk0]);
+            BH[ks2] = *reinterpret_cast<const bf16x8 *>(&svt[w][l16][kk0]);
+        }
+        uint2 VA[2], VC[2];                  // V^T operand halves of the intra-chunk product
+        if (!PASS1) {
+#pragma unroll
+            for (int pi = 0; pi < 2; ++pi) {
+                VA[pi] = *reinterpret_cast<const uint2 *>(&svt[w][l16][32 * pi + 4 * g4]);
+                VC[pi] = *reinterpret_cast<const uint2 *>(&svt[w][l16][32 * pi + 16 + 4 * g4]);
             }
         }
         // next chunk's record and v, in flight during this chunk
-        ZEROS_FETCH(min(c + 1, c_end - 1));
-
-        if (!PASS1) {
-            f32x4 oacc[4];
+        fetch(min(c + 1, c_end - 1), rn);
+        f32x4 ax[4], ay[4], ah[4];
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
+        for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) oacc[tb][i] = 0.f;
-            // carried states: o^T += S^T Q^T, S^T from this wave's float32 accumulators
-            if (t0 > 0) {
-                f32x4 ax[4], ay[4], ah[4];
+            for (int i = 0; i < 4; ++i) ax[tb][i] = ay[tb][i] = ah[tb][i] = 0.f;
+        const bool carried = !PASS1 && t0 > 0;
 #pragma unroll
-                for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) ax[tb][i] = ay[tb][i] = ah[tb][i] = 0.f;
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const f32x4 &x0 = X[2 * ks], &x1 = X[2 * ks + 1];
-                    const f32x4 &y0 = Y[2 * ks], &y1 = Y[2 * ks + 1];
-                    const f32x4 &h0 = Hm[2 * ks], &h1 = Hm[2 * ks + 1];
-                    const bf16x8 AX = as_bf16x8(pack2(x0[0], x0[1]), pack2(x0[2], x0[3]), pack2(x1[0], x1[1]), pack2(x1[2], x1[3]));
-                    const bf16x8 AY = as_bf16x8(pack2(y0[0], y0[1]), pack2(y0[2], y0[3]), pack2(y1[0], y1[1]), pack2(y1[2], y1[3]));
-                    const bf16x8 AH = as_bf16x8(pack2(h0[0], h0[1]), pack2(h0[2], h0[3]), pack2(h1[0], h1[1]), pack2(h1[2], h1[3]));
-#pragma unroll
-                    for (int tb = 0; tb < 4; ++tb) {
-                        const bf16x8 Bq = ld16(rb + R::q_off + (size_t(tb * KS + ks) * 64 + lane) * 16);
-                        ax[tb] = mfma(AX, Bq, ax[tb]);
-                        ay[tb] = mfma(AY, Bq, ay[tb]);
-                        ah[tb] = mfma(AH, Bq, ah[tb]);
-                    }
-                }
+        for (int ks = 0; ks < KS; ++ks) {
+            if (carried) {
+                const f32x4 &x0 = X[2 * ks], &x1 = X[2 * ks + 1];
+                const f32x4 &y0 = Y[2 * ks], &y1 = Y[2 * ks + 1];
+                const f32x4 &h0 = Hm[2 * ks], &h1 = Hm[2 * ks + 1];
+                const bf16x8 AX = as_bf16x8(pack2(x0[0], x0[1]), pack2(x0[2], x0[3]), pack2(x1[0], x1[1]), pack2(x1[2], x1[3]));
+                const bf16x8 AY = as_bf16x8(pack2(y0[0], y0[1]), pack2(y0[2], y0[3]), pack2(y1[0], y1[1]), pack2(y1[2], y1[3]));
+                const bf16x8 AH = as_bf16x8(pack2(h0[0], h0[1]), pack2(h0[2], h0[3]), pack2(h1[0], h1[1]), pack2(h1[2], h1[3]));
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb) {
-                    const float4 cq = *reinterpret_cast<const float4 *>(co + kCoQ + 4 * (16 * tb + l16));  // cX, beta, kappa
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) oacc[tb][i] = cq.x * ax[tb][i] + cq.y * ay[tb][i] + cq.z * ah[tb][i];
+                    const bf16x8 Bq = ld16(rb + R::q_off + (size_t(tb * KS + ks) * 64 + lane) * 16);
+                    ax[tb] = mfma(AX, Bq, ax[tb]);
+                    ay[tb] = mfma(AY, Bq, ay[tb]);
+                    ah[tb] = mfma(AH, Bq, ah[tb]);
                 }
             }
-            // intra-chunk: o^T += V^T W^T over key-block pairs (0,1) and (2,3)
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-#pragma unroll
-                for (int pi = 0; pi < 2; ++pi) {
-                    if (2 * pi > tb) continue;
-                    const uint2 a = *reinterpret_cast<const uint2 *>(&sm.vt[w][l16][32 * pi + 4 * g4]);
-                    const uint2 e = (2 * pi + 1 <= tb) ? *reinterpret_cast<const uint2 *>(&sm.vt[w][l16][32 * pi + 16 + 4 * g4])
-                                                       : make_uint2(0, 0);
-                    const bf16x8 Bw = ld16(rb + R::w_off + (size_t(tb * 2 + pi) * 64 + lane) * 16);
-                    oacc[tb] = mfma(as_bf16x8(a.x, a.y, e.x, e.y), Bw, oacc[tb]);
-                }
-                const int tq = 16 * tb + l16;
-                if (tq < nval) {
-                    const uint2 ov = make_uint2(pack2(oacc[tb][0], oacc[tb][1]), pack2(oacc[tb][2], oacc[tb][3]));
-                    *reinterpret_cast<uint2 *>(og + static_cast<size_t>(t0 + tq) * D + w * kTile + 4 * g4) = ov;
-                }
-            }
-        }
-
-        // ---- state update to the chunk end: rescale to the new basis, then K^T V' on MFMA
-        {
-            const float4 ch = *reinterpret_cast<const float4 *>(co + kCoChunk);   // rX, cHX, cHY, m1
-            if (t0 > 0) {
-#pragma unroll
-                for (int jb = 0; jb < JB; ++jb)
+            for (int jj = 0; jj < 2; ++jj) {
+                const int jb = 2 * ks + jj;
+                if (t0 > 0) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         X[jb][i] = ch.x * X[jb][i] + ch.y * Hm[jb][i];
                         Y[jb][i] = Y[jb][i] + ch.z * Hm[jb][i];
                     }
+                }
+#pragma unroll
+                for (int ks2 = 0; ks2 < kC / 32; ++ks2) {
+                    const bf16x8 Ak = ld16(rb + R::k_off + (size_t(jb * 2 + ks2) * 64 + lane) * 16);
+                    X[jb] = mfma(Ak, BX[ks2], X[jb]);
+                    Y[jb] = mfma(Ak, BY[ks2], Y[jb]);
+                    Hm[jb] = mfma(Ak, BH[ks2], Hm[jb]);
+                }
+            }
+        }
+        if (PASS1) {
+            if (t0 > 0) {
                 Hs = ch.x * Hs + ch.y;
                 Rs = ch.x * Rs;
                 Ys = Ys + ch.z;
@@ -639,27 +623,36 @@ __global__ __launch_bounds__(D * 4) void causal_seg_kernel(Problem p, CausalWork
                 Rs = 0.f;                    // the first chunk of the sequence starts from nothing
                 Hs = 0.f;
             }
+        } else {
+            // ---- outputs: coefficients on the carried-state products, plus V^T W^T (intra-chunk)
 #pragma unroll
-            for (int ks2 = 0; ks2 < kC / 32; ++ks2) {
-                const int kk0 = 32 * ks2 + 8 * g4;
-                const bf16x8 BX = *reinterpret_cast<const bf16x8 *>(&sm.vx[w][l16][kk0]);
-                const bf16x8 BY = *reinterpret_cast<const bf16x8 *>(&sm.vy[w][l16][kk0]);
-                const bf16x8 BH = *reinterpret_cast<const bf16x8 *>(&sm.vt[w][l16][kk0]);
+            for (int tb = 0; tb < 4; ++tb) {
+                f32x4 oacc;
+                const float4 cq = *reinterpret_cast<const float4 *>(co + kCoQ + 4 * (16 * tb + l16));  // cX, beta, kappa
 #pragma unroll
-                for (int jb = 0; jb < JB; ++jb) {
-                    const bf16x8 Ak = ld16(rb + R::k_off + (size_t(jb * 2 + ks2) * 64 + lane) * 16);
-                    X[jb] = mfma(Ak, BX, X[jb]);
-                    Y[jb] = mfma(Ak, BY, Y[jb]);
-                    Hm[jb] = mfma(Ak, BH, Hm[jb]);
+                for (int i = 0; i < 4; ++i) oacc[i] = carried ? cq.x * ax[tb][i] + cq.y * ay[tb][i] + cq.z * ah[tb][i] : 0.f;
+#pragma unroll
+                for (int pi = 0; pi < 2; ++pi) {
+                    if (2 * pi > tb) continue;
+                    const uint2 a = VA[pi];
+                    const uint2 e = (2 * pi + 1 <= tb) ? VC[pi] : make_uint2(0, 0);
+                    const bf16x8 Bw = ld16(rb + R::w_off + (size_t(tb * 2 + pi) * 64 + lane) * 16);
+                    oacc = mfma(as_bf16x8(a.x, a.y, e.x, e.y), Bw, oacc);
                 }
+                // rows past the end go to a sink in the workspace: the store is unconditional, so the
+                // waits for the next chunk's loads never have to cover an optional store
+                const int tq = 16 * tb + l16;
+                uint16_t *dst = tq < nval ? og + static_cast<size_t>(t0 + tq) * D : work.sink + static_cast<size_t>(tq) * D;
+                const uint2 ov = make_uint2(pack2(oacc[0], oacc[1]), pack2(oacc[2], oacc[3]));
+                *reinterpret_cast<uint2 *>(dst + w * kTile + 4 * g4) = ov;
             }
         }
-        ZEROS_PUT_REC(b ^ 1);     // the other buffer was last read before the previous barrier
-        lds_barrier();            // record of chunk c + 1 visible; this chunk's buffer free
+        __syncthreads();          // copies of chunk c + 1 landed (vmcnt) and visible; this buffer free
+    };
+    for (int c = c_begin; c < c_end; c += 2) {
+        chunk(c, recA, recB);
+        if (c + 1 < c_end) chunk(c + 1, recB, recA);
     }
-
-#undef ZEROS_FETCH
-#undef ZEROS_PUT_REC
 
     if (PASS1) {
         // segment-local sums and the composed scalar map, for the combine step
@@ -750,8 +743,6 @@ hipError_t launch_one(const Problem &p, const CausalWork &w, hipStream_t stream)
     static bool attr_set = false;   // idempotent; a race only repeats the same calls
     if (!attr_set) {
         hipError_t err = set_smem(&causal_prep_kernel<D, ROPE>, sizeof(PSmem<D>));
-        if (err == hipSuccess) err = set_smem(&causal_seg_kernel<D, ROPE, false>, sizeof(SSmem<D>));
-        if (err == hipSuccess) err = set_smem(&causal_seg_kernel<D, ROPE, true>, sizeof(SSmem<D>));
         if (err != hipSuccess) return err;
         attr_set = true;
     }
@@ -769,15 +760,14 @@ hipError_t launch_one(const Problem &p, const CausalWork &w, hipStream_t stream)
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if (w.nseg > 1) {
-        hipLaunchKernelGGL((causal_seg_kernel<D, ROPE, true>), dim3(bh * (w.nseg - 1)), dim3(D * 4),
-                           sizeof(SSmem<D>), stream, p, w);
+        hipLaunchKernelGGL((causal_seg_kernel<D, ROPE, true>), dim3(bh * (w.nseg - 1)), dim3(D * 4), 0,
+                           stream, p, w);
         if ((err = hipGetLastError()) != hipSuccess) return err;
         hipLaunchKernelGGL((causal_seg_combine_kernel<D>), dim3(bh, (D * D / 4 + 255) / 256), dim3(256), 0,
                            stream, w);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
-    hipLaunchKernelGGL((causal_seg_kernel<D, ROPE, false>), dim3(bh * w.nseg), dim3(D * 4), sizeof(SSmem<D>),
-                       stream, p, w);
+    hipLaunchKernelGGL((causal_seg_kernel<D, ROPE, false>), dim3(bh * w.nseg), dim3(D * 4), 0, stream, p, w);
     return hipGetLastError();
 }
 
@@ -805,7 +795,8 @@ size_t causal_work_bytes(int B, int H, int N, int du) {
     int nseg, seg_chunks;
     seg_plan(B, H, N, nseg, seg_chunks);
     return up(bh * N * 4) + up(bh * nls * du * 4) + up(bh * nch * 16) + up(size_t(kC) * (du / 2) * 8) +
-           up(bh * nseg * 16) + up(bh * (nseg - 1) * size_t(3) * du * du * 4) + bh * nch * causal_rec_bytes(du);
+           up(bh * nseg * 16) + up(bh * (nseg - 1) * size_t(3) * du * du * 4) + up(size_t(kC) * du * 2) +
+           bh * nch * causal_rec_bytes(du);
 }
 
 CausalWork causal_work_carve(void *base, int B, int H, int N, int du) {
@@ -829,6 +820,8 @@ CausalWork causal_work_carve(void *base, int B, int H, int N, int du) {
     b += up(bh * w.nseg * 16);
     w.segst = reinterpret_cast<float *>(b);
     b += up(bh * (w.nseg - 1) * size_t(3) * du * du * 4);
+    w.sink = reinterpret_cast<uint16_t *>(b);
+    b += up(size_t(kC) * du * 2);
     w.rec = reinterpret_cast<unsigned char *>(b);
     return w;
 }

@@ -32,6 +32,7 @@ struct CausalWork {
     float2 *rope;       // [kCausalChunk, d/2] cos, sin of r * theta_j (RoPE only)
     float4 *segsc;      // [B*H, nseg] composed scalar map (Rs, Hs, Ys, 0) of each scan segment
     float *segst;       // [B*H, nseg-1, 3, d, d] segment-local sums, then segment start states
+    uint16_t *sink;     // [kCausalChunk, d] bf16: output rows past N are written here and ignored
     int nseg;           // scan segments per head
     int seg_chunks;     // chunks per segment (the last one may be shorter)
     unsigned char *rec; // [B*H, nchunk, rec_bytes(d)] per-chunk operands prepared for the scan

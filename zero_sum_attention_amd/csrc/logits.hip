@@ -79,11 +79,21 @@ __global__ __launch_bounds__(kThreads) void useg_sum_kernel(const T *u, float *u
     const int r0 = seg * kLogitSeg, r1 = min(N, r0 + kLogitSeg);
     const T *ub = u + static_cast<size_t>(bh) * N * D;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int r = r0 + rg; r < r1; r += RPI) {
-        float x[8];
-        load8(ub + static_cast<size_t>(r) * D + c0, x);
+    constexpr int U = 8;                       // rows in flight per thread
+    for (int rb = r0 + rg; rb < r1; rb += U * RPI) {
+        float x[U][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += x[i];
+        for (int k = 0; k < U; ++k) {
+            const int r = rb + k * RPI;
+            if (r < r1) load8(ub + static_cast<size_t>(r) * D + c0, x[k]);
+            else
+#pragma unroll
+                for (int i = 0; i < 8; ++i) x[k][i] = 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] += x[k][i];
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) part[rg][c0 + i] = acc[i];
@@ -157,6 +167,122 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(const T *u, const floa
     }
 }
 
+// Logits of one segment, bfloat16 u, by serial token streams: lane (stream st, feature group fg)
+// keeps the running sum of features [8 fg, 8 fg + 8) over the TPS consecutive tokens of its stream
+// (held in registers), so each token costs 3 float ops per feature and no cross-lane scan. The
+// stream starts come from the stream sums (first pass over the registers); the per-token dot
+// partials of the LPT lanes of a stream are summed by a butterfly that leaves token k on lane k.
+constexpr int kStreamThreads = 512;
+
+template <int D>
+__global__ __launch_bounds__(kStreamThreads) void logits_stream_kernel(const bf16 *u, const float *mu, const float *tau,
+                                                                 const float *useg, float *s_out, float4 *agg,
+                                                                 int N, int H, int nseg) {
+    constexpr int LPT = D / 8;                 // lanes per token row
+    constexpr int NS = kStreamThreads / LPT;   // streams
+    constexpr int TPS = kLogitSeg / NS;        // tokens per stream
+    static_assert(TPS % LPT == 0 && LPT <= 16 && D <= kStreamThreads, "stream shape");
+    __shared__ float c0s[D];
+    __shared__ float part[NS][D + 1];
+    __shared__ float sv[kLogitSeg];
+    const int seg = blockIdx.x % nseg;
+    const int bh = blockIdx.x / nseg;
+    const int h = bh % H;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int st = tid / LPT, fg = tid % LPT, l = lane % LPT;
+    const float et = expf(tau[h]);
+    if (tid < D) {
+        float c = et * mu[h * D + tid];
+        const float *us = useg + static_cast<size_t>(bh) * nseg * D + tid;
+        for (int q = 0; q < seg; ++q) c += us[static_cast<size_t>(q) * D];
+        c0s[tid] = c;
+    }
+    const bf16 *ub = u + static_cast<size_t>(bh) * N * D;
+    const int r0 = seg * kLogitSeg + st * TPS;
+    uint4 x[TPS];
+#pragma unroll
+    for (int k = 0; k < TPS; ++k) {
+        const int r = r0 + k;
+        x[k] = r < N ? *reinterpret_cast<const uint4 *>(ub + static_cast<size_t>(r) * D + 8 * fg) : make_uint4(0, 0, 0, 0);
+    }
+    float cs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < TPS; ++k) {
+        const uint32_t wv[4] = {x[k].x, x[k].y, x[k].z, x[k].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            cs[2 * i] += __uint_as_float(wv[i] << 16);
+            cs[2 * i + 1] += __uint_as_float(wv[i] & 0xffff0000u);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) part[st][8 * fg + i] = cs[i];
+    __syncthreads();
+    if (tid < D) {                             // exclusive scan over the streams, one feature per thread
+        float run = c0s[tid];
+        for (int q = 0; q < NS; ++q) {
+            const float t = part[q][tid];
+            part[q][tid] = run;
+            run += t;
+        }
+    }
+    __syncthreads();
+    float R[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) R[i] = part[st][8 * fg + i];
+    float d[TPS];
+#pragma unroll
+    for (int k = 0; k < TPS; ++k) {
+        const uint32_t wv[4] = {x[k].x, x[k].y, x[k].z, x[k].w};
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float a = __uint_as_float(wv[i] << 16), b = __uint_as_float(wv[i] & 0xffff0000u);
+            R[2 * i] += a;
+            R[2 * i + 1] += b;
+            acc = fmaf(a, R[2 * i], acc);
+            acc = fmaf(b, R[2 * i + 1], acc);
+        }
+        d[k] = acc;
+    }
+    // butterfly over the LPT lanes of a stream, LPT tokens at a time: token b*LPT + l ends on lane l
+    const float rs_du = 1.f / sqrtf(static_cast<float>(D));
+#pragma unroll
+    for (int b = 0; b < TPS / LPT; ++b) {
+        float v[LPT];
+#pragma unroll
+        for (int i = 0; i < LPT; ++i) v[i] = d[b * LPT + i];
+#pragma unroll
+        for (int off = LPT / 2; off >= 1; off >>= 1) {
+            const bool hi = (l & off) != 0;
+#pragma unroll
+            for (int i = 0; i < off; ++i) {
+                const float keep = hi ? v[off + i] : v[i];
+                const float send = hi ? v[i] : v[off + i];
+                v[i] = keep + __shfl_xor(send, off, 64);
+            }
+        }
+        const int tk = st * TPS + b * LPT + l;          // token inside the segment
+        const int row = seg * kLogitSeg + tk;
+        sv[tk] = -v[0] * rs_du / (et + static_cast<float>(row + 1));
+    }
+    __syncthreads();
+    // write s and the aggregates of each 64-token chunk (segments are whole chunks)
+    const int r1 = min(N, (seg + 1) * kLogitSeg);
+    const int w = tid >> 6;
+    for (int cb = w; cb < kLogitSeg / 64; cb += kStreamThreads / 64) {
+        const int row = seg * kLogitSeg + cb * 64 + lane;
+        if (seg * kLogitSeg + cb * 64 >= r1) break;
+        const bool valid = row < r1;
+        const float s = sv[cb * 64 + lane];
+        if (valid) s_out[static_cast<size_t>(bh) * N + row] = s;
+        const float mx = lane_f(wave_scan_max(valid ? s : kNegInf), 63);
+        const float se = lane_f(wave_scan_add(valid ? __expf(s - mx) : 0.f), 63);
+        const float ss = lane_f(wave_scan_add(valid ? s : 0.f), 63);
+        if (lane == 0) agg[static_cast<size_t>(bh) * ((N + 63) / 64) + (seg * kLogitSeg) / 64 + cb] = make_float4(mx, se, ss, 0.f);
+    }
+}
+
 template <int D, typename T>
 hipError_t launch_t(const Problem &p, float *useg, float *s_out, float4 *agg, hipStream_t stream) {
     const int nseg = (p.N + kLogitSeg - 1) / kLogitSeg;
@@ -165,8 +291,13 @@ hipError_t launch_t(const Problem &p, float *useg, float *s_out, float4 *agg, hi
                        static_cast<const T *>(p.u), useg, p.N, nseg);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((logits_kernel<D, T>), dim3(grid), dim3(kThreads), 0, stream,
-                       static_cast<const T *>(p.u), p.mu, p.tau, useg, s_out, agg, p.N, p.H, nseg);
+    if constexpr (sizeof(T) == 2 && (D == 64 || D == 128)) {
+        hipLaunchKernelGGL((logits_stream_kernel<D>), dim3(grid), dim3(kStreamThreads), 0, stream,
+                           static_cast<const bf16 *>(p.u), p.mu, p.tau, useg, s_out, agg, p.N, p.H, nseg);
+    } else {
+        hipLaunchKernelGGL((logits_kernel<D, T>), dim3(grid), dim3(kThreads), 0, stream,
+                           static_cast<const T *>(p.u), p.mu, p.tau, useg, s_out, agg, p.N, p.H, nseg);
+    }
     return hipGetLastError();
 }
 

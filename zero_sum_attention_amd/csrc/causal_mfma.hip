@@ -456,8 +456,7 @@ __global__ __launch_bounds__(D * 4) void causal_seg_kernel(Problem p, CausalWork
     constexpr int NT = NW * 64;
     constexpr int KS = D / 32;          // 32-feature steps of the carried-state products
     constexpr int JB = D / 16;          // 16-row state tiles
-    constexpr int NREC = (int(R::bytes / 16) + NT - 1) / NT;   // 16-byte record pieces per thread
-    constexpr int kPieces = int(R::bytes / 16);
+    constexpr int kPieces = int(R::bytes / 16);                 // 16-byte pieces of a record
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -500,19 +499,29 @@ __global__ __launch_bounds__(D * 4) void causal_seg_kernel(Problem p, CausalWork
     const int vtok = 2 * (lane & 31), vh = lane >> 5;
     const size_t vcol = static_cast<size_t>(w) * kTile + 8 * vh;
     uint4 va, vb;
-    // v rows of chunk c into registers, and record chunk c into LDS buffer dst (direct copies:
-    // wave w moves pieces [64 w + NT i, 64 w + NT i + 64) of the record; lanes past the end repeat
-    // the last piece into the padding of the buffer)
+    // record pieces [p0, p1) of chunk c into LDS buffer dst at their record offsets (direct copies:
+    // wave w moves pieces p0 + 64 w + NT i + lane; lanes past p1 repeat the last piece into the
+    // padding of the buffer, which ends on a whole 64-piece copy)
+    auto copy_range = [&](const uint4 *src, unsigned char *dst, const int p0, const int p1) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < (p1 - p0 + NT - 1) / NT; ++i) {
+            const int base = p0 + w * 64 + i * NT;               // wave-uniform
+            if (base < p1)
+                __builtin_amdgcn_global_load_lds(src + min(base + lane, p1 - 1), dst + base * 16, 16, 0, 0);
+        }
+    };
+    // v rows of chunk c into registers, and the record parts this pass reads into LDS buffer dst:
+    // the whole record for the main pass, the k^T operands and the coefficients for pass 1
     auto fetch = [&](const int c, unsigned char *dst) __attribute__((always_inline)) {
         const int t_ = c * kC + vtok;      // rows past N read row N-1 (in bounds), zeroed when staged
         va = *reinterpret_cast<const uint4 *>(vg + static_cast<size_t>(min(t_, N - 1)) * D + vcol);
         vb = *reinterpret_cast<const uint4 *>(vg + static_cast<size_t>(min(t_ + 1, N - 1)) * D + vcol);
         const uint4 *src = reinterpret_cast<const uint4 *>(rec0 + static_cast<size_t>(c) * R::bytes);
-#pragma unroll
-        for (int i = 0; i < NREC; ++i) {
-            const int base = w * 64 + i * NT;                    // wave-uniform
-            if (base < kPieces)
-                __builtin_amdgcn_global_load_lds(src + min(base + lane, kPieces - 1), dst + base * 16, 16, 0, 0);
+        if (PASS1) {
+            copy_range(src, dst, int(R::k_off / 16), int(R::w_off / 16));
+            copy_range(src, dst, int(R::c_off / 16), kPieces);
+        } else {
+            copy_range(src, dst, 0, kPieces);
         }
     };
 

@@ -230,7 +230,7 @@ __global__ __launch_bounds__(kStreamThreads) void logits_stream_kernel(const bf1
     float R[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) R[i] = part[st][8 * fg + i];
-    float d[TPS];
+    float d[TPS];                              // per-token dot partials, reduced in place below
 #pragma unroll
     for (int k = 0; k < TPS; ++k) {
         const uint32_t wv[4] = {x[k].x, x[k].y, x[k].z, x[k].w};
@@ -249,9 +249,7 @@ __global__ __launch_bounds__(kStreamThreads) void logits_stream_kernel(const bf1
     const float rs_du = 1.f / sqrtf(static_cast<float>(D));
 #pragma unroll
     for (int b = 0; b < TPS / LPT; ++b) {
-        float v[LPT];
-#pragma unroll
-        for (int i = 0; i < LPT; ++i) v[i] = d[b * LPT + i];
+        float *v = d + b * LPT;
 #pragma unroll
         for (int off = LPT / 2; off >= 1; off >>= 1) {
             const bool hi = (l & off) != 0;

@@ -170,6 +170,30 @@ def test_encoder_shapes(d, N, dtype, rope):
         assert rel_l2(o, ref) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [64, 65, 300, 1000])
+@pytest.mark.parametrize("rope", [False, True])
+def test_encoder_mfma_chunks(d, N, rope):
+    """bfloat16 encoder on the matrix cores: several 64-token state chunks and 16-token output
+    blocks, ragged tails, both head dims."""
+    wl = CONFIGS[3].with_(B=1, H=2, N=N, d=d, d_u=d, dtype="bf16", seed=3000 + d + N)
+    x = make_inputs(wl)
+    o = to_f64(run_encoder(x, "bf16", rope=rope))
+    ref = R.encoder_forward(**x, rope=rope)
+    err = rel_l2(o, ref)
+    print(f"encoder mfma d={d} N={N} rope={rope} rel_l2={err:.3e}", flush=True)
+    assert err <= TOL["bf16"]
+
+
+def test_encoder_mfma_large_logits():
+    """u scaled by 30: logits spread over a wide range, the global maximum keeps e^{s-m} in range."""
+    wl = CONFIGS[3].with_(B=1, H=2, N=300, d=64, d_u=64, dtype="bf16", seed=3999)
+    x = make_inputs(wl, u_scale=30.0)
+    o = to_f64(run_encoder(x, "bf16"))
+    ref = R.encoder_forward(**x)
+    assert rel_l2(o, ref) <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("scale,tol", [(10.0, 1e-4), (30.0, 1e-3)])
 def test_logit_stress_running_max(scale, tol):
     wl = CONFIGS[2].with_(B=1, H=4, N=300, seed=77)

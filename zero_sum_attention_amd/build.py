@@ -25,6 +25,7 @@ SOURCES = [
     "causal_mfma.hip",
     "logits.hip",
     "encoder_valu.hip",
+    "encoder_mfma.hip",
     "decode.hip",
 ]
 

@@ -132,7 +132,7 @@ def test_workspace_size_and_validation(lib):
     n = lib.zeros_fwd_causal_workspace_bytes(ctypes.byref(bf))
     bh, nch = 2 * 16, 16384 // 64
     logits = bh * 16384 * 4
-    useg = bh * (16384 // 512) * 128 * 4
+    useg = bh * (16384 // 256) * 128 * 4
     agg = bh * nch * 16                                  # (max, sum e, sum s, pad) per 64-token chunk
     rope = 64 * (128 // 2) * 8                           # cos, sin per (in-chunk offset, feature pair)
     nseg = 8                                             # scan segments per head: 32 heads x 8 >= 256

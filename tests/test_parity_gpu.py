@@ -141,6 +141,31 @@ def test_causal_mfma_state_out(rope):
         assert rel_l2(got[key], ref[key]) <= 2e-2, key
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_causal_segments_ragged_sampled_heads(d):
+    """32 heads, N = 3000: 47 chunks cut into 8 scan segments of 6 chunks (the last one 5 chunks,
+    its last chunk 56 tokens), chained by pass 1 and the segment combine; outputs and the final
+    recurrent state of sampled heads against the oracle."""
+    wl = CONFIGS[4].with_(B=2, H=16, N=3000, d=d, d_u=d, seed=3300 + d)
+    x = make_inputs(wl)
+    st = Z.DecodeState(2, 16, d, d).reset()
+    o = run_causal(x, "bf16", rope=True, state_out=st)
+    pairs = [(0, 0), (1, 7), (0, 15)]
+    xs = slice_heads(x, pairs)
+    ref, ref_st = R.causal_forward(**xs, rope=True, return_state=True)
+    got = np.stack([to_f64(o[b, h]) for b, h in pairs])[None]
+    err = rel_l2(got, ref)
+    print(f"segments d={d} N=3000 sampled rel_l2={err:.3e}", flush=True)
+    assert err <= TOL["bf16"]
+    gst = _state_np(st)
+    for key in ("m", "E", "P", "Su"):
+        g = np.stack([gst[key][b, h] for b, h in pairs])[None]
+        assert rel_l2(g, ref_st[key]) <= 1e-5, key
+    for key in ("F", "G", "H"):
+        g = np.stack([gst[key][b, h] for b, h in pairs])[None]
+        assert rel_l2(g, ref_st[key]) <= 2e-2, key
+
+
 def test_causal_workspace_reuse():
     wl = CONFIGS[4].with_(B=1, H=3, N=700, seed=3200)
     x = make_inputs(wl)

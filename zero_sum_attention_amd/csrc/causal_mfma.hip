@@ -179,18 +179,6 @@ struct alignas(16) PSmem {
     float2 rot0[D / 2];                        // cos, sin of t0 * theta_j (chunk start)
 };
 
-// cos, sin of r * theta_j for the in-chunk offsets r in [0, kC) and feature pairs j in [0, D/2):
-// the rotations the prep kernel applies to q and k (every chunk uses the same table).
-template <int D>
-__global__ __launch_bounds__(256) void rope_table_kernel(float2 *tab, float base) {
-    const int idx = blockIdx.x * 256 + threadIdx.x;
-    if (idx >= kC * (D / 2)) return;
-    const int r = idx / (D / 2), j = idx % (D / 2);
-    float c, s;
-    rope_cos_sin(rope_rev_per_pos(j, D, base), r, c, s);
-    tab[idx] = make_float2(c, s);
-}
-
 template <int D, bool ROPE>
 __global__ __launch_bounds__(kPrepThreads) void causal_prep_kernel(Problem p, CausalWork work) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -687,26 +675,42 @@ __global__ __launch_bounds__(D * 4) void causal_seg_kernel(Problem p, CausalWork
 template <int D>
 __global__ __launch_bounds__(256) void causal_seg_combine_kernel(CausalWork work) {
     constexpr size_t Q = size_t(D) * D / 4;              // float4 positions per state matrix
+    constexpr int kMaxSeg = 8;                           // segment-local sums loaded up front
     const size_t pos = static_cast<size_t>(blockIdx.y) * 256 + threadIdx.x;
     if (pos >= Q) return;
     const int bh = blockIdx.x;
     const int nseg = work.nseg;
     float4 x = make_float4(0.f, 0.f, 0.f, 0.f), y = x, h = x;
-    for (int j = 0; j + 1 < nseg; ++j) {
-        float4 *st = reinterpret_cast<float4 *>(work.segst + (static_cast<size_t>(bh) * (nseg - 1) + j) * kSegFloats<D>);
-        const float4 m = work.segsc[static_cast<size_t>(bh) * nseg + j];   // Rs, Hs, Ys
-        const float4 lx = st[pos], ly = st[Q + pos], lh = st[2 * Q + pos];
-        const float4 nx = make_float4(m.x * x.x + m.y * h.x + lx.x, m.x * x.y + m.y * h.y + lx.y,
-                                      m.x * x.z + m.y * h.z + lx.z, m.x * x.w + m.y * h.w + lx.w);
-        const float4 ny = make_float4(y.x + m.z * h.x + ly.x, y.y + m.z * h.y + ly.y,
-                                      y.z + m.z * h.z + ly.z, y.w + m.z * h.w + ly.w);
-        const float4 nh = make_float4(h.x + lh.x, h.y + lh.y, h.z + lh.z, h.w + lh.w);
-        st[pos] = nx;
-        st[Q + pos] = ny;
-        st[2 * Q + pos] = nh;
-        x = nx;
-        y = ny;
-        h = nh;
+    for (int j0 = 0; j0 + 1 < nseg; j0 += kMaxSeg) {
+        const int nj = min(kMaxSeg, nseg - 1 - j0);
+        float4 lx[kMaxSeg], ly[kMaxSeg], lh[kMaxSeg];
+#pragma unroll
+        for (int jj = 0; jj < kMaxSeg; ++jj) {
+            if (jj < nj) {
+                const float4 *st = reinterpret_cast<const float4 *>(work.segst + (static_cast<size_t>(bh) * (nseg - 1) + j0 + jj) * kSegFloats<D>);
+                lx[jj] = st[pos];
+                ly[jj] = st[Q + pos];
+                lh[jj] = st[2 * Q + pos];
+            }
+        }
+#pragma unroll
+        for (int jj = 0; jj < kMaxSeg; ++jj) {
+            if (jj < nj) {
+                float4 *st = reinterpret_cast<float4 *>(work.segst + (static_cast<size_t>(bh) * (nseg - 1) + j0 + jj) * kSegFloats<D>);
+                const float4 m = work.segsc[static_cast<size_t>(bh) * nseg + j0 + jj];   // Rs, Hs, Ys
+                const float4 nx = make_float4(m.x * x.x + m.y * h.x + lx[jj].x, m.x * x.y + m.y * h.y + lx[jj].y,
+                                              m.x * x.z + m.y * h.z + lx[jj].z, m.x * x.w + m.y * h.w + lx[jj].w);
+                const float4 ny = make_float4(y.x + m.z * h.x + ly[jj].x, y.y + m.z * h.y + ly[jj].y,
+                                              y.z + m.z * h.z + ly[jj].z, y.w + m.z * h.w + ly[jj].w);
+                const float4 nh = make_float4(h.x + lh[jj].x, h.y + lh[jj].y, h.z + lh[jj].z, h.w + lh[jj].w);
+                st[pos] = nx;
+                st[Q + pos] = ny;
+                st[2 * Q + pos] = nh;
+                x = nx;
+                y = ny;
+                h = nh;
+            }
+        }
     }
 }
 
@@ -727,11 +731,6 @@ hipError_t launch_one(const Problem &p, const CausalWork &w, hipStream_t stream)
     const int nch = (p.N + kC - 1) / kC;
     const int bh = p.B * p.H;
     hipError_t err;
-    if (ROPE && nch > 0) {
-        hipLaunchKernelGGL((rope_table_kernel<D>), dim3((kC * (D / 2) + 255) / 256), dim3(256), 0, stream,
-                           w.rope, p.rope_base);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
-    }
     if (nch > 0) {
         hipLaunchKernelGGL((causal_prep_kernel<D, ROPE>), dim3(bh * nch), dim3(kPrepThreads),
                            sizeof(PSmem<D>), stream, p, w);
@@ -805,7 +804,7 @@ CausalWork causal_work_carve(void *base, int B, int H, int N, int du) {
 }
 
 hipError_t launch_causal_mfma(const Problem &p, const CausalWork &w, hipStream_t stream) {
-    hipError_t err = launch_logits(p, w.useg, w.s, w.agg, stream);
+    hipError_t err = launch_logits(p, w.useg, w.s, w.agg, p.rope ? w.rope : nullptr, stream);
     if (err != hipSuccess) return err;
     if (p.d == 128) return p.rope ? launch_one<128, true>(p, w, stream) : launch_one<128, false>(p, w, stream);
     if (p.d == 64) return p.rope ? launch_one<64, true>(p, w, stream) : launch_one<64, false>(p, w, stream);

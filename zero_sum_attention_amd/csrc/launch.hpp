@@ -21,7 +21,7 @@ struct Problem {
 };
 
 // Tokens per segment of the two-pass logit computation, and per chunk of the causal scan.
-constexpr int kLogitSeg = 512;
+constexpr int kLogitSeg = 256;
 constexpr int kCausalChunk = 64;
 
 // Workspace of the causal MFMA path, carved from one caller- or library-provided buffer.
@@ -41,7 +41,10 @@ size_t causal_rec_bytes(int d);
 size_t causal_work_bytes(int B, int H, int N, int du);
 CausalWork causal_work_carve(void *base, int B, int H, int N, int du);
 
-hipError_t launch_logits(const Problem &p, float *useg, float *s_out, float4 *agg, hipStream_t stream);
+// Logits of the causal MFMA path; when rope_tab is not null it also fills the in-chunk RoPE angle
+// table [kCausalChunk, d/2] (cos, sin of r * theta_j) used by the prep kernel.
+hipError_t launch_logits(const Problem &p, float *useg, float *s_out, float4 *agg, float2 *rope_tab,
+                         hipStream_t stream);
 hipError_t launch_causal_mfma(const Problem &p, const CausalWork &w, hipStream_t stream);
 hipError_t launch_causal(const Problem &p, hipStream_t stream);
 hipError_t launch_encoder(const Problem &p, hipStream_t stream);

@@ -68,7 +68,8 @@ __device__ __forceinline__ void load_feats(const T *p, bool valid, float (&x)[NE
 
 // Column sums of u over one segment: 8 consecutive features per thread, rows strided.
 template <int D, typename T>
-__global__ __launch_bounds__(kThreads) void useg_sum_kernel(const T *u, float *useg, int N, int nseg) {
+__global__ __launch_bounds__(kThreads) void useg_sum_kernel(const T *u, float *useg, int N, int nseg,
+                                                            float2 *rope_tab, float rope_base) {
     constexpr int VPR = D / 8;                 // threads per row
     constexpr int RPI = kThreads / VPR;        // rows per iteration
     __shared__ float part[RPI][D + 1];
@@ -78,6 +79,13 @@ __global__ __launch_bounds__(kThreads) void useg_sum_kernel(const T *u, float *u
     const int c0 = (tid % VPR) * 8, rg = tid / VPR;
     const int r0 = seg * kLogitSeg, r1 = min(N, r0 + kLogitSeg);
     const T *ub = u + static_cast<size_t>(bh) * N * D;
+    if (rope_tab != nullptr) {           // the RoPE angle table of the prep kernel, spread over the grid
+        for (int e = blockIdx.x * kThreads + tid; e < kCausalChunk * (D / 2); e += gridDim.x * kThreads) {
+            float c, sn;
+            rope_cos_sin(rope_rev_per_pos(e % (D / 2), D, rope_base), e / (D / 2), c, sn);
+            rope_tab[e] = make_float2(c, sn);
+        }
+    }
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     constexpr int U = 8;                       // rows in flight per thread
     for (int rb = r0 + rg; rb < r1; rb += U * RPI) {
@@ -172,7 +180,7 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(const T *u, const floa
 // (held in registers), so each token costs 3 float ops per feature and no cross-lane scan. The
 // stream starts come from the stream sums (first pass over the registers); the per-token dot
 // partials of the LPT lanes of a stream are summed by a butterfly that leaves token k on lane k.
-constexpr int kStreamThreads = 512;
+constexpr int kStreamThreads = 256;
 
 template <int D>
 __global__ __launch_bounds__(kStreamThreads) void logits_stream_kernel(const bf16 *u, const float *mu, const float *tau,
@@ -282,11 +290,11 @@ __global__ __launch_bounds__(kStreamThreads) void logits_stream_kernel(const bf1
 }
 
 template <int D, typename T>
-hipError_t launch_t(const Problem &p, float *useg, float *s_out, float4 *agg, hipStream_t stream) {
+hipError_t launch_t(const Problem &p, float *useg, float *s_out, float4 *agg, float2 *rope_tab, hipStream_t stream) {
     const int nseg = (p.N + kLogitSeg - 1) / kLogitSeg;
     const int grid = p.B * p.H * nseg;
     hipLaunchKernelGGL((useg_sum_kernel<D, T>), dim3(grid), dim3(kThreads), 0, stream,
-                       static_cast<const T *>(p.u), useg, p.N, nseg);
+                       static_cast<const T *>(p.u), useg, p.N, nseg, rope_tab, p.rope_base);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     if constexpr (sizeof(T) == 2 && (D == 64 || D == 128)) {
@@ -300,20 +308,21 @@ hipError_t launch_t(const Problem &p, float *useg, float *s_out, float4 *agg, hi
 }
 
 template <int D>
-hipError_t launch_d(const Problem &p, float *useg, float *s_out, float4 *agg, hipStream_t stream) {
-    return p.dtype == ZEROS_BF16 ? launch_t<D, bf16>(p, useg, s_out, agg, stream)
-                                 : launch_t<D, float>(p, useg, s_out, agg, stream);
+hipError_t launch_d(const Problem &p, float *useg, float *s_out, float4 *agg, float2 *rope_tab, hipStream_t stream) {
+    return p.dtype == ZEROS_BF16 ? launch_t<D, bf16>(p, useg, s_out, agg, rope_tab, stream)
+                                 : launch_t<D, float>(p, useg, s_out, agg, rope_tab, stream);
 }
 
 }  // namespace
 
-hipError_t launch_logits(const Problem &p, float *useg, float *s_out, float4 *agg, hipStream_t stream) {
+hipError_t launch_logits(const Problem &p, float *useg, float *s_out, float4 *agg, float2 *rope_tab,
+                         hipStream_t stream) {
     if (p.N == 0) return hipSuccess;
     switch (p.d) {
-        case 16: return launch_d<16>(p, useg, s_out, agg, stream);
-        case 32: return launch_d<32>(p, useg, s_out, agg, stream);
-        case 64: return launch_d<64>(p, useg, s_out, agg, stream);
-        case 128: return launch_d<128>(p, useg, s_out, agg, stream);
+        case 16: return launch_d<16>(p, useg, s_out, agg, rope_tab, stream);
+        case 32: return launch_d<32>(p, useg, s_out, agg, rope_tab, stream);
+        case 64: return launch_d<64>(p, useg, s_out, agg, rope_tab, stream);
+        case 128: return launch_d<128>(p, useg, s_out, agg, rope_tab, stream);
         default: return hipErrorInvalidValue;
     }
 }

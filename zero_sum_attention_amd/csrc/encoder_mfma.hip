@@ -155,14 +155,34 @@ __global__ __launch_bounds__(kEThreads) void encoder_mfma_kernel(Problem p) {
         for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
             for (int i = 0; i < 4; ++i) X[ft][ct][i] = Y[ft][ct][i] = 0.f;
-    for (int t0 = 0; t0 < N; t0 += kEC) {
+    // k and v rows of a chunk, read one chunk ahead
+    constexpr int JR = kEC / RPP;
+    uint4 kn[JR], vn[JR];
+    auto load_kv = [&](const int t0) __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < kEC / RPP; ++j) {
+        for (int j = 0; j < JR; ++j) {
+            const int r = t0 + rr + RPP * j;
+            const size_t ri = static_cast<size_t>(min(r, N - 1)) * D + 8 * fr;   // in bounds; zeroed below
+            kn[j] = *reinterpret_cast<const uint4 *>(k + ri);
+            vn[j] = *reinterpret_cast<const uint4 *>(v + ri);
+        }
+    };
+    if (N > 0) load_kv(0);
+    for (int t0 = 0; t0 < N; t0 += kEC) {
+        uint4 kc[JR], vc[JR];
+#pragma unroll
+        for (int j = 0; j < JR; ++j) {
+            kc[j] = kn[j];
+            vc[j] = vn[j];
+        }
+        if (t0 + kEC < N) load_kv(t0 + kEC);
+#pragma unroll
+        for (int j = 0; j < JR; ++j) {
             const int rl = rr + RPP * j, r = t0 + rl;
             const bool ok = r < N;
             float kv[8], vv[8];
-            unpack8(ok ? *reinterpret_cast<const uint4 *>(k + static_cast<size_t>(r) * D + 8 * fr) : make_uint4(0, 0, 0, 0), kv);
-            unpack8(ok ? *reinterpret_cast<const uint4 *>(v + static_cast<size_t>(r) * D + 8 * fr) : make_uint4(0, 0, 0, 0), vv);
+            unpack8(ok ? kc[j] : make_uint4(0, 0, 0, 0), kv);
+            unpack8(ok ? vc[j] : make_uint4(0, 0, 0, 0), vv);
             float ss = 0.f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) ss = fmaf(kv[i], kv[i], ss);
@@ -213,17 +233,37 @@ __global__ __launch_bounds__(kEThreads) void encoder_mfma_kernel(Problem p) {
         __syncthreads();
     }
 
-    // ---- C: outputs, 16 tokens per step; each wave writes its own columns
-    for (int tb = 0; tb < (N + 15) / 16; ++tb) {
+    // ---- C: outputs, 16 tokens per step; each wave writes its own columns. The q rows and gates
+    // of the next step are read while this one computes.
+    uint2 qan[KS], qcn[KS];            // features 32ks + 4g4 + [0,4) and 32ks + 16 + 4g4 + [0,4)
+    uint32_t g1n = 0, ghn = 0;
+    auto load_q = [&](const int tb) __attribute__((always_inline)) {
+        const int t = min(16 * tb + l16, N - 1);   // in bounds; rows past N are never stored
+        const size_t tr = static_cast<size_t>(t) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            qan[ks] = *reinterpret_cast<const uint2 *>(q + tr + 32 * ks + 4 * g4);
+            qcn[ks] = *reinterpret_cast<const uint2 *>(q + tr + 32 * ks + 16 + 4 * g4);
+        }
+        g1n = g1[t];
+        ghn = gh[t];
+    };
+    const int ntb = (N + 15) / 16;
+    if (N > 0) load_q(0);
+    for (int tb = 0; tb < ntb; ++tb) {
         const int t = 16 * tb + l16;
         const bool ok = t < N;
-        const size_t tr = static_cast<size_t>(ok ? t : 0) * D;
-        uint2 qa[KS], qc[KS];          // features 32ks + 4g4 + [0,4) and 32ks + 16 + 4g4 + [0,4)
+        uint2 qa[KS], qc[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            qa[ks] = qan[ks];
+            qc[ks] = qcn[ks];
+        }
+        const uint32_t g1v = g1n, ghv = ghn;
+        if (tb + 1 < ntb) load_q(tb + 1);
         float ss = 0.f;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            qa[ks] = ok ? *reinterpret_cast<const uint2 *>(q + tr + 32 * ks + 4 * g4) : make_uint2(0, 0);
-            qc[ks] = ok ? *reinterpret_cast<const uint2 *>(q + tr + 32 * ks + 16 + 4 * g4) : make_uint2(0, 0);
             uint32_t wv[4] = {qa[ks].x, qa[ks].y, qc[ks].x, qc[ks].y};
 #pragma unroll
             for (int i = 0; i < 4; ++i) ss = dot2_bf16(wv[i], ss);
@@ -244,8 +284,8 @@ __global__ __launch_bounds__(kEThreads) void encoder_mfma_kernel(Problem p) {
         ss += __shfl_xor(ss, 16, 64);
         ss += __shfl_xor(ss, 32, 64);
         const float iq = ok ? __frsqrt_rn(fmaxf(ss, 1e-24f)) : 0.f;
-        const float s1 = ok ? __fdividef(1.f, 1.f + __expf(-lo_f(g1[t]))) : 0.f;
-        const float sh = ok ? __fdividef(1.f, 1.f + __expf(-lo_f(gh[t]))) : 0.f;
+        const float s1 = ok ? __fdividef(1.f, 1.f + __expf(-lo_f(g1v))) : 0.f;
+        const float sh = ok ? __fdividef(1.f, 1.f + __expf(-lo_f(ghv))) : 0.f;
         const float ax = sh * iq, ay = (s1 - sh) * invN * iq;
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {

@@ -183,27 +183,37 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(const T *u, const floa
 constexpr int kStreamThreads = 256;
 
 template <int D>
-__global__ __launch_bounds__(kStreamThreads) void logits_stream_kernel(const bf16 *u, const float *mu, const float *tau,
+__global__ __launch_bounds__(kStreamThreads, 4) void logits_stream_kernel(const bf16 *u, const float *mu, const float *tau,
                                                                  const float *useg, float *s_out, float4 *agg,
                                                                  int N, int H, int nseg) {
     constexpr int LPT = D / 8;                 // lanes per token row
     constexpr int NS = kStreamThreads / LPT;   // streams
     constexpr int TPS = kLogitSeg / NS;        // tokens per stream
-    static_assert(TPS % LPT == 0 && LPT <= 16 && D <= kStreamThreads, "stream shape");
-    __shared__ float c0s[D];
-    __shared__ float part[NS][D + 1];
-    __shared__ float sv[kLogitSeg];
+    constexpr int NWV = kStreamThreads / 64;   // waves
+    constexpr int G = kStreamThreads / D;      // threads per feature in the carry sum
+    static_assert(TPS == LPT && kLogitSeg == kStreamThreads && D <= kStreamThreads, "stream shape");
+    __shared__ float c0p[G][D];
+    __shared__ float wtot[NWV][D];
     const int seg = blockIdx.x % nseg;
     const int bh = blockIdx.x / nseg;
     const int h = bh % H;
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int st = tid / LPT, fg = tid % LPT, l = lane % LPT;
     const float et = expf(tau[h]);
-    if (tid < D) {
-        float c = et * mu[h * D + tid];
-        const float *us = useg + static_cast<size_t>(bh) * nseg * D + tid;
-        for (int q = 0; q < seg; ++q) c += us[static_cast<size_t>(q) * D];
-        c0s[tid] = c;
+    {
+        // prior plus the sums of u over the earlier segments: thread (feature f, phase g) adds
+        // segments g, g + G, ..., eight loads in flight at a time
+        const int f = tid % D, g = tid / D;
+        const float *us = useg + static_cast<size_t>(bh) * nseg * D + f;
+        float a[8] = {g == 0 ? et * mu[h * D + f] : 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int q0 = g; q0 < seg; q0 += 8 * G) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int q = q0 + j * G;
+                a[j] += q < seg ? us[static_cast<size_t>(q) * D] : 0.f;
+            }
+        }
+        c0p[g][f] = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
     }
     const bf16 *ub = u + static_cast<size_t>(bh) * N * D;
     const int r0 = seg * kLogitSeg + st * TPS;
@@ -223,21 +233,40 @@ __global__ __launch_bounds__(kStreamThreads) void logits_stream_kernel(const bf1
             cs[2 * i + 1] += __uint_as_float(wv[i] & 0xffff0000u);
         }
     }
+    // exclusive scan over the streams (in token order): the streams of a wave sit LPT lanes apart,
+    // so a shuffle scan covers them; the totals of the earlier waves come through LDS
+    float inc[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) part[st][8 * fg + i] = cs[i];
-    __syncthreads();
-    if (tid < D) {                             // exclusive scan over the streams, one feature per thread
-        float run = c0s[tid];
-        for (int q = 0; q < NS; ++q) {
-            const float t = part[q][tid];
-            part[q][tid] = run;
-            run += t;
+    for (int i = 0; i < 8; ++i) {
+        float v = cs[i];
+#pragma unroll
+        for (int off = LPT; off < 64; off <<= 1) {
+            const float t = __shfl_up(v, off, 64);
+            if (lane >= off) v += t;
         }
+        inc[i] = v;
+    }
+    if (lane >= 64 - LPT) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) wtot[wave][8 * fg + i] = inc[i];
     }
     __syncthreads();
     float R[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) R[i] = part[st][8 * fg + i];
+    for (int i = 0; i < 8; ++i) {
+        const int f = 8 * fg + i;
+        float c = 0.f;
+#pragma unroll
+        for (int g = 0; g < G; ++g) c += c0p[g][f];
+#pragma unroll
+        for (int w2 = 0; w2 < NWV; ++w2) c += w2 < wave ? wtot[w2][f] : 0.f;
+        const float ex = __shfl_up(inc[i], LPT, 64);      // streams of this wave before this one
+        R[i] = lane >= LPT ? c + ex : c;
+    }
+    // the packed rows go through an empty asm: the dot pass unpacks them again instead of the
+    // compiler holding both the packed and the unpacked values (twice the registers) since the sums
+#pragma unroll
+    for (int k = 0; k < TPS; ++k) asm volatile("" : "+v"(x[k].x), "+v"(x[k].y), "+v"(x[k].z), "+v"(x[k].w));
     float d[TPS];                              // per-token dot partials, reduced in place below
 #pragma unroll
     for (int k = 0; k < TPS; ++k) {
@@ -253,39 +282,29 @@ __global__ __launch_bounds__(kStreamThreads) void logits_stream_kernel(const bf1
         }
         d[k] = acc;
     }
-    // butterfly over the LPT lanes of a stream, LPT tokens at a time: token b*LPT + l ends on lane l
-    const float rs_du = 1.f / sqrtf(static_cast<float>(D));
+    // butterfly over the LPT lanes of a stream: token l of the stream ends on lane l. A stream is LPT
+    // tokens, so wave w then holds tokens 64 w + lane of the segment: one 64-token chunk, whose
+    // logits and aggregate (max, sum e^{s - max}, sum s) are written straight from the registers.
 #pragma unroll
-    for (int b = 0; b < TPS / LPT; ++b) {
-        float *v = d + b * LPT;
+    for (int off = LPT / 2; off >= 1; off >>= 1) {
+        const bool hi = (l & off) != 0;
 #pragma unroll
-        for (int off = LPT / 2; off >= 1; off >>= 1) {
-            const bool hi = (l & off) != 0;
-#pragma unroll
-            for (int i = 0; i < off; ++i) {
-                const float keep = hi ? v[off + i] : v[i];
-                const float send = hi ? v[i] : v[off + i];
-                v[i] = keep + __shfl_xor(send, off, 64);
-            }
+        for (int i = 0; i < off; ++i) {
+            const float keep = hi ? d[off + i] : d[i];
+            const float send = hi ? d[i] : d[off + i];
+            d[i] = keep + __shfl_xor(send, off, 64);
         }
-        const int tk = st * TPS + b * LPT + l;          // token inside the segment
-        const int row = seg * kLogitSeg + tk;
-        sv[tk] = -v[0] * rs_du / (et + static_cast<float>(row + 1));
     }
-    __syncthreads();
-    // write s and the aggregates of each 64-token chunk (segments are whole chunks)
-    const int r1 = min(N, (seg + 1) * kLogitSeg);
-    const int w = tid >> 6;
-    for (int cb = w; cb < kLogitSeg / 64; cb += kStreamThreads / 64) {
-        const int row = seg * kLogitSeg + cb * 64 + lane;
-        if (seg * kLogitSeg + cb * 64 >= r1) break;
-        const bool valid = row < r1;
-        const float s = sv[cb * 64 + lane];
+    const int c0 = seg * kLogitSeg + 64 * wave;          // first token of this wave's chunk
+    if (c0 < N) {
+        const int row = c0 + lane;
+        const bool valid = row < N;
+        const float s = -d[0] * (1.f / sqrtf(static_cast<float>(D))) / (et + static_cast<float>(row + 1));
         if (valid) s_out[static_cast<size_t>(bh) * N + row] = s;
         const float mx = lane_f(wave_scan_max(valid ? s : kNegInf), 63);
         const float se = lane_f(wave_scan_add(valid ? __expf(s - mx) : 0.f), 63);
         const float ss = lane_f(wave_scan_add(valid ? s : 0.f), 63);
-        if (lane == 0) agg[static_cast<size_t>(bh) * ((N + 63) / 64) + (seg * kLogitSeg) / 64 + cb] = make_float4(mx, se, ss, 0.f);
+        if (lane == 0) agg[static_cast<size_t>(bh) * ((N + 63) / 64) + c0 / 64] = make_float4(mx, se, ss, 0.f);
     }
 }
 

@@ -138,7 +138,7 @@ def test_workspace_size_and_validation(lib):
     nseg = 8                                             # scan segments per head: 32 heads x 8 >= 256
     segsc = bh * nseg * 16                               # composed scalar map per segment
     segst = bh * (nseg - 1) * 3 * 128 * 128 * 4          # float32 X, Y, H per segment boundary
-    rec = (4 * 4 + 8 * 2 + 4 * 2) * 1024 + (6 * 64 + 8) * 4   # q^, k^T, W operand tiles + coefficients
+    rec = (4 * 4 + 8 * 2 + 6) * 1024 + (6 * 64 + 8) * 4   # q^, k^T, non-zero W operand tiles + coefficients
     sink = 64 * 128 * 2                                  # output rows past N of a last, partial chunk
     assert n == logits + useg + agg + rope + segsc + segst + sink + bh * nch * rec
     assert lib.zeros_fwd_causal_workspace_bytes(ctypes.byref(shape(dtype=0))) == 0   # f32 path: none

@@ -154,17 +154,20 @@ __device__ __forceinline__ void chunk_scan(Coef &cf, int lane, int t0, int nval,
 // ---- per-chunk record written by the prep kernel and read by the main kernel ------------------
 // [ Q^ operands  : 4 query blocks x KS k-steps x 64 lanes x 16 B ]
 // [ K^T operands : d/16 row tiles x 2 key steps x 64 lanes x 16 B ]
-// [ W operands   : 4 query blocks x 2 key-block pairs x 64 lanes x 16 B ]
+// [ W operands   : (query block tb, key-block pair pi) with 2 pi <= tb, the six that the causal mask
+//                  leaves non-zero, x 64 lanes x 16 B; piece index w_piece(tb, pi) ]
 // [ coefficients : (cX, beta, kappa, 0) per query; (w_X, w_Y) per key; rX, cHX, cHY, m1, E1, P1 ]
 template <int D> struct Rec {
     static constexpr int KS = D / 32;
     static constexpr size_t q_off = 0;
     static constexpr size_t k_off = q_off + size_t(4) * KS * 1024;
     static constexpr size_t w_off = k_off + size_t(D / 16) * 2 * 1024;
-    static constexpr size_t c_off = w_off + size_t(8) * 1024;
+    static constexpr size_t c_off = w_off + size_t(6) * 1024;
     static constexpr size_t bytes = c_off + (6 * kC + 8) * 4;
 };
 enum { kCoQ = 0, kCoW = 4 * kC, kCoChunk = 6 * kC };   // float offsets in the coefficient block
+// W piece of query block tb (0..3) and key-block pair pi (keys 32 pi .. 32 pi + 31), 2 pi <= tb
+__device__ __forceinline__ int w_piece(int tb, int pi) { return tb < 2 ? tb : 2 * tb - 2 + pi; }
 
 __device__ __forceinline__ void st16(unsigned char *p, const bf16x8 &v) { *reinterpret_cast<bf16x8 *>(p) = v; }
 __device__ __forceinline__ bf16x8 ld16(const unsigned char *p) { return *reinterpret_cast<const bf16x8 *>(p); }
@@ -341,7 +344,8 @@ __global__ __launch_bounds__(kPrepThreads) void causal_prep_kernel(Problem p, Ca
                 wv[2 * h2] = pack2(w[0], w[1]);
                 wv[2 * h2 + 1] = pack2(w[2], w[3]);
             }
-            st16(rec + R::w_off + (size_t(tb * 2 + pi) * 64 + lane) * 16, as_bf16x8(wv[0], wv[1], wv[2], wv[3]));
+            if (2 * pi <= tb)
+                st16(rec + R::w_off + (size_t(w_piece(tb, pi)) * 64 + lane) * 16, as_bf16x8(wv[0], wv[1], wv[2], wv[3]));
         }
     }
 
@@ -602,7 +606,7 @@ __global__ __launch_bounds__(D * 4) void causal_seg_kernel(Problem p, CausalWork
                     if (2 * pi > tb) continue;
                     const uint2 a = VA[pi];
                     const uint2 e = (2 * pi + 1 <= tb) ? VC[pi] : make_uint2(0, 0);
-                    const bf16x8 Bw = ld16(rb + R::w_off + (size_t(tb * 2 + pi) * 64 + lane) * 16);
+                    const bf16x8 Bw = ld16(rb + R::w_off + (size_t(w_piece(tb, pi)) * 64 + lane) * 16);
                     oacc = mfma(as_bf16x8(a.x, a.y, e.x, e.y), Bw, oacc);
                 }
                 // rows past the end go to a sink in the workspace: the store is unconditional, so the

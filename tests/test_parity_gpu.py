@@ -166,6 +166,24 @@ def test_causal_segments_ragged_sampled_heads(d):
         assert rel_l2(g, ref_st[key]) <= 2e-2, key
 
 
+@pytest.mark.parametrize("scale", [10.0, 30.0])
+def test_causal_segments_large_logits(scale):
+    """bfloat16 scan path with logits scaled up so that the running maximum jumps by many nats
+    between chunks: the chunk factors rX come out tiny or zero, which the scan's scaled state basis
+    has to absorb (fold into the state, floor of the factor) across chained segments."""
+    wl = CONFIGS[4].with_(B=2, H=16, N=1900, d=64, d_u=64, seed=3400 + int(scale))
+    x = make_inputs(wl, u_scale=scale)
+    o = run_causal(x, "bf16", rope=True)
+    pairs = [(0, 1), (1, 12)]
+    xs = slice_heads(x, pairs)
+    ref = R.causal_forward(**xs, rope=True)
+    got = np.stack([to_f64(o[b, h]) for b, h in pairs])[None]
+    assert np.all(np.isfinite(got))
+    err = rel_l2(got, ref)
+    print(f"large logits x{scale} rel_l2={err:.3e}", flush=True)
+    assert err <= TOL["bf16"]
+
+
 def test_causal_workspace_reuse():
     wl = CONFIGS[4].with_(B=1, H=3, N=700, seed=3200)
     x = make_inputs(wl)

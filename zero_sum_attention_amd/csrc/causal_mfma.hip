@@ -454,7 +454,16 @@ __global__ __launch_bounds__(D * 4) void causal_seg_kernel(Problem p, CausalWork
 #pragma unroll
             for (int i = 0; i < 4; ++i) X[jb][i] = Y[jb][i] = Hm[jb][i] = 0.f;
     }
-    float Rs = 1.f, Hs = 0.f, Ys = 0.f;   // composed scalar map of the segment (pass 1)
+    // composed scalar map of the segment (pass 1): X <- Rs X + alp H + ..., Y <- Y + bet H + ...,
+    // with Rs the exact product of the chunk factors rX
+    float Rs = 1.f;
+    // The registers hold X, Y, H in a scaled basis, X = rho Z + alp H and Y = Y' + bet H (Z, Y' in
+    // the X, Y registers): the per-chunk map X <- rX X + cHX H, Y <- Y + cHY H then only changes the
+    // three scalars, rho <- rX rho, alp <- rX alp + cHX, bet <- bet + cHY, and the update operands
+    // and output coefficients absorb them (Z += K^T diag((w_X - alp)/rho) V, Y' += K^T diag(w_Y - bet) V).
+    // rho is folded back into Z before it drops below 2^-40, and rX is floored at 2^-40 (a change of
+    // at most 2^-40 |X| where the exact factor is smaller), so 1/rho stays within 2^80.
+    float rho = 1.f, alp = 0.f, bet = 0.f;
 
     // v of this wave's columns: lane holds tokens 2 (lane & 31), +1 and columns 8 (lane >> 5) + [0, 8)
     const int vtok = 2 * (lane & 31), vh = lane >> 5;
@@ -494,13 +503,29 @@ __global__ __launch_bounds__(D * 4) void causal_seg_kernel(Problem p, CausalWork
         const int t0 = c * kC;
         const int nval = min(kC, N - t0);
         const float *co = reinterpret_cast<const float *>(rb + R::c_off);
+        const float4 ch = *reinterpret_cast<const float4 *>(co + kCoChunk);   // rX, cHX, cHY, m1
+        if (t0 > 0 && rho < 0x1p-40f) {          // fold rho into Z (rare; the same on every lane)
+#pragma unroll
+            for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) X[jb][i] *= rho;
+            rho = 1.f;
+        }
+        // scalars of the basis after this chunk (the first chunk of the sequence starts from nothing
+        // and keeps them)
+        const float rho1 = t0 > 0 ? rho * fmaxf(ch.x, 0x1p-40f) : rho;
+        const float alp1 = t0 > 0 ? ch.x * alp + ch.y : alp;
+        const float bet1 = t0 > 0 ? bet + ch.z : bet;
+        const float irho1 = 1.f / rho1;
 
-        // ---- stage this wave's v tile (token pairs per column) and v * w_X, v * w_Y
+        // ---- stage this wave's v tile (token pairs per column) and the update operands
+        // v (w_X - alp1)/rho1 and v (w_Y - bet1)
         {
             const bool ok0 = t0 + vtok < N, ok1 = t0 + vtok + 1 < N;
             const uint32_t a4[4] = {ok0 ? va.x : 0u, ok0 ? va.y : 0u, ok0 ? va.z : 0u, ok0 ? va.w : 0u};
             const uint32_t b4[4] = {ok1 ? vb.x : 0u, ok1 ? vb.y : 0u, ok1 ? vb.z : 0u, ok1 ? vb.w : 0u};
-            const float4 wv = *reinterpret_cast<const float4 *>(co + kCoW + 2 * vtok);   // wX, wY of both tokens
+            const float4 w4 = *reinterpret_cast<const float4 *>(co + kCoW + 2 * vtok);   // wX, wY of both tokens
+            const float4 wv = make_float4((w4.x - alp1) * irho1, w4.y - bet1, (w4.z - alp1) * irho1, w4.w - bet1);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 // columns 8 vh + 2i (low halves) and 8 vh + 2i + 1 (high halves)
@@ -518,9 +543,8 @@ __global__ __launch_bounds__(D * 4) void causal_seg_kernel(Problem p, CausalWork
         }
 
         // ---- carried-state products and the state update, interleaved by pairs of row tiles:
-        // step ks reads rows 2ks, 2ks+1 of X, Y, H (as bf16 MFMA operands, the state at t0), after
-        // which those rows are rescaled to the chunk-end basis and advanced by K^T V' on MFMA.
-        const float4 ch = *reinterpret_cast<const float4 *>(co + kCoChunk);   // rX, cHX, cHY, m1
+        // step ks reads rows 2ks, 2ks+1 of Z, Y', H (as bf16 MFMA operands, the state at t0), after
+        // which those rows are advanced by K^T V' on MFMA.
         // every operand from this wave's staging area is read here, before the next record's
         // copies are issued: afterwards the wave reads only the current record buffer, which the
         // compiler can tell apart from the copy target (no wait for the copies inside the chunk)
@@ -568,13 +592,6 @@ __global__ __launch_bounds__(D * 4) void causal_seg_kernel(Problem p, CausalWork
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) {
                 const int jb = 2 * ks + jj;
-                if (t0 > 0) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        X[jb][i] = ch.x * X[jb][i] + ch.y * Hm[jb][i];
-                        Y[jb][i] = Y[jb][i] + ch.z * Hm[jb][i];
-                    }
-                }
 #pragma unroll
                 for (int ks2 = 0; ks2 < kC / 32; ++ks2) {
                     const bf16x8 Ak = ld16(rb + R::k_off + (size_t(jb * 2 + ks2) * 64 + lane) * 16);
@@ -585,22 +602,18 @@ __global__ __launch_bounds__(D * 4) void causal_seg_kernel(Problem p, CausalWork
             }
         }
         if (PASS1) {
-            if (t0 > 0) {
-                Hs = ch.x * Hs + ch.y;
-                Rs = ch.x * Rs;
-                Ys = Ys + ch.z;
-            } else {
-                Rs = 0.f;                    // the first chunk of the sequence starts from nothing
-                Hs = 0.f;
-            }
+            // the first chunk of the sequence starts from nothing
+            Rs = t0 > 0 ? ch.x * Rs : 0.f;
         } else {
             // ---- outputs: coefficients on the carried-state products, plus V^T W^T (intra-chunk)
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) {
                 f32x4 oacc;
                 const float4 cq = *reinterpret_cast<const float4 *>(co + kCoQ + 4 * (16 * tb + l16));  // cX, beta, kappa
+                // X = rho Z + alp H, Y = Y' + bet H at t0
+                const float cz = cq.x * rho, chh = cq.z + cq.x * alp + cq.y * bet;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) oacc[i] = carried ? cq.x * ax[tb][i] + cq.y * ay[tb][i] + cq.z * ah[tb][i] : 0.f;
+                for (int i = 0; i < 4; ++i) oacc[i] = carried ? cz * ax[tb][i] + cq.y * ay[tb][i] + chh * ah[tb][i] : 0.f;
 #pragma unroll
                 for (int pi = 0; pi < 2; ++pi) {
                     if (2 * pi > tb) continue;
@@ -617,6 +630,9 @@ __global__ __launch_bounds__(D * 4) void causal_seg_kernel(Problem p, CausalWork
                 *reinterpret_cast<uint2 *>(dst + w * kTile + 4 * g4) = ov;
             }
         }
+        rho = rho1;
+        alp = alp1;
+        bet = bet1;
         __syncthreads();          // copies of chunk c + 1 landed (vmcnt) and visible; this buffer free
     };
     for (int c = c_begin; c < c_end; c += 2) {
@@ -624,6 +640,14 @@ __global__ __launch_bounds__(D * 4) void causal_seg_kernel(Problem p, CausalWork
         if (c + 1 < c_end) chunk(c + 1, recB, recA);
     }
 
+    // back to the plain basis: X = rho Z + alp H, Y = Y' + bet H
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            X[jb][i] = rho * X[jb][i] + alp * Hm[jb][i];
+            Y[jb][i] = Y[jb][i] + bet * Hm[jb][i];
+        }
     if (PASS1) {
         // segment-local sums and the composed scalar map, for the combine step
         float4 *dst = reinterpret_cast<float4 *>(work.segst + (static_cast<size_t>(bh) * (nseg - 1) + seg) * kSegFloats<D>);
@@ -633,7 +657,7 @@ __global__ __launch_bounds__(D * 4) void causal_seg_kernel(Problem p, CausalWork
             dst[(size_t(1 * JB + jb) * NW) * 64 + sidx] = make_float4(Y[jb][0], Y[jb][1], Y[jb][2], Y[jb][3]);
             dst[(size_t(2 * JB + jb) * NW) * 64 + sidx] = make_float4(Hm[jb][0], Hm[jb][1], Hm[jb][2], Hm[jb][3]);
         }
-        if (tid == 0) work.segsc[static_cast<size_t>(bh) * nseg + seg] = make_float4(Rs, Hs, Ys, 0.f);
+        if (tid == 0) work.segsc[static_cast<size_t>(bh) * nseg + seg] = make_float4(Rs, alp, bet, 0.f);
         return;
     }
 

@@ -240,9 +240,9 @@ def main():
                    "accumulate": "f32", "states": "f32"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
-                     "kernel": "zeros_fwd_causal call: useg_sum_kernel + logits_stream_kernel + rope_table_kernel "
-                               "+ causal_prep_kernel + causal_seg_kernel (pass 1) + causal_seg_combine_kernel "
-                               "+ causal_seg_kernel (main)",
+                     "kernel": "zeros_fwd_causal call: useg_sum_kernel (also fills the RoPE angle table) "
+                               "+ logits_stream_kernel + causal_prep_kernel + causal_seg_kernel (pass 1) "
+                               "+ causal_seg_combine_kernel + causal_seg_kernel (main)",
                      "algorithmic_bytes_per_launch": nbytes,
                      "avg_kernel_ms": avg_kernel_ms,
                      "min_kernel_ms": float(np.min(kernel_ms))},

@@ -8,15 +8,15 @@
 // two centred d x d states (zero-sum weights, so of the size of the output and safe to round to
 // bfloat16 as MFMA operands).
 //
-// One workgroup of 4 waves per (batch, head); wave w owns value columns [16 CT w, 16 CT (w+1)) of X
-// and Y, all d rows, in float32 registers.
-//   A: column sums of u -> ubar; logits s_i (lanes of a token row reduce their partial dots);
-//      m = max s, E = sum e^{s-m}, P = sum s by block reductions.
-//   B: per 64-token chunk, k^ (unit, optionally RoPE-rotated), v w_X and v w_Y staged transposed in
-//      LDS; X += K^T (w_X V), Y += K^T (w_Y V) on MFMA.
-//   C: per 16-token block, o^T = X^T q^T and Y^T q^T on MFMA with X^T, Y^T straight from the
-//      registers (their row order, {4g + i, 16 + 4g + i} per 32 features, is the order q^ is
-//      loaded in), scaled per token by sigmah/|q| and (sigma1 - sigmah)/(N |q|).
+// One workgroup of 4 waves per (batch, head, 16-column tile of the value dimension): d/16 workgroups
+// per head, each computing its tile's columns of X and Y and of the output.
+//   A: column sums of u -> ubar; logits s_i (lanes of a token row reduce their partial dots), each
+//      row's (max, sum e^{s - max}, sum s) merged by the lane that ends with its dot, then across
+//      the workgroup. Every tile workgroup of a head repeats this phase (u from L2).
+//   B: per 64-token step, k^ (unit, optionally RoPE-rotated, all features) and the tile's columns
+//      of v w_X and v w_Y staged transposed in LDS; wave w advances feature tiles of X and Y on MFMA.
+//   C: X^T, Y^T of the tile through LDS as bf16 A operands; the waves take 16-token blocks in turn:
+//      o^T = X^T q^T and Y^T q^T on MFMA, scaled per token by sigmah/|q| and (sigma1 - sigmah)/(N |q|).
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "mfma_common.hpp"
@@ -24,7 +24,8 @@
 namespace zeros {
 namespace {
 
-constexpr int kEC = 64;            // tokens per chunk of the state pass
+constexpr int kEC = 64;            // tokens per step of the state pass
+constexpr int kEShortN = 256;      // longest sequence of the short variant (logits buffer in LDS)
 constexpr int kEThreads = 256;     // 4 waves
 constexpr int kEPad = 8;           // bf16 elements of row padding in LDS
 
@@ -36,22 +37,11 @@ __device__ __forceinline__ float row_sum(float x) {
     return x;
 }
 
-// Block-wide max and sum over 256 threads (every thread gets the result).
-__device__ __forceinline__ float block_max(float x, float *scratch) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = x;
-    __syncthreads();
-    return fmaxf(fmaxf(scratch[0], scratch[1]), fmaxf(scratch[2], scratch[3]));
-}
-__device__ __forceinline__ float block_sum(float x, float *scratch) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = x;
-    __syncthreads();
-    return (scratch[0] + scratch[1]) + (scratch[2] + scratch[3]);
+// (max, sum e^{s - max}) of two parts merged; a max of -inf marks an empty part.
+__device__ __forceinline__ void lse_merge(float &m, float &e, float m2, float e2) {
+    const float mm = fmaxf(m, m2);
+    e = (m == kNegInf ? 0.f : e * __expf(m - mm)) + (m2 == kNegInf ? 0.f : e2 * __expf(m2 - mm));
+    m = mm;
 }
 
 __device__ __forceinline__ void unpack8(const uint4 &x, float (&f)[8]) {
@@ -63,25 +53,30 @@ __device__ __forceinline__ void unpack8(const uint4 &x, float (&f)[8]) {
     }
 }
 
-template <int D, bool ROPE>
+template <int D, bool ROPE, int NMAX>
 __global__ __launch_bounds__(kEThreads) void encoder_mfma_kernel(Problem p) {
-    constexpr int CT = D / 64;         // 16-column tiles per wave
-    constexpr int FT = D / 16;         // 16-row feature tiles
+    constexpr int FT = D / 16;         // 16-row feature tiles of a state
+    constexpr int FW = FT / 4;         // feature tiles per wave
     constexpr int KS = D / 32;         // 32-feature steps
     constexpr int LPR = D / 8;         // lanes per token row (8 features, 16 bytes each)
     constexpr int RPP = kEThreads / LPR;   // token rows per pass
     __shared__ float ubar[D];
-    __shared__ float part[RPP][D + 1];
-    __shared__ float sl[kEncoderMfmaMaxN];
-    __shared__ float red[4];
+    __shared__ float part[kEThreads / 64][D];
+    __shared__ float sl[NMAX];         // logits of the sequence (N <= NMAX)
+    __shared__ float4 red[kEThreads / 64];
     __shared__ __align__(16) uint16_t kt[D][kEC + kEPad];    // k^ of the chunk, transposed
-    __shared__ __align__(16) uint16_t vxt[D][kEC + kEPad];   // v w_X, transposed
-    __shared__ __align__(16) uint16_t vyt[D][kEC + kEPad];   // v w_Y, transposed
+    __shared__ __align__(16) uint16_t vxt[16][kEC + kEPad];  // this tile's columns of v w_X, transposed
+    __shared__ __align__(16) uint16_t vyt[16][kEC + kEPad];  // this tile's columns of v w_Y, transposed
+    __shared__ __align__(16) uint16_t sxy[2][16][D + kEPad]; // X^T, Y^T of this tile (bf16), for phase C
+    __shared__ double rev[ROPE ? D / 2 : 1];                 // RoPE turns per position of each pair
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g4 = lane >> 4;
-    const int bh = blockIdx.x;
+    // workgroup (column tile ct, head bh): with B H a multiple of 8 the tiles of a head run on one XCD
+    // (workgroups go to the XCDs in turn) and share its L2 for the q, k, u rows every tile reads
+    const int bhn = p.B * p.H;
+    const int ct = blockIdx.x / bhn, bh = blockIdx.x % bhn;
     const int h = bh % p.H;
     const int N = p.N;
     const size_t row0 = static_cast<size_t>(bh) * N;
@@ -94,191 +89,260 @@ __global__ __launch_bounds__(kEThreads) void encoder_mfma_kernel(Problem p) {
     uint16_t *o = static_cast<uint16_t *>(p.o) + row0 * D;
     const float et = expf(p.tau[h]);
     const int fr = tid % LPR, rr = tid / LPR;       // feature group (8 features) and row of a pass
+    if (ROPE && tid < D / 2) rev[tid] = rope_rev_per_pos(tid, D, p.rope_base);   // ordered by the first barrier
 
-    // ---- A: ubar, logits, and the scalar sums
+    // k rows (all features) and this tile's v columns of a step, read one step ahead. Thread (rr, fr)
+    // takes the token pairs (2 rr + 2 RPP jj, +1) of features 8 fr + [0, 8); for v, token pair
+    // 2 (tid / 4), +1 and columns 16 ct + 4 (tid & 3) + [0, 4). Pairs of tokens make the transposed
+    // LDS writes 32-bit.
+    constexpr int JR = kEC / RPP;      // rows per thread (even)
+    static_assert(JR % 2 == 0 && 2 * kEC <= kEThreads, "state pass shape");
+    const int vtk = 2 * (tid >> 2), vcq = tid & 3;
+    const bool vthr = tid < 2 * kEC;   // kEC / 2 token pairs x 4 column quads
+    auto krow = [&](const int j) { return 2 * rr + (j & 1) + 2 * RPP * (j >> 1); };
+    uint4 kn[JR];
+    uint2 vn[2] = {make_uint2(0, 0), make_uint2(0, 0)};
+    auto load_kv = [&](const int t0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < JR; ++j)
+            kn[j] = *reinterpret_cast<const uint4 *>(k + static_cast<size_t>(min(t0 + krow(j), N - 1)) * D + 8 * fr);   // zeroed below
+        if (vthr) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+                vn[e] = *reinterpret_cast<const uint2 *>(v + static_cast<size_t>(min(t0 + vtk + e, N - 1)) * D + 16 * ct + 4 * vcq);
+        }
+    };
+    load_kv(0);                        // the first step's rows are in flight during phase A
+
+    // ---- A: ubar, logits, and the scalar sums. The first UC rows of each thread are read once and
+    // stay in registers from the column sums to the logits.
+    constexpr int UC = 8;
+    const float mu_t = tid < D ? p.mu[h * D + tid] : 0.f;   // read early: used after the first barrier
+    uint4 ur[UC];
+#pragma unroll
+    for (int j = 0; j < UC; ++j)
+        ur[j] = *reinterpret_cast<const uint4 *>(u + static_cast<size_t>(min(rr + RPP * j, N - 1)) * D + 8 * fr);
     {
         float cs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int r = rr; r < N; r += RPP) {
+#pragma unroll
+        for (int j = 0; j < UC; ++j) {
+            if (rr + RPP * j < N) {
+                float x[8];
+                unpack8(ur[j], x);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) cs[i] += x[i];
+            }
+        }
+        for (int r = rr + RPP * UC; r < N; r += RPP) {
             float x[8];
             unpack8(*reinterpret_cast<const uint4 *>(u + static_cast<size_t>(r) * D + 8 * fr), x);
 #pragma unroll
             for (int i = 0; i < 8; ++i) cs[i] += x[i];
         }
+        // the rows of a wave sit LPR lanes apart: a shuffle sum over them, then the waves through LDS
 #pragma unroll
-        for (int i = 0; i < 8; ++i) part[rr][8 * fr + i] = cs[i];
+        for (int i = 0; i < 8; ++i) {
+#pragma unroll
+            for (int off = LPR; off < 64; off <<= 1) cs[i] += __shfl_xor(cs[i], off, 64);
+        }
+        if (lane < LPR) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) part[w][8 * fr + i] = cs[i];
+        }
         __syncthreads();
         if (tid < D) {
             float su = 0.f;
-            for (int g = 0; g < RPP; ++g) su += part[g][tid];
-            ubar[tid] = (et * p.mu[h * D + tid] + su) / (et + static_cast<float>(N));
+#pragma unroll
+            for (int g = 0; g < kEThreads / 64; ++g) su += part[g][tid];
+            ubar[tid] = (et * mu_t + su) / (et + static_cast<float>(N));
         }
         __syncthreads();
     }
+    // logits, with each row's (max, sum e^{s - max}, sum s) taken by the lane that ends with its dot
+    float mloc = kNegInf, eloc = 0.f, ploc = 0.f;
     {
         float ub[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) ub[i] = ubar[8 * fr + i];
         const float rs_du = 1.f / sqrtf(static_cast<float>(D));
-        for (int r0 = 0; r0 < N; r0 += RPP) {          // uniform trip count: the row reduction is a shuffle
-            const int r = r0 + rr;
+        auto row = [&](const uint4 &raw, const int r) __attribute__((always_inline)) {
             float dot = 0.f;
             if (r < N) {
                 float x[8];
-                unpack8(*reinterpret_cast<const uint4 *>(u + static_cast<size_t>(r) * D + 8 * fr), x);
+                unpack8(raw, x);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) dot = fmaf(x[i], ub[i], dot);
             }
-            dot = row_sum<D>(dot);
-            if (r < N && fr == 0) sl[r] = -dot * rs_du;
+            dot = row_sum<D>(dot);                 // every lane of the row calls this (a shuffle)
+            if (r < N && fr == 0) {
+                const float sv = -dot * rs_du;
+                sl[r] = sv;
+                lse_merge(mloc, eloc, sv, 1.f);
+                ploc += sv;
+            }
+        };
+#pragma unroll
+        for (int j = 0; j < UC; ++j) row(ur[j], rr + RPP * j);
+        for (int r0 = RPP * UC; r0 < N; r0 += RPP) {   // uniform trip count
+            const int r = r0 + rr;
+            row(*reinterpret_cast<const uint4 *>(u + static_cast<size_t>(min(r, N - 1)) * D + 8 * fr), r);
         }
     }
-    __syncthreads();
-    float mloc = kNegInf;
-    for (int r = tid; r < N; r += kEThreads) mloc = fmaxf(mloc, sl[r]);
-    const float M = block_max(mloc, red);
-    float eloc = 0.f, ploc = 0.f;
-    for (int r = tid; r < N; r += kEThreads) {
-        eloc += __expf(sl[r] - M);
-        ploc += sl[r];
+    // block reduction of (max, sum e^{s - max}, sum s): in each wave, then across the waves
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float m2 = __shfl_xor(mloc, off, 64), e2 = __shfl_xor(eloc, off, 64);
+        ploc += __shfl_xor(ploc, off, 64);
+        lse_merge(mloc, eloc, m2, e2);
     }
-    const float E = block_sum(eloc, red);
-    const float P = block_sum(ploc, red);
+    if (lane == 0) red[w] = make_float4(mloc, eloc, ploc, 0.f);
+    __syncthreads();                           // also orders the logits in LDS before phase B
+    float M = kNegInf, E = 0.f, P = 0.f;
+#pragma unroll
+    for (int i = 0; i < kEThreads / 64; ++i) {
+        const float4 rv = red[i];
+        lse_merge(M, E, rv.x, rv.y);
+        P += rv.z;
+    }
     const float invN = N > 0 ? 1.f / static_cast<float>(N) : 0.f;
     const float invE = E > 0.f ? 1.f / E : 0.f;
     const float PN = P * invN;
 
-    // ---- B: X = K^T diag(w_X) V, Y = K^T diag(w_Y) V over chunks of kEC tokens
-    f32x4 X[FT][CT], Y[FT][CT];
+    // ---- B: this tile's columns of X = K^T diag(w_X) V and Y = K^T diag(w_Y) V over chunks of kEC
+    // tokens; wave w owns feature tiles [FW w, FW w + FW)
+    f32x4 X[FW], Y[FW];
 #pragma unroll
-    for (int ft = 0; ft < FT; ++ft)
+    for (int j = 0; j < FW; ++j)
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) X[ft][ct][i] = Y[ft][ct][i] = 0.f;
-    // k and v rows of a chunk, read one chunk ahead
-    constexpr int JR = kEC / RPP;
-    uint4 kn[JR], vn[JR];
-    auto load_kv = [&](const int t0) __attribute__((always_inline)) {
-#pragma unroll
-        for (int j = 0; j < JR; ++j) {
-            const int r = t0 + rr + RPP * j;
-            const size_t ri = static_cast<size_t>(min(r, N - 1)) * D + 8 * fr;   // in bounds; zeroed below
-            kn[j] = *reinterpret_cast<const uint4 *>(k + ri);
-            vn[j] = *reinterpret_cast<const uint4 *>(v + ri);
-        }
-    };
-    if (N > 0) load_kv(0);
+        for (int i = 0; i < 4; ++i) X[j][i] = Y[j][i] = 0.f;
     for (int t0 = 0; t0 < N; t0 += kEC) {
-        uint4 kc[JR], vc[JR];
+        uint4 kc[JR];
 #pragma unroll
-        for (int j = 0; j < JR; ++j) {
-            kc[j] = kn[j];
-            vc[j] = vn[j];
-        }
+        for (int j = 0; j < JR; ++j) kc[j] = kn[j];
+        const uint2 vc0 = vn[0], vc1 = vn[1];
         if (t0 + kEC < N) load_kv(t0 + kEC);
 #pragma unroll
-        for (int j = 0; j < JR; ++j) {
-            const int rl = rr + RPP * j, r = t0 + rl;
-            const bool ok = r < N;
-            float kv[8], vv[8];
-            unpack8(ok ? kc[j] : make_uint4(0, 0, 0, 0), kv);
-            unpack8(ok ? vc[j] : make_uint4(0, 0, 0, 0), vv);
-            float ss = 0.f;
+        for (int jj = 0; jj < JR / 2; ++jj) {
+            float kp[2][8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) ss = fmaf(kv[i], kv[i], ss);
-            ss = row_sum<D>(ss);
-            const float ik = ok ? __frsqrt_rn(fmaxf(ss, 1e-24f)) : 0.f;
-            if (ROPE) {
+            for (int e = 0; e < 2; ++e) {
+                const int r = t0 + krow(2 * jj + e);
+                const bool ok = r < N;
+                float(&kv)[8] = kp[e];
+                unpack8(ok ? kc[2 * jj + e] : make_uint4(0, 0, 0, 0), kv);
+                float ss = 0.f;
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    float cs, sn;
-                    rope_cos_sin(rope_rev_per_pos(4 * fr + jj, D, p.rope_base), r, cs, sn);
-                    const float a = kv[2 * jj], b = kv[2 * jj + 1];
-                    kv[2 * jj] = a * cs - b * sn;
-                    kv[2 * jj + 1] = a * sn + b * cs;
+                for (int i = 0; i < 8; ++i) ss = fmaf(kv[i], kv[i], ss);
+                ss = row_sum<D>(ss);
+                const float ik = ok ? __frsqrt_rn(fmaxf(ss, 1e-24f)) : 0.f;
+                if (ROPE) {
+#pragma unroll
+                    for (int j2 = 0; j2 < 4; ++j2) {
+                        float cs, sn;
+                        rope_cos_sin(rev[4 * fr + j2], r, cs, sn);
+                        const float a = kv[2 * j2], b = kv[2 * j2 + 1];
+                        kv[2 * j2] = a * cs - b * sn;
+                        kv[2 * j2 + 1] = a * sn + b * cs;
+                    }
                 }
-            }
-            const float s = ok ? sl[r] : 0.f;
-            const float wx = ok ? __expf(s - M) * invE - invN : 0.f;
-            const float wy = ok ? s - PN : 0.f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int f = 8 * fr + i;
-                kt[f][rl] = static_cast<uint16_t>(pack2(kv[i] * ik, 0.f) & 0xffffu);
-                vxt[f][rl] = static_cast<uint16_t>(pack2(vv[i] * wx, 0.f) & 0xffffu);
-                vyt[f][rl] = static_cast<uint16_t>(pack2(vv[i] * wy, 0.f) & 0xffffu);
+                for (int i = 0; i < 8; ++i) kv[i] *= ik;
+            }
+            const int rl = krow(2 * jj);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) *reinterpret_cast<uint32_t *>(&kt[8 * fr + i][rl]) = pack2(kp[0][i], kp[1][i]);
+        }
+        if (vthr) {
+            float wx[2], wy[2], vv[2][4];
+            const uint2 vcs[2] = {vc0, vc1};
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int r = t0 + vtk + e;
+                const bool ok = r < N;
+                const float s = ok ? sl[r] : 0.f;
+                wx[e] = ok ? __expf(s - M) * invE - invN : 0.f;
+                wy[e] = ok ? s - PN : 0.f;
+                vv[e][0] = lo_f(vcs[e].x);
+                vv[e][1] = hi_f(vcs[e].x);
+                vv[e][2] = lo_f(vcs[e].y);
+                vv[e][3] = hi_f(vcs[e].y);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                *reinterpret_cast<uint32_t *>(&vxt[4 * vcq + i][vtk]) = pack2(vv[0][i] * wx[0], vv[1][i] * wx[1]);
+                *reinterpret_cast<uint32_t *>(&vyt[4 * vcq + i][vtk]) = pack2(vv[0][i] * wy[0], vv[1][i] * wy[1]);
             }
         }
         __syncthreads();
 #pragma unroll
         for (int ks2 = 0; ks2 < kEC / 32; ++ks2) {
             const int kk0 = 32 * ks2 + 8 * g4;
-            bf16x8 BX[CT], BY[CT];
+            const bf16x8 BX = *reinterpret_cast<const bf16x8 *>(&vxt[l16][kk0]);
+            const bf16x8 BY = *reinterpret_cast<const bf16x8 *>(&vyt[l16][kk0]);
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                const int c = 16 * (CT * w + ct) + l16;
-                BX[ct] = *reinterpret_cast<const bf16x8 *>(&vxt[c][kk0]);
-                BY[ct] = *reinterpret_cast<const bf16x8 *>(&vyt[c][kk0]);
-            }
-#pragma unroll
-            for (int ft = 0; ft < FT; ++ft) {
-                const bf16x8 A = *reinterpret_cast<const bf16x8 *>(&kt[16 * ft + l16][kk0]);
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) {
-                    X[ft][ct] = mfma(A, BX[ct], X[ft][ct]);
-                    Y[ft][ct] = mfma(A, BY[ct], Y[ft][ct]);
-                }
+            for (int j = 0; j < FW; ++j) {
+                const bf16x8 A = *reinterpret_cast<const bf16x8 *>(&kt[16 * (FW * w + j) + l16][kk0]);
+                X[j] = mfma(A, BX, X[j]);
+                Y[j] = mfma(A, BY, Y[j]);
             }
         }
         __syncthreads();
     }
+    // X^T and Y^T of the tile into LDS as bf16: accumulator lane (g4, l16) holds features
+    // 16 ft + 4 g4 + [0, 4) of column l16
+#pragma unroll
+    for (int j = 0; j < FW; ++j) {
+        const int f = 16 * (FW * w + j) + 4 * g4;
+        *reinterpret_cast<uint2 *>(&sxy[0][l16][f]) = make_uint2(pack2(X[j][0], X[j][1]), pack2(X[j][2], X[j][3]));
+        *reinterpret_cast<uint2 *>(&sxy[1][l16][f]) = make_uint2(pack2(Y[j][0], Y[j][1]), pack2(Y[j][2], Y[j][3]));
+    }
+    __syncthreads();
 
-    // ---- C: outputs, 16 tokens per step; each wave writes its own columns. The q rows and gates
-    // of the next step are read while this one computes.
-    uint2 qan[KS], qcn[KS];            // features 32ks + 4g4 + [0,4) and 32ks + 16 + 4g4 + [0,4)
+    // ---- C: outputs of this tile's columns, 16 tokens per step, the waves taking steps in turn.
+    // A operands X^T, Y^T (column l16, features 32 ks + 8 g4 + [0, 8)); B operand q^ of token
+    // 16 tb + l16, the same features. The next step's q rows and gates are read while this one computes.
+    bf16x8 AX[KS], AY[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        AX[ks] = *reinterpret_cast<const bf16x8 *>(&sxy[0][l16][32 * ks + 8 * g4]);
+        AY[ks] = *reinterpret_cast<const bf16x8 *>(&sxy[1][l16][32 * ks + 8 * g4]);
+    }
+    uint4 qn[KS];
     uint32_t g1n = 0, ghn = 0;
     auto load_q = [&](const int tb) __attribute__((always_inline)) {
         const int t = min(16 * tb + l16, N - 1);   // in bounds; rows past N are never stored
         const size_t tr = static_cast<size_t>(t) * D;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            qan[ks] = *reinterpret_cast<const uint2 *>(q + tr + 32 * ks + 4 * g4);
-            qcn[ks] = *reinterpret_cast<const uint2 *>(q + tr + 32 * ks + 16 + 4 * g4);
-        }
+        for (int ks = 0; ks < KS; ++ks) qn[ks] = *reinterpret_cast<const uint4 *>(q + tr + 32 * ks + 8 * g4);
         g1n = g1[t];
         ghn = gh[t];
     };
     const int ntb = (N + 15) / 16;
-    if (N > 0) load_q(0);
-    for (int tb = 0; tb < ntb; ++tb) {
+    if (w < ntb) load_q(w);
+    for (int tb = w; tb < ntb; tb += kEThreads / 64) {
         const int t = 16 * tb + l16;
         const bool ok = t < N;
-        uint2 qa[KS], qc[KS];
+        uint4 qv[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            qa[ks] = qan[ks];
-            qc[ks] = qcn[ks];
-        }
+        for (int ks = 0; ks < KS; ++ks) qv[ks] = qn[ks];
         const uint32_t g1v = g1n, ghv = ghn;
-        if (tb + 1 < ntb) load_q(tb + 1);
+        if (tb + kEThreads / 64 < ntb) load_q(tb + kEThreads / 64);
         float ss = 0.f;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            uint32_t wv[4] = {qa[ks].x, qa[ks].y, qc[ks].x, qc[ks].y};
+            uint32_t wv[4] = {qv[ks].x, qv[ks].y, qv[ks].z, qv[ks].w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) ss = dot2_bf16(wv[i], ss);
             if (ROPE) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    // the pair (2j, 2j+1) sits in one 32-bit word
-                    const int f0 = 32 * ks + (i < 2 ? 4 * g4 + 2 * i : 16 + 4 * g4 + 2 * (i - 2));
+                    // the pair (2j, 2j+1) sits in one 32-bit word: j = 16 ks + 4 g4 + i
                     float cs, sn;
-                    rope_cos_sin(rope_rev_per_pos(f0 / 2, D, p.rope_base), t, cs, sn);
+                    rope_cos_sin(rev[16 * ks + 4 * g4 + i], t, cs, sn);
                     const float a = lo_f(wv[i]), b = hi_f(wv[i]);
                     wv[i] = pack2(a * cs - b * sn, a * sn + b * cs);
                 }
-                qa[ks] = make_uint2(wv[0], wv[1]);
-                qc[ks] = make_uint2(wv[2], wv[3]);
+                qv[ks] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
             }
         }
         ss += __shfl_xor(ss, 16, 64);
@@ -287,33 +351,31 @@ __global__ __launch_bounds__(kEThreads) void encoder_mfma_kernel(Problem p) {
         const float s1 = ok ? __fdividef(1.f, 1.f + __expf(-lo_f(g1v))) : 0.f;
         const float sh = ok ? __fdividef(1.f, 1.f + __expf(-lo_f(ghv))) : 0.f;
         const float ax = sh * iq, ay = (s1 - sh) * invN * iq;
+        f32x4 accX = {0.f, 0.f, 0.f, 0.f}, accY = accX;
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-            f32x4 accX = {0.f, 0.f, 0.f, 0.f}, accY = accX;
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 B = as_bf16x8(qv[ks].x, qv[ks].y, qv[ks].z, qv[ks].w);
+            accX = mfma(AX[ks], B, accX);
+            accY = mfma(AY[ks], B, accY);
+        }
+        if (ok) {
+            float r4[4];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const f32x4 &x0 = X[2 * ks][ct], &x1 = X[2 * ks + 1][ct];
-                const f32x4 &y0 = Y[2 * ks][ct], &y1 = Y[2 * ks + 1][ct];
-                const bf16x8 AX = as_bf16x8(pack2(x0[0], x0[1]), pack2(x0[2], x0[3]), pack2(x1[0], x1[1]), pack2(x1[2], x1[3]));
-                const bf16x8 AY = as_bf16x8(pack2(y0[0], y0[1]), pack2(y0[2], y0[3]), pack2(y1[0], y1[1]), pack2(y1[2], y1[3]));
-                const bf16x8 B = as_bf16x8(qa[ks].x, qa[ks].y, qc[ks].x, qc[ks].y);
-                accX = mfma(AX, B, accX);
-                accY = mfma(AY, B, accY);
-            }
-            if (ok) {
-                float r4[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) r4[i] = ax * accX[i] + ay * accY[i];
-                *reinterpret_cast<uint2 *>(o + static_cast<size_t>(t) * D + 16 * (CT * w + ct) + 4 * g4) =
-                    make_uint2(pack2(r4[0], r4[1]), pack2(r4[2], r4[3]));
-            }
+            for (int i = 0; i < 4; ++i) r4[i] = ax * accX[i] + ay * accY[i];
+            *reinterpret_cast<uint2 *>(o + static_cast<size_t>(t) * D + 16 * ct + 4 * g4) =
+                make_uint2(pack2(r4[0], r4[1]), pack2(r4[2], r4[3]));
         }
     }
 }
 
 template <int D, bool ROPE>
 hipError_t launch_one(const Problem &p, hipStream_t stream) {
-    hipLaunchKernelGGL((encoder_mfma_kernel<D, ROPE>), dim3(p.B * p.H), dim3(kEThreads), 0, stream, p);
+    const dim3 grid((D / 16) * p.B * p.H);
+    // short sequences take the variant with a small logits buffer: less LDS, more workgroups per CU
+    if (p.N <= kEShortN)
+        hipLaunchKernelGGL((encoder_mfma_kernel<D, ROPE, kEShortN>), grid, dim3(kEThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((encoder_mfma_kernel<D, ROPE, kEncoderMfmaMaxN>), grid, dim3(kEThreads), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -483,7 +483,7 @@ __global__ __launch_bounds__(D * 4) void causal_seg_kernel(Problem p, CausalWork
     // v rows of chunk c into registers, and the record parts this pass reads into LDS buffer dst:
     // the whole record for the main pass, the k^T operands and the coefficients for pass 1
     auto fetch = [&](const int c, unsigned char *dst) __attribute__((always_inline)) {
-        const int t_ = c * kC + vtok;      // rows past N read row N-1 (in bounds), zeroed when staged
+        const int t_ = c * kC + vtok;      // rows past N read row N-1 (in bounds)
         va = *reinterpret_cast<const uint4 *>(vg + static_cast<size_t>(min(t_, N - 1)) * D + vcol);
         vb = *reinterpret_cast<const uint4 *>(vg + static_cast<size_t>(min(t_ + 1, N - 1)) * D + vcol);
         const uint4 *src = reinterpret_cast<const uint4 *>(rec0 + static_cast<size_t>(c) * R::bytes);
@@ -521,9 +521,10 @@ __global__ __launch_bounds__(D * 4) void causal_seg_kernel(Problem p, CausalWork
         // ---- stage this wave's v tile (token pairs per column) and the update operands
         // v (w_X - alp1)/rho1 and v (w_Y - bet1)
         {
-            const bool ok0 = t0 + vtok < N, ok1 = t0 + vtok + 1 < N;
-            const uint32_t a4[4] = {ok0 ? va.x : 0u, ok0 ? va.y : 0u, ok0 ? va.z : 0u, ok0 ? va.w : 0u};
-            const uint32_t b4[4] = {ok1 ? vb.x : 0u, ok1 ? vb.y : 0u, ok1 ? vb.z : 0u, ok1 ? vb.w : 0u};
+            // rows past N hold copies of row N - 1 (finite); every product they enter is zero: the
+            // record's k^ rows and W columns of absent tokens are zero
+            const uint32_t a4[4] = {va.x, va.y, va.z, va.w};
+            const uint32_t b4[4] = {vb.x, vb.y, vb.z, vb.w};
             const float4 w4 = *reinterpret_cast<const float4 *>(co + kCoW + 2 * vtok);   // wX, wY of both tokens
             const float4 wv = make_float4((w4.x - alp1) * irho1, w4.y - bet1, (w4.z - alp1) * irho1, w4.w - bet1);
 #pragma unroll
@@ -613,7 +614,8 @@ __global__ __launch_bounds__(D * 4) void causal_seg_kernel(Problem p, CausalWork
                 // X = rho Z + alp H, Y = Y' + bet H at t0
                 const float cz = cq.x * rho, chh = cq.z + cq.x * alp + cq.y * bet;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) oacc[i] = carried ? cz * ax[tb][i] + cq.y * ay[tb][i] + chh * ah[tb][i] : 0.f;
+                // (without a carried state the products are zero and the coefficients finite)
+                for (int i = 0; i < 4; ++i) oacc[i] = cz * ax[tb][i] + cq.y * ay[tb][i] + chh * ah[tb][i];
 #pragma unroll
                 for (int pi = 0; pi < 2; ++pi) {
                     if (2 * pi > tb) continue;

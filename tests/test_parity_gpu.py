@@ -228,6 +228,20 @@ def test_encoder_mfma_chunks(d, N, rope):
     assert err <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("d,N", [(64, 256), (64, 257), (128, 4096), (128, 4097)])
+def test_encoder_length_boundaries(d, N):
+    """Sequence lengths at the edges of the encoder's variants: 256 / 257 tokens (small and large
+    logits buffer) and 4096 / 4097 (the longest sequence on the matrix cores, and the first one on
+    the float32 kernel)."""
+    wl = CONFIGS[3].with_(B=1, H=2, N=N, d=d, d_u=d, dtype="bf16", seed=3100 + d + N)
+    x = make_inputs(wl)
+    o = to_f64(run_encoder(x, "bf16", rope=True))
+    ref = R.encoder_forward(**x, rope=True)
+    err = rel_l2(o, ref)
+    print(f"encoder d={d} N={N} rel_l2={err:.3e}", flush=True)
+    assert err <= TOL["bf16"]
+
+
 def test_encoder_mfma_large_logits():
     """u scaled by 30: logits spread over a wide range, the global maximum keeps e^{s-m} in range."""
     wl = CONFIGS[3].with_(B=1, H=2, N=300, d=64, d_u=64, dtype="bf16", seed=3999)

@@ -457,12 +457,14 @@ __global__ __launch_bounds__(D * 4) void causal_seg_kernel(Problem p, CausalWork
     // composed scalar map of the segment (pass 1): X <- Rs X + alp H + ..., Y <- Y + bet H + ...,
     // with Rs the exact product of the chunk factors rX
     float Rs = 1.f;
-    // The registers hold X, Y, H in a scaled basis, X = rho Z + alp H and Y = Y' + bet H (Z, Y' in
-    // the X, Y registers): the per-chunk map X <- rX X + cHX H, Y <- Y + cHY H then only changes the
-    // three scalars, rho <- rX rho, alp <- rX alp + cHX, bet <- bet + cHY, and the update operands
-    // and output coefficients absorb them (Z += K^T diag((w_X - alp)/rho) V, Y' += K^T diag(w_Y - bet) V).
-    // rho is folded back into Z before it drops below 2^-40, and rX is floored at 2^-40 (a change of
-    // at most 2^-40 |X| where the exact factor is smaller), so 1/rho stays within 2^80.
+    // The X registers hold Z = X / rho. Per chunk the map X <- rX X + cHX H becomes rho <- rX rho and
+    // Z += (cHX / rho) H, with the update operands scaled by 1/rho (Z += K^T diag(w_X / rho) V) and the
+    // output coefficient of the X product by rho, so the multiply by rX disappears. The H couplings
+    // of X and Y stay explicit: late in a sequence X and Y are far smaller than their H terms, and
+    // carrying those terms as scalars too would make the states and update weights cancel before
+    // bf16 rounding. rho is folded back into Z before it drops below 2^-40, and rX is floored at
+    // 2^-40 (a change of at most 2^-40 |X| where the exact factor is smaller), so 1/rho stays within
+    // 2^80. alp and bet are the composed H coefficients of X and Y (pass 1's segment map).
     float rho = 1.f, alp = 0.f, bet = 0.f;
 
     // v of this wave's columns: lane holds tokens 2 (lane & 31), +1 and columns 8 (lane >> 5) + [0, 8)
@@ -517,16 +519,18 @@ __global__ __launch_bounds__(D * 4) void causal_seg_kernel(Problem p, CausalWork
         const float alp1 = t0 > 0 ? ch.x * alp + ch.y : alp;
         const float bet1 = t0 > 0 ? bet + ch.z : bet;
         const float irho1 = 1.f / rho1;
+        const float hz = t0 > 0 ? ch.y * irho1 : 0.f;   // Z += hz H
+        const float hy = t0 > 0 ? ch.z : 0.f;           // Y += hy H
 
         // ---- stage this wave's v tile (token pairs per column) and the update operands
-        // v (w_X - alp1)/rho1 and v (w_Y - bet1)
+        // v w_X / rho1 and v w_Y
         {
             // rows past N hold copies of row N - 1 (finite); every product they enter is zero: the
             // record's k^ rows and W columns of absent tokens are zero
             const uint32_t a4[4] = {va.x, va.y, va.z, va.w};
             const uint32_t b4[4] = {vb.x, vb.y, vb.z, vb.w};
             const float4 w4 = *reinterpret_cast<const float4 *>(co + kCoW + 2 * vtok);   // wX, wY of both tokens
-            const float4 wv = make_float4((w4.x - alp1) * irho1, w4.y - bet1, (w4.z - alp1) * irho1, w4.w - bet1);
+            const float4 wv = make_float4(w4.x * irho1, w4.y, w4.z * irho1, w4.w);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 // columns 8 vh + 2i (low halves) and 8 vh + 2i + 1 (high halves)
@@ -594,6 +598,11 @@ __global__ __launch_bounds__(D * 4) void causal_seg_kernel(Problem p, CausalWork
             for (int jj = 0; jj < 2; ++jj) {
                 const int jb = 2 * ks + jj;
 #pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    X[jb][i] += hz * Hm[jb][i];
+                    Y[jb][i] += hy * Hm[jb][i];
+                }
+#pragma unroll
                 for (int ks2 = 0; ks2 < kC / 32; ++ks2) {
                     const bf16x8 Ak = ld16(rb + R::k_off + (size_t(jb * 2 + ks2) * 64 + lane) * 16);
                     X[jb] = mfma(Ak, BX[ks2], X[jb]);
@@ -611,8 +620,8 @@ __global__ __launch_bounds__(D * 4) void causal_seg_kernel(Problem p, CausalWork
             for (int tb = 0; tb < 4; ++tb) {
                 f32x4 oacc;
                 const float4 cq = *reinterpret_cast<const float4 *>(co + kCoQ + 4 * (16 * tb + l16));  // cX, beta, kappa
-                // X = rho Z + alp H, Y = Y' + bet H at t0
-                const float cz = cq.x * rho, chh = cq.z + cq.x * alp + cq.y * bet;
+                // X = rho Z at t0
+                const float cz = cq.x * rho, chh = cq.z;
 #pragma unroll
                 // (without a carried state the products are zero and the coefficients finite)
                 for (int i = 0; i < 4; ++i) oacc[i] = cz * ax[tb][i] + cq.y * ay[tb][i] + chh * ah[tb][i];
@@ -642,14 +651,11 @@ __global__ __launch_bounds__(D * 4) void causal_seg_kernel(Problem p, CausalWork
         if (c + 1 < c_end) chunk(c + 1, recB, recA);
     }
 
-    // back to the plain basis: X = rho Z + alp H, Y = Y' + bet H
+    // back to the plain basis: X = rho Z
 #pragma unroll
     for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            X[jb][i] = rho * X[jb][i] + alp * Hm[jb][i];
-            Y[jb][i] = Y[jb][i] + bet * Hm[jb][i];
-        }
+        for (int i = 0; i < 4; ++i) X[jb][i] *= rho;
     if (PASS1) {
         // segment-local sums and the composed scalar map, for the combine step
         float4 *dst = reinterpret_cast<float4 *>(work.segst + (static_cast<size_t>(bh) * (nseg - 1) + seg) * kSegFloats<D>);

@@ -184,6 +184,24 @@ def test_causal_segments_large_logits(scale):
     assert err <= TOL["bf16"]
 
 
+def test_causal_long_sequence_tail_precision():
+    """Two heads at N = 16384 (128 scan segments of 2 chunks, so a long combine chain). Late in the
+    sequence the outputs are small and the carried states nearly cancel against their H terms; the
+    centred state basis keeps the error there at the level of the bf16 operand rounding. The bar
+    for t > 1024 (6e-3, measured 3.9e-3) is tighter than the 2e-2 contract on purpose: a basis
+    change that lets the states cancel before rounding doubles this error while staying under 2e-2."""
+    wl = CONFIGS[4].with_(B=1, H=2, seed=3500)
+    x = make_inputs(wl)
+    o = run_causal(x, "bf16", rope=True)
+    got = to_f64(o)
+    ref = R.causal_forward(**x, rope=True)
+    err = rel_l2(got, ref)
+    tail = rel_l2(got[:, :, 1024:], ref[:, :, 1024:])
+    print(f"long sequence rel_l2={err:.3e} tail={tail:.3e}", flush=True)
+    assert err <= TOL["bf16"]
+    assert tail <= 6e-3
+
+
 def test_causal_workspace_reuse():
     wl = CONFIGS[4].with_(B=1, H=3, N=700, seed=3200)
     x = make_inputs(wl)

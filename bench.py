@@ -164,8 +164,8 @@ def copy_probe(mib: int) -> None:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the encoder and decode-step measurements")
@@ -245,7 +245,10 @@ def main():
                                "+ causal_seg_combine_kernel + causal_seg_kernel (main)",
                      "algorithmic_bytes_per_launch": nbytes,
                      "avg_kernel_ms": avg_kernel_ms,
-                     "min_kernel_ms": float(np.min(kernel_ms))},
+                     "min_kernel_ms": float(np.min(kernel_ms)),
+                     "p10_kernel_ms": float(np.percentile(kernel_ms, 10)),
+                     "median_kernel_ms": float(np.median(kernel_ms)),
+                     "p90_kernel_ms": float(np.percentile(kernel_ms, 90))},
         "cpu_baseline": cpu,
     }
     if ref:

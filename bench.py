@@ -27,6 +27,7 @@ if ROOT not in sys.path:
 from synth import CONFIGS, make_inputs  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+FP32_PEAK_TFLOPS = 157.3        # MI355X float32 vector, published
 WORKLOAD = CONFIGS[4]
 # the bounded CPU sample: 16 of the 32 (b, h) heads at full length (about 20 s of CPU work)
 SAMPLE_HEADS = [(b, h) for h in range(0, 16, 2) for b in (0, 1)]
@@ -109,6 +110,24 @@ def secondary(dev, steps: int = 20) -> list:
         return a.elapsed_time(b) / steps
 
     out = []
+    # the LM-layer-shaped causal forward in float32 (the float32 path: 1e-4 parity needs float32
+    # arithmetic, so its roof is the float32 vector rate on the recurrence's 12 d^2 flop per
+    # token-head, 157.3 TFLOP/s)
+    wl = CONFIGS[2]
+    x = make_inputs(wl)
+    t = {k: torch.from_numpy(v).to(device=dev, dtype=torch.float32) for k, v in x.items()}
+    o = torch.empty_like(t["v"])
+    ms = timed(lambda st: Z.zeros_fwd_causal(t["q"], t["k"], t["v"], t["u"], t["mu"], t["tau"], t["g1"],
+                                             t["gh"], out=o, stream=st))
+    nbytes = algorithmic_bytes(wl)
+    flops = 12 * wl.d * wl.d * wl.B * wl.H * wl.N
+    out.append({"workload": wl.name, "call": "zeros_fwd_causal", "dtype": "f32", "ms": ms,
+                "tokens_per_s": wl.B * wl.N / (ms * 1e-3), "algorithmic_bytes": nbytes,
+                "achieved_GBs": nbytes / (ms * 1e-3) / 1e9, "algorithmic_flops": flops,
+                "achieved_TFLOPs": flops / (ms * 1e-3) / 1e12,
+                "frac_fp32_vector": flops / (ms * 1e-3) / 1e12 / FP32_PEAK_TFLOPS})
+    del t, o
+
     wl = CONFIGS[3]
     x = make_inputs(wl)
     t = {k: torch.from_numpy(v).to(device=dev, dtype=torch.float32 if k in ("mu", "tau") else torch.bfloat16)

@@ -88,10 +88,32 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p) {
         (&sm.Hs[0][0])[x] = 0.f;
     }
 
+    // the rows of the next chunk are read while the current one is processed
+    const int vr = tid / 8, vm = (tid % 8) * 2;
+    float nq[EPT], nk[EPT], nu[EPT], nv[2], ng1 = 0.f, ngh = 0.f;
+    auto prefetch = [&](const int t0) __attribute__((always_inline)) {
+        const int tok = min(t0 + lr, N - 1);               // in bounds; rows past N are zeroed below
+#pragma unroll
+        for (int c = 0; c < EPT; ++c) {
+            const size_t idx = static_cast<size_t>(tok) * D + c0 + c;
+            nq[c] = ld(q, idx);
+            nk[c] = ld(k, idx);
+            nu[c] = ld(u, idx);
+        }
+        const size_t vidx = static_cast<size_t>(min(t0 + vr, N - 1)) * D + tile * kTile + vm;
+        nv[0] = ld(v, vidx);
+        nv[1] = ld(v, vidx + 1);
+        if (tid < kC) {
+            ng1 = ld(g1, min(t0 + tid, N - 1));
+            ngh = ld(gh, min(t0 + tid, N - 1));
+        }
+    };
+    if (N > 0) prefetch(0);
+
     for (int t0 = 0; t0 < N; t0 += kC) {
         const int nval = min(kC, N - t0);
 
-        // ---- load, normalise, rotate
+        // ---- normalise, rotate and stage the rows read ahead; read the next chunk's rows
         {
             const int tok = t0 + lr;
             const bool valid = lr < nval;
@@ -99,10 +121,9 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p) {
             float ssq = 0.f, ssk = 0.f;
 #pragma unroll
             for (int c = 0; c < EPT; ++c) {
-                const size_t idx = static_cast<size_t>(tok) * D + c0 + c;
-                xq[c] = valid ? ld(q, idx) : 0.f;
-                xk[c] = valid ? ld(k, idx) : 0.f;
-                xu[c] = valid ? ld(u, idx) : 0.f;
+                xq[c] = valid ? nq[c] : 0.f;
+                xk[c] = valid ? nk[c] : 0.f;
+                xu[c] = valid ? nu[c] : 0.f;
                 ssq += xq[c] * xq[c];
                 ssk += xk[c] * xk[c];
             }
@@ -136,26 +157,30 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p) {
             }
         }
         {
-            const int r = tid / 8, mc = (tid % 8) * 2;
-            const bool valid = r < nval;
-            const size_t idx = static_cast<size_t>(t0 + r) * D + tile * kTile + mc;
-            sm.vt[r][mc] = valid ? ld(v, idx) : 0.f;
-            sm.vt[r][mc + 1] = valid ? ld(v, idx + 1) : 0.f;
+            const bool valid = vr < nval;
+            sm.vt[vr][vm] = valid ? nv[0] : 0.f;
+            sm.vt[vr][vm + 1] = valid ? nv[1] : 0.f;
         }
         if (tid < kC) {
             const bool valid = tid < nval;
-            sm.sig1[tid] = valid ? sigmoidf(ld(g1, t0 + tid)) : 0.f;
-            sm.sigh[tid] = valid ? sigmoidf(ld(gh, t0 + tid)) : 0.f;
+            sm.sig1[tid] = valid ? sigmoidf(ng1) : 0.f;
+            sm.sigh[tid] = valid ? sigmoidf(ngh) : 0.f;
             sm.invden[tid] = 1.f / (et + static_cast<float>(t0 + tid + 1));
         }
+        if (t0 + kC < N) prefetch(t0 + kC);
         __syncthreads();
 
         // ---- running u-sum and ubar: products u_i * ubar_i in place
         if (tid < D) {
-            for (int r = 0; r < nval; ++r) {
-                const float ur = sm.ub[r][tid];
-                Su += ur;
-                sm.ub[r][tid] = ur * ((emu + Su) * sm.invden[r]);
+            // all kC rows (absent ones hold zeros, so the sum is unchanged): the loop unrolls and
+            // its LDS reads are in flight together
+            float ur[kC];
+#pragma unroll
+            for (int r = 0; r < kC; ++r) ur[r] = sm.ub[r][tid];
+#pragma unroll
+            for (int r = 0; r < kC; ++r) {
+                Su += ur[r];
+                sm.ub[r][tid] = ur[r] * ((emu + Su) * sm.invden[r]);
             }
         }
         __syncthreads();
@@ -235,22 +260,29 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p) {
 
         // ---- outputs: intra-chunk part plus the carried states
         {
+            // token t, columns m0, m0 + 1: each LDS read of q^, W serves both columns
             const int t = tid / 8, m0 = (tid % 8) * 2;
-            float out[2];
+            float in0 = 0.f, in1 = 0.f;
 #pragma unroll
-            for (int x = 0; x < 2; ++x) {
-                const int mm = m0 + x;
-                float intra = 0.f;
-                for (int i = 0; i <= t; ++i) intra += sm.W[t][i] * sm.vt[i][mm];
-                float xF = 0.f, xG = 0.f, xH = 0.f;
-                for (int j = 0; j < D; ++j) {
-                    const float qv = sm.qh[t][j];
-                    xF += qv * sm.F[j][mm];
-                    xG += qv * sm.G[j][mm];
-                    xH += qv * sm.Hs[j][mm];
-                }
-                out[x] = intra + sm.a_in[t] * xF + sm.brow[t] * xG + sm.grow[t] * xH;
+            for (int i = 0; i < kC; ++i) {                   // W[t][i] = 0 for i > t
+                const float wti = sm.W[t][i];
+                const float2 vv = *reinterpret_cast<const float2 *>(&sm.vt[i][m0]);
+                in0 += wti * vv.x;
+                in1 += wti * vv.y;
             }
+            float xF0 = 0.f, xF1 = 0.f, xG0 = 0.f, xG1 = 0.f, xH0 = 0.f, xH1 = 0.f;
+#pragma unroll 8
+            for (int j = 0; j < D; ++j) {
+                const float qv = sm.qh[t][j];
+                const float2 f2 = *reinterpret_cast<const float2 *>(&sm.F[j][m0]);
+                const float2 g2 = *reinterpret_cast<const float2 *>(&sm.G[j][m0]);
+                const float2 h2 = *reinterpret_cast<const float2 *>(&sm.Hs[j][m0]);
+                xF0 += qv * f2.x; xF1 += qv * f2.y;
+                xG0 += qv * g2.x; xG1 += qv * g2.y;
+                xH0 += qv * h2.x; xH1 += qv * h2.y;
+            }
+            const float out[2] = {in0 + sm.a_in[t] * xF0 + sm.brow[t] * xG0 + sm.grow[t] * xH0,
+                                  in1 + sm.a_in[t] * xF1 + sm.brow[t] * xG1 + sm.grow[t] * xH1};
             if (t < nval) {
                 const size_t idx = static_cast<size_t>(t0 + t) * D + tile * kTile + m0;
                 o[idx] = from_f32<T>(out[0]);
@@ -261,19 +293,37 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p) {
 
         // ---- fold the chunk's keys into the states
         {
-            const int mm = tid % kTile;
+            // thread: column mm, rows j0 + JS r; the key's v, e^{s - m1} and s are read once for
+            // all of its rows
+            constexpr int JS = kThreads / kTile;             // row stride
+            constexpr int RPT = (D + JS - 1) / JS;           // rows per thread
+            const int mm = tid % kTile, j0 = tid / kTile;
             const float decay = sm.carry[3];
-            for (int j = tid / kTile; j < D; j += kThreads / kTile) {
-                float f = 0.f, g = 0.f, hh = 0.f;
-                for (int i = 0; i < nval; ++i) {
-                    const float kv = sm.kh[i][j] * sm.vt[i][mm];
-                    f += sm.estate[i] * kv;
-                    g += sm.s[i] * kv;
-                    hh += kv;
+            float f[RPT], g[RPT], hh[RPT];
+#pragma unroll
+            for (int r = 0; r < RPT; ++r) f[r] = g[r] = hh[r] = 0.f;
+#pragma unroll
+            for (int i = 0; i < kC; ++i) {                   // absent keys: k^ and v rows are zero
+                const float vi = sm.vt[i][mm], ei = sm.estate[i], si = sm.s[i];
+#pragma unroll
+                for (int r = 0; r < RPT; ++r) {
+                    const int j = j0 + JS * r;
+                    if (RPT * JS == D || j < D) {
+                        const float kv = sm.kh[i][j] * vi;
+                        f[r] += ei * kv;
+                        g[r] += si * kv;
+                        hh[r] += kv;
+                    }
                 }
-                sm.F[j][mm] = decay * sm.F[j][mm] + f;
-                sm.G[j][mm] += g;
-                sm.Hs[j][mm] += hh;
+            }
+#pragma unroll
+            for (int r = 0; r < RPT; ++r) {
+                const int j = j0 + JS * r;
+                if (RPT * JS == D || j < D) {
+                    sm.F[j][mm] = decay * sm.F[j][mm] + f[r];
+                    sm.G[j][mm] += g[r];
+                    sm.Hs[j][mm] += hh[r];
+                }
             }
         }
         m_c = m_new;

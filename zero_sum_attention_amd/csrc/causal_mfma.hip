@@ -191,7 +191,6 @@ __global__ __launch_bounds__(kPrepThreads) void causal_prep_kernel(Problem p, Ca
     constexpr int RT = D / 64;
     constexpr int QW = D / 4;           // features per thread in the load phase
     constexpr int NV = QW / 8;
-    constexpr int NP = QW / 2;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, g4 = lane >> 4;
     const int N = p.N;
@@ -799,9 +798,10 @@ static void seg_plan(int B, int H, int N, int &nseg, int &seg_chunks) {
     nseg = nch > 0 ? (nch + seg_chunks - 1) / seg_chunks : 1;
 }
 
+// workspace regions start on 256-byte boundaries
+static size_t up(size_t x) { return (x + 255) / 256 * 256; }
+
 size_t causal_work_bytes(int B, int H, int N, int du) {
-    const size_t a = 256;
-    auto up = [a](size_t x) { return (x + a - 1) / a * a; };
     const size_t nls = (static_cast<size_t>(N) + kLogitSeg - 1) / kLogitSeg;
     const size_t nch = (static_cast<size_t>(N) + kC - 1) / kC;
     const size_t bh = static_cast<size_t>(B) * H;
@@ -813,8 +813,6 @@ size_t causal_work_bytes(int B, int H, int N, int du) {
 }
 
 CausalWork causal_work_carve(void *base, int B, int H, int N, int du) {
-    const size_t a = 256;
-    auto up = [a](size_t x) { return (x + a - 1) / a * a; };
     const size_t nls = (static_cast<size_t>(N) + kLogitSeg - 1) / kLogitSeg;
     const size_t nch = (static_cast<size_t>(N) + kC - 1) / kC;
     const size_t bh = static_cast<size_t>(B) * H;

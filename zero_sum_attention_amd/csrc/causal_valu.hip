@@ -21,6 +21,7 @@ namespace {
 constexpr int kC = 32;         // tokens per chunk
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kTile = 16;      // value columns per workgroup
+constexpr int kCPT = kTile / 8;  // value columns per thread in the staging and output passes
 constexpr int kTPR = 8;        // threads per token row in the load phase
 
 template <int D>
@@ -89,8 +90,8 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p) {
     }
 
     // the rows of the next chunk are read while the current one is processed
-    const int vr = tid / 8, vm = (tid % 8) * 2;
-    float nq[EPT], nk[EPT], nu[EPT], nv[2], ng1 = 0.f, ngh = 0.f;
+    const int vr = tid / 8, vm = (tid % 8) * kCPT;
+    float nq[EPT], nk[EPT], nu[EPT], nv[kCPT], ng1 = 0.f, ngh = 0.f;
     auto prefetch = [&](const int t0) __attribute__((always_inline)) {
         const int tok = min(t0 + lr, N - 1);               // in bounds; rows past N are zeroed below
 #pragma unroll
@@ -101,8 +102,8 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p) {
             nu[c] = ld(u, idx);
         }
         const size_t vidx = static_cast<size_t>(min(t0 + vr, N - 1)) * D + tile * kTile + vm;
-        nv[0] = ld(v, vidx);
-        nv[1] = ld(v, vidx + 1);
+#pragma unroll
+        for (int c = 0; c < kCPT; ++c) nv[c] = ld(v, vidx + c);
         if (tid < kC) {
             ng1 = ld(g1, min(t0 + tid, N - 1));
             ngh = ld(gh, min(t0 + tid, N - 1));
@@ -158,8 +159,8 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p) {
         }
         {
             const bool valid = vr < nval;
-            sm.vt[vr][vm] = valid ? nv[0] : 0.f;
-            sm.vt[vr][vm + 1] = valid ? nv[1] : 0.f;
+#pragma unroll
+            for (int c = 0; c < kCPT; ++c) sm.vt[vr][vm + c] = valid ? nv[c] : 0.f;
         }
         if (tid < kC) {
             const bool valid = tid < nval;
@@ -240,6 +241,7 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p) {
         {
             const int t = tid / 8, i0 = (tid % 8) * 4;
             float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
             for (int j = 0; j < D; ++j) {
                 const float qv = sm.qh[t][j];
 #pragma unroll
@@ -260,33 +262,34 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p) {
 
         // ---- outputs: intra-chunk part plus the carried states
         {
-            // token t, columns m0, m0 + 1: each LDS read of q^, W serves both columns
-            const int t = tid / 8, m0 = (tid % 8) * 2;
-            float in0 = 0.f, in1 = 0.f;
+            // token t, columns m0 + [0, kCPT): each LDS read of q^, W serves all of them
+            const int t = tid / 8, m0 = (tid % 8) * kCPT;
+            float in[kCPT], xF[kCPT], xG[kCPT], xH[kCPT];
+#pragma unroll
+            for (int c = 0; c < kCPT; ++c) in[c] = xF[c] = xG[c] = xH[c] = 0.f;
 #pragma unroll
             for (int i = 0; i < kC; ++i) {                   // W[t][i] = 0 for i > t
                 const float wti = sm.W[t][i];
-                const float2 vv = *reinterpret_cast<const float2 *>(&sm.vt[i][m0]);
-                in0 += wti * vv.x;
-                in1 += wti * vv.y;
+#pragma unroll
+                for (int c = 0; c < kCPT; ++c) in[c] += wti * sm.vt[i][m0 + c];
             }
-            float xF0 = 0.f, xF1 = 0.f, xG0 = 0.f, xG1 = 0.f, xH0 = 0.f, xH1 = 0.f;
 #pragma unroll 8
             for (int j = 0; j < D; ++j) {
                 const float qv = sm.qh[t][j];
-                const float2 f2 = *reinterpret_cast<const float2 *>(&sm.F[j][m0]);
-                const float2 g2 = *reinterpret_cast<const float2 *>(&sm.G[j][m0]);
-                const float2 h2 = *reinterpret_cast<const float2 *>(&sm.Hs[j][m0]);
-                xF0 += qv * f2.x; xF1 += qv * f2.y;
-                xG0 += qv * g2.x; xG1 += qv * g2.y;
-                xH0 += qv * h2.x; xH1 += qv * h2.y;
+#pragma unroll
+                for (int c = 0; c < kCPT; ++c) {
+                    xF[c] += qv * sm.F[j][m0 + c];
+                    xG[c] += qv * sm.G[j][m0 + c];
+                    xH[c] += qv * sm.Hs[j][m0 + c];
+                }
             }
-            const float out[2] = {in0 + sm.a_in[t] * xF0 + sm.brow[t] * xG0 + sm.grow[t] * xH0,
-                                  in1 + sm.a_in[t] * xF1 + sm.brow[t] * xG1 + sm.grow[t] * xH1};
+            float out[kCPT];
+#pragma unroll
+            for (int c = 0; c < kCPT; ++c) out[c] = in[c] + sm.a_in[t] * xF[c] + sm.brow[t] * xG[c] + sm.grow[t] * xH[c];
             if (t < nval) {
                 const size_t idx = static_cast<size_t>(t0 + t) * D + tile * kTile + m0;
-                o[idx] = from_f32<T>(out[0]);
-                o[idx + 1] = from_f32<T>(out[1]);
+#pragma unroll
+                for (int c = 0; c < kCPT; ++c) o[idx + c] = from_f32<T>(out[c]);
             }
         }
         __syncthreads();

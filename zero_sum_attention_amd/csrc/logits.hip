@@ -5,9 +5,9 @@
 // ubar_i = (e^tau mu + sum_{j<=i} u_j) / (e^tau + i). The logit depends on the step i only, so
 // all of them can be formed before the attention scan, in two passes over u:
 //   pass 1 (useg_sum_kernel): per (head, segment of kSeg tokens), the column sums of u;
-//   pass 2 (logits_kernel):   per (head, segment), the running sum starts from e^tau mu plus
-//                             the sums of the earlier segments, then a lane-parallel scan over
-//                             64-token blocks gives ubar_i and s_i.
+//   pass 2 (logits_stream_kernel for bfloat16 and d 64/128, logits_kernel otherwise): per
+//                             (head, segment), the running sum starts from e^tau mu plus the
+//                             sums of the earlier segments and gives ubar_i and s_i.
 // Output: s [B*H, N] float32, the per-segment sums [B*H, nseg, d_u] (their total is the u-sum of
 // the recurrent state) and, per 64-token chunk, (max s, sum e^{s - max}, sum s) [B*H, nchunk, 4].
 #include "device_common.hpp"
@@ -175,11 +175,12 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(const T *u, const floa
     }
 }
 
-// Logits of one segment, bfloat16 u, by serial token streams: lane (stream st, feature group fg)
-// keeps the running sum of features [8 fg, 8 fg + 8) over the TPS consecutive tokens of its stream
-// (held in registers), so each token costs 3 float ops per feature and no cross-lane scan. The
-// stream starts come from the stream sums (first pass over the registers); the per-token dot
-// partials of the LPT lanes of a stream are summed by a butterfly that leaves token k on lane k.
+// Logits of one segment, bfloat16 u, by token streams: lane (stream st, feature group fg) keeps
+// the running sum of features [8 fg, 8 fg + 8) over the TPS consecutive tokens of its stream (held
+// in registers), so each token costs 3 float ops per feature. The stream starts are an exclusive
+// scan of the stream sums: a shuffle scan over the streams of a wave (LPT lanes apart) plus the
+// totals of the earlier waves and segments; the per-token dot partials of the LPT lanes of a
+// stream are summed by a butterfly that leaves token k on lane k.
 constexpr int kStreamThreads = 256;
 
 template <int D>

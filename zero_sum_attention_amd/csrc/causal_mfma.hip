@@ -757,15 +757,20 @@ hipError_t set_smem(K kernel, size_t bytes) {
 
 template <int D, bool ROPE>
 hipError_t launch_one(const Problem &p, const CausalWork &w, hipStream_t stream) {
-    static bool attr_set = false;   // idempotent; a race only repeats the same calls
-    if (!attr_set) {
-        hipError_t err = set_smem(&causal_prep_kernel<D, ROPE>, sizeof(PSmem<D>));
+    // the LDS size attribute is per device: set once on each device the library launches on
+    // (idempotent; two threads racing here only repeat the same call)
+    constexpr int kMaxDev = 64;
+    static bool attr_set[kMaxDev] = {};
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= kMaxDev || !attr_set[dev]) {
+        err = set_smem(&causal_prep_kernel<D, ROPE>, sizeof(PSmem<D>));
         if (err != hipSuccess) return err;
-        attr_set = true;
+        if (dev >= 0 && dev < kMaxDev) attr_set[dev] = true;
     }
     const int nch = (p.N + kC - 1) / kC;
     const int bh = p.B * p.H;
-    hipError_t err;
     if (nch > 0) {
         hipLaunchKernelGGL((causal_prep_kernel<D, ROPE>), dim3(bh * nch), dim3(kPrepThreads),
                            sizeof(PSmem<D>), stream, p, w);

@@ -141,7 +141,9 @@ def test_workspace_size_and_validation(lib):
     rec = (4 * 4 + 8 * 2 + 6) * 1024 + (6 * 64 + 8) * 4   # q^, k^T, non-zero W operand tiles + coefficients
     sink = 64 * 128 * 2                                  # output rows past N of a last, partial chunk
     assert n == logits + useg + agg + rope + segsc + segst + sink + bh * nch * rec
-    assert lib.zeros_fwd_causal_workspace_bytes(ctypes.byref(shape(dtype=0))) == 0   # f32 path: none
+    # float32 path: logits [2, 8], u sums of one 256-token segment [2, 1, 16], aggregates of one
+    # 64-token chunk [2, 1] float4, each region rounded up to 256 bytes
+    assert lib.zeros_fwd_causal_workspace_bytes(ctypes.byref(shape(dtype=0))) == 3 * 256
     assert lib.zeros_fwd_causal_workspace_bytes(None) == 0
     small = shape(B=1, H=2, N=8, d=64, d_u=64, dtype=1)
     need = lib.zeros_fwd_causal_workspace_bytes(ctypes.byref(small))

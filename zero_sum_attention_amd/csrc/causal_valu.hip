@@ -10,8 +10,8 @@
 //   o_t = sum_{t0<i<=t} W_{t,i} v_i + q^_t (a_t e^{m0-m_t} F + beta_t G + gamma_t H)   (states at t0)
 // with W_{t,i} = (q^_t.k^_i)(a_t e^{s_i-m_t} + beta_t s_i + gamma_t), a_t = sigmah_t / E_t, and
 // E, F rescaled by the running logit maximum m. The chunk then folds its keys into F, G, H.
-// The u running sum, logits and scalar scans are recomputed by every tile of a head (they are
-// O(C d) per chunk against O(C d^2) for the contractions).
+// The logits s_i and the per-segment u sums come from logits.hip (computed once per head, ahead of
+// this kernel); the scalar scans are recomputed by every tile of a head (O(C) per chunk).
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -28,11 +28,10 @@ template <int D>
 struct CausalSmem {
     float qh[kC][D + 1];   // normalised (and rotated) queries of the chunk
     float kh[kC][D + 1];   // normalised (and rotated) keys
-    float ub[kC][D + 1];   // u, then u * ubar
     float vt[kC][kTile];   // this workgroup's value columns
     float W[kC][kC + 1];   // intra-chunk weights times cosines
     float F[D][kTile], G[D][kTile], Hs[D][kTile];
-    float s[kC], sig1[kC], sigh[kC], invden[kC];
+    float s[kC], sig1[kC], sigh[kC];
     float a_in[kC];        // a_t e^{m0 - m_t}: multiplies the carried F
     float a_loc[kC];       // a_t = sigmah_t / E_t (E relative to m_t)
     float mrow[kC], brow[kC], grow[kC];
@@ -44,7 +43,7 @@ template <typename T>
 __device__ __forceinline__ float ld(const T *p, size_t i) { return to_f32(p[i]); }
 
 template <int D, typename T, bool ROPE>
-__global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p) {
+__global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p, const float *s_all, const float *useg, int nls) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     CausalSmem<D> &sm = *reinterpret_cast<CausalSmem<D> *>(smem_raw);
     constexpr int NTILE = D / kTile;
@@ -58,19 +57,16 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p) {
     if ((G & 7) == 0) L = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
     const int tile = L % NTILE;
     const int bh = L / NTILE;
-    const int h = bh % p.H;
     const int N = p.N;
     const size_t row0 = static_cast<size_t>(bh) * N;
     const T *q = static_cast<const T *>(p.q) + row0 * D;
     const T *k = static_cast<const T *>(p.k) + row0 * D;
     const T *v = static_cast<const T *>(p.v) + row0 * D;
-    const T *u = static_cast<const T *>(p.u) + row0 * D;
     const T *g1 = static_cast<const T *>(p.g1) + row0;
     const T *gh = static_cast<const T *>(p.gh) + row0;
     T *o = static_cast<T *>(p.o) + row0 * D;
 
-    const float et = expf(p.tau[h]);
-    const float rs_du = 1.f / sqrtf(static_cast<float>(D));
+    const float *srow = s_all + row0;
 
     const int lr = tid / kTPR, lp = tid % kTPR, c0 = lp * EPT;
     double rope_rev[ROPE ? EPT / 2 : 1];
@@ -79,8 +75,6 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p) {
         for (int jj = 0; jj < EPT / 2; ++jj) rope_rev[jj] = rope_rev_per_pos(c0 / 2 + jj, D, p.rope_base);
     }
 
-    float Su = 0.f;                                         // owned by thread tid < D
-    const float emu = (tid < D) ? et * p.mu[h * D + tid] : 0.f;
     float m_c = kNegInf, E_c = 0.f, P_c = 0.f;
 
     for (int x = tid; x < D * kTile; x += kThreads) {
@@ -91,7 +85,7 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p) {
 
     // the rows of the next chunk are read while the current one is processed
     const int vr = tid / 8, vm = (tid % 8) * kCPT;
-    float nq[EPT], nk[EPT], nu[EPT], nv[kCPT], ng1 = 0.f, ngh = 0.f;
+    float nq[EPT], nk[EPT], nv[kCPT], ng1 = 0.f, ngh = 0.f, ns = 0.f;
     auto prefetch = [&](const int t0) __attribute__((always_inline)) {
         const int tok = min(t0 + lr, N - 1);               // in bounds; rows past N are zeroed below
 #pragma unroll
@@ -99,7 +93,6 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p) {
             const size_t idx = static_cast<size_t>(tok) * D + c0 + c;
             nq[c] = ld(q, idx);
             nk[c] = ld(k, idx);
-            nu[c] = ld(u, idx);
         }
         const size_t vidx = static_cast<size_t>(min(t0 + vr, N - 1)) * D + tile * kTile + vm;
 #pragma unroll
@@ -107,6 +100,7 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p) {
         if (tid < kC) {
             ng1 = ld(g1, min(t0 + tid, N - 1));
             ngh = ld(gh, min(t0 + tid, N - 1));
+            ns = srow[min(t0 + tid, N - 1)];
         }
     };
     if (N > 0) prefetch(0);
@@ -118,13 +112,12 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p) {
         {
             const int tok = t0 + lr;
             const bool valid = lr < nval;
-            float xq[EPT], xk[EPT], xu[EPT];
+            float xq[EPT], xk[EPT];
             float ssq = 0.f, ssk = 0.f;
 #pragma unroll
             for (int c = 0; c < EPT; ++c) {
                 xq[c] = valid ? nq[c] : 0.f;
                 xk[c] = valid ? nk[c] : 0.f;
-                xu[c] = valid ? nu[c] : 0.f;
                 ssq += xq[c] * xq[c];
                 ssk += xk[c] * xk[c];
             }
@@ -154,7 +147,6 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p) {
             for (int c = 0; c < EPT; ++c) {
                 sm.qh[lr][c0 + c] = xq[c];
                 sm.kh[lr][c0 + c] = xk[c];
-                sm.ub[lr][c0 + c] = xu[c];
             }
         }
         {
@@ -166,32 +158,9 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p) {
             const bool valid = tid < nval;
             sm.sig1[tid] = valid ? sigmoidf(ng1) : 0.f;
             sm.sigh[tid] = valid ? sigmoidf(ngh) : 0.f;
-            sm.invden[tid] = 1.f / (et + static_cast<float>(t0 + tid + 1));
+            sm.s[tid] = valid ? ns : 0.f;
         }
         if (t0 + kC < N) prefetch(t0 + kC);
-        __syncthreads();
-
-        // ---- running u-sum and ubar: products u_i * ubar_i in place
-        if (tid < D) {
-            // all kC rows (absent ones hold zeros, so the sum is unchanged): the loop unrolls and
-            // its LDS reads are in flight together
-            float ur[kC];
-#pragma unroll
-            for (int r = 0; r < kC; ++r) ur[r] = sm.ub[r][tid];
-#pragma unroll
-            for (int r = 0; r < kC; ++r) {
-                Su += ur[r];
-                sm.ub[r][tid] = ur[r] * ((emu + Su) * sm.invden[r]);
-            }
-        }
-        __syncthreads();
-        {
-            float acc = 0.f;
-#pragma unroll
-            for (int c = 0; c < EPT; ++c) acc += sm.ub[lr][c0 + c];
-            acc = group_sum<kTPR>(acc);
-            if (lp == 0) sm.s[lr] = -acc * rs_du;
-        }
         __syncthreads();
 
         // ---- scans of (max, sum e^{s-max}, sum s) over the chunk, joined with the carry
@@ -346,7 +315,11 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p) {
             p.st.Hs[idx] = sm.Hs[j][mm];
         }
         if (tile == 0) {
-            if (tid < D) p.st.Su[static_cast<size_t>(bh) * D + tid] = Su;
+            if (tid < D) {
+                float su = 0.f;
+                for (int sg = 0; sg < nls; ++sg) su += useg[(static_cast<size_t>(bh) * nls + sg) * D + tid];
+                p.st.Su[static_cast<size_t>(bh) * D + tid] = su;
+            }
             if (tid == 0) {
                 p.st.m[bh] = m_c;
                 p.st.E[bh] = E_c;
@@ -358,32 +331,61 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p) {
 }
 
 template <int D, typename T, bool ROPE>
-hipError_t launch_one(const Problem &p, hipStream_t stream) {
+hipError_t launch_one(const Problem &p, const ValuWork &w, hipStream_t stream) {
     const size_t smem = sizeof(CausalSmem<D>);
     const void *fn = reinterpret_cast<const void *>(&causal_valu_kernel<D, T, ROPE>);
     hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                          static_cast<int>(smem));
     if (err != hipSuccess) return err;
     const int grid = p.B * p.H * (D / kTile);
-    hipLaunchKernelGGL((causal_valu_kernel<D, T, ROPE>), dim3(grid), dim3(kThreads), smem, stream, p);
+    const int nls = (p.N + kLogitSeg - 1) / kLogitSeg;
+    hipLaunchKernelGGL((causal_valu_kernel<D, T, ROPE>), dim3(grid), dim3(kThreads), smem, stream, p, w.s, w.useg,
+                       nls);
     return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_d(const Problem &p, hipStream_t stream) {
+hipError_t launch_d(const Problem &p, const ValuWork &w, hipStream_t stream) {
     if (p.dtype == ZEROS_BF16)
-        return p.rope ? launch_one<D, bf16, true>(p, stream) : launch_one<D, bf16, false>(p, stream);
-    return p.rope ? launch_one<D, float, true>(p, stream) : launch_one<D, float, false>(p, stream);
+        return p.rope ? launch_one<D, bf16, true>(p, w, stream) : launch_one<D, bf16, false>(p, w, stream);
+    return p.rope ? launch_one<D, float, true>(p, w, stream) : launch_one<D, float, false>(p, w, stream);
 }
+
+// workspace regions start on 256-byte boundaries
+size_t up256(size_t x) { return (x + 255) / 256 * 256; }
 
 }  // namespace
 
-hipError_t launch_causal_valu(const Problem &p, hipStream_t stream) {
+// Workspace of the float32 / small-d causal path: logits [B H, N], u sums per logit segment
+// [B H, nls, d_u], per-64-token logit aggregates [B H, ceil(N/64)] (written by the logits kernels).
+size_t causal_valu_work_bytes(int B, int H, int N, int du) {
+    const size_t bh = static_cast<size_t>(B) * H;
+    const size_t nls = (static_cast<size_t>(N) + kLogitSeg - 1) / kLogitSeg;
+    const size_t n64 = (static_cast<size_t>(N) + 63) / 64;
+    return up256(bh * N * 4) + up256(bh * nls * du * 4) + up256(bh * n64 * 16);
+}
+
+ValuWork causal_valu_work_carve(void *base, int B, int H, int N, int du) {
+    const size_t bh = static_cast<size_t>(B) * H;
+    const size_t nls = (static_cast<size_t>(N) + kLogitSeg - 1) / kLogitSeg;
+    char *b = static_cast<char *>(base);
+    ValuWork w;
+    w.s = reinterpret_cast<float *>(b);
+    b += up256(bh * N * 4);
+    w.useg = reinterpret_cast<float *>(b);
+    b += up256(bh * nls * du * 4);
+    w.agg = reinterpret_cast<float4 *>(b);
+    return w;
+}
+
+hipError_t launch_causal_valu(const Problem &p, const ValuWork &w, hipStream_t stream) {
+    hipError_t err = launch_logits(p, w.useg, w.s, w.agg, nullptr, stream);
+    if (err != hipSuccess) return err;
     switch (p.d) {
-        case 16: return launch_d<16>(p, stream);
-        case 32: return launch_d<32>(p, stream);
-        case 64: return launch_d<64>(p, stream);
-        case 128: return launch_d<128>(p, stream);
+        case 16: return launch_d<16>(p, w, stream);
+        case 32: return launch_d<32>(p, w, stream);
+        case 64: return launch_d<64>(p, w, stream);
+        case 128: return launch_d<128>(p, w, stream);
         default: return hipErrorInvalidValue;
     }
 }

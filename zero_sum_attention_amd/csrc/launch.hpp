@@ -41,12 +41,21 @@ size_t causal_rec_bytes(int d);
 size_t causal_work_bytes(int B, int H, int N, int du);
 CausalWork causal_work_carve(void *base, int B, int H, int N, int du);
 
-// Logits of the causal MFMA path; when rope_tab is not null it also fills the in-chunk RoPE angle
+// Workspace of the float32 / small-d causal path (logits computed ahead of the scan kernel).
+struct ValuWork {
+    float *s;           // [B*H, N] logits
+    float *useg;        // [B*H, ceil(N/kLogitSeg), d_u] u sums per logit segment
+    float4 *agg;        // [B*H, ceil(N/64)] per-64-token logit aggregates (written, not read)
+};
+size_t causal_valu_work_bytes(int B, int H, int N, int du);
+ValuWork causal_valu_work_carve(void *base, int B, int H, int N, int du);
+hipError_t launch_causal_valu(const Problem &p, const ValuWork &w, hipStream_t stream);
+
+// Logits of the causal paths; when rope_tab is not null it also fills the in-chunk RoPE angle
 // table [kCausalChunk, d/2] (cos, sin of r * theta_j) used by the prep kernel.
 hipError_t launch_logits(const Problem &p, float *useg, float *s_out, float4 *agg, float2 *rope_tab,
                          hipStream_t stream);
 hipError_t launch_causal_mfma(const Problem &p, const CausalWork &w, hipStream_t stream);
-hipError_t launch_causal(const Problem &p, hipStream_t stream);
 hipError_t launch_encoder(const Problem &p, hipStream_t stream);
 // Matrix-core encoder for bfloat16, d in {64, 128}, N <= kEncoderMfmaMaxN (logits kept in LDS).
 constexpr int kEncoderMfmaMaxN = 4096;

@@ -10,7 +10,6 @@
 #include "launch.hpp"
 
 namespace zeros {
-hipError_t launch_causal_valu(const Problem &p, hipStream_t stream);
 }
 
 namespace {
@@ -132,9 +131,9 @@ zeros_status zeros_fwd_causal(const zeros_shape *shape, const void *q, const voi
     if (shape->N == 0 && !state_out) return ok();
     const zeros::Problem p = make_problem(shape, q, k, v, u, mu, tau, g1, gh, o, state_out);
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    if (!causal_uses_mfma(shape))
-        return hip_result(zeros::launch_causal_valu(p, hs), "zeros_fwd_causal");
-    const size_t need = zeros::causal_work_bytes(shape->B, shape->H, shape->N, shape->d_u);
+    const bool mfma = causal_uses_mfma(shape);
+    const size_t need = mfma ? zeros::causal_work_bytes(shape->B, shape->H, shape->N, shape->d_u)
+                             : zeros::causal_valu_work_bytes(shape->B, shape->H, shape->N, shape->d_u);
     void *ws = workspace;
     bool owned = false;
     if (ws) {
@@ -142,13 +141,14 @@ zeros_status zeros_fwd_causal(const zeros_shape *shape, const void *q, const voi
             return fail(ZEROS_ERR_SHAPE, "zeros_fwd_causal: workspace smaller than zeros_fwd_causal_workspace_bytes()");
         if (reinterpret_cast<uintptr_t>(ws) & 255u)
             return fail(ZEROS_ERR_SHAPE, "zeros_fwd_causal: workspace must be 256-byte aligned");
-    } else {
+    } else if (need > 0) {          // (an empty sequence on the float32 path needs none)
         hipError_t err = hipMallocAsync(&ws, need, hs);
         if (err != hipSuccess) return hip_result(err, "zeros_fwd_causal (workspace)");
         owned = true;
     }
-    const zeros::CausalWork w = zeros::causal_work_carve(ws, shape->B, shape->H, shape->N, shape->d_u);
-    hipError_t err = zeros::launch_causal_mfma(p, w, hs);
+    const int B = shape->B, H = shape->H, N = shape->N, du = shape->d_u;
+    hipError_t err = mfma ? zeros::launch_causal_mfma(p, zeros::causal_work_carve(ws, B, H, N, du), hs)
+                          : zeros::launch_causal_valu(p, zeros::causal_valu_work_carve(ws, B, H, N, du), hs);
     if (owned) {
         hipError_t e2 = hipFreeAsync(ws, hs);
         if (err == hipSuccess) err = e2;
@@ -158,7 +158,7 @@ zeros_status zeros_fwd_causal(const zeros_shape *shape, const void *q, const voi
 
 size_t zeros_fwd_causal_workspace_bytes(const zeros_shape *shape) {
     if (!shape || shape->B < 1 || shape->H < 1 || shape->N < 0 || shape->d_u < 1) return 0;
-    if (!causal_uses_mfma(shape)) return 0;
+    if (!causal_uses_mfma(shape)) return zeros::causal_valu_work_bytes(shape->B, shape->H, shape->N, shape->d_u);
     return zeros::causal_work_bytes(shape->B, shape->H, shape->N, shape->d_u);
 }
 

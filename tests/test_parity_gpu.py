@@ -216,6 +216,26 @@ def test_causal_workspace_reuse():
     assert rel_l2(to_f64(o1), R.causal_forward(**x, rope=True)) <= TOL["bf16"]
 
 
+def test_causal_f32_workspace_reuse():
+    """The float32 path's workspace (logits, u sums, aggregates): a caller-owned buffer reused by two
+    calls of different lengths gives the same outputs as calls that allocate their own."""
+    ws = None
+    for N in (700, 300):
+        wl = CONFIGS[2].with_(B=2, H=3, N=N, seed=3250 + N)
+        x = make_inputs(wl)
+        t = to_device(x, "f32")
+        if ws is None:
+            n = Z.zeros_fwd_causal_workspace_bytes(2, 3, 700, 64, 64, torch.float32)
+            assert n > 0
+            ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+        args = [t[k] for k in ("q", "k", "v", "u", "mu", "tau", "g1", "gh")]
+        o1 = Z.zeros_fwd_causal(*args, workspace=ws)
+        o2 = Z.zeros_fwd_causal(*args)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2)
+        assert rel_l2(to_f64(o1), R.causal_forward(**x)) <= TOL["f32"]
+
+
 @pytest.mark.parametrize("d", [16, 64, 128])
 @pytest.mark.parametrize("N", [1, 2, 47, 197])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

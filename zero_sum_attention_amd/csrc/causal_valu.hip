@@ -14,6 +14,7 @@
 // this kernel); the scalar scans are recomputed by every tile of a head (O(C) per chunk).
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "mfma_common.hpp"
 
 namespace zeros {
 namespace {
@@ -263,38 +264,37 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p, const 
         }
         __syncthreads();
 
-        // ---- fold the chunk's keys into the states
+        // ---- fold the chunk's keys into the states on the float32 matrix cores (exact float32
+        // products, float32 sums): wave w owns 16-row tiles rt = w, w + 4, ... of F, G, H.
+        // A = k^T (rows: features 16 rt + l16, k: keys k0 + g4), B = the weighted v (k: keys, columns
+        // l16); the accumulator lane holds rows 16 rt + 4 g4 + [0, 4) of column l16.
         {
-            // thread: column mm, rows j0 + JS r; the key's v, e^{s - m1} and s are read once for
-            // all of its rows
-            constexpr int JS = kThreads / kTile;             // row stride
-            constexpr int RPT = (D + JS - 1) / JS;           // rows per thread
-            const int mm = tid % kTile, j0 = tid / kTile;
+            const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6), l16 = lane & 15, g4 = lane >> 4;
             const float decay = sm.carry[3];
-            float f[RPT], g[RPT], hh[RPT];
+            for (int rt = wv; rt < D / 16; rt += kThreads / 64) {
+                f32x4 aF, aG, aH;
 #pragma unroll
-            for (int r = 0; r < RPT; ++r) f[r] = g[r] = hh[r] = 0.f;
-#pragma unroll
-            for (int i = 0; i < kC; ++i) {                   // absent keys: k^ and v rows are zero
-                const float vi = sm.vt[i][mm], ei = sm.estate[i], si = sm.s[i];
-#pragma unroll
-                for (int r = 0; r < RPT; ++r) {
-                    const int j = j0 + JS * r;
-                    if (RPT * JS == D || j < D) {
-                        const float kv = sm.kh[i][j] * vi;
-                        f[r] += ei * kv;
-                        g[r] += si * kv;
-                        hh[r] += kv;
-                    }
+                for (int i = 0; i < 4; ++i) {
+                    const int j = 16 * rt + 4 * g4 + i;
+                    aF[i] = decay * sm.F[j][l16];
+                    aG[i] = sm.G[j][l16];
+                    aH[i] = sm.Hs[j][l16];
                 }
-            }
 #pragma unroll
-            for (int r = 0; r < RPT; ++r) {
-                const int j = j0 + JS * r;
-                if (RPT * JS == D || j < D) {
-                    sm.F[j][mm] = decay * sm.F[j][mm] + f[r];
-                    sm.G[j][mm] += g[r];
-                    sm.Hs[j][mm] += hh[r];
+                for (int k0 = 0; k0 < kC; k0 += 4) {         // absent keys: k^ and v rows are zero
+                    const int key = k0 + g4;
+                    const float a = sm.kh[key][16 * rt + l16];
+                    const float vv = sm.vt[key][l16];
+                    aF = __builtin_amdgcn_mfma_f32_16x16x4f32(a, sm.estate[key] * vv, aF, 0, 0, 0);
+                    aG = __builtin_amdgcn_mfma_f32_16x16x4f32(a, sm.s[key] * vv, aG, 0, 0, 0);
+                    aH = __builtin_amdgcn_mfma_f32_16x16x4f32(a, vv, aH, 0, 0, 0);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int j = 16 * rt + 4 * g4 + i;
+                    sm.F[j][l16] = aF[i];
+                    sm.G[j][l16] = aG[i];
+                    sm.Hs[j][l16] = aH[i];
                 }
             }
         }

@@ -32,6 +32,7 @@ struct CausalSmem {
     float vt[kC][kTile];   // this workgroup's value columns
     float W[kC][kC + 1];   // intra-chunk weights times cosines
     float F[D][kTile], G[D][kTile], Hs[D][kTile];
+    float part[4][kC][kTile];  // the output pass's four products (q^ F, q^ G, q^ H scaled; W V)
     float s[kC], sig1[kC], sigh[kC];
     float a_in[kC];        // a_t e^{m0 - m_t}: multiplies the carried F
     float a_loc[kC];       // a_t = sigmah_t / E_t (E relative to m_t)
@@ -230,36 +231,46 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p, const 
         }
         __syncthreads();
 
-        // ---- outputs: intra-chunk part plus the carried states
+        // ---- outputs on the float32 matrix cores: wave 0, 1, 2 forms q^ F, q^ G, q^ H (scaled per token
+        // by a_in, beta, gamma), wave 3 the intra-chunk W V, each for both 16-token tiles; the
+        // products meet in LDS. Tile (columns l16 ... as A rows, tokens as B columns):
+        //   q^ S: A[col][f] = S[f][col], B[f][tok] = q^[tok][f];   W V: A[col][i] = v[i][col], B[i][tok] = W[tok][i]
+        // and the accumulator lane holds columns 4 g4 + [0, 4) of token 16 tt + l16.
         {
-            // token t, columns m0 + [0, kCPT): each LDS read of q^, W serves all of them
-            const int t = tid / 8, m0 = (tid % 8) * kCPT;
-            float in[kCPT], xF[kCPT], xG[kCPT], xH[kCPT];
+            static_assert(kThreads / 64 == 4 && kTile == 16 && kC % 16 == 0, "output pass shape");
+            const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6), l16 = lane & 15, g4 = lane >> 4;
 #pragma unroll
-            for (int c = 0; c < kCPT; ++c) in[c] = xF[c] = xG[c] = xH[c] = 0.f;
+            for (int tt = 0; tt < kC / 16; ++tt) {
+                const int tok = 16 * tt + l16;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                if (wv < 3) {
+                    const float(*S)[kTile] = wv == 0 ? sm.F : (wv == 1 ? sm.G : sm.Hs);
+#pragma unroll 4
+                    for (int k0 = 0; k0 < D; k0 += 4)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(S[k0 + g4][l16], sm.qh[tok][k0 + g4], acc, 0, 0, 0);
+                    const float cf = wv == 0 ? sm.a_in[tok] : (wv == 1 ? sm.brow[tok] : sm.grow[tok]);
 #pragma unroll
-            for (int i = 0; i < kC; ++i) {                   // W[t][i] = 0 for i > t
-                const float wti = sm.W[t][i];
+                    for (int i = 0; i < 4; ++i) acc[i] *= cf;
+                } else {
 #pragma unroll
-                for (int c = 0; c < kCPT; ++c) in[c] += wti * sm.vt[i][m0 + c];
-            }
-#pragma unroll 8
-            for (int j = 0; j < D; ++j) {
-                const float qv = sm.qh[t][j];
-#pragma unroll
-                for (int c = 0; c < kCPT; ++c) {
-                    xF[c] += qv * sm.F[j][m0 + c];
-                    xG[c] += qv * sm.G[j][m0 + c];
-                    xH[c] += qv * sm.Hs[j][m0 + c];
+                    for (int k0 = 0; k0 < kC; k0 += 4)       // W[t][i] = 0 for i > t
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.vt[k0 + g4][l16], sm.W[tok][k0 + g4], acc, 0, 0, 0);
                 }
-            }
-            float out[kCPT];
 #pragma unroll
-            for (int c = 0; c < kCPT; ++c) out[c] = in[c] + sm.a_in[t] * xF[c] + sm.brow[t] * xG[c] + sm.grow[t] * xH[c];
+                for (int i = 0; i < 4; ++i) sm.part[wv][tok][4 * g4 + i] = acc[i];
+            }
+        }
+        __syncthreads();
+        {
+            const int t = tid / 8, m0 = (tid % 8) * kCPT;
             if (t < nval) {
                 const size_t idx = static_cast<size_t>(t0 + t) * D + tile * kTile + m0;
 #pragma unroll
-                for (int c = 0; c < kCPT; ++c) o[idx + c] = from_f32<T>(out[c]);
+                for (int c = 0; c < kCPT; ++c) {
+                    const float out = (sm.part[0][t][m0 + c] + sm.part[1][t][m0 + c]) +
+                                      (sm.part[2][t][m0 + c] + sm.part[3][t][m0 + c]);
+                    o[idx + c] = from_f32<T>(out);
+                }
             }
         }
         __syncthreads();

@@ -208,23 +208,29 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p, const 
         const float m_new = sm.carry[0];
         if (tid < kC) sm.estate[tid] = (tid < nval) ? expf(sm.s[tid] - m_new) : 0.f;
 
-        // ---- intra-chunk weights W_{t,i} (i <= t)
+        // ---- intra-chunk weights W_{t,i} (i <= t): A^T = K Q^T on the float32 matrix cores, wave w
+        // taking key tile kt = w >> 1 and query tile qt = w & 1 (A[key][f] = k^[key][f],
+        // B[f][query] = q^[query][f]); the accumulator lane holds keys 16 kt + 4 g4 + [0, 4) of query
+        // 16 qt + l16. Tiles with every key after every query are zero.
         {
-            const int t = tid / 8, i0 = (tid % 8) * 4;
-            float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-            for (int j = 0; j < D; ++j) {
-                const float qv = sm.qh[t][j];
-#pragma unroll
-                for (int x = 0; x < 4; ++x) acc[x] += qv * sm.kh[i0 + x][j];
+            static_assert(kThreads / 64 == 4 && kC == 32, "intra-chunk pass shape");
+            const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6), l16 = lane & 15, g4 = lane >> 4;
+            const int kt = wv >> 1, qt = wv & 1;
+            const int t = 16 * qt + l16;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            if (kt <= qt) {
+#pragma unroll 4
+                for (int k0 = 0; k0 < D; k0 += 4)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.kh[16 * kt + l16][k0 + g4], sm.qh[t][k0 + g4], acc, 0, 0, 0);
             }
+            const float at = sm.a_loc[t], mt = sm.mrow[t], bt = sm.brow[t], gt = sm.grow[t];
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const int i = i0 + x;
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * kt + 4 * g4 + r;
                 float w = 0.f;
                 if (i <= t && t < nval) {
                     const float si = sm.s[i];
-                    w = acc[x] * (sm.a_loc[t] * expf(si - sm.mrow[t]) + sm.brow[t] * si + sm.grow[t]);
+                    w = acc[r] * (at * expf(si - mt) + bt * si + gt);
                 }
                 sm.W[t][i] = w;
             }

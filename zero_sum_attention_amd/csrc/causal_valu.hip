@@ -1,4 +1,5 @@
-// Causal ZeroS forward, float32 VALU path (all d, both storage types).
+// Causal ZeroS forward, float32 path (all d, both storage types): float32 arithmetic throughout,
+// the contractions on the float32 matrix cores (v_mfma_f32_16x16x4f32), the rest on the vector ALU.
 //
 // Method: Paper-Notes page "ZeroS: Zero-Sum Linear Attention for Efficient Transformers",
 // 关键设计 (zero-sum weights, radial-angular decoupling, deviation logits, linear-time prefix
@@ -10,6 +11,7 @@
 //   o_t = sum_{t0<i<=t} W_{t,i} v_i + q^_t (a_t e^{m0-m_t} F + beta_t G + gamma_t H)   (states at t0)
 // with W_{t,i} = (q^_t.k^_i)(a_t e^{s_i-m_t} + beta_t s_i + gamma_t), a_t = sigmah_t / E_t, and
 // E, F rescaled by the running logit maximum m. The chunk then folds its keys into F, G, H.
+// The states live in LDS (float32); K Q^T, the output products and the fold are 16x16 tiles per wave.
 // The logits s_i and the per-segment u sums come from logits.hip (computed once per head, ahead of
 // this kernel); the scalar scans are recomputed by every tile of a head (O(C) per chunk).
 #include "device_common.hpp"

@@ -281,7 +281,9 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p, const 
                 }
             }
         }
-        __syncthreads();
+        // (no barrier: the fold reads the staged rows and writes F, G, H, which the output products
+        // finished reading before the barrier above; the products in LDS are not touched again
+        // before the barrier at the end of the chunk)
 
         // ---- fold the chunk's keys into the states on the float32 matrix cores (exact float32
         // products, float32 sums): wave w owns 16-row tiles rt = w, w + 4, ... of F, G, H.

@@ -21,7 +21,7 @@
 namespace zeros {
 namespace {
 
-constexpr int kC = 32;         // tokens per chunk
+constexpr int kC = 32;         // tokens per chunk (64 measured no faster)
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kTile = 16;      // value columns per workgroup
 constexpr int kCPT = kTile / 8;  // value columns per thread in the staging and output passes
@@ -87,20 +87,26 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p, const 
         (&sm.Hs[0][0])[x] = 0.f;
     }
 
-    // the rows of the next chunk are read while the current one is processed
+    // the rows of the next chunk are read while the current one is processed; a thread takes rows
+    // lr + RSTEP rs (rs < RS) of the chunk
+    constexpr int RSTEP = kThreads / kTPR, RS = kC / RSTEP;
+    static_assert(kC % RSTEP == 0 && kThreads / 8 == RSTEP, "row split");
     const int vr = tid / 8, vm = (tid % 8) * kCPT;
-    float nq[EPT], nk[EPT], nv[kCPT], ng1 = 0.f, ngh = 0.f, ns = 0.f;
+    float nq[RS][EPT], nk[RS][EPT], nv[RS][kCPT], ng1 = 0.f, ngh = 0.f, ns = 0.f;
     auto prefetch = [&](const int t0) __attribute__((always_inline)) {
-        const int tok = min(t0 + lr, N - 1);               // in bounds; rows past N are zeroed below
 #pragma unroll
-        for (int c = 0; c < EPT; ++c) {
-            const size_t idx = static_cast<size_t>(tok) * D + c0 + c;
-            nq[c] = ld(q, idx);
-            nk[c] = ld(k, idx);
+        for (int rs = 0; rs < RS; ++rs) {
+            const int tok = min(t0 + lr + RSTEP * rs, N - 1);   // in bounds; rows past N are zeroed below
+#pragma unroll
+            for (int c = 0; c < EPT; ++c) {
+                const size_t idx = static_cast<size_t>(tok) * D + c0 + c;
+                nq[rs][c] = ld(q, idx);
+                nk[rs][c] = ld(k, idx);
+            }
+            const size_t vidx = static_cast<size_t>(min(t0 + vr + RSTEP * rs, N - 1)) * D + tile * kTile + vm;
+#pragma unroll
+            for (int c = 0; c < kCPT; ++c) nv[rs][c] = ld(v, vidx + c);
         }
-        const size_t vidx = static_cast<size_t>(min(t0 + vr, N - 1)) * D + tile * kTile + vm;
-#pragma unroll
-        for (int c = 0; c < kCPT; ++c) nv[c] = ld(v, vidx + c);
         if (tid < kC) {
             ng1 = ld(g1, min(t0 + tid, N - 1));
             ngh = ld(gh, min(t0 + tid, N - 1));
@@ -113,15 +119,17 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p, const 
         const int nval = min(kC, N - t0);
 
         // ---- normalise, rotate and stage the rows read ahead; read the next chunk's rows
-        {
-            const int tok = t0 + lr;
-            const bool valid = lr < nval;
+#pragma unroll
+        for (int rs = 0; rs < RS; ++rs) {
+            const int lrr = lr + RSTEP * rs;
+            const int tok = t0 + lrr;
+            const bool valid = lrr < nval;
             float xq[EPT], xk[EPT];
             float ssq = 0.f, ssk = 0.f;
 #pragma unroll
             for (int c = 0; c < EPT; ++c) {
-                xq[c] = valid ? nq[c] : 0.f;
-                xk[c] = valid ? nk[c] : 0.f;
+                xq[c] = valid ? nq[rs][c] : 0.f;
+                xk[c] = valid ? nk[rs][c] : 0.f;
                 ssq += xq[c] * xq[c];
                 ssk += xk[c] * xk[c];
             }
@@ -149,14 +157,16 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p, const 
             }
 #pragma unroll
             for (int c = 0; c < EPT; ++c) {
-                sm.qh[lr][c0 + c] = xq[c];
-                sm.kh[lr][c0 + c] = xk[c];
+                sm.qh[lrr][c0 + c] = xq[c];
+                sm.kh[lrr][c0 + c] = xk[c];
             }
         }
-        {
-            const bool valid = vr < nval;
 #pragma unroll
-            for (int c = 0; c < kCPT; ++c) sm.vt[vr][vm + c] = valid ? nv[c] : 0.f;
+        for (int rs = 0; rs < RS; ++rs) {
+            const int vrr = vr + RSTEP * rs;
+            const bool valid = vrr < nval;
+#pragma unroll
+            for (int c = 0; c < kCPT; ++c) sm.vt[vrr][vm + c] = valid ? nv[rs][c] : 0.f;
         }
         if (tid < kC) {
             const bool valid = tid < nval;
@@ -210,31 +220,34 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p, const 
         const float m_new = sm.carry[0];
         if (tid < kC) sm.estate[tid] = (tid < nval) ? expf(sm.s[tid] - m_new) : 0.f;
 
-        // ---- intra-chunk weights W_{t,i} (i <= t): A^T = K Q^T on the float32 matrix cores, wave w
-        // taking key tile kt = w >> 1 and query tile qt = w & 1 (A[key][f] = k^[key][f],
+        // ---- intra-chunk weights W_{t,i} (i <= t): A^T = K Q^T on the float32 matrix cores, the 16x16
+        // tiles (key tile kt, query tile qt) taken by the waves in turn (A[key][f] = k^[key][f],
         // B[f][query] = q^[query][f]); the accumulator lane holds keys 16 kt + 4 g4 + [0, 4) of query
         // 16 qt + l16. Tiles with every key after every query are zero.
         {
-            static_assert(kThreads / 64 == 4 && kC == 32, "intra-chunk pass shape");
+            static_assert(kThreads / 64 == 4 && kC % 16 == 0 && kC <= 64, "intra-chunk pass shape");
+            constexpr int NTT = kC / 16;                     // 16-token tiles per chunk
             const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6), l16 = lane & 15, g4 = lane >> 4;
-            const int kt = wv >> 1, qt = wv & 1;
-            const int t = 16 * qt + l16;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            if (kt <= qt) {
+            for (int ti = wv; ti < NTT * NTT; ti += 4) {     // tiles (kt, qt) in turn over the waves
+                const int kt = ti % NTT, qt = ti / NTT;
+                const int t = 16 * qt + l16;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                if (kt <= qt) {
 #pragma unroll 4
-                for (int k0 = 0; k0 < D; k0 += 4)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.kh[16 * kt + l16][k0 + g4], sm.qh[t][k0 + g4], acc, 0, 0, 0);
-            }
-            const float at = sm.a_loc[t], mt = sm.mrow[t], bt = sm.brow[t], gt = sm.grow[t];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * kt + 4 * g4 + r;
-                float w = 0.f;
-                if (i <= t && t < nval) {
-                    const float si = sm.s[i];
-                    w = acc[r] * (at * expf(si - mt) + bt * si + gt);
+                    for (int k0 = 0; k0 < D; k0 += 4)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.kh[16 * kt + l16][k0 + g4], sm.qh[t][k0 + g4], acc, 0, 0, 0);
                 }
-                sm.W[t][i] = w;
+                const float at = sm.a_loc[t], mt = sm.mrow[t], bt = sm.brow[t], gt = sm.grow[t];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 16 * kt + 4 * g4 + r;
+                    float w = 0.f;
+                    if (i <= t && t < nval) {
+                        const float si = sm.s[i];
+                        w = acc[r] * (at * expf(si - mt) + bt * si + gt);
+                    }
+                    sm.W[t][i] = w;
+                }
             }
         }
         __syncthreads();
@@ -269,8 +282,9 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p, const 
             }
         }
         __syncthreads();
-        {
-            const int t = tid / 8, m0 = (tid % 8) * kCPT;
+#pragma unroll
+        for (int rs = 0; rs < RS; ++rs) {
+            const int t = tid / 8 + RSTEP * rs, m0 = (tid % 8) * kCPT;
             if (t < nval) {
                 const size_t idx = static_cast<size_t>(t0 + t) * D + tile * kTile + m0;
 #pragma unroll

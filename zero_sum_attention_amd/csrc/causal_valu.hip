@@ -178,25 +178,37 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p, const 
         __syncthreads();
 
         // ---- scans of (max, sum e^{s-max}, sum s) over the chunk, joined with the carry
+        // (one wave, lane r = token t0 + r + 1). Sums of s and the running maximum are DPP prefix
+        // scans; the sums of e^{s} take a causal fixed reference (the carried maximum, or the chunk's
+        // first logit at the start of the sequence), one exponential per token. A lane whose running
+        // maximum exceeds the reference by more than 60 takes the exact (max, sum) scan instead,
+        // which is only formed when some lane needs it. Every lane's result depends on its own
+        // prefix only, so outputs never depend on later tokens, not even in rounding.
         if (tid < 64) {
             const int r = tid;
             const bool valid = r < nval;
             const float sr = valid ? sm.s[r] : 0.f;
-            float m = valid ? sr : kNegInf, e = valid ? 1.f : 0.f, ps = valid ? sr : 0.f;
+            const float ps = wave_scan_add(sr);
+            const float mloc = wave_scan_max(valid ? sr : kNegInf);
+            const float M = fmaxf(m_c, mloc);                      // m_t
+            const float ref = (m_c == kNegInf) ? lane_f(sr, 0) : m_c;
+            const bool fixed_ok = M - ref <= 60.f;
+            const float pe = wave_scan_add(valid && fixed_ok ? expf(sr - ref) : 0.f);
+            float E = (exp_diff(m_c, ref) * E_c + pe) * expf(ref - M);
+            if (__builtin_amdgcn_ballot_w64(valid && !fixed_ok) != 0) {   // the same on every lane
+                float m = valid ? sr : kNegInf, e = valid ? 1.f : 0.f;
 #pragma unroll
-            for (int off = 1; off < kC; off <<= 1) {
-                const float m2 = __shfl_up(m, off, 64);
-                const float e2 = __shfl_up(e, off, 64);
-                const float p2 = __shfl_up(ps, off, 64);
-                if (r >= off) {
-                    const float M = fmaxf(m, m2);
-                    e = e * exp_diff(m, M) + e2 * exp_diff(m2, M);
-                    ps += p2;
-                    m = M;
+                for (int off = 1; off < kC; off <<= 1) {
+                    const float m2 = __shfl_up(m, off, 64);
+                    const float e2 = __shfl_up(e, off, 64);
+                    if (r >= off) {
+                        const float Mx = fmaxf(m, m2);
+                        e = e * exp_diff(m, Mx) + e2 * exp_diff(m2, Mx);
+                        m = Mx;
+                    }
                 }
+                if (!fixed_ok) E = E_c * exp_diff(m_c, M) + e * exp_diff(m, M);
             }
-            const float M = fmaxf(m_c, m);
-            const float E = E_c * exp_diff(m_c, M) + e * exp_diff(m, M);
             const float P = P_c + ps;
             if (valid) {
                 const float tt = static_cast<float>(t0 + r + 1);

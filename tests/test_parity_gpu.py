@@ -202,6 +202,22 @@ def test_causal_long_sequence_tail_precision():
     assert tail <= 6e-3
 
 
+def test_causal_one_head_very_long():
+    """One head at N = 65536: 1024 chunks cut into 256 scan segments of 4 (a 255-step combine chain,
+    loaded 8 segments at a time), and the precision of the carried states far past the lengths of
+    the other tests."""
+    wl = CONFIGS[4].with_(B=1, H=1, N=65536, seed=3600)
+    x = make_inputs(wl)
+    o = run_causal(x, "bf16", rope=True)
+    got = to_f64(o)
+    ref = R.causal_forward(**x, rope=True)
+    err = rel_l2(got, ref)
+    tail = rel_l2(got[:, :, 32768:], ref[:, :, 32768:])
+    print(f"one head N=65536 rel_l2={err:.3e} tail(t>32768)={tail:.3e}", flush=True)
+    assert err <= TOL["bf16"]
+    assert tail <= TOL["bf16"]
+
+
 def test_causal_workspace_reuse():
     wl = CONFIGS[4].with_(B=1, H=3, N=700, seed=3200)
     x = make_inputs(wl)

@@ -270,6 +270,11 @@ def main():
                      "p90_kernel_ms": float(np.percentile(kernel_ms, 90))},
         "cpu_baseline": cpu,
     }
+    traffic = out["roofline"]["traffic"]
+    if traffic:
+        # measured HBM bytes per call over the same time: how busy HBM actually is
+        out["roofline"]["traffic_GBs"] = traffic / (avg_kernel_ms * 1e-3) / 1e9
+        out["roofline"]["traffic_frac"] = out["roofline"]["traffic_GBs"] / HBM_PEAK_GBS
     if ref:
         got = np.stack([o[b, h].double().cpu().numpy() for b, h in SAMPLE_HEADS])
         want = np.stack([ref[p] for p in SAMPLE_HEADS])

@@ -39,6 +39,9 @@ Readings taken where the pages leave a step open (each is listed in the design n
     applied after normalisation to both q^ and k^.
   * Encoder mode: one global prior-smoothed mean ubar over all N tokens, and every query uses
     the full-sequence sums with t replaced by N and its own gates.
+  * Optional zero-order gate [Notes/zero-sum, design motivation; Summary/plain]: a first layer
+    may keep the uniform term with its own step gate, w_{t,i} += sigma0_t / t (t = N in encoder
+    mode); sigma0 = sigmoid(g0). Without g0 the term is absent (the default).
   * A running maximum m_t of the logits rescales e^{s}: the state stores
     Et = sum e^{s_i - m_t} and Ft = sum e^{s_i - m_t} k^_i^T v_i (this leaves o unchanged).
 
@@ -137,7 +140,7 @@ def deviation_logits_encoder(u, mu, tau):
     return -np.einsum("...nc,...c->...n", u, ubar) / np.sqrt(F64(du))
 
 
-def coefficients(t, Et, Pt, sig1, sigh):
+def coefficients(t, Et, Pt, sig1, sigh, sig0=None):
     """alpha, beta, gamma of o_t = q^_t(alpha F + beta G + gamma H).
 
     Derivation from [Notes/zero-sum] with the readings above:
@@ -145,12 +148,15 @@ def coefficients(t, Et, Pt, sig1, sigh):
               = (sigh/E_t) e^{s_i} + ((sig1 - sigh)/t) s_i + (-(sig1 - sigh) P_t/t^2 - sigh/t).
     Summing over i <= t gives alpha E_t + beta P_t + gamma t = 0 (the zero-sum property).
     ``Et`` may be the max-rescaled sum; alpha then multiplies the equally rescaled F.
+    A zero-order gate adds the constant sig0/t to every w_{t,i}, that is to gamma.
     """
     t = _f64(t)
     d1 = _f64(sig1) - _f64(sigh)
     alpha = _f64(sigh) / _f64(Et)
     beta = d1 / t
     gamma = -d1 * _f64(Pt) / (t * t) - _f64(sigh) / t
+    if sig0 is not None:
+        gamma = gamma + _f64(sig0) / t
     return alpha, beta, gamma
 
 
@@ -173,19 +179,19 @@ def empty_state(lead, d, d_u):
     }
 
 
-def decode_step(state, q, k, v, u, mu, tau, g1, gh, rope=False, rope_base=10000.0):
+def decode_step(state, q, k, v, u, mu, tau, g1, gh, rope=False, rope_base=10000.0, g0=None):
     """Advance the state by one token and return (o, new_state); ``state`` is not modified.
 
-    q, k, v [..., d]; u [..., d_u]; mu [..., d_u]; tau, g1, gh [...]. The token is at 1-based
+    q, k, v [..., d]; u [..., d_u]; mu [..., d_u]; tau, g1, gh (and g0) [...]. The token is at 1-based
     position t = state["t"] + 1 (RoPE position t - 1). States follow [Notes/scan]; the logit uses
     the running u-sum of [Notes/logits]; coefficients as in ``coefficients``.
     """
     st = {key: np.array(val, copy=True) for key, val in state.items()}
-    o = _step_inplace(st, q, k, v, u, mu, tau, g1, gh, rope, rope_base)
+    o = _step_inplace(st, q, k, v, u, mu, tau, g1, gh, rope, rope_base, g0)
     return o, st
 
 
-def _step_inplace(st, q, k, v, u, mu, tau, g1, gh, rope, rope_base):
+def _step_inplace(st, q, k, v, u, mu, tau, g1, gh, rope, rope_base, g0=None):
     t = st["t"] + 1
     tf = t.astype(F64)
     d_u = st["Su"].shape[-1]
@@ -212,7 +218,8 @@ def _step_inplace(st, q, k, v, u, mu, tau, g1, gh, rope, rope_base):
     H += kv
     st["m"] = m_new
     st["t"] = t
-    a, b, g = coefficients(tf, st["E"], st["P"], sigmoid(g1), sigmoid(gh))
+    a, b, g = coefficients(tf, st["E"], st["P"], sigmoid(g1), sigmoid(gh),
+                           None if g0 is None else sigmoid(g0))
     M = a[..., None, None] * F + b[..., None, None] * G + g[..., None, None] * H
     return np.einsum("...j,...jm->...m", qh, M)
 
@@ -228,12 +235,13 @@ def _rope_per_item(x, pos, base):
 
 
 def causal_forward(q, k, v, u, mu, tau, g1, gh, rope=False, rope_base=10000.0,
-                   return_state=False, state=None):
+                   return_state=False, state=None, g0=None):
     """Causal ZeroS forward as the sequential five-state recurrence (one step per token).
 
     q, k, v [..., N, d]; u [..., N, d_u]; mu [..., d_u] (per head, broadcast over batch);
     tau [...]; g1, gh [..., N]. Returns o [..., N, d] (float64), and the final state if asked.
-    ``state`` continues from a previous state instead of the empty one.
+    ``state`` continues from a previous state instead of the empty one. ``g0`` [..., N], if
+    given, is the zero-order gate.
     """
     q, k, v, u = _f64(q), _f64(k), _f64(v), _f64(u)
     g1, gh = _f64(g1), _f64(gh)
@@ -249,11 +257,12 @@ def causal_forward(q, k, v, u, mu, tau, g1, gh, rope=False, rope_base=10000.0,
     o = np.empty(lead + (N, v.shape[-1]), dtype=F64)
     for n in range(N):
         o[..., n, :] = _step_inplace(st, q[..., n, :], k[..., n, :], v[..., n, :], u[..., n, :],
-                                     mu_b, tau_b, g1[..., n], gh[..., n], rope, rope_base)
+                                     mu_b, tau_b, g1[..., n], gh[..., n], rope, rope_base,
+                                     None if g0 is None else _f64(g0)[..., n])
     return (o, st) if return_state else o
 
 
-def encoder_forward(q, k, v, u, mu, tau, g1, gh, rope=False, rope_base=10000.0):
+def encoder_forward(q, k, v, u, mu, tau, g1, gh, rope=False, rope_base=10000.0, g0=None):
     """Non-causal ZeroS forward [Notes/training]: every query uses the full-sequence sums.
 
     With t = N for every query: m = max s, E = sum e^{s-m}, P = sum s, F = sum e^{s-m} k^T v,
@@ -271,7 +280,8 @@ def encoder_forward(q, k, v, u, mu, tau, g1, gh, rope=False, rope_base=10000.0):
     F = np.einsum("...nj,...n,...nm->...jm", kh, e, v)
     G = np.einsum("...nj,...n,...nm->...jm", kh, s, v)
     H = np.einsum("...nj,...nm->...jm", kh, v)
-    a, b, g = coefficients(F64(N), E[..., None], P[..., None], sigmoid(g1), sigmoid(gh))
+    a, b, g = coefficients(F64(N), E[..., None], P[..., None], sigmoid(g1), sigmoid(gh),
+                           None if g0 is None else sigmoid(g0))
     return (a[..., None] * (qh @ F) + b[..., None] * (qh @ G) + g[..., None] * (qh @ H))
 
 
@@ -279,11 +289,12 @@ def encoder_forward(q, k, v, u, mu, tau, g1, gh, rope=False, rope_base=10000.0):
 # Explicit O(N^2) weights: the plain definition, used to pin the recurrence on small inputs.
 # --------------------------------------------------------------------------------------------
 
-def explicit_weights_causal(s, g1, gh):
+def explicit_weights_causal(s, g1, gh, g0=None):
     """W[..., t, i] = w_{t,i} for i <= t, 0 above the diagonal [Notes/zero-sum].
 
     Row t (1-based) takes a softmax over s_1..s_t, its mean, delta = s_i - mean,
-    eps = softmax - 1/t - delta/t, w = sigma1_t delta/t + sigmah_t eps.
+    eps = softmax - 1/t - delta/t, w = sigma1_t delta/t + sigmah_t eps (+ sigma0_t / t with a
+    zero-order gate).
     """
     s = _f64(s)
     N = s.shape[-1]
@@ -297,10 +308,12 @@ def explicit_weights_causal(s, g1, gh):
         delta = row - np.mean(row, axis=-1, keepdims=True)
         eps = sm - 1.0 / t - delta / t
         W[..., ti, :t] = s1[..., ti, None] * delta / t + sh[..., ti, None] * eps
+        if g0 is not None:
+            W[..., ti, :t] += sigmoid(_f64(g0)[..., ti, None]) / t
     return W
 
 
-def explicit_weights_encoder(s, g1, gh):
+def explicit_weights_encoder(s, g1, gh, g0=None):
     """Encoder weights: the same construction with the softmax and mean over all N tokens."""
     s = _f64(s)
     N = s.shape[-1]
@@ -309,21 +322,24 @@ def explicit_weights_encoder(s, g1, gh):
     delta = s - np.mean(s, axis=-1, keepdims=True)
     eps = sm - 1.0 / N - delta / N
     s1, sh = sigmoid(g1)[..., :, None], sigmoid(gh)[..., :, None]
-    return s1 * delta[..., None, :] / N + sh * eps[..., None, :]
+    W = s1 * delta[..., None, :] / N + sh * eps[..., None, :]
+    if g0 is not None:
+        W = W + sigmoid(_f64(g0))[..., :, None] / N
+    return W
 
 
-def causal_brute_force(q, k, v, u, mu, tau, g1, gh, rope=False, rope_base=10000.0):
+def causal_brute_force(q, k, v, u, mu, tau, g1, gh, rope=False, rope_base=10000.0, g0=None):
     """o_t = sum_{i<=t} w_{t,i} (q^_t . k^_i) v_i with the explicit weights [Notes/radial]."""
     qh, kh = angular_vectors(q, k, rope, rope_base)
     s = deviation_logits_causal(u, mu, tau)
-    W = explicit_weights_causal(s, g1, gh)
+    W = explicit_weights_causal(s, g1, gh, g0)
     cos = qh @ np.swapaxes(kh, -1, -2)
     return (W * cos) @ _f64(v)
 
 
-def encoder_brute_force(q, k, v, u, mu, tau, g1, gh, rope=False, rope_base=10000.0):
+def encoder_brute_force(q, k, v, u, mu, tau, g1, gh, rope=False, rope_base=10000.0, g0=None):
     qh, kh = angular_vectors(q, k, rope, rope_base)
     s = deviation_logits_encoder(u, mu, tau)
-    W = explicit_weights_encoder(s, g1, gh)
+    W = explicit_weights_encoder(s, g1, gh, g0)
     cos = qh @ np.swapaxes(kh, -1, -2)
     return (W * cos) @ _f64(v)

@@ -306,3 +306,68 @@ def test_decode_continues_forward(rope):
                                 tok["g1"], tok["gh"], rope=rope)
     assert rel(o_step, o_full[..., 32, :]) < TOL
     assert np.all(st2["t"] == 33) and np.all(st["t"] == 32)
+
+
+# ---------------------------------------------------------------- optional zero-order gate
+
+def _gate0(x, seed):
+    return np.random.default_rng(seed).normal(0.0, 1.5, size=x["g1"].shape)
+
+
+def test_zero_order_gate_weight_rows_sum_to_sigma0():
+    """With the zero-order term kept, row t of the weights sums to sigma0_t (1/t over t keys)."""
+    x = small_inputs(2, 2, 30, 8, 8, seed=41)
+    g0 = _gate0(x, 1)
+    s = R.deviation_logits_causal(x["u"], x["mu"], x["tau"])
+    W = R.explicit_weights_causal(s, x["g1"], x["gh"], g0)
+    sig0 = 1.0 / (1.0 + np.exp(-g0))
+    assert np.max(np.abs(W.sum(-1) - sig0)) < TOL
+    assert np.all(np.triu(np.ones((30, 30)), 1)[None, None] * W == 0)
+    We = R.explicit_weights_encoder(s, x["g1"], x["gh"], g0)
+    assert np.max(np.abs(We.sum(-1) - sig0)) < TOL
+
+
+def test_zero_order_gate_alone_is_causal_mean():
+    """sigma1 = sigmah = 0, sigma0 = 1, q and k along one direction (cos = 1): o_t is the running
+    mean of v_1..v_t, built here with a cumulative sum."""
+    x = small_inputs(1, 2, 29, 8, 8, seed=42)
+    x["k"] = np.broadcast_to(x["q"][:, :, :1, :], x["q"].shape).copy()
+    x["q"] = 3.0 * x["k"]
+    x["g1"] = np.full_like(x["g1"], -1000.0)
+    x["gh"] = np.full_like(x["gh"], -1000.0)
+    g0 = np.full(x["g1"].shape, 1000.0)
+    v = x["v"].astype(float)
+    ref = np.cumsum(v, axis=-2) / np.arange(1, 30)[:, None]
+    assert rel(R.causal_forward(**x, g0=g0), ref) < TOL
+    enc = R.encoder_forward(**x, g0=g0)
+    assert rel(enc, np.broadcast_to(v.mean(axis=-2, keepdims=True), v.shape)) < TOL
+
+
+@pytest.mark.parametrize("rope", [False, True])
+def test_zero_order_gate_recurrence_matches_explicit_weights(rope):
+    x = small_inputs(2, 3, 37, 16, 16, seed=43)
+    g0 = _gate0(x, 2)
+    o = R.causal_forward(**x, rope=rope, g0=g0)
+    assert rel(o, R.causal_brute_force(**x, rope=rope, g0=g0)) < TOL
+    assert rel(R.encoder_forward(**x, rope=rope, g0=g0), R.encoder_brute_force(**x, rope=rope, g0=g0)) < TOL
+    # the term is additive: the difference to the gate-free output is sigma0_t/t sum_{i<=t} cos v
+    cos = _cos(x, rope)
+    N = cos.shape[-1]
+    mask = np.tril(np.ones((N, N)))
+    sig0 = 1.0 / (1.0 + np.exp(-g0))
+    extra = ((cos * mask) @ x["v"].astype(float)) * (sig0 / np.arange(1, N + 1))[..., None]
+    assert rel(o - R.causal_forward(**x, rope=rope), extra) < 1e-10
+
+
+def test_zero_order_gate_decode_continues_forward():
+    x = small_inputs(2, 2, 33, 16, 16, seed=44)
+    g0 = _gate0(x, 3)
+    o_full = R.causal_forward(**x, g0=g0)
+    head = {key: (val[..., :32, :] if val.ndim == 4 else val[..., :32] if val.ndim == 3 else val)
+            for key, val in x.items()}
+    _, st = R.causal_forward(**head, return_state=True, g0=g0[..., :32])
+    tok = {key: (val[..., 32, :] if val.ndim == 4 else val[..., 32] if val.ndim == 3 else val)
+           for key, val in x.items()}
+    o_step, _ = R.decode_step(st, tok["q"], tok["k"], tok["v"], tok["u"], x["mu"], x["tau"],
+                              tok["g1"], tok["gh"], g0=g0[..., 32])
+    assert rel(o_step, o_full[..., 32, :]) < TOL

@@ -18,14 +18,21 @@
  * beta_t = (sigma1_t - sigmah_t)/t, gamma_t = -(sigma1_t - sigmah_t) P_t/t^2 - sigmah_t/t, and
  * sigma = logistic sigmoid of the gate pre-activations g1, gh.
  *
+ * Optional zero-order gate (Paper-Notes 关键设计, the design motivation of the zero-order removal:
+ * a first layer may keep the uniform term; ai.info "Methodology in Plain English": a gate
+ * sigma0_t decides how much of it to keep): when g0 is not NULL every weight of row t gains
+ * sigma0_t / t, i.e. gamma_t += sigmoid(g0_t) / t (t = N in the encoder). The weights then sum
+ * to sigma0_t instead of zero. g0 = NULL leaves the term out (the pages' default).
+ *
  * Conventions shared by every entry point
  *   Memory:    every pointer is DEVICE memory owned by the caller; the library allocates
  *              nothing and keeps no state between calls (an error message is kept per thread).
- *              Token tensors (q, k, v, u, g1, gh, o) may be NULL when N = 0; mu and tau never.
+ *              Token tensors (q, k, v, u, g1, gh, o) may be NULL when N = 0; mu and tau never;
+ *              g0 may always be NULL.
  *   Layout:    contiguous row-major, feature dimension innermost:
- *              q, k, v, o [B, H, N, d]; u [B, H, N, d_u]; g1, gh [B, H, N];
+ *              q, k, v, o [B, H, N, d]; u [B, H, N, d_u]; g1, gh, g0 [B, H, N];
  *              mu [H, d_u] float32; tau [H] float32 (per head, shared across the batch).
- *   Types:     q, k, v, u, g1, gh and o share `dtype` (float32 or bfloat16); arithmetic is
+ *   Types:     q, k, v, u, g1, gh, g0 and o share `dtype` (float32 or bfloat16); arithmetic is
  *              float32 (states, sums and accumulation); o is written in `dtype`.
  *   Streams:   work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the call
  *              returns without synchronising.
@@ -49,7 +56,7 @@
 extern "C" {
 #endif
 
-#define ZEROS_ABI_VERSION 1
+#define ZEROS_ABI_VERSION 2
 
 typedef enum {
     ZEROS_OK = 0,
@@ -103,7 +110,7 @@ typedef struct {
 zeros_status zeros_fwd_causal(const zeros_shape *shape,
                               const void *q, const void *k, const void *v, const void *u,
                               const float *mu, const float *tau,
-                              const void *g1, const void *gh,
+                              const void *g1, const void *gh, const void *g0,
                               void *o, const zeros_state *state_out,
                               void *workspace, size_t workspace_bytes, void *stream);
 
@@ -118,19 +125,19 @@ size_t zeros_fwd_causal_workspace_bytes(const zeros_shape *shape);
 zeros_status zeros_fwd_encoder(const zeros_shape *shape,
                                const void *q, const void *k, const void *v, const void *u,
                                const float *mu, const float *tau,
-                               const void *g1, const void *gh,
+                               const void *g1, const void *gh, const void *g0,
                                void *o, void *stream);
 
 /*
  * One recurrent step (the O(d^2)-per-token update of 关键设计 / 线性时间前缀扫描):
  * shape->B = S sequences, shape->N must be 1. q, k, v, o [S, H, d]; u [S, H, d_u];
- * g1, gh [S, H]. Each (sequence, head) consumes one token at position state.t + 1 and its state
+ * g1, gh, g0 [S, H]. Each (sequence, head) consumes one token at position state.t + 1 and its state
  * is updated in place.
  */
 zeros_status zeros_decode_step(const zeros_shape *shape,
                                const void *q, const void *k, const void *v, const void *u,
                                const float *mu, const float *tau,
-                               const void *g1, const void *gh,
+                               const void *g1, const void *gh, const void *g0,
                                void *o, const zeros_state *state, void *stream);
 
 /* Bytes of one state for S x H heads when packed by zeros_state_from_buffer (256-B aligned

@@ -80,12 +80,13 @@ def round_to_dtype(x: np.ndarray, dtype: str) -> np.ndarray:
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
-def make_inputs(wl: Workload, *, u_scale: float = 1.0) -> dict:
+def make_inputs(wl: Workload, *, u_scale: float = 1.0, gate0: bool = False) -> dict:
     """Draw one batch of inputs for ``wl``.
 
     Shapes: q, k, v [B, H, N, d]; u [B, H, N, d_u]; mu [H, d_u]; tau [H]; g1, gh [B, H, N].
     For decode workloads N is 1 (one new token per sequence). ``u_scale`` multiplies u before
-    rounding (logit stress cases).
+    rounding (logit stress cases). ``gate0`` adds zero-order gate pre-activations g0 ~ N(0, 1)
+    [B, H, N], drawn after everything else so the other inputs do not change.
     """
     rng = np.random.default_rng(wl.seed)
     B, H, N, d, du = wl.B, wl.H, wl.N, wl.d, wl.d_u
@@ -103,11 +104,14 @@ def make_inputs(wl: Workload, *, u_scale: float = 1.0) -> dict:
     if u_scale != 1.0:
         u = (u * np.float32(u_scale)).astype(np.float32)
     dt = wl.dtype
-    return {
+    out = {
         "q": round_to_dtype(q, dt), "k": round_to_dtype(k, dt), "v": round_to_dtype(v, dt),
         "u": round_to_dtype(u, dt), "mu": mu, "tau": tau,
         "g1": round_to_dtype(g1, dt), "gh": round_to_dtype(gh, dt),
     }
+    if gate0:
+        out["g0"] = round_to_dtype(rng.standard_normal((B, H, N), dtype=np.float32), dt)
+    return out
 
 
 def decode_prefill_batch(wl: Workload, s0: int, s1: int, device="cuda"):

@@ -59,7 +59,7 @@ def test_struct_layout_matches_header():
 
 
 # placeholder addresses, far apart so they never overlap unless a test wants them to
-P = {name: 0x10000000 * (i + 1) for i, name in enumerate(("q", "k", "v", "u", "mu", "tau", "g1", "gh", "o"))}
+P = {name: 0x10000000 * (i + 1) for i, name in enumerate(("q", "k", "v", "u", "mu", "tau", "g1", "gh", "o", "g0"))}
 
 
 def shape(B=1, H=2, N=8, d=16, d_u=16, dtype=0, rope=0, base=10000.0):
@@ -69,19 +69,20 @@ def shape(B=1, H=2, N=8, d=16, d_u=16, dtype=0, rope=0, base=10000.0):
 def call_causal(lib, shp, ptrs=None, state=None):
     p = dict(P, **(ptrs or {}))
     return lib.zeros_fwd_causal(ctypes.byref(shp) if shp is not None else None, p["q"], p["k"], p["v"],
-                                p["u"], p["mu"], p["tau"], p["g1"], p["gh"], p["o"], state, None, 0, None)
+                                p["u"], p["mu"], p["tau"], p["g1"], p["gh"], p["g0"], p["o"], state, None, 0,
+                                None)
 
 
 def call_encoder(lib, shp, ptrs=None):
     p = dict(P, **(ptrs or {}))
     return lib.zeros_fwd_encoder(ctypes.byref(shp), p["q"], p["k"], p["v"], p["u"], p["mu"], p["tau"],
-                                 p["g1"], p["gh"], p["o"], None)
+                                 p["g1"], p["gh"], p["g0"], p["o"], None)
 
 
 def call_decode(lib, shp, state, ptrs=None):
     p = dict(P, **(ptrs or {}))
     return lib.zeros_decode_step(ctypes.byref(shp), p["q"], p["k"], p["v"], p["u"], p["mu"], p["tau"],
-                                 p["g1"], p["gh"], p["o"], state, None)
+                                 p["g1"], p["gh"], p["g0"], p["o"], state, None)
 
 
 def test_null_shape(lib):
@@ -120,6 +121,8 @@ def test_output_alias(lib):
     # o starts inside q's byte range: [B,H,N,d] = 1*2*8*16 f32 = 1024 bytes
     assert call_causal(lib, shape(), {"o": P["q"] + 512}) == L.ZEROS_ERR_ALIAS
     assert call_encoder(lib, shape(), {"o": P["gh"]}) == L.ZEROS_ERR_ALIAS
+    assert call_decode(lib, shape(N=1), None, {"o": P["g0"]}) != L.ZEROS_OK
+    assert call_encoder(lib, shape(), {"o": P["g0"]}) == L.ZEROS_ERR_ALIAS    # the optional gate too
 
 
 def test_misaligned_tensors_rejected(lib):
@@ -149,10 +152,10 @@ def test_workspace_size_and_validation(lib):
     need = lib.zeros_fwd_causal_workspace_bytes(ctypes.byref(small))
     p = dict(P)
     r = lib.zeros_fwd_causal(ctypes.byref(small), p["q"], p["k"], p["v"], p["u"], p["mu"], p["tau"], p["g1"],
-                             p["gh"], p["o"], None, 0x7000000, need - 1, None)
+                             p["gh"], None, p["o"], None, 0x7000000, need - 1, None)
     assert r == L.ZEROS_ERR_SHAPE
     r = lib.zeros_fwd_causal(ctypes.byref(small), p["q"], p["k"], p["v"], p["u"], p["mu"], p["tau"], p["g1"],
-                             p["gh"], p["o"], None, 0x7000010, need, None)
+                             p["gh"], None, p["o"], None, 0x7000010, need, None)
     assert r == L.ZEROS_ERR_SHAPE                                                       # misaligned
 
 

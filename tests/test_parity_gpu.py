@@ -46,7 +46,7 @@ def run_encoder(x, dtype, rope=False):
 
 def test_library_is_native():
     lib = Z.load_library()
-    assert lib.zeros_abi_version() == 1
+    assert lib.zeros_abi_version() == 2
     assert torch.cuda.is_available()
 
 

@@ -51,7 +51,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         raise ImportError(f"{path} is not built; run `python -m zero_sum_attention_amd.build`")
     lib = ctypes.CDLL(path)
     vp, i32, f32p = ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p
-    fwd = [ctypes.POINTER(zeros_shape), vp, vp, vp, vp, f32p, f32p, vp, vp, vp]
+    # shape, q, k, v, u, mu, tau, g1, gh, g0, o
+    fwd = [ctypes.POINTER(zeros_shape), vp, vp, vp, vp, f32p, f32p, vp, vp, vp, vp]
     lib.zeros_fwd_causal.argtypes = fwd + [ctypes.POINTER(zeros_state), vp, ctypes.c_size_t, vp]
     lib.zeros_fwd_causal.restype = i32
     lib.zeros_fwd_causal_workspace_bytes.argtypes = [ctypes.POINTER(zeros_shape)]
@@ -94,15 +95,15 @@ def _need(cond: bool, msg: str) -> None:
         raise ValueError(msg)
 
 
-def _check_tensors(q, k, v, u, mu, tau, g1, gh, n_tok_dims: int):
+def _check_tensors(q, k, v, u, mu, tau, g1, gh, n_tok_dims: int, g0=None):
     """Validate [B, H, N, d] (n_tok_dims = 1) or [S, H, d] (n_tok_dims = 0) tensors."""
     _need(q.dtype in _DT, f"q dtype {q.dtype} is not float32 or bfloat16")
     dev = q.device
     _need(dev.type == "cuda", "tensors must be on a GPU")
-    for name, t in (("q", q), ("k", k), ("v", v), ("u", u), ("g1", g1), ("gh", gh)):
+    gates = (("g1", g1), ("gh", gh)) + ((("g0", g0),) if g0 is not None else ())
+    for name, t in (("q", q), ("k", k), ("v", v), ("u", u)) + gates:
         _need(t.dtype == q.dtype, f"{name} dtype {t.dtype} differs from q ({q.dtype})")
-    for name, t in (("q", q), ("k", k), ("v", v), ("u", u), ("mu", mu), ("tau", tau),
-                    ("g1", g1), ("gh", gh)):
+    for name, t in (("q", q), ("k", k), ("v", v), ("u", u), ("mu", mu), ("tau", tau)) + gates:
         _need(t.device == dev, f"{name} is on {t.device}, q on {dev}")
         _need(t.is_contiguous(), f"{name} must be contiguous")
     _need(mu.dtype == torch.float32 and tau.dtype == torch.float32, "mu and tau must be float32")
@@ -110,7 +111,7 @@ def _check_tensors(q, k, v, u, mu, tau, g1, gh, n_tok_dims: int):
     _need(q.dim() == nd, f"q must have {nd} dims")
     _need(k.shape == q.shape and v.shape == q.shape, "q, k, v shapes differ")
     _need(u.shape[:-1] == q.shape[:-1], "u leading dims differ from q")
-    _need(g1.shape == q.shape[:-1] and gh.shape == q.shape[:-1], "gate shapes must be q.shape[:-1]")
+    _need(all(t.shape == q.shape[:-1] for _, t in gates), "gate shapes must be q.shape[:-1]")
     H, du = q.shape[1], u.shape[-1]
     _need(mu.shape == (H, du), f"mu must be [H, d_u] = [{H}, {du}]")
     _need(tau.shape == (H,), f"tau must be [H] = [{H}]")
@@ -171,14 +172,16 @@ class DecodeState:
         return self
 
 
-def zeros_fwd_causal(q, k, v, u, mu, tau, g1, gh, *, rope: bool = False, rope_base: float = 10000.0,
-                     out: torch.Tensor | None = None, state_out: DecodeState | None = None,
-                     workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+def zeros_fwd_causal(q, k, v, u, mu, tau, g1, gh, *, g0: torch.Tensor | None = None, rope: bool = False,
+                     rope_base: float = 10000.0, out: torch.Tensor | None = None,
+                     state_out: DecodeState | None = None, workspace: torch.Tensor | None = None,
+                     stream=None) -> torch.Tensor:
     """Causal forward over q, k, v [B, H, N, d], u [B, H, N, d_u], g1, gh [B, H, N].
 
-    ``workspace`` (optional uint8 tensor) is reused scratch; without it one is allocated per call
-    when the path needs it (see zeros_fwd_causal_workspace_bytes)."""
-    _check_tensors(q, k, v, u, mu, tau, g1, gh, 1)
+    ``g0`` [B, H, N] (optional) enables the zero-order gate. ``workspace`` (optional uint8 tensor)
+    is reused scratch; without it one is allocated per call when the path needs it (see
+    zeros_fwd_causal_workspace_bytes)."""
+    _check_tensors(q, k, v, u, mu, tau, g1, gh, 1, g0)
     o = torch.empty_like(v) if out is None else out
     _need(o.shape == v.shape and o.dtype == v.dtype and o.is_contiguous() and o.device == q.device,
           "out must match v")
@@ -195,7 +198,7 @@ def zeros_fwd_causal(q, k, v, u, mu, tau, g1, gh, *, rope: bool = False, rope_ba
         _need(workspace.dtype == torch.uint8 and workspace.device == q.device and workspace.is_contiguous(),
               "workspace must be a contiguous uint8 tensor on q's device")
     _check(lib.zeros_fwd_causal(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(u), _ptr(mu),
-                                _ptr(tau), _ptr(g1), _ptr(gh), _ptr(o), st,
+                                _ptr(tau), _ptr(g1), _ptr(gh), _ptr(g0), _ptr(o), st,
                                 _ptr(workspace), 0 if workspace is None else workspace.numel(),
                                 _stream(q.device, stream)))
     return o
@@ -208,25 +211,27 @@ def zeros_fwd_causal_workspace_bytes(B: int, H: int, N: int, d: int, d_u: int, d
     return int(lib.zeros_fwd_causal_workspace_bytes(ctypes.byref(shp)))
 
 
-def zeros_fwd_encoder(q, k, v, u, mu, tau, g1, gh, *, rope: bool = False, rope_base: float = 10000.0,
-                      out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """Non-causal forward; same tensor layout as zeros_fwd_causal."""
-    _check_tensors(q, k, v, u, mu, tau, g1, gh, 1)
+def zeros_fwd_encoder(q, k, v, u, mu, tau, g1, gh, *, g0: torch.Tensor | None = None, rope: bool = False,
+                      rope_base: float = 10000.0, out: torch.Tensor | None = None,
+                      stream=None) -> torch.Tensor:
+    """Non-causal forward; same tensor layout (and optional ``g0``) as zeros_fwd_causal."""
+    _check_tensors(q, k, v, u, mu, tau, g1, gh, 1, g0)
     o = torch.empty_like(v) if out is None else out
     _need(o.shape == v.shape and o.dtype == v.dtype and o.is_contiguous() and o.device == q.device,
           "out must match v")
     lib = load_library()
     shp = _shape(q, u, q.shape[2], rope, rope_base)
     _check(lib.zeros_fwd_encoder(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(u), _ptr(mu),
-                                 _ptr(tau), _ptr(g1), _ptr(gh), _ptr(o), _stream(q.device, stream)))
+                                 _ptr(tau), _ptr(g1), _ptr(gh), _ptr(g0), _ptr(o),
+                                 _stream(q.device, stream)))
     return o
 
 
-def zeros_decode_step(q, k, v, u, mu, tau, g1, gh, state: DecodeState, *, rope: bool = False,
-                      rope_base: float = 10000.0, out: torch.Tensor | None = None,
+def zeros_decode_step(q, k, v, u, mu, tau, g1, gh, state: DecodeState, *, g0: torch.Tensor | None = None,
+                      rope: bool = False, rope_base: float = 10000.0, out: torch.Tensor | None = None,
                       stream=None) -> torch.Tensor:
-    """One token per (sequence, head): q, k, v [S, H, d], u [S, H, d_u], g1, gh [S, H]."""
-    _check_tensors(q, k, v, u, mu, tau, g1, gh, 0)
+    """One token per (sequence, head): q, k, v [S, H, d], u [S, H, d_u], g1, gh (and g0) [S, H]."""
+    _check_tensors(q, k, v, u, mu, tau, g1, gh, 0, g0)
     _need((state.S, state.H, state.d, state.d_u) == (q.shape[0], q.shape[1], q.shape[-1], u.shape[-1]),
           "state sizes differ from the token tensors")
     o = torch.empty_like(v) if out is None else out
@@ -235,6 +240,6 @@ def zeros_decode_step(q, k, v, u, mu, tau, g1, gh, state: DecodeState, *, rope: 
     lib = load_library()
     shp = _shape(q, u, 1, rope, rope_base)
     _check(lib.zeros_decode_step(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(u), _ptr(mu),
-                                 _ptr(tau), _ptr(g1), _ptr(gh), _ptr(o), ctypes.byref(state.c),
+                                 _ptr(tau), _ptr(g1), _ptr(gh), _ptr(g0), _ptr(o), ctypes.byref(state.c),
                                  _stream(q.device, stream)))
     return o

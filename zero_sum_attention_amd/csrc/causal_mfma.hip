@@ -3,7 +3,8 @@
 // Method: Paper-Notes page "ZeroS: Zero-Sum Linear Attention for Efficient Transformers", 关键设计
 // (zero-sum weights w_{t,i} = alpha_t e^{s_i} + beta_t s_i + gamma_t after expanding the gated
 // first-order and residual terms; angular factor q^_t . k^_i with RoPE as a relative rotation;
-// the prefix states of the linear-time scan). The logits s_i and per-chunk logit aggregates come
+// the prefix states of the linear-time scan). The optional zero-order gate of the same section
+// (a first layer may keep the uniform term) adds sigma0_t/t to gamma_t. The logits s_i and per-chunk logit aggregates come
 // from logits.hip. The sequence is cut into chunks of kC = 64 tokens.
 //
 // causal_prep_kernel, one workgroup per (batch, head, chunk), all chunks in parallel: everything
@@ -62,12 +63,12 @@ __device__ __forceinline__ void lse_combine(float &m, float &e, float m2, float 
 }
 
 // Scalar scan of one chunk (one wave; lane r = token t0 + r + 1) and its coefficients.
-// Inputs: the chunk's logits and gate pre-activations in lanes; the carry (m0, E0, P0) at t0,
-// updated to the chunk end on return. The sums of e^{s} use the chunk-end maximum M1 as a fixed
+// Inputs: the chunk's logits and gate pre-activations in lanes (s0 = sigma0 of the optional
+// zero-order gate, 0 without it); the carry (m0, E0, P0) at t0, updated to the chunk end on return. The sums of e^{s} use the chunk-end maximum M1 as a fixed
 // reference (plain prefix sums); when the running maximum rises by more than e^60 inside the
 // chunk, an exact (max, sum) scan is used instead so that nothing under- or overflows.
 __device__ __forceinline__ void chunk_scan(Coef &cf, int lane, int t0, int nval, float sr_in, float g1v,
-                                           float ghv, float &m0, float &E0, float &P0) {
+                                           float ghv, float s0, float &m0, float &E0, float &P0) {
     const int r = lane;
     const bool valid = r < nval;
     const float t0f = static_cast<float>(t0);
@@ -111,12 +112,13 @@ __device__ __forceinline__ void chunk_scan(Coef &cf, int lane, int t0, int nval,
         cf.qa[r] = fixed_ref ? a * __expf(M1 - M) : a;
         cf.qm[r] = M;
         cf.qb[r] = d1 * itt;
-        cf.qg[r] = -d1 * (Pt * itt) * itt - sh * itt;
+        // the zero-order term adds s0/t to gamma and so to the coefficient of H
+        cf.qg[r] = -d1 * (Pt * itt) * itt + (s0 - sh) * itt;
         if (t0 > 0) {
             const float dt = tt - t0f;
             cf.qcx[r] = a * E0p;
             cf.qkap[r] = sh * __fdividef(E0p * dt - t0f * dE, Et * tt * t0f) +
-                         d1 * __fdividef(P0 * dt - t0f * pp, tt * tt * t0f);
+                         d1 * __fdividef(P0 * dt - t0f * pp, tt * tt * t0f) + s0 * itt;
         } else {
             cf.qcx[r] = 0.f;
             cf.qkap[r] = 0.f;
@@ -230,7 +232,10 @@ __global__ __launch_bounds__(kPrepThreads) void causal_prep_kernel(Problem p, Ca
         const float sv = vs ? work.s[row0 + t0 + lane] : 0.f;
         const float g1v = vs ? lo_f(static_cast<const uint16_t *>(p.g1)[row0 + t0 + lane]) : 0.f;
         const float ghv = vs ? lo_f(static_cast<const uint16_t *>(p.gh)[row0 + t0 + lane]) : 0.f;
-        chunk_scan(sm.cf, lane, t0, nval, sv, g1v, ghv, m0, E0, P0);
+        const float s0 = (vs && p.g0 != nullptr)
+                             ? __fdividef(1.f, 1.f + __expf(-lo_f(static_cast<const uint16_t *>(p.g0)[row0 + t0 + lane])))
+                             : 0.f;
+        chunk_scan(sm.cf, lane, t0, nval, sv, g1v, ghv, s0, m0, E0, P0);
     }
 
     // ---- unit q^, k^ rows, rotated by their offset inside the chunk

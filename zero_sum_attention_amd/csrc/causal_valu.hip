@@ -4,7 +4,8 @@
 // Method: Paper-Notes page "ZeroS: Zero-Sum Linear Attention for Efficient Transformers",
 // 关键设计 (zero-sum weights, radial-angular decoupling, deviation logits, linear-time prefix
 // scan). Per head the output is o_t = sum_{i<=t} (alpha_t e^{s_i} + beta_t s_i + gamma_t)
-// (q^_t . k^_i) v_i, which the prefix states turn into a recurrence.
+// (q^_t . k^_i) v_i, which the prefix states turn into a recurrence; the optional zero-order gate
+// of the same section adds sigma0_t / t to gamma_t.
 //
 // Work split: one workgroup per (batch, head, 16-column tile of v/o). The workgroup walks the
 // sequence in chunks of kC tokens. For a chunk covering (t0, t1]:
@@ -35,7 +36,7 @@ struct CausalSmem {
     float W[kC][kC + 1];   // intra-chunk weights times cosines
     float F[D][kTile], G[D][kTile], Hs[D][kTile];
     float part[4][kC][kTile];  // the output pass's four products (q^ F, q^ G, q^ H scaled; W V)
-    float s[kC], sig1[kC], sigh[kC];
+    float s[kC], sig1[kC], sigh[kC], sig0[kC];   // sig0: zero-order gate (0 when off)
     float a_in[kC];        // a_t e^{m0 - m_t}: multiplies the carried F
     float a_loc[kC];       // a_t = sigmah_t / E_t (E relative to m_t)
     float mrow[kC], brow[kC], grow[kC];
@@ -68,6 +69,7 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p, const 
     const T *v = static_cast<const T *>(p.v) + row0 * D;
     const T *g1 = static_cast<const T *>(p.g1) + row0;
     const T *gh = static_cast<const T *>(p.gh) + row0;
+    const T *g0 = p.g0 != nullptr ? static_cast<const T *>(p.g0) + row0 : nullptr;
     T *o = static_cast<T *>(p.o) + row0 * D;
 
     const float *srow = s_all + row0;
@@ -92,7 +94,7 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p, const 
     constexpr int RSTEP = kThreads / kTPR, RS = kC / RSTEP;
     static_assert(kC % RSTEP == 0 && kThreads / 8 == RSTEP, "row split");
     const int vr = tid / 8, vm = (tid % 8) * kCPT;
-    float nq[RS][EPT], nk[RS][EPT], nv[RS][kCPT], ng1 = 0.f, ngh = 0.f, ns = 0.f;
+    float nq[RS][EPT], nk[RS][EPT], nv[RS][kCPT], ng1 = 0.f, ngh = 0.f, ng0 = 0.f, ns = 0.f;
     auto prefetch = [&](const int t0) __attribute__((always_inline)) {
 #pragma unroll
         for (int rs = 0; rs < RS; ++rs) {
@@ -110,6 +112,7 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p, const 
         if (tid < kC) {
             ng1 = ld(g1, min(t0 + tid, N - 1));
             ngh = ld(gh, min(t0 + tid, N - 1));
+            if (g0 != nullptr) ng0 = ld(g0, min(t0 + tid, N - 1));
             ns = srow[min(t0 + tid, N - 1)];
         }
     };
@@ -172,6 +175,7 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p, const 
             const bool valid = tid < nval;
             sm.sig1[tid] = valid ? sigmoidf(ng1) : 0.f;
             sm.sigh[tid] = valid ? sigmoidf(ngh) : 0.f;
+            sm.sig0[tid] = (valid && g0 != nullptr) ? sigmoidf(ng0) : 0.f;
             sm.s[tid] = valid ? ns : 0.f;
         }
         if (t0 + kC < N) prefetch(t0 + kC);
@@ -219,7 +223,8 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p, const 
                 sm.a_in[r] = a * exp_diff(m_c, M);
                 sm.mrow[r] = M;
                 sm.brow[r] = d1 / tt;
-                sm.grow[r] = -d1 * (P / tt) / tt - sh / tt;
+                // the zero-order term adds sigma0_t / t to gamma
+                sm.grow[r] = -d1 * (P / tt) / tt + (sm.sig0[r] - sh) / tt;
             }
             if (r == nval - 1) {
                 sm.carry[0] = M;

@@ -115,7 +115,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Problem p) {
             coef[2] = s;
             coef[3] = sgh / E;
             coef[4] = d1 / tn;
-            coef[5] = -d1 * (P / tn) / tn - sgh / tn;
+            // the optional zero-order gate adds sigma0_t / t to gamma
+            const float s0 = p.g0 != nullptr ? sigmoidf(ld(static_cast<const T *>(p.g0), sh_idx)) : 0.f;
+            coef[5] = -d1 * (P / tn) / tn + (s0 - sgh) / tn;
             p.st.m[sh_idx] = m_new;
             p.st.E[sh_idx] = E;
             p.st.P[sh_idx] = P;

@@ -6,7 +6,9 @@
 //   alpha_t F + beta_t G + gamma_t H = sigmah_t X + ((sigma1_t - sigmah_t)/N) Y,
 //   X = sum_i (e^{s_i - m}/E - 1/N) k^_i^T v_i,   Y = sum_i (s_i - P/N) k^_i^T v_i,
 // two centred d x d states (zero-sum weights, so of the size of the output and safe to round to
-// bfloat16 as MFMA operands).
+// bfloat16 as MFMA operands). The optional zero-order gate of the same section (a first layer may
+// keep the uniform term) adds (sigma0_t/N) q^_t H with H = sum_i k^_i^T v_i, a third state
+// (the G0 instances).
 //
 // One workgroup of 4 waves per (batch, head, 16-column tile of the value dimension): d/16 workgroups
 // per head, each computing its tile's columns of X and Y and of the output.
@@ -53,8 +55,9 @@ __device__ __forceinline__ void unpack8(const uint4 &x, float (&f)[8]) {
     }
 }
 
-template <int D, bool ROPE, int NMAX>
+template <int D, bool ROPE, int NMAX, bool G0>
 __global__ __launch_bounds__(kEThreads) void encoder_mfma_kernel(Problem p) {
+    constexpr int NS = G0 ? 3 : 2;     // states: X, Y (and H)
     constexpr int FT = D / 16;         // 16-row feature tiles of a state
     constexpr int FW = FT / 4;         // feature tiles per wave
     constexpr int KS = D / 32;         // 32-feature steps
@@ -67,7 +70,8 @@ __global__ __launch_bounds__(kEThreads) void encoder_mfma_kernel(Problem p) {
     __shared__ __align__(16) uint16_t kt[D][kEC + kEPad];    // k^ of the chunk, transposed
     __shared__ __align__(16) uint16_t vxt[16][kEC + kEPad];  // this tile's columns of v w_X, transposed
     __shared__ __align__(16) uint16_t vyt[16][kEC + kEPad];  // this tile's columns of v w_Y, transposed
-    __shared__ __align__(16) uint16_t sxy[2][16][D + kEPad]; // X^T, Y^T of this tile (bf16), for phase C
+    __shared__ __align__(16) uint16_t vht[G0 ? 16 : 1][kEC + kEPad];  // this tile's columns of v (H)
+    __shared__ __align__(16) uint16_t sxy[NS][16][D + kEPad]; // X^T, Y^T (H^T) of this tile (bf16), for phase C
     __shared__ double rev[ROPE ? D / 2 : 1];                 // RoPE turns per position of each pair
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -86,6 +90,7 @@ __global__ __launch_bounds__(kEThreads) void encoder_mfma_kernel(Problem p) {
     const uint16_t *u = static_cast<const uint16_t *>(p.u) + row0 * D;
     const uint16_t *g1 = static_cast<const uint16_t *>(p.g1) + row0;
     const uint16_t *gh = static_cast<const uint16_t *>(p.gh) + row0;
+    const uint16_t *g0 = G0 ? static_cast<const uint16_t *>(p.g0) + row0 : nullptr;
     uint16_t *o = static_cast<uint16_t *>(p.o) + row0 * D;
     const float et = expf(p.tau[h]);
     const int fr = tid % LPR, rr = tid / LPR;       // feature group (8 features) and row of a pass
@@ -210,11 +215,15 @@ __global__ __launch_bounds__(kEThreads) void encoder_mfma_kernel(Problem p) {
 
     // ---- B: this tile's columns of X = K^T diag(w_X) V and Y = K^T diag(w_Y) V over chunks of kEC
     // tokens; wave w owns feature tiles [FW w, FW w + FW)
-    f32x4 X[FW], Y[FW];
+    f32x4 X[FW], Y[FW], Hc[G0 ? FW : 1];
 #pragma unroll
     for (int j = 0; j < FW; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) X[j][i] = Y[j][i] = 0.f;
+#pragma unroll
+    for (int j = 0; j < (G0 ? FW : 1); ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Hc[j][i] = 0.f;
     for (int t0 = 0; t0 < N; t0 += kEC) {
         uint4 kc[JR];
 #pragma unroll
@@ -253,7 +262,7 @@ __global__ __launch_bounds__(kEThreads) void encoder_mfma_kernel(Problem p) {
             for (int i = 0; i < 8; ++i) *reinterpret_cast<uint32_t *>(&kt[8 * fr + i][rl]) = pack2(kp[0][i], kp[1][i]);
         }
         if (vthr) {
-            float wx[2], wy[2], vv[2][4];
+            float wx[2], wy[2], wh[2], vv[2][4];
             const uint2 vcs[2] = {vc0, vc1};
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
@@ -262,6 +271,7 @@ __global__ __launch_bounds__(kEThreads) void encoder_mfma_kernel(Problem p) {
                 const float s = ok ? sl[r] : 0.f;
                 wx[e] = ok ? __expf(s - M) * invE - invN : 0.f;
                 wy[e] = ok ? s - PN : 0.f;
+                wh[e] = ok ? 1.f : 0.f;             // rows past N read row N-1: zero them for H
                 vv[e][0] = lo_f(vcs[e].x);
                 vv[e][1] = hi_f(vcs[e].x);
                 vv[e][2] = lo_f(vcs[e].y);
@@ -271,6 +281,8 @@ __global__ __launch_bounds__(kEThreads) void encoder_mfma_kernel(Problem p) {
             for (int i = 0; i < 4; ++i) {
                 *reinterpret_cast<uint32_t *>(&vxt[4 * vcq + i][vtk]) = pack2(vv[0][i] * wx[0], vv[1][i] * wx[1]);
                 *reinterpret_cast<uint32_t *>(&vyt[4 * vcq + i][vtk]) = pack2(vv[0][i] * wy[0], vv[1][i] * wy[1]);
+                if (G0)
+                    *reinterpret_cast<uint32_t *>(&vht[4 * vcq + i][vtk]) = pack2(vv[0][i] * wh[0], vv[1][i] * wh[1]);
             }
         }
         __syncthreads();
@@ -279,11 +291,13 @@ __global__ __launch_bounds__(kEThreads) void encoder_mfma_kernel(Problem p) {
             const int kk0 = 32 * ks2 + 8 * g4;
             const bf16x8 BX = *reinterpret_cast<const bf16x8 *>(&vxt[l16][kk0]);
             const bf16x8 BY = *reinterpret_cast<const bf16x8 *>(&vyt[l16][kk0]);
+            const bf16x8 BH = G0 ? *reinterpret_cast<const bf16x8 *>(&vht[l16][kk0]) : BY;
 #pragma unroll
             for (int j = 0; j < FW; ++j) {
                 const bf16x8 A = *reinterpret_cast<const bf16x8 *>(&kt[16 * (FW * w + j) + l16][kk0]);
                 X[j] = mfma(A, BX, X[j]);
                 Y[j] = mfma(A, BY, Y[j]);
+                if (G0) Hc[j] = mfma(A, BH, Hc[j]);
             }
         }
         __syncthreads();
@@ -295,20 +309,24 @@ __global__ __launch_bounds__(kEThreads) void encoder_mfma_kernel(Problem p) {
         const int f = 16 * (FW * w + j) + 4 * g4;
         *reinterpret_cast<uint2 *>(&sxy[0][l16][f]) = make_uint2(pack2(X[j][0], X[j][1]), pack2(X[j][2], X[j][3]));
         *reinterpret_cast<uint2 *>(&sxy[1][l16][f]) = make_uint2(pack2(Y[j][0], Y[j][1]), pack2(Y[j][2], Y[j][3]));
+        if (G0)
+            *reinterpret_cast<uint2 *>(&sxy[NS - 1][l16][f]) =
+                make_uint2(pack2(Hc[j][0], Hc[j][1]), pack2(Hc[j][2], Hc[j][3]));
     }
     __syncthreads();
 
     // ---- C: outputs of this tile's columns, 16 tokens per step, the waves taking steps in turn.
     // A operands X^T, Y^T (column l16, features 32 ks + 8 g4 + [0, 8)); B operand q^ of token
     // 16 tb + l16, the same features. The next step's q rows and gates are read while this one computes.
-    bf16x8 AX[KS], AY[KS];
+    bf16x8 AX[KS], AY[KS], AH[G0 ? KS : 1];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         AX[ks] = *reinterpret_cast<const bf16x8 *>(&sxy[0][l16][32 * ks + 8 * g4]);
         AY[ks] = *reinterpret_cast<const bf16x8 *>(&sxy[1][l16][32 * ks + 8 * g4]);
+        if (G0) AH[ks] = *reinterpret_cast<const bf16x8 *>(&sxy[NS - 1][l16][32 * ks + 8 * g4]);
     }
     uint4 qn[KS];
-    uint32_t g1n = 0, ghn = 0;
+    uint32_t g1n = 0, ghn = 0, g0n = 0;
     auto load_q = [&](const int tb) __attribute__((always_inline)) {
         const int t = min(16 * tb + l16, N - 1);   // in bounds; rows past N are never stored
         const size_t tr = static_cast<size_t>(t) * D;
@@ -316,6 +334,7 @@ __global__ __launch_bounds__(kEThreads) void encoder_mfma_kernel(Problem p) {
         for (int ks = 0; ks < KS; ++ks) qn[ks] = *reinterpret_cast<const uint4 *>(q + tr + 32 * ks + 8 * g4);
         g1n = g1[t];
         ghn = gh[t];
+        if (G0) g0n = g0[t];
     };
     const int ntb = (N + 15) / 16;
     if (w < ntb) load_q(w);
@@ -325,7 +344,7 @@ __global__ __launch_bounds__(kEThreads) void encoder_mfma_kernel(Problem p) {
         uint4 qv[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) qv[ks] = qn[ks];
-        const uint32_t g1v = g1n, ghv = ghn;
+        const uint32_t g1v = g1n, ghv = ghn, g0v = g0n;
         if (tb + kEThreads / 64 < ntb) load_q(tb + kEThreads / 64);
         float ss = 0.f;
 #pragma unroll
@@ -351,32 +370,39 @@ __global__ __launch_bounds__(kEThreads) void encoder_mfma_kernel(Problem p) {
         const float s1 = ok ? __fdividef(1.f, 1.f + __expf(-lo_f(g1v))) : 0.f;
         const float sh = ok ? __fdividef(1.f, 1.f + __expf(-lo_f(ghv))) : 0.f;
         const float ax = sh * iq, ay = (s1 - sh) * invN * iq;
-        f32x4 accX = {0.f, 0.f, 0.f, 0.f}, accY = accX;
+        const float ah = (G0 && ok) ? __fdividef(1.f, 1.f + __expf(-lo_f(g0v))) * invN * iq : 0.f;
+        f32x4 accX = {0.f, 0.f, 0.f, 0.f}, accY = accX, accH = accX;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const bf16x8 B = as_bf16x8(qv[ks].x, qv[ks].y, qv[ks].z, qv[ks].w);
             accX = mfma(AX[ks], B, accX);
             accY = mfma(AY[ks], B, accY);
+            if (G0) accH = mfma(AH[ks], B, accH);
         }
         if (ok) {
             float r4[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) r4[i] = ax * accX[i] + ay * accY[i];
+            for (int i = 0; i < 4; ++i) r4[i] = ax * accX[i] + ay * accY[i] + (G0 ? ah * accH[i] : 0.f);
             *reinterpret_cast<uint2 *>(o + static_cast<size_t>(t) * D + 16 * ct + 4 * g4) =
                 make_uint2(pack2(r4[0], r4[1]), pack2(r4[2], r4[3]));
         }
     }
 }
 
-template <int D, bool ROPE>
-hipError_t launch_one(const Problem &p, hipStream_t stream) {
+template <int D, bool ROPE, bool G0>
+hipError_t launch_g(const Problem &p, hipStream_t stream) {
     const dim3 grid((D / 16) * p.B * p.H);
     // short sequences take the variant with a small logits buffer: less LDS, more workgroups per CU
     if (p.N <= kEShortN)
-        hipLaunchKernelGGL((encoder_mfma_kernel<D, ROPE, kEShortN>), grid, dim3(kEThreads), 0, stream, p);
+        hipLaunchKernelGGL((encoder_mfma_kernel<D, ROPE, kEShortN, G0>), grid, dim3(kEThreads), 0, stream, p);
     else
-        hipLaunchKernelGGL((encoder_mfma_kernel<D, ROPE, kEncoderMfmaMaxN>), grid, dim3(kEThreads), 0, stream, p);
+        hipLaunchKernelGGL((encoder_mfma_kernel<D, ROPE, kEncoderMfmaMaxN, G0>), grid, dim3(kEThreads), 0, stream, p);
     return hipGetLastError();
+}
+
+template <int D, bool ROPE>
+hipError_t launch_one(const Problem &p, hipStream_t stream) {
+    return p.g0 != nullptr ? launch_g<D, ROPE, true>(p, stream) : launch_g<D, ROPE, false>(p, stream);
 }
 
 }  // namespace

@@ -5,7 +5,8 @@
 // every query using the full-sequence sums (t = N) and one global prior-smoothed mean ubar,
 //   alpha_t F + beta_t G + gamma_t H = sigmah_t X + ((sigma1_t - sigmah_t)/N) Y,
 //   X = sum_i (e^{s_i}/E - 1/N) k^_i^T v_i = F/E - H/N,   Y = sum_i (s_i - P/N) k^_i^T v_i = G - (P/N) H,
-// so two centred d x d states carry the whole output.
+// so two centred d x d states carry the whole output. The optional zero-order gate (same section:
+// a first layer may keep the uniform term) adds (sigma0_t / N) q^_t H.
 //
 // One workgroup per (batch, head, 16-column tile). Pass 1 sums u over the sequence; pass 2 forms
 // the logits and accumulates F (rescaled by the running max), G, H for the tile; pass 3 applies
@@ -28,7 +29,7 @@ struct EncSmem {
     float vt[kC][kTile];
     float ubar[D];
     float F[D][kTile], G[D][kTile], Hs[D][kTile];
-    float s[kC], w1[kC], wh[kC];
+    float s[kC], w1[kC], wh[kC], w0[kC];
     float carry[4];
 };
 
@@ -90,6 +91,7 @@ __global__ __launch_bounds__(kThreads) void encoder_valu_kernel(Problem p) {
     const T *u = static_cast<const T *>(p.u) + row0 * D;
     const T *g1 = static_cast<const T *>(p.g1) + row0;
     const T *gh = static_cast<const T *>(p.gh) + row0;
+    const T *g0 = p.g0 != nullptr ? static_cast<const T *>(p.g0) + row0 : nullptr;
     T *o = static_cast<T *>(p.o) + row0 * D;
     const float et = expf(p.tau[h]);
     const float rs_du = 1.f / sqrtf(static_cast<float>(D));
@@ -201,7 +203,7 @@ __global__ __launch_bounds__(kThreads) void encoder_valu_kernel(Problem p) {
     }
     __syncthreads();
 
-    // ---- pass 3: o_t = sigmah_t q^_t X + ((sigma1_t - sigmah_t)/N) q^_t Y
+    // ---- pass 3: o_t = sigmah_t q^_t X + ((sigma1_t - sigmah_t)/N) q^_t Y (+ (sigma0_t/N) q^_t H)
     for (int t0 = 0; t0 < N; t0 += kC) {
         const int nval = min(kC, N - t0);
         load_unit_rows<D, T, ROPE>(q, t0, nval, sm.xh, rope_rev);
@@ -211,6 +213,7 @@ __global__ __launch_bounds__(kThreads) void encoder_valu_kernel(Problem p) {
             const float sh = valid ? sigmoidf(ld(gh, t0 + tid)) : 0.f;
             sm.wh[tid] = sh;
             sm.w1[tid] = (s1 - sh) * invN;
+            sm.w0[tid] = (valid && g0 != nullptr) ? sigmoidf(ld(g0, t0 + tid)) * invN : 0.f;
         }
         __syncthreads();
         {
@@ -219,13 +222,14 @@ __global__ __launch_bounds__(kThreads) void encoder_valu_kernel(Problem p) {
 #pragma unroll
             for (int x = 0; x < 2; ++x) {
                 const int mm = m0 + x;
-                float xX = 0.f, xY = 0.f;
+                float xX = 0.f, xY = 0.f, xH = 0.f;
                 for (int j = 0; j < D; ++j) {
                     const float qv = sm.xh[t][j];
                     xX += qv * sm.F[j][mm];
                     xY += qv * sm.G[j][mm];
+                    if (g0 != nullptr) xH += qv * sm.Hs[j][mm];
                 }
-                out[x] = sm.wh[t] * xX + sm.w1[t] * xY;
+                out[x] = sm.wh[t] * xX + sm.w1[t] * xY + sm.w0[t] * xH;
             }
             if (t < nval) {
                 const size_t idx = static_cast<size_t>(t0 + t) * D + tile * kTile + m0;

@@ -12,6 +12,7 @@ struct Problem {
     const void *q, *k, *v, *u;
     const float *mu, *tau;
     const void *g1, *gh;
+    const void *g0;     // zero-order gate pre-activations, or NULL (term off)
     void *o;
     zeros_state st;     // all NULL when no state is read or written
     int B, H, N, d, du;

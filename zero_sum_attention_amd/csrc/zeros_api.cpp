@@ -51,7 +51,7 @@ bool overlap(const Range &a, const Range &b) {
 // token rows per (b, h) that the call reads (N for the forward calls, 1 for decode).
 zeros_status check_common(const zeros_shape *s, const void *q, const void *k, const void *v,
                           const void *u, const float *mu, const float *tau, const void *g1,
-                          const void *gh, const void *o, const char *fn) {
+                          const void *gh, const void *g0, const void *o, const char *fn) {
     const std::string f(fn);
     if (!s) return fail(ZEROS_ERR_NULL, f + ": shape is NULL");
     if (!mu || !tau) return fail(ZEROS_ERR_NULL, f + ": mu or tau is NULL");
@@ -78,6 +78,7 @@ zeros_status check_common(const zeros_shape *s, const void *q, const void *k, co
         return fail(ZEROS_ERR_SHAPE, f + ": q, k, v, u and o must be 16-byte aligned");
     const Range out{o, tens};
     const Range ins[] = {{q, tens}, {k, tens}, {v, tens}, {u, tens}, {g1, gate}, {gh, gate},
+                         {g0, g0 ? gate : 0},
                          {mu, static_cast<size_t>(s->H) * s->d_u * 4}, {tau, static_cast<size_t>(s->H) * 4}};
     for (const Range &r : ins)
         if (overlap(out, r)) return fail(ZEROS_ERR_ALIAS, f + ": o overlaps an input");
@@ -97,9 +98,10 @@ bool state_aligned(const zeros_state *st) {
 
 zeros::Problem make_problem(const zeros_shape *s, const void *q, const void *k, const void *v,
                             const void *u, const float *mu, const float *tau, const void *g1,
-                            const void *gh, void *o, const zeros_state *st) {
+                            const void *gh, const void *g0, void *o, const zeros_state *st) {
     zeros::Problem p{};
     p.q = q; p.k = k; p.v = v; p.u = u; p.mu = mu; p.tau = tau; p.g1 = g1; p.gh = gh; p.o = o;
+    p.g0 = s->N != 0 ? g0 : nullptr;
     if (st) p.st = *st;
     p.B = s->B; p.H = s->H; p.N = s->N; p.d = s->d; p.du = s->d_u;
     p.dtype = s->dtype; p.rope = s->rope; p.rope_base = s->rope_base;
@@ -120,16 +122,16 @@ extern "C" {
 
 zeros_status zeros_fwd_causal(const zeros_shape *shape, const void *q, const void *k, const void *v,
                               const void *u, const float *mu, const float *tau, const void *g1,
-                              const void *gh, void *o, const zeros_state *state_out,
+                              const void *gh, const void *g0, void *o, const zeros_state *state_out,
                               void *workspace, size_t workspace_bytes, void *stream) {
-    zeros_status st = check_common(shape, q, k, v, u, mu, tau, g1, gh, o, "zeros_fwd_causal");
+    zeros_status st = check_common(shape, q, k, v, u, mu, tau, g1, gh, g0, o, "zeros_fwd_causal");
     if (st != ZEROS_OK) return st;
     if (state_out && !state_complete(state_out))
         return fail(ZEROS_ERR_NULL, "zeros_fwd_causal: a state_out field is NULL");
     if (state_out && !state_aligned(state_out))
         return fail(ZEROS_ERR_SHAPE, "zeros_fwd_causal: state_out matrices must be 16-byte aligned");
     if (shape->N == 0 && !state_out) return ok();
-    const zeros::Problem p = make_problem(shape, q, k, v, u, mu, tau, g1, gh, o, state_out);
+    const zeros::Problem p = make_problem(shape, q, k, v, u, mu, tau, g1, gh, g0, o, state_out);
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const bool mfma = causal_uses_mfma(shape);
     const size_t need = mfma ? zeros::causal_work_bytes(shape->B, shape->H, shape->N, shape->d_u)
@@ -164,25 +166,26 @@ size_t zeros_fwd_causal_workspace_bytes(const zeros_shape *shape) {
 
 zeros_status zeros_fwd_encoder(const zeros_shape *shape, const void *q, const void *k, const void *v,
                                const void *u, const float *mu, const float *tau, const void *g1,
-                               const void *gh, void *o, void *stream) {
-    zeros_status st = check_common(shape, q, k, v, u, mu, tau, g1, gh, o, "zeros_fwd_encoder");
+                               const void *gh, const void *g0, void *o, void *stream) {
+    zeros_status st = check_common(shape, q, k, v, u, mu, tau, g1, gh, g0, o, "zeros_fwd_encoder");
     if (st != ZEROS_OK) return st;
     if (shape->N == 0) return ok();
-    const zeros::Problem p = make_problem(shape, q, k, v, u, mu, tau, g1, gh, o, nullptr);
+    const zeros::Problem p = make_problem(shape, q, k, v, u, mu, tau, g1, gh, g0, o, nullptr);
     return hip_result(zeros::launch_encoder(p, static_cast<hipStream_t>(stream)), "zeros_fwd_encoder");
 }
 
 zeros_status zeros_decode_step(const zeros_shape *shape, const void *q, const void *k, const void *v,
                                const void *u, const float *mu, const float *tau, const void *g1,
-                               const void *gh, void *o, const zeros_state *state, void *stream) {
-    zeros_status st = check_common(shape, q, k, v, u, mu, tau, g1, gh, o, "zeros_decode_step");
+                               const void *gh, const void *g0, void *o, const zeros_state *state,
+                               void *stream) {
+    zeros_status st = check_common(shape, q, k, v, u, mu, tau, g1, gh, g0, o, "zeros_decode_step");
     if (st != ZEROS_OK) return st;
     if (shape->N != 1) return fail(ZEROS_ERR_SHAPE, "zeros_decode_step: N must be 1");
     if (!state) return fail(ZEROS_ERR_NULL, "zeros_decode_step: state is NULL");
     if (!state_complete(state)) return fail(ZEROS_ERR_NULL, "zeros_decode_step: a state field is NULL");
     if (!state_aligned(state))
         return fail(ZEROS_ERR_SHAPE, "zeros_decode_step: state matrices must be 16-byte aligned");
-    const zeros::Problem p = make_problem(shape, q, k, v, u, mu, tau, g1, gh, o, state);
+    const zeros::Problem p = make_problem(shape, q, k, v, u, mu, tau, g1, gh, g0, o, state);
     return hip_result(zeros::launch_decode(p, static_cast<hipStream_t>(stream)), "zeros_decode_step");
 }
 

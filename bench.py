@@ -89,9 +89,10 @@ def cpu_baseline(x):
 
 
 def secondary(dev, steps: int = 20) -> list:
-    """The other hot-path calls at their workload sizes: the ViT-shaped encoder forward and one
-    decode step of 256 sequences x 32 heads at t = 8192 (state values are random: the step's
-    work does not depend on them). Each is timed with HIP events on the launch stream."""
+    """The other hot-path calls at their workload sizes: the float32 LM-layer causal forward, the
+    ViT-shaped encoder forward, one decode step of 256 sequences x 32 heads at t = 8192 (state
+    values are random: the step's work does not depend on them) and the long causal forward with
+    the zero-order gate. Each is timed with HIP events on the launch stream."""
     import torch
 
     import zero_sum_attention_amd as Z
@@ -164,6 +165,26 @@ def secondary(dev, steps: int = 20) -> list:
     out.append({"workload": wl.name, "call": "zeros_decode_step", "ms": ms, "steps_per_s": 1e3 / ms,
                 "algorithmic_bytes": nbytes, "achieved_GBs": nbytes / (ms * 1e-3) / 1e9,
                 "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS})
+    del st, tok, o
+    torch.cuda.empty_cache()
+
+    # the long causal workload with the optional zero-order gate on (one more gate tensor read;
+    # the prep kernel adds sigma0/t to its coefficients)
+    wl = WORKLOAD
+    x = make_inputs(wl, gate0=True)
+    t = {k: torch.from_numpy(v).to(device=dev, dtype=torch.float32 if k in ("mu", "tau") else torch.bfloat16)
+         for k, v in x.items()}
+    o = torch.empty_like(t["v"])
+    ws = torch.empty(Z.zeros_fwd_causal_workspace_bytes(wl.B, wl.H, wl.N, wl.d, wl.d_u, torch.bfloat16, wl.rope),
+                     dtype=torch.uint8, device=dev)
+    ms = timed(lambda st: Z.zeros_fwd_causal(t["q"], t["k"], t["v"], t["u"], t["mu"], t["tau"], t["g1"],
+                                             t["gh"], g0=t["g0"], rope=wl.rope, rope_base=wl.rope_base,
+                                             out=o, workspace=ws, stream=st))
+    nbytes = algorithmic_bytes(wl) + wl.B * wl.H * wl.N * 2
+    out.append({"workload": wl.name + "-gate0", "call": "zeros_fwd_causal (g0 given)", "ms": ms,
+                "tokens_per_s": wl.B * wl.N / (ms * 1e-3), "algorithmic_bytes": nbytes,
+                "achieved_GBs": nbytes / (ms * 1e-3) / 1e9, "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS})
+    del t, o, ws, x
     return out
 
 

@@ -97,8 +97,14 @@ typedef struct {
  * Causal forward (Paper-Notes 关键设计: zero-sum weights, radial-angular decoupling, deviation
  * logits and the linear-time prefix scan; decoder mode per 损失函数 / 训练策略).
  * Inputs as in the conventions above; writes o [B, H, N, d].
- * state_out (nullable): receives the state after token N for every (b, h) (S = B); its
- *   buffers must not overlap the inputs or o.
+ * state_in (nullable): continue every (b, h) from this state (S = B) instead of the empty one:
+ *   the N tokens are positions state_in.t + 1 ... state_in.t + N of their sequences (logit
+ *   running mean, coefficients and RoPE angles included), as if the earlier tokens had been
+ *   part of the call (chunked prefill). Heads may have consumed different numbers of tokens.
+ *   Read only; with it the call runs on the float32 path for every dtype and d.
+ * state_out (nullable): receives the state after the call's last token for every (b, h) (S = B);
+ *   its buffers must not overlap the inputs, state_in or o (continue in place by alternating
+ *   two states).
  * workspace (nullable): device scratch of at least zeros_fwd_causal_workspace_bytes(shape)
  *   bytes, 256-byte aligned, used only while the call's work runs on `stream` (it holds the
  *   logits s_i, per-segment u sums, per-64-token logit aggregates and, on the bfloat16
@@ -111,10 +117,11 @@ zeros_status zeros_fwd_causal(const zeros_shape *shape,
                               const void *q, const void *k, const void *v, const void *u,
                               const float *mu, const float *tau,
                               const void *g1, const void *gh, const void *g0,
-                              void *o, const zeros_state *state_out,
+                              void *o, const zeros_state *state_in, const zeros_state *state_out,
                               void *workspace, size_t workspace_bytes, void *stream);
 
-/* Scratch bytes zeros_fwd_causal needs for `shape` (0 if none, or if shape is invalid). */
+/* Scratch bytes zeros_fwd_causal needs for `shape`, with or without state_in (0 if none, or if
+ * shape is invalid). */
 size_t zeros_fwd_causal_workspace_bytes(const zeros_shape *shape);
 
 /*

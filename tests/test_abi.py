@@ -66,11 +66,11 @@ def shape(B=1, H=2, N=8, d=16, d_u=16, dtype=0, rope=0, base=10000.0):
     return L.zeros_shape(B, H, N, d, d_u, dtype, rope, base)
 
 
-def call_causal(lib, shp, ptrs=None, state=None):
+def call_causal(lib, shp, ptrs=None, state=None, state_in=None):
     p = dict(P, **(ptrs or {}))
     return lib.zeros_fwd_causal(ctypes.byref(shp) if shp is not None else None, p["q"], p["k"], p["v"],
-                                p["u"], p["mu"], p["tau"], p["g1"], p["gh"], p["g0"], p["o"], state, None, 0,
-                                None)
+                                p["u"], p["mu"], p["tau"], p["g1"], p["gh"], p["g0"], p["o"], state_in, state,
+                                None, 0, None)
 
 
 def call_encoder(lib, shp, ptrs=None):
@@ -152,16 +152,35 @@ def test_workspace_size_and_validation(lib):
     need = lib.zeros_fwd_causal_workspace_bytes(ctypes.byref(small))
     p = dict(P)
     r = lib.zeros_fwd_causal(ctypes.byref(small), p["q"], p["k"], p["v"], p["u"], p["mu"], p["tau"], p["g1"],
-                             p["gh"], None, p["o"], None, 0x7000000, need - 1, None)
+                             p["gh"], None, p["o"], None, None, 0x7000000, need - 1, None)
     assert r == L.ZEROS_ERR_SHAPE
     r = lib.zeros_fwd_causal(ctypes.byref(small), p["q"], p["k"], p["v"], p["u"], p["mu"], p["tau"], p["g1"],
-                             p["gh"], None, p["o"], None, 0x7000010, need, None)
+                             p["gh"], None, p["o"], None, None, 0x7000010, need, None)
     assert r == L.ZEROS_ERR_SHAPE                                                       # misaligned
 
 
 def test_partial_state_rejected(lib):
     st = L.zeros_state(1, 2, 3, 4, 5, 6, 7, None)
     assert call_causal(lib, shape(), state=ctypes.byref(st)) == L.ZEROS_ERR_NULL
+
+
+def _aligned_state(base):
+    return L.zeros_state(*(base + 0x100000 * i for i in range(8)))
+
+
+def test_state_in_validation(lib):
+    partial = L.zeros_state(1, 2, 3, 4, 5, 6, 7, None)
+    assert call_causal(lib, shape(), state_in=ctypes.byref(partial)) == L.ZEROS_ERR_NULL
+    mis = L.zeros_state(0x1000008, 0x2000000, 0x3000000, 0x4000000, 0x5000000, 0x6000000, 0x7000000, 0x8000000)
+    assert call_causal(lib, shape(), state_in=ctypes.byref(mis)) == L.ZEROS_ERR_SHAPE
+    a, b = _aligned_state(0x40000000), _aligned_state(0x50000000)
+    # the same state as input and output, or overlapping fields, is rejected
+    assert call_causal(lib, shape(), state=ctypes.byref(a), state_in=ctypes.byref(a)) == L.ZEROS_ERR_ALIAS
+    c = _aligned_state(0x50000000)
+    c.m = a.E
+    assert call_causal(lib, shape(), state=ctypes.byref(c), state_in=ctypes.byref(a)) == L.ZEROS_ERR_ALIAS
+    # o inside state_in's F
+    assert call_causal(lib, shape(), {"o": a.F}, state=ctypes.byref(b), state_in=ctypes.byref(a)) == L.ZEROS_ERR_ALIAS
 
 
 def test_decode_validation(lib):

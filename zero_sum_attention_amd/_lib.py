@@ -53,7 +53,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     vp, i32, f32p = ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p
     # shape, q, k, v, u, mu, tau, g1, gh, g0, o
     fwd = [ctypes.POINTER(zeros_shape), vp, vp, vp, vp, f32p, f32p, vp, vp, vp, vp]
-    lib.zeros_fwd_causal.argtypes = fwd + [ctypes.POINTER(zeros_state), vp, ctypes.c_size_t, vp]
+    lib.zeros_fwd_causal.argtypes = fwd + [ctypes.POINTER(zeros_state), ctypes.POINTER(zeros_state), vp,
+                                           ctypes.c_size_t, vp]
     lib.zeros_fwd_causal.restype = i32
     lib.zeros_fwd_causal_workspace_bytes.argtypes = [ctypes.POINTER(zeros_shape)]
     lib.zeros_fwd_causal_workspace_bytes.restype = ctypes.c_size_t
@@ -174,23 +175,26 @@ class DecodeState:
 
 def zeros_fwd_causal(q, k, v, u, mu, tau, g1, gh, *, g0: torch.Tensor | None = None, rope: bool = False,
                      rope_base: float = 10000.0, out: torch.Tensor | None = None,
-                     state_out: DecodeState | None = None, workspace: torch.Tensor | None = None,
-                     stream=None) -> torch.Tensor:
+                     state_in: DecodeState | None = None, state_out: DecodeState | None = None,
+                     workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Causal forward over q, k, v [B, H, N, d], u [B, H, N, d_u], g1, gh [B, H, N].
 
-    ``g0`` [B, H, N] (optional) enables the zero-order gate. ``workspace`` (optional uint8 tensor)
-    is reused scratch; without it one is allocated per call when the path needs it (see
-    zeros_fwd_causal_workspace_bytes)."""
+    ``g0`` [B, H, N] (optional) enables the zero-order gate. ``state_in`` continues every
+    (b, h) from a state (chunked prefill); ``state_out`` receives the final state and must be a
+    different state object. ``workspace`` (optional uint8 tensor) is reused scratch; without it
+    one is allocated per call when the path needs it (see zeros_fwd_causal_workspace_bytes)."""
     _check_tensors(q, k, v, u, mu, tau, g1, gh, 1, g0)
     o = torch.empty_like(v) if out is None else out
     _need(o.shape == v.shape and o.dtype == v.dtype and o.is_contiguous() and o.device == q.device,
           "out must match v")
-    if state_out is not None:
-        _need((state_out.S, state_out.H, state_out.d, state_out.d_u) ==
-              (q.shape[0], q.shape[1], q.shape[-1], u.shape[-1]), "state_out sizes differ")
+    for name, s_ in (("state_in", state_in), ("state_out", state_out)):
+        if s_ is not None:
+            _need((s_.S, s_.H, s_.d, s_.d_u) == (q.shape[0], q.shape[1], q.shape[-1], u.shape[-1]),
+                  f"{name} sizes differ")
     lib = load_library()
     shp = _shape(q, u, q.shape[2], rope, rope_base)
     st = ctypes.byref(state_out.c) if state_out is not None else None
+    sti = ctypes.byref(state_in.c) if state_in is not None else None
     nws = lib.zeros_fwd_causal_workspace_bytes(ctypes.byref(shp))
     if workspace is None and nws > 0:
         workspace = torch.empty(nws, dtype=torch.uint8, device=q.device)
@@ -198,7 +202,7 @@ def zeros_fwd_causal(q, k, v, u, mu, tau, g1, gh, *, g0: torch.Tensor | None = N
         _need(workspace.dtype == torch.uint8 and workspace.device == q.device and workspace.is_contiguous(),
               "workspace must be a contiguous uint8 tensor on q's device")
     _check(lib.zeros_fwd_causal(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(u), _ptr(mu),
-                                _ptr(tau), _ptr(g1), _ptr(gh), _ptr(g0), _ptr(o), st,
+                                _ptr(tau), _ptr(g1), _ptr(gh), _ptr(g0), _ptr(o), sti, st,
                                 _ptr(workspace), 0 if workspace is None else workspace.numel(),
                                 _stream(q.device, stream)))
     return o

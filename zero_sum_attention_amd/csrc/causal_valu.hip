@@ -15,6 +15,8 @@
 // The states live in LDS (float32); K Q^T, the output products and the fold are 16x16 tiles per wave.
 // The logits s_i and the per-segment u sums come from logits.hip (computed once per head, ahead of
 // this kernel); the scalar scans are recomputed by every tile of a head (O(C) per chunk).
+// A continued sequence (state in: the recurrence of the linear-time prefix scan paused after
+// t_in tokens) starts from that state's F, G, H, m, E, P, with positions shifted by t_in.
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "mfma_common.hpp"
@@ -73,6 +75,9 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p, const 
     T *o = static_cast<T *>(p.o) + row0 * D;
 
     const float *srow = s_all + row0;
+    // a continued sequence starts from the given state: its tokens are positions tin + 1 ...
+    const bool cont = p.sin.F != nullptr;
+    const int tin = cont ? p.sin.t[bh] : 0;
 
     const int lr = tid / kTPR, lp = tid % kTPR, c0 = lp * EPT;
     double rope_rev[ROPE ? EPT / 2 : 1];
@@ -81,12 +86,14 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p, const 
         for (int jj = 0; jj < EPT / 2; ++jj) rope_rev[jj] = rope_rev_per_pos(c0 / 2 + jj, D, p.rope_base);
     }
 
-    float m_c = kNegInf, E_c = 0.f, P_c = 0.f;
+    float m_c = cont ? p.sin.m[bh] : kNegInf, E_c = cont ? p.sin.E[bh] : 0.f, P_c = cont ? p.sin.P[bh] : 0.f;
 
+    const size_t mat0 = static_cast<size_t>(bh) * D * D;
     for (int x = tid; x < D * kTile; x += kThreads) {
-        (&sm.F[0][0])[x] = 0.f;
-        (&sm.G[0][0])[x] = 0.f;
-        (&sm.Hs[0][0])[x] = 0.f;
+        const size_t idx = mat0 + static_cast<size_t>(x / kTile) * D + tile * kTile + x % kTile;
+        (&sm.F[0][0])[x] = cont ? p.sin.F[idx] : 0.f;
+        (&sm.G[0][0])[x] = cont ? p.sin.G[idx] : 0.f;
+        (&sm.Hs[0][0])[x] = cont ? p.sin.Hs[idx] : 0.f;
     }
 
     // the rows of the next chunk are read while the current one is processed; a thread takes rows
@@ -125,7 +132,7 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p, const 
 #pragma unroll
         for (int rs = 0; rs < RS; ++rs) {
             const int lrr = lr + RSTEP * rs;
-            const int tok = t0 + lrr;
+            const int tok = tin + t0 + lrr;      // 0-based position in the sequence (RoPE)
             const bool valid = lrr < nval;
             float xq[EPT], xk[EPT];
             float ssq = 0.f, ssk = 0.f;
@@ -215,7 +222,7 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p, const 
             }
             const float P = P_c + ps;
             if (valid) {
-                const float tt = static_cast<float>(t0 + r + 1);
+                const float tt = static_cast<float>(tin + t0 + r + 1);
                 const float s1 = sm.sig1[r], sh = sm.sigh[r];
                 const float a = sh / E;
                 const float d1 = s1 - sh;
@@ -358,7 +365,6 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p, const 
 
     // ---- final state
     if (p.st.F != nullptr) {
-        const size_t mat0 = static_cast<size_t>(bh) * D * D;
         for (int x = tid; x < D * kTile; x += kThreads) {
             const int j = x / kTile, mm = x % kTile;
             const size_t idx = mat0 + static_cast<size_t>(j) * D + tile * kTile + mm;
@@ -368,7 +374,7 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p, const 
         }
         if (tile == 0) {
             if (tid < D) {
-                float su = 0.f;
+                float su = cont ? p.sin.Su[static_cast<size_t>(bh) * D + tid] : 0.f;
                 for (int sg = 0; sg < nls; ++sg) su += useg[(static_cast<size_t>(bh) * nls + sg) * D + tid];
                 p.st.Su[static_cast<size_t>(bh) * D + tid] = su;
             }
@@ -376,7 +382,7 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p, const 
                 p.st.m[bh] = m_c;
                 p.st.E[bh] = E_c;
                 p.st.P[bh] = P_c;
-                p.st.t[bh] = N;
+                p.st.t[bh] = tin + N;
             }
         }
     }

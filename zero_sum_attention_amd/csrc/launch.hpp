@@ -15,6 +15,7 @@ struct Problem {
     const void *g0;     // zero-order gate pre-activations, or NULL (term off)
     void *o;
     zeros_state st;     // all NULL when no state is read or written
+    zeros_state sin;    // causal: state to continue from (all NULL: the empty state)
     int B, H, N, d, du;
     int dtype;          // zeros_dtype
     int rope;

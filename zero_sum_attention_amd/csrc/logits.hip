@@ -115,10 +115,13 @@ __global__ __launch_bounds__(kThreads) void useg_sum_kernel(const T *u, float *u
 
 // Logits of one segment. Lane = token within a 64-token block, wave w = features
 // [w*D/4, (w+1)*D/4). The running sum over the block is an inclusive lane scan per feature.
+// su_in, t_in (both NULL, or both set): u sum and token count of earlier tokens of the sequence
+// (a continued sequence), which join the prior.
 template <int D, typename T>
 __global__ __launch_bounds__(kThreads) void logits_kernel(const T *u, const float *mu, const float *tau,
                                                           const float *useg, float *s_out, float4 *agg,
-                                                          int N, int H, int nseg) {
+                                                          int N, int H, int nseg, const float *su_in,
+                                                          const int *t_in) {
     constexpr int DW = D / 4;                  // features per wave
     __shared__ float c0s[D];
     __shared__ float part[4][64];
@@ -127,8 +130,9 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(const T *u, const floa
     const int h = bh % H;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const float et = expf(tau[h]);
+    const float tprev = t_in != nullptr ? static_cast<float>(t_in[bh]) : 0.f;
     if (tid < D) {
-        float s = et * mu[h * D + tid];
+        float s = et * mu[h * D + tid] + (su_in != nullptr ? su_in[static_cast<size_t>(bh) * D + tid] : 0.f);
         const float *us = useg + static_cast<size_t>(bh) * nseg * D + tid;
         for (int p = 0; p < seg; ++p) s += us[static_cast<size_t>(p) * D];
         c0s[tid] = s;
@@ -150,7 +154,7 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(const T *u, const floa
         load_feats<DW>(ub + static_cast<size_t>(row) * D + w * DW, valid, x);
 #pragma unroll
         for (int i = 0; i < DW; ++i) S[i] = wave_scan_add(x[i]);
-        const float inv = 1.f / (et + static_cast<float>(row + 1));
+        const float inv = 1.f / (et + tprev + static_cast<float>(row + 1));
         float dot = 0.f;
 #pragma unroll
         for (int i = 0; i < DW; ++i) {
@@ -317,13 +321,17 @@ hipError_t launch_t(const Problem &p, float *useg, float *s_out, float4 *agg, fl
                        static_cast<const T *>(p.u), useg, p.N, nseg, rope_tab, p.rope_base);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
+    // a continued sequence (state in) takes the generic kernel, which adds the earlier tokens
     if constexpr (sizeof(T) == 2 && (D == 64 || D == 128)) {
-        hipLaunchKernelGGL((logits_stream_kernel<D>), dim3(grid), dim3(kStreamThreads), 0, stream,
-                           static_cast<const bf16 *>(p.u), p.mu, p.tau, useg, s_out, agg, p.N, p.H, nseg);
-    } else {
-        hipLaunchKernelGGL((logits_kernel<D, T>), dim3(grid), dim3(kThreads), 0, stream,
-                           static_cast<const T *>(p.u), p.mu, p.tau, useg, s_out, agg, p.N, p.H, nseg);
+        if (p.sin.Su == nullptr) {
+            hipLaunchKernelGGL((logits_stream_kernel<D>), dim3(grid), dim3(kStreamThreads), 0, stream,
+                               static_cast<const bf16 *>(p.u), p.mu, p.tau, useg, s_out, agg, p.N, p.H, nseg);
+            return hipGetLastError();
+        }
     }
+    hipLaunchKernelGGL((logits_kernel<D, T>), dim3(grid), dim3(kThreads), 0, stream,
+                       static_cast<const T *>(p.u), p.mu, p.tau, useg, s_out, agg, p.N, p.H, nseg,
+                       p.sin.Su, p.sin.t);
     return hipGetLastError();
 }
 

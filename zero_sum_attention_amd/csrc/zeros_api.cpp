@@ -2,6 +2,7 @@
 // Every check runs on the host before any HIP call, so invalid arguments never reach a kernel.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -96,6 +97,15 @@ bool state_aligned(const zeros_state *st) {
            al(st->E, 4) && al(st->P, 4) && al(st->t, 4);
 }
 
+// Byte ranges of the fields of a state of S x H heads (for the overlap checks).
+void state_ranges(const zeros_state *st, const zeros_shape *s, Range (&r)[8]) {
+    const size_t n = static_cast<size_t>(s->B) * s->H;
+    const size_t mat = n * s->d * s->d * 4;
+    r[0] = {st->F, mat}; r[1] = {st->G, mat}; r[2] = {st->Hs, mat};
+    r[3] = {st->Su, n * s->d_u * 4}; r[4] = {st->m, n * 4}; r[5] = {st->E, n * 4};
+    r[6] = {st->P, n * 4}; r[7] = {st->t, n * 4};
+}
+
 zeros::Problem make_problem(const zeros_shape *s, const void *q, const void *k, const void *v,
                             const void *u, const float *mu, const float *tau, const void *g1,
                             const void *gh, const void *g0, void *o, const zeros_state *st) {
@@ -122,18 +132,39 @@ extern "C" {
 
 zeros_status zeros_fwd_causal(const zeros_shape *shape, const void *q, const void *k, const void *v,
                               const void *u, const float *mu, const float *tau, const void *g1,
-                              const void *gh, const void *g0, void *o, const zeros_state *state_out,
-                              void *workspace, size_t workspace_bytes, void *stream) {
+                              const void *gh, const void *g0, void *o, const zeros_state *state_in,
+                              const zeros_state *state_out, void *workspace, size_t workspace_bytes,
+                              void *stream) {
     zeros_status st = check_common(shape, q, k, v, u, mu, tau, g1, gh, g0, o, "zeros_fwd_causal");
     if (st != ZEROS_OK) return st;
+    if (state_in && !state_complete(state_in))
+        return fail(ZEROS_ERR_NULL, "zeros_fwd_causal: a state_in field is NULL");
+    if (state_in && !state_aligned(state_in))
+        return fail(ZEROS_ERR_SHAPE, "zeros_fwd_causal: state_in matrices must be 16-byte aligned");
     if (state_out && !state_complete(state_out))
         return fail(ZEROS_ERR_NULL, "zeros_fwd_causal: a state_out field is NULL");
     if (state_out && !state_aligned(state_out))
         return fail(ZEROS_ERR_SHAPE, "zeros_fwd_causal: state_out matrices must be 16-byte aligned");
+    if (state_in && state_out) {
+        Range a[8], b[8];
+        state_ranges(state_in, shape, a);
+        state_ranges(state_out, shape, b);
+        for (const Range &x : a)
+            for (const Range &y : b)
+                if (overlap(x, y)) return fail(ZEROS_ERR_ALIAS, "zeros_fwd_causal: state_out overlaps state_in");
+    }
+    if (state_in && shape->N != 0) {
+        Range a[8];
+        state_ranges(state_in, shape, a);
+        const Range out{o, static_cast<size_t>(shape->B) * shape->H * shape->N * shape->d * elem_bytes(shape->dtype)};
+        for (const Range &x : a)
+            if (overlap(x, out)) return fail(ZEROS_ERR_ALIAS, "zeros_fwd_causal: o overlaps state_in");
+    }
     if (shape->N == 0 && !state_out) return ok();
-    const zeros::Problem p = make_problem(shape, q, k, v, u, mu, tau, g1, gh, g0, o, state_out);
+    zeros::Problem p = make_problem(shape, q, k, v, u, mu, tau, g1, gh, g0, o, state_out);
+    if (state_in) p.sin = *state_in;
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    const bool mfma = causal_uses_mfma(shape);
+    const bool mfma = !state_in && causal_uses_mfma(shape);
     const size_t need = mfma ? zeros::causal_work_bytes(shape->B, shape->H, shape->N, shape->d_u)
                              : zeros::causal_valu_work_bytes(shape->B, shape->H, shape->N, shape->d_u);
     void *ws = workspace;
@@ -160,8 +191,10 @@ zeros_status zeros_fwd_causal(const zeros_shape *shape, const void *q, const voi
 
 size_t zeros_fwd_causal_workspace_bytes(const zeros_shape *shape) {
     if (!shape || shape->B < 1 || shape->H < 1 || shape->N < 0 || shape->d_u < 1) return 0;
-    if (!causal_uses_mfma(shape)) return zeros::causal_valu_work_bytes(shape->B, shape->H, shape->N, shape->d_u);
-    return zeros::causal_work_bytes(shape->B, shape->H, shape->N, shape->d_u);
+    const size_t valu = zeros::causal_valu_work_bytes(shape->B, shape->H, shape->N, shape->d_u);
+    if (!causal_uses_mfma(shape)) return valu;
+    // a call with state_in takes the float32 path: cover both
+    return std::max(valu, zeros::causal_work_bytes(shape->B, shape->H, shape->N, shape->d_u));
 }
 
 zeros_status zeros_fwd_encoder(const zeros_shape *shape, const void *q, const void *k, const void *v,

@@ -103,8 +103,8 @@ typedef struct {
  *   part of the call (chunked prefill). Heads may have consumed different numbers of tokens.
  *   Read only; with it the call runs on the float32 path for every dtype and d.
  * state_out (nullable): receives the state after the call's last token for every (b, h) (S = B);
- *   its buffers must not overlap the inputs, state_in or o (continue in place by alternating
- *   two states).
+ *   its buffers must not overlap the inputs, state_in, o or each other (ZEROS_ERR_ALIAS; continue
+ *   in place by alternating two states).
  * workspace (nullable): device scratch of at least zeros_fwd_causal_workspace_bytes(shape)
  *   bytes, 256-byte aligned, used only while the call's work runs on `stream` (it holds the
  *   logits s_i, per-segment u sums, per-64-token logit aggregates and, on the bfloat16
@@ -139,7 +139,8 @@ zeros_status zeros_fwd_encoder(const zeros_shape *shape,
  * One recurrent step (the O(d^2)-per-token update of 关键设计 / 线性时间前缀扫描):
  * shape->B = S sequences, shape->N must be 1. q, k, v, o [S, H, d]; u [S, H, d_u];
  * g1, gh, g0 [S, H]. Each (sequence, head) consumes one token at position state.t + 1 and its state
- * is updated in place.
+ * is updated in place; the state must not overlap the token tensors, mu, tau or o, and its
+ * fields must not overlap each other (ZEROS_ERR_ALIAS).
  */
 zeros_status zeros_decode_step(const zeros_shape *shape,
                                const void *q, const void *k, const void *v, const void *u,

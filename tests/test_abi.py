@@ -173,14 +173,33 @@ def test_state_in_validation(lib):
     assert call_causal(lib, shape(), state_in=ctypes.byref(partial)) == L.ZEROS_ERR_NULL
     mis = L.zeros_state(0x1000008, 0x2000000, 0x3000000, 0x4000000, 0x5000000, 0x6000000, 0x7000000, 0x8000000)
     assert call_causal(lib, shape(), state_in=ctypes.byref(mis)) == L.ZEROS_ERR_SHAPE
-    a, b = _aligned_state(0x40000000), _aligned_state(0x50000000)
+    a, b = _aligned_state(0xB0000000), _aligned_state(0xC0000000)      # away from the placeholders
     # the same state as input and output, or overlapping fields, is rejected
     assert call_causal(lib, shape(), state=ctypes.byref(a), state_in=ctypes.byref(a)) == L.ZEROS_ERR_ALIAS
-    c = _aligned_state(0x50000000)
+    c = _aligned_state(0xC0000000)
     c.m = a.E
     assert call_causal(lib, shape(), state=ctypes.byref(c), state_in=ctypes.byref(a)) == L.ZEROS_ERR_ALIAS
     # o inside state_in's F
     assert call_causal(lib, shape(), {"o": a.F}, state=ctypes.byref(b), state_in=ctypes.byref(a)) == L.ZEROS_ERR_ALIAS
+
+
+def test_written_state_must_not_overlap(lib):
+    """A state the call writes (causal state_out, the decode state) may not overlap a tensor
+    argument, o, or itself."""
+    s = _aligned_state(0xB0000000)
+    s.Su = P["q"]
+    assert call_causal(lib, shape(), state=ctypes.byref(s)) == L.ZEROS_ERR_ALIAS
+    s = _aligned_state(0xB0000000)
+    s.t = P["o"]
+    assert call_causal(lib, shape(), state=ctypes.byref(s)) == L.ZEROS_ERR_ALIAS
+    assert call_decode(lib, shape(N=1), ctypes.byref(s)) == L.ZEROS_ERR_ALIAS
+    s = _aligned_state(0xB0000000)
+    s.G = s.F + 256                                   # F is 2 KiB at B1 H2 d16
+    assert call_causal(lib, shape(), state=ctypes.byref(s)) == L.ZEROS_ERR_ALIAS
+    assert call_decode(lib, shape(N=1), ctypes.byref(s)) == L.ZEROS_ERR_ALIAS
+    s = _aligned_state(0xB0000000)
+    s.m = P["g0"]
+    assert call_decode(lib, shape(N=1), ctypes.byref(s)) == L.ZEROS_ERR_ALIAS
 
 
 def test_decode_validation(lib):

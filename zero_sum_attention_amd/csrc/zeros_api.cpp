@@ -106,6 +106,28 @@ void state_ranges(const zeros_state *st, const zeros_shape *s, Range (&r)[8]) {
     r[6] = {st->P, n * 4}; r[7] = {st->t, n * 4};
 }
 
+// A state the call writes must not overlap the call's inputs, its output or itself.
+zeros_status check_written_state(const zeros_state *st, const zeros_shape *s, const void *q, const void *k,
+                                 const void *v, const void *u, const float *mu, const float *tau,
+                                 const void *g1, const void *gh, const void *g0, const void *o,
+                                 const char *fn) {
+    const size_t eb = elem_bytes(s->dtype);
+    const size_t tens = static_cast<size_t>(s->B) * s->H * s->N * s->d * eb;
+    const size_t gate = static_cast<size_t>(s->B) * s->H * s->N * eb;
+    const Range io[] = {{q, tens}, {k, tens}, {v, tens}, {u, tens}, {g1, gate}, {gh, gate},
+                        {g0, g0 ? gate : 0}, {o, tens},
+                        {mu, static_cast<size_t>(s->H) * s->d_u * 4}, {tau, static_cast<size_t>(s->H) * 4}};
+    Range r[8];
+    state_ranges(st, s, r);
+    for (int i = 0; i < 8; ++i) {
+        for (const Range &x : io)
+            if (overlap(r[i], x)) return fail(ZEROS_ERR_ALIAS, std::string(fn) + ": the written state overlaps a tensor argument");
+        for (int j = 0; j < i; ++j)
+            if (overlap(r[i], r[j])) return fail(ZEROS_ERR_ALIAS, std::string(fn) + ": fields of the written state overlap");
+    }
+    return ZEROS_OK;
+}
+
 zeros::Problem make_problem(const zeros_shape *s, const void *q, const void *k, const void *v,
                             const void *u, const float *mu, const float *tau, const void *g1,
                             const void *gh, const void *g0, void *o, const zeros_state *st) {
@@ -145,6 +167,10 @@ zeros_status zeros_fwd_causal(const zeros_shape *shape, const void *q, const voi
         return fail(ZEROS_ERR_NULL, "zeros_fwd_causal: a state_out field is NULL");
     if (state_out && !state_aligned(state_out))
         return fail(ZEROS_ERR_SHAPE, "zeros_fwd_causal: state_out matrices must be 16-byte aligned");
+    if (state_out) {
+        st = check_written_state(state_out, shape, q, k, v, u, mu, tau, g1, gh, g0, o, "zeros_fwd_causal");
+        if (st != ZEROS_OK) return st;
+    }
     if (state_in && state_out) {
         Range a[8], b[8];
         state_ranges(state_in, shape, a);
@@ -218,6 +244,8 @@ zeros_status zeros_decode_step(const zeros_shape *shape, const void *q, const vo
     if (!state_complete(state)) return fail(ZEROS_ERR_NULL, "zeros_decode_step: a state field is NULL");
     if (!state_aligned(state))
         return fail(ZEROS_ERR_SHAPE, "zeros_decode_step: state matrices must be 16-byte aligned");
+    st = check_written_state(state, shape, q, k, v, u, mu, tau, g1, gh, g0, o, "zeros_decode_step");
+    if (st != ZEROS_OK) return st;
     const zeros::Problem p = make_problem(shape, q, k, v, u, mu, tau, g1, gh, g0, o, state);
     return hip_result(zeros::launch_decode(p, static_cast<hipStream_t>(stream)), "zeros_decode_step");
 }

@@ -7,7 +7,9 @@
 //   pass 1 (useg_sum_kernel): per (head, segment of kSeg tokens), the column sums of u;
 //   pass 2 (logits_stream_kernel for bfloat16 and d 64/128, logits_kernel otherwise): per
 //                             (head, segment), the running sum starts from e^tau mu plus the
-//                             sums of the earlier segments and gives ubar_i and s_i.
+//                             sums of the earlier segments and gives ubar_i and s_i. A sequence
+//                             continued from a state takes logits_kernel, which also adds the
+//                             state's u-sum and token count.
 // Output: s [B*H, N] float32, the per-segment sums [B*H, nseg, d_u] (their total is the u-sum of
 // the recurrent state) and, per 64-token chunk, (max s, sum e^{s - max}, sum s) [B*H, nchunk, 4].
 #include "device_common.hpp"

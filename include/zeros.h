@@ -101,7 +101,8 @@ typedef struct {
  *   the N tokens are positions state_in.t + 1 ... state_in.t + N of their sequences (logit
  *   running mean, coefficients and RoPE angles included), as if the earlier tokens had been
  *   part of the call (chunked prefill). Heads may have consumed different numbers of tokens.
- *   Read only; with it the call runs on the float32 path for every dtype and d.
+ *   Read only. bfloat16 d 64/128 calls stay on the matrix-core path (the state enters in its
+ *   centred basis); the others, and a call with N = 0, take the float32 path.
  * state_out (nullable): receives the state after the call's last token for every (b, h) (S = B);
  *   its buffers must not overlap the inputs, state_in, o or each other (ZEROS_ERR_ALIAS; continue
  *   in place by alternating two states).

@@ -44,8 +44,8 @@ def _state_np(st):
 @pytest.mark.parametrize("rope", [False, True])
 def test_continuation_matches_one_pass(d, dtype, cut, N, rope):
     """Prefix [0, cut) with state_out, then [cut, N) from it: the outputs and the final state
-    equal the oracle's single pass. bfloat16 d 64/128 prefixes run on the matrix-core path, the
-    continuation on the float32 path."""
+    equal the oracle's single pass. bfloat16 d 64/128 calls (prefix and continuation) run on the
+    matrix-core path, the continuation over several scan segments."""
     wl = CONFIGS[2].with_(B=2, H=3, N=N, d=d, d_u=d, dtype=dtype, seed=6000 + d + cut)
     x = make_inputs(wl, gate0=(d == 64))
     t = to_device(x, dtype)
@@ -65,11 +65,12 @@ def test_continuation_matches_one_pass(d, dtype, cut, N, rope):
         assert rel_l2(got[key], st[key]) <= bar, key
 
 
-def test_continuation_heads_at_different_positions():
+@pytest.mark.parametrize("d,dtype", [(32, "f32"), (64, "bf16"), (128, "bf16")])
+def test_continuation_heads_at_different_positions(d, dtype):
     """Batch 0 continues after 40 tokens, batch 1 after 75 (one state assembled from two
-    prefills); each continues for 50 tokens in one call."""
-    d, dtype = 32, "f32"
-    wl = CONFIGS[2].with_(B=2, H=2, N=125, d=d, d_u=d, dtype=dtype, seed=6100)
+    prefills); each continues for 50 tokens in one call (bfloat16 d 64/128: the matrix-core
+    path with a per-head position offset)."""
+    wl = CONFIGS[2].with_(B=2, H=2, N=125, d=d, d_u=d, dtype=dtype, seed=6100 + d)
     x = make_inputs(wl)
     t = to_device(x, dtype)
     s40 = Z.DecodeState(2, 2, d, d).reset()
@@ -93,7 +94,8 @@ def test_continuation_heads_at_different_positions():
 
 
 def test_continuation_long_bf16_prefix():
-    """A 4096-token bf16 d 128 RoPE prefix on the matrix-core path, then 1000 more tokens."""
+    """A 4096-token bf16 d 128 RoPE prefix, then 1000 more tokens (16 scan segments of one chunk:
+    the combine starts from the given state)."""
     wl = CONFIGS[4].with_(B=1, H=2, N=5096, seed=6200)
     x = make_inputs(wl)
     t = to_device(x, wl.dtype)

@@ -202,19 +202,25 @@ __global__ __launch_bounds__(kPrepThreads) void causal_prep_kernel(Problem p, Ca
     const int t0 = c * kC, nval = min(kC, N - t0);
     const size_t row0 = static_cast<size_t>(bh) * N;
     unsigned char *rec = work.rec + (static_cast<size_t>(bh) * nch + c) * R::bytes;
+    // a sequence continued from a state: its tokens are positions tin + 1 ...
+    const bool cont = p.sin.F != nullptr;
+    const int tin = cont ? p.sin.t[bh] : 0;
 
     if (ROPE) {
         if (tid < D / 2) {
             float c0, s0;
-            rope_cos_sin(rope_rev_per_pos(tid, D, p.rope_base), t0, c0, s0);
+            rope_cos_sin(rope_rev_per_pos(tid, D, p.rope_base), tin + t0, c0, s0);
             sm.rot0[tid] = make_float2(c0, s0);
         }
         __syncthreads();
     }
 
-    // ---- wave 0: logit carry at t0 from the earlier chunks, then this chunk's scan
+    // ---- wave 0: logit carry at t0 from the state (if any) and the earlier chunks, then this
+    // chunk's scan
     if (wave == 0) {
-        float m = kNegInf, e = 0.f, ps = 0.f;
+        const bool from_state = cont && lane == 0;
+        float m = from_state ? p.sin.m[bh] : kNegInf, e = from_state ? p.sin.E[bh] : 0.f;
+        float ps = from_state ? p.sin.P[bh] : 0.f;
         const float4 *ag = work.agg + static_cast<size_t>(bh) * nch;
         for (int j = lane; j < c; j += 64) {
             const float4 a = ag[j];
@@ -235,7 +241,7 @@ __global__ __launch_bounds__(kPrepThreads) void causal_prep_kernel(Problem p, Ca
         const float s0 = (vs && p.g0 != nullptr)
                              ? __fdividef(1.f, 1.f + __expf(-lo_f(static_cast<const uint16_t *>(p.g0)[row0 + t0 + lane])))
                              : 0.f;
-        chunk_scan(sm.cf, lane, t0, nval, sv, g1v, ghv, s0, m0, E0, P0);
+        chunk_scan(sm.cf, lane, tin + t0, nval, sv, g1v, ghv, s0, m0, E0, P0);
     }
 
     // ---- unit q^, k^ rows, rotated by their offset inside the chunk
@@ -437,11 +443,30 @@ __global__ __launch_bounds__(D * 4) void causal_seg_kernel(Problem p, CausalWork
     const uint16_t *vg = static_cast<const uint16_t *>(p.v) + row0 * D;
     uint16_t *og = static_cast<uint16_t *>(p.o) + row0 * D;
     const unsigned char *rec0 = work.rec + static_cast<size_t>(bh) * nch * R::bytes;
+    // a sequence continued from a state: tokens are positions tin + 1 ..., and the first segment
+    // of the main pass starts from that state
+    const bool cont = p.sin.F != nullptr;
+    const int tin = cont ? p.sin.t[bh] : 0;
 
     // state of this wave's columns: X, Y, H rows 16 jb + 4 g4 + i, column 16 w + l16
     f32x4 X[JB], Y[JB], Hm[JB];
     const size_t sidx = static_cast<size_t>(w) * 64 + lane;       // float4 index inside a (s, jb) block
-    if (!PASS1 && seg > 0) {
+    if (!PASS1 && seg == 0 && tin > 0) {
+        // the given state in the centred basis: X = F/E - H/t, Y = G - (P/t) H
+        const size_t mat0 = static_cast<size_t>(bh) * D * D;
+        const float iE = 1.f / p.sin.E[bh], it = 1.f / static_cast<float>(tin);
+        const float pt = p.sin.P[bh] * it;
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const size_t idx = mat0 + static_cast<size_t>(16 * jb + 4 * g4 + i) * D + w * kTile + l16;
+                const float hh = p.sin.Hs[idx];
+                X[jb][i] = p.sin.F[idx] * iE - hh * it;
+                Y[jb][i] = p.sin.G[idx] - pt * hh;
+                Hm[jb][i] = hh;
+            }
+    } else if (!PASS1 && seg > 0) {
         const float4 *st0 = reinterpret_cast<const float4 *>(work.segst + (static_cast<size_t>(bh) * (nseg - 1) + seg - 1) * kSegFloats<D>);
 #pragma unroll
         for (int jb = 0; jb < JB; ++jb) {
@@ -508,9 +533,10 @@ __global__ __launch_bounds__(D * 4) void causal_seg_kernel(Problem p, CausalWork
     auto chunk = [&](const int c, const unsigned char *rb, unsigned char *rn) __attribute__((always_inline)) {
         const int t0 = c * kC;
         const int nval = min(kC, N - t0);
+        const bool has_prev = tin + t0 > 0;      // tokens before this chunk (a carried state)
         const float *co = reinterpret_cast<const float *>(rb + R::c_off);
         const float4 ch = *reinterpret_cast<const float4 *>(co + kCoChunk);   // rX, cHX, cHY, m1
-        if (t0 > 0 && rho < 0x1p-40f) {          // fold rho into Z (rare; the same on every lane)
+        if (has_prev && rho < 0x1p-40f) {        // fold rho into Z (rare; the same on every lane)
 #pragma unroll
             for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
@@ -519,12 +545,12 @@ __global__ __launch_bounds__(D * 4) void causal_seg_kernel(Problem p, CausalWork
         }
         // scalars of the basis after this chunk (the first chunk of the sequence starts from nothing
         // and keeps them)
-        const float rho1 = t0 > 0 ? rho * fmaxf(ch.x, 0x1p-40f) : rho;
-        const float alp1 = t0 > 0 ? ch.x * alp + ch.y : alp;
-        const float bet1 = t0 > 0 ? bet + ch.z : bet;
+        const float rho1 = has_prev ? rho * fmaxf(ch.x, 0x1p-40f) : rho;
+        const float alp1 = has_prev ? ch.x * alp + ch.y : alp;
+        const float bet1 = has_prev ? bet + ch.z : bet;
         const float irho1 = 1.f / rho1;
-        const float hz = t0 > 0 ? ch.y * irho1 : 0.f;   // Z += hz H
-        const float hy = t0 > 0 ? ch.z : 0.f;           // Y += hy H
+        const float hz = has_prev ? ch.y * irho1 : 0.f;   // Z += hz H
+        const float hy = has_prev ? ch.z : 0.f;           // Y += hy H
 
         // ---- stage this wave's v tile (token pairs per column) and the update operands
         // v w_X / rho1 and v w_Y
@@ -580,7 +606,7 @@ __global__ __launch_bounds__(D * 4) void causal_seg_kernel(Problem p, CausalWork
         for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) ax[tb][i] = ay[tb][i] = ah[tb][i] = 0.f;
-        const bool carried = !PASS1 && t0 > 0;
+        const bool carried = !PASS1 && has_prev;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             if (carried) {
@@ -617,7 +643,7 @@ __global__ __launch_bounds__(D * 4) void causal_seg_kernel(Problem p, CausalWork
         }
         if (PASS1) {
             // the first chunk of the sequence starts from nothing
-            Rs = t0 > 0 ? ch.x * Rs : 0.f;
+            Rs = has_prev ? ch.x * Rs : 0.f;
         } else {
             // ---- outputs: coefficients on the carried-state products, plus V^T W^T (intra-chunk)
 #pragma unroll
@@ -683,7 +709,7 @@ __global__ __launch_bounds__(D * 4) void causal_seg_kernel(Problem p, CausalWork
             P0 = co[kCoChunk + 5];
         }
         const size_t mat0 = static_cast<size_t>(bh) * D * D;
-        const float tf = static_cast<float>(N);
+        const float tf = static_cast<float>(tin + N);
 #pragma unroll
         for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
@@ -697,7 +723,7 @@ __global__ __launch_bounds__(D * 4) void causal_seg_kernel(Problem p, CausalWork
             }
         const int nls = (N + kLogitSeg - 1) / kLogitSeg;
         if (tid < D) {
-            float su = 0.f;
+            float su = cont ? p.sin.Su[static_cast<size_t>(bh) * D + tid] : 0.f;
             for (int sg = 0; sg < nls; ++sg) su += work.useg[(static_cast<size_t>(bh) * nls + sg) * D + tid];
             p.st.Su[static_cast<size_t>(bh) * D + tid] = su;
         }
@@ -705,15 +731,16 @@ __global__ __launch_bounds__(D * 4) void causal_seg_kernel(Problem p, CausalWork
             p.st.m[bh] = m0;
             p.st.E[bh] = E0;
             p.st.P[bh] = P0;
-            p.st.t[bh] = N;
+            p.st.t[bh] = tin + N;
         }
     }
 }
 
 // Start states of segments 1 .. nseg-1 (in place over the segment-local sums), one float4 position
-// of the three state matrices per thread: S_{j+1} = M_j S_j + L_j with S_0 = 0.
+// of the three state matrices per thread: S_{j+1} = M_j S_j + L_j with S_0 = 0, or the given state
+// in the centred basis for a continued sequence.
 template <int D>
-__global__ __launch_bounds__(256) void causal_seg_combine_kernel(CausalWork work) {
+__global__ __launch_bounds__(256) void causal_seg_combine_kernel(Problem p, CausalWork work) {
     constexpr size_t Q = size_t(D) * D / 4;              // float4 positions per state matrix
     constexpr int kMaxSeg = 8;                           // segment-local sums loaded up front
     const size_t pos = static_cast<size_t>(blockIdx.y) * 256 + threadIdx.x;
@@ -721,6 +748,27 @@ __global__ __launch_bounds__(256) void causal_seg_combine_kernel(CausalWork work
     const int bh = blockIdx.x;
     const int nseg = work.nseg;
     float4 x = make_float4(0.f, 0.f, 0.f, 0.f), y = x, h = x;
+    const int tin = p.sin.F != nullptr ? p.sin.t[bh] : 0;
+    if (tin > 0) {
+        // float4 position pos of a segment state holds rows 16 jb + 4 g4 + [0, 4) of column
+        // 16 w + l16, with pos = (jb (d/16) + w) 64 + 16 g4 + l16 (the scan kernel's register order)
+        constexpr int NW = D / 16;
+        const int jb = static_cast<int>(pos / (NW * 64)), rem = static_cast<int>(pos % (NW * 64));
+        const int col = 16 * (rem / 64) + (rem & 15), row = 16 * jb + 4 * ((rem & 63) >> 4);
+        const size_t base = static_cast<size_t>(bh) * D * D + static_cast<size_t>(row) * D + col;
+        const float iE = 1.f / p.sin.E[bh], it = 1.f / static_cast<float>(tin);
+        const float pt = p.sin.P[bh] * it;
+        float xs[4], ys[4], hs[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            hs[i] = p.sin.Hs[base + static_cast<size_t>(i) * D];
+            xs[i] = p.sin.F[base + static_cast<size_t>(i) * D] * iE - hs[i] * it;
+            ys[i] = p.sin.G[base + static_cast<size_t>(i) * D] - pt * hs[i];
+        }
+        x = make_float4(xs[0], xs[1], xs[2], xs[3]);
+        y = make_float4(ys[0], ys[1], ys[2], ys[3]);
+        h = make_float4(hs[0], hs[1], hs[2], hs[3]);
+    }
     for (int j0 = 0; j0 + 1 < nseg; j0 += kMaxSeg) {
         const int nj = min(kMaxSeg, nseg - 1 - j0);
         float4 lx[kMaxSeg], ly[kMaxSeg], lh[kMaxSeg];
@@ -786,7 +834,7 @@ hipError_t launch_one(const Problem &p, const CausalWork &w, hipStream_t stream)
                            stream, p, w);
         if ((err = hipGetLastError()) != hipSuccess) return err;
         hipLaunchKernelGGL((causal_seg_combine_kernel<D>), dim3(bh, (D * D / 4 + 255) / 256), dim3(256), 0,
-                           stream, w);
+                           stream, p, w);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     hipLaunchKernelGGL((causal_seg_kernel<D, ROPE, false>), dim3(bh * w.nseg), dim3(D * 4), 0, stream, p, w);

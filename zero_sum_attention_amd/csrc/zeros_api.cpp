@@ -190,7 +190,8 @@ zeros_status zeros_fwd_causal(const zeros_shape *shape, const void *q, const voi
     zeros::Problem p = make_problem(shape, q, k, v, u, mu, tau, g1, gh, g0, o, state_out);
     if (state_in) p.sin = *state_in;
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    const bool mfma = !state_in && causal_uses_mfma(shape);
+    // a continued empty call (a copy of the state) takes the float32 path
+    const bool mfma = causal_uses_mfma(shape) && !(state_in && shape->N == 0);
     const size_t need = mfma ? zeros::causal_work_bytes(shape->B, shape->H, shape->N, shape->d_u)
                              : zeros::causal_valu_work_bytes(shape->B, shape->H, shape->N, shape->d_u);
     void *ws = workspace;

@@ -91,8 +91,9 @@ def cpu_baseline(x):
 def secondary(dev, steps: int = 20) -> list:
     """The other hot-path calls at their workload sizes: the float32 LM-layer causal forward, the
     ViT-shaped encoder forward, one decode step of 256 sequences x 32 heads at t = 8192 (state
-    values are random: the step's work does not depend on them) and the long causal forward with
-    the zero-order gate. Each is timed with HIP events on the launch stream."""
+    values are random: the step's work does not depend on them), the long causal forward with
+    the zero-order gate, and the same sequence as four chained calls of a quarter each (chunked
+    prefill through state_in / state_out). Each is timed with HIP events on the launch stream."""
     import torch
 
     import zero_sum_attention_amd as Z
@@ -184,7 +185,31 @@ def secondary(dev, steps: int = 20) -> list:
     out.append({"workload": wl.name + "-gate0", "call": "zeros_fwd_causal (g0 given)", "ms": ms,
                 "tokens_per_s": wl.B * wl.N / (ms * 1e-3), "algorithmic_bytes": nbytes,
                 "achieved_GBs": nbytes / (ms * 1e-3) / 1e9, "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS})
-    del t, o, ws, x
+    # chunked prefill: the same sequence as four calls of N/4 tokens, each continuing from the
+    # previous call's state (two states alternate)
+    parts = 4
+    n_part = wl.N // parts
+    chunks = [{k: (v[:, :, i * n_part:(i + 1) * n_part].contiguous() if v.dim() >= 3 else v)
+               for k, v in t.items() if k != "g0"} for i in range(parts)]
+    del t
+    sts = [Z.DecodeState(wl.B, wl.H, wl.d, wl.d_u, device=dev) for _ in range(2)]
+    o_part = torch.empty_like(chunks[0]["v"])
+    ws_part = torch.empty(Z.zeros_fwd_causal_workspace_bytes(wl.B, wl.H, n_part, wl.d, wl.d_u, torch.bfloat16,
+                                                             wl.rope), dtype=torch.uint8, device=dev)
+
+    def prefill(st_):
+        for i, c in enumerate(chunks):
+            Z.zeros_fwd_causal(c["q"], c["k"], c["v"], c["u"], c["mu"], c["tau"], c["g1"], c["gh"],
+                               rope=wl.rope, rope_base=wl.rope_base, out=o_part,
+                               state_in=sts[(i + 1) % 2] if i > 0 else None, state_out=sts[i % 2],
+                               workspace=ws_part, stream=st_)
+
+    ms = timed(prefill)
+    nbytes = algorithmic_bytes(wl)
+    out.append({"workload": wl.name + "-chunked4", "call": f"zeros_fwd_causal x {parts} (state_in -> state_out)",
+                "ms": ms, "tokens_per_s": wl.B * wl.N / (ms * 1e-3), "algorithmic_bytes": nbytes,
+                "achieved_GBs": nbytes / (ms * 1e-3) / 1e9, "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS})
+    del o, ws, x, chunks, sts, o_part, ws_part
     return out
 
 

@@ -243,3 +243,14 @@ def test_state_bytes_and_packing(lib):
     assert fields == sorted(fields)
     assert st.t + n * 4 <= base + expect
     assert lib.zeros_state_from_buffer(None, S, H, d, du, ctypes.byref(st)) == L.ZEROS_ERR_NULL
+
+
+def test_binding_arity_matches_header(lib):
+    """The ctypes declarations of the binding take as many arguments as the header declares."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    for name in ("zeros_fwd_causal", "zeros_fwd_encoder", "zeros_decode_step",
+                 "zeros_fwd_causal_workspace_bytes", "zeros_state_bytes", "zeros_state_from_buffer"):
+        m = re.search(r"\b%s\s*\(([^)]*)\)\s*;" % name, text)
+        assert m, name
+        params = [p for p in m.group(1).split(",") if p.strip() and p.strip() != "void"]
+        assert len(getattr(lib, name).argtypes) == len(params), name

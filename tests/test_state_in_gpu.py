@@ -119,3 +119,21 @@ def test_continuation_empty_call_copies_state():
     torch.cuda.synchronize()
     for name in ("F", "G", "Hs", "Su", "m", "E", "P", "t"):
         assert torch.equal(getattr(a, name), getattr(b, name)), name
+
+
+@pytest.mark.parametrize("d,dtype", [(16, "f32"), (128, "bf16")])
+def test_continuation_from_empty_state(d, dtype):
+    """state_in at t = 0 (a reset state) gives the plain forward and its final state."""
+    wl = CONFIGS[2].with_(B=2, H=2, N=150, d=d, d_u=d, dtype=dtype, seed=6400 + d)
+    x = make_inputs(wl)
+    t = to_device(x, dtype)
+    a = Z.DecodeState(2, 2, d, d).reset()
+    b = Z.DecodeState(2, 2, d, d).reset()
+    o = to_f64(_causal(t, True, state_in=a, state_out=b))
+    ref, st = R.causal_forward(**x, rope=True, return_state=True)
+    assert rel_l2(o, ref) <= TOL[dtype]
+    got = _state_np(b)
+    assert np.all(got["t"] == 150)
+    bar = 1e-5 if dtype == "f32" else 2e-2
+    for key in ("m", "E", "P", "Su", "F", "G", "H"):
+        assert rel_l2(got[key], st[key]) <= bar, key

@@ -336,7 +336,7 @@ def main():
         torch.cuda.empty_cache()
         out["secondary"] = secondary(dev)
     out["notes"] = {"pages_quote_no_hardware_timings": True, "input_gen_s": round(t_gen, 2),
-                    "hbm_peak_note": "peak is the published 8 TB/s; a 1 GiB device copy reaches 5.0 TB/s on the box"}
+                    "hbm_peak_note": "peak is the published 8 TB/s; a 1 GiB device copy reaches 5.0 TB/s on the same MI355X"}
     print(json.dumps(out), flush=True)
 
 

@@ -371,3 +371,30 @@ def test_zero_order_gate_decode_continues_forward():
     o_step, _ = R.decode_step(st, tok["q"], tok["k"], tok["v"], tok["u"], x["mu"], x["tau"],
                               tok["g1"], tok["gh"], g0=g0[..., 32])
     assert rel(o_step, o_full[..., 32, :]) < TOL
+
+
+@pytest.mark.parametrize("cut", [1, 17, 32])
+def test_causal_forward_continues_from_state(cut):
+    """causal_forward(state=...) over the rest of a sequence equals one pass over all of it, for
+    the outputs and the final state (the continuation contract of the library's state_in)."""
+    x = small_inputs(2, 2, 41, 16, 16, seed=45)
+    g0 = _gate0(x, 4)
+    o_full, st_full = R.causal_forward(**x, rope=True, g0=g0, return_state=True)
+    head = {k: (v[..., :cut, :] if v.ndim == 4 else v[..., :cut] if v.ndim == 3 else v) for k, v in x.items()}
+    tail = {k: (v[..., cut:, :] if v.ndim == 4 else v[..., cut:] if v.ndim == 3 else v) for k, v in x.items()}
+    o1, st = R.causal_forward(**head, rope=True, g0=g0[..., :cut], return_state=True)
+    o2, st2 = R.causal_forward(**tail, rope=True, g0=g0[..., cut:], state=st, return_state=True)
+    assert rel(np.concatenate([o1, o2], axis=-2), o_full) < TOL
+    for key in ("m", "E", "P", "Su", "F", "G", "H"):
+        assert rel(st2[key], st_full[key]) < TOL, key
+    assert np.all(st2["t"] == 41)
+
+
+def test_zero_order_gate_first_token():
+    """At t = 1 the zero-sum part vanishes and o_1 = sigma0_1 (q^_1 . k^_1) v_1."""
+    x = small_inputs(2, 2, 1, 8, 8, seed=46)
+    g0 = _gate0(x, 5)
+    o = R.causal_forward(**x, g0=g0)
+    sig0 = 1.0 / (1.0 + np.exp(-g0))
+    ref = sig0[..., None] * _cos(x)[..., 0, 0][..., None, None] * x["v"].astype(float)
+    assert rel(o, ref) < TOL

@@ -137,3 +137,31 @@ def test_continuation_from_empty_state(d, dtype):
     bar = 1e-5 if dtype == "f32" else 2e-2
     for key in ("m", "E", "P", "Su", "F", "G", "H"):
         assert rel_l2(got[key], st[key]) <= bar, key
+
+
+# ------------------------------------------------------------------ segmented float32 scan
+
+@pytest.mark.parametrize("d,N,dtype,B,H", [(64, 1000, "f32", 1, 2), (16, 777, "f32", 2, 1), (128, 700, "f32", 1, 1),
+                                           (32, 900, "bf16", 1, 2)])
+@pytest.mark.parametrize("rope", [False, True])
+def test_float32_path_segments(d, N, dtype, B, H, rope):
+    """Sequences long enough for the float32 path to split each head into scan segments (pass 1,
+    combine, main): outputs and final state against the oracle; the same again continued from a
+    state after 320 tokens."""
+    wl = CONFIGS[2].with_(B=B, H=H, N=N, d=d, d_u=d, dtype=dtype, seed=6500 + d + N)
+    x = make_inputs(wl, gate0=(d == 16))
+    t = to_device(x, dtype)
+    st = Z.DecodeState(B, H, d, d).reset()
+    o = to_f64(_causal(t, rope, state_out=st))
+    ref, sref = R.causal_forward(**x, rope=rope, return_state=True)
+    err = rel_l2(o, ref)
+    print(f"segmented float32 path d={d} N={N} rel_l2={err:.3e}", flush=True)
+    assert err <= TOL[dtype]
+    got = _state_np(st)
+    bar = 1e-5 if dtype == "f32" else 2e-2
+    for key in ("m", "E", "P", "Su", "F", "G", "H"):
+        assert rel_l2(got[key], sref[key]) <= bar, key
+    a = Z.DecodeState(B, H, d, d).reset()
+    _causal(_part(t, 0, 320), rope, state_out=a)
+    o2 = to_f64(_causal(_part(t, 320, N), rope, state_in=a))
+    assert rel_l2(o2, ref[:, :, 320:]) <= TOL[dtype]

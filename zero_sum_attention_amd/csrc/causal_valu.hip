@@ -49,8 +49,12 @@ struct CausalSmem {
 template <typename T>
 __device__ __forceinline__ float ld(const T *p, size_t i) { return to_f32(p[i]); }
 
+// One launch runs either pass 1 (pass1 = 1: segments 0 .. nseg-2 from a zero state, writing their
+// local sums and the logit maximum at their end, no outputs) or the main pass (every segment from
+// its start state: outputs, and the final state in the last segment). With nseg = 1 the main pass
+// is the whole sequence.
 template <int D, typename T, bool ROPE>
-__global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p, const float *s_all, const float *useg, int nls) {
+__global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p, ValuWork w, int nls, int pass1) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     CausalSmem<D> &sm = *reinterpret_cast<CausalSmem<D> *>(smem_raw);
     constexpr int NTILE = D / kTile;
@@ -62,9 +66,13 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p, const 
     const int G = gridDim.x;
     int L = blockIdx.x;
     if ((G & 7) == 0) L = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+    const int nsg = pass1 ? w.nseg - 1 : w.nseg;   // segments this launch covers
     const int tile = L % NTILE;
-    const int bh = L / NTILE;
+    const int seg = (L / NTILE) % nsg;
+    const int bh = (L / NTILE) / nsg;
     const int N = p.N;
+    const int t_beg = seg * w.seg_chunks * kC, t_end = min(N, (seg + 1) * w.seg_chunks * kC);
+    const float *useg = w.useg;
     const size_t row0 = static_cast<size_t>(bh) * N;
     const T *q = static_cast<const T *>(p.q) + row0 * D;
     const T *k = static_cast<const T *>(p.k) + row0 * D;
@@ -74,7 +82,7 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p, const 
     const T *g0 = p.g0 != nullptr ? static_cast<const T *>(p.g0) + row0 : nullptr;
     T *o = static_cast<T *>(p.o) + row0 * D;
 
-    const float *srow = s_all + row0;
+    const float *srow = w.s + row0;
     // a continued sequence starts from the given state: its tokens are positions tin + 1 ...
     const bool cont = p.sin.F != nullptr;
     const int tin = cont ? p.sin.t[bh] : 0;
@@ -87,13 +95,62 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p, const 
     }
 
     float m_c = cont ? p.sin.m[bh] : kNegInf, E_c = cont ? p.sin.E[bh] : 0.f, P_c = cont ? p.sin.P[bh] : 0.f;
+    if (seg > 0) {
+        // logit carry at the segment start: the state's plus the aggregates of the 64-token blocks
+        // before it (segments start on block boundaries)
+        if (tid < 64) {
+            float m = tid == 0 ? m_c : kNegInf, e = tid == 0 ? E_c : 0.f, ps = tid == 0 ? P_c : 0.f;
+            auto merge = [](float &ma, float &ea, const float mb, const float eb) {
+                const float mx = fmaxf(ma, mb);
+                ea = exp_diff(ma, mx) * ea + exp_diff(mb, mx) * eb;
+                ma = mx;
+            };
+            const float4 *ag = w.agg + static_cast<size_t>(bh) * ((N + 63) / 64);
+            for (int j = tid; j < t_beg / 64; j += 64) {
+                const float4 a = ag[j];
+                merge(m, e, a.x, a.y);
+                ps += a.z;
+            }
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float m2 = __shfl_xor(m, off, 64), e2 = __shfl_xor(e, off, 64);
+                ps += __shfl_xor(ps, off, 64);
+                merge(m, e, m2, e2);
+            }
+            if (tid == 0) {
+                sm.carry[0] = m;
+                sm.carry[1] = e;
+                sm.carry[2] = ps;
+            }
+        }
+        __syncthreads();
+        m_c = sm.carry[0];
+        E_c = sm.carry[1];
+        P_c = sm.carry[2];
+        __syncthreads();          // sm.carry is written again by the first chunk's scan
+    }
 
+    // start state: the given one (first segment), the combined start state (later segments of the
+    // main pass) or zero (pass 1)
     const size_t mat0 = static_cast<size_t>(bh) * D * D;
+    const float *S0F = nullptr, *S0G = nullptr, *S0H = nullptr;
+    size_t s0base = mat0;
+    if (!pass1 && seg > 0) {
+        const float *st = w.segst + (static_cast<size_t>(bh) * (w.nseg - 1) + seg - 1) * 3 * D * D;
+        S0F = st;
+        S0G = st + D * D;
+        S0H = st + 2 * D * D;
+        s0base = 0;
+    } else if (!pass1 && cont) {
+        S0F = p.sin.F;
+        S0G = p.sin.G;
+        S0H = p.sin.Hs;
+    }
     for (int x = tid; x < D * kTile; x += kThreads) {
-        const size_t idx = mat0 + static_cast<size_t>(x / kTile) * D + tile * kTile + x % kTile;
-        (&sm.F[0][0])[x] = cont ? p.sin.F[idx] : 0.f;
-        (&sm.G[0][0])[x] = cont ? p.sin.G[idx] : 0.f;
-        (&sm.Hs[0][0])[x] = cont ? p.sin.Hs[idx] : 0.f;
+        const size_t idx = s0base + static_cast<size_t>(x / kTile) * D + tile * kTile + x % kTile;
+        (&sm.F[0][0])[x] = S0F != nullptr ? S0F[idx] : 0.f;
+        (&sm.G[0][0])[x] = S0F != nullptr ? S0G[idx] : 0.f;
+        (&sm.Hs[0][0])[x] = S0F != nullptr ? S0H[idx] : 0.f;
     }
 
     // the rows of the next chunk are read while the current one is processed; a thread takes rows
@@ -123,9 +180,9 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p, const 
             ns = srow[min(t0 + tid, N - 1)];
         }
     };
-    if (N > 0) prefetch(0);
+    if (t_beg < t_end) prefetch(t_beg);
 
-    for (int t0 = 0; t0 < N; t0 += kC) {
+    for (int t0 = t_beg; t0 < t_end; t0 += kC) {
         const int nval = min(kC, N - t0);
 
         // ---- normalise, rotate and stage the rows read ahead; read the next chunk's rows
@@ -185,7 +242,7 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p, const 
             sm.sig0[tid] = (valid && g0 != nullptr) ? sigmoidf(ng0) : 0.f;
             sm.s[tid] = valid ? ns : 0.f;
         }
-        if (t0 + kC < N) prefetch(t0 + kC);
+        if (t0 + kC < t_end) prefetch(t0 + kC);
         __syncthreads();
 
         // ---- scans of (max, sum e^{s-max}, sum s) over the chunk, joined with the carry
@@ -243,6 +300,9 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p, const 
         __syncthreads();
         const float m_new = sm.carry[0];
         if (tid < kC) sm.estate[tid] = (tid < nval) ? expf(sm.s[tid] - m_new) : 0.f;
+        if (pass1) {
+            __syncthreads();      // key weights visible to the fold; pass 1 forms no outputs
+        } else {
 
         // ---- intra-chunk weights W_{t,i} (i <= t): A^T = K Q^T on the float32 matrix cores, the 16x16
         // tiles (key tile kt, query tile qt) taken by the waves in turn (A[key][f] = k^[key][f],
@@ -322,6 +382,7 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p, const 
         // (no barrier: the fold reads the staged rows and writes F, G, H, which the output products
         // finished reading before the barrier above; the products in LDS are not touched again
         // before the barrier at the end of the chunk)
+        }
 
         // ---- fold the chunk's keys into the states on the float32 matrix cores (exact float32
         // products, float32 sums): wave w owns 16-row tiles rt = w, w + 4, ... of F, G, H.
@@ -363,8 +424,21 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p, const 
         __syncthreads();
     }
 
+    if (pass1) {
+        // segment-local sums (F relative to the logit maximum at the segment end) for the combine
+        float *dst = w.segst + (static_cast<size_t>(bh) * (w.nseg - 1) + seg) * 3 * D * D;
+        for (int x = tid; x < D * kTile; x += kThreads) {
+            const size_t idx = static_cast<size_t>(x / kTile) * D + tile * kTile + x % kTile;
+            dst[idx] = (&sm.F[0][0])[x];
+            dst[D * D + idx] = (&sm.G[0][0])[x];
+            dst[2 * D * D + idx] = (&sm.Hs[0][0])[x];
+        }
+        if (tile == 0 && tid == 0) w.segm[static_cast<size_t>(bh) * w.nseg + seg] = m_c;
+        return;
+    }
+
     // ---- final state
-    if (p.st.F != nullptr) {
+    if (p.st.F != nullptr && seg == w.nseg - 1) {
         for (int x = tid; x < D * kTile; x += kThreads) {
             const int j = x / kTile, mm = x % kTile;
             const size_t idx = mat0 + static_cast<size_t>(j) * D + tile * kTile + mm;
@@ -388,6 +462,31 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p, const 
     }
 }
 
+// Start states of segments 1 .. nseg-1, one element of the d x d matrices per thread, in place over
+// the segment-local sums: F <- e^{m_prev - m_end} F + L_F, G <- G + L_G, H <- H + L_H per segment,
+// from the given state (continued sequence) or zero.
+template <int D>
+__global__ __launch_bounds__(256) void causal_valu_combine_kernel(Problem p, ValuWork w) {
+    const int x = blockIdx.y * 256 + threadIdx.x;
+    if (x >= D * D) return;
+    const int bh = blockIdx.x;
+    const bool cont = p.sin.F != nullptr;
+    const size_t e = static_cast<size_t>(bh) * D * D + x;
+    float f = cont ? p.sin.F[e] : 0.f, g = cont ? p.sin.G[e] : 0.f, h = cont ? p.sin.Hs[e] : 0.f;
+    float m = cont ? p.sin.m[bh] : kNegInf;
+    for (int j = 0; j + 1 < w.nseg; ++j) {
+        float *st = w.segst + (static_cast<size_t>(bh) * (w.nseg - 1) + j) * 3 * D * D;
+        const float m1 = w.segm[static_cast<size_t>(bh) * w.nseg + j];
+        f = exp_diff(m, m1) * f + st[x];
+        g += st[D * D + x];
+        h += st[2 * D * D + x];
+        st[x] = f;
+        st[D * D + x] = g;
+        st[2 * D * D + x] = h;
+        m = m1;
+    }
+}
+
 template <int D, typename T, bool ROPE>
 hipError_t launch_one(const Problem &p, const ValuWork &w, hipStream_t stream) {
     const size_t smem = sizeof(CausalSmem<D>);
@@ -397,8 +496,16 @@ hipError_t launch_one(const Problem &p, const ValuWork &w, hipStream_t stream) {
     if (err != hipSuccess) return err;
     const int grid = p.B * p.H * (D / kTile);
     const int nls = (p.N + kLogitSeg - 1) / kLogitSeg;
-    hipLaunchKernelGGL((causal_valu_kernel<D, T, ROPE>), dim3(grid), dim3(kThreads), smem, stream, p, w.s, w.useg,
-                       nls);
+    if (w.nseg > 1) {
+        hipLaunchKernelGGL((causal_valu_kernel<D, T, ROPE>), dim3(grid * (w.nseg - 1)), dim3(kThreads), smem,
+                           stream, p, w, nls, 1);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        hipLaunchKernelGGL((causal_valu_combine_kernel<D>), dim3(p.B * p.H, (D * D + 255) / 256), dim3(256), 0,
+                           stream, p, w);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    hipLaunchKernelGGL((causal_valu_kernel<D, T, ROPE>), dim3(grid * w.nseg), dim3(kThreads), smem, stream, p, w,
+                       nls, 0);
     return hipGetLastError();
 }
 
@@ -412,27 +519,55 @@ hipError_t launch_d(const Problem &p, const ValuWork &w, hipStream_t stream) {
 // workspace regions start on 256-byte boundaries
 size_t up256(size_t x) { return (x + 255) / 256 * 256; }
 
+// Segments of the scan: whole 64-token blocks (an even number of chunks), at least four chunks
+// each, and enough (head, tile, segment) workgroups for one per CU. (A grid that already fills
+// the chip is left whole: its chunk work is bound by the CUs' throughput, and three workgroups
+// per CU measured no faster than one.)
+void valu_seg_plan(int B, int H, int N, int d, int &nseg, int &seg_chunks) {
+    const int nch = (N + kC - 1) / kC;
+    const long wg = static_cast<long>(B) * H * (d / kTile);
+    long want = (256 + wg - 1) / wg;
+    if (want > nch / 4) want = nch / 4;
+    if (want < 1) want = 1;
+    seg_chunks = static_cast<int>((nch + want - 1) / want);
+    seg_chunks += seg_chunks & 1;
+    nseg = nch > 0 ? (nch + seg_chunks - 1) / seg_chunks : 1;
+}
+
 }  // namespace
 
 // Workspace of the float32 / small-d causal path: logits [B H, N], u sums per logit segment
-// [B H, nls, d_u], per-64-token logit aggregates [B H, ceil(N/64)] (written by the logits kernels).
+// [B H, nls, d_u], per-64-token logit aggregates [B H, ceil(N/64)] (written by the logits kernels),
+// and for a segmented scan the segment states [B H, nseg-1, 3, d, d] and maxima [B H, nseg].
 size_t causal_valu_work_bytes(int B, int H, int N, int du) {
     const size_t bh = static_cast<size_t>(B) * H;
     const size_t nls = (static_cast<size_t>(N) + kLogitSeg - 1) / kLogitSeg;
     const size_t n64 = (static_cast<size_t>(N) + 63) / 64;
-    return up256(bh * N * 4) + up256(bh * nls * du * 4) + up256(bh * n64 * 16);
+    int nseg, seg_chunks;
+    valu_seg_plan(B, H, N, du, nseg, seg_chunks);
+    size_t b = up256(bh * N * 4) + up256(bh * nls * du * 4) + up256(bh * n64 * 16);
+    if (nseg > 1) b += up256(bh * (nseg - 1) * size_t(3) * du * du * 4) + up256(bh * nseg * 4);
+    return b;
 }
 
 ValuWork causal_valu_work_carve(void *base, int B, int H, int N, int du) {
     const size_t bh = static_cast<size_t>(B) * H;
     const size_t nls = (static_cast<size_t>(N) + kLogitSeg - 1) / kLogitSeg;
+    const size_t n64 = (static_cast<size_t>(N) + 63) / 64;
     char *b = static_cast<char *>(base);
-    ValuWork w;
+    ValuWork w{};
+    valu_seg_plan(B, H, N, du, w.nseg, w.seg_chunks);
     w.s = reinterpret_cast<float *>(b);
     b += up256(bh * N * 4);
     w.useg = reinterpret_cast<float *>(b);
     b += up256(bh * nls * du * 4);
     w.agg = reinterpret_cast<float4 *>(b);
+    b += up256(bh * n64 * 16);
+    if (w.nseg > 1) {
+        w.segst = reinterpret_cast<float *>(b);
+        b += up256(bh * (w.nseg - 1) * size_t(3) * du * du * 4);
+        w.segm = reinterpret_cast<float *>(b);
+    }
     return w;
 }
 

@@ -47,7 +47,11 @@ CausalWork causal_work_carve(void *base, int B, int H, int N, int du);
 struct ValuWork {
     float *s;           // [B*H, N] logits
     float *useg;        // [B*H, ceil(N/kLogitSeg), d_u] u sums per logit segment
-    float4 *agg;        // [B*H, ceil(N/64)] per-64-token logit aggregates (written, not read)
+    float4 *agg;        // [B*H, ceil(N/64)] per-64-token logit aggregates (segment start carries)
+    float *segst;       // [B*H, nseg-1, 3, d, d] segment-local F, G, H, then segment start states
+    float *segm;        // [B*H, nseg] running logit maximum at the end of each segment
+    int nseg;           // scan segments per head (1: a single pass)
+    int seg_chunks;     // 32-token chunks per segment (even: segments start on 64-token blocks)
 };
 size_t causal_valu_work_bytes(int B, int H, int N, int du);
 ValuWork causal_valu_work_carve(void *base, int B, int H, int N, int du);

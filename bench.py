@@ -89,8 +89,8 @@ def cpu_baseline(x):
 
 
 def secondary(dev, steps: int = 20) -> list:
-    """The other hot-path calls at their workload sizes: the float32 LM-layer causal forward, the
-    ViT-shaped encoder forward, one decode step of 256 sequences x 32 heads at t = 8192 (state
+    """The other hot-path calls at their workload sizes: the float32 LM-layer causal forward, a long
+    float32 sequence on two heads (segmented scan), the ViT-shaped encoder forward, one decode step of 256 sequences x 32 heads at t = 8192 (state
     values are random: the step's work does not depend on them), the long causal forward with
     the zero-order gate, and the same sequence as four chained calls of a quarter each (chunked
     prefill through state_in / state_out). Each is timed with HIP events on the launch stream."""
@@ -129,6 +129,22 @@ def secondary(dev, steps: int = 20) -> list:
                 "achieved_TFLOPs": flops / (ms * 1e-3) / 1e12,
                 "frac_fp32_vector": flops / (ms * 1e-3) / 1e12 / FP32_PEAK_TFLOPS})
     del t, o
+
+    # a long float32 sequence on few heads: the float32 path's segmented scan
+    wl = CONFIGS[2].with_(B=1, H=2, N=8192, seed=21)
+    x = make_inputs(wl)
+    t = {k: torch.from_numpy(v).to(device=dev, dtype=torch.float32) for k, v in x.items()}
+    o = torch.empty_like(t["v"])
+    ws = torch.empty(Z.zeros_fwd_causal_workspace_bytes(wl.B, wl.H, wl.N, wl.d, wl.d_u, torch.float32),
+                     dtype=torch.uint8, device=dev)
+    ms = timed(lambda st: Z.zeros_fwd_causal(t["q"], t["k"], t["v"], t["u"], t["mu"], t["tau"], t["g1"],
+                                             t["gh"], out=o, workspace=ws, stream=st))
+    flops = 12 * wl.d * wl.d * wl.B * wl.H * wl.N
+    out.append({"workload": "long-f32-causal-B1H2N8192d64", "call": "zeros_fwd_causal", "dtype": "f32", "ms": ms,
+                "tokens_per_s": wl.B * wl.N / (ms * 1e-3), "algorithmic_flops": flops,
+                "achieved_TFLOPs": flops / (ms * 1e-3) / 1e12,
+                "frac_fp32_vector": flops / (ms * 1e-3) / 1e12 / FP32_PEAK_TFLOPS})
+    del t, o, ws, x
 
     wl = CONFIGS[3]
     x = make_inputs(wl)

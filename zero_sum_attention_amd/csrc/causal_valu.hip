@@ -474,16 +474,33 @@ __global__ __launch_bounds__(256) void causal_valu_combine_kernel(Problem p, Val
     const size_t e = static_cast<size_t>(bh) * D * D + x;
     float f = cont ? p.sin.F[e] : 0.f, g = cont ? p.sin.G[e] : 0.f, h = cont ? p.sin.Hs[e] : 0.f;
     float m = cont ? p.sin.m[bh] : kNegInf;
-    for (int j = 0; j + 1 < w.nseg; ++j) {
-        float *st = w.segst + (static_cast<size_t>(bh) * (w.nseg - 1) + j) * 3 * D * D;
-        const float m1 = w.segm[static_cast<size_t>(bh) * w.nseg + j];
-        f = exp_diff(m, m1) * f + st[x];
-        g += st[D * D + x];
-        h += st[2 * D * D + x];
-        st[x] = f;
-        st[D * D + x] = g;
-        st[2 * D * D + x] = h;
-        m = m1;
+    constexpr int kBatch = 8;               // segments whose sums are loaded together
+    for (int j0 = 0; j0 + 1 < w.nseg; j0 += kBatch) {
+        const int nj = min(kBatch, w.nseg - 1 - j0);
+        float lf[kBatch], lg[kBatch], lh[kBatch], lm[kBatch];
+#pragma unroll
+        for (int jj = 0; jj < kBatch; ++jj) {
+            if (jj < nj) {
+                const float *st = w.segst + (static_cast<size_t>(bh) * (w.nseg - 1) + j0 + jj) * 3 * D * D;
+                lf[jj] = st[x];
+                lg[jj] = st[D * D + x];
+                lh[jj] = st[2 * D * D + x];
+                lm[jj] = w.segm[static_cast<size_t>(bh) * w.nseg + j0 + jj];
+            }
+        }
+#pragma unroll
+        for (int jj = 0; jj < kBatch; ++jj) {
+            if (jj < nj) {
+                float *st = w.segst + (static_cast<size_t>(bh) * (w.nseg - 1) + j0 + jj) * 3 * D * D;
+                f = exp_diff(m, lm[jj]) * f + lf[jj];
+                g += lg[jj];
+                h += lh[jj];
+                st[x] = f;
+                st[D * D + x] = g;
+                st[2 * D * D + x] = h;
+                m = lm[jj];
+            }
+        }
     }
 }
 

@@ -7,9 +7,9 @@
 //   pass 1 (useg_sum_kernel): per (head, segment of kSeg tokens), the column sums of u;
 //   pass 2 (logits_stream_kernel for bfloat16 and d 64/128, logits_kernel otherwise): per
 //                             (head, segment), the running sum starts from e^tau mu plus the
-//                             sums of the earlier segments and gives ubar_i and s_i. A sequence
-//                             continued from a state takes logits_kernel, which also adds the
-//                             state's u-sum and token count.
+//                             sums of the earlier segments and gives ubar_i and s_i; for a
+//                             sequence continued from a state, both also add the state's u-sum
+//                             and token count.
 // Output: s [B*H, N] float32, the per-segment sums [B*H, nseg, d_u] (their total is the u-sum of
 // the recurrent state) and, per 64-token chunk, (max s, sum e^{s - max}, sum s) [B*H, nchunk, 4].
 #include "device_common.hpp"
@@ -192,7 +192,8 @@ constexpr int kStreamThreads = 256;
 template <int D>
 __global__ __launch_bounds__(kStreamThreads, 4) void logits_stream_kernel(const bf16 *u, const float *mu, const float *tau,
                                                                  const float *useg, float *s_out, float4 *agg,
-                                                                 int N, int H, int nseg) {
+                                                                 int N, int H, int nseg, const float *su_in,
+                                                                 const int *t_in) {
     constexpr int LPT = D / 8;                 // lanes per token row
     constexpr int NS = kStreamThreads / LPT;   // streams
     constexpr int TPS = kLogitSeg / NS;        // tokens per stream
@@ -208,11 +209,13 @@ __global__ __launch_bounds__(kStreamThreads, 4) void logits_stream_kernel(const 
     const int st = tid / LPT, fg = tid % LPT, l = lane % LPT;
     const float et = expf(tau[h]);
     {
-        // prior plus the sums of u over the earlier segments: thread (feature f, phase g) adds
-        // segments g, g + G, ..., eight loads in flight at a time
+        // prior (and the u-sum of a continued sequence's earlier tokens) plus the sums of u over
+        // the earlier segments: thread (feature f, phase g) adds segments g, g + G, ..., eight
+        // loads in flight at a time
         const int f = tid % D, g = tid / D;
         const float *us = useg + static_cast<size_t>(bh) * nseg * D + f;
-        float a[8] = {g == 0 ? et * mu[h * D + f] : 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        const float pri = et * mu[h * D + f] + (su_in != nullptr ? su_in[static_cast<size_t>(bh) * D + f] : 0.f);
+        float a[8] = {g == 0 ? pri : 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         for (int q0 = g; q0 < seg; q0 += 8 * G) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -306,7 +309,9 @@ __global__ __launch_bounds__(kStreamThreads, 4) void logits_stream_kernel(const 
     if (c0 < N) {
         const int row = c0 + lane;
         const bool valid = row < N;
-        const float s = -d[0] * (1.f / sqrtf(static_cast<float>(D))) / (et + static_cast<float>(row + 1));
+        // (tokens of a continued sequence are positions t_in + 1 ...; read here, where it is used)
+        const float tprev = t_in != nullptr ? static_cast<float>(t_in[bh]) : 0.f;
+        const float s = -d[0] * (1.f / sqrtf(static_cast<float>(D))) / (et + tprev + static_cast<float>(row + 1));
         if (valid) s_out[static_cast<size_t>(bh) * N + row] = s;
         const float mx = lane_f(wave_scan_max(valid ? s : kNegInf), 63);
         const float se = lane_f(wave_scan_add(valid ? __expf(s - mx) : 0.f), 63);
@@ -323,13 +328,12 @@ hipError_t launch_t(const Problem &p, float *useg, float *s_out, float4 *agg, fl
                        static_cast<const T *>(p.u), useg, p.N, nseg, rope_tab, p.rope_base);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    // a continued sequence (state in) takes the generic kernel, which adds the earlier tokens
+    // (a continued sequence passes the state's u-sum and token count, which join the prior)
     if constexpr (sizeof(T) == 2 && (D == 64 || D == 128)) {
-        if (p.sin.Su == nullptr) {
-            hipLaunchKernelGGL((logits_stream_kernel<D>), dim3(grid), dim3(kStreamThreads), 0, stream,
-                               static_cast<const bf16 *>(p.u), p.mu, p.tau, useg, s_out, agg, p.N, p.H, nseg);
-            return hipGetLastError();
-        }
+        hipLaunchKernelGGL((logits_stream_kernel<D>), dim3(grid), dim3(kStreamThreads), 0, stream,
+                           static_cast<const bf16 *>(p.u), p.mu, p.tau, useg, s_out, agg, p.N, p.H, nseg,
+                           p.sin.Su, p.sin.t);
+        return hipGetLastError();
     }
     hipLaunchKernelGGL((logits_kernel<D, T>), dim3(grid), dim3(kThreads), 0, stream,
                        static_cast<const T *>(p.u), p.mu, p.tau, useg, s_out, agg, p.N, p.H, nseg,

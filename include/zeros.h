@@ -108,9 +108,9 @@ typedef struct {
  *   in place by alternating two states).
  * workspace (nullable): device scratch of at least zeros_fwd_causal_workspace_bytes(shape)
  *   bytes, 256-byte aligned, used only while the call's work runs on `stream` (it holds the
- *   logits s_i, per-segment u sums, per-64-token logit aggregates and, on the bfloat16
- *   d = 64/128 path, a per-64-token-chunk operand record and the scan's segment states, there
- *   in all roughly 2.6 times the bytes of q). When NULL and scratch is needed, the library takes it
+ *   logits s_i, per-segment u sums, per-64-token logit aggregates, the scan's segment states
+ *   when a head is split into segments, and on the bfloat16 d = 64/128 path a per-64-token-chunk
+ *   operand record, there in all roughly 2.6 times the bytes of q). When NULL and scratch is needed, the library takes it
  *   from the stream-ordered allocator (hipMallocAsync / hipFreeAsync on `stream`).
  *   A workspace smaller than required is ZEROS_ERR_SHAPE.
  */

@@ -134,10 +134,14 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(const T *u, const floa
     const float et = expf(tau[h]);
     const float tprev = t_in != nullptr ? static_cast<float>(t_in[bh]) : 0.f;
     if (tid < D) {
-        float s = et * mu[h * D + tid] + (su_in != nullptr ? su_in[static_cast<size_t>(bh) * D + tid] : 0.f);
+        const float s = et * mu[h * D + tid] + (su_in != nullptr ? su_in[static_cast<size_t>(bh) * D + tid] : 0.f);
         const float *us = useg + static_cast<size_t>(bh) * nseg * D + tid;
-        for (int p = 0; p < seg; ++p) s += us[static_cast<size_t>(p) * D];
-        c0s[tid] = s;
+        float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};   // eight segment sums in flight
+        for (int p0 = 0; p0 < seg; p0 += 8) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) a[j] += p0 + j < seg ? us[static_cast<size_t>(p0 + j) * D] : 0.f;
+        }
+        c0s[tid] = s + (((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7])));
     }
     __syncthreads();
     float c0[DW], carry[DW];

@@ -165,3 +165,18 @@ def test_float32_path_segments(d, N, dtype, B, H, rope):
     _causal(_part(t, 0, 320), rope, state_out=a)
     o2 = to_f64(_causal(_part(t, 320, N), rope, state_in=a))
     assert rel_l2(o2, ref[:, :, 320:]) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("B,H,N,d", [(1, 3, 577, 32), (1, 1, 255, 16), (1, 1, 257, 16), (3, 1, 1000, 128),
+                                     (1, 1, 4097, 64)])
+def test_float32_segment_boundaries(B, H, N, d):
+    """Segment plans with a one-token last segment (577 tokens, 3 heads), two segments of 127/128
+    and 129/128 tokens, an odd head count (no XCD regrouping), and 22 segments (three combine
+    batches); outputs against the oracle."""
+    wl = CONFIGS[2].with_(B=B, H=H, N=N, d=d, d_u=d, dtype="f32", seed=6600 + N + d)
+    x = make_inputs(wl)
+    t = to_device(x, "f32")
+    o = to_f64(_causal(t, True))
+    err = rel_l2(o, R.causal_forward(**x, rope=True))
+    print(f"f32 segments B{B} H{H} N{N} d{d} rel_l2={err:.3e}", flush=True)
+    assert err <= TOL["f32"]

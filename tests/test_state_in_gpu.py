@@ -180,3 +180,26 @@ def test_float32_segment_boundaries(B, H, N, d):
     err = rel_l2(o, R.causal_forward(**x, rope=True))
     print(f"f32 segments B{B} H{H} N{N} d{d} rel_l2={err:.3e}", flush=True)
     assert err <= TOL["f32"]
+
+
+def test_empty_bf16_call_writes_empty_state():
+    """N = 0 on the bfloat16 d 128 shape: without state_in the (matrix-core) call writes the empty
+    state; with state_in it copies that state."""
+    wl = CONFIGS[4].with_(B=1, H=2, N=40, seed=6700)
+    t = to_device(make_inputs(wl), wl.dtype)
+    a = Z.DecodeState(1, 2, 128, 128)
+    for name in ("F", "G", "Hs", "Su", "m", "E", "P"):
+        getattr(a, name).fill_(7.0)
+    a.t.fill_(5)
+    _causal(_part(t, 0, 0), True, state_out=a)
+    torch.cuda.synchronize()
+    for name in ("F", "G", "Hs", "Su", "E", "P"):
+        assert torch.all(getattr(a, name) == 0), name
+    assert torch.all(a.t == 0) and torch.all(torch.isneginf(a.m))
+    b = Z.DecodeState(1, 2, 128, 128).reset()
+    _causal(_part(t, 0, 40), True, state_out=b)
+    c = Z.DecodeState(1, 2, 128, 128)
+    _causal(_part(t, 40, 40), True, state_in=b, state_out=c)
+    torch.cuda.synchronize()
+    for name in ("F", "G", "Hs", "Su", "m", "E", "P", "t"):
+        assert torch.equal(getattr(b, name), getattr(c, name)), name

@@ -25,8 +25,9 @@
  * to sigma0_t instead of zero. g0 = NULL leaves the term out (the pages' default).
  *
  * Conventions shared by every entry point
- *   Memory:    every pointer is DEVICE memory owned by the caller; the library allocates
- *              nothing and keeps no state between calls (an error message is kept per thread).
+ *   Memory:    every pointer is DEVICE memory owned by the caller; the library keeps no state
+ *              between calls (an error message is kept per thread) and allocates only the
+ *              stream-ordered scratch (hipMallocAsync / hipFreeAsync on `stream`) noted below.
  *              Token tensors (q, k, v, u, g1, gh, o) may be NULL when N = 0; mu and tau never;
  *              g0 may always be NULL.
  *   Layout:    contiguous row-major, feature dimension innermost:
@@ -129,6 +130,8 @@ size_t zeros_fwd_causal_workspace_bytes(const zeros_shape *shape);
  * Encoder (non-causal) forward (Paper-Notes 损失函数 / 训练策略: both modes are supported).
  * Every query t uses the sums over all N tokens, ubar is the single prior-smoothed mean of all
  * N u's, and the coefficients use t = N with the gates of token t. Writes o [B, H, N, d].
+ * bfloat16 calls with d 64/128 and N > 4096 take 4 N d/16 bytes per (b, h) of stream-ordered
+ * scratch for the logits.
  */
 zeros_status zeros_fwd_encoder(const zeros_shape *shape,
                                const void *q, const void *k, const void *v, const void *u,

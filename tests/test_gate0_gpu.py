@@ -67,7 +67,7 @@ def test_causal_gate0_long_sampled_heads():
 
 @pytest.mark.parametrize("d,N,dtype", [(16, 47, "f32"), (64, 197, "f32"), (64, 197, "bf16"),
                                        (128, 65, "bf16"), (64, 300, "bf16"), (128, 1000, "bf16"),
-                                       (64, 1, "bf16"), (16, 2, "f32")])
+                                       (64, 1, "bf16"), (16, 2, "f32"), (128, 5000, "bf16")])
 @pytest.mark.parametrize("rope", [False, True])
 def test_encoder_gate0(d, N, dtype, rope):
     """Encoder: float32 path and both bfloat16 matrix-core variants (N <= 256 and longer)."""

@@ -282,11 +282,11 @@ def test_encoder_mfma_chunks(d, N, rope):
     assert err <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("d,N", [(64, 256), (64, 257), (128, 4096), (128, 4097)])
+@pytest.mark.parametrize("d,N", [(64, 256), (64, 257), (128, 4096), (128, 4097), (64, 9000)])
 def test_encoder_length_boundaries(d, N):
     """Sequence lengths at the edges of the encoder's variants: 256 / 257 tokens (small and large
-    logits buffer) and 4096 / 4097 (the longest sequence on the matrix cores, and the first one on
-    the float32 kernel)."""
+    LDS logits buffer), 4096 (the longest with the logits in LDS), 4097 and 9000 (logits in global
+    scratch)."""
     wl = CONFIGS[3].with_(B=1, H=2, N=N, d=d, d_u=d, dtype="bf16", seed=3100 + d + N)
     x = make_inputs(wl)
     o = to_f64(run_encoder(x, "bf16", rope=True))

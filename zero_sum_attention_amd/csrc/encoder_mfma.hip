@@ -55,8 +55,10 @@ __device__ __forceinline__ void unpack8(const uint4 &x, float (&f)[8]) {
     }
 }
 
+// NMAX > 0: the logits of the sequence stay in LDS (N <= NMAX); NMAX = 0: any N, the logits go to
+// sg, a global scratch region per (column tile, head) that only this workgroup writes and reads.
 template <int D, bool ROPE, int NMAX, bool G0>
-__global__ __launch_bounds__(kEThreads) void encoder_mfma_kernel(Problem p) {
+__global__ __launch_bounds__(kEThreads) void encoder_mfma_kernel(Problem p, float *sg) {
     constexpr int NS = G0 ? 3 : 2;     // states: X, Y (and H)
     constexpr int FT = D / 16;         // 16-row feature tiles of a state
     constexpr int FW = FT / 4;         // feature tiles per wave
@@ -65,7 +67,7 @@ __global__ __launch_bounds__(kEThreads) void encoder_mfma_kernel(Problem p) {
     constexpr int RPP = kEThreads / LPR;   // token rows per pass
     __shared__ float ubar[D];
     __shared__ float part[kEThreads / 64][D];
-    __shared__ float sl[NMAX];         // logits of the sequence (N <= NMAX)
+    __shared__ float sl_lds[NMAX > 0 ? NMAX : 1];   // logits of the sequence (N <= NMAX)
     __shared__ float4 red[kEThreads / 64];
     __shared__ __align__(16) uint16_t kt[D][kEC + kEPad];    // k^ of the chunk, transposed
     __shared__ __align__(16) uint16_t vxt[16][kEC + kEPad];  // this tile's columns of v w_X, transposed
@@ -93,6 +95,7 @@ __global__ __launch_bounds__(kEThreads) void encoder_mfma_kernel(Problem p) {
     const uint16_t *g0 = G0 ? static_cast<const uint16_t *>(p.g0) + row0 : nullptr;
     uint16_t *o = static_cast<uint16_t *>(p.o) + row0 * D;
     const float et = expf(p.tau[h]);
+    float *sl = NMAX > 0 ? sl_lds : sg + (static_cast<size_t>(ct) * bhn + bh) * N;
     const int fr = tid % LPR, rr = tid / LPR;       // feature group (8 features) and row of a pass
     if (ROPE && tid < D / 2) rev[tid] = rope_rev_per_pos(tid, D, p.rope_base);   // ordered by the first barrier
 
@@ -201,7 +204,7 @@ __global__ __launch_bounds__(kEThreads) void encoder_mfma_kernel(Problem p) {
         lse_merge(mloc, eloc, m2, e2);
     }
     if (lane == 0) red[w] = make_float4(mloc, eloc, ploc, 0.f);
-    __syncthreads();                           // also orders the logits in LDS before phase B
+    __syncthreads();                           // also orders the logits (LDS or sg) before phase B
     float M = kNegInf, E = 0.f, P = 0.f;
 #pragma unroll
     for (int i = 0; i < kEThreads / 64; ++i) {
@@ -393,11 +396,24 @@ template <int D, bool ROPE, bool G0>
 hipError_t launch_g(const Problem &p, hipStream_t stream) {
     const dim3 grid((D / 16) * p.B * p.H);
     // short sequences take the variant with a small logits buffer: less LDS, more workgroups per CU
-    if (p.N <= kEShortN)
-        hipLaunchKernelGGL((encoder_mfma_kernel<D, ROPE, kEShortN, G0>), grid, dim3(kEThreads), 0, stream, p);
-    else
-        hipLaunchKernelGGL((encoder_mfma_kernel<D, ROPE, kEncoderMfmaMaxN, G0>), grid, dim3(kEThreads), 0, stream, p);
-    return hipGetLastError();
+    if (p.N <= kEShortN) {
+        hipLaunchKernelGGL((encoder_mfma_kernel<D, ROPE, kEShortN, G0>), grid, dim3(kEThreads), 0, stream, p, nullptr);
+        return hipGetLastError();
+    }
+    if (p.N <= kEncoderMfmaMaxN) {
+        hipLaunchKernelGGL((encoder_mfma_kernel<D, ROPE, kEncoderMfmaMaxN, G0>), grid, dim3(kEThreads), 0, stream, p,
+                           nullptr);
+        return hipGetLastError();
+    }
+    // longer sequences: the logits in stream-ordered global scratch, one region per workgroup
+    float *sg = nullptr;
+    hipError_t err = hipMallocAsync(reinterpret_cast<void **>(&sg), static_cast<size_t>(grid.x) * p.N * sizeof(float),
+                                    stream);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((encoder_mfma_kernel<D, ROPE, 0, G0>), grid, dim3(kEThreads), 0, stream, p, sg);
+    err = hipGetLastError();
+    const hipError_t e2 = hipFreeAsync(sg, stream);
+    return err != hipSuccess ? err : e2;
 }
 
 template <int D, bool ROPE>

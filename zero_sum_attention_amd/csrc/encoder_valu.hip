@@ -265,7 +265,7 @@ hipError_t launch_d(const Problem &p, hipStream_t stream) {
 hipError_t launch_encoder(const Problem &p, hipStream_t stream) {
     // bfloat16 inputs with d 64 or 128 (d_u = d) run on the matrix cores; float32 inputs need the
     // float32 arithmetic of this file (bfloat16 operands cannot meet their tolerance)
-    if (p.dtype == ZEROS_BF16 && (p.d == 64 || p.d == 128) && p.du == p.d && p.N <= kEncoderMfmaMaxN)
+    if (p.dtype == ZEROS_BF16 && (p.d == 64 || p.d == 128) && p.du == p.d)
         return launch_encoder_mfma(p, stream);
     switch (p.d) {
         case 16: return launch_d<16>(p, stream);

@@ -63,7 +63,8 @@ hipError_t launch_logits(const Problem &p, float *useg, float *s_out, float4 *ag
                          hipStream_t stream);
 hipError_t launch_causal_mfma(const Problem &p, const CausalWork &w, hipStream_t stream);
 hipError_t launch_encoder(const Problem &p, hipStream_t stream);
-// Matrix-core encoder for bfloat16, d in {64, 128}, N <= kEncoderMfmaMaxN (logits kept in LDS).
+// Matrix-core encoder for bfloat16, d in {64, 128}: the logits stay in LDS up to kEncoderMfmaMaxN
+// tokens, beyond that in stream-ordered global scratch.
 constexpr int kEncoderMfmaMaxN = 4096;
 hipError_t launch_encoder_mfma(const Problem &p, hipStream_t stream);
 hipError_t launch_decode(const Problem &p, hipStream_t stream);

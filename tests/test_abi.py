@@ -254,3 +254,27 @@ def test_binding_arity_matches_header(lib):
         assert m, name
         params = [p for p in m.group(1).split(",") if p.strip() and p.strip() != "void"]
         assert len(getattr(lib, name).argtypes) == len(params), name
+
+
+def test_missing_library_fails_loudly():
+    """No fallback: loading a library that is not there raises (in a fresh process, since the
+    binding keeps the library it loaded)."""
+    import subprocess
+    import sys
+    code = ("import zero_sum_attention_amd._lib as L\n"
+            "try:\n    L.load_library('/nonexistent/libzeros.so')\n"
+            "except ImportError as e:\n    print('raised', e)\n")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT, timeout=120)
+    assert "raised" in out.stdout and "not built" in out.stdout, out.stdout + out.stderr
+
+
+def test_cpu_tensors_rejected():
+    """The binding runs only the GPU library: CPU tensors are refused, nothing computes on the host."""
+    import torch
+    import zero_sum_attention_amd as Z
+    q = torch.zeros(1, 1, 4, 16)
+    g = torch.zeros(1, 1, 4)
+    with pytest.raises(ValueError, match="GPU"):
+        Z.zeros_fwd_causal(q, q, q, q, torch.zeros(1, 16), torch.zeros(1), g, g)
+    with pytest.raises(ValueError, match="GPU"):
+        Z.zeros_fwd_encoder(q, q, q, q, torch.zeros(1, 16), torch.zeros(1), g, g)

@@ -103,7 +103,9 @@ typedef struct {
  *   running mean, coefficients and RoPE angles included), as if the earlier tokens had been
  *   part of the call (chunked prefill). Heads may have consumed different numbers of tokens.
  *   Read only. bfloat16 d 64/128 calls stay on the matrix-core path (the state enters in its
- *   centred basis); the others, and a call with N = 0, take the float32 path.
+ *   centred basis); the others, and a call with N = 0, take the float32 path. Its contents are
+ *   device data and are not checked: it must be a state as this library writes it (t >= 0;
+ *   m finite and E > 0 when t > 0; the empty state otherwise), else the outputs are undefined.
  * state_out (nullable): receives the state after the call's last token for every (b, h) (S = B);
  *   its buffers must not overlap the inputs, state_in, o or each other (ZEROS_ERR_ALIAS; continue
  *   in place by alternating two states).

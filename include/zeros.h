@@ -41,8 +41,10 @@
  *              host before any launch; a failed launch returns ZEROS_ERR_HIP. NaN/Inf in the
  *              inputs propagate to the outputs they influence and are not checked.
  *   Alignment: q, k, v, u and o must be 16-byte aligned (ZEROS_ERR_SHAPE otherwise).
- *   Aliasing:  o must not overlap any input. Decode updates its state in place.
- *   Shapes:    d in {16, 32, 64, 128}, d_u == d, B, H >= 1, N >= 0 (N = 0 is a no-op),
+ *   Aliasing:  o must not overlap any input; a state the call writes must not overlap the other
+ *              arguments or itself (ZEROS_ERR_ALIAS). Decode updates its state in place.
+ *   Shapes:    d in {16, 32, 64, 128}, d_u == d, B, H >= 1, N >= 0 (N = 0 computes no output;
+ *              a causal call with state_out still writes the state),
  *              B*H*N*d < 2^31 elements per tensor; anything else is ZEROS_ERR_UNSUPPORTED or
  *              ZEROS_ERR_SHAPE.
  *   Threads:   calls are thread-safe; calls that write the same buffers race.

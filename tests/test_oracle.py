@@ -398,3 +398,33 @@ def test_zero_order_gate_first_token():
     sig0 = 1.0 / (1.0 + np.exp(-g0))
     ref = sig0[..., None] * _cos(x)[..., 0, 0][..., None, None] * x["v"].astype(float)
     assert rel(o, ref) < TOL
+
+
+def test_encoder_single_token_is_zero_and_two_tokens_closed_form():
+    """Encoder, N = 1: delta = 0 and softmax = 1, so every weight is zero. N = 2 with sigma1 = 1,
+    sigmah = 0: w_{t,i} = (s_i - (s_1 + s_2)/2)/2, i.e. +-(s_2 - s_1)/4, the same for both queries."""
+    x = small_inputs(2, 2, 1, 8, 8, seed=47)
+    assert np.max(np.abs(R.encoder_forward(**x))) < 1e-12 * np.max(np.abs(x["v"]))
+    x = small_inputs(1, 1, 2, 8, 8, seed=48)
+    x["g1"] = np.full_like(x["g1"], 1000.0)
+    x["gh"] = np.full_like(x["gh"], -1000.0)
+    s = R.deviation_logits_encoder(x["u"], x["mu"], x["tau"])[0, 0]
+    cos = _cos(x)[0, 0]
+    v = x["v"][0, 0].astype(float)
+    half = (s[1] - s[0]) / 4.0
+    ref = np.stack([cos[t, 0] * (-half) * v[0] + cos[t, 1] * half * v[1] for t in range(2)])
+    assert rel(R.encoder_forward(**x)[0, 0], ref) < TOL
+
+
+def test_decode_from_empty_state_is_first_token():
+    """One decode step from the empty state equals the causal forward of that one token (zero
+    without the zero-order gate, sigma0 (q^.k^) v with it)."""
+    x = small_inputs(2, 3, 1, 16, 16, seed=49)
+    st = R.empty_state((2, 3), 16, 16)
+    tok = {k: (v[..., 0, :] if v.ndim == 4 else v[..., 0] if v.ndim == 3 else v) for k, v in x.items()}
+    g0 = _gate0(x, 6)
+    o, st2 = R.decode_step(st, tok["q"], tok["k"], tok["v"], tok["u"], x["mu"], x["tau"], tok["g1"], tok["gh"],
+                           g0=g0[..., 0])
+    ref = R.causal_forward(**x, g0=g0)[..., 0, :]
+    assert rel(o, ref) < TOL
+    assert np.all(st2["t"] == 1)

@@ -25,9 +25,11 @@
  * to sigma0_t instead of zero. g0 = NULL leaves the term out (the pages' default).
  *
  * Conventions shared by every entry point
- *   Memory:    every pointer is DEVICE memory owned by the caller; the library keeps no state
- *              between calls (an error message is kept per thread) and allocates only the
- *              stream-ordered scratch (hipMallocAsync / hipFreeAsync on `stream`) noted below.
+ *   Memory:    every pointer is DEVICE memory owned by the caller; the library allocates no
+ *              memory and keeps no state between calls (an error message is kept per thread,
+ *              and a per-device flag records that a kernel attribute was set). Scratch memory
+ *              comes from the caller as a workspace argument whose size a *_workspace_bytes
+ *              query gives; a call that needs scratch and gets none returns ZEROS_ERR_NULL.
  *              Token tensors (q, k, v, u, g1, gh, o) may be NULL when N = 0; mu and tau never;
  *              g0 may always be NULL.
  *   Layout:    contiguous row-major, feature dimension innermost:
@@ -59,7 +61,7 @@
 extern "C" {
 #endif
 
-#define ZEROS_ABI_VERSION 2
+#define ZEROS_ABI_VERSION 3
 
 typedef enum {
     ZEROS_OK = 0,
@@ -111,13 +113,13 @@ typedef struct {
  * state_out (nullable): receives the state after the call's last token for every (b, h) (S = B);
  *   its buffers must not overlap the inputs, state_in, o or each other (ZEROS_ERR_ALIAS; continue
  *   in place by alternating two states).
- * workspace (nullable): device scratch of at least zeros_fwd_causal_workspace_bytes(shape)
- *   bytes, 256-byte aligned, used only while the call's work runs on `stream` (it holds the
- *   logits s_i, per-segment u sums, per-64-token logit aggregates, the scan's segment states
- *   when a head is split into segments, and on the bfloat16 d = 64/128 path a per-64-token-chunk
- *   operand record, there in all roughly 2.6 times the bytes of q). When NULL and scratch is needed, the library takes it
- *   from the stream-ordered allocator (hipMallocAsync / hipFreeAsync on `stream`).
- *   A workspace smaller than required is ZEROS_ERR_SHAPE.
+ * workspace: device scratch of at least zeros_fwd_causal_workspace_bytes(shape) bytes,
+ *   256-byte aligned, owned by the caller and used only while the call's work runs on `stream`
+ *   (it holds the logits s_i, per-segment u sums, per-64-token logit aggregates, the scan's
+ *   segment states when a head is split into segments, and on the bfloat16 d = 64/128 path a
+ *   per-64-token-chunk operand record, there in all roughly 2.6 times the bytes of q). NULL is
+ *   ZEROS_ERR_NULL whenever the query returns more than 0 (it does for every N > 0); a workspace
+ *   smaller than required or not 256-byte aligned is ZEROS_ERR_SHAPE.
  */
 zeros_status zeros_fwd_causal(const zeros_shape *shape,
                               const void *q, const void *k, const void *v, const void *u,
@@ -126,22 +128,28 @@ zeros_status zeros_fwd_causal(const zeros_shape *shape,
                               void *o, const zeros_state *state_in, const zeros_state *state_out,
                               void *workspace, size_t workspace_bytes, void *stream);
 
-/* Scratch bytes zeros_fwd_causal needs for `shape`, with or without state_in (0 if none, or if
- * shape is invalid). */
+/* Scratch bytes zeros_fwd_causal needs for `shape`, with or without state_in (0 if it needs none,
+ * or if shape is invalid). Depends on B, H, N, d, d_u and dtype only. */
 size_t zeros_fwd_causal_workspace_bytes(const zeros_shape *shape);
 
 /*
  * Encoder (non-causal) forward (Paper-Notes 损失函数 / 训练策略: both modes are supported).
  * Every query t uses the sums over all N tokens, ubar is the single prior-smoothed mean of all
  * N u's, and the coefficients use t = N with the gates of token t. Writes o [B, H, N, d].
- * bfloat16 calls with d 64/128 and N > 4096 take 4 N d/16 bytes per (b, h) of stream-ordered
- * scratch for the logits.
+ * workspace: device scratch of zeros_fwd_encoder_workspace_bytes(shape) bytes, 256-byte aligned,
+ *   owned by the caller and used only while the call's work runs on `stream`. Only bfloat16
+ *   calls with d 64/128 and N > 4096 need any (4 N d/16 bytes per (b, h): the logits of the
+ *   sequence once per 16-column tile); for every other shape it may be NULL. NULL when scratch
+ *   is needed is ZEROS_ERR_NULL; too small or not 256-byte aligned is ZEROS_ERR_SHAPE.
  */
 zeros_status zeros_fwd_encoder(const zeros_shape *shape,
                                const void *q, const void *k, const void *v, const void *u,
                                const float *mu, const float *tau,
                                const void *g1, const void *gh, const void *g0,
-                               void *o, void *stream);
+                               void *o, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Scratch bytes zeros_fwd_encoder needs for `shape` (0 if it needs none, or if shape is invalid). */
+size_t zeros_fwd_encoder_workspace_bytes(const zeros_shape *shape);
 
 /*
  * One recurrent step (the O(d^2)-per-token update of 关键设计 / 线性时间前缀扫描):

@@ -7,6 +7,24 @@ TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
 #   float32 inputs: 1e-4; bfloat16 inputs with float32 accumulation: 2e-2.
 TOL = {"f32": 1e-4, "bf16": 2e-2}
 
+# Bar on the recurrent state (F, G, H) written by the bfloat16 matrix-core path. Each state is a
+# float32 sum over tokens of k^_i^T (v_i w_i) whose MFMA operands are rounded to bfloat16 once each
+# (k^, and v times the float32 weight), a relative rounding of at most 2^-8 per element and about
+# 1.7e-3 in RMS; the roundings are independent across tokens, so the relative L2 error of a sum is
+# sqrt(number of rounded operands) x 1.7e-3: 1.7e-3 for H (k^ only) and 2.4e-3 for F and G
+# (k^ and v w). Emulating exactly those roundings in float64 measures 1.7e-3 (F, H) and 2.2-2.5e-3
+# (G) at N = 333 and 3000. The bar is twice the two-operand estimate.
+STATE_TOL_BF16 = 5e-3
+# The float32 scalars of the state (m, E, P, S_u) come from float32 sums of the logits and of u on
+# every path.
+SCALAR_STATE_TOL = 1e-5
+
+
+def state_matrix_tol(dtype: str, d: int) -> float:
+    """Bar on F, G, H: bfloat16 inputs with d 64/128 run on the matrix cores (bfloat16 operands);
+    every other call runs the float32 path (float32 arithmetic on the upcast inputs)."""
+    return STATE_TOL_BF16 if dtype == "bf16" and d in (64, 128) else SCALAR_STATE_TOL
+
 
 def to_device(x: dict, dtype: str, device="cuda"):
     """Seeded numpy inputs (already rounded to dtype) -> torch tensors on the GPU."""
@@ -28,6 +46,17 @@ def rel_l2(a, b) -> float:
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def row_rel_p99(a, b, floor_frac: float = 0.0) -> float:
+    """99th percentile over rows (tokens) of |o_t - ref_t| / |ref_t|: shows error that a global
+    relative L2 would hide in the late, small rows. Rows whose reference norm is below
+    floor_frac x the median row norm are skipped (o_1 = 0 exactly)."""
+    a = np.asarray(a, dtype=np.float64).reshape(-1, np.shape(a)[-1])
+    b = np.asarray(b, dtype=np.float64).reshape(-1, np.shape(b)[-1])
+    nb = np.linalg.norm(b, axis=-1)
+    keep = nb > max(floor_frac * np.median(nb), 1e-300)
+    return float(np.percentile(np.linalg.norm(a - b, axis=-1)[keep] / nb[keep], 99))
 
 
 def tail_rel_l2(a, b, start: int) -> float:

@@ -30,7 +30,7 @@ def declared_functions():
 def test_header_declares_entry_points():
     names = declared_functions()
     for n in ("zeros_fwd_causal", "zeros_fwd_encoder", "zeros_decode_step", "zeros_state_bytes",
-              "zeros_fwd_causal_workspace_bytes",
+              "zeros_fwd_causal_workspace_bytes", "zeros_fwd_encoder_workspace_bytes",
               "zeros_state_from_buffer", "zeros_status_str", "zeros_last_error", "zeros_abi_version"):
         assert n in names
 
@@ -73,10 +73,10 @@ def call_causal(lib, shp, ptrs=None, state=None, state_in=None):
                                 None, 0, None)
 
 
-def call_encoder(lib, shp, ptrs=None):
+def call_encoder(lib, shp, ptrs=None, ws=None, ws_bytes=0):
     p = dict(P, **(ptrs or {}))
     return lib.zeros_fwd_encoder(ctypes.byref(shp), p["q"], p["k"], p["v"], p["u"], p["mu"], p["tau"],
-                                 p["g1"], p["gh"], p["g0"], p["o"], None)
+                                 p["g1"], p["gh"], p["g0"], p["o"], ws, ws_bytes, None)
 
 
 def call_decode(lib, shp, state, ptrs=None):
@@ -157,6 +157,30 @@ def test_workspace_size_and_validation(lib):
     r = lib.zeros_fwd_causal(ctypes.byref(small), p["q"], p["k"], p["v"], p["u"], p["mu"], p["tau"], p["g1"],
                              p["gh"], None, p["o"], None, None, 0x7000010, need, None)
     assert r == L.ZEROS_ERR_SHAPE                                                       # misaligned
+
+
+def test_library_never_allocates_scratch(lib):
+    """Scratch comes from the caller: a call that needs a workspace and gets none is refused on the
+    host (ZEROS_ERR_NULL, nothing launched), on both causal paths and for long bf16 encoders."""
+    for shp in (shape(B=1, H=2, N=8, d=64, d_u=64, dtype=1), shape(dtype=0)):
+        assert lib.zeros_fwd_causal_workspace_bytes(ctypes.byref(shp)) > 0
+        assert call_causal(lib, shp) == L.ZEROS_ERR_NULL
+        assert "workspace is NULL" in lib.zeros_last_error().decode()
+    long_bf = shape(B=1, H=1, N=4097, d=64, d_u=64, dtype=1)
+    need = lib.zeros_fwd_encoder_workspace_bytes(ctypes.byref(long_bf))
+    assert need == 4 * 4097 * 64 // 16            # the logits per 16-column tile, as float32
+    assert call_encoder(lib, long_bf) == L.ZEROS_ERR_NULL
+    assert call_encoder(lib, long_bf, ws=0x7000000, ws_bytes=need - 1) == L.ZEROS_ERR_SHAPE
+    assert call_encoder(lib, long_bf, ws=0x7000010, ws_bytes=need) == L.ZEROS_ERR_SHAPE   # misaligned
+
+
+@pytest.mark.parametrize("kw,need", [(dict(N=4096, d=128, d_u=128, dtype=1), 0),           # logits in LDS
+                                     (dict(N=4097, d=128, d_u=128, dtype=1), 4097 * 8 * 4 * 6),
+                                     (dict(N=9000, d=64, d_u=64, dtype=1), 9000 * 4 * 4 * 6),
+                                     (dict(N=9000, d=64, d_u=64, dtype=0), 0),             # float32 kernel
+                                     (dict(N=9000, d=32, d_u=32, dtype=1), 0)])            # VALU kernel
+def test_encoder_workspace_bytes(lib, kw, need):
+    assert lib.zeros_fwd_encoder_workspace_bytes(ctypes.byref(shape(B=2, H=3, **kw))) == need
 
 
 def test_partial_state_rejected(lib):
@@ -249,7 +273,8 @@ def test_binding_arity_matches_header(lib):
     """The ctypes declarations of the binding take as many arguments as the header declares."""
     text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
     for name in ("zeros_fwd_causal", "zeros_fwd_encoder", "zeros_decode_step",
-                 "zeros_fwd_causal_workspace_bytes", "zeros_state_bytes", "zeros_state_from_buffer"):
+                 "zeros_fwd_causal_workspace_bytes", "zeros_fwd_encoder_workspace_bytes",
+                 "zeros_state_bytes", "zeros_state_from_buffer"):
         m = re.search(r"\b%s\s*\(([^)]*)\)\s*;" % name, text)
         assert m, name
         params = [p for p in m.group(1).split(",") if p.strip() and p.strip() != "void"]

@@ -11,13 +11,20 @@ import torch
 from oracle import zeros_ref as R
 from synth import CONFIGS, make_inputs
 from synth.inputs import decode_prefill_batch
-from tests.gpu_helpers import TOL, rel_l2, slice_heads, tail_rel_l2, to_device, to_f64
+from tests.gpu_helpers import (SCALAR_STATE_TOL, STATE_TOL_BF16, TOL, rel_l2, row_rel_p99, slice_heads,
+                               tail_rel_l2, to_device, to_f64)
 
 pytestmark = pytest.mark.gpu
 
 # Where the exact output is zero (a single token, u = 0) float32 rounding leaves residues of
 # order eps32 * |v|: bound them absolutely.
 ZERO_ABS = 1e-6
+# The same on the bfloat16 matrix-core path: the weight of the single key of row 1 is formed in
+# float32 as sigmah*1 + (sigma1 - sigmah) s_1 - (sigma1 - sigmah) s_1 - sigmah (exactly 0), which
+# leaves |w| <= a few ulp of (|sigma| + |s_1|) < 6, i.e. below 4 * 6 * 2^-24 = 1.5e-6; rounding w to
+# bfloat16 keeps it that small, |q^ . k^| <= 1 and |v| < 6 for N(0,1) rows of 128 features, and
+# the bfloat16 output rounding is relative, so |o_1| < 1e-5.
+ZERO_ABS_MFMA = 1e-5
 
 import zero_sum_attention_amd as Z  # noqa: E402
 
@@ -46,7 +53,7 @@ def run_encoder(x, dtype, rope=False):
 
 def test_library_is_native():
     lib = Z.load_library()
-    assert lib.zeros_abi_version() == 2
+    assert lib.zeros_abi_version() == 3
     assert torch.cuda.is_available()
 
 
@@ -123,7 +130,9 @@ def test_causal_mfma_chunks(d, N, rope):
     err = rel_l2(o, ref)
     print(f"mfma d={d} N={N} rope={rope} rel_l2={err:.3e}", flush=True)
     assert err <= TOL["bf16"]
-    assert np.max(np.abs(o[..., 0, :])) <= 1e-3
+    o1 = float(np.max(np.abs(o[..., 0, :])))
+    print(f"mfma d={d} N={N} rope={rope} max|o_1|={o1:.2e}", flush=True)
+    assert o1 <= ZERO_ABS_MFMA
 
 
 @pytest.mark.parametrize("rope", [False, True])
@@ -136,9 +145,11 @@ def test_causal_mfma_state_out(rope):
     got = _state_np(st)
     assert np.all(got["t"] == 333)
     for key in ("m", "E", "P", "Su"):
-        assert rel_l2(got[key], ref[key]) <= 1e-5, key
-    for key in ("F", "G", "H"):
-        assert rel_l2(got[key], ref[key]) <= 2e-2, key
+        assert rel_l2(got[key], ref[key]) <= SCALAR_STATE_TOL, key
+    errs = {key: rel_l2(got[key], ref[key]) for key in ("F", "G", "H")}
+    print("mfma state_out " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    for key, e in errs.items():
+        assert e <= STATE_TOL_BF16, key
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -160,10 +171,12 @@ def test_causal_segments_ragged_sampled_heads(d):
     gst = _state_np(st)
     for key in ("m", "E", "P", "Su"):
         g = np.stack([gst[key][b, h] for b, h in pairs])[None]
-        assert rel_l2(g, ref_st[key]) <= 1e-5, key
+        assert rel_l2(g, ref_st[key]) <= SCALAR_STATE_TOL, key
     for key in ("F", "G", "H"):
         g = np.stack([gst[key][b, h] for b, h in pairs])[None]
-        assert rel_l2(g, ref_st[key]) <= 2e-2, key
+        e = rel_l2(g, ref_st[key])
+        print(f"segments d={d} state {key}={e:.2e}", flush=True)
+        assert e <= STATE_TOL_BF16, key
 
 
 @pytest.mark.parametrize("scale", [10.0, 30.0])
@@ -307,11 +320,20 @@ def test_encoder_mfma_large_logits():
 
 @pytest.mark.parametrize("scale,tol", [(10.0, 1e-4), (30.0, 1e-3)])
 def test_logit_stress_running_max(scale, tol):
+    """float32 inputs with u scaled by 10 and 30: the running maximum must keep e^{s} finite.
+
+    Bar at u x 30: the logits reach |s| of about 3.7e3 there (|s| ~ 4e2 at u x 10). Computing s in
+    float32 alone leaves an absolute error of up to |s| 2^-24 = 2.2e-4 in s, and e^{s - m} carries
+    that as a relative error in every softmax-type weight, so the float32 output cannot be held to
+    1e-4 at u x 30; the bar is 1e-3, 4.5 times that conditioning floor. At u x 10 the floor is
+    2.5e-5 and the 1e-4 contract applies."""
     wl = CONFIGS[2].with_(B=1, H=4, N=300, seed=77)
     x = make_inputs(wl, u_scale=scale)
     o = to_f64(run_causal(x, "f32"))
     assert np.all(np.isfinite(o))
-    assert rel_l2(o, R.causal_forward(**x)) <= tol
+    err = rel_l2(o, R.causal_forward(**x))
+    print(f"logit stress u x {scale}: rel_l2={err:.3e} (bar {tol:g})", flush=True)
+    assert err <= tol
 
 
 def test_first_row_zero_and_constant_logits():
@@ -336,6 +358,54 @@ def test_deterministic_and_causal():
     o3 = run_causal(y, "f32").cpu()
     assert torch.equal(o1[..., :150, :], o3[..., :150, :])
     assert not torch.equal(o1[..., 150:, :], o3[..., 150:, :])
+
+
+@pytest.mark.parametrize("cut", [640, 768])
+def test_mfma_deterministic_and_causal(cut):
+    """bfloat16 d 128 RoPE on the matrix-core path, 32 heads x 1500 tokens: 24 chunks in 8 scan
+    segments of 3 (pass 1, combine, main). Two calls give identical bits; changing q, k, v, u and the
+    gates of every token from a 64-token chunk boundary on leaves every earlier output bit for bit
+    unchanged: 640 starts the second chunk of a segment (the chunk scan's reference maximum and the
+    segment's pass-1 sums see the change only from there), 768 starts a segment and a 256-token
+    logit segment."""
+    wl = CONFIGS[4].with_(B=2, H=16, N=1500, seed=3800)
+    x = make_inputs(wl)
+    o1 = run_causal(x, "bf16", rope=True).cpu()
+    o2 = run_causal(x, "bf16", rope=True).cpu()
+    assert torch.equal(o1, o2)
+    y = {k: np.array(v, copy=True) for k, v in x.items()}
+    rng = np.random.default_rng(cut)
+    for key in ("q", "k", "v", "u"):
+        y[key][..., cut:, :] = rng.standard_normal(y[key][..., cut:, :].shape).astype(np.float32)
+    for key in ("g1", "gh"):
+        y[key][..., cut:] = rng.standard_normal(y[key][..., cut:].shape).astype(np.float32)
+    o3 = run_causal(y, "bf16", rope=True).cpu()
+    assert torch.equal(o1[..., :cut, :], o3[..., :cut, :])
+    assert not torch.equal(o1[..., cut:, :], o3[..., cut:, :])
+
+
+def test_side_stream_call():
+    """A call launched on a side stream: the output and workspace the binding allocates belong to
+    that stream, so allocations on the default stream while its kernels run cannot take their
+    memory. Parity against the oracle after the side stream finishes."""
+    wl = CONFIGS[4].with_(B=1, H=4, N=2000, seed=3900)
+    x = make_inputs(wl)
+    t = to_device(x, "bf16")
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    outs = []
+    for _ in range(3):
+        o = Z.zeros_fwd_causal(t["q"], t["k"], t["v"], t["u"], t["mu"], t["tau"], t["g1"], t["gh"],
+                               rope=True, stream=side)
+        outs.append(o)
+        # default-stream work that allocates and writes while the side stream's kernels may run
+        junk = [torch.full((1 << 24,), 0x7F, dtype=torch.uint8, device="cuda") for _ in range(4)]
+        del junk
+    side.synchronize()
+    ref = R.causal_forward(**x, rope=True)
+    for o in outs:
+        assert rel_l2(to_f64(o), ref) <= TOL["bf16"]
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
 
 
 # ------------------------------------------------------------------ state and decode
@@ -434,9 +504,11 @@ def test_config5_decode_full_size():
         _, ref = R.causal_forward(px["q"], px["k"], px["v"], px["u"], step["mu"][h], step["tau"][h],
                                   px["g1"], px["gh"], return_state=True)
         for key, gk in (("F", st.F), ("G", st.G), ("H", st.Hs)):
-            assert rel_l2(to_f64(gk[s, h]), ref[key]) <= TOL["bf16"], (s, h, key)
-        assert abs(float(st.m[s, h]) - ref["m"]) <= 1e-4
-        assert rel_l2(to_f64(st.Su[s, h]), ref["Su"]) <= 1e-4
+            e = rel_l2(to_f64(gk[s, h]), ref[key])
+            print(f"config5 prefill state ({s},{h}) {key}={e:.2e}", flush=True)
+            assert e <= STATE_TOL_BF16, (s, h, key)
+        assert abs(float(st.m[s, h]) - ref["m"]) <= SCALAR_STATE_TOL * max(1.0, abs(ref["m"]))
+        assert rel_l2(to_f64(st.Su[s, h]), ref["Su"]) <= SCALAR_STATE_TOL
     # (a) one step from the identical state
     before = {k: getattr(st, a).cpu() for k, a in (("F", "F"), ("G", "G"), ("H", "Hs"), ("Su", "Su"),
                                                  ("m", "m"), ("E", "E"), ("P", "P"), ("t", "t"))}

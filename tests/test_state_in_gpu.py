@@ -1,13 +1,15 @@
 """GPU parity of the causal forward continued from a state (chunked prefill), through the C ABI,
 against the float64 oracle run over the whole sequence in one pass (bars as in the other parity
-tests: relative L2 <= 1e-4 for float32, <= 2e-2 for bfloat16)."""
+tests: relative L2 <= 1e-4 for float32, <= 2e-2 for bfloat16; the final state's float32 scalars to
+1e-5, its matrices to 1e-5 on the float32 path and to the bfloat16-operand bar on the matrix-core
+path)."""
 import numpy as np
 import pytest
 import torch
 
 from oracle import zeros_ref as R
 from synth import CONFIGS, make_inputs
-from tests.gpu_helpers import TOL, rel_l2, to_device, to_f64
+from tests.gpu_helpers import SCALAR_STATE_TOL, TOL, rel_l2, state_matrix_tol, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -31,6 +33,18 @@ def _part(t, a, b):
 def _causal(t, rope, state_in=None, state_out=None):
     return Z.zeros_fwd_causal(t["q"], t["k"], t["v"], t["u"], t["mu"], t["tau"], t["g1"], t["gh"],
                               g0=t.get("g0"), rope=rope, state_in=state_in, state_out=state_out)
+
+
+def _check_state(got, ref, dtype, d):
+    """Scalars (m, E, P, S_u) to 1e-5 on every path; F, G, H to the bar of the path that ran."""
+    for key in ("m", "E", "P", "Su"):
+        assert rel_l2(got[key], ref[key]) <= SCALAR_STATE_TOL, key
+    bar = state_matrix_tol(dtype, d)
+    errs = {key: rel_l2(got[key], ref[key]) for key in ("F", "G", "H")}
+    print(f"state {dtype} d={d} " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()) + f" (bar {bar:g})",
+          flush=True)
+    for key, e in errs.items():
+        assert e <= bar, key
 
 
 def _state_np(st):
@@ -60,9 +74,7 @@ def test_continuation_matches_one_pass(d, dtype, cut, N, rope):
     assert rel_l2(o, ref) <= TOL[dtype]
     got = _state_np(b)
     assert np.all(got["t"] == N)
-    bar = 1e-5 if dtype == "f32" else 2e-2
-    for key in ("m", "E", "P", "Su", "F", "G", "H"):
-        assert rel_l2(got[key], st[key]) <= bar, key
+    _check_state(got, st, dtype, d)
 
 
 @pytest.mark.parametrize("d,dtype", [(32, "f32"), (64, "bf16"), (128, "bf16")])
@@ -134,9 +146,7 @@ def test_continuation_from_empty_state(d, dtype):
     assert rel_l2(o, ref) <= TOL[dtype]
     got = _state_np(b)
     assert np.all(got["t"] == 150)
-    bar = 1e-5 if dtype == "f32" else 2e-2
-    for key in ("m", "E", "P", "Su", "F", "G", "H"):
-        assert rel_l2(got[key], st[key]) <= bar, key
+    _check_state(got, st, dtype, d)
 
 
 # ------------------------------------------------------------------ segmented float32 scan
@@ -158,9 +168,7 @@ def test_float32_path_segments(d, N, dtype, B, H, rope):
     print(f"segmented float32 path d={d} N={N} rel_l2={err:.3e}", flush=True)
     assert err <= TOL[dtype]
     got = _state_np(st)
-    bar = 1e-5 if dtype == "f32" else 2e-2
-    for key in ("m", "E", "P", "Su", "F", "G", "H"):
-        assert rel_l2(got[key], sref[key]) <= bar, key
+    _check_state(got, sref, dtype, d)
     a = Z.DecodeState(B, H, d, d).reset()
     _causal(_part(t, 0, 320), rope, state_out=a)
     o2 = to_f64(_causal(_part(t, 320, N), rope, state_in=a))

@@ -58,8 +58,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.zeros_fwd_causal.restype = i32
     lib.zeros_fwd_causal_workspace_bytes.argtypes = [ctypes.POINTER(zeros_shape)]
     lib.zeros_fwd_causal_workspace_bytes.restype = ctypes.c_size_t
-    lib.zeros_fwd_encoder.argtypes = fwd + [vp]
+    lib.zeros_fwd_encoder.argtypes = fwd + [vp, ctypes.c_size_t, vp]
     lib.zeros_fwd_encoder.restype = i32
+    lib.zeros_fwd_encoder_workspace_bytes.argtypes = [ctypes.POINTER(zeros_shape)]
+    lib.zeros_fwd_encoder_workspace_bytes.restype = ctypes.c_size_t
     lib.zeros_decode_step.argtypes = fwd + [ctypes.POINTER(zeros_state), vp]
     lib.zeros_decode_step.restype = i32
     lib.zeros_state_bytes.argtypes = [i32, i32, i32, i32]
@@ -86,9 +88,26 @@ def _ptr(t: torch.Tensor | None) -> int | None:
     return None if t is None else t.data_ptr()
 
 
-def _stream(device: torch.device, stream) -> int:
-    s = torch.cuda.current_stream(device) if stream is None else stream
-    return s.cuda_stream
+def _stream(device: torch.device, stream) -> torch.cuda.Stream:
+    """The stream the call's kernels are launched on (the current stream by default)."""
+    return torch.cuda.current_stream(device) if stream is None else stream
+
+
+def _alloc_on(stream: torch.cuda.Stream, fn):
+    """Allocate through torch's caching allocator as the launch stream's memory: a block freed
+    after the call is reused only by later work on that same stream, so it cannot be handed to
+    another stream while the call's kernels still use it."""
+    with torch.cuda.stream(stream):
+        return fn()
+
+
+def _workspace(nbytes: int, workspace, device, stream):
+    if workspace is None and nbytes > 0:
+        workspace = _alloc_on(stream, lambda: torch.empty(nbytes, dtype=torch.uint8, device=device))
+    if workspace is not None:
+        _need(workspace.dtype == torch.uint8 and workspace.device == device and workspace.is_contiguous(),
+              "workspace must be a contiguous uint8 tensor on q's device")
+    return workspace
 
 
 def _need(cond: bool, msg: str) -> None:
@@ -182,9 +201,12 @@ def zeros_fwd_causal(q, k, v, u, mu, tau, g1, gh, *, g0: torch.Tensor | None = N
     ``g0`` [B, H, N] (optional) enables the zero-order gate. ``state_in`` continues every
     (b, h) from a state (chunked prefill); ``state_out`` receives the final state and must be a
     different state object. ``workspace`` (optional uint8 tensor) is reused scratch; without it
-    one is allocated per call when the path needs it (see zeros_fwd_causal_workspace_bytes)."""
+    one is allocated per call when the path needs it (see zeros_fwd_causal_workspace_bytes).
+    ``stream`` (a torch.cuda.Stream, default the current one) receives the kernels; the output
+    and the workspace allocated here belong to it."""
     _check_tensors(q, k, v, u, mu, tau, g1, gh, 1, g0)
-    o = torch.empty_like(v) if out is None else out
+    s_ = _stream(q.device, stream)
+    o = _alloc_on(s_, lambda: torch.empty_like(v)) if out is None else out
     _need(o.shape == v.shape and o.dtype == v.dtype and o.is_contiguous() and o.device == q.device,
           "out must match v")
     for name, s_ in (("state_in", state_in), ("state_out", state_out)):
@@ -196,15 +218,11 @@ def zeros_fwd_causal(q, k, v, u, mu, tau, g1, gh, *, g0: torch.Tensor | None = N
     st = ctypes.byref(state_out.c) if state_out is not None else None
     sti = ctypes.byref(state_in.c) if state_in is not None else None
     nws = lib.zeros_fwd_causal_workspace_bytes(ctypes.byref(shp))
-    if workspace is None and nws > 0:
-        workspace = torch.empty(nws, dtype=torch.uint8, device=q.device)
-    if workspace is not None:
-        _need(workspace.dtype == torch.uint8 and workspace.device == q.device and workspace.is_contiguous(),
-              "workspace must be a contiguous uint8 tensor on q's device")
+    workspace = _workspace(nws, workspace, q.device, s_)
     _check(lib.zeros_fwd_causal(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(u), _ptr(mu),
                                 _ptr(tau), _ptr(g1), _ptr(gh), _ptr(g0), _ptr(o), sti, st,
                                 _ptr(workspace), 0 if workspace is None else workspace.numel(),
-                                _stream(q.device, stream)))
+                                s_.cuda_stream))
     return o
 
 
@@ -217,18 +235,29 @@ def zeros_fwd_causal_workspace_bytes(B: int, H: int, N: int, d: int, d_u: int, d
 
 def zeros_fwd_encoder(q, k, v, u, mu, tau, g1, gh, *, g0: torch.Tensor | None = None, rope: bool = False,
                       rope_base: float = 10000.0, out: torch.Tensor | None = None,
-                      stream=None) -> torch.Tensor:
-    """Non-causal forward; same tensor layout (and optional ``g0``) as zeros_fwd_causal."""
+                      workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Non-causal forward; same tensor layout (and optional ``g0``) as zeros_fwd_causal.
+    ``workspace`` as for zeros_fwd_causal (only long bfloat16 sequences need one)."""
     _check_tensors(q, k, v, u, mu, tau, g1, gh, 1, g0)
-    o = torch.empty_like(v) if out is None else out
+    s_ = _stream(q.device, stream)
+    o = _alloc_on(s_, lambda: torch.empty_like(v)) if out is None else out
     _need(o.shape == v.shape and o.dtype == v.dtype and o.is_contiguous() and o.device == q.device,
           "out must match v")
     lib = load_library()
     shp = _shape(q, u, q.shape[2], rope, rope_base)
+    workspace = _workspace(lib.zeros_fwd_encoder_workspace_bytes(ctypes.byref(shp)), workspace, q.device, s_)
     _check(lib.zeros_fwd_encoder(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(u), _ptr(mu),
                                  _ptr(tau), _ptr(g1), _ptr(gh), _ptr(g0), _ptr(o),
-                                 _stream(q.device, stream)))
+                                 _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                                 s_.cuda_stream))
     return o
+
+
+def zeros_fwd_encoder_workspace_bytes(B: int, H: int, N: int, d: int, d_u: int, dtype) -> int:
+    """Scratch bytes zeros_fwd_encoder needs for these sizes (0 when it needs none)."""
+    lib = load_library()
+    shp = zeros_shape(B, H, N, d, d_u, _DT[dtype], 0, 10000.0)
+    return int(lib.zeros_fwd_encoder_workspace_bytes(ctypes.byref(shp)))
 
 
 def zeros_decode_step(q, k, v, u, mu, tau, g1, gh, state: DecodeState, *, g0: torch.Tensor | None = None,
@@ -238,12 +267,13 @@ def zeros_decode_step(q, k, v, u, mu, tau, g1, gh, state: DecodeState, *, g0: to
     _check_tensors(q, k, v, u, mu, tau, g1, gh, 0, g0)
     _need((state.S, state.H, state.d, state.d_u) == (q.shape[0], q.shape[1], q.shape[-1], u.shape[-1]),
           "state sizes differ from the token tensors")
-    o = torch.empty_like(v) if out is None else out
+    s_ = _stream(q.device, stream)
+    o = _alloc_on(s_, lambda: torch.empty_like(v)) if out is None else out
     _need(o.shape == v.shape and o.dtype == v.dtype and o.is_contiguous() and o.device == q.device,
           "out must match v")
     lib = load_library()
     shp = _shape(q, u, 1, rope, rope_base)
     _check(lib.zeros_decode_step(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(u), _ptr(mu),
                                  _ptr(tau), _ptr(g1), _ptr(gh), _ptr(g0), _ptr(o), ctypes.byref(state.c),
-                                 _stream(q.device, stream)))
+                                 s_.cuda_stream))
     return o

@@ -28,6 +28,8 @@
 // are in the absolute frame and need no re-basing between chunks.
 #include <hip/hip_bf16.h>
 
+#include <atomic>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "mfma_common.hpp"
@@ -810,17 +812,19 @@ hipError_t set_smem(K kernel, size_t bytes) {
 
 template <int D, bool ROPE>
 hipError_t launch_one(const Problem &p, const CausalWork &w, hipStream_t stream) {
-    // the LDS size attribute is per device: set once on each device the library launches on
-    // (idempotent; two threads racing here only repeat the same call)
+    // the LDS size attribute is per device: set once on each device the library launches on.
+    // The flags are atomics, so concurrent first calls from several threads are well defined (both
+    // may set the attribute; the call is idempotent).
     constexpr int kMaxDev = 64;
-    static bool attr_set[kMaxDev] = {};
+    static std::atomic<bool> attr_set[kMaxDev];
     int dev = 0;
     hipError_t err = hipGetDevice(&dev);
     if (err != hipSuccess) return err;
-    if (dev < 0 || dev >= kMaxDev || !attr_set[dev]) {
+    const bool known = dev >= 0 && dev < kMaxDev;
+    if (!known || !attr_set[dev].load(std::memory_order_acquire)) {
         err = set_smem(&causal_prep_kernel<D, ROPE>, sizeof(PSmem<D>));
         if (err != hipSuccess) return err;
-        if (dev >= 0 && dev < kMaxDev) attr_set[dev] = true;
+        if (known) attr_set[dev].store(true, std::memory_order_release);
     }
     const int nch = (p.N + kC - 1) / kC;
     const int bh = p.B * p.H;

@@ -393,7 +393,7 @@ __global__ __launch_bounds__(kEThreads) void encoder_mfma_kernel(Problem p, floa
 }
 
 template <int D, bool ROPE, bool G0>
-hipError_t launch_g(const Problem &p, hipStream_t stream) {
+hipError_t launch_g(const Problem &p, float *work, hipStream_t stream) {
     const dim3 grid((D / 16) * p.B * p.H);
     // short sequences take the variant with a small logits buffer: less LDS, more workgroups per CU
     if (p.N <= kEShortN) {
@@ -405,27 +405,23 @@ hipError_t launch_g(const Problem &p, hipStream_t stream) {
                            nullptr);
         return hipGetLastError();
     }
-    // longer sequences: the logits in stream-ordered global scratch, one region per workgroup
-    float *sg = nullptr;
-    hipError_t err = hipMallocAsync(reinterpret_cast<void **>(&sg), static_cast<size_t>(grid.x) * p.N * sizeof(float),
-                                    stream);
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((encoder_mfma_kernel<D, ROPE, 0, G0>), grid, dim3(kEThreads), 0, stream, p, sg);
-    err = hipGetLastError();
-    const hipError_t e2 = hipFreeAsync(sg, stream);
-    return err != hipSuccess ? err : e2;
+    // longer sequences: the logits in the caller's scratch, one region of N floats per workgroup
+    // (encoder_work_bytes; validated by the front end)
+    if (work == nullptr) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((encoder_mfma_kernel<D, ROPE, 0, G0>), grid, dim3(kEThreads), 0, stream, p, work);
+    return hipGetLastError();
 }
 
 template <int D, bool ROPE>
-hipError_t launch_one(const Problem &p, hipStream_t stream) {
-    return p.g0 != nullptr ? launch_g<D, ROPE, true>(p, stream) : launch_g<D, ROPE, false>(p, stream);
+hipError_t launch_one(const Problem &p, float *work, hipStream_t stream) {
+    return p.g0 != nullptr ? launch_g<D, ROPE, true>(p, work, stream) : launch_g<D, ROPE, false>(p, work, stream);
 }
 
 }  // namespace
 
-hipError_t launch_encoder_mfma(const Problem &p, hipStream_t stream) {
-    if (p.d == 128) return p.rope ? launch_one<128, true>(p, stream) : launch_one<128, false>(p, stream);
-    if (p.d == 64) return p.rope ? launch_one<64, true>(p, stream) : launch_one<64, false>(p, stream);
+hipError_t launch_encoder_mfma(const Problem &p, float *work, hipStream_t stream) {
+    if (p.d == 128) return p.rope ? launch_one<128, true>(p, work, stream) : launch_one<128, false>(p, work, stream);
+    if (p.d == 64) return p.rope ? launch_one<64, true>(p, work, stream) : launch_one<64, false>(p, work, stream);
     return hipErrorInvalidValue;
 }
 

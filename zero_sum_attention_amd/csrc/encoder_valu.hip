@@ -262,11 +262,19 @@ hipError_t launch_d(const Problem &p, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_encoder(const Problem &p, hipStream_t stream) {
-    // bfloat16 inputs with d 64 or 128 (d_u = d) run on the matrix cores; float32 inputs need the
-    // float32 arithmetic of this file (bfloat16 operands cannot meet their tolerance)
-    if (p.dtype == ZEROS_BF16 && (p.d == 64 || p.d == 128) && p.du == p.d)
-        return launch_encoder_mfma(p, stream);
+// bfloat16 inputs with d 64 or 128 (d_u = d) run on the matrix cores; float32 inputs need the
+// float32 arithmetic of this file (bfloat16 operands cannot meet their tolerance)
+static bool encoder_uses_mfma(const Problem &p) {
+    return p.dtype == ZEROS_BF16 && (p.d == 64 || p.d == 128) && p.du == p.d;
+}
+
+size_t encoder_work_bytes(const Problem &p) {
+    if (!encoder_uses_mfma(p) || p.N <= kEncoderMfmaMaxN) return 0;
+    return static_cast<size_t>(p.d / 16) * p.B * p.H * p.N * sizeof(float);
+}
+
+hipError_t launch_encoder(const Problem &p, void *work, hipStream_t stream) {
+    if (encoder_uses_mfma(p)) return launch_encoder_mfma(p, static_cast<float *>(work), stream);
     switch (p.d) {
         case 16: return launch_d<16>(p, stream);
         case 32: return launch_d<32>(p, stream);

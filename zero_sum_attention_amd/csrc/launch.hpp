@@ -62,11 +62,13 @@ hipError_t launch_causal_valu(const Problem &p, const ValuWork &w, hipStream_t s
 hipError_t launch_logits(const Problem &p, float *useg, float *s_out, float4 *agg, float2 *rope_tab,
                          hipStream_t stream);
 hipError_t launch_causal_mfma(const Problem &p, const CausalWork &w, hipStream_t stream);
-hipError_t launch_encoder(const Problem &p, hipStream_t stream);
+// Encoder: `work` is caller scratch of encoder_work_bytes(p) bytes (NULL when that is 0).
+hipError_t launch_encoder(const Problem &p, void *work, hipStream_t stream);
 // Matrix-core encoder for bfloat16, d in {64, 128}: the logits stay in LDS up to kEncoderMfmaMaxN
-// tokens, beyond that in stream-ordered global scratch.
+// tokens, beyond that in the caller's scratch (4 N bytes per (b, h, 16-column tile)).
 constexpr int kEncoderMfmaMaxN = 4096;
-hipError_t launch_encoder_mfma(const Problem &p, hipStream_t stream);
+size_t encoder_work_bytes(const Problem &p);
+hipError_t launch_encoder_mfma(const Problem &p, float *work, hipStream_t stream);
 hipError_t launch_decode(const Problem &p, hipStream_t stream);
 
 }  // namespace zeros

@@ -10,9 +10,6 @@
 
 #include "launch.hpp"
 
-namespace zeros {
-}
-
 namespace {
 // The matrix-core path covers bfloat16 inputs with d in {64, 128}; everything else (float32
 // inputs, small heads) runs on the float32 VALU kernel.
@@ -148,6 +145,19 @@ zeros_status hip_result(hipError_t err, const char *fn) {
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// The library allocates nothing: scratch comes from the caller. `need` = 0 accepts any workspace
+// (including NULL).
+zeros_status check_workspace(const void *ws, size_t bytes, size_t need, const char *fn) {
+    if (need == 0) return ZEROS_OK;
+    if (!ws)
+        return fail(ZEROS_ERR_NULL, std::string(fn) + ": workspace is NULL but this call needs " + std::to_string(need) +
+                                        " bytes of scratch (see the *_workspace_bytes query)");
+    if (bytes < need) return fail(ZEROS_ERR_SHAPE, std::string(fn) + ": workspace smaller than the *_workspace_bytes query");
+    if (reinterpret_cast<uintptr_t>(ws) & 255u)
+        return fail(ZEROS_ERR_SHAPE, std::string(fn) + ": workspace must be 256-byte aligned");
+    return ZEROS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -194,25 +204,11 @@ zeros_status zeros_fwd_causal(const zeros_shape *shape, const void *q, const voi
     const bool mfma = causal_uses_mfma(shape) && !(state_in && shape->N == 0);
     const size_t need = mfma ? zeros::causal_work_bytes(shape->B, shape->H, shape->N, shape->d_u)
                              : zeros::causal_valu_work_bytes(shape->B, shape->H, shape->N, shape->d_u);
-    void *ws = workspace;
-    bool owned = false;
-    if (ws) {
-        if (workspace_bytes < need)
-            return fail(ZEROS_ERR_SHAPE, "zeros_fwd_causal: workspace smaller than zeros_fwd_causal_workspace_bytes()");
-        if (reinterpret_cast<uintptr_t>(ws) & 255u)
-            return fail(ZEROS_ERR_SHAPE, "zeros_fwd_causal: workspace must be 256-byte aligned");
-    } else if (need > 0) {          // (an empty sequence on the float32 path needs none)
-        hipError_t err = hipMallocAsync(&ws, need, hs);
-        if (err != hipSuccess) return hip_result(err, "zeros_fwd_causal (workspace)");
-        owned = true;
-    }
+    st = check_workspace(workspace, workspace_bytes, need, "zeros_fwd_causal");
+    if (st != ZEROS_OK) return st;
     const int B = shape->B, H = shape->H, N = shape->N, du = shape->d_u;
-    hipError_t err = mfma ? zeros::launch_causal_mfma(p, zeros::causal_work_carve(ws, B, H, N, du), hs)
-                          : zeros::launch_causal_valu(p, zeros::causal_valu_work_carve(ws, B, H, N, du), hs);
-    if (owned) {
-        hipError_t e2 = hipFreeAsync(ws, hs);
-        if (err == hipSuccess) err = e2;
-    }
+    const hipError_t err = mfma ? zeros::launch_causal_mfma(p, zeros::causal_work_carve(workspace, B, H, N, du), hs)
+                                : zeros::launch_causal_valu(p, zeros::causal_valu_work_carve(workspace, B, H, N, du), hs);
     return hip_result(err, "zeros_fwd_causal");
 }
 
@@ -220,18 +216,30 @@ size_t zeros_fwd_causal_workspace_bytes(const zeros_shape *shape) {
     if (!shape || shape->B < 1 || shape->H < 1 || shape->N < 0 || shape->d_u < 1) return 0;
     const size_t valu = zeros::causal_valu_work_bytes(shape->B, shape->H, shape->N, shape->d_u);
     if (!causal_uses_mfma(shape)) return valu;
-    // a call with state_in takes the float32 path: cover both
+    // a call continued from a state with N = 0 (a copy of the state) takes the float32 path;
+    // every other call of this shape takes the matrix-core path: cover both
     return std::max(valu, zeros::causal_work_bytes(shape->B, shape->H, shape->N, shape->d_u));
 }
 
 zeros_status zeros_fwd_encoder(const zeros_shape *shape, const void *q, const void *k, const void *v,
                                const void *u, const float *mu, const float *tau, const void *g1,
-                               const void *gh, const void *g0, void *o, void *stream) {
+                               const void *gh, const void *g0, void *o, void *workspace,
+                               size_t workspace_bytes, void *stream) {
     zeros_status st = check_common(shape, q, k, v, u, mu, tau, g1, gh, g0, o, "zeros_fwd_encoder");
     if (st != ZEROS_OK) return st;
     if (shape->N == 0) return ok();
     const zeros::Problem p = make_problem(shape, q, k, v, u, mu, tau, g1, gh, g0, o, nullptr);
-    return hip_result(zeros::launch_encoder(p, static_cast<hipStream_t>(stream)), "zeros_fwd_encoder");
+    st = check_workspace(workspace, workspace_bytes, zeros::encoder_work_bytes(p), "zeros_fwd_encoder");
+    if (st != ZEROS_OK) return st;
+    return hip_result(zeros::launch_encoder(p, workspace, static_cast<hipStream_t>(stream)), "zeros_fwd_encoder");
+}
+
+size_t zeros_fwd_encoder_workspace_bytes(const zeros_shape *shape) {
+    if (!shape || shape->B < 1 || shape->H < 1 || shape->N < 0 || shape->d < 1 || shape->d_u < 1) return 0;
+    zeros::Problem p{};
+    p.B = shape->B; p.H = shape->H; p.N = shape->N; p.d = shape->d; p.du = shape->d_u;
+    p.dtype = shape->dtype;
+    return zeros::encoder_work_bytes(p);
 }
 
 zeros_status zeros_decode_step(const zeros_shape *shape, const void *q, const void *k, const void *v,

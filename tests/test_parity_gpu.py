@@ -318,22 +318,20 @@ def test_encoder_mfma_large_logits():
     assert rel_l2(o, ref) <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("scale,tol", [(10.0, 1e-4), (30.0, 1e-3)])
-def test_logit_stress_running_max(scale, tol):
-    """float32 inputs with u scaled by 10 and 30: the running maximum must keep e^{s} finite.
-
-    Bar at u x 30: the logits reach |s| of about 3.7e3 there (|s| ~ 4e2 at u x 10). Computing s in
-    float32 alone leaves an absolute error of up to |s| 2^-24 = 2.2e-4 in s, and e^{s - m} carries
-    that as a relative error in every softmax-type weight, so the float32 output cannot be held to
-    1e-4 at u x 30; the bar is 1e-3, 4.5 times that conditioning floor. At u x 10 the floor is
-    2.5e-5 and the 1e-4 contract applies."""
+@pytest.mark.parametrize("scale", [10.0, 30.0])
+def test_logit_stress_running_max(scale):
+    """float32 inputs with u scaled by 10 and 30: the running maximum must keep e^{s} finite, and
+    the 1e-4 contract still holds. At u x 30 the logits reach |s| of about 3.7e3, so float32
+    rounding puts absolute errors of up to |s| 2^-24 = 2.2e-4 on them; but those extreme logits
+    are the very negative ones at the start of the sequence, whose weights e^{s - m} vanish. Near
+    the running maximum |s| <= 214, which bounds the relative error of e^{s - m} by 1.3e-5."""
     wl = CONFIGS[2].with_(B=1, H=4, N=300, seed=77)
     x = make_inputs(wl, u_scale=scale)
     o = to_f64(run_causal(x, "f32"))
     assert np.all(np.isfinite(o))
     err = rel_l2(o, R.causal_forward(**x))
-    print(f"logit stress u x {scale}: rel_l2={err:.3e} (bar {tol:g})", flush=True)
-    assert err <= tol
+    print(f"logit stress u x {scale}: rel_l2={err:.3e}", flush=True)
+    assert err <= TOL["f32"]
 
 
 def test_first_row_zero_and_constant_logits():

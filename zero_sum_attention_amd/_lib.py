@@ -209,9 +209,9 @@ def zeros_fwd_causal(q, k, v, u, mu, tau, g1, gh, *, g0: torch.Tensor | None = N
     o = _alloc_on(s_, lambda: torch.empty_like(v)) if out is None else out
     _need(o.shape == v.shape and o.dtype == v.dtype and o.is_contiguous() and o.device == q.device,
           "out must match v")
-    for name, s_ in (("state_in", state_in), ("state_out", state_out)):
-        if s_ is not None:
-            _need((s_.S, s_.H, s_.d, s_.d_u) == (q.shape[0], q.shape[1], q.shape[-1], u.shape[-1]),
+    for name, st_ in (("state_in", state_in), ("state_out", state_out)):
+        if st_ is not None:
+            _need((st_.S, st_.H, st_.d, st_.d_u) == (q.shape[0], q.shape[1], q.shape[-1], u.shape[-1]),
                   f"{name} sizes differ")
     lib = load_library()
     shp = _shape(q, u, q.shape[2], rope, rope_base)

@@ -26,10 +26,12 @@
  *
  * Conventions shared by every entry point
  *   Memory:    every pointer is DEVICE memory owned by the caller; the library allocates no
- *              memory and keeps no state between calls (an error message is kept per thread,
- *              and a per-device flag records that a kernel attribute was set). Scratch memory
- *              comes from the caller as a workspace argument whose size a *_workspace_bytes
- *              query gives; a call that needs scratch and gets none returns ZEROS_ERR_NULL.
+ *              memory at run time and keeps no state between calls (an error message is kept
+ *              per thread, a per-device flag records that a kernel attribute was set, and the
+ *              device address of the fixed scratch array of zeros_fwd_causal_noalloc is kept
+ *              per device). Scratch memory comes from the caller as a workspace argument whose
+ *              size a *_workspace_bytes query gives; a call that needs scratch and gets none
+ *              returns ZEROS_ERR_NULL.
  *              Token tensors (q, k, v, u, g1, gh, o) may be NULL when N = 0; mu and tau never;
  *              g0 may always be NULL.
  *   Layout:    contiguous row-major, feature dimension innermost:
@@ -131,6 +133,27 @@ zeros_status zeros_fwd_causal(const zeros_shape *shape,
 /* Scratch bytes zeros_fwd_causal needs for `shape`, with or without state_in (0 if it needs none,
  * or if shape is invalid). Depends on B, H, N, d, d_u and dtype only. */
 size_t zeros_fwd_causal_workspace_bytes(const zeros_shape *shape);
+
+/*
+ * zeros_fwd_causal without a workspace and without any allocation, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). Same arguments, results and validation as zeros_fwd_causal; the scratch is
+ * a fixed array of ZEROS_NOALLOC_SCRATCH_BYTES in device memory, one per GPU, held from the
+ * library's load until the process ends. A call whose zeros_fwd_causal_workspace_bytes exceeds
+ * that size returns ZEROS_ERR_UNSUPPORTED before any launch. Every call on one GPU uses that GPU's
+ * array, so calls that overlap in time on the same GPU (on different streams, or from different
+ * threads without ordering) race and give undefined results; calls ordered on one stream are
+ * safe. No part of the array needs to start at zero (every region is written before it is read
+ * within a call). The first call on a device resolves the array's device address
+ * (hipGetSymbolAddress) and keeps it.
+ */
+#define ZEROS_NOALLOC_SCRATCH_BYTES (64u << 20)
+zeros_status zeros_fwd_causal_noalloc(const zeros_shape *shape,
+                                      const void *q, const void *k, const void *v, const void *u,
+                                      const float *mu, const float *tau,
+                                      const void *g1, const void *gh, const void *g0,
+                                      void *o, const zeros_state *state_in, const zeros_state *state_out,
+                                      void *stream);
 
 /*
  * Encoder (non-causal) forward (Paper-Notes 损失函数 / 训练策略: both modes are supported).

@@ -183,6 +183,19 @@ def test_encoder_workspace_bytes(lib, kw, need):
     assert lib.zeros_fwd_encoder_workspace_bytes(ctypes.byref(shape(B=2, H=3, **kw))) == need
 
 
+def test_noalloc_rejects_oversize_on_the_host(lib):
+    """zeros_fwd_causal_noalloc refuses a call whose scratch exceeds its fixed array before any
+    HIP call (placeholder pointers are never used)."""
+    big = shape(B=2, H=16, N=16384, d=128, d_u=128, dtype=1)
+    assert lib.zeros_fwd_causal_workspace_bytes(ctypes.byref(big)) > (64 << 20)
+    p = dict(P)
+    r = lib.zeros_fwd_causal_noalloc(ctypes.byref(big), p["q"], p["k"], p["v"], p["u"], p["mu"], p["tau"],
+                                     p["g1"], p["gh"], None, p["o"], None, None, None)
+    assert r == L.ZEROS_ERR_UNSUPPORTED
+    assert "more than the fixed" in lib.zeros_last_error().decode()
+    assert lib.zeros_fwd_causal_noalloc(None, *([None] * 12)) == L.ZEROS_ERR_NULL
+
+
 def test_partial_state_rejected(lib):
     st = L.zeros_state(1, 2, 3, 4, 5, 6, 7, None)
     assert call_causal(lib, shape(), state=ctypes.byref(st)) == L.ZEROS_ERR_NULL

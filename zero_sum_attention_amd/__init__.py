@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     load_library,
     zeros_decode_step,
     zeros_fwd_causal,
+    zeros_fwd_causal_noalloc,
     zeros_fwd_causal_workspace_bytes,
     zeros_fwd_encoder,
     zeros_fwd_encoder_workspace_bytes,

@@ -56,6 +56,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.zeros_fwd_causal.argtypes = fwd + [ctypes.POINTER(zeros_state), ctypes.POINTER(zeros_state), vp,
                                            ctypes.c_size_t, vp]
     lib.zeros_fwd_causal.restype = i32
+    lib.zeros_fwd_causal_noalloc.argtypes = fwd + [ctypes.POINTER(zeros_state), ctypes.POINTER(zeros_state), vp]
+    lib.zeros_fwd_causal_noalloc.restype = i32
     lib.zeros_fwd_causal_workspace_bytes.argtypes = [ctypes.POINTER(zeros_shape)]
     lib.zeros_fwd_causal_workspace_bytes.restype = ctypes.c_size_t
     lib.zeros_fwd_encoder.argtypes = fwd + [vp, ctypes.c_size_t, vp]
@@ -223,6 +225,32 @@ def zeros_fwd_causal(q, k, v, u, mu, tau, g1, gh, *, g0: torch.Tensor | None = N
                                 _ptr(tau), _ptr(g1), _ptr(gh), _ptr(g0), _ptr(o), sti, st,
                                 _ptr(workspace), 0 if workspace is None else workspace.numel(),
                                 s_.cuda_stream))
+    return o
+
+
+def zeros_fwd_causal_noalloc(q, k, v, u, mu, tau, g1, gh, *, g0: torch.Tensor | None = None, rope: bool = False,
+                             rope_base: float = 10000.0, out: torch.Tensor | None = None,
+                             state_in: DecodeState | None = None, state_out: DecodeState | None = None,
+                             stream=None) -> torch.Tensor:
+    """zeros_fwd_causal through the entry point that allocates nothing (its scratch is a fixed
+    per-GPU array of ZEROS_NOALLOC_SCRATCH_BYTES). Calls that overlap on one GPU race; ``out``
+    lets the caller avoid torch's allocation of the output as well."""
+    _check_tensors(q, k, v, u, mu, tau, g1, gh, 1, g0)
+    s_ = _stream(q.device, stream)
+    o = _alloc_on(s_, lambda: torch.empty_like(v)) if out is None else out
+    _need(o.shape == v.shape and o.dtype == v.dtype and o.is_contiguous() and o.device == q.device,
+          "out must match v")
+    for name, st_ in (("state_in", state_in), ("state_out", state_out)):
+        if st_ is not None:
+            _need((st_.S, st_.H, st_.d, st_.d_u) == (q.shape[0], q.shape[1], q.shape[-1], u.shape[-1]),
+                  f"{name} sizes differ")
+    lib = load_library()
+    shp = _shape(q, u, q.shape[2], rope, rope_base)
+    _check(lib.zeros_fwd_causal_noalloc(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(u), _ptr(mu),
+                                        _ptr(tau), _ptr(g1), _ptr(gh), _ptr(g0), _ptr(o),
+                                        ctypes.byref(state_in.c) if state_in is not None else None,
+                                        ctypes.byref(state_out.c) if state_out is not None else None,
+                                        s_.cuda_stream))
     return o
 
 

@@ -3,12 +3,19 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
 #include <string>
 
 #include "launch.hpp"
+
+// Fixed scratch of zeros_fwd_causal_noalloc: one copy per device, held until the process ends.
+// Host code never uses its name as an address (on the host it is only a stand-in): the device
+// address comes from hipGetSymbolAddress, once per device with that device current, and is kept
+// per device.
+static __device__ __align__(256) unsigned char scratch[ZEROS_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 // The matrix-core path covers bfloat16 inputs with d in {64, 128}; everything else (float32
@@ -158,6 +165,80 @@ zeros_status check_workspace(const void *ws, size_t bytes, size_t need, const ch
     return ZEROS_OK;
 }
 
+// Validation shared by the causal entry points. On success `noop` tells whether the call has
+// nothing to do (N = 0 without a state to write); otherwise `p` is the problem, `mfma` the path
+// it takes and `need` the scratch bytes of that path.
+zeros_status causal_prepare(const char *fn, const zeros_shape *shape, const void *q, const void *k,
+                            const void *v, const void *u, const float *mu, const float *tau, const void *g1,
+                            const void *gh, const void *g0, void *o, const zeros_state *state_in,
+                            const zeros_state *state_out, zeros::Problem &p, bool &mfma, size_t &need,
+                            bool &noop) {
+    const std::string f(fn);
+    zeros_status st = check_common(shape, q, k, v, u, mu, tau, g1, gh, g0, o, fn);
+    if (st != ZEROS_OK) return st;
+    if (state_in && !state_complete(state_in)) return fail(ZEROS_ERR_NULL, f + ": a state_in field is NULL");
+    if (state_in && !state_aligned(state_in))
+        return fail(ZEROS_ERR_SHAPE, f + ": state_in matrices must be 16-byte aligned");
+    if (state_out && !state_complete(state_out)) return fail(ZEROS_ERR_NULL, f + ": a state_out field is NULL");
+    if (state_out && !state_aligned(state_out))
+        return fail(ZEROS_ERR_SHAPE, f + ": state_out matrices must be 16-byte aligned");
+    if (state_out) {
+        st = check_written_state(state_out, shape, q, k, v, u, mu, tau, g1, gh, g0, o, fn);
+        if (st != ZEROS_OK) return st;
+    }
+    if (state_in && state_out) {
+        Range a[8], b[8];
+        state_ranges(state_in, shape, a);
+        state_ranges(state_out, shape, b);
+        for (const Range &x : a)
+            for (const Range &y : b)
+                if (overlap(x, y)) return fail(ZEROS_ERR_ALIAS, f + ": state_out overlaps state_in");
+    }
+    if (state_in && shape->N != 0) {
+        Range a[8];
+        state_ranges(state_in, shape, a);
+        const Range out{o, static_cast<size_t>(shape->B) * shape->H * shape->N * shape->d * elem_bytes(shape->dtype)};
+        for (const Range &x : a)
+            if (overlap(x, out)) return fail(ZEROS_ERR_ALIAS, f + ": o overlaps state_in");
+    }
+    noop = shape->N == 0 && !state_out;
+    if (noop) return ZEROS_OK;
+    p = make_problem(shape, q, k, v, u, mu, tau, g1, gh, g0, o, state_out);
+    if (state_in) p.sin = *state_in;
+    // a continued empty call (a copy of the state) takes the float32 path
+    mfma = causal_uses_mfma(shape) && !(state_in && shape->N == 0);
+    need = mfma ? zeros::causal_work_bytes(shape->B, shape->H, shape->N, shape->d_u)
+                : zeros::causal_valu_work_bytes(shape->B, shape->H, shape->N, shape->d_u);
+    return ZEROS_OK;
+}
+
+hipError_t causal_launch(const zeros::Problem &p, bool mfma, void *ws, hipStream_t hs) {
+    return mfma ? zeros::launch_causal_mfma(p, zeros::causal_work_carve(ws, p.B, p.H, p.N, p.du), hs)
+                : zeros::launch_causal_valu(p, zeros::causal_valu_work_carve(ws, p.B, p.H, p.N, p.du), hs);
+}
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch array.
+zeros_status scratch_for_current_device(void **ptr, const char *fn) {
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return hip_result(err, fn);
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(ZEROS_ERR_UNSUPPORTED, std::string(fn) + ": device index beyond the supported 64");
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        // two threads may both resolve it on a first call; they store the same address
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess) return hip_result(err, fn);
+        if (!p) return fail(ZEROS_ERR_HIP, std::string(fn) + ": hipGetSymbolAddress returned NULL");
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    *ptr = p;
+    return ZEROS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -167,49 +248,39 @@ zeros_status zeros_fwd_causal(const zeros_shape *shape, const void *q, const voi
                               const void *gh, const void *g0, void *o, const zeros_state *state_in,
                               const zeros_state *state_out, void *workspace, size_t workspace_bytes,
                               void *stream) {
-    zeros_status st = check_common(shape, q, k, v, u, mu, tau, g1, gh, g0, o, "zeros_fwd_causal");
+    zeros::Problem p{};
+    bool mfma = false, noop = false;
+    size_t need = 0;
+    zeros_status st = causal_prepare("zeros_fwd_causal", shape, q, k, v, u, mu, tau, g1, gh, g0, o, state_in,
+                                     state_out, p, mfma, need, noop);
     if (st != ZEROS_OK) return st;
-    if (state_in && !state_complete(state_in))
-        return fail(ZEROS_ERR_NULL, "zeros_fwd_causal: a state_in field is NULL");
-    if (state_in && !state_aligned(state_in))
-        return fail(ZEROS_ERR_SHAPE, "zeros_fwd_causal: state_in matrices must be 16-byte aligned");
-    if (state_out && !state_complete(state_out))
-        return fail(ZEROS_ERR_NULL, "zeros_fwd_causal: a state_out field is NULL");
-    if (state_out && !state_aligned(state_out))
-        return fail(ZEROS_ERR_SHAPE, "zeros_fwd_causal: state_out matrices must be 16-byte aligned");
-    if (state_out) {
-        st = check_written_state(state_out, shape, q, k, v, u, mu, tau, g1, gh, g0, o, "zeros_fwd_causal");
-        if (st != ZEROS_OK) return st;
-    }
-    if (state_in && state_out) {
-        Range a[8], b[8];
-        state_ranges(state_in, shape, a);
-        state_ranges(state_out, shape, b);
-        for (const Range &x : a)
-            for (const Range &y : b)
-                if (overlap(x, y)) return fail(ZEROS_ERR_ALIAS, "zeros_fwd_causal: state_out overlaps state_in");
-    }
-    if (state_in && shape->N != 0) {
-        Range a[8];
-        state_ranges(state_in, shape, a);
-        const Range out{o, static_cast<size_t>(shape->B) * shape->H * shape->N * shape->d * elem_bytes(shape->dtype)};
-        for (const Range &x : a)
-            if (overlap(x, out)) return fail(ZEROS_ERR_ALIAS, "zeros_fwd_causal: o overlaps state_in");
-    }
-    if (shape->N == 0 && !state_out) return ok();
-    zeros::Problem p = make_problem(shape, q, k, v, u, mu, tau, g1, gh, g0, o, state_out);
-    if (state_in) p.sin = *state_in;
-    hipStream_t hs = static_cast<hipStream_t>(stream);
-    // a continued empty call (a copy of the state) takes the float32 path
-    const bool mfma = causal_uses_mfma(shape) && !(state_in && shape->N == 0);
-    const size_t need = mfma ? zeros::causal_work_bytes(shape->B, shape->H, shape->N, shape->d_u)
-                             : zeros::causal_valu_work_bytes(shape->B, shape->H, shape->N, shape->d_u);
+    if (noop) return ok();
     st = check_workspace(workspace, workspace_bytes, need, "zeros_fwd_causal");
     if (st != ZEROS_OK) return st;
-    const int B = shape->B, H = shape->H, N = shape->N, du = shape->d_u;
-    const hipError_t err = mfma ? zeros::launch_causal_mfma(p, zeros::causal_work_carve(workspace, B, H, N, du), hs)
-                                : zeros::launch_causal_valu(p, zeros::causal_valu_work_carve(workspace, B, H, N, du), hs);
-    return hip_result(err, "zeros_fwd_causal");
+    return hip_result(causal_launch(p, mfma, workspace, static_cast<hipStream_t>(stream)), "zeros_fwd_causal");
+}
+
+zeros_status zeros_fwd_causal_noalloc(const zeros_shape *shape, const void *q, const void *k, const void *v,
+                                      const void *u, const float *mu, const float *tau, const void *g1,
+                                      const void *gh, const void *g0, void *o, const zeros_state *state_in,
+                                      const zeros_state *state_out, void *stream) {
+    const char *fn = "zeros_fwd_causal_noalloc";
+    zeros::Problem p{};
+    bool mfma = false, noop = false;
+    size_t need = 0;
+    zeros_status st = causal_prepare(fn, shape, q, k, v, u, mu, tau, g1, gh, g0, o, state_in, state_out, p, mfma,
+                                     need, noop);
+    if (st != ZEROS_OK) return st;
+    if (noop) return ok();
+    if (need > static_cast<size_t>(ZEROS_NOALLOC_SCRATCH_BYTES))
+        return fail(ZEROS_ERR_UNSUPPORTED, std::string(fn) + ": this call needs " + std::to_string(need) +
+                                               " bytes of scratch, more than the fixed " +
+                                               std::to_string(static_cast<size_t>(ZEROS_NOALLOC_SCRATCH_BYTES)) +
+                                               " (use zeros_fwd_causal with a workspace)");
+    void *ws = nullptr;
+    st = scratch_for_current_device(&ws, fn);
+    if (st != ZEROS_OK) return st;
+    return hip_result(causal_launch(p, mfma, ws, static_cast<hipStream_t>(stream)), fn);
 }
 
 size_t zeros_fwd_causal_workspace_bytes(const zeros_shape *shape) {

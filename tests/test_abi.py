@@ -193,7 +193,7 @@ def test_noalloc_rejects_oversize_on_the_host(lib):
                                      p["g1"], p["gh"], None, p["o"], None, None, None)
     assert r == L.ZEROS_ERR_UNSUPPORTED
     assert "more than the fixed" in lib.zeros_last_error().decode()
-    assert lib.zeros_fwd_causal_noalloc(None, *([None] * 12)) == L.ZEROS_ERR_NULL
+    assert lib.zeros_fwd_causal_noalloc(None, *([None] * 13)) == L.ZEROS_ERR_NULL
 
 
 def test_partial_state_rejected(lib):

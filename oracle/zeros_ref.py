@@ -45,6 +45,10 @@ Readings taken where the pages leave a step open (each is listed in the design n
   * A running maximum m_t of the logits rescales e^{s}: the state stores
     Et = sum e^{s_i - m_t} and Ft = sum e^{s_i - m_t} k^_i^T v_i (this leaves o unchanged).
 
+Backward: ``causal_backward`` gives the gradients of L = <dO, o> for every input, by the chain
+rule through the explicit weight definition (training replaces attention by this module
+[Notes/training]); it is pinned by finite differences of the recurrent forward.
+
 Array conventions: leading dimensions [B, H] (any number of leading dims works), then tokens,
 then features. All arithmetic is float64.
 """
@@ -343,3 +347,118 @@ def encoder_brute_force(q, k, v, u, mu, tau, g1, gh, rope=False, rope_base=10000
     W = explicit_weights_encoder(s, g1, gh, g0)
     cos = qh @ np.swapaxes(kh, -1, -2)
     return (W * cos) @ _f64(v)
+
+
+# --------------------------------------------------------------------------------------------
+# Backward pass: gradients of L = <dO, o> for the causal forward, by the chain rule through the
+# explicit O(N^2) definition above (training uses the module in place of attention:
+# [Notes/training]). Pinned by central finite differences of the recurrent ``causal_forward``.
+# --------------------------------------------------------------------------------------------
+
+def _unbroadcast(grad, shape):
+    """Sum ``grad`` over the leading axes that broadcasting added to an input of ``shape``."""
+    grad = _f64(grad)
+    while grad.ndim > len(shape):
+        grad = grad.sum(axis=0)
+    for ax, n in enumerate(shape):
+        if n == 1 and grad.shape[ax] != 1:
+            grad = grad.sum(axis=ax, keepdims=True)
+    return grad
+
+
+def causal_backward(q, k, v, u, mu, tau, g1, gh, dO, rope=False, rope_base=10000.0, g0=None):
+    """Gradients of L = sum_t dO_t . o_t through the causal forward.
+
+    Shapes as in ``causal_forward``; dO [..., N, d]. Returns a dict with the gradients of q, k, v,
+    u (the shapes of the inputs), mu and tau (summed over the dims they were broadcast over: the
+    batch for per-head parameters), g1, gh and, when g0 is given, g0. Steps, in the order of the
+    forward definition [Notes/zero-sum], [Notes/radial], [Notes/logits]:
+      o = (W * C) v with C_{t,i} = q^_t . k^_i and the explicit weights W (i <= t);
+      W_{t,i} = sigma1_t delta_{t,i}/t + sigmah_t eps_{t,i} (+ sigma0_t/t),
+      delta_{t,i} = s_i - mean_{j<=t} s_j, eps = softmax_{t,i} - 1/t - delta/t;
+      s_i = -(u_i . ubar_i)/sqrt(d_u), ubar_i = (e^tau mu + sum_{j<=i} u_j)/(e^tau + i);
+      q^ = RoPE(q/|q|), k^ = RoPE(k/|k|).
+    """
+    q, k, v, u, dO = _f64(q), _f64(k), _f64(v), _f64(u), _f64(dO)
+    lead = q.shape[:-2]
+    N, d = q.shape[-2], q.shape[-1]
+    du_dim = u.shape[-1]
+    mu_in, tau_in = _f64(mu), _f64(tau)
+    mu_b = np.broadcast_to(mu_in, lead + (du_dim,))
+    tau_b = np.broadcast_to(tau_in, lead)
+    tt = np.arange(1, N + 1, dtype=F64)                       # 1-based positions
+    mask = np.tril(np.ones((N, N), dtype=bool))               # i <= t
+
+    # ---- forward quantities of the explicit definition
+    nq = np.maximum(np.sqrt(np.sum(q * q, axis=-1, keepdims=True)), 1e-12)
+    nk = np.maximum(np.sqrt(np.sum(k * k, axis=-1, keepdims=True)), 1e-12)
+    uq, uk = q / nq, k / nk                                   # unit vectors before RoPE
+    pos = np.arange(N, dtype=F64)
+    qh = rope_rotate(uq, pos, rope_base) if rope else uq
+    kh = rope_rotate(uk, pos, rope_base) if rope else uk
+    emu, et = _prior(mu_b, tau_b)
+    S = np.cumsum(u, axis=-2)
+    den = et[..., None] + tt                                  # e^tau + i
+    ubar = (emu[..., None, :] + S) / den[..., None]
+    s = -np.sum(u * ubar, axis=-1) / np.sqrt(F64(du_dim))
+    sig1, sigh = sigmoid(g1), sigmoid(gh)
+    sig0 = sigmoid(g0) if g0 is not None else None
+    srow = np.where(mask, s[..., None, :], -np.inf)           # [..., t, i]
+    ex = np.exp(srow - np.max(srow, axis=-1, keepdims=True))
+    sm = ex / np.sum(ex, axis=-1, keepdims=True)              # softmax over i <= t (0 above)
+    mean = np.cumsum(s, axis=-1) / tt                         # (1/t) sum_{j<=t} s_j
+    delta = np.where(mask, s[..., None, :] - mean[..., :, None], 0.0)
+    eps = np.where(mask, sm - 1.0 / tt[:, None] - delta / tt[:, None], 0.0)
+    W = sig1[..., :, None] * delta / tt[:, None] + sigh[..., :, None] * eps
+    if sig0 is not None:
+        W = W + np.where(mask, sig0[..., :, None] / tt[:, None], 0.0)
+    C = qh @ np.swapaxes(kh, -1, -2)
+
+    # ---- o = (W * C) v
+    Pm = W * C
+    dv = np.swapaxes(Pm, -1, -2) @ dO
+    dP = np.where(mask, dO @ np.swapaxes(v, -1, -2), 0.0)     # dO_t . v_i
+    dW = dP * C
+    dC = dP * W
+    dqh = dC @ kh
+    dkh = np.swapaxes(dC, -1, -2) @ qh
+
+    # ---- W = sigma1 delta/t + sigmah eps (+ sigma0/t)
+    dsig1 = np.sum(dW * delta, axis=-1) / tt
+    dsigh = np.sum(dW * eps, axis=-1)
+    dsig0 = np.sum(dW, axis=-1) / tt if sig0 is not None else None
+    # eps = sm - 1/t - delta/t, so delta enters W with (sigma1 - sigmah)/t and sm with sigmah
+    ddelta = dW * ((sig1 - sigh)[..., :, None] / tt[:, None])
+    dsm = dW * sigh[..., :, None]
+    # delta_{t,i} = s_i - (1/t) sum_{j<=t} s_j
+    ds = np.sum(ddelta, axis=-2)
+    rowsum = np.sum(ddelta, axis=-1)                          # [..., t]
+    ds = ds - np.where(mask, (rowsum / tt)[..., :, None], 0.0).sum(axis=-2)
+    # softmax Jacobian per row t: ds_j += sm_tj (dsm_tj - sum_i sm_ti dsm_ti)
+    inner = np.sum(sm * dsm, axis=-1, keepdims=True)
+    ds = ds + np.sum(sm * (dsm - inner), axis=-2)
+
+    # ---- s = -(u . ubar)/sqrt(d_u), ubar_i = (e^tau mu + S_i)/(e^tau + i), S_i = sum_{j<=i} u_j
+    rs = 1.0 / np.sqrt(F64(du_dim))
+    du_ = -ubar * (ds * rs)[..., None]
+    dubar = -u * (ds * rs)[..., None]
+    dS = dubar / den[..., None]
+    du_ = du_ + np.flip(np.cumsum(np.flip(dS, axis=-2), axis=-2), axis=-2)   # sum over i >= j
+    dmu_full = et[..., None] * np.sum(dS, axis=-2)
+    dtau_full = np.sum(np.sum(dubar * (mu_b[..., None, :] - ubar), axis=-1) * et[..., None] / den, axis=-1)
+
+    # ---- q^ = RoPE(q/|q|): undo the rotation, then project out the radial direction
+    if rope:
+        dqh = rope_rotate(dqh, -pos, rope_base)
+        dkh = rope_rotate(dkh, -pos, rope_base)
+    dq = (dqh - uq * np.sum(uq * dqh, axis=-1, keepdims=True)) / nq
+    dk = (dkh - uk * np.sum(uk * dkh, axis=-1, keepdims=True)) / nk
+
+    out = {
+        "q": dq, "k": dk, "v": dv, "u": du_,
+        "mu": _unbroadcast(dmu_full, mu_in.shape), "tau": _unbroadcast(dtau_full, tau_in.shape),
+        "g1": dsig1 * sig1 * (1.0 - sig1), "gh": dsigh * sigh * (1.0 - sigh),
+    }
+    if sig0 is not None:
+        out["g0"] = dsig0 * sig0 * (1.0 - sig0)
+    return out

@@ -80,13 +80,14 @@ def round_to_dtype(x: np.ndarray, dtype: str) -> np.ndarray:
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
-def make_inputs(wl: Workload, *, u_scale: float = 1.0, gate0: bool = False) -> dict:
+def make_inputs(wl: Workload, *, u_scale: float = 1.0, gate0: bool = False, grad_out: bool = False) -> dict:
     """Draw one batch of inputs for ``wl``.
 
     Shapes: q, k, v [B, H, N, d]; u [B, H, N, d_u]; mu [H, d_u]; tau [H]; g1, gh [B, H, N].
     For decode workloads N is 1 (one new token per sequence). ``u_scale`` multiplies u before
     rounding (logit stress cases). ``gate0`` adds zero-order gate pre-activations g0 ~ N(0, 1)
-    [B, H, N], drawn after everything else so the other inputs do not change.
+    [B, H, N], drawn after everything else so the other inputs do not change. ``grad_out`` adds
+    an upstream gradient dO ~ N(0, 1) [B, H, N, d] (the backward pass's input), drawn last.
     """
     rng = np.random.default_rng(wl.seed)
     B, H, N, d, du = wl.B, wl.H, wl.N, wl.d, wl.d_u
@@ -111,6 +112,8 @@ def make_inputs(wl: Workload, *, u_scale: float = 1.0, gate0: bool = False) -> d
     }
     if gate0:
         out["g0"] = round_to_dtype(rng.standard_normal((B, H, N), dtype=np.float32), dt)
+    if grad_out:
+        out["dO"] = round_to_dtype(rng.standard_normal((B, H, N, d), dtype=np.float32), dt)
     return out
 
 

@@ -4,7 +4,8 @@ Each case below changes one step of the float64 oracle's source text (a dropped 
 an index or scale off by one, a transposed operand), loads the changed module in place of
 ``oracle.zeros_ref`` in a fresh interpreter, and runs the oracle's pin tests
 (``tests/test_oracle.py``: hand-worked fixtures, closed forms, the explicit O(N^2) weights,
-library softmax limits, invariants). Every planted mistake must make at least one pin fail. The
+library softmax limits, invariants; ``tests/test_oracle_backward.py``: finite differences of the
+recurrent forward and the identities of the backward). Every planted mistake must make at least one pin fail. The
 mutation is applied on the CPU, to a copy of the source in memory; nothing is written to disk.
 Each original fragment must occur exactly once, so a case cannot silently stop applying when the
 oracle's text changes.
@@ -29,8 +30,8 @@ MUTATIONS = [
     ("running mean counts i - 1 tokens",
      "ubar = (emu[..., None, :] + S) / (et[..., None, None] + i[:, None])",
      "ubar = (emu[..., None, :] + S) / (et[..., None, None] + i[:, None] - 1.0)"),
-    ("running mean excludes u_i", "    S = np.cumsum(u, axis=-2)\n",
-     "    S = np.cumsum(u, axis=-2) - u\n"),
+    ("running mean excludes u_i", "    S = np.cumsum(u, axis=-2)\n    i = np.arange",
+     "    S = np.cumsum(u, axis=-2) - u\n    i = np.arange"),
     ("recurrent logit excludes u_i", '    st["Su"] += u\n    ubar = (emu + st["Su"]) / (et + tf)[..., None]\n',
      '    ubar = (emu + st["Su"]) / (et + tf)[..., None]\n    st["Su"] += u\n'),
     ("logit scale 1/d instead of 1/sqrt(d)", "return -np.sum(u * ubar, axis=-1) / np.sqrt(F64(du))",
@@ -55,6 +56,29 @@ MUTATIONS = [
     ("delta without the mean", "delta = row - np.mean(row, axis=-1, keepdims=True)", "delta = row"),
     ("eps keeps the uniform term", "eps = sm - 1.0 / t - delta / t", "eps = sm - delta / t"),
     ("zero-order gate without 1/t", "gamma = gamma + _f64(sig0) / t", "gamma = gamma + _f64(sig0)"),
+    # backward
+    ("bwd: softmax Jacobian without its mean term", "ds = ds + np.sum(sm * (dsm - inner), axis=-2)",
+     "ds = ds + np.sum(sm * dsm, axis=-2)"),
+    ("bwd: delta without the row-mean term",
+     "ds = ds - np.where(mask, (rowsum / tt)[..., :, None], 0.0).sum(axis=-2)", ""),
+    ("bwd: delta scaled by sigma1 only", "ddelta = dW * ((sig1 - sigh)[..., :, None] / tt[:, None])",
+     "ddelta = dW * (sig1[..., :, None] / tt[:, None])"),
+    ("bwd: u misses the running-mean path",
+     "du_ = du_ + np.flip(np.cumsum(np.flip(dS, axis=-2), axis=-2), axis=-2)", ""),
+    ("bwd: running-mean path summed over i <= j", "du_ = du_ + np.flip(np.cumsum(np.flip(dS, axis=-2), axis=-2), axis=-2)",
+     "du_ = du_ + np.cumsum(dS, axis=-2)"),
+    ("bwd: mu without e^tau", "dmu_full = et[..., None] * np.sum(dS, axis=-2)", "dmu_full = np.sum(dS, axis=-2)"),
+    ("bwd: tau sign", "dtau_full = np.sum(np.sum(dubar * (mu_b[..., None, :] - ubar)",
+     "dtau_full = np.sum(np.sum(dubar * (ubar - mu_b[..., None, :])"),
+    ("bwd: RoPE not undone", "        dqh = rope_rotate(dqh, -pos, rope_base)\n", ""),
+    ("bwd: norm without the radial projection",
+     "dq = (dqh - uq * np.sum(uq * dqh, axis=-1, keepdims=True)) / nq", "dq = dqh / nq"),
+    ("bwd: v gradient uses W without the cosines", "dv = np.swapaxes(Pm, -1, -2) @ dO",
+     "dv = np.swapaxes(W, -1, -2) @ dO"),
+    ("bwd: k gradient from the untransposed product", "dkh = np.swapaxes(dC, -1, -2) @ qh", "dkh = dC @ qh"),
+    ("bwd: sigmah gradient from delta", "dsigh = np.sum(dW * eps, axis=-1)", "dsigh = np.sum(dW * delta, axis=-1)"),
+    ("bwd: gate derivative", '"g1": dsig1 * sig1 * (1.0 - sig1)', '"g1": dsig1 * sig1'),
+    ("bwd: zero-order gate without 1/t", "dsig0 = np.sum(dW, axis=-1) / tt if", "dsig0 = np.sum(dW, axis=-1) if"),
 ]
 
 RUNNER = r"""
@@ -70,7 +94,7 @@ exec(compile(src.replace(old, new), {oracle!r}, "exec"), mod.__dict__)
 sys.modules["oracle.zeros_ref"] = mod
 oracle.zeros_ref = mod
 import pytest
-sys.exit(pytest.main([{tests!r}, "-x", "-q", "-p", "no:cacheprovider", "-W", "ignore"]))
+sys.exit(pytest.main([{tests!r}, {tests_bwd!r}, "-x", "-q", "-p", "no:cacheprovider", "-W", "ignore"]))
 """
 
 
@@ -83,7 +107,8 @@ def test_fragments_present():
 @pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
 def test_planted_mistake_is_caught(name, old, new):
     code = RUNNER.format(root=ROOT, old=old, new=new, oracle=ORACLE,
-                         tests=os.path.join(ROOT, "tests", "test_oracle.py"))
+                         tests=os.path.join(ROOT, "tests", "test_oracle.py"),
+                         tests_bwd=os.path.join(ROOT, "tests", "test_oracle_backward.py"))
     res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT, timeout=300)
     assert "fragment no longer unique" not in res.stderr, res.stderr[-2000:]
     # pytest exit code 1: a pin failed (the mistake was caught); 0 would mean every pin passed

@@ -187,6 +187,32 @@ zeros_status zeros_decode_step(const zeros_shape *shape,
                                const void *g1, const void *gh, const void *g0,
                                void *o, const zeros_state *state, void *stream);
 
+/*
+ * Backward of the causal forward (training uses the module in place of attention: Paper-Notes
+ * 损失函数 / 训练策略; the gradients follow the chain rule through the explicit weights of
+ * 关键设计): given the upstream gradient dO [B, H, N, d] of o, writes the gradients of
+ * L = sum_t dO_t . o_t with respect to every input: dq, dk, dv [B, H, N, d], du [B, H, N, d_u],
+ * dg1, dgh (and dg0 when g0 is given, else it must be NULL) [B, H, N], all in `dtype`, and
+ * dmu [H, d_u], dtau [H] in float32, summed over the batch (mu and tau are per head). The
+ * forward is recomputed from the inputs (the empty initial state; no state_in / state_out).
+ * Arithmetic is float32 throughout for both dtypes. Gradients must not overlap the inputs, dO or
+ * each other (ZEROS_ERR_ALIAS); dO, dq, dk, dv, du 16-byte aligned, dmu and dtau 4-byte
+ * aligned. workspace: zeros_bwd_causal_workspace_bytes(shape) bytes, 256-byte aligned, caller-
+ * owned, used while the call's work runs on `stream` (float32 copies of q^, k^, v, dO, the three
+ * scans' results and per-token scalars: about 7 N d + 20 N floats per (b, h)); NULL when needed is
+ * ZEROS_ERR_NULL. N = 0 writes zero dmu and dtau.
+ */
+zeros_status zeros_bwd_causal(const zeros_shape *shape,
+                              const void *q, const void *k, const void *v, const void *u,
+                              const float *mu, const float *tau,
+                              const void *g1, const void *gh, const void *g0, const void *dO,
+                              void *dq, void *dk, void *dv, void *du, float *dmu, float *dtau,
+                              void *dg1, void *dgh, void *dg0,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/* Scratch bytes zeros_bwd_causal needs for `shape` (0 for invalid sizes). */
+size_t zeros_bwd_causal_workspace_bytes(const zeros_shape *shape);
+
 /* Bytes of one state for S x H heads when packed by zeros_state_from_buffer (256-B aligned
  * fields, order F, G, Hs, Su, m, E, P, t). Returns 0 for invalid sizes. */
 size_t zeros_state_bytes(int32_t S, int32_t H, int32_t d, int32_t d_u);

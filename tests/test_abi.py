@@ -287,6 +287,7 @@ def test_binding_arity_matches_header(lib):
     text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
     for name in ("zeros_fwd_causal", "zeros_fwd_encoder", "zeros_decode_step",
                  "zeros_fwd_causal_workspace_bytes", "zeros_fwd_encoder_workspace_bytes",
+                 "zeros_fwd_causal_noalloc", "zeros_bwd_causal", "zeros_bwd_causal_workspace_bytes",
                  "zeros_state_bytes", "zeros_state_from_buffer"):
         m = re.search(r"\b%s\s*\(([^)]*)\)\s*;" % name, text)
         assert m, name

@@ -8,6 +8,8 @@ from ._lib import (  # noqa: F401
     DecodeState,
     ZerosError,
     load_library,
+    zeros_bwd_causal,
+    zeros_bwd_causal_workspace_bytes,
     zeros_decode_step,
     zeros_fwd_causal,
     zeros_fwd_causal_noalloc,

@@ -66,6 +66,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.zeros_fwd_encoder_workspace_bytes.restype = ctypes.c_size_t
     lib.zeros_decode_step.argtypes = fwd + [ctypes.POINTER(zeros_state), vp]
     lib.zeros_decode_step.restype = i32
+    lib.zeros_bwd_causal.argtypes = fwd[:10] + [vp] * 5 + [f32p, f32p] + [vp] * 3 + [vp, ctypes.c_size_t, vp]
+    lib.zeros_bwd_causal.restype = i32
+    lib.zeros_bwd_causal_workspace_bytes.argtypes = [ctypes.POINTER(zeros_shape)]
+    lib.zeros_bwd_causal_workspace_bytes.restype = ctypes.c_size_t
     lib.zeros_state_bytes.argtypes = [i32, i32, i32, i32]
     lib.zeros_state_bytes.restype = ctypes.c_size_t
     lib.zeros_state_from_buffer.argtypes = [vp, i32, i32, i32, i32, ctypes.POINTER(zeros_state)]
@@ -305,3 +309,40 @@ def zeros_decode_step(q, k, v, u, mu, tau, g1, gh, state: DecodeState, *, g0: to
                                  _ptr(tau), _ptr(g1), _ptr(gh), _ptr(g0), _ptr(o), ctypes.byref(state.c),
                                  s_.cuda_stream))
     return o
+
+
+def zeros_bwd_causal(q, k, v, u, mu, tau, g1, gh, dO, *, g0: torch.Tensor | None = None, rope: bool = False,
+                     rope_base: float = 10000.0, workspace: torch.Tensor | None = None, stream=None) -> dict:
+    """Gradients of sum(dO * zeros_fwd_causal(...)) for every input (the backward of the causal
+    forward from the empty state). Returns a dict with q, k, v, u, g1, gh (and g0) in the input
+    dtype and mu [H, d_u], tau [H] in float32, summed over the batch."""
+    _check_tensors(q, k, v, u, mu, tau, g1, gh, 1, g0)
+    _need(dO.shape == v.shape and dO.dtype == v.dtype and dO.is_contiguous() and dO.device == q.device,
+          "dO must match v")
+    s_ = _stream(q.device, stream)
+    lib = load_library()
+    shp = _shape(q, u, q.shape[2], rope, rope_base)
+
+    def alloc():
+        out = {"q": torch.empty_like(q), "k": torch.empty_like(k), "v": torch.empty_like(v),
+               "u": torch.empty_like(u), "g1": torch.empty_like(g1), "gh": torch.empty_like(gh),
+               "mu": torch.empty_like(mu), "tau": torch.empty_like(tau)}
+        if g0 is not None:
+            out["g0"] = torch.empty_like(g0)
+        return out
+
+    g = _alloc_on(s_, alloc)
+    workspace = _workspace(lib.zeros_bwd_causal_workspace_bytes(ctypes.byref(shp)), workspace, q.device, s_)
+    _check(lib.zeros_bwd_causal(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(u), _ptr(mu), _ptr(tau),
+                                _ptr(g1), _ptr(gh), _ptr(g0), _ptr(dO), _ptr(g["q"]), _ptr(g["k"]), _ptr(g["v"]),
+                                _ptr(g["u"]), _ptr(g["mu"]), _ptr(g["tau"]), _ptr(g["g1"]), _ptr(g["gh"]),
+                                _ptr(g.get("g0")), _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                                s_.cuda_stream))
+    return g
+
+
+def zeros_bwd_causal_workspace_bytes(B: int, H: int, N: int, d: int, d_u: int, dtype) -> int:
+    """Scratch bytes zeros_bwd_causal needs for these sizes."""
+    lib = load_library()
+    shp = zeros_shape(B, H, N, d, d_u, _DT[dtype], 0, 10000.0)
+    return int(lib.zeros_bwd_causal_workspace_bytes(ctypes.byref(shp)))

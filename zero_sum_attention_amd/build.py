@@ -27,6 +27,7 @@ SOURCES = [
     "encoder_valu.hip",
     "encoder_mfma.hip",
     "decode.hip",
+    "backward.hip",
 ]
 
 # Packed FP32 instructions are disabled for all device code (v_pk_* fp32 forms are avoided).

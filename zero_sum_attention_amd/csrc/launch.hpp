@@ -71,4 +71,24 @@ size_t encoder_work_bytes(const Problem &p);
 hipError_t launch_encoder_mfma(const Problem &p, float *work, hipStream_t stream);
 hipError_t launch_decode(const Problem &p, hipStream_t stream);
 
+// Backward of the causal forward (backward.hip). Gradient outputs in the storage dtype except
+// dmu [H, d_u] and dtau [H] (float32, summed over the batch).
+struct BwdGrads {
+    const void *dO;
+    void *dq, *dk, *dv, *du;
+    float *dmu, *dtau;
+    void *dg1, *dgh, *dg0;     // dg0 NULL when the zero-order gate is off
+};
+// Float32 scratch of the backward, carved from the caller's workspace.
+struct BwdWork {
+    float *s, *m, *E, *P, *al, *be, *ga, *s1, *sh, *s0, *ds;   // [B*H, N] per token
+    float4 *agg;                                               // [B*H, ceil(N/64)] (logits kernel)
+    float *qh, *kh, *vf, *dOf, *dqh, *dkh, *dvf;               // [B*H, N, d]
+    float *dotsA, *dotsB;                                      // [d/16, 3 or 2, B*H, N]
+    float *useg, *dseg, *dmu_p, *dtau_p;                       // [B*H, ceil(N/256), d_u]
+};
+size_t causal_bwd_work_bytes(int B, int H, int N, int d);
+BwdWork causal_bwd_work_carve(void *base, int B, int H, int N, int d);
+hipError_t launch_causal_bwd(const Problem &p, const BwdGrads &g, const BwdWork &w, hipStream_t stream);
+
 }  // namespace zeros

@@ -330,6 +330,55 @@ zeros_status zeros_decode_step(const zeros_shape *shape, const void *q, const vo
     return hip_result(zeros::launch_decode(p, static_cast<hipStream_t>(stream)), "zeros_decode_step");
 }
 
+zeros_status zeros_bwd_causal(const zeros_shape *shape, const void *q, const void *k, const void *v,
+                              const void *u, const float *mu, const float *tau, const void *g1,
+                              const void *gh, const void *g0, const void *dO, void *dq, void *dk, void *dv,
+                              void *du, float *dmu, float *dtau, void *dg1, void *dgh, void *dg0,
+                              void *workspace, size_t workspace_bytes, void *stream) {
+    const char *fn = "zeros_bwd_causal";
+    const std::string f(fn);
+    zeros_status st = check_common(shape, q, k, v, u, mu, tau, g1, gh, g0, dq, fn);
+    if (st != ZEROS_OK) return st;
+    const bool empty = shape->N == 0;
+    if (!dmu || !dtau) return fail(ZEROS_ERR_NULL, f + ": dmu or dtau is NULL");
+    if (!empty && (!dO || !dk || !dv || !du || !dg1 || !dgh))
+        return fail(ZEROS_ERR_NULL, f + ": a gradient pointer is NULL");
+    if (!empty && (g0 != nullptr) != (dg0 != nullptr))
+        return fail(ZEROS_ERR_NULL, f + ": dg0 must be given exactly when g0 is");
+    auto al16 = [](const void *x) { return (reinterpret_cast<uintptr_t>(x) & 15u) == 0; };
+    if (!empty && !(al16(dO) && al16(dk) && al16(dv) && al16(du)))
+        return fail(ZEROS_ERR_SHAPE, f + ": dO, dq, dk, dv and du must be 16-byte aligned");
+    auto al4 = [](const void *x) { return (reinterpret_cast<uintptr_t>(x) & 3u) == 0; };
+    if (!al4(dmu) || !al4(dtau)) return fail(ZEROS_ERR_SHAPE, f + ": dmu and dtau must be 4-byte aligned");
+    const size_t eb = elem_bytes(shape->dtype);
+    const size_t tens = static_cast<size_t>(shape->B) * shape->H * shape->N * shape->d * eb;
+    const size_t gate = static_cast<size_t>(shape->B) * shape->H * shape->N * eb;
+    const size_t mub = static_cast<size_t>(shape->H) * shape->d_u * 4, taub = static_cast<size_t>(shape->H) * 4;
+    const Range ins[] = {{q, tens}, {k, tens}, {v, tens}, {u, tens}, {g1, gate}, {gh, gate},
+                         {g0, g0 ? gate : 0}, {dO, tens}, {mu, mub}, {tau, taub}};
+    const Range outs[] = {{dq, tens}, {dk, tens}, {dv, tens}, {du, tens}, {dg1, gate}, {dgh, gate},
+                          {dg0, dg0 ? gate : 0}, {dmu, mub}, {dtau, taub}};
+    for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+        for (const Range &r : ins)
+            if (overlap(outs[i], r)) return fail(ZEROS_ERR_ALIAS, f + ": a gradient overlaps an input");
+        for (size_t j = 0; j < i; ++j)
+            if (overlap(outs[i], outs[j])) return fail(ZEROS_ERR_ALIAS, f + ": two gradients overlap");
+    }
+    const size_t need = zeros::causal_bwd_work_bytes(shape->B, shape->H, shape->N, shape->d);
+    st = check_workspace(workspace, workspace_bytes, need, fn);
+    if (st != ZEROS_OK) return st;
+    const zeros::Problem p = make_problem(shape, q, k, v, u, mu, tau, g1, gh, g0, nullptr, nullptr);
+    const zeros::BwdGrads g{dO, dq, dk, dv, du, dmu, dtau, dg1, dgh, g0 ? dg0 : nullptr};
+    const zeros::BwdWork w = zeros::causal_bwd_work_carve(workspace, shape->B, shape->H, shape->N, shape->d);
+    return hip_result(zeros::launch_causal_bwd(p, g, w, static_cast<hipStream_t>(stream)), fn);
+}
+
+size_t zeros_bwd_causal_workspace_bytes(const zeros_shape *shape) {
+    if (!shape || shape->B < 1 || shape->H < 1 || shape->N < 0) return 0;
+    if (shape->d != 16 && shape->d != 32 && shape->d != 64 && shape->d != 128) return 0;
+    return zeros::causal_bwd_work_bytes(shape->B, shape->H, shape->N, shape->d);
+}
+
 size_t zeros_state_bytes(int32_t S, int32_t H, int32_t d, int32_t d_u) {
     if (S < 1 || H < 1 || d < 1 || d_u < 1) return 0;
     const long double heads = static_cast<long double>(S) * H;

@@ -4,31 +4,32 @@
 // (zero-sum weights w_{t,i} = alpha_t e^{s_i} + beta_t s_i + gamma_t after expanding the gated
 // first-order and residual terms; angular factor q^_t . k^_i with RoPE as a relative rotation;
 // the prefix states of the linear-time scan). The optional zero-order gate of the same section
-// (a first layer may keep the uniform term) adds sigma0_t/t to gamma_t. The logits s_i and per-chunk logit aggregates come
-// from logits.hip. The sequence is cut into chunks of kC = 64 tokens.
+// (a first layer may keep the uniform term) adds sigma0_t/t to gamma_t. The logits s_i and
+// per-chunk logit aggregates come from logits.hip. The sequence is cut into chunks of kC = 64
+// tokens.
 //
-// causal_prep_kernel, one workgroup per (batch, head, chunk), all chunks in parallel: everything
-//   that depends on the tokens of a chunk but not on the value columns, done once per head:
-//   the logit carry at the chunk start (combining the aggregates of the earlier chunks), the
-//   chunk's scalar scan and coefficients, unit (RoPE-rotated) q^ and k^, A^T = K Q^T on MFMA and
-//   the intra-chunk weights W_{t,i} = A (a_t e^{s_i-m_t} + b_t s_i + g_t), i <= t. It writes them
-//   to a per-chunk record already laid out as MFMA operands (q^, k^T, W) plus the coefficients.
-// causal_seg_kernel, one workgroup of d/16 waves per (batch, head, segment of the chunks), walks
+// causal_scan_kernel, one workgroup of d/16 waves per (batch, head, segment of the chunks), walks
 //   its chunks in order; wave w owns value columns [16w, 16w+16) and all d rows of X, Y, H in
-//   float32 registers. Per chunk: o^T = S^T Q^T (carried states, S^T straight from the registers)
-//   + V^T W^T (intra-chunk), then the states advance to the chunk end with K^T V' on MFMA. The W
-//   accumulator layout of the prep kernel is the B-operand layout of V^T W^T up to a permutation
-//   of the contraction index, which V^T is read with. Segments are chained exactly by a pass over
-//   each segment from a zero state and a combine step (see the segment-parallel scan below).
+//   float32 registers. Per chunk, in LDS only:
+//   (1) every thread takes 16 features of one token row of the raw q and k (copied into LDS by
+//       direct global-to-LDS loads during the previous chunk) to unit, RoPE-rotated q^ and k^
+//       rows in bf16; wave 0 runs the chunk's scalar scan and coefficients from the logit carry;
+//   (2) the waves build k^T as MFMA A-operands and A^T = K Q^T on MFMA, turned into the
+//       intra-chunk weights W_{t,i} = A (a_t e^{s_i-m_t} + b_t s_i + g_t), i <= t, as B-operands;
+//   (3) each wave: o^T = S^T Q^T (carried states, S^T straight from the registers) + V^T W^T
+//       (intra-chunk), then the states advance to the chunk end with K^T V' on MFMA. The W
+//       accumulator layout is the B-operand layout of V^T W^T up to a permutation of the
+//       contraction index, which V^T is read with.
+//   Segments are chained exactly by a pass over each segment from a zero state (the same kernel
+//   without queries and outputs) and a combine step (see the segment-parallel scan below).
 // States are kept in a centred basis, X = F/E - H/t0 and Y = G - (P/t0) H. Both have zero-sum
 // weights, so they stay of the size of the output, and rounding them (and the update operands)
 // to bfloat16 for the MFMA is not amplified by the cancellation between alpha F, beta G and
-// gamma H. With RoPE, q^ and k^ are rotated by their absolute position (the angle of the chunk
-// start composed with the tabulated angle of the offset inside the chunk), so the carried states
-// are in the absolute frame and need no re-basing between chunks.
+// gamma H. With RoPE, q^ and k^ are rotated by their absolute position (the phase of the chunk
+// start, reduced in double precision, plus the in-chunk offset times the frequency, in
+// revolutions for the hardware sine and cosine), so the carried states are in the absolute frame
+// and need no re-basing between chunks.
 #include <hip/hip_bf16.h>
-
-#include <atomic>
 
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -40,13 +41,6 @@ namespace {
 constexpr int kC = 64;          // tokens per chunk
 constexpr int kTile = 16;       // value columns per workgroup
 constexpr int kPad = 8;         // bf16 elements of row padding in LDS
-
-// Per-chunk coefficients, produced one chunk ahead by wave 0 (double-buffered).
-struct Coef {
-    float qa[kC], qm[kC], qb[kC], qg[kC], qcx[kC], qkap[kC];   // per query t
-    float wx[kC], wy[kC], s[kC], ek[kC];                        // per key i; ek = e^{s_i - m1}
-    float chunk[8];                      // m1, E1, P1, rX, cHX, cHY, exact-exp flag
-};
 
 // Column-block swizzle of the k rows in LDS: 16-byte block b of row `key` is stored at
 // b ^ kswz(key), so the 8-key column gathers hit distinct LDS banks.
@@ -155,245 +149,69 @@ __device__ __forceinline__ void chunk_scan(Coef &cf, int lane, int t0, int nval,
 }
 
 
-// ---- per-chunk record written by the prep kernel and read by the main kernel ------------------
-// [ Q^ operands  : 4 query blocks x KS k-steps x 64 lanes x 16 B ]
-// [ K^T operands : d/16 row tiles x 2 key steps x 64 lanes x 16 B ]
-// [ W operands   : (query block tb, key-block pair pi) with 2 pi <= tb, the six that the causal mask
-//                  leaves non-zero, x 64 lanes x 16 B; piece index w_piece(tb, pi) ]
-// [ coefficients : (cX, beta, kappa, 0) per query; (w_X, w_Y) per key; rX, cHX, cHY, m1, E1, P1 ]
-template <int D> struct Rec {
-    static constexpr int KS = D / 32;
-    static constexpr size_t q_off = 0;
-    static constexpr size_t k_off = q_off + size_t(4) * KS * 1024;
-    static constexpr size_t w_off = k_off + size_t(D / 16) * 2 * 1024;
-    static constexpr size_t c_off = w_off + size_t(6) * 1024;
-    static constexpr size_t bytes = c_off + (6 * kC + 8) * 4;
-};
-enum { kCoQ = 0, kCoW = 4 * kC, kCoChunk = 6 * kC };   // float offsets in the coefficient block
-// W piece of query block tb (0..3) and key-block pair pi (keys 32 pi .. 32 pi + 31), 2 pi <= tb
+
+// ---- per-chunk coefficients ---------------------------------------------------------------
+// One wave per (batch, head, chunk), all chunks in parallel: the logit carry at the chunk start
+// (the given state's (m, E, P) merged with the aggregates of the earlier chunks) and the chunk's
+// scalar scan. The record (sizeof(Coef) bytes) is read by both scan passes.
+constexpr int kCoefWaves = 4;
+static_assert(sizeof(Coef) % 16 == 0, "coefficient records are copied in 16-byte pieces");
+// LDS bytes of a coefficient record rounded up to whole 64-piece (1 KiB) wave copies
+constexpr int kCoefLds = int((sizeof(Coef) / 16 + 63) / 64 * 64 * 16);
+
+__global__ __launch_bounds__(64 * kCoefWaves) void causal_coef_kernel(Problem p, CausalWork work) {
+    const int lane = threadIdx.x & 63;
+    const int N = p.N;
+    const int nch = (N + kC - 1) / kC;
+    const int item = blockIdx.x * kCoefWaves + (threadIdx.x >> 6);
+    if (item >= p.B * p.H * nch) return;           // (wave-uniform)
+    const int bh = item / nch, c = item % nch;
+    const int t0 = c * kC, nval = min(kC, N - t0);
+    const size_t row0 = static_cast<size_t>(bh) * N;
+    const bool cont = p.sin.F != nullptr;
+    const int tin = cont ? p.sin.t[bh] : 0;
+    const bool from_state = cont && lane == 0;
+    float m = from_state ? p.sin.m[bh] : kNegInf, e = from_state ? p.sin.E[bh] : 0.f;
+    float ps = from_state ? p.sin.P[bh] : 0.f;
+    const float4 *ag = work.agg + static_cast<size_t>(bh) * nch;
+    for (int j = lane; j < c; j += 64) {
+        const float4 a = ag[j];
+        lse_combine(m, e, a.x, a.y);
+        ps += a.z;
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float m2 = __shfl_xor(m, off, 64), e2 = __shfl_xor(e, off, 64), p2 = __shfl_xor(ps, off, 64);
+        lse_combine(m, e, m2, e2);
+        ps += p2;
+    }
+    float m0 = lane_f(m, 0), E0 = lane_f(e, 0), P0 = lane_f(ps, 0);
+    const bool vs = lane < nval;
+    const float sv = vs ? work.s[row0 + t0 + lane] : 0.f;
+    const float g1v = vs ? lo_f(static_cast<const uint16_t *>(p.g1)[row0 + t0 + lane]) : 0.f;
+    const float ghv = vs ? lo_f(static_cast<const uint16_t *>(p.gh)[row0 + t0 + lane]) : 0.f;
+    const float s0 = (vs && p.g0 != nullptr)
+                         ? __fdividef(1.f, 1.f + __expf(-lo_f(static_cast<const uint16_t *>(p.g0)[row0 + t0 + lane])))
+                         : 0.f;
+    chunk_scan(work.coef[item], lane, tin + t0, nval, sv, g1v, ghv, s0, m0, E0, P0);
+}
+
+// W piece of query block tb (0..3) and key-block pair pi (keys 32 pi .. 32 pi + 31), 2 pi <= tb:
+// the six pieces the causal mask leaves non-zero.
 __device__ __forceinline__ int w_piece(int tb, int pi) { return tb < 2 ? tb : 2 * tb - 2 + pi; }
+__device__ __forceinline__ void piece_tb_pi(int piece, int &tb, int &pi) {
+    tb = piece < 2 ? piece : (piece + 2) / 2;
+    pi = piece < 2 ? 0 : piece & 1;
+}
 
 __device__ __forceinline__ void st16(unsigned char *p, const bf16x8 &v) { *reinterpret_cast<bf16x8 *>(p) = v; }
 __device__ __forceinline__ bf16x8 ld16(const unsigned char *p) { return *reinterpret_cast<const bf16x8 *>(p); }
-
-constexpr int kPrepThreads = 256;
-
-template <int D>
-struct alignas(16) PSmem {
-    alignas(16) uint16_t qh[kC][D + kPad];     // unit (rotated) q rows, bf16
-    alignas(16) uint16_t kh[kC][D + kPad];     // unit (rotated) k rows, 16-byte blocks swizzled
-    Coef cf;
-    float2 rot0[D / 2];                        // cos, sin of t0 * theta_j (chunk start)
-};
-
-template <int D, bool ROPE>
-__global__ __launch_bounds__(kPrepThreads) void causal_prep_kernel(Problem p, CausalWork work) {
-    extern __shared__ __align__(16) unsigned char smem_raw[];
-    PSmem<D> &sm = *reinterpret_cast<PSmem<D> *>(smem_raw);
-    using R = Rec<D>;
-    constexpr int KS = D / 32;
-    constexpr int RT = D / 64;
-    constexpr int QW = D / 4;           // features per thread in the load phase
-    constexpr int NV = QW / 8;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int l16 = lane & 15, g4 = lane >> 4;
-    const int N = p.N;
-    const int nch = (N + kC - 1) / kC;
-    const int c = blockIdx.x % nch;
-    const int bh = blockIdx.x / nch;
-    const int t0 = c * kC, nval = min(kC, N - t0);
-    const size_t row0 = static_cast<size_t>(bh) * N;
-    unsigned char *rec = work.rec + (static_cast<size_t>(bh) * nch + c) * R::bytes;
-    // a sequence continued from a state: its tokens are positions tin + 1 ...
-    const bool cont = p.sin.F != nullptr;
-    const int tin = cont ? p.sin.t[bh] : 0;
-
-    if (ROPE) {
-        if (tid < D / 2) {
-            float c0, s0;
-            rope_cos_sin(rope_rev_per_pos(tid, D, p.rope_base), tin + t0, c0, s0);
-            sm.rot0[tid] = make_float2(c0, s0);
-        }
-        __syncthreads();
-    }
-
-    // ---- wave 0: logit carry at t0 from the state (if any) and the earlier chunks, then this
-    // chunk's scan
-    if (wave == 0) {
-        const bool from_state = cont && lane == 0;
-        float m = from_state ? p.sin.m[bh] : kNegInf, e = from_state ? p.sin.E[bh] : 0.f;
-        float ps = from_state ? p.sin.P[bh] : 0.f;
-        const float4 *ag = work.agg + static_cast<size_t>(bh) * nch;
-        for (int j = lane; j < c; j += 64) {
-            const float4 a = ag[j];
-            lse_combine(m, e, a.x, a.y);
-            ps += a.z;
-        }
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float m2 = __shfl_xor(m, off, 64), e2 = __shfl_xor(e, off, 64), p2 = __shfl_xor(ps, off, 64);
-            lse_combine(m, e, m2, e2);
-            ps += p2;
-        }
-        float m0 = lane_f(m, 0), E0 = lane_f(e, 0), P0 = lane_f(ps, 0);
-        const bool vs = lane < nval;
-        const float sv = vs ? work.s[row0 + t0 + lane] : 0.f;
-        const float g1v = vs ? lo_f(static_cast<const uint16_t *>(p.g1)[row0 + t0 + lane]) : 0.f;
-        const float ghv = vs ? lo_f(static_cast<const uint16_t *>(p.gh)[row0 + t0 + lane]) : 0.f;
-        const float s0 = (vs && p.g0 != nullptr)
-                             ? __fdividef(1.f, 1.f + __expf(-lo_f(static_cast<const uint16_t *>(p.g0)[row0 + t0 + lane])))
-                             : 0.f;
-        chunk_scan(sm.cf, lane, tin + t0, nval, sv, g1v, ghv, s0, m0, E0, P0);
-    }
-
-    // ---- unit q^, k^ rows, rotated by their offset inside the chunk
-    {
-        const int lr = tid >> 2, f0 = (tid & 3) * QW;
-        const bool valid = lr < nval;
-        const size_t base = (row0 + t0 + lr) * D + f0;
-        const uint16_t *qg = static_cast<const uint16_t *>(p.q), *kg = static_cast<const uint16_t *>(p.k);
-        uint4 pq[NV], pk[NV];
-#pragma unroll
-        for (int a = 0; a < NV; ++a) {
-            pq[a] = valid ? *reinterpret_cast<const uint4 *>(qg + base + 8 * a) : make_uint4(0, 0, 0, 0);
-            pk[a] = valid ? *reinterpret_cast<const uint4 *>(kg + base + 8 * a) : make_uint4(0, 0, 0, 0);
-        }
-        float ssq = 0.f, ssk = 0.f;
-#pragma unroll
-        for (int a = 0; a < NV; ++a) {
-            ssq = dot2_bf16(pq[a].x, ssq); ssq = dot2_bf16(pq[a].y, ssq);
-            ssq = dot2_bf16(pq[a].z, ssq); ssq = dot2_bf16(pq[a].w, ssq);
-            ssk = dot2_bf16(pk[a].x, ssk); ssk = dot2_bf16(pk[a].y, ssk);
-            ssk = dot2_bf16(pk[a].z, ssk); ssk = dot2_bf16(pk[a].w, ssk);
-        }
-        ssq = group_sum<4>(ssq);
-        ssk = group_sum<4>(ssk);
-        const float iq = valid ? __frsqrt_rn(fmaxf(ssq, 1e-24f)) : 0.f;
-        const float ik = valid ? __frsqrt_rn(fmaxf(ssk, 1e-24f)) : 0.f;
-#pragma unroll
-        for (int a = 0; a < NV; ++a) {
-            uint32_t wq[4] = {pq[a].x, pq[a].y, pq[a].z, pq[a].w};
-            uint32_t wk[4] = {pk[a].x, pk[a].y, pk[a].z, pk[a].w};
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const float q0 = lo_f(wq[b]), q1 = hi_f(wq[b]);
-                const float k0 = lo_f(wk[b]), k1 = hi_f(wk[b]);
-                if (ROPE) {
-                    // angle of position t0 + lr = angle of t0 + angle of lr
-                    const int jp = f0 / 2 + 4 * a + b;
-                    const float2 tr = work.rope[lr * (D / 2) + jp], t0r = sm.rot0[jp];
-                    const float cs = t0r.x * tr.x - t0r.y * tr.y, sn = t0r.y * tr.x + t0r.x * tr.y;
-                    const float cq = cs * iq, sq = sn * iq, ck = cs * ik, sk = sn * ik;
-                    wq[b] = pack2(q0 * cq - q1 * sq, q0 * sq + q1 * cq);
-                    wk[b] = pack2(k0 * ck - k1 * sk, k0 * sk + k1 * ck);
-                } else {
-                    wq[b] = pack2(q0 * iq, q1 * iq);
-                    wk[b] = pack2(k0 * ik, k1 * ik);
-                }
-            }
-            const int blk = f0 / 8 + a;
-            *reinterpret_cast<uint4 *>(&sm.qh[lr][8 * blk]) = make_uint4(wq[0], wq[1], wq[2], wq[3]);
-            *reinterpret_cast<uint4 *>(&sm.kh[lr][8 * (blk ^ kswz(lr))]) = make_uint4(wk[0], wk[1], wk[2], wk[3]);
-        }
-    }
-    __syncthreads();
-
-    // ---- query block tb = wave: q^ operands, A^T tiles, intra-chunk weights
-    {
-        const int tb = wave;
-        const Coef &cf = sm.cf;
-        bf16x8 qop[KS];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            qop[ks] = *reinterpret_cast<const bf16x8 *>(&sm.qh[16 * tb + l16][32 * ks + 8 * g4]);
-            // the record holds features {32ks + 4g4 + i, 32ks + 16 + 4g4 + i}, i < 4: the order in
-            // which a lane of the scan kernel holds the rows of two 16-row state accumulator tiles
-            const uint2 qa = *reinterpret_cast<const uint2 *>(&sm.qh[16 * tb + l16][32 * ks + 4 * g4]);
-            const uint2 qc = *reinterpret_cast<const uint2 *>(&sm.qh[16 * tb + l16][32 * ks + 16 + 4 * g4]);
-            st16(rec + R::q_off + (size_t(tb * KS + ks) * 64 + lane) * 16, as_bf16x8(qa.x, qa.y, qc.x, qc.y));
-        }
-        f32x4 at[4];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) at[kb][i] = 0.f;
-            if (kb <= tb) {
-                const int key = 16 * kb + l16;
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&sm.kh[key][8 * ((4 * ks + g4) ^ kswz(key))]);
-                    at[kb] = mfma(a, qop[ks], at[kb]);
-                }
-            }
-        }
-        const int tq = 16 * tb + l16;
-        const float qa = cf.qa[tq], qm = cf.qm[tq], qb = cf.qb[tq], qgm = cf.qg[tq];
-        const bool exact_exp = cf.chunk[6] != 0.f;
-#pragma unroll
-        for (int pi = 0; pi < 2; ++pi) {
-            uint32_t wv[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-                const int kb = 2 * pi + h2;
-                if (kb > tb) continue;
-                const float4 s4 = *reinterpret_cast<const float4 *>(&cf.s[16 * kb + 4 * g4]);
-                const float ks_[4] = {s4.x, s4.y, s4.z, s4.w};
-                float ke_[4];
-                if (exact_exp) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) ke_[i] = __expf(ks_[i] - qm);
-                } else {
-                    const float4 e4 = *reinterpret_cast<const float4 *>(&cf.ek[16 * kb + 4 * g4]);
-                    ke_[0] = e4.x; ke_[1] = e4.y; ke_[2] = e4.z; ke_[3] = e4.w;
-                }
-                float w[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int key = 16 * kb + 4 * g4 + i;
-                    const float x = at[kb][i] * (qa * ke_[i] + qb * ks_[i] + qgm);
-                    w[i] = (key <= tq && tq < nval) ? x : 0.f;
-                }
-                wv[2 * h2] = pack2(w[0], w[1]);
-                wv[2 * h2 + 1] = pack2(w[2], w[3]);
-            }
-            if (2 * pi <= tb)
-                st16(rec + R::w_off + (size_t(w_piece(tb, pi)) * 64 + lane) * 16, as_bf16x8(wv[0], wv[1], wv[2], wv[3]));
-        }
-    }
-
-    // ---- k^T operands of the state update: row tiles [RT*wave, RT*wave+RT), 2 key steps
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        const int jb = RT * wave + rt;
-        const int j = 16 * jb + l16;
-#pragma unroll
-        for (int ks2 = 0; ks2 < kC / 32; ++ks2) {
-            const int kk0 = 32 * ks2 + 8 * g4;
-            const int jc = (((j >> 3) ^ (2 * g4)) << 3) | (j & 7);   // kswz(kk0 + c) == 2 * g4
-            bf16x8 a;
-#pragma unroll
-            for (int cc = 0; cc < 8; ++cc) a[cc] = static_cast<short>(sm.kh[kk0 + cc][jc]);
-            st16(rec + R::k_off + (size_t(jb * 2 + ks2) * 64 + lane) * 16, a);
-        }
-    }
-
-    // ---- coefficients used by the main kernel
-    if (tid < kC) {
-        float *co = reinterpret_cast<float *>(rec + R::c_off);
-        *reinterpret_cast<float4 *>(co + kCoQ + 4 * tid) = make_float4(sm.cf.qcx[tid], sm.cf.qb[tid], sm.cf.qkap[tid], 0.f);
-        *reinterpret_cast<float2 *>(co + kCoW + 2 * tid) = make_float2(sm.cf.wx[tid], sm.cf.wy[tid]);
-        if (tid < 8) {
-            const int src[8] = {3, 4, 5, 0, 1, 2, 7, 7};   // rX, cHX, cHY, m1, E1, P1, 0, 0
-            co[kCoChunk + tid] = tid < 6 ? sm.cf.chunk[src[tid]] : 0.f;
-        }
-    }
-}
 
 // ---- segment-parallel scan ----------------------------------------------------------------
 //
 // The chunks of a head are cut into nseg segments of seg_chunks chunks. One workgroup of D/16 waves
 // owns a whole head (wave w: value columns [16w, 16w+16), all D state rows of X, Y, H in float32
-// registers) for one segment, so every record chunk is read once per head.
+// registers) for one segment, so every chunk's q^, k^ and weights are formed once per head.
 //
 // Within a segment the per-chunk recurrence of the centred states is affine:
 //   X <- rX X + cHX H + dX,   Y <- Y + cHY H + dY,   H <- H + dH        (d: the chunk's K^T V')
@@ -409,27 +227,51 @@ __global__ __launch_bounds__(kPrepThreads) void causal_prep_kernel(Problem p, Ca
 // lane holds rows 16 jb + 4 (lane >> 4) + i, i < 4, column 16 w + (lane & 15) of state s (X, Y, H).
 template <int D> constexpr size_t kSegFloats = size_t(3) * D * D;
 
-// LDS bytes of one staged record: whole 64-piece (1 KiB) wave copies
-template <int D> constexpr int kRecLds = int((Rec<D>::bytes / 16 + 63) / 64 * 64 * 16);
+// one wave per 16 value columns: 8 waves (two per SIMD) at d = 128, 4 at d = 64
+template <int D> constexpr int kScanThreads = 4 * D;
 
 template <int D, bool ROPE, bool PASS1>
-__global__ __launch_bounds__(D * 4) void causal_seg_kernel(Problem p, CausalWork work) {
-    // Two record buffers as separate objects: the next chunk is copied into one by direct
-    // global-to-LDS loads while the other is read, and the compiler can tell the two apart (so
-    // it does not wait for the copy before reading the current one).
-    __shared__ __align__(16) unsigned char recA[kRecLds<D>];
-    __shared__ __align__(16) unsigned char recB[kRecLds<D>];
-    // per wave: its v tile transposed, vt[m][token] (also the H update operand), and the update
-    // operands v * w_X, v * w_Y, transposed
-    __shared__ __align__(16) uint16_t svt[D / 16][kTile][kC + kPad];
-    __shared__ __align__(16) uint16_t svx[D / 16][kTile][kC + kPad];
-    __shared__ __align__(16) uint16_t svy[D / 16][kTile][kC + kPad];
-    using R = Rec<D>;
+__global__ __launch_bounds__(kScanThreads<D>) void causal_scan_kernel(Problem p, CausalWork work) {
     constexpr int NW = D / 16;          // waves
-    constexpr int NT = NW * 64;
+    constexpr int NT = kScanThreads<D>;
+    constexpr int CT = D / (16 * NW);   // 16-column tiles of the value dimension per wave
+    constexpr int NGT = D / 16;         // 16-column tiles of a head (= 16-row state tiles)
     constexpr int KS = D / 32;          // 32-feature steps of the carried-state products
     constexpr int JB = D / 16;          // 16-row state tiles
-    constexpr int kPieces = int(R::bytes / 16);                 // 16-byte pieces of a record
+    constexpr int TPR = NT / kC;        // prep threads per token row
+    constexpr int FB = D / (16 * TPR);  // 16-feature blocks per prep thread
+    constexpr int RP = kC * D / 8;      // 16-byte pieces of one chunk's rows of q (or k)
+    static_assert(CT == 1 && FB >= 1, "d must be 64 or 128");
+
+    // Separate LDS objects, so that the compiler can tell the target of the direct global-to-LDS
+    // copies (raw rows of the next chunk) from the buffers read meanwhile, and does not wait for
+    // the copies before reading them.
+    // raw bf16 rows of the next chunk, copied by direct global-to-LDS loads (16-byte pieces)
+    __shared__ __align__(16) uint16_t s_rawk[kC * D];
+    __shared__ __align__(16) uint16_t s_rawq[PASS1 ? 8 : kC * D];
+    // unit, rotated rows of this chunk; the k rows with their 16-byte blocks swizzled
+    __shared__ __align__(16) uint16_t s_kh[kC][D + kPad];
+    __shared__ __align__(16) uint16_t s_qh[PASS1 ? 1 : kC][D + kPad];
+    // k^T as A operands of the update: (row tile jb, key step ks2) x 64 lanes x 16 bytes
+    __shared__ __align__(16) unsigned char s_kt[JB * 2 * 1024];
+    // intra-chunk weights as B operands of V^T W^T, piece w_piece(tb, pi) x 64 lanes x 16 bytes
+    __shared__ __align__(16) unsigned char s_wop[PASS1 ? 16 : 6 * 1024];
+    // per column tile: its v tile transposed, vt[m][token] (also the H update operand), and the
+    // update operands v * w_X, v * w_Y, transposed
+    __shared__ __align__(16) uint16_t s_svt[NGT][kTile][kC + kPad];
+    __shared__ __align__(16) uint16_t s_svx[NGT][kTile][kC + kPad];
+    __shared__ __align__(16) uint16_t s_svy[NGT][kTile][kC + kPad];
+    // the chunk's coefficient record and RoPE phase of the chunk start (revolutions, in
+    // [-1/2, 1/2]), double-buffered as separate objects: the next chunk's are written meanwhile.
+    // A wave's direct copy writes 64 pieces of 16 bytes: the record buffers are padded to whole
+    // copies, so the lanes past the record's end write into the padding.
+    __shared__ __align__(16) unsigned char s_cfA_raw[kCoefLds];
+    __shared__ __align__(16) unsigned char s_cfB_raw[kCoefLds];
+    Coef &s_cfA = *reinterpret_cast<Coef *>(s_cfA_raw);
+    Coef &s_cfB = *reinterpret_cast<Coef *>(s_cfB_raw);
+    __shared__ float s_revA[D / 2];
+    __shared__ float s_revB[D / 2];
+    __shared__ float s_rpp[D / 2];       // RoPE revolutions per position of pair j
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -442,48 +284,54 @@ __global__ __launch_bounds__(D * 4) void causal_seg_kernel(Problem p, CausalWork
     const int c_begin = seg * work.seg_chunks;
     const int c_end = min(nch, c_begin + work.seg_chunks);
     const size_t row0 = static_cast<size_t>(bh) * N;
+    const uint16_t *qg = static_cast<const uint16_t *>(p.q) + row0 * D;
+    const uint16_t *kg = static_cast<const uint16_t *>(p.k) + row0 * D;
     const uint16_t *vg = static_cast<const uint16_t *>(p.v) + row0 * D;
     uint16_t *og = static_cast<uint16_t *>(p.o) + row0 * D;
-    const unsigned char *rec0 = work.rec + static_cast<size_t>(bh) * nch * R::bytes;
     // a sequence continued from a state: tokens are positions tin + 1 ..., and the first segment
     // of the main pass starts from that state
     const bool cont = p.sin.F != nullptr;
     const int tin = cont ? p.sin.t[bh] : 0;
 
-    // state of this wave's columns: X, Y, H rows 16 jb + 4 g4 + i, column 16 w + l16
-    f32x4 X[JB], Y[JB], Hm[JB];
-    const size_t sidx = static_cast<size_t>(w) * 64 + lane;       // float4 index inside a (s, jb) block
-    if (!PASS1 && seg == 0 && tin > 0) {
-        // the given state in the centred basis: X = F/E - H/t, Y = G - (P/t) H
-        const size_t mat0 = static_cast<size_t>(bh) * D * D;
-        const float iE = 1.f / p.sin.E[bh], it = 1.f / static_cast<float>(tin);
-        const float pt = p.sin.P[bh] * it;
+    // state of this wave's column tiles gt = CT w + ct: X, Y, H rows 16 jb + 4 g4 + i, column
+    // 16 gt + l16
+    f32x4 X[CT][JB], Y[CT][JB], Hm[CT][JB];
 #pragma unroll
-        for (int jb = 0; jb < JB; ++jb)
+    for (int ct = 0; ct < CT; ++ct) {
+        const int gt = CT * w + ct;
+        const size_t sidx = static_cast<size_t>(gt) * 64 + lane;     // float4 index inside a (s, jb) block
+        if (!PASS1 && seg == 0 && tin > 0) {
+            // the given state in the centred basis: X = F/E - H/t, Y = G - (P/t) H
+            const size_t mat0 = static_cast<size_t>(bh) * D * D;
+            const float iE = 1.f / p.sin.E[bh], it = 1.f / static_cast<float>(tin);
+            const float pt = p.sin.P[bh] * it;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const size_t idx = mat0 + static_cast<size_t>(16 * jb + 4 * g4 + i) * D + w * kTile + l16;
-                const float hh = p.sin.Hs[idx];
-                X[jb][i] = p.sin.F[idx] * iE - hh * it;
-                Y[jb][i] = p.sin.G[idx] - pt * hh;
-                Hm[jb][i] = hh;
+            for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const size_t idx = mat0 + static_cast<size_t>(16 * jb + 4 * g4 + i) * D + gt * kTile + l16;
+                    const float hh = p.sin.Hs[idx];
+                    X[ct][jb][i] = p.sin.F[idx] * iE - hh * it;
+                    Y[ct][jb][i] = p.sin.G[idx] - pt * hh;
+                    Hm[ct][jb][i] = hh;
+                }
+        } else if (!PASS1 && seg > 0) {
+            const float4 *st0 = reinterpret_cast<const float4 *>(work.segst + (static_cast<size_t>(bh) * (nseg - 1) + seg - 1) * kSegFloats<D>);
+#pragma unroll
+            for (int jb = 0; jb < JB; ++jb) {
+                const float4 a = st0[(size_t(0 * JB + jb) * NGT) * 64 + sidx];
+                const float4 b = st0[(size_t(1 * JB + jb) * NGT) * 64 + sidx];
+                const float4 c = st0[(size_t(2 * JB + jb) * NGT) * 64 + sidx];
+                X[ct][jb] = f32x4{a.x, a.y, a.z, a.w};
+                Y[ct][jb] = f32x4{b.x, b.y, b.z, b.w};
+                Hm[ct][jb] = f32x4{c.x, c.y, c.z, c.w};
             }
-    } else if (!PASS1 && seg > 0) {
-        const float4 *st0 = reinterpret_cast<const float4 *>(work.segst + (static_cast<size_t>(bh) * (nseg - 1) + seg - 1) * kSegFloats<D>);
+        } else {
 #pragma unroll
-        for (int jb = 0; jb < JB; ++jb) {
-            const float4 a = st0[(size_t(0 * JB + jb) * NW) * 64 + sidx];
-            const float4 b = st0[(size_t(1 * JB + jb) * NW) * 64 + sidx];
-            const float4 c = st0[(size_t(2 * JB + jb) * NW) * 64 + sidx];
-            X[jb] = f32x4{a.x, a.y, a.z, a.w};
-            Y[jb] = f32x4{b.x, b.y, b.z, b.w};
-            Hm[jb] = f32x4{c.x, c.y, c.z, c.w};
+            for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) X[ct][jb][i] = Y[ct][jb][i] = Hm[ct][jb][i] = 0.f;
         }
-    } else {
-#pragma unroll
-        for (int jb = 0; jb < JB; ++jb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) X[jb][i] = Y[jb][i] = Hm[jb][i] = 0.f;
     }
     // composed scalar map of the segment (pass 1): X <- Rs X + alp H + ..., Y <- Y + bet H + ...,
     // with Rs the exact product of the chunk factors rX
@@ -498,51 +346,208 @@ __global__ __launch_bounds__(D * 4) void causal_seg_kernel(Problem p, CausalWork
     // 2^80. alp and bet are the composed H coefficients of X and Y (pass 1's segment map).
     float rho = 1.f, alp = 0.f, bet = 0.f;
 
-    // v of this wave's columns: lane holds tokens 2 (lane & 31), +1 and columns 8 (lane >> 5) + [0, 8)
-    const int vtok = 2 * (lane & 31), vh = lane >> 5;
-    const size_t vcol = static_cast<size_t>(w) * kTile + 8 * vh;
-    uint4 va, vb;
-    // record pieces [p0, p1) of chunk c into LDS buffer dst at their record offsets (direct copies:
-    // wave w moves pieces p0 + 64 w + NT i + lane; lanes past p1 repeat the last piece into the
-    // padding of the buffer, which ends on a whole 64-piece copy)
-    auto copy_range = [&](const uint4 *src, unsigned char *dst, const int p0, const int p1) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < (p1 - p0 + NT - 1) / NT; ++i) {
-            const int base = p0 + w * 64 + i * NT;               // wave-uniform
-            if (base < p1)
-                __builtin_amdgcn_global_load_lds(src + min(base + lane, p1 - 1), dst + base * 16, 16, 0, 0);
-        }
-    };
-    // v rows of chunk c into registers, and the record parts this pass reads into LDS buffer dst:
-    // the whole record for the main pass, the k^T operands and the coefficients for pass 1
-    auto fetch = [&](const int c, unsigned char *dst) __attribute__((always_inline)) {
-        const int t_ = c * kC + vtok;      // rows past N read row N-1 (in bounds)
-        va = *reinterpret_cast<const uint4 *>(vg + static_cast<size_t>(min(t_, N - 1)) * D + vcol);
-        vb = *reinterpret_cast<const uint4 *>(vg + static_cast<size_t>(min(t_ + 1, N - 1)) * D + vcol);
-        const uint4 *src = reinterpret_cast<const uint4 *>(rec0 + static_cast<size_t>(c) * R::bytes);
-        if (PASS1) {
-            copy_range(src, dst, int(R::k_off / 16), int(R::w_off / 16));
-            copy_range(src, dst, int(R::c_off / 16), kPieces);
-        } else {
-            copy_range(src, dst, 0, kPieces);
-        }
-    };
+    if (ROPE && tid < D / 2) {
+        const double rev = rope_rev_per_pos(tid, D, p.rope_base);
+        s_rpp[tid] = static_cast<float>(rev);
+        double r = static_cast<double>(tin + c_begin * kC) * rev;
+        s_revA[tid] = static_cast<float>(r - rint(r));
+    }
 
-    if (c_begin < c_end) fetch(c_begin, recA);
+    // v of this wave's column tiles: lane holds tokens 2 (lane & 31), +1 and columns 8 (lane >> 5) + [0, 8)
+    const int vtok = 2 * (lane & 31), vh = lane >> 5;
+    uint4 va[CT], vb[CT];
+    auto fetch_v = [&](const int c) __attribute__((always_inline)) {
+        const int t_ = c * kC + vtok;      // rows past N read row N-1 (in bounds)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            const size_t vcol = static_cast<size_t>(CT * w + ct) * kTile + 8 * vh;
+            va[ct] = *reinterpret_cast<const uint4 *>(vg + static_cast<size_t>(min(t_, N - 1)) * D + vcol);
+            vb[ct] = *reinterpret_cast<const uint4 *>(vg + static_cast<size_t>(min(t_ + 1, N - 1)) * D + vcol);
+        }
+    };
+    // the coefficient record and the raw q and k rows of chunk c into LDS: the chunk's rows are
+    // contiguous in memory, so piece i (16 bytes) is element 8 i of the block; pieces past the
+    // last token repeat the last valid piece (the rows they fill are zeroed when read)
+    auto fetch_raw = [&](const int c, Coef &cdst) __attribute__((always_inline)) {
+        {
+            constexpr int CP = int(sizeof(Coef) / 16);
+            const uint4 *srcc = reinterpret_cast<const uint4 *>(work.coef + static_cast<size_t>(bh) * nch + c);
+#pragma unroll
+            for (int i = 0; i < (CP + NT - 1) / NT; ++i) {
+                const int base = w * 64 + i * NT;                // wave-uniform
+                if (base < CP)
+                    __builtin_amdgcn_global_load_lds(srcc + min(base + lane, CP - 1),
+                                                     reinterpret_cast<unsigned char *>(&cdst) + base * 16, 16, 0, 0);
+            }
+        }
+        const int nv = min(kC, N - c * kC) * (D / 8);
+        const uint4 *srck = reinterpret_cast<const uint4 *>(kg + static_cast<size_t>(c) * kC * D);
+        const uint4 *srcq = reinterpret_cast<const uint4 *>(qg + static_cast<size_t>(c) * kC * D);
+#pragma unroll
+        for (int i = 0; i < RP / NT; ++i) {
+            const int base = w * 64 + i * NT;                    // wave-uniform
+            __builtin_amdgcn_global_load_lds(srck + min(base + lane, nv - 1),
+                                             reinterpret_cast<unsigned char *>(s_rawk) + base * 16, 16, 0, 0);
+            if (!PASS1)
+                __builtin_amdgcn_global_load_lds(srcq + min(base + lane, nv - 1),
+                                                 reinterpret_cast<unsigned char *>(s_rawq) + base * 16, 16, 0, 0);
+        }
+    };
+    if (c_begin < c_end) {
+        fetch_raw(c_begin, s_cfA);
+        fetch_v(c_begin);
+    }
     // unconditional: the start-state loads and the first copies are complete on every path into
-    // the loop, so no wait inside it has to cover them
+    // the loop
     __syncthreads();
-    auto chunk = [&](const int c, const unsigned char *rb, unsigned char *rn) __attribute__((always_inline)) {
+
+    // one chunk: its coefficient record and start phase in (cfc, revc); the next chunk's are
+    // written into (cfn, revn)
+    auto chunk = [&](const int c, const Coef &cfc, Coef &cfn, const float *revc, float *revn) __attribute__((always_inline)) {
         const int t0 = c * kC;
         const int nval = min(kC, N - t0);
         const bool has_prev = tin + t0 > 0;      // tokens before this chunk (a carried state)
-        const float *co = reinterpret_cast<const float *>(rb + R::c_off);
-        const float4 ch = *reinterpret_cast<const float4 *>(co + kCoChunk);   // rX, cHX, cHY, m1
+
+        // ---- (1) unit, rotated q^ and k^ rows: thread = (row r, FB blocks of 16 features)
+        {
+            const int r = tid / TPR;
+            const bool valid = r < nval;
+            uint4 k4[FB][2], q4[FB][2];
+#pragma unroll
+            for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int f0 = 16 * ((tid % TPR) * FB + fb) + 8 * h;
+                    k4[fb][h] = valid ? *reinterpret_cast<const uint4 *>(&s_rawk[r * D + f0]) : make_uint4(0, 0, 0, 0);
+                    if (!PASS1)
+                        q4[fb][h] = valid ? *reinterpret_cast<const uint4 *>(&s_rawq[r * D + f0]) : make_uint4(0, 0, 0, 0);
+                }
+            float ssk = 0.f, ssq = 0.f;
+#pragma unroll
+            for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    ssk = dot2_bf16(k4[fb][h].x, ssk); ssk = dot2_bf16(k4[fb][h].y, ssk);
+                    ssk = dot2_bf16(k4[fb][h].z, ssk); ssk = dot2_bf16(k4[fb][h].w, ssk);
+                    if (!PASS1) {
+                        ssq = dot2_bf16(q4[fb][h].x, ssq); ssq = dot2_bf16(q4[fb][h].y, ssq);
+                        ssq = dot2_bf16(q4[fb][h].z, ssq); ssq = dot2_bf16(q4[fb][h].w, ssq);
+                    }
+                }
+            ssk = group_sum<TPR>(ssk);
+            const float ik = valid ? __frsqrt_rn(fmaxf(ssk, 1e-24f)) : 0.f;
+            float iq = 0.f;
+            if (!PASS1) {
+                ssq = group_sum<TPR>(ssq);
+                iq = valid ? __frsqrt_rn(fmaxf(ssq, 1e-24f)) : 0.f;
+            }
+#pragma unroll
+            for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int blk = 2 * ((tid % TPR) * FB + fb) + h;     // 8-feature block
+                    uint32_t wk[4] = {k4[fb][h].x, k4[fb][h].y, k4[fb][h].z, k4[fb][h].w};
+                    uint32_t wq[4] = {q4[fb][h].x, q4[fb][h].y, q4[fb][h].z, q4[fb][h].w};
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        float cs = 1.f, sn = 0.f;
+                        if (ROPE) {
+                            // phase of position tin + t0 + r for pair j, in revolutions
+                            const int j = 4 * blk + b;
+                            float rev = fmaf(static_cast<float>(r), s_rpp[j], revc[j]);
+                            rev -= rintf(rev);
+                            cs = __builtin_amdgcn_cosf(rev);
+                            sn = __builtin_amdgcn_sinf(rev);
+                        }
+                        const float k0 = lo_f(wk[b]), k1 = hi_f(wk[b]);
+                        const float ck = cs * ik, sk = sn * ik;
+                        wk[b] = pack2(k0 * ck - k1 * sk, k0 * sk + k1 * ck);
+                        if (!PASS1) {
+                            const float q0 = lo_f(wq[b]), q1 = hi_f(wq[b]);
+                            const float cq = cs * iq, sq = sn * iq;
+                            wq[b] = pack2(q0 * cq - q1 * sq, q0 * sq + q1 * cq);
+                        }
+                    }
+                    *reinterpret_cast<uint4 *>(&s_kh[r][8 * (blk ^ kswz(r))]) = make_uint4(wk[0], wk[1], wk[2], wk[3]);
+                    if (!PASS1) *reinterpret_cast<uint4 *>(&s_qh[r][8 * blk]) = make_uint4(wq[0], wq[1], wq[2], wq[3]);
+                }
+            if (ROPE && tid < D / 2 && c + 1 < c_end) {
+                const double r2 = static_cast<double>(tin + t0 + kC) * rope_rev_per_pos(tid, D, p.rope_base);
+                revn[tid] = static_cast<float>(r2 - rint(r2));
+            }
+        }
+        lds_barrier();
+
+        // ---- (2) next chunk's record and raw rows in flight; k^T operands; A^T and W
+        if (c + 1 < c_end) fetch_raw(c + 1, cfn);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            // k^T operands of row tile jb: 8 keys per lane gathered from the swizzled rows
+            const int jb = CT * w + ct;
+            const int j = 16 * jb + l16;
+#pragma unroll
+            for (int ks2 = 0; ks2 < kC / 32; ++ks2) {
+                const int kk0 = 32 * ks2 + 8 * g4;
+                const int jc = (((j >> 3) ^ (2 * g4)) << 3) | (j & 7);   // kswz(kk0 + cc) == 2 * g4
+                bf16x8 a;
+#pragma unroll
+                for (int cc = 0; cc < 8; ++cc) a[cc] = static_cast<short>(s_kh[kk0 + cc][jc]);
+                st16(s_kt + (size_t(jb * 2 + ks2) * 64 + lane) * 16, a);
+            }
+        }
+        if (!PASS1) {
+            // the ten (query block tb, key block kb <= tb) tiles of A^T, spread over the waves; each
+            // fills its half (8 bytes per lane) of the W piece of key pair kb / 2, and the tiles
+            // (0, 0) and (2, 2) also the zero half whose keys all follow the queries
+            const Coef &cf = cfc;
+            const bool exact_exp = cf.chunk[6] != 0.f;
+            for (int blk = w; blk < 10; blk += NW) {
+                const int tb = blk < 1 ? 0 : blk < 3 ? 1 : blk < 6 ? 2 : 3;
+                const int kb = blk - tb * (tb + 1) / 2;
+                const int tq = 16 * tb + l16;
+                const int key = 16 * kb + l16;
+                f32x4 at = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const bf16x8 qop = *reinterpret_cast<const bf16x8 *>(&s_qh[tq][32 * ks + 8 * g4]);
+                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&s_kh[key][8 * ((4 * ks + g4) ^ kswz(key))]);
+                    at = mfma(a, qop, at);
+                }
+                const float qa = cf.qa[tq], qm = cf.qm[tq], qb = cf.qb[tq], qgm = cf.qg[tq];
+                const float4 s4 = *reinterpret_cast<const float4 *>(&cf.s[16 * kb + 4 * g4]);
+                const float ks_[4] = {s4.x, s4.y, s4.z, s4.w};
+                float ke_[4];
+                if (exact_exp) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) ke_[i] = __expf(ks_[i] - qm);
+                } else {
+                    const float4 e4 = *reinterpret_cast<const float4 *>(&cf.ek[16 * kb + 4 * g4]);
+                    ke_[0] = e4.x; ke_[1] = e4.y; ke_[2] = e4.z; ke_[3] = e4.w;
+                }
+                float wt[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int kk = 16 * kb + 4 * g4 + i;
+                    const float x = at[i] * (qa * ke_[i] + qb * ks_[i] + qgm);
+                    wt[i] = (kk <= tq && tq < nval) ? x : 0.f;
+                }
+                unsigned char *dst = s_wop + (size_t(w_piece(tb, kb >> 1)) * 64 + lane) * 16;
+                *reinterpret_cast<uint2 *>(dst + (kb & 1) * 8) = make_uint2(pack2(wt[0], wt[1]), pack2(wt[2], wt[3]));
+                if ((kb & 1) == 0 && kb + 1 > tb) *reinterpret_cast<uint2 *>(dst + 8) = make_uint2(0u, 0u);
+            }
+        }
+        lds_barrier();
+
+        // ---- (3) per wave: the carried-state products, V^T W^T, outputs, and the state update
+        const Coef &cf = cfc;
+        const float4 ch = make_float4(cf.chunk[3], cf.chunk[4], cf.chunk[5], cf.chunk[0]);   // rX, cHX, cHY, m1
         if (has_prev && rho < 0x1p-40f) {        // fold rho into Z (rare; the same on every lane)
 #pragma unroll
-            for (int jb = 0; jb < JB; ++jb)
+            for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) X[jb][i] *= rho;
+                for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) X[ct][jb][i] *= rho;
             rho = 1.f;
         }
         // scalars of the basis after this chunk (the first chunk of the sequence starts from nothing
@@ -554,92 +559,112 @@ __global__ __launch_bounds__(D * 4) void causal_seg_kernel(Problem p, CausalWork
         const float hz = has_prev ? ch.y * irho1 : 0.f;   // Z += hz H
         const float hy = has_prev ? ch.z : 0.f;           // Y += hy H
 
-        // ---- stage this wave's v tile (token pairs per column) and the update operands
-        // v w_X / rho1 and v w_Y
-        {
+        // stage each tile's v (token pairs per column) and the update operands v w_X / rho1, v w_Y
+        const float4 wv = make_float4(cf.wx[vtok] * irho1, cf.wy[vtok], cf.wx[vtok + 1] * irho1, cf.wy[vtok + 1]);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
             // rows past N hold copies of row N - 1 (finite); every product they enter is zero: the
-            // record's k^ rows and W columns of absent tokens are zero
-            const uint32_t a4[4] = {va.x, va.y, va.z, va.w};
-            const uint32_t b4[4] = {vb.x, vb.y, vb.z, vb.w};
-            const float4 w4 = *reinterpret_cast<const float4 *>(co + kCoW + 2 * vtok);   // wX, wY of both tokens
-            const float4 wv = make_float4(w4.x * irho1, w4.y, w4.z * irho1, w4.w);
+            // k^ rows and W columns of absent tokens are zero
+            const int gt = CT * w + ct;
+            const uint32_t a4[4] = {va[ct].x, va[ct].y, va[ct].z, va[ct].w};
+            const uint32_t b4[4] = {vb[ct].x, vb[ct].y, vb[ct].z, vb[ct].w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 // columns 8 vh + 2i (low halves) and 8 vh + 2i + 1 (high halves)
                 const uint32_t plo = (a4[i] & 0xffffu) | (b4[i] << 16);           // (a.lo, b.lo)
                 const uint32_t phi = (a4[i] >> 16) | (b4[i] & 0xffff0000u);       // (a.hi, b.hi)
-                const int m0 = 8 * vh + 2 * i;
-                *reinterpret_cast<uint32_t *>(&svt[w][m0][vtok]) = plo;
-                *reinterpret_cast<uint32_t *>(&svt[w][m0 + 1][vtok]) = phi;
+                const int mm = 8 * vh + 2 * i;
+                *reinterpret_cast<uint32_t *>(&s_svt[gt][mm][vtok]) = plo;
+                *reinterpret_cast<uint32_t *>(&s_svt[gt][mm + 1][vtok]) = phi;
                 const float x0 = lo_f(a4[i]), y0 = lo_f(b4[i]), x1 = hi_f(a4[i]), y1 = hi_f(b4[i]);
-                *reinterpret_cast<uint32_t *>(&svx[w][m0][vtok]) = pack2(x0 * wv.x, y0 * wv.z);
-                *reinterpret_cast<uint32_t *>(&svx[w][m0 + 1][vtok]) = pack2(x1 * wv.x, y1 * wv.z);
-                *reinterpret_cast<uint32_t *>(&svy[w][m0][vtok]) = pack2(x0 * wv.y, y0 * wv.w);
-                *reinterpret_cast<uint32_t *>(&svy[w][m0 + 1][vtok]) = pack2(x1 * wv.y, y1 * wv.w);
+                *reinterpret_cast<uint32_t *>(&s_svx[gt][mm][vtok]) = pack2(x0 * wv.x, y0 * wv.z);
+                *reinterpret_cast<uint32_t *>(&s_svx[gt][mm + 1][vtok]) = pack2(x1 * wv.x, y1 * wv.z);
+                *reinterpret_cast<uint32_t *>(&s_svy[gt][mm][vtok]) = pack2(x0 * wv.y, y0 * wv.w);
+                *reinterpret_cast<uint32_t *>(&s_svy[gt][mm + 1][vtok]) = pack2(x1 * wv.y, y1 * wv.w);
             }
         }
+        bf16x8 BX[CT][kC / 32], BY[CT][kC / 32], BH[CT][kC / 32];
+        uint2 VA[CT][2], VC[CT][2];          // V^T operand halves of the intra-chunk product
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            const int gt = CT * w + ct;
+#pragma unroll
+            for (int ks2 = 0; ks2 < kC / 32; ++ks2) {
+                const int kk0 = 32 * ks2 + 8 * g4;
+                BX[ct][ks2] = *reinterpret_cast<const bf16x8 *>(&s_svx[gt][l16][kk0]);
+                BY[ct][ks2] = *reinterpret_cast<const bf16x8 *>(&s_svy[gt][l16][kk0]);
+                BH[ct][ks2] = *reinterpret_cast<const bf16x8 *>(&s_svt[gt][l16][kk0]);
+            }
+            if (!PASS1) {
+#pragma unroll
+                for (int pi = 0; pi < 2; ++pi) {
+                    VA[ct][pi] = *reinterpret_cast<const uint2 *>(&s_svt[gt][l16][32 * pi + 4 * g4]);
+                    VC[ct][pi] = *reinterpret_cast<const uint2 *>(&s_svt[gt][l16][32 * pi + 16 + 4 * g4]);
+                }
+            }
+        }
+        // next chunk's v, in flight during this chunk's matrix-core work
+        if (c + 1 < c_end) fetch_v(c + 1);
 
-        // ---- carried-state products and the state update, interleaved by pairs of row tiles:
-        // step ks reads rows 2ks, 2ks+1 of Z, Y', H (as bf16 MFMA operands, the state at t0), after
-        // which those rows are advanced by K^T V' on MFMA.
-        // every operand from this wave's staging area is read here, before the next record's
-        // copies are issued: afterwards the wave reads only the current record buffer, which the
-        // compiler can tell apart from the copy target (no wait for the copies inside the chunk)
-        bf16x8 BX[kC / 32], BY[kC / 32], BH[kC / 32];
+        // carried-state products and the state update, interleaved by pairs of row tiles: step ks
+        // reads rows 2ks, 2ks+1 of Z, Y', H (as bf16 MFMA operands, the state at t0), after which
+        // those rows are advanced by K^T V' on MFMA; each q^ and k^T operand serves every column
+        // tile of the wave
+        f32x4 ax[CT][4], ay[CT][4], ah[CT][4];
 #pragma unroll
-        for (int ks2 = 0; ks2 < kC / 32; ++ks2) {
-            const int kk0 = 32 * ks2 + 8 * g4;
-            BX[ks2] = *reinterpret_cast<const bf16x8 *>(&svx[w][l16][kk0]);
-            BY[ks2] = *reinterpret_cast<const bf16x8 *>(&svy[w][l16][kk0]);
-            BH[ks2] = *reinterpret_cast<const bf16x8 *>(&svt[w][l16][kk0]);
-        }
-        uint2 VA[2], VC[2];                  // V^T operand halves of the intra-chunk product
-        if (!PASS1) {
+        for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-            for (int pi = 0; pi < 2; ++pi) {
-                VA[pi] = *reinterpret_cast<const uint2 *>(&svt[w][l16][32 * pi + 4 * g4]);
-                VC[pi] = *reinterpret_cast<const uint2 *>(&svt[w][l16][32 * pi + 16 + 4 * g4]);
-            }
-        }
-        // next chunk's record and v, in flight during this chunk
-        fetch(min(c + 1, c_end - 1), rn);
-        f32x4 ax[4], ay[4], ah[4];
+            for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) ax[tb][i] = ay[tb][i] = ah[tb][i] = 0.f;
+                for (int i = 0; i < 4; ++i) ax[ct][tb][i] = ay[ct][tb][i] = ah[ct][tb][i] = 0.f;
         const bool carried = !PASS1 && has_prev;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             if (carried) {
-                const f32x4 &x0 = X[2 * ks], &x1 = X[2 * ks + 1];
-                const f32x4 &y0 = Y[2 * ks], &y1 = Y[2 * ks + 1];
-                const f32x4 &h0 = Hm[2 * ks], &h1 = Hm[2 * ks + 1];
-                const bf16x8 AX = as_bf16x8(pack2(x0[0], x0[1]), pack2(x0[2], x0[3]), pack2(x1[0], x1[1]), pack2(x1[2], x1[3]));
-                const bf16x8 AY = as_bf16x8(pack2(y0[0], y0[1]), pack2(y0[2], y0[3]), pack2(y1[0], y1[1]), pack2(y1[2], y1[3]));
-                const bf16x8 AH = as_bf16x8(pack2(h0[0], h0[1]), pack2(h0[2], h0[3]), pack2(h1[0], h1[1]), pack2(h1[2], h1[3]));
+                bf16x8 AX[CT], AY[CT], AH[CT];
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    const f32x4 &x0 = X[ct][2 * ks], &x1 = X[ct][2 * ks + 1];
+                    const f32x4 &y0 = Y[ct][2 * ks], &y1 = Y[ct][2 * ks + 1];
+                    const f32x4 &h0 = Hm[ct][2 * ks], &h1 = Hm[ct][2 * ks + 1];
+                    AX[ct] = as_bf16x8(pack2(x0[0], x0[1]), pack2(x0[2], x0[3]), pack2(x1[0], x1[1]), pack2(x1[2], x1[3]));
+                    AY[ct] = as_bf16x8(pack2(y0[0], y0[1]), pack2(y0[2], y0[3]), pack2(y1[0], y1[1]), pack2(y1[2], y1[3]));
+                    AH[ct] = as_bf16x8(pack2(h0[0], h0[1]), pack2(h0[2], h0[3]), pack2(h1[0], h1[1]), pack2(h1[2], h1[3]));
+                }
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb) {
-                    const bf16x8 Bq = ld16(rb + R::q_off + (size_t(tb * KS + ks) * 64 + lane) * 16);
-                    ax[tb] = mfma(AX, Bq, ax[tb]);
-                    ay[tb] = mfma(AY, Bq, ay[tb]);
-                    ah[tb] = mfma(AH, Bq, ah[tb]);
+                    // q^ features {32 ks + 4 g4 + i, 32 ks + 16 + 4 g4 + i}: the order in which a lane
+                    // holds the rows of the two 16-row state tiles
+                    const uint2 qa = *reinterpret_cast<const uint2 *>(&s_qh[16 * tb + l16][32 * ks + 4 * g4]);
+                    const uint2 qc = *reinterpret_cast<const uint2 *>(&s_qh[16 * tb + l16][32 * ks + 16 + 4 * g4]);
+                    const bf16x8 Bq = as_bf16x8(qa.x, qa.y, qc.x, qc.y);
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) {
+                        ax[ct][tb] = mfma(AX[ct], Bq, ax[ct][tb]);
+                        ay[ct][tb] = mfma(AY[ct], Bq, ay[ct][tb]);
+                        ah[ct][tb] = mfma(AH[ct], Bq, ah[ct][tb]);
+                    }
                 }
             }
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) {
                 const int jb = 2 * ks + jj;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    X[jb][i] += hz * Hm[jb][i];
-                    Y[jb][i] += hy * Hm[jb][i];
-                }
+                for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        X[ct][jb][i] += hz * Hm[ct][jb][i];
+                        Y[ct][jb][i] += hy * Hm[ct][jb][i];
+                    }
 #pragma unroll
                 for (int ks2 = 0; ks2 < kC / 32; ++ks2) {
-                    const bf16x8 Ak = ld16(rb + R::k_off + (size_t(jb * 2 + ks2) * 64 + lane) * 16);
-                    X[jb] = mfma(Ak, BX[ks2], X[jb]);
-                    Y[jb] = mfma(Ak, BY[ks2], Y[jb]);
-                    Hm[jb] = mfma(Ak, BH[ks2], Hm[jb]);
+                    const bf16x8 Ak = ld16(s_kt + (size_t(jb * 2 + ks2) * 64 + lane) * 16);
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) {
+                        X[ct][jb] = mfma(Ak, BX[ct][ks2], X[ct][jb]);
+                        Y[ct][jb] = mfma(Ak, BY[ct][ks2], Y[ct][jb]);
+                        Hm[ct][jb] = mfma(Ak, BH[ct][ks2], Hm[ct][jb]);
+                    }
                 }
             }
         }
@@ -647,55 +672,62 @@ __global__ __launch_bounds__(D * 4) void causal_seg_kernel(Problem p, CausalWork
             // the first chunk of the sequence starts from nothing
             Rs = has_prev ? ch.x * Rs : 0.f;
         } else {
-            // ---- outputs: coefficients on the carried-state products, plus V^T W^T (intra-chunk)
+            // outputs: coefficients on the carried-state products, plus V^T W^T (intra-chunk)
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) {
-                f32x4 oacc;
-                const float4 cq = *reinterpret_cast<const float4 *>(co + kCoQ + 4 * (16 * tb + l16));  // cX, beta, kappa
-                // X = rho Z at t0
-                const float cz = cq.x * rho, chh = cq.z;
-#pragma unroll
-                // (without a carried state the products are zero and the coefficients finite)
-                for (int i = 0; i < 4; ++i) oacc[i] = cz * ax[tb][i] + cq.y * ay[tb][i] + chh * ah[tb][i];
-#pragma unroll
-                for (int pi = 0; pi < 2; ++pi) {
-                    if (2 * pi > tb) continue;
-                    const uint2 a = VA[pi];
-                    const uint2 e = (2 * pi + 1 <= tb) ? VC[pi] : make_uint2(0, 0);
-                    const bf16x8 Bw = ld16(rb + R::w_off + (size_t(w_piece(tb, pi)) * 64 + lane) * 16);
-                    oacc = mfma(as_bf16x8(a.x, a.y, e.x, e.y), Bw, oacc);
-                }
-                // rows past the end go to a sink in the workspace: the store is unconditional, so the
-                // waits for the next chunk's loads never have to cover an optional store
                 const int tq = 16 * tb + l16;
+                // X = rho Z at t0 (without a carried state the products are zero and the
+                // coefficients finite)
+                const float cz = cf.qcx[tq] * rho, cb = cf.qb[tq], chh = cf.qkap[tq];
+                // rows past the end go to a sink in the workspace: the store is unconditional
                 uint16_t *dst = tq < nval ? og + static_cast<size_t>(t0 + tq) * D : work.sink + static_cast<size_t>(tq) * D;
-                const uint2 ov = make_uint2(pack2(oacc[0], oacc[1]), pack2(oacc[2], oacc[3]));
-                *reinterpret_cast<uint2 *>(dst + w * kTile + 4 * g4) = ov;
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    f32x4 oacc;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) oacc[i] = cz * ax[ct][tb][i] + cb * ay[ct][tb][i] + chh * ah[ct][tb][i];
+#pragma unroll
+                    for (int pi = 0; pi < 2; ++pi) {
+                        if (2 * pi > tb) continue;
+                        const uint2 a = VA[ct][pi];
+                        const uint2 e = (2 * pi + 1 <= tb) ? VC[ct][pi] : make_uint2(0, 0);
+                        const bf16x8 Bw = ld16(s_wop + (size_t(w_piece(tb, pi)) * 64 + lane) * 16);
+                        oacc = mfma(as_bf16x8(a.x, a.y, e.x, e.y), Bw, oacc);
+                    }
+                    const uint2 ov = make_uint2(pack2(oacc[0], oacc[1]), pack2(oacc[2], oacc[3]));
+                    *reinterpret_cast<uint2 *>(dst + (CT * w + ct) * kTile + 4 * g4) = ov;
+                }
             }
         }
         rho = rho1;
         alp = alp1;
         bet = bet1;
-        __syncthreads();          // copies of chunk c + 1 landed (vmcnt) and visible; this buffer free
+        __syncthreads();          // copies of chunk c + 1 landed (vmcnt) and visible; LDS reads done
     };
-    for (int c = c_begin; c < c_end; c += 2) {
-        chunk(c, recA, recB);
-        if (c + 1 < c_end) chunk(c + 1, recB, recA);
+    for (int c = c_begin; c < c_end; ++c) {
+        const bool odd = ((c - c_begin) & 1) != 0;      // the segment's chunks alternate buffers
+        chunk(c, odd ? s_cfB : s_cfA, odd ? s_cfA : s_cfB, odd ? s_revB : s_revA, odd ? s_revA : s_revB);
     }
 
     // back to the plain basis: X = rho Z
 #pragma unroll
-    for (int jb = 0; jb < JB; ++jb)
+    for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) X[jb][i] *= rho;
+        for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) X[ct][jb][i] *= rho;
     if (PASS1) {
         // segment-local sums and the composed scalar map, for the combine step
         float4 *dst = reinterpret_cast<float4 *>(work.segst + (static_cast<size_t>(bh) * (nseg - 1) + seg) * kSegFloats<D>);
 #pragma unroll
-        for (int jb = 0; jb < JB; ++jb) {
-            dst[(size_t(0 * JB + jb) * NW) * 64 + sidx] = make_float4(X[jb][0], X[jb][1], X[jb][2], X[jb][3]);
-            dst[(size_t(1 * JB + jb) * NW) * 64 + sidx] = make_float4(Y[jb][0], Y[jb][1], Y[jb][2], Y[jb][3]);
-            dst[(size_t(2 * JB + jb) * NW) * 64 + sidx] = make_float4(Hm[jb][0], Hm[jb][1], Hm[jb][2], Hm[jb][3]);
+        for (int ct = 0; ct < CT; ++ct) {
+            const size_t sidx = static_cast<size_t>(CT * w + ct) * 64 + lane;
+#pragma unroll
+            for (int jb = 0; jb < JB; ++jb) {
+                dst[(size_t(0 * JB + jb) * NGT) * 64 + sidx] = make_float4(X[ct][jb][0], X[ct][jb][1], X[ct][jb][2], X[ct][jb][3]);
+                dst[(size_t(1 * JB + jb) * NGT) * 64 + sidx] = make_float4(Y[ct][jb][0], Y[ct][jb][1], Y[ct][jb][2], Y[ct][jb][3]);
+                dst[(size_t(2 * JB + jb) * NGT) * 64 + sidx] = make_float4(Hm[ct][jb][0], Hm[ct][jb][1], Hm[ct][jb][2], Hm[ct][jb][3]);
+            }
         }
         if (tid == 0) work.segsc[static_cast<size_t>(bh) * nseg + seg] = make_float4(Rs, alp, bet, 0.f);
         return;
@@ -703,36 +735,35 @@ __global__ __launch_bounds__(D * 4) void causal_seg_kernel(Problem p, CausalWork
 
     // ---- final recurrent state (last segment): back to F = E (X + H/t), G = Y + (P/t) H
     if (p.st.F != nullptr && seg == nseg - 1) {
-        float m0 = kNegInf, E0 = 0.f, P0 = 0.f;
-        if (N > 0) {
-            const float *co = reinterpret_cast<const float *>(rec0 + static_cast<size_t>(nch - 1) * R::bytes + R::c_off);
-            m0 = co[kCoChunk + 3];
-            E0 = co[kCoChunk + 4];
-            P0 = co[kCoChunk + 5];
-        }
+        // the logit carry after the last chunk: its coefficient record (the segment's chunks
+        // alternate between the two buffers, starting with A)
+        const Coef &cl = ((c_end - c_begin) & 1) ? s_cfA : s_cfB;
+        const float mE = cl.chunk[0], EE = cl.chunk[1], PE = cl.chunk[2];
         const size_t mat0 = static_cast<size_t>(bh) * D * D;
         const float tf = static_cast<float>(tin + N);
 #pragma unroll
-        for (int jb = 0; jb < JB; ++jb)
+        for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float hh = Hm[jb][i];
-                const int j = 16 * jb + 4 * g4 + i;
-                const size_t idx = mat0 + static_cast<size_t>(j) * D + w * kTile + l16;
-                p.st.F[idx] = N > 0 ? E0 * (X[jb][i] + hh / tf) : 0.f;
-                p.st.G[idx] = N > 0 ? Y[jb][i] + (P0 / tf) * hh : 0.f;
-                p.st.Hs[idx] = hh;
-            }
+            for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float hh = Hm[ct][jb][i];
+                    const int j = 16 * jb + 4 * g4 + i;
+                    const size_t idx = mat0 + static_cast<size_t>(j) * D + (CT * w + ct) * kTile + l16;
+                    p.st.F[idx] = N > 0 ? EE * (X[ct][jb][i] + hh / tf) : 0.f;
+                    p.st.G[idx] = N > 0 ? Y[ct][jb][i] + (PE / tf) * hh : 0.f;
+                    p.st.Hs[idx] = hh;
+                }
         const int nls = (N + kLogitSeg - 1) / kLogitSeg;
-        if (tid < D) {
-            float su = cont ? p.sin.Su[static_cast<size_t>(bh) * D + tid] : 0.f;
-            for (int sg = 0; sg < nls; ++sg) su += work.useg[(static_cast<size_t>(bh) * nls + sg) * D + tid];
-            p.st.Su[static_cast<size_t>(bh) * D + tid] = su;
+        for (int f = tid; f < D; f += NT) {
+            float su = cont ? p.sin.Su[static_cast<size_t>(bh) * D + f] : 0.f;
+            for (int sg = 0; sg < nls; ++sg) su += work.useg[(static_cast<size_t>(bh) * nls + sg) * D + f];
+            p.st.Su[static_cast<size_t>(bh) * D + f] = su;
         }
         if (tid == 0) {
-            p.st.m[bh] = m0;
-            p.st.E[bh] = E0;
-            p.st.P[bh] = P0;
+            p.st.m[bh] = N > 0 ? mE : kNegInf;
+            p.st.E[bh] = N > 0 ? EE : 0.f;
+            p.st.P[bh] = N > 0 ? PE : 0.f;
             p.st.t[bh] = tin + N;
         }
     }
@@ -804,50 +835,31 @@ __global__ __launch_bounds__(256) void causal_seg_combine_kernel(Problem p, Caus
     }
 }
 
-template <typename K>
-hipError_t set_smem(K kernel, size_t bytes) {
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                               static_cast<int>(bytes));
-}
 
 template <int D, bool ROPE>
 hipError_t launch_one(const Problem &p, const CausalWork &w, hipStream_t stream) {
-    // the LDS size attribute is per device: set once on each device the library launches on.
-    // The flags are atomics, so concurrent first calls from several threads are well defined (both
-    // may set the attribute; the call is idempotent).
-    constexpr int kMaxDev = 64;
-    static std::atomic<bool> attr_set[kMaxDev];
-    int dev = 0;
-    hipError_t err = hipGetDevice(&dev);
-    if (err != hipSuccess) return err;
-    const bool known = dev >= 0 && dev < kMaxDev;
-    if (!known || !attr_set[dev].load(std::memory_order_acquire)) {
-        err = set_smem(&causal_prep_kernel<D, ROPE>, sizeof(PSmem<D>));
-        if (err != hipSuccess) return err;
-        if (known) attr_set[dev].store(true, std::memory_order_release);
-    }
-    const int nch = (p.N + kC - 1) / kC;
+    hipError_t err;
     const int bh = p.B * p.H;
+    const int nch = (p.N + kC - 1) / kC;
     if (nch > 0) {
-        hipLaunchKernelGGL((causal_prep_kernel<D, ROPE>), dim3(bh * nch), dim3(kPrepThreads),
-                           sizeof(PSmem<D>), stream, p, w);
+        hipLaunchKernelGGL(causal_coef_kernel, dim3((bh * nch + kCoefWaves - 1) / kCoefWaves), dim3(64 * kCoefWaves), 0,
+                           stream, p, w);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if (w.nseg > 1) {
-        hipLaunchKernelGGL((causal_seg_kernel<D, ROPE, true>), dim3(bh * (w.nseg - 1)), dim3(D * 4), 0,
-                           stream, p, w);
+        hipLaunchKernelGGL((causal_scan_kernel<D, ROPE, true>), dim3(bh * (w.nseg - 1)), dim3(kScanThreads<D>),
+                           0, stream, p, w);
         if ((err = hipGetLastError()) != hipSuccess) return err;
         hipLaunchKernelGGL((causal_seg_combine_kernel<D>), dim3(bh, (D * D / 4 + 255) / 256), dim3(256), 0,
                            stream, p, w);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
-    hipLaunchKernelGGL((causal_seg_kernel<D, ROPE, false>), dim3(bh * w.nseg), dim3(D * 4), 0, stream, p, w);
+    hipLaunchKernelGGL((causal_scan_kernel<D, ROPE, false>), dim3(bh * w.nseg), dim3(kScanThreads<D>),
+                       0, stream, p, w);
     return hipGetLastError();
 }
 
 }  // namespace
-
-size_t causal_rec_bytes(int d) { return d == 128 ? Rec<128>::bytes : Rec<64>::bytes; }
 
 // Segments of the scan: enough (head, segment) workgroups to cover the chip, whole chunks each.
 static void seg_plan(int B, int H, int N, int &nseg, int &seg_chunks) {
@@ -869,9 +881,8 @@ size_t causal_work_bytes(int B, int H, int N, int du) {
     const size_t bh = static_cast<size_t>(B) * H;
     int nseg, seg_chunks;
     seg_plan(B, H, N, nseg, seg_chunks);
-    return up(bh * N * 4) + up(bh * nls * du * 4) + up(bh * nch * 16) + up(size_t(kC) * (du / 2) * 8) +
-           up(bh * nseg * 16) + up(bh * (nseg - 1) * size_t(3) * du * du * 4) + up(size_t(kC) * du * 2) +
-           bh * nch * causal_rec_bytes(du);
+    return up(bh * N * 4) + up(bh * nls * du * 4) + up(bh * nch * 16) + up(bh * nseg * 16) +
+           up(bh * (nseg - 1) * size_t(3) * du * du * 4) + up(size_t(kC) * du * 2) + bh * nch * sizeof(Coef);
 }
 
 CausalWork causal_work_carve(void *base, int B, int H, int N, int du) {
@@ -887,20 +898,18 @@ CausalWork causal_work_carve(void *base, int B, int H, int N, int du) {
     b += up(bh * nls * du * 4);
     w.agg = reinterpret_cast<float4 *>(b);
     b += up(bh * nch * 16);
-    w.rope = reinterpret_cast<float2 *>(b);
-    b += up(size_t(kC) * (du / 2) * 8);
     w.segsc = reinterpret_cast<float4 *>(b);
     b += up(bh * w.nseg * 16);
     w.segst = reinterpret_cast<float *>(b);
     b += up(bh * (w.nseg - 1) * size_t(3) * du * du * 4);
     w.sink = reinterpret_cast<uint16_t *>(b);
     b += up(size_t(kC) * du * 2);
-    w.rec = reinterpret_cast<unsigned char *>(b);
+    w.coef = reinterpret_cast<Coef *>(b);
     return w;
 }
 
 hipError_t launch_causal_mfma(const Problem &p, const CausalWork &w, hipStream_t stream) {
-    hipError_t err = launch_logits(p, w.useg, w.s, w.agg, p.rope ? w.rope : nullptr, stream);
+    hipError_t err = launch_logits(p, w.useg, w.s, w.agg, nullptr, stream);
     if (err != hipSuccess) return err;
     if (p.d == 128) return p.rope ? launch_one<128, true>(p, w, stream) : launch_one<128, false>(p, w, stream);
     if (p.d == 64) return p.rope ? launch_one<64, true>(p, w, stream) : launch_one<64, false>(p, w, stream);

@@ -26,20 +26,27 @@ struct Problem {
 constexpr int kLogitSeg = 256;
 constexpr int kCausalChunk = 64;
 
+// Per-chunk scalar scan and coefficients of the causal MFMA path (written by its coefficient
+// kernel, read by both scan passes).
+struct Coef {
+    float qa[kCausalChunk], qm[kCausalChunk], qb[kCausalChunk], qg[kCausalChunk];   // per query t
+    float qcx[kCausalChunk], qkap[kCausalChunk];
+    float wx[kCausalChunk], wy[kCausalChunk], s[kCausalChunk], ek[kCausalChunk];     // per key i
+    float chunk[8];          // m1, E1, P1, rX, cHX, cHY, exact-exp flag (chunk end / chunk map)
+};
+
 // Workspace of the causal MFMA path, carved from one caller- or library-provided buffer.
 struct CausalWork {
     float *s;           // [B*H, N] logits
     float *useg;        // [B*H, nseg, d_u] per-segment u sums
     float4 *agg;        // [B*H, nchunk] per-chunk (max s, sum e^{s-max}, sum s, 0)
-    float2 *rope;       // [kCausalChunk, d/2] cos, sin of r * theta_j (RoPE only)
     float4 *segsc;      // [B*H, nseg] composed scalar map (Rs, Hs, Ys, 0) of each scan segment
     float *segst;       // [B*H, nseg-1, 3, d, d] segment-local sums, then segment start states
     uint16_t *sink;     // [kCausalChunk, d] bf16: output rows past N are written here and ignored
     int nseg;           // scan segments per head
     int seg_chunks;     // chunks per segment (the last one may be shorter)
-    unsigned char *rec; // [B*H, nchunk, rec_bytes(d)] per-chunk operands prepared for the scan
+    Coef *coef;         // [B*H, nchunk] scalar scan and coefficients of each chunk
 };
-size_t causal_rec_bytes(int d);
 size_t causal_work_bytes(int B, int H, int N, int du);
 CausalWork causal_work_carve(void *base, int B, int H, int N, int du);
 

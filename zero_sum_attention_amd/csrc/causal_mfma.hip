@@ -272,6 +272,7 @@ __global__ __launch_bounds__(kScanThreads<D>) void causal_scan_kernel(Problem p,
     __shared__ float s_revA[D / 2];
     __shared__ float s_revB[D / 2];
     __shared__ float s_rpp[D / 2];       // RoPE revolutions per position of pair j
+    __shared__ double s_rppd[D / 2];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -349,6 +350,7 @@ __global__ __launch_bounds__(kScanThreads<D>) void causal_scan_kernel(Problem p,
     if (ROPE && tid < D / 2) {
         const double rev = rope_rev_per_pos(tid, D, p.rope_base);
         s_rpp[tid] = static_cast<float>(rev);
+        s_rppd[tid] = rev;
         double r = static_cast<double>(tin + c_begin * kC) * rev;
         s_revA[tid] = static_cast<float>(r - rint(r));
     }
@@ -472,7 +474,7 @@ __global__ __launch_bounds__(kScanThreads<D>) void causal_scan_kernel(Problem p,
                     if (!PASS1) *reinterpret_cast<uint4 *>(&s_qh[r][8 * blk]) = make_uint4(wq[0], wq[1], wq[2], wq[3]);
                 }
             if (ROPE && tid < D / 2 && c + 1 < c_end) {
-                const double r2 = static_cast<double>(tin + t0 + kC) * rope_rev_per_pos(tid, D, p.rope_base);
+                const double r2 = static_cast<double>(tin + t0 + kC) * s_rppd[tid];
                 revn[tid] = static_cast<float>(r2 - rint(r2));
             }
         }

@@ -46,6 +46,14 @@ constexpr int kPad = 8;         // bf16 elements of row padding in LDS
 // b ^ kswz(key), so the 8-key column gathers hit distinct LDS banks.
 __device__ __forceinline__ int kswz(int key) { return ((key >> 3) & 3) << 1; }
 
+// Order of the keys along the contraction index of every K^T V-type product in a 32-key block:
+// lane group g4 holds keys {4 g4 + [0, 4)} and {16 + 4 g4 + [0, 4)}, which is the order the
+// intra-chunk weights W come in from the A^T tiles (each tile gives a lane 4 keys). The staged v
+// operands are stored in this order, so the same 16 bytes serve the state update and V^T W^T.
+__device__ __forceinline__ int kperm(int key) {
+    return (key & ~31) | (((key & 15) >> 2) << 3) | (((key >> 4) & 1) << 2) | (key & 3);
+}
+
 // (max, sum e^{s-max}) combine of two partial scans; a max of -inf marks an empty part.
 __device__ __forceinline__ void lse_combine(float &m, float &e, float m2, float e2) {
     if (m2 == kNegInf) return;
@@ -158,6 +166,7 @@ constexpr int kCoefWaves = 4;
 static_assert(sizeof(Coef) % 16 == 0, "coefficient records are copied in 16-byte pieces");
 // LDS bytes of a coefficient record rounded up to whole 64-piece (1 KiB) wave copies
 constexpr int kCoefLds = int((sizeof(Coef) / 16 + 63) / 64 * 64 * 16);
+constexpr int kCoefStage = 8 * 64 * 16;   // one 64-piece direct copy per wave, up to 8 waves
 
 __global__ __launch_bounds__(64 * kCoefWaves) void causal_coef_kernel(Problem p, CausalWork work) {
     const int lane = threadIdx.x & 63;
@@ -242,6 +251,8 @@ __global__ __launch_bounds__(kScanThreads<D>) void causal_scan_kernel(Problem p,
     constexpr int FB = D / (16 * TPR);  // 16-feature blocks per prep thread
     constexpr int RP = kC * D / 8;      // 16-byte pieces of one chunk's rows of q (or k)
     static_assert(CT == 1 && FB >= 1, "d must be 64 or 128");
+    // wave w's threads take rows [kC w / NW, kC (w + 1) / NW) in step 1, RP / NW pieces
+    static_assert(kC % NW == 0 && (RP / NW) % 64 == 0 && RP / NW == (kC / NW) * (D / 8), "copy split");
 
     // Separate LDS objects, so that the compiler can tell the target of the direct global-to-LDS
     // copies (raw rows of the next chunk) from the buffers read meanwhile, and does not wait for
@@ -256,19 +267,25 @@ __global__ __launch_bounds__(kScanThreads<D>) void causal_scan_kernel(Problem p,
     __shared__ __align__(16) unsigned char s_kt[JB * 2 * 1024];
     // intra-chunk weights as B operands of V^T W^T, piece w_piece(tb, pi) x 64 lanes x 16 bytes
     __shared__ __align__(16) unsigned char s_wop[PASS1 ? 16 : 6 * 1024];
-    // per column tile: its v tile transposed, vt[m][token] (also the H update operand), and the
-    // update operands v * w_X, v * w_Y, transposed
+    // per column tile: its v tile transposed, vt[m][kperm(token)] (also the H update operand), and
+    // the update operands v * w_X, v * w_Y, transposed in the same order
     __shared__ __align__(16) uint16_t s_svt[NGT][kTile][kC + kPad];
     __shared__ __align__(16) uint16_t s_svx[NGT][kTile][kC + kPad];
     __shared__ __align__(16) uint16_t s_svy[NGT][kTile][kC + kPad];
-    // the chunk's coefficient record and RoPE phase of the chunk start (revolutions, in
-    // [-1/2, 1/2]), double-buffered as separate objects: the next chunk's are written meanwhile.
-    // A wave's direct copy writes 64 pieces of 16 bytes: the record buffers are padded to whole
-    // copies, so the lanes past the record's end write into the padding.
-    __shared__ __align__(16) unsigned char s_cfA_raw[kCoefLds];
-    __shared__ __align__(16) unsigned char s_cfB_raw[kCoefLds];
-    Coef &s_cfA = *reinterpret_cast<Coef *>(s_cfA_raw);
-    Coef &s_cfB = *reinterpret_cast<Coef *>(s_cfB_raw);
+    // the coefficient record of the next chunk as it arrives by direct copy (s_cfS), and the current
+    // chunk's (s_cfC), copied over from s_cfS at the start of the chunk: the copies always target
+    // the one object, which is never read while they are in flight (a copy whose target is not a
+    // fixed object makes the compiler wait for it before every later LDS access). A wave's direct
+    // copy writes 64 pieces of 16 bytes: the buffers are padded to whole copies, so the lanes past
+    // the record's end write into the padding. The RoPE phase of the chunk start (revolutions, in
+    // [-1/2, 1/2]) is double-buffered: the next chunk's is written meanwhile.
+    // one 64-piece copy per wave (D / 16 waves); a fixed size (with a size that depends on D the
+    // host compiler drops the kernel's launch stub)
+    __shared__ __align__(16) unsigned char s_cfS_raw[kCoefStage];
+    static_assert(NW * 64 * 16 <= kCoefStage, "coefficient staging buffer");
+    __shared__ __align__(16) unsigned char s_cfC_raw[kCoefLds];
+    Coef &s_cfS = *reinterpret_cast<Coef *>(s_cfS_raw);
+    const Coef &s_cfC = *reinterpret_cast<const Coef *>(s_cfC_raw);
     __shared__ float s_revA[D / 2];
     __shared__ float s_revB[D / 2];
     __shared__ float s_rpp[D / 2];       // RoPE revolutions per position of pair j
@@ -357,6 +374,7 @@ __global__ __launch_bounds__(kScanThreads<D>) void causal_scan_kernel(Problem p,
 
     // v of this wave's column tiles: lane holds tokens 2 (lane & 31), +1 and columns 8 (lane >> 5) + [0, 8)
     const int vtok = 2 * (lane & 31), vh = lane >> 5;
+    const int vpos = kperm(vtok);       // and kperm(vtok + 1) = vpos + 1
     uint4 va[CT], vb[CT];
     auto fetch_v = [&](const int c) __attribute__((always_inline)) {
         const int t_ = c * kC + vtok;      // rows past N read row N-1 (in bounds)
@@ -369,25 +387,26 @@ __global__ __launch_bounds__(kScanThreads<D>) void causal_scan_kernel(Problem p,
     };
     // the coefficient record and the raw q and k rows of chunk c into LDS: the chunk's rows are
     // contiguous in memory, so piece i (16 bytes) is element 8 i of the block; pieces past the
-    // last token repeat the last valid piece (the rows they fill are zeroed when read)
-    auto fetch_raw = [&](const int c, Coef &cdst) __attribute__((always_inline)) {
+    // last token repeat the last valid piece (the rows they fill are zeroed when read). Wave w
+    // copies exactly the pieces its own threads read next: rows [kC w / NW, kC (w + 1) / NW) of q
+    // and k in step 1, and pieces [64 w, 64 w + 64) of the record in the copy to s_cfC, so each
+    // wave's wait for its own copies (which the compiler places) is all the reads need.
+    auto fetch_raw = [&](const int c) __attribute__((always_inline)) {
         {
+            // every wave issues one copy (the waves past the record copy its last piece into their
+            // part of the padding): the same memory operations on every wave and trip, so the
+            // waits the compiler places for them are exact counts
             constexpr int CP = int(sizeof(Coef) / 16);
+            static_assert(CP <= NT, "the record fits one copy per wave");
             const uint4 *srcc = reinterpret_cast<const uint4 *>(work.coef + static_cast<size_t>(bh) * nch + c);
-#pragma unroll
-            for (int i = 0; i < (CP + NT - 1) / NT; ++i) {
-                const int base = w * 64 + i * NT;                // wave-uniform
-                if (base < CP)
-                    __builtin_amdgcn_global_load_lds(srcc + min(base + lane, CP - 1),
-                                                     reinterpret_cast<unsigned char *>(&cdst) + base * 16, 16, 0, 0);
-            }
+            __builtin_amdgcn_global_load_lds(srcc + min(w * 64 + lane, CP - 1), s_cfS_raw + w * 64 * 16, 16, 0, 0);
         }
         const int nv = min(kC, N - c * kC) * (D / 8);
         const uint4 *srck = reinterpret_cast<const uint4 *>(kg + static_cast<size_t>(c) * kC * D);
         const uint4 *srcq = reinterpret_cast<const uint4 *>(qg + static_cast<size_t>(c) * kC * D);
 #pragma unroll
         for (int i = 0; i < RP / NT; ++i) {
-            const int base = w * 64 + i * NT;                    // wave-uniform
+            const int base = w * (RP / NW) + i * 64;             // wave-uniform
             __builtin_amdgcn_global_load_lds(srck + min(base + lane, nv - 1),
                                              reinterpret_cast<unsigned char *>(s_rawk) + base * 16, 16, 0, 0);
             if (!PASS1)
@@ -396,19 +415,22 @@ __global__ __launch_bounds__(kScanThreads<D>) void causal_scan_kernel(Problem p,
         }
     };
     if (c_begin < c_end) {
-        fetch_raw(c_begin, s_cfA);
+        fetch_raw(c_begin);
         fetch_v(c_begin);
     }
     // unconditional: the start-state loads and the first copies are complete on every path into
     // the loop
     __syncthreads();
 
-    // one chunk: its coefficient record and start phase in (cfc, revc); the next chunk's are
-    // written into (cfn, revn)
-    auto chunk = [&](const int c, const Coef &cfc, Coef &cfn, const float *revc, float *revn) __attribute__((always_inline)) {
+    // one chunk: its start phase in revc, the next chunk's written into revn
+    auto chunk = [&](const int c, const float *revc, float *revn) __attribute__((always_inline)) {
         const int t0 = c * kC;
         const int nval = min(kC, N - t0);
         const bool has_prev = tin + t0 > 0;      // tokens before this chunk (a carried state)
+        // this chunk's coefficient record, from the copy's target to the buffer read below (published
+        // by the barrier after step 1)
+        if (tid < int(sizeof(Coef) / 16))
+            reinterpret_cast<uint4 *>(s_cfC_raw)[tid] = reinterpret_cast<const uint4 *>(s_cfS_raw)[tid];
 
         // ---- (1) unit, rotated q^ and k^ rows: thread = (row r, FB blocks of 16 features)
         {
@@ -481,27 +503,37 @@ __global__ __launch_bounds__(kScanThreads<D>) void causal_scan_kernel(Problem p,
         lds_barrier();
 
         // ---- (2) next chunk's record and raw rows in flight; k^T operands; A^T and W
-        if (c + 1 < c_end) fetch_raw(c + 1, cfn);
+        // unconditional (the last chunk fetches itself again, into buffers no longer read), so that
+        // every trip issues the same memory operations and the waits for them are exact counts
+        fetch_raw(min(c + 1, c_end - 1));
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
             // k^T operands of row tile jb: 8 keys per lane gathered from the swizzled rows
             const int jb = CT * w + ct;
             const int j = 16 * jb + l16;
+            // keys in kperm order: {4 g4 + [0, 4)} with swizzle 2 (g4 >> 1), {16 + 4 g4 + [0, 4)} with
+            // swizzle 2 ((2 + (g4 >> 1)) & 3). (All gathers before the stores: an LDS read that
+            // follows an LDS store while direct copies are in flight makes the compiler wait for the
+            // copies.)
+            const int jlo = (((j >> 3) ^ (2 * (g4 >> 1))) << 3) | (j & 7);
+            const int jhi = (((j >> 3) ^ (2 * ((2 + (g4 >> 1)) & 3))) << 3) | (j & 7);
+            bf16x8 a2[kC / 32];
 #pragma unroll
             for (int ks2 = 0; ks2 < kC / 32; ++ks2) {
-                const int kk0 = 32 * ks2 + 8 * g4;
-                const int jc = (((j >> 3) ^ (2 * g4)) << 3) | (j & 7);   // kswz(kk0 + cc) == 2 * g4
-                bf16x8 a;
 #pragma unroll
-                for (int cc = 0; cc < 8; ++cc) a[cc] = static_cast<short>(s_kh[kk0 + cc][jc]);
-                st16(s_kt + (size_t(jb * 2 + ks2) * 64 + lane) * 16, a);
+                for (int cc = 0; cc < 4; ++cc) {
+                    a2[ks2][cc] = static_cast<short>(s_kh[32 * ks2 + 4 * g4 + cc][jlo]);
+                    a2[ks2][cc + 4] = static_cast<short>(s_kh[32 * ks2 + 16 + 4 * g4 + cc][jhi]);
+                }
             }
+#pragma unroll
+            for (int ks2 = 0; ks2 < kC / 32; ++ks2) st16(s_kt + (size_t(jb * 2 + ks2) * 64 + lane) * 16, a2[ks2]);
         }
         if (!PASS1) {
             // the ten (query block tb, key block kb <= tb) tiles of A^T, spread over the waves; each
             // fills its half (8 bytes per lane) of the W piece of key pair kb / 2, and the tiles
             // (0, 0) and (2, 2) also the zero half whose keys all follow the queries
-            const Coef &cf = cfc;
+            const Coef &cf = s_cfC;
             const bool exact_exp = cf.chunk[6] != 0.f;
             for (int blk = w; blk < 10; blk += NW) {
                 const int tb = blk < 1 ? 0 : blk < 3 ? 1 : blk < 6 ? 2 : 3;
@@ -541,7 +573,7 @@ __global__ __launch_bounds__(kScanThreads<D>) void causal_scan_kernel(Problem p,
         lds_barrier();
 
         // ---- (3) per wave: the carried-state products, V^T W^T, outputs, and the state update
-        const Coef &cf = cfc;
+        const Coef &cf = s_cfC;
         const float4 ch = make_float4(cf.chunk[3], cf.chunk[4], cf.chunk[5], cf.chunk[0]);   // rX, cHX, cHY, m1
         if (has_prev && rho < 0x1p-40f) {        // fold rho into Z (rare; the same on every lane)
 #pragma unroll
@@ -576,17 +608,16 @@ __global__ __launch_bounds__(kScanThreads<D>) void causal_scan_kernel(Problem p,
                 const uint32_t plo = (a4[i] & 0xffffu) | (b4[i] << 16);           // (a.lo, b.lo)
                 const uint32_t phi = (a4[i] >> 16) | (b4[i] & 0xffff0000u);       // (a.hi, b.hi)
                 const int mm = 8 * vh + 2 * i;
-                *reinterpret_cast<uint32_t *>(&s_svt[gt][mm][vtok]) = plo;
-                *reinterpret_cast<uint32_t *>(&s_svt[gt][mm + 1][vtok]) = phi;
+                *reinterpret_cast<uint32_t *>(&s_svt[gt][mm][vpos]) = plo;
+                *reinterpret_cast<uint32_t *>(&s_svt[gt][mm + 1][vpos]) = phi;
                 const float x0 = lo_f(a4[i]), y0 = lo_f(b4[i]), x1 = hi_f(a4[i]), y1 = hi_f(b4[i]);
-                *reinterpret_cast<uint32_t *>(&s_svx[gt][mm][vtok]) = pack2(x0 * wv.x, y0 * wv.z);
-                *reinterpret_cast<uint32_t *>(&s_svx[gt][mm + 1][vtok]) = pack2(x1 * wv.x, y1 * wv.z);
-                *reinterpret_cast<uint32_t *>(&s_svy[gt][mm][vtok]) = pack2(x0 * wv.y, y0 * wv.w);
-                *reinterpret_cast<uint32_t *>(&s_svy[gt][mm + 1][vtok]) = pack2(x1 * wv.y, y1 * wv.w);
+                *reinterpret_cast<uint32_t *>(&s_svx[gt][mm][vpos]) = pack2(x0 * wv.x, y0 * wv.z);
+                *reinterpret_cast<uint32_t *>(&s_svx[gt][mm + 1][vpos]) = pack2(x1 * wv.x, y1 * wv.z);
+                *reinterpret_cast<uint32_t *>(&s_svy[gt][mm][vpos]) = pack2(x0 * wv.y, y0 * wv.w);
+                *reinterpret_cast<uint32_t *>(&s_svy[gt][mm + 1][vpos]) = pack2(x1 * wv.y, y1 * wv.w);
             }
         }
         bf16x8 BX[CT][kC / 32], BY[CT][kC / 32], BH[CT][kC / 32];
-        uint2 VA[CT][2], VC[CT][2];          // V^T operand halves of the intra-chunk product
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
             const int gt = CT * w + ct;
@@ -597,16 +628,9 @@ __global__ __launch_bounds__(kScanThreads<D>) void causal_scan_kernel(Problem p,
                 BY[ct][ks2] = *reinterpret_cast<const bf16x8 *>(&s_svy[gt][l16][kk0]);
                 BH[ct][ks2] = *reinterpret_cast<const bf16x8 *>(&s_svt[gt][l16][kk0]);
             }
-            if (!PASS1) {
-#pragma unroll
-                for (int pi = 0; pi < 2; ++pi) {
-                    VA[ct][pi] = *reinterpret_cast<const uint2 *>(&s_svt[gt][l16][32 * pi + 4 * g4]);
-                    VC[ct][pi] = *reinterpret_cast<const uint2 *>(&s_svt[gt][l16][32 * pi + 16 + 4 * g4]);
-                }
-            }
         }
         // next chunk's v, in flight during this chunk's matrix-core work
-        if (c + 1 < c_end) fetch_v(c + 1);
+        fetch_v(min(c + 1, c_end - 1));
 
         // carried-state products and the state update, interleaved by pairs of row tiles: step ks
         // reads rows 2ks, 2ks+1 of Z, Y', H (as bf16 MFMA operands, the state at t0), after which
@@ -691,10 +715,12 @@ __global__ __launch_bounds__(kScanThreads<D>) void causal_scan_kernel(Problem p,
 #pragma unroll
                     for (int pi = 0; pi < 2; ++pi) {
                         if (2 * pi > tb) continue;
-                        const uint2 a = VA[ct][pi];
-                        const uint2 e = (2 * pi + 1 <= tb) ? VC[ct][pi] : make_uint2(0, 0);
+                        // V^T: keys {32 pi + 4 g4 + [0, 4)} and {32 pi + 16 + 4 g4 + [0, 4)}, which is
+                        // BH (kperm order); the second half is zero where all its keys follow the queries
+                        bf16x8 vt = BH[ct][pi];
+                        if (2 * pi + 1 > tb) vt[4] = vt[5] = vt[6] = vt[7] = 0;
                         const bf16x8 Bw = ld16(s_wop + (size_t(w_piece(tb, pi)) * 64 + lane) * 16);
-                        oacc = mfma(as_bf16x8(a.x, a.y, e.x, e.y), Bw, oacc);
+                        oacc = mfma(vt, Bw, oacc);
                     }
                     const uint2 ov = make_uint2(pack2(oacc[0], oacc[1]), pack2(oacc[2], oacc[3]));
                     *reinterpret_cast<uint2 *>(dst + (CT * w + ct) * kTile + 4 * g4) = ov;
@@ -704,11 +730,14 @@ __global__ __launch_bounds__(kScanThreads<D>) void causal_scan_kernel(Problem p,
         rho = rho1;
         alp = alp1;
         bet = bet1;
-        __syncthreads();          // copies of chunk c + 1 landed (vmcnt) and visible; LDS reads done
+        // LDS reads and writes of this chunk done everywhere. No memory fence: it would wait for the
+        // next chunk's v loads just issued; the direct copies of chunk c + 1 are read only by the
+        // wave that issued them, after the wait the compiler places for it.
+        lds_barrier();
     };
     for (int c = c_begin; c < c_end; ++c) {
-        const bool odd = ((c - c_begin) & 1) != 0;      // the segment's chunks alternate buffers
-        chunk(c, odd ? s_cfB : s_cfA, odd ? s_cfA : s_cfB, odd ? s_revB : s_revA, odd ? s_revA : s_revB);
+        const bool odd = ((c - c_begin) & 1) != 0;      // the segment's chunks alternate phase buffers
+        chunk(c, odd ? s_revB : s_revA, odd ? s_revA : s_revB);
     }
 
     // back to the plain basis: X = rho Z
@@ -737,9 +766,8 @@ __global__ __launch_bounds__(kScanThreads<D>) void causal_scan_kernel(Problem p,
 
     // ---- final recurrent state (last segment): back to F = E (X + H/t), G = Y + (P/t) H
     if (p.st.F != nullptr && seg == nseg - 1) {
-        // the logit carry after the last chunk: its coefficient record (the segment's chunks
-        // alternate between the two buffers, starting with A)
-        const Coef &cl = ((c_end - c_begin) & 1) ? s_cfA : s_cfB;
+        // the logit carry after the last chunk: its coefficient record, still in s_cfC
+        const Coef &cl = s_cfC;
         const float mE = cl.chunk[0], EE = cl.chunk[1], PE = cl.chunk[2];
         const size_t mat0 = static_cast<size_t>(bh) * D * D;
         const float tf = static_cast<float>(tin + N);

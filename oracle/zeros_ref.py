@@ -22,6 +22,10 @@ Sources (cited by page title and section; the pages are web summaries of arXiv 2
                     non-causal (encoder) modes.
   [Summary/plain]   ai.info page "ZeroS: Zero-Sum Linear Attention for Efficient Transformers",
                     section "Methodology in Plain English" (same method in English).
+  [Summary/SM]      same ai.info page and section: the same reweighting applied to standard
+                    softmax attention gives the quadratic-time variant ZeroS-SM (also a row of the
+                    MAD table in the Paper-Notes section 实验关键数据). Its exact form is in an
+                    appendix the pages do not carry: parity unpinned against the authors.
 
 Readings taken where the pages leave a step open (each is listed in the design notes):
   * delta_{t,i} = s_i - (1/t) sum_{j<=t} s_j, the first-order Taylor term of softmax about equal
@@ -44,6 +48,11 @@ Readings taken where the pages leave a step open (each is listed in the design n
     mode); sigma0 = sigmoid(g0). Without g0 the term is absent (the default).
   * A running maximum m_t of the logits rescales e^{s}: the state stores
     Et = sum e^{s_i - m_t} and Ft = sum e^{s_i - m_t} k^_i^T v_i (this leaves o unchanged).
+  * ZeroS-SM [Summary/SM]: the logits are the standard scaled dot products
+    l_{t,i} = q_t . k_i / sqrt(d) (q and k as given, rotated by RoPE at their 0-based positions
+    when asked; no normalisation and no separate cosine factor, the logits carry both); the row
+    softmax over i <= t is split and reweighted exactly as above, w_{t,i} = sigma1_t delta_{t,i}/t
+    + sigmah_t eps_{t,i} (+ sigma0_t / t), and o_t = sum_{i<=t} w_{t,i} v_i. Causal only.
 
 Backward: ``causal_backward`` gives the gradients of L = <dO, o> for every input, by the chain
 rule through the explicit weight definition (training replaces attention by this module
@@ -462,3 +471,53 @@ def causal_backward(q, k, v, u, mu, tau, g1, gh, dO, rope=False, rope_base=10000
     if sig0 is not None:
         out["g0"] = dsig0 * sig0 * (1.0 - sig0)
     return out
+
+
+# --------------------------------------------------------------------------------------------
+# ZeroS-SM: the zero-sum reweighting applied to standard (quadratic) softmax attention.
+# --------------------------------------------------------------------------------------------
+
+def sm_logit_row(q, k, t, rope=False, rope_base=10000.0):
+    """l_{t,i} = q_t . k_i / sqrt(d) for i = 1..t (1-based t) [Summary/SM]; with RoPE, q_t and
+    k_i are rotated by their 0-based positions t - 1 and i - 1 first."""
+    q, k = _f64(q), _f64(k)
+    d = q.shape[-1]
+    qt = q[..., t - 1:t, :]
+    kr = k[..., :t, :]
+    if rope:
+        qt = rope_rotate(qt, np.array([t - 1], dtype=F64), rope_base)
+        kr = rope_rotate(kr, np.arange(t, dtype=F64), rope_base)
+    return np.sum(qt * kr, axis=-1) / np.sqrt(F64(d))              # [..., t]
+
+
+def sm_weight_row(q, k, t, g1, gh, rope=False, rope_base=10000.0, g0=None):
+    """Weights w_{t,1..t} of ZeroS-SM [Summary/SM] with the split of [Notes/zero-sum]: softmax
+    p over the row, its first-order part dl = l - mean(l), the residual r = p - 1/t - dl/t, and
+    w = sigma1_t dl / t + sigmah_t r (+ sigma0_t / t). g1, gh (g0) are the row's pre-activations."""
+    lg = sm_logit_row(q, k, t, rope, rope_base)
+    p = np.exp(lg - np.max(lg, axis=-1, keepdims=True))
+    p = p / np.sum(p, axis=-1, keepdims=True)
+    dl = lg - np.mean(lg, axis=-1, keepdims=True)
+    r = p - 1.0 / t - dl / t
+    w = sigmoid(g1)[..., None] * dl / t + sigmoid(gh)[..., None] * r
+    if g0 is not None:
+        w = w + sigmoid(g0)[..., None] / t
+    return w
+
+
+def sm_causal_forward(q, k, v, g1, gh, rope=False, rope_base=10000.0, g0=None, rows=None):
+    """ZeroS-SM causal output o_t = sum_{i<=t} w_{t,i} v_i [Summary/SM], row by row.
+
+    q, k, v [..., N, d]; g1, gh (g0) [..., N]. ``rows`` (1-based positions) limits the output to
+    those rows, returned as [..., len(rows), d]; each row costs O(t d).
+    """
+    v = _f64(v)
+    N = v.shape[-2]
+    ts = range(1, N + 1) if rows is None else rows
+    out = []
+    for t in ts:
+        w = sm_weight_row(q, k, t, _f64(g1)[..., t - 1], _f64(gh)[..., t - 1], rope, rope_base,
+                          None if g0 is None else _f64(g0)[..., t - 1])
+        out.append(np.einsum("...i,...id->...d", w, v[..., :t, :]))
+    return np.stack(out, axis=-2)
+

@@ -5,7 +5,8 @@ an index or scale off by one, a transposed operand), loads the changed module in
 ``oracle.zeros_ref`` in a fresh interpreter, and runs the oracle's pin tests
 (``tests/test_oracle.py``: hand-worked fixtures, closed forms, the explicit O(N^2) weights,
 library softmax limits, invariants; ``tests/test_oracle_backward.py``: finite differences of the
-recurrent forward and the identities of the backward). Every planted mistake must make at least one pin fail. The
+recurrent forward and the identities of the backward; ``tests/test_oracle_sm.py``: the ZeroS-SM
+pins). Every planted mistake must make at least one pin fail. The
 mutation is applied on the CPU, to a copy of the source in memory; nothing is written to disk.
 Each original fragment must occur exactly once, so a case cannot silently stop applying when the
 oracle's text changes.
@@ -78,6 +79,20 @@ MUTATIONS = [
     ("bwd: k gradient from the untransposed product", "dkh = np.swapaxes(dC, -1, -2) @ qh", "dkh = dC @ qh"),
     ("bwd: sigmah gradient from delta", "dsigh = np.sum(dW * eps, axis=-1)", "dsigh = np.sum(dW * delta, axis=-1)"),
     ("bwd: gate derivative", '"g1": dsig1 * sig1 * (1.0 - sig1)', '"g1": dsig1 * sig1'),
+    # ZeroS-SM
+    ("SM: logits without 1/sqrt(d)", "return np.sum(qt * kr, axis=-1) / np.sqrt(F64(d))",
+     "return np.sum(qt * kr, axis=-1)"),
+    ("SM: residual keeps the uniform term", "r = p - 1.0 / t - dl / t", "r = p - dl / t"),
+    ("SM: first order without the row mean", "dl = lg - np.mean(lg, axis=-1, keepdims=True)", "dl = lg"),
+    ("SM: first-order term without 1/t", "w = sigmoid(g1)[..., None] * dl / t + sigmoid(gh)",
+     "w = sigmoid(g1)[..., None] * dl + sigmoid(gh)"),
+    ("SM: gates swapped", "w = sigmoid(g1)[..., None] * dl / t + sigmoid(gh)[..., None] * r",
+     "w = sigmoid(gh)[..., None] * dl / t + sigmoid(g1)[..., None] * r"),
+    ("SM: query rotated one position late", "qt = rope_rotate(qt, np.array([t - 1], dtype=F64), rope_base)",
+     "qt = rope_rotate(qt, np.array([t], dtype=F64), rope_base)"),
+    ("SM: zero-order gate without 1/t", "w = w + sigmoid(g0)[..., None] / t", "w = w + sigmoid(g0)[..., None]"),
+    ("SM: softmax not normalised", "p = np.exp(lg - np.max(lg, axis=-1, keepdims=True))\n    p = p / np.sum(p, axis=-1, keepdims=True)",
+     "p = np.exp(lg - np.max(lg, axis=-1, keepdims=True))"),
     ("bwd: zero-order gate without 1/t", "dsig0 = np.sum(dW, axis=-1) / tt if", "dsig0 = np.sum(dW, axis=-1) if"),
 ]
 
@@ -94,7 +109,7 @@ exec(compile(src.replace(old, new), {oracle!r}, "exec"), mod.__dict__)
 sys.modules["oracle.zeros_ref"] = mod
 oracle.zeros_ref = mod
 import pytest
-sys.exit(pytest.main([{tests!r}, {tests_bwd!r}, "-x", "-q", "-p", "no:cacheprovider", "-W", "ignore"]))
+sys.exit(pytest.main([{tests!r}, {tests_bwd!r}, {tests_sm!r}, "-x", "-q", "-p", "no:cacheprovider", "-W", "ignore"]))
 """
 
 
@@ -108,7 +123,8 @@ def test_fragments_present():
 def test_planted_mistake_is_caught(name, old, new):
     code = RUNNER.format(root=ROOT, old=old, new=new, oracle=ORACLE,
                          tests=os.path.join(ROOT, "tests", "test_oracle.py"),
-                         tests_bwd=os.path.join(ROOT, "tests", "test_oracle_backward.py"))
+                         tests_bwd=os.path.join(ROOT, "tests", "test_oracle_backward.py"),
+                         tests_sm=os.path.join(ROOT, "tests", "test_oracle_sm.py"))
     res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT, timeout=300)
     assert "fragment no longer unique" not in res.stderr, res.stderr[-2000:]
     # pytest exit code 1: a pin failed (the mistake was caught); 0 would mean every pin passed

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define ZEROS_ABI_VERSION 3
+#define ZEROS_ABI_VERSION 4
 
 typedef enum {
     ZEROS_OK = 0,
@@ -212,6 +212,28 @@ zeros_status zeros_bwd_causal(const zeros_shape *shape,
 
 /* Scratch bytes zeros_bwd_causal needs for `shape` (0 for invalid sizes). */
 size_t zeros_bwd_causal_workspace_bytes(const zeros_shape *shape);
+
+/*
+ * ZeroS-SM, causal (ai.info page "ZeroS: Zero-Sum Linear Attention for Efficient Transformers",
+ * Methodology in Plain English: the same zero-sum reweighting applied to standard softmax
+ * attention, the quadratic-time variant; the split and the gates as in the Paper-Notes page,
+ * 关键设计). With l_{t,i} = q_t . k_i / sqrt(d) for i <= t (q, k rotated by RoPE at their 0-based
+ * positions when shape->rope is 1), p_t = softmax over i of l_{t,i}, delta_{t,i} = l_{t,i} minus the
+ * row mean:  o_t = sum_{i<=t} [sigma1_t delta_{t,i}/t + sigmah_t (p_{t,i} - 1/t - delta_{t,i}/t)
+ * (+ sigma0_t/t)] v_i, sigma = sigmoid of g1, gh (g0: NULL for none). The pages give ZeroS-SM only
+ * by that sentence; this reading is the plainest one (no cosine factor: the logits carry it).
+ * q, k, v, o [B, H, N, d]; g1, gh, g0 [B, H, N]; bfloat16 only (ZEROS_ERR_UNSUPPORTED otherwise),
+ * d = 64 or 128, float32 accumulation; shape->d_u is not used (any value >= 1). o must not overlap
+ * an input; q, k, v, o 16-byte aligned. workspace: zeros_sm_fwd_causal_workspace_bytes(shape) bytes
+ * (the rotated q and k with RoPE, else 0 and it may be NULL), 256-byte aligned, caller-owned, used
+ * while the call's work runs on `stream`.
+ */
+zeros_status zeros_sm_fwd_causal(const zeros_shape *shape, const void *q, const void *k, const void *v,
+                                 const void *g1, const void *gh, const void *g0, void *o,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/* Scratch bytes zeros_sm_fwd_causal needs for `shape` (0 without RoPE or for invalid sizes). */
+size_t zeros_sm_fwd_causal_workspace_bytes(const zeros_shape *shape);
 
 /* Bytes of one state for S x H heads when packed by zeros_state_from_buffer (256-B aligned
  * fields, order F, G, Hs, Su, m, E, P, t). Returns 0 for invalid sizes. */

@@ -332,3 +332,41 @@ def test_float32_segment_plan_workspace(lib, B, H, N, d, nseg):
         expect += up(bh * (nseg - 1) * 3 * d * d * 4) + up(bh * nseg * 4)
     got = lib.zeros_fwd_causal_workspace_bytes(ctypes.byref(shape(B=B, H=H, N=N, d=d, d_u=d, dtype=0)))
     assert got == expect
+
+
+# ---- ZeroS-SM (zeros_sm_fwd_causal): host-side validation only
+
+def call_sm(lib, shp, ptrs=None, ws=None, ws_bytes=0):
+    p = dict(P, **(ptrs or {}))
+    return lib.zeros_sm_fwd_causal(ctypes.byref(shp) if shp is not None else None, p["q"], p["k"], p["v"],
+                                   p["g1"], p["gh"], p["g0"], p["o"], ws, ws_bytes, None)
+
+
+def sm_shape(**kw):
+    base = dict(B=1, H=2, N=8, d=64, d_u=64, dtype=1)
+    base.update(kw)
+    return shape(**base)
+
+
+def test_sm_rejects_bad_arguments(lib):
+    assert call_sm(lib, None) == L.ZEROS_ERR_NULL
+    for name in ("q", "k", "v", "g1", "gh", "o"):
+        assert call_sm(lib, sm_shape(), {name: None}) == L.ZEROS_ERR_NULL
+    assert call_sm(lib, sm_shape(dtype=0)) == L.ZEROS_ERR_UNSUPPORTED          # bfloat16 only
+    assert call_sm(lib, sm_shape(dtype=7)) == L.ZEROS_ERR_DTYPE
+    for d in (16, 32, 96, 256):
+        assert call_sm(lib, sm_shape(d=d, d_u=d)) == L.ZEROS_ERR_UNSUPPORTED
+    assert call_sm(lib, sm_shape(N=-1)) == L.ZEROS_ERR_SHAPE
+    assert call_sm(lib, sm_shape(rope=1, base=0.5)) == L.ZEROS_ERR_SHAPE
+    assert call_sm(lib, sm_shape(), {"q": P["q"] + 2}) == L.ZEROS_ERR_SHAPE  # misaligned
+    assert call_sm(lib, sm_shape(), {"o": P["v"] + 256}) == L.ZEROS_ERR_ALIAS
+    assert call_sm(lib, sm_shape(), {"o": P["g0"]}) == L.ZEROS_ERR_ALIAS
+    # RoPE needs the workspace for the rotated q and k
+    assert call_sm(lib, sm_shape(rope=1)) == L.ZEROS_ERR_NULL
+    need = lib.zeros_sm_fwd_causal_workspace_bytes(ctypes.byref(sm_shape(rope=1)))
+    assert need == 2 * 1 * 2 * 8 * 64 * 2
+    assert call_sm(lib, sm_shape(rope=1), ws=0x7f000000, ws_bytes=need - 1) == L.ZEROS_ERR_SHAPE
+    assert call_sm(lib, sm_shape(rope=1), ws=P["q"], ws_bytes=need) == L.ZEROS_ERR_ALIAS
+    assert lib.zeros_sm_fwd_causal_workspace_bytes(ctypes.byref(sm_shape())) == 0
+    # no tokens: nothing to do, whatever the pointers
+    assert call_sm(lib, sm_shape(N=0), {"q": None, "o": None}) == L.ZEROS_OK

@@ -53,7 +53,7 @@ def run_encoder(x, dtype, rope=False):
 
 def test_library_is_native():
     lib = Z.load_library()
-    assert lib.zeros_abi_version() == 3
+    assert lib.zeros_abi_version() == 4
     assert torch.cuda.is_available()
 
 

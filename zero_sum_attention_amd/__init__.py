@@ -16,4 +16,6 @@ from ._lib import (  # noqa: F401
     zeros_fwd_causal_workspace_bytes,
     zeros_fwd_encoder,
     zeros_fwd_encoder_workspace_bytes,
+    zeros_sm_fwd_causal,
+    zeros_sm_fwd_causal_workspace_bytes,
 )

@@ -70,6 +70,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.zeros_bwd_causal.restype = i32
     lib.zeros_bwd_causal_workspace_bytes.argtypes = [ctypes.POINTER(zeros_shape)]
     lib.zeros_bwd_causal_workspace_bytes.restype = ctypes.c_size_t
+    # shape, q, k, v, g1, gh, g0, o, workspace, workspace_bytes, stream
+    lib.zeros_sm_fwd_causal.argtypes = [ctypes.POINTER(zeros_shape), vp, vp, vp, vp, vp, vp, vp, vp,
+                                        ctypes.c_size_t, vp]
+    lib.zeros_sm_fwd_causal.restype = i32
+    lib.zeros_sm_fwd_causal_workspace_bytes.argtypes = [ctypes.POINTER(zeros_shape)]
+    lib.zeros_sm_fwd_causal_workspace_bytes.restype = ctypes.c_size_t
     lib.zeros_state_bytes.argtypes = [i32, i32, i32, i32]
     lib.zeros_state_bytes.restype = ctypes.c_size_t
     lib.zeros_state_from_buffer.argtypes = [vp, i32, i32, i32, i32, ctypes.POINTER(zeros_state)]
@@ -290,6 +296,40 @@ def zeros_fwd_encoder_workspace_bytes(B: int, H: int, N: int, d: int, d_u: int, 
     lib = load_library()
     shp = zeros_shape(B, H, N, d, d_u, _DT[dtype], 0, 10000.0)
     return int(lib.zeros_fwd_encoder_workspace_bytes(ctypes.byref(shp)))
+
+
+def zeros_sm_fwd_causal(q, k, v, g1, gh, *, g0: torch.Tensor | None = None, rope: bool = False,
+                        rope_base: float = 10000.0, out: torch.Tensor | None = None,
+                        workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """ZeroS-SM, causal: the zero-sum reweighting of standard softmax attention. q, k, v [B, H, N, d]
+    bfloat16 (d 64 or 128), g1, gh (and g0) [B, H, N] bfloat16. ``workspace`` (rotated q and k, with
+    RoPE only) as for zeros_fwd_causal."""
+    _need(q.dim() == 4 and k.shape == q.shape and v.shape == q.shape, "q, k, v must be [B, H, N, d]")
+    _need(q.dtype in _DT, f"q dtype {q.dtype} is not float32 or bfloat16")
+    _need(g1.shape == q.shape[:3] and gh.shape == q.shape[:3] and (g0 is None or g0.shape == q.shape[:3]),
+          "g1, gh, g0 must be [B, H, N]")
+    for t in (q, k, v, g1, gh) + (() if g0 is None else (g0,)):
+        _need(t.is_contiguous() and t.device == q.device and t.dtype == q.dtype, "tensors must be contiguous, "
+              "on one device and of one dtype")
+    s_ = _stream(q.device, stream)
+    o = _alloc_on(s_, lambda: torch.empty_like(v)) if out is None else out
+    _need(o.shape == v.shape and o.dtype == v.dtype and o.is_contiguous() and o.device == q.device,
+          "out must match v")
+    lib = load_library()
+    B, H, N, d = q.shape
+    shp = zeros_shape(B, H, N, d, d, _DT[q.dtype], int(rope), float(rope_base))
+    workspace = _workspace(lib.zeros_sm_fwd_causal_workspace_bytes(ctypes.byref(shp)), workspace, q.device, s_)
+    _check(lib.zeros_sm_fwd_causal(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(g1), _ptr(gh), _ptr(g0),
+                                   _ptr(o), _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                                   s_.cuda_stream))
+    return o
+
+
+def zeros_sm_fwd_causal_workspace_bytes(B: int, H: int, N: int, d: int, dtype, rope: bool = False) -> int:
+    """Scratch bytes zeros_sm_fwd_causal needs for these sizes (0 without RoPE)."""
+    lib = load_library()
+    shp = zeros_shape(B, H, N, d, d, _DT[dtype], int(rope), 10000.0)
+    return int(lib.zeros_sm_fwd_causal_workspace_bytes(ctypes.byref(shp)))
 
 
 def zeros_decode_step(q, k, v, u, mu, tau, g1, gh, state: DecodeState, *, g0: torch.Tensor | None = None,

@@ -23,6 +23,7 @@ SOURCES = [
     "zeros_api.cpp",
     "causal_valu.hip",
     "causal_mfma.hip",
+    "sm_causal.hip",
     "logits.hip",
     "encoder_valu.hip",
     "encoder_mfma.hip",

@@ -78,6 +78,11 @@ size_t encoder_work_bytes(const Problem &p);
 hipError_t launch_encoder_mfma(const Problem &p, float *work, hipStream_t stream);
 hipError_t launch_decode(const Problem &p, hipStream_t stream);
 
+// ZeroS-SM, the zero-sum reweighting of standard causal softmax attention (sm_causal.hip):
+// bfloat16, d = 64 or 128; with RoPE, `work` holds the rotated q and k (sm_work_bytes).
+size_t sm_work_bytes(const Problem &p);
+hipError_t launch_sm_causal(const Problem &p, void *work, hipStream_t stream);
+
 // Backward of the causal forward (backward.hip). Gradient outputs in the storage dtype except
 // dmu [H, d_u] and dtau [H] (float32, summed over the batch).
 struct BwdGrads {

@@ -313,6 +313,74 @@ size_t zeros_fwd_encoder_workspace_bytes(const zeros_shape *shape) {
     return zeros::encoder_work_bytes(p);
 }
 
+namespace {
+// Validation of a ZeroS-SM call (no u, mu, tau; bfloat16 with d 64 or 128 only).
+zeros_status sm_check(const zeros_shape *s, const void *q, const void *k, const void *v, const void *g1,
+                      const void *gh, const void *g0, const void *o, const char *fn) {
+    const std::string f(fn);
+    if (!s) return fail(ZEROS_ERR_NULL, f + ": shape is NULL");
+    if ((!q || !k || !v || !g1 || !gh || !o) && s->N != 0) return fail(ZEROS_ERR_NULL, f + ": a tensor pointer is NULL");
+    if (s->dtype != ZEROS_F32 && s->dtype != ZEROS_BF16)
+        return fail(ZEROS_ERR_DTYPE, f + ": dtype must be ZEROS_F32 or ZEROS_BF16");
+    if (s->B < 1 || s->H < 1 || s->N < 0 || s->d < 1 || s->d_u < 1)
+        return fail(ZEROS_ERR_SHAPE, f + ": need B, H, d, d_u >= 1 and N >= 0");
+    if (s->dtype != ZEROS_BF16) return fail(ZEROS_ERR_UNSUPPORTED, f + ": only bfloat16 inputs are supported");
+    if (s->d != 64 && s->d != 128) return fail(ZEROS_ERR_UNSUPPORTED, f + ": d must be 64 or 128");
+    if (s->rope != 0 && s->rope != 1) return fail(ZEROS_ERR_UNSUPPORTED, f + ": rope must be 0 or 1");
+    if (s->rope == 1 && !(std::isfinite(s->rope_base) && s->rope_base > 1.0f))
+        return fail(ZEROS_ERR_SHAPE, f + ": rope_base must be finite and > 1");
+    const long double elems = static_cast<long double>(s->B) * s->H * s->N * s->d;
+    if (elems >= 2147483648.0L) return fail(ZEROS_ERR_SHAPE, f + ": tensor has 2^31 elements or more");
+    auto al16 = [](const void *x) { return (reinterpret_cast<uintptr_t>(x) & 15u) == 0; };
+    if (s->N != 0 && !(al16(q) && al16(k) && al16(v) && al16(o)))
+        return fail(ZEROS_ERR_SHAPE, f + ": q, k, v and o must be 16-byte aligned");
+    const size_t tens = static_cast<size_t>(s->B) * s->H * s->N * s->d * 2;
+    const size_t gate = static_cast<size_t>(s->B) * s->H * s->N * 2;
+    const Range out{o, tens};
+    const Range ins[] = {{q, tens}, {k, tens}, {v, tens}, {g1, gate}, {gh, gate}, {g0, g0 ? gate : 0}};
+    for (const Range &r : ins)
+        if (overlap(out, r)) return fail(ZEROS_ERR_ALIAS, f + ": o overlaps an input");
+    return ZEROS_OK;
+}
+
+zeros::Problem sm_problem(const zeros_shape *s, const void *q, const void *k, const void *v, const void *g1,
+                          const void *gh, const void *g0, void *o) {
+    zeros::Problem p{};
+    p.q = q; p.k = k; p.v = v; p.g1 = g1; p.gh = gh; p.g0 = s->N != 0 ? g0 : nullptr; p.o = o;
+    p.B = s->B; p.H = s->H; p.N = s->N; p.d = s->d; p.du = s->d_u;
+    p.dtype = s->dtype; p.rope = s->rope; p.rope_base = s->rope_base;
+    return p;
+}
+}  // namespace
+
+zeros_status zeros_sm_fwd_causal(const zeros_shape *shape, const void *q, const void *k, const void *v,
+                                 const void *g1, const void *gh, const void *g0, void *o, void *workspace,
+                                 size_t workspace_bytes, void *stream) {
+    const char *fn = "zeros_sm_fwd_causal";
+    zeros_status st = sm_check(shape, q, k, v, g1, gh, g0, o, fn);
+    if (st != ZEROS_OK) return st;
+    if (shape->N == 0) return ok();
+    const zeros::Problem p = sm_problem(shape, q, k, v, g1, gh, g0, o);
+    st = check_workspace(workspace, workspace_bytes, zeros::sm_work_bytes(p), fn);
+    if (st != ZEROS_OK) return st;
+    if (workspace) {
+        // the rotated q and k are written there: it must not overlap the inputs or o
+        const size_t tens = static_cast<size_t>(p.B) * p.H * p.N * p.d * 2;
+        const Range wr{workspace, zeros::sm_work_bytes(p)};
+        const Range io[] = {{q, tens}, {k, tens}, {v, tens}, {o, tens}};
+        for (const Range &r : io)
+            if (overlap(wr, r)) return fail(ZEROS_ERR_ALIAS, std::string(fn) + ": workspace overlaps a tensor argument");
+    }
+    return hip_result(zeros::launch_sm_causal(p, workspace, static_cast<hipStream_t>(stream)), fn);
+}
+
+size_t zeros_sm_fwd_causal_workspace_bytes(const zeros_shape *shape) {
+    if (!shape || shape->B < 1 || shape->H < 1 || shape->N < 0 || shape->d < 1) return 0;
+    zeros::Problem p{};
+    p.B = shape->B; p.H = shape->H; p.N = shape->N; p.d = shape->d; p.rope = shape->rope == 1;
+    return zeros::sm_work_bytes(p);
+}
+
 zeros_status zeros_decode_step(const zeros_shape *shape, const void *q, const void *k, const void *v,
                                const void *u, const float *mu, const float *tau, const void *g1,
                                const void *gh, const void *g0, void *o, const zeros_state *state,

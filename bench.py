@@ -301,6 +301,37 @@ def secondary(dev, oracle: dict, cores: int, steps: int = 20) -> list:
     log(f"secondary chunked4: {ms:.4f} ms")
     del o, ws, chunks, sts, o_parts, ws_part, whole, chained
 
+    # ZeroS-SM (the zero-sum reweighting of standard softmax attention, quadratic) at the same shape:
+    # matrix-core bound; algorithmic flops = the three products Q K^T, P V and L V over the causal
+    # pairs, 3 x 2 d N (N + 1) / 2 per head (the running sum of v needs no product)
+    g = torch.Generator(device=dev).manual_seed(wl.seed + 200)
+    xs = {key: torch.randn(t["q"].shape, generator=g, device=dev).to(torch.bfloat16) for key in ("q", "k", "v")}
+    xs.update({key: torch.randn(t["g1"].shape, generator=g, device=dev).to(torch.bfloat16) for key in ("g1", "gh")})
+    os_ = torch.empty_like(xs["v"])
+    wss = torch.empty(Z.zeros_sm_fwd_causal_workspace_bytes(wl.B, wl.H, wl.N, wl.d, torch.bfloat16, wl.rope),
+                      dtype=torch.uint8, device=dev)
+    ms = _timed(dev, lambda st: Z.zeros_sm_fwd_causal(xs["q"], xs["k"], xs["v"], xs["g1"], xs["gh"], rope=wl.rope,
+                                                      rope_base=wl.rope_base, out=os_, workspace=wss, stream=st),
+                max(3, steps // 4))
+    flops = 3 * 2 * wl.d * wl.N * (wl.N + 1) // 2 * wl.B * wl.H
+    ent = {"workload": wl.name + "-zeros-sm", "call": "zeros_sm_fwd_causal", "ms": ms,
+           "tokens_per_s": wl.B * wl.N / (ms * 1e-3), "algorithmic_flops": flops,
+           "achieved_TFLOPs": flops / (ms * 1e-3) / 1e12, "frac_bf16_mfma": flops / (ms * 1e-3) / 1e12 / 2500.0}
+    if oracle:
+        from oracle import zeros_ref as R
+
+        rows = [1, 2, 65, 4097, 16384]
+        errs = []
+        for b, h in ((0, 0), (1, 15)):
+            f = {key: xs[key][b, h].float().cpu().numpy().astype(np.float64) for key in xs}
+            ref = R.sm_causal_forward(f["q"], f["k"], f["v"], f["g1"], f["gh"], rope=wl.rope, rope_base=wl.rope_base,
+                                      rows=rows)
+            errs.append(rel_l2(_f64(os_[b, h, [r - 1 for r in rows]]), ref))
+        ent["parity"] = {"heads": 2, "rows": rows, "rel_l2": max(errs), "bar": BAR["bf16"]}
+    out.append(ent)
+    log(f"secondary zeros-sm: {ms:.4f} ms")
+    del xs, os_, wss
+
     # the backward of the headline call (gradients of every input; upstream gradient ~ N(0, 1))
     g = torch.Generator(device=dev).manual_seed(wl.seed + 100)
     dO = torch.randn(t["v"].shape, generator=g, device=dev).to(torch.bfloat16)

@@ -1,5 +1,7 @@
 /*
- * libzeros: ZeroS (zero-sum linear attention) forward pass for AMD Instinct MI355X (gfx950).
+ * libzeros: ZeroS (zero-sum linear attention) for AMD Instinct MI355X (gfx950): the causal and
+ * encoder forward passes, the recurrent decode step, the backward of the causal forward, and the
+ * quadratic variant ZeroS-SM.
  *
  * The method (arXiv 2602.05230) is described on the Paper-Notes page "ZeroS: Zero-Sum Linear
  * Attention for Efficient Transformers" (section 关键设计) and on the ai.info summary of the same
@@ -118,8 +120,9 @@ typedef struct {
  * workspace: device scratch of at least zeros_fwd_causal_workspace_bytes(shape) bytes,
  *   256-byte aligned, owned by the caller and used only while the call's work runs on `stream`
  *   (it holds the logits s_i, per-segment u sums, per-64-token logit aggregates, the scan's
- *   segment states when a head is split into segments, and on the bfloat16 d = 64/128 path a
- *   per-64-token-chunk operand record, there in all roughly 2.6 times the bytes of q). NULL is
+ *   segment states when a head is split into segments, and on the bfloat16 d = 64/128 path the
+ *   per-64-token-chunk scalar coefficients, 2.6 KB per chunk; 68.6 MB in all at B=2 H=16
+ *   N=16384 d=128, half the bytes of q). NULL is
  *   ZEROS_ERR_NULL whenever the query returns more than 0 (it does for every N > 0); a workspace
  *   smaller than required or not 256-byte aligned is ZEROS_ERR_SHAPE.
  */

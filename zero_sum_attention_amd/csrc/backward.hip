@@ -24,8 +24,11 @@
 //   -> zscan x3 -> bwd_chain_kernel (reverse scans of the scalar chain: ds, dg1, dgh, dg0)
 //   -> bwd_useg_kernel + bwd_logit_kernel (du and per-segment dmu, dtau partials)
 //   -> bwd_finish_kernel (dq, dk through RoPE and the normalisation; dv) -> bwd_reduce_kernel.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "mfma_common.hpp"
 
 namespace zeros {
 namespace {
@@ -144,7 +147,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(Problem p, BwdWork w, con
 //   O3_a = sum_b psi3_b (Q_a . K_b) V_b;   out_a = c1_a O1_a + c2_a O2_a + c3_a O3_a
 // and, when Dv is given, the partial dot products Dv_a . O{1,2,3}_a over this workgroup's value
 // columns. theta = sgn_th * th, lambda = sgn_la * la; a NULL factor array means 1. The states are
-// S1 = sum kappa e^{lambda - R} K^T V (R: the running maximum of lambda), S2, S3, in LDS.
+// S1 = sum kappa e^{lambda - R} K^T V (R: the running maximum of lambda), S2, S3.
 struct ZArgs {
     const float *Q, *K, *V, *Dv;
     const float *th, *la, *ka, *p2, *p3, *c1, *c2, *c3;
@@ -153,160 +156,328 @@ struct ZArgs {
     int ndots;
 };
 
+// One workgroup per (sequence-head, 16 value columns), four waves, 32-token chunks, every
+// contraction on the float32 matrix cores (v_mfma_f32_16x16x4f32: A[i][k] from lane i + 16 k,
+// B[k][j] from lane j + 16 k, the accumulator lane j + 16 g holding rows 4 g + [0, 4) of column j).
+// Wave r < 3 keeps state S_{r+1} (d rows, 16 columns) in its accumulator registers: tile rt holds
+// the rows f = JT i + rt (JT = d / 16, i < 16), so lane (l16, g4) has rows JT (4 g4 + ii) + rt in
+// register ii of tile rt. Read with that feature order, the registers are the A operand of the
+// carried product S^T Q^T directly, and both its Q operands and the K^T operands of the update are
+// runs of JT consecutive features (16-byte LDS reads). Per chunk, two barriers, which wait for LDS
+// traffic only (the next chunk's loads stay in flight across them):
+//   A: waves 0-2 the carried products (the state at the chunk start), wave 3 the chunk's Q K^T
+//      tiles; every thread issues the loads of the next chunk's rows into registers;
+//   B: waves 0-2 the intra-chunk products W_r V (each forming its own weights from Q K^T), their
+//      parts O_r of the output, and the state update S_r += K^T diag(w_r) V; wave 3 the outputs of
+//      the previous chunk (c1 O1 + c2 O2 + c3 O3) and its Dv dot products; every thread stores the
+//      next chunk's rows into the other LDS buffer (wave 3 its v, Dv, scalars and the maximum of
+//      lambda, after reading that buffer's previous contents).
 template <int D>
 struct ZSmem {
-    float Q[kZC][D + 1], K[kZC][D + 1];
-    float V[kZC][kZTile], Dv[kZC][kZTile];
-    float W[3][kZC][kZC + 1];          // A_{a,b} times the three weights (b <= a)
-    float S[3][D][kZTile];
-    float th[kZC], la[kZC], ka[kZC], p2[kZC], p3[kZC], c1[kZC], c2[kZC], c3[kZC];
-    float e1[kZC];                     // kappa_b e^{lambda_b - R'} for the S1 update
-    int pos[kZC];
+    float Q[2][kZC][D + 4], K[2][kZC][D + 4];      // rows, double-buffered (16-byte aligned rows)
+    float V[2][kZC][kZTile], Dv[2][kZC][kZTile];
+    float sc[2][8][kZC];                           // theta, lambda, kappa, psi2, psi3, c1, c2, c3
+    int pos[2][kZC];                               // sequence position of each row (-1: none)
+    float cmax[2];                                 // maximum of lambda over the chunk's rows
+    float A[kZC][kZC + 1];                         // Q_a . K_b
+    float part[2][3][kZC][kZTile + 4];             // O_r of a chunk, per wave r, double-buffered
 };
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, const f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// n consecutive floats from LDS (p aligned to min(n, 4) floats)
+template <int n>
+__device__ __forceinline__ void lds_run(const float *p, float (&o)[n]) {
+    if constexpr (n >= 4) {
+#pragma unroll
+        for (int q = 0; q < n / 4; ++q) {
+            const float4 v = reinterpret_cast<const float4 *>(p)[q];
+            o[4 * q] = v.x; o[4 * q + 1] = v.y; o[4 * q + 2] = v.z; o[4 * q + 3] = v.w;
+        }
+    } else if constexpr (n == 2) {
+        const float2 v = *reinterpret_cast<const float2 *>(p);
+        o[0] = v.x; o[1] = v.y;
+    } else {
+        o[0] = p[0];
+    }
+}
 
 template <int D, bool REV>
 __global__ __launch_bounds__(kZThreads) void zscan_kernel(ZArgs z, int N, int BH) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     ZSmem<D> &sm = *reinterpret_cast<ZSmem<D> *>(smem_raw);
+    static_assert(kZThreads == 256 && kZC == 32 && kZTile == 16, "scan shape");
     constexpr int NT = D / kZTile;
-    constexpr int TPR = kZThreads / D;         // update threads per state row
-    constexpr int EPT = kZTile / TPR;          // state columns per update thread
-    const int tid = threadIdx.x;
+    constexpr int JT = D / 16;                      // 16-row tiles of a state
+    constexpr int RF4 = kZC * D / 4;                // float4 pieces of a chunk's Q (or K) rows
+    constexpr int RPT = (RF4 + kZThreads - 1) / kZThreads;
+    constexpr int VF4 = kZC * kZTile / 4;           // float4 pieces of a chunk's V (or Dv) tile
+    static_assert(VF4 == 2 * 64, "v staging: two pieces per lane of wave 3");
+    const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int bh = blockIdx.x / NT, tile = blockIdx.x % NT;
     const size_t row0 = static_cast<size_t>(bh) * N;
-    const int qa = tid >> 3, mp = (tid & 7) * 2;          // output: query a, columns mp, mp + 1
-    const int uj = tid / TPR, um = (tid % TPR) * EPT;     // update: state row, first column
-    float st[3][EPT];
-#pragma unroll
-    for (int r = 0; r < 3; ++r)
-#pragma unroll
-        for (int e = 0; e < EPT; ++e) st[r][e] = 0.f;
-    for (int i = tid; i < 3 * D * kZTile; i += kZThreads) (&sm.S[0][0][0])[i] = 0.f;
-    float R = kNegInf;
     const int nch = (N + kZC - 1) / kZC;
-    for (int c = 0; c < nch; ++c) {
-        // ---- stage the chunk
-        if (tid < kZC) {
-            const int j = c * kZC + tid;
+
+    // the next chunk's rows, held in registers from phase A to phase B. The loads read clamped,
+    // in-bounds rows unconditionally and nothing is computed from them before the store, so no
+    // wait for them falls inside phase A; rows past the end are zeroed (and their factors set) when
+    // stored.
+    float4 rq[RPT], rk[RPT], rv[2], rdv[2] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
+    float rs[8];
+    auto src_row = [&](const int j) __attribute__((always_inline)) {
+        const int jc = min(j, N - 1);
+        return row0 + (REV ? N - 1 - jc : jc);
+    };
+    auto load = [&](const int c) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int idx = min(tid + i * kZThreads, RF4 - 1);
+            const int r = idx / (D / 4), f4 = idx % (D / 4);
+            const size_t g = src_row(c * kZC + r) * D + 4 * f4;
+            rq[i] = *reinterpret_cast<const float4 *>(z.Q + g);
+            rk[i] = *reinterpret_cast<const float4 *>(z.K + g);
+        }
+        if (w == 3) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int vi = lane + 64 * h;
+                const int r = vi / (kZTile / 4), f4 = vi % (kZTile / 4);
+                const size_t g = src_row(c * kZC + r) * D + tile * kZTile + 4 * f4;
+                rv[h] = *reinterpret_cast<const float4 *>(z.V + g);
+                if (z.Dv) rdv[h] = *reinterpret_cast<const float4 *>(z.Dv + g);
+            }
+            const size_t ix = src_row(c * kZC + (lane & 31));
+            rs[0] = z.th[ix];
+            rs[1] = z.la[ix];
+            rs[2] = z.ka ? z.ka[ix] : 1.f;
+            rs[3] = z.p2 ? z.p2[ix] : 1.f;
+            rs[4] = z.p3 ? z.p3[ix] : 1.f;
+            rs[5] = z.c1 ? z.c1[ix] : 1.f;
+            rs[6] = z.c2 ? z.c2[ix] : 1.f;
+            rs[7] = z.c3 ? z.c3[ix] : 1.f;
+        }
+    };
+    auto store = [&](const int c, const int b) __attribute__((always_inline)) {
+        const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int idx = tid + i * kZThreads;
+            if (idx < RF4) {
+                const int r = idx / (D / 4), f4 = idx % (D / 4);
+                float4 xq = rq[i], xk = rk[i];
+                if (c * kZC + r >= N) xq = xk = zero4;
+                *reinterpret_cast<float4 *>(&sm.Q[b][r][4 * f4]) = xq;
+                *reinterpret_cast<float4 *>(&sm.K[b][r][4 * f4]) = xk;
+            }
+        }
+        if (w == 3) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int vi = lane + 64 * h;
+                const int r = vi / (kZTile / 4), f4 = vi % (kZTile / 4);
+                float4 xv = rv[h], xd = rdv[h];
+                if (c * kZC + r >= N) xv = xd = zero4;
+                *reinterpret_cast<float4 *>(&sm.V[b][r][4 * f4]) = xv;
+                *reinterpret_cast<float4 *>(&sm.Dv[b][r][4 * f4]) = xd;
+            }
+            const int t = lane & 31, j = c * kZC + t;
             const bool valid = j < N;
-            const int pos = valid ? (REV ? N - 1 - j : j) : -1;
-            sm.pos[tid] = pos;
-            const size_t ix = row0 + (valid ? pos : 0);
-            sm.th[tid] = valid ? z.sgn_th * z.th[ix] : 0.f;
-            sm.la[tid] = valid ? z.sgn_la * z.la[ix] : kNegInf;
-            sm.ka[tid] = valid ? (z.ka ? z.ka[ix] : 1.f) : 0.f;
-            sm.p2[tid] = valid ? (z.p2 ? z.p2[ix] : 1.f) : 0.f;
-            sm.p3[tid] = valid ? (z.p3 ? z.p3[ix] : 1.f) : 0.f;
-            sm.c1[tid] = z.c1 && valid ? z.c1[ix] : 1.f;
-            sm.c2[tid] = z.c2 && valid ? z.c2[ix] : 1.f;
-            sm.c3[tid] = z.c3 && valid ? z.c3[ix] : 1.f;
-        }
-        for (int i = tid; i < kZC * D; i += kZThreads) {
-            const int r = i / D, f = i % D;
-            const int j = c * kZC + r;
-            const bool valid = j < N;
-            const size_t g = (row0 + (valid ? (REV ? N - 1 - j : j) : 0)) * D + f;
-            sm.Q[r][f] = valid ? z.Q[g] : 0.f;
-            sm.K[r][f] = valid ? z.K[g] : 0.f;
-        }
-        for (int i = tid; i < kZC * kZTile; i += kZThreads) {
-            const int r = i / kZTile, f = i % kZTile;
-            const int j = c * kZC + r;
-            const bool valid = j < N;
-            const size_t g = (row0 + (valid ? (REV ? N - 1 - j : j) : 0)) * D + tile * kZTile + f;
-            sm.V[r][f] = valid ? z.V[g] : 0.f;
-            sm.Dv[r][f] = (valid && z.Dv) ? z.Dv[g] : 0.f;
-        }
-        __syncthreads();
-        float Rc = R;
-#pragma unroll 8
-        for (int b = 0; b < kZC; ++b) Rc = fmaxf(Rc, sm.la[b]);
-        // ---- intra-chunk products A_{a,b} = Q_a . K_b (b <= a) times the three weights
-        {
-            const int a = tid >> 3, b0 = (tid & 7) * 4;
-            float acc[4] = {0.f, 0.f, 0.f, 0.f};
-            for (int f = 0; f < D; ++f) {
-                const float qf = sm.Q[a][f];
+            const float la = valid ? z.sgn_la * rs[1] : kNegInf;
+            if (lane < kZC) {
+                sm.sc[b][0][t] = valid ? z.sgn_th * rs[0] : 0.f;
+                sm.sc[b][1][t] = la;
+                sm.sc[b][2][t] = valid ? rs[2] : 0.f;
+                sm.sc[b][3][t] = valid ? rs[3] : 0.f;
+                sm.sc[b][4][t] = valid ? rs[4] : 0.f;
+                sm.sc[b][5][t] = valid ? rs[5] : 1.f;
+                sm.sc[b][6][t] = valid ? rs[6] : 1.f;
+                sm.sc[b][7][t] = valid ? rs[7] : 1.f;
+                sm.pos[b][t] = valid ? (REV ? N - 1 - j : j) : -1;
+            }
+            float mx = la;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] += qf * sm.K[b0 + i][f];
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int b = b0 + i;
-                const bool in = b <= a && sm.la[b] != kNegInf;
-                const float ex = in ? expf(sm.th[a] + sm.la[b]) : 0.f;
-                sm.W[0][a][b] = in ? acc[i] * sm.ka[b] * ex : 0.f;
-                sm.W[1][a][b] = in ? acc[i] * sm.p2[b] : 0.f;
-                sm.W[2][a][b] = in ? acc[i] * sm.p3[b] : 0.f;
-            }
-            if (tid < kZC) sm.e1[tid] = sm.la[tid] == kNegInf ? 0.f : sm.ka[tid] * expf(sm.la[tid] - Rc);
+            for (int off = 1; off < 32; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+            if (lane == 0) sm.cmax[b] = mx;
         }
-        __syncthreads();
-        // ---- outputs of query a, columns mp, mp + 1: carried states plus the intra-chunk part
-        {
-            float x[3][2] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
-            for (int f = 0; f < D; ++f) {
-                const float qf = sm.Q[qa][f];
+    };
+    // outputs and Dv dot products of a finished chunk (its rows in buffer b, its parts in part[b]),
+    // by wave 3: lane = (row a, 8 columns)
+    auto emit = [&](const int b) __attribute__((always_inline)) {
+        const int a = lane >> 1, m = (lane & 1) * 8;
+        const int ps = sm.pos[b][a];
+        float x[3][8];
 #pragma unroll
-                for (int r = 0; r < 3; ++r) {
-                    x[r][0] += qf * sm.S[r][f][mp];
-                    x[r][1] += qf * sm.S[r][f][mp + 1];
-                }
-            }
-            const float sc1 = (R == kNegInf) ? 0.f : expf(sm.th[qa] + R);
-            x[0][0] *= sc1;
-            x[0][1] *= sc1;
-            for (int b = 0; b <= qa; ++b) {
-                const float v0 = sm.V[b][mp], v1 = sm.V[b][mp + 1];
+        for (int r = 0; r < 3; ++r) lds_run<8>(&sm.part[b][r][a][m], x[r]);
+        const float c1 = sm.sc[b][5][a], c2 = sm.sc[b][6][a], c3 = sm.sc[b][7][a];
+        float o[8];
 #pragma unroll
-                for (int r = 0; r < 3; ++r) {
-                    x[r][0] += sm.W[r][qa][b] * v0;
-                    x[r][1] += sm.W[r][qa][b] * v1;
-                }
-            }
-            const int pos = sm.pos[qa];
-            if (pos >= 0) {
-                const float o0 = sm.c1[qa] * x[0][0] + sm.c2[qa] * x[1][0] + sm.c3[qa] * x[2][0];
-                const float o1 = sm.c1[qa] * x[0][1] + sm.c2[qa] * x[1][1] + sm.c3[qa] * x[2][1];
-                *reinterpret_cast<float2 *>(z.out + (row0 + pos) * D + tile * kZTile + mp) = make_float2(o0, o1);
-            }
-            if (z.ndots > 0) {
-                const float d0 = sm.Dv[qa][mp], d1 = sm.Dv[qa][mp + 1];
-                for (int r = 0; r < z.ndots; ++r) {
-                    float pd = d0 * x[r][0] + d1 * x[r][1];
+        for (int e = 0; e < 8; ++e) o[e] = (c1 * x[0][e] + c2 * x[1][e]) + c3 * x[2][e];
+        if (ps >= 0) {
+            float4 *dst = reinterpret_cast<float4 *>(z.out + (row0 + ps) * D + tile * kZTile + m);
+            dst[0] = make_float4(o[0], o[1], o[2], o[3]);
+            dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+        }
+        if (z.ndots > 0) {
+            float dv[8];
+            lds_run<8>(&sm.Dv[b][a][m], dv);
+#pragma unroll
+            for (int r = 0; r < 3; ++r) {
+                if (r < z.ndots) {
+                    float pd = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) pd += dv[e] * x[r][e];
                     pd += __shfl_xor(pd, 1, 64);
-                    pd += __shfl_xor(pd, 2, 64);
-                    pd += __shfl_xor(pd, 4, 64);
-                    if ((tid & 7) == 0 && pos >= 0)
-                        z.dots[(static_cast<size_t>(tile * z.ndots + r) * BH + bh) * N + pos] = pd;
+                    if ((lane & 1) == 0 && ps >= 0)
+                        z.dots[(static_cast<size_t>(tile * z.ndots + r) * BH + bh) * N + ps] = pd;
                 }
             }
         }
-        // ---- state update: S1 <- e^{R - Rc} S1 + K^T diag(e1) V, S2 += K^T diag(psi2) V, S3 likewise
-        {
-            const float dec = (R == kNegInf) ? 0.f : expf(R - Rc);
+    };
+
+    // state S_{w+1} of waves 0-2: rows JT (4 g4 + ii) + rt in register ii of tile rt, column l16
+    f32x4 S[JT];
 #pragma unroll
-            for (int e = 0; e < EPT; ++e) st[0][e] *= dec;
-            for (int b = 0; b < kZC; ++b) {
-                const float kj = sm.K[b][uj];
-                const float w1 = sm.e1[b] * kj, w2 = sm.p2[b] * kj, w3 = sm.p3[b] * kj;
-#pragma unroll
-                for (int e = 0; e < EPT; ++e) {
-                    const float vv = sm.V[b][um + e];
-                    st[0][e] += w1 * vv;
-                    st[1][e] += w2 * vv;
-                    st[2][e] += w3 * vv;
-                }
-            }
-        }
-        __syncthreads();          // every read of this chunk's S, Q, K, V, W is done
-#pragma unroll
-        for (int r = 0; r < 3; ++r)
-#pragma unroll
-            for (int e = 0; e < EPT; ++e) sm.S[r][uj][um + e] = st[r][e];
-        R = Rc;
-        // (the next chunk's staging writes Q, K, V, scalars only; S is read after its barrier)
+    for (int rt = 0; rt < JT; ++rt) S[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float R = kNegInf;
+    if (nch > 0) {
+        load(0);
+        store(0, 0);
     }
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) {
+        const int b = c & 1;
+        if (c + 1 < nch) load(c + 1);
+        const float Rc = fmaxf(R, sm.cmax[b]);     // running maximum of lambda after this chunk
+
+        // ---- phase A
+        f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        if (w < 3) {
+            // carried product of query tile tt: x[col][tok] = sum_f S[f][col] Q[tok][f], feature
+            // f = JT (4 g4 + ii) + rt for (rt, ii) (two accumulators per tile, even and odd ii)
+            f32x4 ac2[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) {
+                    float qv[JT];
+                    lds_run<JT>(&sm.Q[b][16 * tt + l16][JT * (4 * g4 + ii)], qv);
+                    f32x4 &x = (ii & 1) ? ac2[tt] : acc[tt];
+#pragma unroll
+                    for (int rt = 0; rt < JT; ++rt) x = mfma4(S[rt][ii], qv[rt], x);
+                }
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[tt][i] += ac2[tt][i];
+            if (w == 0) {        // S1 is relative to R: scale by e^{theta_a + R}
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) {
+                    const float s1 = (R == kNegInf) ? 0.f : expf(sm.sc[b][0][16 * tt + l16] + R);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[tt][i] *= s1;
+                }
+            }
+        } else {
+            // Q K^T tiles (key tile kt, query tile qt) = (0, 0), (0, 1), (1, 1): A[key][f] = K,
+            // B[f][tok] = Q; the accumulator lane holds keys 16 kt + 4 g4 + i of query 16 qt + l16
+            f32x4 at[3] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int s = 0; s < D / 16; ++s) {
+                const float4 k0 = *reinterpret_cast<const float4 *>(&sm.K[b][l16][16 * s + 4 * g4]);
+                const float4 k1 = *reinterpret_cast<const float4 *>(&sm.K[b][16 + l16][16 * s + 4 * g4]);
+                const float4 q0 = *reinterpret_cast<const float4 *>(&sm.Q[b][l16][16 * s + 4 * g4]);
+                const float4 q1 = *reinterpret_cast<const float4 *>(&sm.Q[b][16 + l16][16 * s + 4 * g4]);
+                at[0] = mfma4(k0.x, q0.x, at[0]); at[1] = mfma4(k0.x, q1.x, at[1]); at[2] = mfma4(k1.x, q1.x, at[2]);
+                at[0] = mfma4(k0.y, q0.y, at[0]); at[1] = mfma4(k0.y, q1.y, at[1]); at[2] = mfma4(k1.y, q1.y, at[2]);
+                at[0] = mfma4(k0.z, q0.z, at[0]); at[1] = mfma4(k0.z, q1.z, at[1]); at[2] = mfma4(k1.z, q1.z, at[2]);
+                at[0] = mfma4(k0.w, q0.w, at[0]); at[1] = mfma4(k0.w, q1.w, at[1]); at[2] = mfma4(k1.w, q1.w, at[2]);
+            }
+#pragma unroll
+            for (int ti = 0; ti < 3; ++ti) {
+                const int kt = ti == 2 ? 1 : 0, qt = ti == 0 ? 0 : 1;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sm.A[16 * qt + l16][16 * kt + 4 * g4 + i] = at[ti][i];
+            }
+        }
+        lds_barrier();
+
+        // ---- phase B
+        // wave r < 3, with r known at compile time inside (straight-line code, no per-element
+        // branches on r)
+        auto phase_b = [&](auto rc) __attribute__((always_inline)) {
+            constexpr int r = decltype(rc)::value;
+            // this lane's keys 4 kk + g4: lambda, the weight factor, v
+            float lk[kZC / 4], fk[kZC / 4], vk[kZC / 4];
+#pragma unroll
+            for (int kk = 0; kk < kZC / 4; ++kk) {
+                const int key = 4 * kk + g4;
+                lk[kk] = sm.sc[b][1][key];
+                fk[kk] = sm.sc[b][r == 0 ? 2 : 2 + r][key];
+                vk[kk] = sm.V[b][key][l16];
+            }
+            // intra-chunk part: x[col][tok] += sum_{key <= tok} V[key][col] W_r[tok][key], with
+            // W_0 = A kappa e^{theta + lambda}, W_1 = A psi2, W_2 = A psi3 (query tile 0 meets only
+            // key tile 0). Every A entry read is written and finite, so it is read unconditionally
+            // and masked by its factor (a read under the mask would wait for LDS once per element).
+            float av[2][kZC / 4];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int kk = 0; kk < 4 * (tt + 1); ++kk) av[tt][kk] = sm.A[16 * tt + l16][4 * kk + g4];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                const int a = 16 * tt + l16;
+                const float tha = sm.sc[b][0][a];
+#pragma unroll
+                for (int kk = 0; kk < 4 * (tt + 1); ++kk) {
+                    const int key = 4 * kk + g4;
+                    const bool in = key <= a && lk[kk] != kNegInf;
+                    const float f = r == 0 ? fk[kk] * __expf(tha + lk[kk]) : fk[kk];
+                    acc[tt] = mfma4(vk[kk], av[tt][kk] * (in ? f : 0.f), acc[tt]);
+                }
+            }
+            // lane: columns 4 g4 + i of token 16 tt + l16
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+                *reinterpret_cast<float4 *>(&sm.part[b][r][16 * tt + l16][4 * g4]) =
+                    make_float4(acc[tt][0], acc[tt][1], acc[tt][2], acc[tt][3]);
+            // state update S_r <- dec S_r + K^T diag(w_r) V: A[f][key] = K[key][f], B[key][col] =
+            // w_r[key] V[key][col], w_0 = kappa e^{lambda - Rc}; S1 decays only when the maximum moves
+            if (r == 0 && Rc != R) {
+                const float dec = (R == kNegInf) ? 0.f : __expf(R - Rc);
+#pragma unroll
+                for (int rt = 0; rt < JT; ++rt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) S[rt][i] *= dec;
+            }
+#pragma unroll
+            for (int kk = 0; kk < kZC / 4; ++kk) {
+                const int key = 4 * kk + g4;
+                const float wk = r != 0 ? fk[kk] : (lk[kk] == kNegInf ? 0.f : fk[kk] * __expf(lk[kk] - Rc));
+                const float bv = wk * vk[kk];
+                float kr[JT];
+                lds_run<JT>(&sm.K[b][key][JT * l16], kr);
+#pragma unroll
+                for (int rt = 0; rt < JT; ++rt) S[rt] = mfma4(kr[rt], bv, S[rt]);
+            }
+        };
+        if (w == 0) {
+            phase_b(std::integral_constant<int, 0>{});
+        } else if (w == 1) {
+            phase_b(std::integral_constant<int, 1>{});
+        } else if (w == 2) {
+            phase_b(std::integral_constant<int, 2>{});
+        } else if (c > 0) {
+            emit(b ^ 1);        // before this wave's store overwrites that buffer
+        }
+        if (c + 1 < nch) store(c + 1, b ^ 1);
+        R = Rc;
+        lds_barrier();
+    }
+    if (nch > 0 && w == 3) emit((nch - 1) & 1);
 }
 
 // ---- scalar chain, one wave per head, reverse over 64-token blocks -----------------------------

@@ -21,7 +21,8 @@
 // Launch sequence (all on the caller's stream; scratch in the caller's workspace):
 //   logits (logits.hip) -> bwd_scalar_kernel (m, E, P, gates, alpha, beta, gamma per token)
 //   -> bwd_prep_kernel (q^, k^ rotated and normalised, v and dO in float32)
-//   -> zscan x3 -> bwd_chain_kernel (reverse scans of the scalar chain: ds, dg1, dgh, dg0)
+//   -> zscan x3 -> bwd_chain_local_kernel + bwd_chain_apply_kernel (reverse scans of the scalar
+//   chain: ds, dg1, dgh, dg0)
 //   -> bwd_useg_kernel + bwd_logit_kernel (du and per-segment dmu, dtau partials)
 //   -> bwd_finish_kernel (dq, dk through RoPE and the normalisation; dv) -> bwd_reduce_kernel.
 #include <type_traits>
@@ -48,47 +49,60 @@ __device__ __forceinline__ void lse_merge(float &m, float &e, float m2, float e2
     }
 }
 
-// ---- per-token scalars of the forward, one wave per head --------------------------------------
+// ---- per-token scalars of the forward, one wave per (head, 64-token block) ----------------------
 // m_t (running maximum of the logits), E_t = sum_{i<=t} e^{s_i - m_t}, P_t = sum s_i, the gates,
 // alpha_t = sigmah_t / E_t, beta_t = (sigma1_t - sigmah_t) / t,
 // gamma_t = -(sigma1_t - sigmah_t) P_t / t^2 - sigmah_t / t (+ sigma0_t / t).
+// The carry of the earlier blocks is the merge of their aggregates (max, sum e^{s - max}, sum s),
+// written by the logits kernel, 64 blocks per step.
 template <typename T>
 __global__ __launch_bounds__(64) void bwd_scalar_kernel(Problem p, BwdWork w) {
-    const int bh = blockIdx.x, lane = threadIdx.x, N = p.N;
+    const int N = p.N, nblk = (N + 63) / 64;
+    const int bh = blockIdx.x / nblk, blk = blockIdx.x % nblk, lane = threadIdx.x;
     const size_t row0 = static_cast<size_t>(bh) * N;
     const T *g1 = static_cast<const T *>(p.g1) + row0, *gh = static_cast<const T *>(p.gh) + row0;
     const T *g0 = p.g0 != nullptr ? static_cast<const T *>(p.g0) + row0 : nullptr;
     float mc = kNegInf, ec = 0.f, pc = 0.f;
-    for (int c0 = 0; c0 < N; c0 += 64) {
-        const int t = c0 + lane;
-        const bool valid = t < N;
-        const float sv = valid ? w.s[row0 + t] : 0.f;
-        float m = valid ? sv : kNegInf, e = valid ? 1.f : 0.f;
+    for (int j0 = 0; j0 < blk; j0 += 64) {
+        const int j = j0 + lane;
+        float m = kNegInf, e = 0.f, ps = 0.f;
+        if (j < blk) {
+            const float4 ag = w.agg[static_cast<size_t>(bh) * nblk + j];
+            m = ag.x; e = ag.y; ps = ag.z;
+        }
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float m2 = __shfl_up(m, off, 64), e2 = __shfl_up(e, off, 64);
-            if (lane >= off) lse_merge(m, e, m2, e2);
+        for (int off = 32; off > 0; off >>= 1) {
+            const float m2 = __shfl_xor(m, off, 64), e2 = __shfl_xor(e, off, 64);
+            lse_merge(m, e, m2, e2);
+            ps += __shfl_xor(ps, off, 64);
         }
-        lse_merge(m, e, mc, ec);                       // the carry of the earlier chunks
-        const float P = pc + wave_scan_add(sv);
-        if (valid) {
-            const float s1 = sigmoidf(to_f32(g1[t])), sh = sigmoidf(to_f32(gh[t]));
-            const float s0 = g0 != nullptr ? sigmoidf(to_f32(g0[t])) : 0.f;
-            const float tt = static_cast<float>(t + 1);
-            w.m[row0 + t] = m;
-            w.E[row0 + t] = e;
-            w.P[row0 + t] = P;
-            w.al[row0 + t] = sh / e;
-            w.be[row0 + t] = (s1 - sh) / tt;
-            w.ga[row0 + t] = -(s1 - sh) * P / (tt * tt) + (s0 - sh) / tt;
-            w.s1[row0 + t] = s1;
-            w.sh[row0 + t] = sh;
-            w.s0[row0 + t] = s0;
-        }
-        const int last = min(63, N - 1 - c0);
-        mc = lane_f(m, last);
-        ec = lane_f(e, last);
-        pc = lane_f(P, last);
+        lse_merge(mc, ec, m, e);
+        pc += ps;
+    }
+    const int t = blk * 64 + lane;
+    const bool valid = t < N;
+    const float sv = valid ? w.s[row0 + t] : 0.f;
+    float m = valid ? sv : kNegInf, e = valid ? 1.f : 0.f;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float m2 = __shfl_up(m, off, 64), e2 = __shfl_up(e, off, 64);
+        if (lane >= off) lse_merge(m, e, m2, e2);
+    }
+    lse_merge(m, e, mc, ec);                       // the carry of the earlier blocks
+    const float P = pc + wave_scan_add(sv);
+    if (valid) {
+        const float s1 = sigmoidf(to_f32(g1[t])), sh = sigmoidf(to_f32(gh[t]));
+        const float s0 = g0 != nullptr ? sigmoidf(to_f32(g0[t])) : 0.f;
+        const float tt = static_cast<float>(t + 1);
+        w.m[row0 + t] = m;
+        w.E[row0 + t] = e;
+        w.P[row0 + t] = P;
+        w.al[row0 + t] = sh / e;
+        w.be[row0 + t] = (s1 - sh) / tt;
+        w.ga[row0 + t] = -(s1 - sh) * P / (tt * tt) + (s0 - sh) / tt;
+        w.s1[row0 + t] = s1;
+        w.sh[row0 + t] = sh;
+        w.s0[row0 + t] = s0;
     }
 }
 
@@ -480,73 +494,103 @@ __global__ __launch_bounds__(kZThreads) void zscan_kernel(ZArgs z, int N, int BH
     if (nch > 0 && w == 3) emit((nch - 1) & 1);
 }
 
-// ---- scalar chain, one wave per head, reverse over 64-token blocks -----------------------------
+// ---- scalar chain, reverse: one wave per (head, 64-token block) -------------------------------
 // From a_t, b_t, c_t (sums over the column tiles of the causal scan's dots) and the direct logit
-// gradient (the anti-causal scan's dots): dsigma, the reverse sums through E and P, ds, dg.
+// gradient (the anti-causal scan's dots): dsigma, dg, and the reverse recurrences
+//   T_t = dE_t + e^{m_t - m_{t+1}} T_{t+1},   Q_t = sum_{t' >= t} dP_t'
+// that carry dE and dP back to the logits: ds_t = dd_t + e^{s_t - m_t} T_t + Q_t. The recurrences
+// are affine, so each block forms its part from zero (the local T and Q, and the factor on the T
+// that enters at its end), and a second pass composes the later blocks' aggregates into each
+// block's carry. Between the passes the local parts stay in the be and ga buffers (no longer
+// read by then) and dd + Q in ds; the block aggregates (T, factor, Q) replace the logit aggregates.
 template <typename T>
-__global__ __launch_bounds__(64) void bwd_chain_kernel(Problem p, BwdWork w, T *dg1, T *dgh, T *dg0, int NT) {
-    const int bh = blockIdx.x, lane = threadIdx.x, N = p.N, BH = p.B * p.H;
+__global__ __launch_bounds__(64) void bwd_chain_local_kernel(Problem p, BwdWork w, T *dg1, T *dgh, T *dg0, int NT) {
+    const int N = p.N, BH = p.B * p.H, nblk = (N + 63) / 64;
+    const int bh = blockIdx.x / nblk, blk = blockIdx.x % nblk, lane = threadIdx.x;
     const size_t row0 = static_cast<size_t>(bh) * N;
-    float Tc = 0.f, Qc = 0.f, mnext = 0.f;
-    bool have_next = false;
-    const int nblk = (N + 63) / 64;
-    for (int blk = nblk - 1; blk >= 0; --blk) {
-        const int t = blk * 64 + lane;
-        const bool valid = t < N;
-        const size_t ix = row0 + (valid ? t : 0);
-        float a = 0.f, b = 0.f, c = 0.f, dd = 0.f;
-        if (valid) {
-            for (int tl = 0; tl < NT; ++tl) {
-                const float *da = w.dotsA + static_cast<size_t>(tl * 3) * BH * N;
-                a += da[ix];
-                b += da[static_cast<size_t>(BH) * N + ix];
-                c += da[static_cast<size_t>(2) * BH * N + ix];
-                const float *db = w.dotsB + static_cast<size_t>(tl * 2) * BH * N;
-                dd += db[ix] + db[static_cast<size_t>(BH) * N + ix];
-            }
+    const int t = blk * 64 + lane;
+    const bool valid = t < N;
+    const size_t ix = row0 + (valid ? t : 0);
+    float a = 0.f, b = 0.f, c = 0.f, dd = 0.f;
+    if (valid) {
+        for (int tl = 0; tl < NT; ++tl) {
+            const float *da = w.dotsA + static_cast<size_t>(tl * 3) * BH * N;
+            a += da[ix];
+            b += da[static_cast<size_t>(BH) * N + ix];
+            c += da[static_cast<size_t>(2) * BH * N + ix];
+            const float *db = w.dotsB + static_cast<size_t>(tl * 2) * BH * N;
+            dd += db[ix] + db[static_cast<size_t>(BH) * N + ix];
         }
-        const float m = valid ? w.m[ix] : 0.f, E = valid ? w.E[ix] : 1.f, P = valid ? w.P[ix] : 0.f;
-        const float al = valid ? w.al[ix] : 0.f, s1 = valid ? w.s1[ix] : 0.f, sh = valid ? w.sh[ix] : 0.f;
-        const float sv = valid ? w.s[ix] : 0.f;
-        const float tt = static_cast<float>(t + 1);
-        const float it = 1.f / tt, it2 = it * it;
-        const float dsh = a / E - b * it + c * (P * it2 - it);
-        const float ds1 = b * it - c * P * it2;
-        const float ds0 = c * it;
-        const float dE = -a * al / E;
-        const float dP = -c * (s1 - sh) * it2;
-        // T_t = dE_t + e^{m_t - m_{t+1}} T_{t+1} and Q_t = sum_{t' >= t} dP_t', suffix scans
-        const float mn = __shfl_down(m, 1, 64);
-        float F;
-        if (!valid) F = 0.f;
-        else if (lane < 63 && t + 1 < N) F = expf(m - mn);
-        else F = have_next ? expf(m - mnext) : 0.f;
-        float X = valid ? dE : 0.f, Qs = valid ? dP : 0.f;
+    }
+    const float m = valid ? w.m[ix] : 0.f, E = valid ? w.E[ix] : 1.f, P = valid ? w.P[ix] : 0.f;
+    const float al = valid ? w.al[ix] : 0.f, s1 = valid ? w.s1[ix] : 0.f, sh = valid ? w.sh[ix] : 0.f;
+    const float tt = static_cast<float>(t + 1);
+    const float it = 1.f / tt, it2 = it * it;
+    const float dsh = a / E - b * it + c * (P * it2 - it);
+    const float ds1 = b * it - c * P * it2;
+    const float ds0 = c * it;
+    const float dE = -a * al / E;
+    const float dP = -c * (s1 - sh) * it2;
+    // factor of T_{t+1} in T_t (zero at the last token)
+    float F = 0.f;
+    if (valid && t + 1 < N) F = expf(m - w.m[ix + 1]);
+    float X = valid ? dE : 0.f, Qs = valid ? dP : 0.f;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float X2 = __shfl_down(X, off, 64), F2 = __shfl_down(F, off, 64), Q2 = __shfl_down(Qs, off, 64);
+        if (lane + off < 64) {
+            X += F * X2;
+            F *= F2;
+            Qs += Q2;
+        }
+    }
+    // now T_t = X + F T_{start of the next block}, Q_t = Qs + Q_{start of the next block}
+    if (valid) {
+        w.be[ix] = X;
+        w.ga[ix] = F;
+        w.ds[ix] = dd + Qs;
+        dg1[ix] = from_f32<T>(ds1 * s1 * (1.f - s1));
+        dgh[ix] = from_f32<T>(dsh * sh * (1.f - sh));
+        if (dg0 != nullptr) {
+            const float s0 = w.s0[ix];
+            dg0[ix] = from_f32<T>(ds0 * s0 * (1.f - s0));
+        }
+    }
+    if (lane == 0) w.agg[static_cast<size_t>(bh) * nblk + blk] = make_float4(X, F, Qs, 0.f);
+}
+
+template <typename T>
+__global__ __launch_bounds__(64) void bwd_chain_apply_kernel(Problem p, BwdWork w) {
+    const int N = p.N, nblk = (N + 63) / 64;
+    const int bh = blockIdx.x / nblk, blk = blockIdx.x % nblk, lane = threadIdx.x;
+    const size_t row0 = static_cast<size_t>(bh) * N;
+    // T and Q at the start of block blk + 1: the blocks after it composed in order, 64 per step
+    float Tn = 0.f, Qn = 0.f, Fr = 1.f;         // Tn + Fr T_{start of the first block not yet read}
+    for (int j0 = blk + 1; j0 < nblk; j0 += 64) {
+        const int j = j0 + lane;
+        float X = 0.f, F = 1.f, Q = 0.f;
+        if (j < nblk) {
+            const float4 ag = w.agg[static_cast<size_t>(bh) * nblk + j];
+            X = ag.x; F = ag.y; Q = ag.z;
+        }
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
-            const float X2 = __shfl_down(X, off, 64), F2 = __shfl_down(F, off, 64), Q2 = __shfl_down(Qs, off, 64);
+            const float X2 = __shfl_down(X, off, 64), F2 = __shfl_down(F, off, 64), Q2 = __shfl_down(Q, off, 64);
             if (lane + off < 64) {
                 X += F * X2;
                 F *= F2;
-                Qs += Q2;
+                Q += Q2;
             }
         }
-        const float Tt = X + F * Tc;
-        const float Qt = Qs + Qc;
-        if (valid) {
-            const float ds = dd + expf(sv - m) * Tt + Qt;
-            w.ds[ix] = ds;
-            dg1[ix] = from_f32<T>(ds1 * s1 * (1.f - s1));
-            dgh[ix] = from_f32<T>(dsh * sh * (1.f - sh));
-            if (dg0 != nullptr) {
-                const float s0 = w.s0[ix];
-                dg0[ix] = from_f32<T>(ds0 * s0 * (1.f - s0));
-            }
-        }
-        Tc = lane_f(Tt, 0);
-        Qc = lane_f(Qt, 0);
-        mnext = lane_f(m, 0);
-        have_next = true;
+        Tn += Fr * lane_f(X, 0);
+        Fr *= lane_f(F, 0);
+        Qn += lane_f(Q, 0);
+    }
+    const int t = blk * 64 + lane;
+    if (t < N) {
+        const size_t ix = row0 + t;
+        const float Tt = w.be[ix] + w.ga[ix] * Tn;
+        w.ds[ix] = w.ds[ix] + Qn + expf(w.s[ix] - w.m[ix]) * Tt;
     }
 }
 
@@ -695,9 +739,9 @@ hipError_t launch_bwd(const Problem &p, const BwdGrads &g, const BwdWork &w, hip
     if (N > 0) {
         err = launch_logits(p, w.useg, w.s, w.agg, nullptr, stream);
         if (err != hipSuccess) return err;
-        hipLaunchKernelGGL((bwd_scalar_kernel<T>), dim3(BH), dim3(64), 0, stream, p, w);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
         const int nblk = (N + 63) / 64;
+        hipLaunchKernelGGL((bwd_scalar_kernel<T>), dim3(BH * nblk), dim3(64), 0, stream, p, w);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
         hipLaunchKernelGGL((bwd_prep_kernel<D, T, ROPE>), dim3(BH * nblk), dim3(256), 0, stream, p, w,
                            static_cast<const T *>(g.dO));
         if ((err = hipGetLastError()) != hipSuccess) return err;
@@ -714,8 +758,10 @@ hipError_t launch_bwd(const Problem &p, const BwdGrads &g, const BwdWork &w, hip
         ZArgs zc{w.vf, w.dOf, w.qh, nullptr, w.s, w.m, w.al, w.be, w.ga, nullptr, w.s, nullptr,
                  1.f, -1.f, w.dkh, nullptr, 0};
         if ((err = launch_zscan<D, true>(zc, N, BH, stream)) != hipSuccess) return err;
-        hipLaunchKernelGGL((bwd_chain_kernel<T>), dim3(BH), dim3(64), 0, stream, p, w, static_cast<T *>(g.dg1),
-                           static_cast<T *>(g.dgh), static_cast<T *>(g.dg0), D / kZTile);
+        hipLaunchKernelGGL((bwd_chain_local_kernel<T>), dim3(BH * nblk), dim3(64), 0, stream, p, w,
+                           static_cast<T *>(g.dg1), static_cast<T *>(g.dgh), static_cast<T *>(g.dg0), D / kZTile);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        hipLaunchKernelGGL((bwd_chain_apply_kernel<T>), dim3(BH * nblk), dim3(64), 0, stream, p, w);
         if ((err = hipGetLastError()) != hipSuccess) return err;
         hipLaunchKernelGGL((bwd_useg_kernel<D, T>), dim3(BH * nls), dim3(D), 0, stream, p, w, nls);
         if ((err = hipGetLastError()) != hipSuccess) return err;

@@ -177,15 +177,15 @@ struct ZArgs {
 // the rows f = JT i + rt (JT = d / 16, i < 16), so lane (l16, g4) has rows JT (4 g4 + ii) + rt in
 // register ii of tile rt. Read with that feature order, the registers are the A operand of the
 // carried product S^T Q^T directly, and both its Q operands and the K^T operands of the update are
-// runs of JT consecutive features (16-byte LDS reads). Per chunk, two barriers, which wait for LDS
-// traffic only (the next chunk's loads stay in flight across them):
-//   A: waves 0-2 the carried products (the state at the chunk start), wave 3 the chunk's Q K^T
-//      tiles; every thread issues the loads of the next chunk's rows into registers;
+// runs of JT consecutive features (16-byte LDS reads). Per chunk c, two barriers, which wait for LDS
+// traffic only (loads stay in flight across them), and wave 3 one chunk ahead:
+//   A: waves 0-2 the carried products (the state at the chunk start); wave 3 the outputs of chunk
+//      c - 1 (c1 O1 + c2 O2 + c3 O3) and its Dv dot products; every thread stores chunk c + 1's rows
+//      (loaded during the previous phase B) into the other LDS buffer (wave 3 its v, Dv, scalars and
+//      the maximum of lambda, after reading that buffer's previous contents);
 //   B: waves 0-2 the intra-chunk products W_r V (each forming its own weights from Q K^T), their
-//      parts O_r of the output, and the state update S_r += K^T diag(w_r) V; wave 3 the outputs of
-//      the previous chunk (c1 O1 + c2 O2 + c3 O3) and its Dv dot products; every thread stores the
-//      next chunk's rows into the other LDS buffer (wave 3 its v, Dv, scalars and the maximum of
-//      lambda, after reading that buffer's previous contents).
+//      parts O_r of the output, and the state update S_r += K^T diag(w_r) V; wave 3 the Q K^T tiles
+//      of chunk c + 1; every thread issues the loads of chunk c + 2's rows into registers.
 template <int D>
 struct ZSmem {
     float Q[2][kZC][D + 4], K[2][kZC][D + 4];      // rows, double-buffered (16-byte aligned rows)
@@ -193,7 +193,7 @@ struct ZSmem {
     float sc[2][8][kZC];                           // theta, lambda, kappa, psi2, psi3, c1, c2, c3
     int pos[2][kZC];                               // sequence position of each row (-1: none)
     float cmax[2];                                 // maximum of lambda over the chunk's rows
-    float A[kZC][kZC + 1];                         // Q_a . K_b
+    float A[2][kZC][kZC + 1];                      // Q_a . K_b, double-buffered
     float part[2][3][kZC][kZTile + 4];             // O_r of a chunk, per wave r, double-buffered
 };
 
@@ -356,14 +356,39 @@ __global__ __launch_bounds__(kZThreads) void zscan_kernel(ZArgs z, int N, int BH
 #pragma unroll
     for (int rt = 0; rt < JT; ++rt) S[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float R = kNegInf;
+    // Q K^T tiles of the chunk in buffer bb, by wave 3
+    auto qk_tiles = [&](const int bb) __attribute__((always_inline)) {
+        // Q K^T tiles (key tile kt, query tile qt) = (0, 0), (0, 1), (1, 1): A[key][f] = K,
+        // B[f][tok] = Q; the accumulator lane holds keys 16 kt + 4 g4 + i of query 16 qt + l16
+        f32x4 at[3] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+            const float4 k0 = *reinterpret_cast<const float4 *>(&sm.K[bb][l16][16 * s + 4 * g4]);
+            const float4 k1 = *reinterpret_cast<const float4 *>(&sm.K[bb][16 + l16][16 * s + 4 * g4]);
+            const float4 q0 = *reinterpret_cast<const float4 *>(&sm.Q[bb][l16][16 * s + 4 * g4]);
+            const float4 q1 = *reinterpret_cast<const float4 *>(&sm.Q[bb][16 + l16][16 * s + 4 * g4]);
+            at[0] = mfma4(k0.x, q0.x, at[0]); at[1] = mfma4(k0.x, q1.x, at[1]); at[2] = mfma4(k1.x, q1.x, at[2]);
+            at[0] = mfma4(k0.y, q0.y, at[0]); at[1] = mfma4(k0.y, q1.y, at[1]); at[2] = mfma4(k1.y, q1.y, at[2]);
+            at[0] = mfma4(k0.z, q0.z, at[0]); at[1] = mfma4(k0.z, q1.z, at[1]); at[2] = mfma4(k1.z, q1.z, at[2]);
+            at[0] = mfma4(k0.w, q0.w, at[0]); at[1] = mfma4(k0.w, q1.w, at[1]); at[2] = mfma4(k1.w, q1.w, at[2]);
+        }
+#pragma unroll
+        for (int ti = 0; ti < 3; ++ti) {
+            const int kt = ti == 2 ? 1 : 0, qt = ti == 0 ? 0 : 1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sm.A[bb][16 * qt + l16][16 * kt + 4 * g4 + i] = at[ti][i];
+        }
+    };
     if (nch > 0) {
         load(0);
         store(0, 0);
     }
     __syncthreads();
+    if (nch > 0 && w == 3) qk_tiles(0);
+    if (nch > 1) load(1);
+    lds_barrier();
     for (int c = 0; c < nch; ++c) {
         const int b = c & 1;
-        if (c + 1 < nch) load(c + 1);
         const float Rc = fmaxf(R, sm.cmax[b]);     // running maximum of lambda after this chunk
 
         // ---- phase A
@@ -394,28 +419,10 @@ __global__ __launch_bounds__(kZThreads) void zscan_kernel(ZArgs z, int N, int BH
                     for (int i = 0; i < 4; ++i) acc[tt][i] *= s1;
                 }
             }
-        } else {
-            // Q K^T tiles (key tile kt, query tile qt) = (0, 0), (0, 1), (1, 1): A[key][f] = K,
-            // B[f][tok] = Q; the accumulator lane holds keys 16 kt + 4 g4 + i of query 16 qt + l16
-            f32x4 at[3] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-            for (int s = 0; s < D / 16; ++s) {
-                const float4 k0 = *reinterpret_cast<const float4 *>(&sm.K[b][l16][16 * s + 4 * g4]);
-                const float4 k1 = *reinterpret_cast<const float4 *>(&sm.K[b][16 + l16][16 * s + 4 * g4]);
-                const float4 q0 = *reinterpret_cast<const float4 *>(&sm.Q[b][l16][16 * s + 4 * g4]);
-                const float4 q1 = *reinterpret_cast<const float4 *>(&sm.Q[b][16 + l16][16 * s + 4 * g4]);
-                at[0] = mfma4(k0.x, q0.x, at[0]); at[1] = mfma4(k0.x, q1.x, at[1]); at[2] = mfma4(k1.x, q1.x, at[2]);
-                at[0] = mfma4(k0.y, q0.y, at[0]); at[1] = mfma4(k0.y, q1.y, at[1]); at[2] = mfma4(k1.y, q1.y, at[2]);
-                at[0] = mfma4(k0.z, q0.z, at[0]); at[1] = mfma4(k0.z, q1.z, at[1]); at[2] = mfma4(k1.z, q1.z, at[2]);
-                at[0] = mfma4(k0.w, q0.w, at[0]); at[1] = mfma4(k0.w, q1.w, at[1]); at[2] = mfma4(k1.w, q1.w, at[2]);
-            }
-#pragma unroll
-            for (int ti = 0; ti < 3; ++ti) {
-                const int kt = ti == 2 ? 1 : 0, qt = ti == 0 ? 0 : 1;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sm.A[16 * qt + l16][16 * kt + 4 * g4 + i] = at[ti][i];
-            }
+        } else if (c > 0) {
+            emit(b ^ 1);        // before this wave's store overwrites that buffer
         }
+        if (c + 1 < nch) store(c + 1, b ^ 1);
         lds_barrier();
 
         // ---- phase B
@@ -440,7 +447,7 @@ __global__ __launch_bounds__(kZThreads) void zscan_kernel(ZArgs z, int N, int BH
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                for (int kk = 0; kk < 4 * (tt + 1); ++kk) av[tt][kk] = sm.A[16 * tt + l16][4 * kk + g4];
+                for (int kk = 0; kk < 4 * (tt + 1); ++kk) av[tt][kk] = sm.A[b][16 * tt + l16][4 * kk + g4];
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
                 const int a = 16 * tt + l16;
@@ -484,10 +491,10 @@ __global__ __launch_bounds__(kZThreads) void zscan_kernel(ZArgs z, int N, int BH
             phase_b(std::integral_constant<int, 1>{});
         } else if (w == 2) {
             phase_b(std::integral_constant<int, 2>{});
-        } else if (c > 0) {
-            emit(b ^ 1);        // before this wave's store overwrites that buffer
+        } else if (c + 1 < nch) {
+            qk_tiles(b ^ 1);
         }
-        if (c + 1 < nch) store(c + 1, b ^ 1);
+        if (c + 2 < nch) load(c + 2);
         R = Rc;
         lds_barrier();
     }

@@ -395,18 +395,27 @@ __global__ __launch_bounds__(kZThreads) void zscan_kernel(ZArgs z, int N, int BH
         f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
         if (w < 3) {
             // carried product of query tile tt: x[col][tok] = sum_f S[f][col] Q[tok][f], feature
-            // f = JT (4 g4 + ii) + rt for (rt, ii) (two accumulators per tile, even and odd ii)
+            // f = JT (4 g4 + ii) + rt for (rt, ii); four accumulators (tile, parity of ii) taken in
+            // turn, so consecutive matrix ops are independent
             f32x4 ac2[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii)
+            for (int ip = 0; ip < 2; ++ip) {
+                float qv[2][2][JT];
 #pragma unroll
-                for (int tt = 0; tt < 2; ++tt) {
-                    float qv[JT];
-                    lds_run<JT>(&sm.Q[b][16 * tt + l16][JT * (4 * g4 + ii)], qv);
-                    f32x4 &x = (ii & 1) ? ac2[tt] : acc[tt];
+                for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                    for (int rt = 0; rt < JT; ++rt) x = mfma4(S[rt][ii], qv[rt], x);
-                }
+                    for (int iq = 0; iq < 2; ++iq)
+                        lds_run<JT>(&sm.Q[b][16 * tt + l16][JT * (4 * g4 + 2 * ip + iq)], qv[tt][iq]);
+#pragma unroll
+                for (int rt = 0; rt < JT; ++rt)
+#pragma unroll
+                    for (int iq = 0; iq < 2; ++iq)
+#pragma unroll
+                        for (int tt = 0; tt < 2; ++tt) {
+                            f32x4 &x = iq ? ac2[tt] : acc[tt];
+                            x = mfma4(S[rt][2 * ip + iq], qv[tt][iq][rt], x);
+                        }
+            }
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -448,6 +457,7 @@ __global__ __launch_bounds__(kZThreads) void zscan_kernel(ZArgs z, int N, int BH
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
                 for (int kk = 0; kk < 4 * (tt + 1); ++kk) av[tt][kk] = sm.A[b][16 * tt + l16][4 * kk + g4];
+            float wv[2][kZC / 4];
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
                 const int a = 16 * tt + l16;
@@ -457,9 +467,19 @@ __global__ __launch_bounds__(kZThreads) void zscan_kernel(ZArgs z, int N, int BH
                     const int key = 4 * kk + g4;
                     const bool in = key <= a && lk[kk] != kNegInf;
                     const float f = r == 0 ? fk[kk] * __expf(tha + lk[kk]) : fk[kk];
-                    acc[tt] = mfma4(vk[kk], av[tt][kk] * (in ? f : 0.f), acc[tt]);
+                    wv[tt][kk] = av[tt][kk] * (in ? f : 0.f);
                 }
             }
+            // three accumulators in turn: tile 0, tile 1 over key tile 0, tile 1 over key tile 1
+            f32x4 ac3 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                acc[0] = mfma4(vk[kk], wv[0][kk], acc[0]);
+                acc[1] = mfma4(vk[kk], wv[1][kk], acc[1]);
+                ac3 = mfma4(vk[kk + 4], wv[1][kk + 4], ac3);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[1][i] += ac3[i];
             // lane: columns 4 g4 + i of token 16 tt + l16
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)

@@ -60,10 +60,22 @@ __device__ __forceinline__ void rope_cos_sin(double rev_per_pos, int pos, float 
     sincosf(ang, &s, &c);
 }
 
-// Sum over groups of G consecutive lanes (G a power of two <= 64); every lane gets the sum.
+// DPP control codes: quad_perm [1,0,3,2] (lane ^ 1), quad_perm [2,3,0,1] (lane ^ 2), row_half_mirror
+// (lane i of 8 from lane 7 - i), row_mirror (lane i of 16 from lane 15 - i).
+constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kRowHalfMirror = 0x141, kRowMirror = 0x140;
+
+// Sum over groups of G consecutive lanes (G a power of two <= 64); every lane gets the sum. Within a
+// row of 16 lanes the partner values come by DPP (no LDS round trip): after the two quad swaps every
+// lane holds its quad's sum, and the (half-)row mirror pairs it with the other quad (or half-row),
+// so each step adds the same two partial sums as a butterfly would.
 template <int G> __device__ __forceinline__ float group_sum(float x) {
-#pragma unroll
-    for (int off = 1; off < G; off <<= 1) x += __shfl_xor(x, off, 64);
+    static_assert(G >= 1 && G <= 64 && (G & (G - 1)) == 0, "group size");
+    if constexpr (G >= 2) x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kQuadXor1, 0xf, 0xf, false));
+    if constexpr (G >= 4) x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kQuadXor2, 0xf, 0xf, false));
+    if constexpr (G >= 8) x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kRowHalfMirror, 0xf, 0xf, false));
+    if constexpr (G >= 16) x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kRowMirror, 0xf, 0xf, false));
+    if constexpr (G >= 32) x += __shfl_xor(x, 16, 64);
+    if constexpr (G >= 64) x += __shfl_xor(x, 32, 64);
     return x;
 }
 

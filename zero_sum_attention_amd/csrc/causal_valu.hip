@@ -243,7 +243,7 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p, ValuWo
             sm.s[tid] = valid ? ns : 0.f;
         }
         if (t0 + kC < t_end) prefetch(t0 + kC);
-        __syncthreads();
+        lds_barrier();
 
         // ---- scans of (max, sum e^{s-max}, sum s) over the chunk, joined with the carry
         // (one wave, lane r = token t0 + r + 1). Sums of s and the running maximum are DPP prefix
@@ -297,11 +297,11 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p, ValuWo
                 sm.carry[3] = exp_diff(m_c, M);
             }
         }
-        __syncthreads();
+        lds_barrier();
         const float m_new = sm.carry[0];
         if (tid < kC) sm.estate[tid] = (tid < nval) ? expf(sm.s[tid] - m_new) : 0.f;
         if (pass1) {
-            __syncthreads();      // key weights visible to the fold; pass 1 forms no outputs
+            lds_barrier();      // key weights visible to the fold; pass 1 forms no outputs
         } else {
 
         // ---- intra-chunk weights W_{t,i} (i <= t): A^T = K Q^T on the float32 matrix cores, the 16x16
@@ -334,7 +334,7 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p, ValuWo
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- outputs on the float32 matrix cores: wave 0, 1, 2 forms q^ F, q^ G, q^ H (scaled per token
         // by a_in, beta, gamma), wave 3 the intra-chunk W V, each for both 16-token tiles; the
@@ -365,7 +365,7 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p, ValuWo
                 for (int i = 0; i < 4; ++i) sm.part[wv][tok][4 * g4 + i] = acc[i];
             }
         }
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int rs = 0; rs < RS; ++rs) {
             const int t = tid / 8 + RSTEP * rs, m0 = (tid % 8) * kCPT;
@@ -421,7 +421,7 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p, ValuWo
         m_c = m_new;
         E_c = sm.carry[1];
         P_c = sm.carry[2];
-        __syncthreads();
+        lds_barrier();
     }
 
     if (pass1) {

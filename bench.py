@@ -340,10 +340,32 @@ def secondary(dev, oracle: dict, cores: int, steps: int = 20) -> list:
     ms = _timed(dev, lambda st: Z.zeros_bwd_causal(t["q"], t["k"], t["v"], t["u"], t["mu"], t["tau"], t["g1"],
                                                    t["gh"], dO, rope=wl.rope, rope_base=wl.rope_base,
                                                    workspace=wsb, stream=st), max(3, steps // 4))
-    out.append({"workload": wl.name + "-backward", "call": "zeros_bwd_causal", "ms": ms,
-                "tokens_per_s": wl.B * wl.N / (ms * 1e-3)})
-    log(f"secondary backward: {ms:.4f} ms")
+    # algorithmic flops of the recurrence form: three scans (dq^, dv, dk^), each with the carried
+    # products and the state updates of three d x d states, 12 d^2 per token-head; the scans run on
+    # the float32 matrix cores
+    flops = 3 * 12 * wl.d * wl.d * wl.N * wl.B * wl.H
+    ent = {"workload": wl.name + "-backward", "call": "zeros_bwd_causal", "ms": ms,
+           "tokens_per_s": wl.B * wl.N / (ms * 1e-3), "algorithmic_flops": flops,
+           "achieved_TFLOPs": flops / (ms * 1e-3) / 1e12, "frac_f32_mfma": flops / (ms * 1e-3) / 1e12 / 157.3}
     del t, dO, wsb
+    if oracle:
+        # parity at a shorter sequence of the same kind (the oracle's backward is quadratic in N)
+        from oracle import zeros_ref as R
+
+        pw = wl.with_(name="bwd-parity-B1H2N2048d128-rope", B=1, H=2, N=2048, seed=wl.seed + 300)
+        x = make_inputs(pw, grad_out=True)
+        tp = _dev_inputs(x, pw.dtype, dev)
+        gp = Z.zeros_bwd_causal(tp["q"], tp["k"], tp["v"], tp["u"], tp["mu"], tp["tau"], tp["g1"], tp["gh"], tp["dO"],
+                                rope=pw.rope, rope_base=pw.rope_base)
+        torch.cuda.synchronize()
+        ref = R.causal_backward(*(x[key] for key in ("q", "k", "v", "u", "mu", "tau", "g1", "gh")), dO=x["dO"],
+                                rope=pw.rope, rope_base=pw.rope_base)
+        errs = {key: rel_l2(_f64(gp[key]), ref[key]) for key in ref}
+        ent["parity"] = {"workload": pw.name, "rel_l2": errs,
+                         "bar": {key: (1e-4 if key in ("mu", "tau") else 5e-3) for key in errs}}
+        del x, tp, gp, ref
+    out.append(ent)
+    log(f"secondary backward: {ms:.4f} ms")
     torch.cuda.empty_cache()
     return out
 
@@ -576,7 +598,12 @@ def main():
         if "parity" in out:
             par[wl.name] = {"rel_l2": out["parity"]["rel_l2"], "bar": out["parity"]["bar"]}
         if par:
-            out["parity_all"] = {"configs": par, "all_within_bar": all(v["rel_l2"] <= v["bar"] for v in par.values())}
+            def within(v):   # a scalar error and bar, or one per gradient
+                if isinstance(v["rel_l2"], dict):
+                    return all(v["rel_l2"][key] <= v["bar"][key] for key in v["rel_l2"])
+                return v["rel_l2"] <= v["bar"]
+
+            out["parity_all"] = {"configs": par, "all_within_bar": all(within(v) for v in par.values())}
     out["notes"] = {"pages_quote_no_hardware_timings": True, "input_gen_s": round(t_gen, 2),
                     "hbm_peak_note": "peak is the published 8 TB/s; a 1 GiB device copy reaches 5.0 TB/s on the same MI355X"}
     print(json.dumps(out), flush=True)

@@ -443,6 +443,40 @@ def copy_probe(mib: int) -> None:
     print(json.dumps({"copy_probe_bytes": n * 4}), flush=True)
 
 
+def probe(name: str, steps: int) -> None:
+    """Only run one of the other calls at the headline shape, `steps` times (for profiles):
+    "backward" (zeros_bwd_causal) or "zeros-sm" (zeros_sm_fwd_causal)."""
+    import torch
+
+    import zero_sum_attention_amd as Z
+
+    wl = WORKLOAD
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(wl.seed + 400)
+    shp, shg = (wl.B, wl.H, wl.N, wl.d), (wl.B, wl.H, wl.N)
+    t = {key: torch.randn(shp, generator=g, device=dev).to(torch.bfloat16) for key in ("q", "k", "v", "u", "dO")}
+    t.update({key: torch.randn(shg, generator=g, device=dev).to(torch.bfloat16) for key in ("g1", "gh")})
+    t["mu"] = 0.1 * torch.randn((wl.H, wl.d_u), generator=g, device=dev)
+    t["tau"] = torch.zeros(wl.H, device=dev)
+    if name == "backward":
+        ws = torch.empty(Z.zeros_bwd_causal_workspace_bytes(wl.B, wl.H, wl.N, wl.d, wl.d_u, torch.bfloat16),
+                         dtype=torch.uint8, device=dev)
+        fn = lambda: Z.zeros_bwd_causal(t["q"], t["k"], t["v"], t["u"], t["mu"], t["tau"], t["g1"], t["gh"], t["dO"],
+                                        rope=wl.rope, rope_base=wl.rope_base, workspace=ws)
+    elif name == "zeros-sm":
+        ws = torch.empty(Z.zeros_sm_fwd_causal_workspace_bytes(wl.B, wl.H, wl.N, wl.d, torch.bfloat16, wl.rope),
+                         dtype=torch.uint8, device=dev)
+        o = torch.empty_like(t["v"])
+        fn = lambda: Z.zeros_sm_fwd_causal(t["q"], t["k"], t["v"], t["g1"], t["gh"], rope=wl.rope,
+                                           rope_base=wl.rope_base, out=o, workspace=ws)
+    else:
+        raise SystemExit(f"unknown probe {name!r}")
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    print(json.dumps({"probe": name, "workload": wl.name, "calls": steps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -455,7 +489,12 @@ def main():
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="only run a plain device copy of this many MiB (calibrates the HBM "
                          "traffic counters) and exit")
+    ap.add_argument("--probe", choices=("backward", "zeros-sm"), default=None,
+                    help="only run that call at the headline shape --steps times (for profiles) and exit")
     args = ap.parse_args()
+    if args.probe:
+        probe(args.probe, args.steps)
+        return
     if args.copy_probe_mb:
         copy_probe(args.copy_probe_mb)
         return

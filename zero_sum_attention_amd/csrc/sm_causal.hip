@@ -45,7 +45,7 @@ struct SmArgs {
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void sm_causal_kernel(SmArgs a) {
+__global__ __launch_bounds__(256, 2) void sm_causal_kernel(SmArgs a) {
     constexpr int KS = D / 32;                    // 32-feature steps of K Q^T
     constexpr int CTN = D / 16;                   // 16-column tiles of the output
     constexpr int KP = kSmK * (D / 8) / 256;      // 16-byte pieces of a K block per thread

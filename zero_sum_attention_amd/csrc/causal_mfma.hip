@@ -42,10 +42,6 @@ constexpr int kC = 64;          // tokens per chunk
 constexpr int kTile = 16;       // value columns per workgroup
 constexpr int kPad = 8;         // bf16 elements of row padding in LDS
 
-// Column-block swizzle of the k rows in LDS: 16-byte block b of row `key` is stored at
-// b ^ kswz(key), so the 8-key column gathers hit distinct LDS banks.
-__device__ __forceinline__ int kswz(int key) { return ((key >> 3) & 3) << 1; }
-
 // Order of the keys along the contraction index of every K^T V-type product in a 32-key block:
 // lane group g4 holds keys {4 g4 + [0, 4)} and {16 + 4 g4 + [0, 4)}, which is the order the
 // intra-chunk weights W come in from the A^T tiles (each tile gives a lane 4 keys). The staged v
@@ -216,6 +212,16 @@ __device__ __forceinline__ void piece_tb_pi(int piece, int &tb, int &pi) {
 __device__ __forceinline__ void st16(unsigned char *p, const bf16x8 &v) { *reinterpret_cast<bf16x8 *>(p) = v; }
 __device__ __forceinline__ bf16x8 ld16(const unsigned char *p) { return *reinterpret_cast<const bf16x8 *>(p); }
 
+// Transposing LDS read (ds_read_b64_tr_b16): every lane names 8 bytes (4 bfloat16), and within each
+// group of 16 lanes, lane i receives element i & 3 of the 8 bytes named by lanes 4 e + (i >> 2),
+// e = 0 .. 3 (measured layout). Four lanes naming 16 consecutive features of four rows thus give
+// each lane its feature of the four rows.
+__device__ __forceinline__ uint2 lds_tr16(const uint16_t *p) {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(p));
+    return __builtin_bit_cast(uint2, r);
+}
+
 // ---- segment-parallel scan ----------------------------------------------------------------
 //
 // The chunks of a head are cut into nseg segments of seg_chunks chunks. One workgroup of D/16 waves
@@ -260,11 +266,9 @@ __global__ __launch_bounds__(kScanThreads<D>) void causal_scan_kernel(Problem p,
     // raw bf16 rows of the next chunk, copied by direct global-to-LDS loads (16-byte pieces)
     __shared__ __align__(16) uint16_t s_rawk[kC * D];
     __shared__ __align__(16) uint16_t s_rawq[PASS1 ? 8 : kC * D];
-    // unit, rotated rows of this chunk; the k rows with their 16-byte blocks swizzled
+    // unit, rotated rows of this chunk
     __shared__ __align__(16) uint16_t s_kh[kC][D + kPad];
     __shared__ __align__(16) uint16_t s_qh[PASS1 ? 1 : kC][D + kPad];
-    // k^T as A operands of the update: (row tile jb, key step ks2) x 64 lanes x 16 bytes
-    __shared__ __align__(16) unsigned char s_kt[JB * 2 * 1024];
     // intra-chunk weights as B operands of V^T W^T, piece w_piece(tb, pi) x 64 lanes x 16 bytes
     __shared__ __align__(16) unsigned char s_wop[PASS1 ? 16 : 6 * 1024];
     // per column tile: its v tile transposed, vt[m][kperm(token)] (also the H update operand), and
@@ -422,6 +426,17 @@ __global__ __launch_bounds__(kScanThreads<D>) void causal_scan_kernel(Problem p,
     // the loop
     __syncthreads();
 
+    // the k^T operand of row tile jb (features 16 jb + l16) and key step ks2, in kperm order (keys
+    // 32 ks2 + 4 g4 + [0, 4), then + 16), straight from the k^ rows by two transposing reads: lane
+    // (g4, l16) names features 16 jb + 4 (l16 & 3) + [0, 4) of key 32 ks2 + 4 g4 + (l16 >> 2)
+    auto k_operand = [&](const int jb, const int ks2) __attribute__((always_inline)) {
+        const int f = 16 * jb + 4 * (l16 & 3);
+        const int r0 = 32 * ks2 + 4 * g4 + (l16 >> 2);
+        const uint2 a = lds_tr16(&s_kh[r0][f]);
+        const uint2 b = lds_tr16(&s_kh[r0 + 16][f]);
+        return as_bf16x8(a.x, a.y, b.x, b.y);
+    };
+
     // one chunk: its start phase in revc, the next chunk's written into revn
     auto chunk = [&](const int c, const float *revc, float *revn) __attribute__((always_inline)) {
         const int t0 = c * kC;
@@ -492,7 +507,7 @@ __global__ __launch_bounds__(kScanThreads<D>) void causal_scan_kernel(Problem p,
                             wq[b] = pack2(q0 * cq - q1 * sq, q0 * sq + q1 * cq);
                         }
                     }
-                    *reinterpret_cast<uint4 *>(&s_kh[r][8 * (blk ^ kswz(r))]) = make_uint4(wk[0], wk[1], wk[2], wk[3]);
+                    *reinterpret_cast<uint4 *>(&s_kh[r][8 * blk]) = make_uint4(wk[0], wk[1], wk[2], wk[3]);
                     if (!PASS1) *reinterpret_cast<uint4 *>(&s_qh[r][8 * blk]) = make_uint4(wq[0], wq[1], wq[2], wq[3]);
                 }
             if (ROPE && tid < D / 2 && c + 1 < c_end) {
@@ -502,33 +517,10 @@ __global__ __launch_bounds__(kScanThreads<D>) void causal_scan_kernel(Problem p,
         }
         lds_barrier();
 
-        // ---- (2) next chunk's record and raw rows in flight; k^T operands; A^T and W
+        // ---- (2) next chunk's record and raw rows in flight; A^T and W
         // unconditional (the last chunk fetches itself again, into buffers no longer read), so that
         // every trip issues the same memory operations and the waits for them are exact counts
         fetch_raw(min(c + 1, c_end - 1));
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-            // k^T operands of row tile jb: 8 keys per lane gathered from the swizzled rows
-            const int jb = CT * w + ct;
-            const int j = 16 * jb + l16;
-            // keys in kperm order: {4 g4 + [0, 4)} with swizzle 2 (g4 >> 1), {16 + 4 g4 + [0, 4)} with
-            // swizzle 2 ((2 + (g4 >> 1)) & 3). (All gathers before the stores: an LDS read that
-            // follows an LDS store while direct copies are in flight makes the compiler wait for the
-            // copies.)
-            const int jlo = (((j >> 3) ^ (2 * (g4 >> 1))) << 3) | (j & 7);
-            const int jhi = (((j >> 3) ^ (2 * ((2 + (g4 >> 1)) & 3))) << 3) | (j & 7);
-            bf16x8 a2[kC / 32];
-#pragma unroll
-            for (int ks2 = 0; ks2 < kC / 32; ++ks2) {
-#pragma unroll
-                for (int cc = 0; cc < 4; ++cc) {
-                    a2[ks2][cc] = static_cast<short>(s_kh[32 * ks2 + 4 * g4 + cc][jlo]);
-                    a2[ks2][cc + 4] = static_cast<short>(s_kh[32 * ks2 + 16 + 4 * g4 + cc][jhi]);
-                }
-            }
-#pragma unroll
-            for (int ks2 = 0; ks2 < kC / 32; ++ks2) st16(s_kt + (size_t(jb * 2 + ks2) * 64 + lane) * 16, a2[ks2]);
-        }
         if (!PASS1) {
             // the ten (query block tb, key block kb <= tb) tiles of A^T, spread over the waves; each
             // fills its half (8 bytes per lane) of the W piece of key pair kb / 2, and the tiles
@@ -544,7 +536,7 @@ __global__ __launch_bounds__(kScanThreads<D>) void causal_scan_kernel(Problem p,
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     const bf16x8 qop = *reinterpret_cast<const bf16x8 *>(&s_qh[tq][32 * ks + 8 * g4]);
-                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&s_kh[key][8 * ((4 * ks + g4) ^ kswz(key))]);
+                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&s_kh[key][32 * ks + 8 * g4]);
                     at = mfma(a, qop, at);
                 }
                 const float qa = cf.qa[tq], qm = cf.qm[tq], qb = cf.qb[tq], qgm = cf.qg[tq];
@@ -569,8 +561,8 @@ __global__ __launch_bounds__(kScanThreads<D>) void causal_scan_kernel(Problem p,
                 *reinterpret_cast<uint2 *>(dst + (kb & 1) * 8) = make_uint2(pack2(wt[0], wt[1]), pack2(wt[2], wt[3]));
                 if ((kb & 1) == 0 && kb + 1 > tb) *reinterpret_cast<uint2 *>(dst + 8) = make_uint2(0u, 0u);
             }
+            lds_barrier();          // W is in LDS (pass 1 writes nothing in step 2)
         }
-        lds_barrier();
 
         // ---- (3) per wave: the carried-state products, V^T W^T, outputs, and the state update
         const Coef &cf = s_cfC;
@@ -684,7 +676,7 @@ __global__ __launch_bounds__(kScanThreads<D>) void causal_scan_kernel(Problem p,
                     }
 #pragma unroll
                 for (int ks2 = 0; ks2 < kC / 32; ++ks2) {
-                    const bf16x8 Ak = ld16(s_kt + (size_t(jb * 2 + ks2) * 64 + lane) * 16);
+                    const bf16x8 Ak = k_operand(jb, ks2);
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct) {
                         X[ct][jb] = mfma(Ak, BX[ct][ks2], X[ct][jb]);

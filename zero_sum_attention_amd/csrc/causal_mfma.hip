@@ -271,11 +271,9 @@ __global__ __launch_bounds__(kScanThreads<D>) void causal_scan_kernel(Problem p,
     __shared__ __align__(16) uint16_t s_qh[PASS1 ? 1 : kC][D + kPad];
     // intra-chunk weights as B operands of V^T W^T, piece w_piece(tb, pi) x 64 lanes x 16 bytes
     __shared__ __align__(16) unsigned char s_wop[PASS1 ? 16 : 6 * 1024];
-    // per column tile: its v tile transposed, vt[m][kperm(token)] (also the H update operand), and
-    // the update operands v * w_X, v * w_Y, transposed in the same order
-    __shared__ __align__(16) uint16_t s_svt[NGT][kTile][kC + kPad];
-    __shared__ __align__(16) uint16_t s_svx[NGT][kTile][kC + kPad];
-    __shared__ __align__(16) uint16_t s_svy[NGT][kTile][kC + kPad];
+    // per wave: the v rows of its 16 value columns (64 tokens x 16 columns, token-major), copied by
+    // direct global-to-LDS loads and read transposed in step 3
+    __shared__ __align__(16) uint16_t s_rawv[NW][kC][kTile];
     // the coefficient record of the next chunk as it arrives by direct copy (s_cfS), and the current
     // chunk's (s_cfC), copied over from s_cfS at the start of the chunk: the copies always target
     // the one object, which is never read while they are in flight (a copy whose target is not a
@@ -376,17 +374,18 @@ __global__ __launch_bounds__(kScanThreads<D>) void causal_scan_kernel(Problem p,
         s_revA[tid] = static_cast<float>(r - rint(r));
     }
 
-    // v of this wave's column tiles: lane holds tokens 2 (lane & 31), +1 and columns 8 (lane >> 5) + [0, 8)
-    const int vtok = 2 * (lane & 31), vh = lane >> 5;
-    const int vpos = kperm(vtok);       // and kperm(vtok + 1) = vpos + 1
-    uint4 va[CT], vb[CT];
-    auto fetch_v = [&](const int c) __attribute__((always_inline)) {
-        const int t_ = c * kC + vtok;      // rows past N read row N-1 (in bounds)
+    // the v rows of this wave's columns 16 w + [0, 16) of chunk c into s_rawv[w] by direct copies:
+    // 128 pieces of 16 bytes, piece p = (token p >> 1, half p & 1), rows past N read row N - 1
+    // (finite; every product they enter is zero: the k^ rows and W columns of absent tokens are
+    // zero). Each wave copies exactly the tile it reads, after its own last read of the previous one.
+    auto fetch_vt = [&](const int c) __attribute__((always_inline)) {
+        static_assert(CT == 1 && kC * kTile * 2 == 2 * 64 * 16, "v tile: two 64-piece copies per wave");
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-            const size_t vcol = static_cast<size_t>(CT * w + ct) * kTile + 8 * vh;
-            va[ct] = *reinterpret_cast<const uint4 *>(vg + static_cast<size_t>(min(t_, N - 1)) * D + vcol);
-            vb[ct] = *reinterpret_cast<const uint4 *>(vg + static_cast<size_t>(min(t_ + 1, N - 1)) * D + vcol);
+        for (int i = 0; i < 2; ++i) {
+            const int pc = 64 * i + lane;
+            const int t_ = min(c * kC + (pc >> 1), N - 1);
+            const uint4 *src = reinterpret_cast<const uint4 *>(vg + static_cast<size_t>(t_) * D + w * kTile + 8 * (pc & 1));
+            __builtin_amdgcn_global_load_lds(src, reinterpret_cast<unsigned char *>(&s_rawv[w][0][0]) + i * 1024, 16, 0, 0);
         }
     };
     // the coefficient record and the raw q and k rows of chunk c into LDS: the chunk's rows are
@@ -420,7 +419,7 @@ __global__ __launch_bounds__(kScanThreads<D>) void causal_scan_kernel(Problem p,
     };
     if (c_begin < c_end) {
         fetch_raw(c_begin);
-        fetch_v(c_begin);
+        fetch_vt(c_begin);
     }
     // unconditional: the start-state loads and the first copies are complete on every path into
     // the loop
@@ -585,44 +584,31 @@ __global__ __launch_bounds__(kScanThreads<D>) void causal_scan_kernel(Problem p,
         const float hz = has_prev ? ch.y * irho1 : 0.f;   // Z += hz H
         const float hy = has_prev ? ch.z : 0.f;           // Y += hy H
 
-        // stage each tile's v (token pairs per column) and the update operands v w_X / rho1, v w_Y
-        const float4 wv = make_float4(cf.wx[vtok] * irho1, cf.wy[vtok], cf.wx[vtok + 1] * irho1, cf.wy[vtok + 1]);
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-            // rows past N hold copies of row N - 1 (finite); every product they enter is zero: the
-            // k^ rows and W columns of absent tokens are zero
-            const int gt = CT * w + ct;
-            const uint32_t a4[4] = {va[ct].x, va[ct].y, va[ct].z, va[ct].w};
-            const uint32_t b4[4] = {vb[ct].x, vb[ct].y, vb[ct].z, vb[ct].w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                // columns 8 vh + 2i (low halves) and 8 vh + 2i + 1 (high halves)
-                const uint32_t plo = (a4[i] & 0xffffu) | (b4[i] << 16);           // (a.lo, b.lo)
-                const uint32_t phi = (a4[i] >> 16) | (b4[i] & 0xffff0000u);       // (a.hi, b.hi)
-                const int mm = 8 * vh + 2 * i;
-                *reinterpret_cast<uint32_t *>(&s_svt[gt][mm][vpos]) = plo;
-                *reinterpret_cast<uint32_t *>(&s_svt[gt][mm + 1][vpos]) = phi;
-                const float x0 = lo_f(a4[i]), y0 = lo_f(b4[i]), x1 = hi_f(a4[i]), y1 = hi_f(b4[i]);
-                *reinterpret_cast<uint32_t *>(&s_svx[gt][mm][vpos]) = pack2(x0 * wv.x, y0 * wv.z);
-                *reinterpret_cast<uint32_t *>(&s_svx[gt][mm + 1][vpos]) = pack2(x1 * wv.x, y1 * wv.z);
-                *reinterpret_cast<uint32_t *>(&s_svy[gt][mm][vpos]) = pack2(x0 * wv.y, y0 * wv.w);
-                *reinterpret_cast<uint32_t *>(&s_svy[gt][mm + 1][vpos]) = pack2(x1 * wv.y, y1 * wv.w);
-            }
-        }
+        // the v operands of this wave's column tile, in kperm order (keys 32 ks2 + 4 g4 + [0, 4), then
+        // + 16), read transposed from its v rows (lane (g4, l16) names columns 4 (l16 & 3) + [0, 4) of
+        // key 32 ks2 + 4 g4 + (l16 >> 2)): v itself (the H update and V^T W^T), and the update
+        // operands v w_X / rho1, v w_Y with the keys' weights from the coefficient record
         bf16x8 BX[CT][kC / 32], BY[CT][kC / 32], BH[CT][kC / 32];
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-            const int gt = CT * w + ct;
-#pragma unroll
-            for (int ks2 = 0; ks2 < kC / 32; ++ks2) {
-                const int kk0 = 32 * ks2 + 8 * g4;
-                BX[ct][ks2] = *reinterpret_cast<const bf16x8 *>(&s_svx[gt][l16][kk0]);
-                BY[ct][ks2] = *reinterpret_cast<const bf16x8 *>(&s_svy[gt][l16][kk0]);
-                BH[ct][ks2] = *reinterpret_cast<const bf16x8 *>(&s_svt[gt][l16][kk0]);
-            }
+        for (int ks2 = 0; ks2 < kC / 32; ++ks2) {
+            const int k0 = 32 * ks2 + 4 * g4;
+            const int tok = k0 + (l16 >> 2);
+            const uint2 va = lds_tr16(&s_rawv[w][tok][4 * (l16 & 3)]);
+            const uint2 vb = lds_tr16(&s_rawv[w][tok + 16][4 * (l16 & 3)]);
+            BH[0][ks2] = as_bf16x8(va.x, va.y, vb.x, vb.y);
+            const float4 xa = *reinterpret_cast<const float4 *>(&cf.wx[k0]);
+            const float4 xb = *reinterpret_cast<const float4 *>(&cf.wx[k0 + 16]);
+            const float4 ya = *reinterpret_cast<const float4 *>(&cf.wy[k0]);
+            const float4 yb = *reinterpret_cast<const float4 *>(&cf.wy[k0 + 16]);
+            const float vv[8] = {lo_f(va.x), hi_f(va.x), lo_f(va.y), hi_f(va.y), lo_f(vb.x), hi_f(vb.x), lo_f(vb.y), hi_f(vb.y)};
+            const float wxs[8] = {xa.x * irho1, xa.y * irho1, xa.z * irho1, xa.w * irho1,
+                                  xb.x * irho1, xb.y * irho1, xb.z * irho1, xb.w * irho1};
+            const float wys[8] = {ya.x, ya.y, ya.z, ya.w, yb.x, yb.y, yb.z, yb.w};
+            BX[0][ks2] = as_bf16x8(pack2(vv[0] * wxs[0], vv[1] * wxs[1]), pack2(vv[2] * wxs[2], vv[3] * wxs[3]),
+                                   pack2(vv[4] * wxs[4], vv[5] * wxs[5]), pack2(vv[6] * wxs[6], vv[7] * wxs[7]));
+            BY[0][ks2] = as_bf16x8(pack2(vv[0] * wys[0], vv[1] * wys[1]), pack2(vv[2] * wys[2], vv[3] * wys[3]),
+                                   pack2(vv[4] * wys[4], vv[5] * wys[5]), pack2(vv[6] * wys[6], vv[7] * wys[7]));
         }
-        // next chunk's v, in flight during this chunk's matrix-core work
-        fetch_v(min(c + 1, c_end - 1));
 
         // carried-state products and the state update, interleaved by pairs of row tiles: step ks
         // reads rows 2ks, 2ks+1 of Z, Y', H (as bf16 MFMA operands, the state at t0), after which
@@ -722,9 +708,11 @@ __global__ __launch_bounds__(kScanThreads<D>) void causal_scan_kernel(Problem p,
         rho = rho1;
         alp = alp1;
         bet = bet1;
+        // next chunk's v tile, after this wave's reads of this one (their values are in use above)
+        fetch_vt(min(c + 1, c_end - 1));
         // LDS reads and writes of this chunk done everywhere. No memory fence: it would wait for the
-        // next chunk's v loads just issued; the direct copies of chunk c + 1 are read only by the
-        // wave that issued them, after the wait the compiler places for it.
+        // copies just issued; the direct copies of chunk c + 1 are read only by the wave that issued
+        // them, after the wait the compiler places for it.
         lds_barrier();
     };
     for (int c = c_begin; c < c_end; ++c) {

@@ -20,6 +20,8 @@
 // come straight from the S^T accumulators: two 16-key tiles give a lane the keys {4 g4 + [0, 4)} and
 // {16 + 4 g4 + [0, 4)} of a 32-key half, which is the order the keys of V^T are stored in.
 // With RoPE, q and k are rotated once by a pass of their own into the caller's workspace.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "mfma_common.hpp"
@@ -54,6 +56,7 @@ __global__ __launch_bounds__(256, 2) void sm_causal_kernel(SmArgs a) {
                   "d must be 64 or 128");
     __shared__ __align__(16) uint16_t s_k[kSmK][D + kSmPad];
     __shared__ __align__(16) uint16_t s_vt[D][kSmK + kSmPad];
+    __shared__ float s_vsum[D];                   // column sums of v over the full key blocks
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, g4 = lane >> 4;
     const int N = a.N;
@@ -110,24 +113,31 @@ __global__ __launch_bounds__(256, 2) void sm_causal_kernel(SmArgs a) {
         }
     };
 
-    f32x4 ap[CTN], al[CTN], a1[CTN];
+    f32x4 ap[CTN], al[CTN];
 #pragma unroll
     for (int ct = 0; ct < CTN; ++ct)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ap[ct][i] = al[ct][i] = a1[ct][i] = 0.f;
+        for (int i = 0; i < 4; ++i) ap[ct][i] = al[ct][i] = 0.f;
     // running maximum of query tq's logits, and this lane's parts of sum e^{l - m} and sum l
     float m = kNegInf, lsum = 0.f, rsum = 0.f;
     const float rsd = 1.f / sqrtf(static_cast<float>(D));
     constexpr uint32_t kOne = 0x3f80u;            // bfloat16 1.0
+    // V_t = sum_{i <= t} v_i: over the full key blocks (every key before every query of the
+    // workgroup) a column sum, the same for all queries: thread = (column, part of the keys), its
+    // sum over those blocks in vrun; over the diagonal block a product with the causal mask
+    constexpr int VPARTS = 256 / D, VKEYS = kSmK / VPARTS;
+    const int vcol = tid / VPARTS, vpart = tid % VPARTS;
+    float vrun = 0.f;
 
-    fetch(0);
-    for (int kb = 0; kb <= qb; ++kb) {
+    // one key block; DIAG: the block that holds this workgroup's queries (causal mask, and the mask
+    // product for V_t)
+    auto block = [&](const int kb, auto diag_c, f32x4 *a1) __attribute__((always_inline)) {
+        constexpr bool DIAG = decltype(diag_c)::value;
         lds_barrier();                            // the previous block's LDS reads are done
         stage();
         lds_barrier();                            // this block is in LDS
-        if (kb < qb) fetch(kb + 1);
-        const bool diag = kb == qb;               // the block that holds this workgroup's queries
-
+        if (!DIAG) fetch(kb + 1);
+        const bool diag = DIAG;
         // S^T = K Q^T: lane holds keys 16 kt + 4 g4 + i of query tq; in the diagonal block the
         // tiles whose keys all follow this wave's queries are skipped
         float lg[4][4];
@@ -162,7 +172,7 @@ __global__ __launch_bounds__(256, 2) void sm_causal_kernel(SmArgs a) {
             for (int i = 0; i < 4; ++i) ap[ct][i] *= sc;
         lsum *= sc;
         m = mn;
-        uint32_t pp[4][2], ll[4][2], mm[4][2];
+        uint32_t pp[4][2], ll[4][2], mm[4][2] = {};
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
             float p4[4], l4[4];
@@ -180,26 +190,56 @@ __global__ __launch_bounds__(256, 2) void sm_causal_kernel(SmArgs a) {
             // the running sum of the logits takes the bfloat16 values of the L^T operand, so that the
             // first-order part sum (l - lbar) v keeps its zero sum over the keys exactly
             rsum += (lo_f(ll[kt][0]) + hi_f(ll[kt][0])) + (lo_f(ll[kt][1]) + hi_f(ll[kt][1]));
-            const bool v0 = key0 + 16 * kt <= tq, v1 = key0 + 16 * kt + 1 <= tq;
-            const bool v2 = key0 + 16 * kt + 2 <= tq, v3 = key0 + 16 * kt + 3 <= tq;
-            mm[kt][0] = (v0 ? kOne : 0u) | (v1 ? kOne << 16 : 0u);
-            mm[kt][1] = (v2 ? kOne : 0u) | (v3 ? kOne << 16 : 0u);
+            if (DIAG) {
+                const bool v0 = key0 + 16 * kt <= tq, v1 = key0 + 16 * kt + 1 <= tq;
+                const bool v2 = key0 + 16 * kt + 2 <= tq, v3 = key0 + 16 * kt + 3 <= tq;
+                mm[kt][0] = (v0 ? kOne : 0u) | (v1 ? kOne << 16 : 0u);
+                mm[kt][1] = (v2 ? kOne : 0u) | (v3 ? kOne << 16 : 0u);
+            }
         }
-        // O^T += V^T P^T, V^T L^T, V^T M^T over the two 32-key halves
+        // O^T += V^T P^T, V^T L^T (and V^T M^T in the diagonal block) over the two 32-key halves
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             if (diag && 32 * h > 16 * w + 15) continue;      // every key of the half follows the wave's queries
             const bf16x8 bp = as_bf16x8(pp[2 * h][0], pp[2 * h][1], pp[2 * h + 1][0], pp[2 * h + 1][1]);
             const bf16x8 bl = as_bf16x8(ll[2 * h][0], ll[2 * h][1], ll[2 * h + 1][0], ll[2 * h + 1][1]);
-            const bf16x8 bm = as_bf16x8(mm[2 * h][0], mm[2 * h][1], mm[2 * h + 1][0], mm[2 * h + 1][1]);
 #pragma unroll
             for (int ct = 0; ct < CTN; ++ct) {
                 const bf16x8 av = *reinterpret_cast<const bf16x8 *>(&s_vt[16 * ct + l16][32 * h + 8 * g4]);
                 ap[ct] = mfma(av, bp, ap[ct]);
                 al[ct] = mfma(av, bl, al[ct]);
-                a1[ct] = mfma(av, bm, a1[ct]);
+                if (DIAG) {
+                    const bf16x8 bm = as_bf16x8(mm[2 * h][0], mm[2 * h][1], mm[2 * h + 1][0], mm[2 * h + 1][1]);
+                    a1[ct] = mfma(av, bm, a1[ct]);
+                }
             }
         }
+        if (!DIAG) {
+            // this thread's part of the column sum of the block (the keys' order does not matter)
+#pragma unroll
+            for (int j = 0; j < VKEYS / 8; ++j) {
+                const uint4 x = *reinterpret_cast<const uint4 *>(&s_vt[vcol][VKEYS * vpart + 8 * j]);
+                vrun += ((lo_f(x.x) + hi_f(x.x)) + (lo_f(x.y) + hi_f(x.y))) + ((lo_f(x.z) + hi_f(x.z)) + (lo_f(x.w) + hi_f(x.w)));
+            }
+        }
+    };
+
+    fetch(0);
+    for (int kb = 0; kb < qb; ++kb) block(kb, std::false_type{}, nullptr);
+    f32x4 a1[CTN];
+#pragma unroll
+    for (int ct = 0; ct < CTN; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a1[ct][i] = 0.f;
+    block(qb, std::true_type{}, a1);
+    // the full blocks' column sums: the parts of a column are adjacent lanes
+    vrun = group_sum<VPARTS>(vrun);
+    if (vpart == 0) s_vsum[vcol] = vrun;
+    lds_barrier();
+#pragma unroll
+    for (int ct = 0; ct < CTN; ++ct) {
+        const float4 vs = *reinterpret_cast<const float4 *>(&s_vsum[16 * ct + 4 * g4]);
+        a1[ct][0] += vs.x; a1[ct][1] += vs.y; a1[ct][2] += vs.z; a1[ct][3] += vs.w;
     }
 
     lsum += __shfl_xor(lsum, 16, 64);

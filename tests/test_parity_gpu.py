@@ -97,9 +97,31 @@ def test_config4_long_rope_sampled_heads():
     ref = R.causal_forward(**xs, rope=True)
     got = np.stack([to_f64(o[b, h]) for b, h in pairs])[None]
     err, tail = rel_l2(got, ref), tail_rel_l2(got, ref, 1024)
-    print(f"config4 sampled rel_l2={err:.3e} tail(t>1024)={tail:.3e}", flush=True)
+    p99 = row_rel_p99(got, ref, 1e-3)
+    print(f"config4 sampled rel_l2={err:.3e} tail(t>1024)={tail:.3e} row_p99={p99:.3e}", flush=True)
     assert err <= TOL["bf16"]
+    # the late rows: the tail bar of the long-sequence test, and 3x the per-row p99 measured on
+    # correct builds (1.1e-2); a chunk computed from another chunk's v shows ~1e-1
+    assert tail <= 6e-3
+    assert p99 <= 3e-2
     assert np.all(np.isfinite(to_f64(o)))
+
+
+def test_config4_repeat_bitwise():
+    """The full-size call twice on the same inputs and workspace gives the same bits: every
+    reduction order is fixed, so a difference can only come from a read racing a write (such as a
+    direct copy into LDS not yet landed), which a full-size run under load exposes."""
+    wl = CONFIGS[4]
+    t = to_device(make_inputs(wl), wl.dtype)
+    ws = torch.empty(Z.zeros_fwd_causal_workspace_bytes(wl.B, wl.H, wl.N, wl.d, wl.d_u, torch.bfloat16, True),
+                     dtype=torch.uint8, device=t["q"].device)
+    outs = []
+    for _ in range(3):
+        o = Z.zeros_fwd_causal(t["q"], t["k"], t["v"], t["u"], t["mu"], t["tau"], t["g1"], t["gh"], rope=True,
+                               workspace=ws)
+        torch.cuda.synchronize()
+        outs.append(o)
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
 
 
 # ------------------------------------------------------------------ shapes, tails, options

@@ -588,6 +588,14 @@ __global__ __launch_bounds__(kScanThreads<D>) void causal_scan_kernel(Problem p,
         // + 16), read transposed from its v rows (lane (g4, l16) names columns 4 (l16 & 3) + [0, 4) of
         // key 32 ks2 + 4 g4 + (l16 >> 2)): v itself (the H update and V^T W^T), and the update
         // operands v w_X / rho1, v w_Y with the keys' weights from the coefficient record
+        // The wave's copies of this v tile (issued at the end of the previous chunk) are older than
+        // the record and row copies of the next chunk issued in step 2 (kNewer of them). The
+        // transposing reads carry no memory operand the compiler can match against the copies, so
+        // it does not reliably wait for them: the wait is explicit.
+        {
+            constexpr int kNewer = 1 + RP / NT + (PASS1 ? 0 : RP / NT);
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kNewer) : "memory");
+        }
         bf16x8 BX[CT][kC / 32], BY[CT][kC / 32], BH[CT][kC / 32];
 #pragma unroll
         for (int ks2 = 0; ks2 < kC / 32; ++ks2) {

@@ -22,6 +22,7 @@ ARCH = "gfx950"
 SOURCES = [
     "zeros_api.cpp",
     "causal_valu.hip",
+    "causal_f32.hip",
     "causal_mfma.hip",
     "sm_causal.hip",
     "logits.hip",

@@ -465,12 +465,51 @@ __global__ __launch_bounds__(kThreads) void causal_valu_kernel(Problem p, ValuWo
 // Start states of segments 1 .. nseg-1, one element of the d x d matrices per thread, in place over
 // the segment-local sums: F <- e^{m_prev - m_end} F + L_F, G <- G + L_G, H <- H + L_H per segment,
 // from the given state (continued sequence) or zero.
+// Block (bh, 0) also writes the logit carry (m, E, P) at the start of every segment: the given
+// state's merged with the (max, sum e^{s - max}, sum s) aggregates of the 64-token blocks before
+// the segment, as an in-order lane scan over the blocks.
 template <int D>
 __global__ __launch_bounds__(256) void causal_valu_combine_kernel(Problem p, ValuWork w) {
-    const int x = blockIdx.y * 256 + threadIdx.x;
-    if (x >= D * D) return;
     const int bh = blockIdx.x;
     const bool cont = p.sin.F != nullptr;
+    if (blockIdx.y == 0 && threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        const int bps = w.seg_chunks / 2;                 // 64-token blocks per segment
+        const int nb = (w.nseg - 1) * bps;                // blocks before the last segment
+        const float4 *ag = w.agg + static_cast<size_t>(bh) * ((p.N + 63) / 64);
+        float4 *sc = w.segc + static_cast<size_t>(bh) * w.nseg;
+        float cm = cont ? p.sin.m[bh] : kNegInf, ce = cont ? p.sin.E[bh] : 0.f, cp = cont ? p.sin.P[bh] : 0.f;
+        if (lane == 0) sc[0] = make_float4(cm, ce, cp, 0.f);
+        for (int b0 = 0; b0 < nb; b0 += 64) {
+            float m = kNegInf, e = 0.f, ps = 0.f;
+            if (b0 + lane < nb) {
+                const float4 a = ag[b0 + lane];
+                m = a.x;
+                e = a.y;
+                ps = a.z;
+            }
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float m2 = __shfl_up(m, off, 64), e2 = __shfl_up(e, off, 64), p2 = __shfl_up(ps, off, 64);
+                if (lane >= off) {
+                    const float mx = fmaxf(m2, m);
+                    e = e2 * exp_diff(m2, mx) + e * exp_diff(m, mx);
+                    m = mx;
+                    ps = p2 + ps;
+                }
+            }
+            const float mx = fmaxf(cm, m);
+            const float E = ce * exp_diff(cm, mx) + e * exp_diff(m, mx), P = cp + ps;
+            const int blk = b0 + lane;
+            if (blk < nb && (blk + 1) % bps == 0) sc[(blk + 1) / bps] = make_float4(mx, E, P, 0.f);
+            const int last = min(63, nb - 1 - b0);
+            cm = lane_f(mx, last);
+            ce = lane_f(E, last);
+            cp = lane_f(P, last);
+        }
+    }
+    const int x = blockIdx.y * 256 + threadIdx.x;
+    if (x >= D * D) return;
     const size_t e = static_cast<size_t>(bh) * D * D + x;
     float f = cont ? p.sin.F[e] : 0.f, g = cont ? p.sin.G[e] : 0.f, h = cont ? p.sin.Hs[e] : 0.f;
     float m = cont ? p.sin.m[bh] : kNegInf;
@@ -517,9 +556,7 @@ hipError_t launch_one(const Problem &p, const ValuWork &w, hipStream_t stream) {
         hipLaunchKernelGGL((causal_valu_kernel<D, T, ROPE>), dim3(grid * (w.nseg - 1)), dim3(kThreads), smem,
                            stream, p, w, nls, 1);
         if ((err = hipGetLastError()) != hipSuccess) return err;
-        hipLaunchKernelGGL((causal_valu_combine_kernel<D>), dim3(p.B * p.H, (D * D + 255) / 256), dim3(256), 0,
-                           stream, p, w);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
+        if ((err = launch_valu_combine(p, w, stream)) != hipSuccess) return err;
     }
     hipLaunchKernelGGL((causal_valu_kernel<D, T, ROPE>), dim3(grid * w.nseg), dim3(kThreads), smem, stream, p, w,
                        nls, 0);
@@ -536,15 +573,22 @@ hipError_t launch_d(const Problem &p, const ValuWork &w, hipStream_t stream) {
 // workspace regions start on 256-byte boundaries
 size_t up256(size_t x) { return (x + 255) / 256 * 256; }
 
-// Segments of the scan: whole 64-token blocks (an even number of chunks), at least four chunks
-// each, and enough (head, tile, segment) workgroups for one per CU. (A grid that already fills
-// the chip is left whole: its chunk work is bound by the CUs' throughput, and three workgroups
-// per CU measured no faster than one.)
+// Segments of the scan: whole 64-token blocks (an even number of chunks). The per-tile kernel (d 16
+// and 32, and bfloat16 state copies) takes at least four chunks per segment and enough (head, tile,
+// segment) workgroups for one per CU; a grid that already fills the chip is left whole (its chunk
+// work is bound by the CUs' throughput: three workgroups per CU measured no faster than one). The
+// per-head float32 kernel (d 64 and 128) takes enough (head, segment) workgroups for one per CU, at
+// most kF32MaxSeg segments per head (the combine chains them in order).
+constexpr int kF32MaxSeg = 32;
+// The per-head kernel addresses one head's rows with 32-bit offsets.
+bool f32_per_head(int d, int N) { return d >= 64 && static_cast<long long>(N) * d * 4 < (1LL << 31); }
 void valu_seg_plan(int B, int H, int N, int d, int &nseg, int &seg_chunks) {
     const int nch = (N + kC - 1) / kC;
-    const long wg = static_cast<long>(B) * H * (d / kTile);
+    const bool per_head = f32_per_head(d, N);
+    const long wg = static_cast<long>(B) * H * (per_head ? 1 : d / kTile);
     long want = (256 + wg - 1) / wg;
-    if (want > nch / 4) want = nch / 4;
+    if (want > nch / (per_head ? 2 : 4)) want = nch / (per_head ? 2 : 4);
+    if (per_head && want > kF32MaxSeg) want = kF32MaxSeg;
     if (want < 1) want = 1;
     seg_chunks = static_cast<int>((nch + want - 1) / want);
     seg_chunks += seg_chunks & 1;
@@ -555,7 +599,8 @@ void valu_seg_plan(int B, int H, int N, int d, int &nseg, int &seg_chunks) {
 
 // Workspace of the float32 / small-d causal path: logits [B H, N], u sums per logit segment
 // [B H, nls, d_u], per-64-token logit aggregates [B H, ceil(N/64)] (written by the logits kernels),
-// and for a segmented scan the segment states [B H, nseg-1, 3, d, d] and maxima [B H, nseg].
+// and for a segmented scan the segment states [B H, nseg-1, 3, d, d], maxima [B H, nseg] and the
+// logit carries (m, E, P) at the segment starts [B H, nseg].
 size_t causal_valu_work_bytes(int B, int H, int N, int du) {
     const size_t bh = static_cast<size_t>(B) * H;
     const size_t nls = (static_cast<size_t>(N) + kLogitSeg - 1) / kLogitSeg;
@@ -563,7 +608,7 @@ size_t causal_valu_work_bytes(int B, int H, int N, int du) {
     int nseg, seg_chunks;
     valu_seg_plan(B, H, N, du, nseg, seg_chunks);
     size_t b = up256(bh * N * 4) + up256(bh * nls * du * 4) + up256(bh * n64 * 16);
-    if (nseg > 1) b += up256(bh * (nseg - 1) * size_t(3) * du * du * 4) + up256(bh * nseg * 4);
+    if (nseg > 1) b += up256(bh * (nseg - 1) * size_t(3) * du * du * 4) + up256(bh * nseg * 4) + up256(bh * nseg * 16);
     return b;
 }
 
@@ -584,13 +629,30 @@ ValuWork causal_valu_work_carve(void *base, int B, int H, int N, int du) {
         w.segst = reinterpret_cast<float *>(b);
         b += up256(bh * (w.nseg - 1) * size_t(3) * du * du * 4);
         w.segm = reinterpret_cast<float *>(b);
+        b += up256(bh * w.nseg * 4);
+        w.segc = reinterpret_cast<float4 *>(b);
     }
     return w;
+}
+
+hipError_t launch_valu_combine(const Problem &p, const ValuWork &w, hipStream_t stream) {
+    const dim3 grid(p.B * p.H, (p.d * p.d + 255) / 256);
+    switch (p.d) {
+        case 16: hipLaunchKernelGGL((causal_valu_combine_kernel<16>), grid, dim3(256), 0, stream, p, w); break;
+        case 32: hipLaunchKernelGGL((causal_valu_combine_kernel<32>), grid, dim3(256), 0, stream, p, w); break;
+        case 64: hipLaunchKernelGGL((causal_valu_combine_kernel<64>), grid, dim3(256), 0, stream, p, w); break;
+        case 128: hipLaunchKernelGGL((causal_valu_combine_kernel<128>), grid, dim3(256), 0, stream, p, w); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_causal_valu(const Problem &p, const ValuWork &w, hipStream_t stream) {
     hipError_t err = launch_logits(p, w.useg, w.s, w.agg, nullptr, stream);
     if (err != hipSuccess) return err;
+    // float32 with d 64 or 128: the per-head kernel (a bfloat16 call reaches this path only as a copy
+    // of the state with N = 0, which the per-tile kernel does)
+    if (p.dtype == ZEROS_F32 && f32_per_head(p.d, p.N)) return launch_causal_f32(p, w, stream);
     switch (p.d) {
         case 16: return launch_d<16>(p, w, stream);
         case 32: return launch_d<32>(p, w, stream);

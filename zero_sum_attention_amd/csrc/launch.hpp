@@ -50,19 +50,26 @@ struct CausalWork {
 size_t causal_work_bytes(int B, int H, int N, int du);
 CausalWork causal_work_carve(void *base, int B, int H, int N, int du);
 
-// Workspace of the float32 / small-d causal path (logits computed ahead of the scan kernel).
+// Workspace of the float32 / small-d causal path (logits computed ahead of the scan kernel). Its
+// segment plan counts in chunks of kValuChunk tokens.
+constexpr int kValuChunk = 32;
 struct ValuWork {
     float *s;           // [B*H, N] logits
     float *useg;        // [B*H, ceil(N/kLogitSeg), d_u] u sums per logit segment
     float4 *agg;        // [B*H, ceil(N/64)] per-64-token logit aggregates (segment start carries)
     float *segst;       // [B*H, nseg-1, 3, d, d] segment-local F, G, H, then segment start states
     float *segm;        // [B*H, nseg] running logit maximum at the end of each segment
+    float4 *segc;       // [B*H, nseg] logit carry (m, E, P, 0) at the start of each segment
     int nseg;           // scan segments per head (1: a single pass)
     int seg_chunks;     // 32-token chunks per segment (even: segments start on 64-token blocks)
 };
 size_t causal_valu_work_bytes(int B, int H, int N, int du);
 ValuWork causal_valu_work_carve(void *base, int B, int H, int N, int du);
 hipError_t launch_causal_valu(const Problem &p, const ValuWork &w, hipStream_t stream);
+// Pieces of the float32 path: the combine of the segment states (segmented scans), and the per-head
+// scan kernels for float32 with d in {64, 128} (logits already in the workspace).
+hipError_t launch_valu_combine(const Problem &p, const ValuWork &w, hipStream_t stream);
+hipError_t launch_causal_f32(const Problem &p, const ValuWork &w, hipStream_t stream);
 
 // Logits of the causal paths; when rope_tab is not null it also fills the in-chunk RoPE angle
 // table [kCausalChunk, d/2] (cos, sin of r * theta_j) used by the prep kernel.

@@ -56,18 +56,6 @@ __device__ __forceinline__ void load4<float>(const float *p, float (&x)[4]) {
     x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
 }
 
-// NE contiguous features (NE a multiple of 4) into x, or zeros when !valid.
-template <int NE, typename T>
-__device__ __forceinline__ void load_feats(const T *p, bool valid, float (&x)[NE]) {
-#pragma unroll
-    for (int i = 0; i < NE; i += 4) {
-        float y[4] = {0.f, 0.f, 0.f, 0.f};
-        if (valid) load4(p + i, y);
-#pragma unroll
-        for (int a = 0; a < 4; ++a) x[i + a] = y[a];
-    }
-}
-
 // Column sums of u over one segment: 8 consecutive features per thread, rows strided.
 template <int D, typename T>
 __global__ __launch_bounds__(kThreads) void useg_sum_kernel(const T *u, float *useg, int N, int nseg,
@@ -151,13 +139,29 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(const T *u, const floa
         carry[i] = 0.f;
     }
     const float rs_du = 1.f / sqrtf(static_cast<float>(D));
-    const T *ub = u + static_cast<size_t>(bh) * N * D;
+    const T *ub = u + static_cast<size_t>(bh) * N * D + w * DW;
     const int r0 = seg * kLogitSeg, r1 = min(N, r0 + kLogitSeg);
+    // rows of the next 64-token block are read while this one is processed (clamped into the
+    // sequence; rows past r1 are zeroed when used)
+    float xn[DW];
+    auto load_block = [&](const int b0) __attribute__((always_inline)) {
+        const T *src = ub + static_cast<size_t>(min(b0 + lane, N - 1)) * D;
+#pragma unroll
+        for (int i = 0; i < DW; i += 4) {
+            float y[4];
+            load4(src + i, y);
+#pragma unroll
+            for (int a = 0; a < 4; ++a) xn[i + a] = y[a];
+        }
+    };
+    if (r0 < r1) load_block(r0);
     for (int b0 = r0; b0 < r1; b0 += 64) {
         const int row = b0 + lane;
         const bool valid = row < r1;
         float x[DW], S[DW];
-        load_feats<DW>(ub + static_cast<size_t>(row) * D + w * DW, valid, x);
+#pragma unroll
+        for (int i = 0; i < DW; ++i) x[i] = valid ? xn[i] : 0.f;
+        if (b0 + 64 < r1) load_block(b0 + 64);
 #pragma unroll
         for (int i = 0; i < DW; ++i) S[i] = wave_scan_add(x[i]);
         const float inv = 1.f / (et + tprev + static_cast<float>(row + 1));

@@ -319,13 +319,13 @@ def test_cpu_tensors_rejected():
         Z.zeros_fwd_encoder(q, q, q, q, torch.zeros(1, 16), torch.zeros(1), g, g)
 
 
-@pytest.mark.parametrize("B,H,N,d,nseg", [(1, 2, 8192, 64, 32), (8, 8, 512, 64, 4), (1, 1, 1000, 128, 16),
+@pytest.mark.parametrize("B,H,N,d,nseg", [(1, 2, 8192, 64, 64), (8, 8, 512, 64, 4), (1, 1, 1000, 128, 16),
                                           (64, 8, 512, 64, 1), (1, 1, 255, 16, 2), (1, 3, 577, 32, 4),
                                           (2, 2, 100, 16, 1)])
 def test_float32_segment_plan_workspace(lib, B, H, N, d, nseg):
     """The float32 path's workspace carries segment states and carries exactly when the plan splits a
     head. Segments are whole 64-token blocks. d 64/128 (one workgroup per head segment): about one
-    workgroup per CU, at most 32 segments, at least 64 tokens each. d 16/32 (one workgroup per
+    workgroup per CU, at most 64 segments, at least 64 tokens each. d 16/32 (one workgroup per
     16-column tile): at least 128 tokens each."""
     def up(x):
         return (x + 255) // 256 * 256

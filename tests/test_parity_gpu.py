@@ -303,11 +303,12 @@ def test_encoder_shapes(d, N, dtype, rope):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("N", [64, 65, 300, 1000])
+@pytest.mark.parametrize("N", [64, 65, 128, 129, 255, 300, 1000])
 @pytest.mark.parametrize("rope", [False, True])
 def test_encoder_mfma_chunks(d, N, rope):
     """bfloat16 encoder on the matrix cores: several 64-token state chunks and 16-token output
-    blocks, ragged tails, both head dims."""
+    blocks, ragged tails, both head dims; at d = 64 and N <= 256 the per-head variant, whose state
+    pass stages 128 tokens per round (128 / 129: one or two rounds)."""
     wl = CONFIGS[3].with_(B=1, H=2, N=N, d=d, d_u=d, dtype="bf16", seed=3000 + d + N)
     x = make_inputs(wl)
     o = to_f64(run_encoder(x, "bf16", rope=rope))
@@ -331,9 +332,11 @@ def test_encoder_length_boundaries(d, N):
     assert err <= TOL["bf16"]
 
 
-def test_encoder_mfma_large_logits():
-    """u scaled by 30: logits spread over a wide range, the global maximum keeps e^{s-m} in range."""
-    wl = CONFIGS[3].with_(B=1, H=2, N=300, d=64, d_u=64, dtype="bf16", seed=3999)
+@pytest.mark.parametrize("N", [200, 300])
+def test_encoder_mfma_large_logits(N):
+    """u scaled by 30: logits spread over a wide range, the global maximum keeps e^{s-m} in range
+    (N = 200: the per-head variant, N = 300: the tile variant)."""
+    wl = CONFIGS[3].with_(B=1, H=2, N=N, d=64, d_u=64, dtype="bf16", seed=3999)
     x = make_inputs(wl, u_scale=30.0)
     o = to_f64(run_encoder(x, "bf16"))
     ref = R.encoder_forward(**x)

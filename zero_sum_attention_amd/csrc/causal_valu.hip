@@ -508,24 +508,25 @@ __global__ __launch_bounds__(256) void causal_valu_combine_kernel(Problem p, Val
             cp = lane_f(P, last);
         }
     }
-    const int x = blockIdx.y * 256 + threadIdx.x;
+    const int x = blockIdx.y * blockDim.x + threadIdx.x;
     if (x >= D * D) return;
     const size_t e = static_cast<size_t>(bh) * D * D + x;
     float f = cont ? p.sin.F[e] : 0.f, g = cont ? p.sin.G[e] : 0.f, h = cont ? p.sin.Hs[e] : 0.f;
     float m = cont ? p.sin.m[bh] : kNegInf;
-    constexpr int kBatch = 8;               // segments whose sums are loaded together
+    // segments whose sums are loaded together: the loads are unconditional (the index clamped to the
+    // last segment) so they issue back to back; a guard per load compiles to a branch and a wait each
+    constexpr int kBatch = 32;
     for (int j0 = 0; j0 + 1 < w.nseg; j0 += kBatch) {
         const int nj = min(kBatch, w.nseg - 1 - j0);
         float lf[kBatch], lg[kBatch], lh[kBatch], lm[kBatch];
 #pragma unroll
         for (int jj = 0; jj < kBatch; ++jj) {
-            if (jj < nj) {
-                const float *st = w.segst + (static_cast<size_t>(bh) * (w.nseg - 1) + j0 + jj) * 3 * D * D;
-                lf[jj] = st[x];
-                lg[jj] = st[D * D + x];
-                lh[jj] = st[2 * D * D + x];
-                lm[jj] = w.segm[static_cast<size_t>(bh) * w.nseg + j0 + jj];
-            }
+            const int j = min(j0 + jj, w.nseg - 2);
+            const float *st = w.segst + (static_cast<size_t>(bh) * (w.nseg - 1) + j) * 3 * D * D;
+            lf[jj] = st[x];
+            lg[jj] = st[D * D + x];
+            lh[jj] = st[2 * D * D + x];
+            lm[jj] = w.segm[static_cast<size_t>(bh) * w.nseg + j];
         }
 #pragma unroll
         for (int jj = 0; jj < kBatch; ++jj) {
@@ -579,7 +580,7 @@ size_t up256(size_t x) { return (x + 255) / 256 * 256; }
 // work is bound by the CUs' throughput: three workgroups per CU measured no faster than one). The
 // per-head float32 kernel (d 64 and 128) takes enough (head, segment) workgroups for one per CU, at
 // most kF32MaxSeg segments per head (the combine chains them in order).
-constexpr int kF32MaxSeg = 32;
+constexpr int kF32MaxSeg = 64;
 // The per-head kernel addresses one head's rows with 32-bit offsets.
 bool f32_per_head(int d, int N) { return d >= 64 && static_cast<long long>(N) * d * 4 < (1LL << 31); }
 void valu_seg_plan(int B, int H, int N, int d, int &nseg, int &seg_chunks) {
@@ -636,12 +637,15 @@ ValuWork causal_valu_work_carve(void *base, int B, int H, int N, int du) {
 }
 
 hipError_t launch_valu_combine(const Problem &p, const ValuWork &w, hipStream_t stream) {
-    const dim3 grid(p.B * p.H, (p.d * p.d + 255) / 256);
+    // one thread per state element, each chaining all segments; with few heads, one-wave blocks
+    // spread the chains over more CUs
+    const int nt = p.B * p.H < 64 ? 64 : 256;
+    const dim3 grid(p.B * p.H, (p.d * p.d + nt - 1) / nt);
     switch (p.d) {
-        case 16: hipLaunchKernelGGL((causal_valu_combine_kernel<16>), grid, dim3(256), 0, stream, p, w); break;
-        case 32: hipLaunchKernelGGL((causal_valu_combine_kernel<32>), grid, dim3(256), 0, stream, p, w); break;
-        case 64: hipLaunchKernelGGL((causal_valu_combine_kernel<64>), grid, dim3(256), 0, stream, p, w); break;
-        case 128: hipLaunchKernelGGL((causal_valu_combine_kernel<128>), grid, dim3(256), 0, stream, p, w); break;
+        case 16: hipLaunchKernelGGL((causal_valu_combine_kernel<16>), grid, dim3(nt), 0, stream, p, w); break;
+        case 32: hipLaunchKernelGGL((causal_valu_combine_kernel<32>), grid, dim3(nt), 0, stream, p, w); break;
+        case 64: hipLaunchKernelGGL((causal_valu_combine_kernel<64>), grid, dim3(nt), 0, stream, p, w); break;
+        case 128: hipLaunchKernelGGL((causal_valu_combine_kernel<128>), grid, dim3(nt), 0, stream, p, w); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

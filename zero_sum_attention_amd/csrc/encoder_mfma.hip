@@ -31,13 +31,9 @@ constexpr int kEShortN = 256;      // longest sequence of the short variant (log
 constexpr int kEThreads = 256;     // 4 waves
 constexpr int kEPad = 8;           // bf16 elements of row padding in LDS
 
+// Sum over the D/8 consecutive lanes that hold one token row (DPP within a row of 16 lanes).
 template <int D>
-__device__ __forceinline__ float row_sum(float x) {
-    // sum over the D/8 consecutive lanes that hold one token row
-#pragma unroll
-    for (int off = 1; off < D / 8; off <<= 1) x += __shfl_xor(x, off, 64);
-    return x;
-}
+__device__ __forceinline__ float row_sum(float x) { return group_sum<D / 8>(x); }
 
 // (max, sum e^{s - max}) of two parts merged; a max of -inf marks an empty part.
 __device__ __forceinline__ void lse_merge(float &m, float &e, float m2, float e2) {
@@ -45,6 +41,37 @@ __device__ __forceinline__ void lse_merge(float &m, float &e, float m2, float e2
     e = (m == kNegInf ? 0.f : e * __expf(m - mm)) + (m2 == kNegInf ? 0.f : e2 * __expf(m2 - mm));
     m = mm;
 }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// (max, sum e^{s - max}, sum s) merged over the 64 lanes of a wave; every lane gets the result.
+// Within a row of 16 lanes the partners come by DPP (the pairings of group_sum), then the four row
+// results by readlane.
+__device__ __forceinline__ void wave_lse_merge(float &m, float &e, float &ps) {
+    lse_merge(m, e, dpp_mov<kQuadXor1>(m), dpp_mov<kQuadXor1>(e));
+    ps += dpp_mov<kQuadXor1>(ps);
+    lse_merge(m, e, dpp_mov<kQuadXor2>(m), dpp_mov<kQuadXor2>(e));
+    ps += dpp_mov<kQuadXor2>(ps);
+    lse_merge(m, e, dpp_mov<kRowHalfMirror>(m), dpp_mov<kRowHalfMirror>(e));
+    ps += dpp_mov<kRowHalfMirror>(ps);
+    lse_merge(m, e, dpp_mov<kRowMirror>(m), dpp_mov<kRowMirror>(e));
+    ps += dpp_mov<kRowMirror>(ps);
+    float M = lane_f(m, 0), E = lane_f(e, 0), P = lane_f(ps, 0);
+#pragma unroll
+    for (int r = 16; r < 64; r += 16) {
+        lse_merge(M, E, lane_f(m, r), lane_f(e, r));
+        P += lane_f(ps, r);
+    }
+    m = M;
+    e = E;
+    ps = P;
+}
+
+// float -> bfloat16 bits (round to nearest even)
+__device__ __forceinline__ uint16_t bf16_bits(float x) { return static_cast<uint16_t>(pack2(x, 0.f) & 0xffffu); }
 
 __device__ __forceinline__ void unpack8(const uint4 &x, float (&f)[8]) {
     const uint32_t w[4] = {x.x, x.y, x.z, x.w};
@@ -66,7 +93,7 @@ __global__ __launch_bounds__(kEThreads) void encoder_mfma_kernel(Problem p, floa
     constexpr int LPR = D / 8;         // lanes per token row (8 features, 16 bytes each)
     constexpr int RPP = kEThreads / LPR;   // token rows per pass
     __shared__ float ubar[D];
-    __shared__ float part[kEThreads / 64][D];
+    __shared__ __align__(16) float colp[RPP][D];          // partial column sums of u, one row per token row of a pass
     __shared__ float sl_lds[NMAX > 0 ? NMAX : 1];   // logits of the sequence (N <= NMAX)
     __shared__ float4 red[kEThreads / 64];
     __shared__ __align__(16) uint16_t kt[D][kEC + kEPad];    // k^ of the chunk, transposed
@@ -121,6 +148,22 @@ __global__ __launch_bounds__(kEThreads) void encoder_mfma_kernel(Problem p, floa
         }
     };
     load_kv(0);                        // the first step's rows are in flight during phase A
+    // phase C's first q rows and gates of this wave (token block w), read now so that phase C
+    // starts without a memory round trip
+    constexpr int KS0 = D / 32;
+    uint4 qn[KS0];
+    uint32_t g1n = 0, ghn = 0, g0n = 0;
+    auto load_q = [&](const int tb) __attribute__((always_inline)) {
+        const int t = min(16 * tb + l16, N - 1);   // in bounds; rows past N are never stored
+        const size_t tr = static_cast<size_t>(t) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS0; ++ks) qn[ks] = *reinterpret_cast<const uint4 *>(q + tr + 32 * ks + 8 * g4);
+        g1n = g1[t];
+        ghn = gh[t];
+        if (G0) g0n = g0[t];
+    };
+    const int ntb = (N + 15) / 16;
+    if (w < ntb) load_q(w);
 
     // ---- A: ubar, logits, and the scalar sums. The first UC rows of each thread are read once and
     // stay in registers from the column sums to the logits.
@@ -147,21 +190,15 @@ __global__ __launch_bounds__(kEThreads) void encoder_mfma_kernel(Problem p, floa
 #pragma unroll
             for (int i = 0; i < 8; ++i) cs[i] += x[i];
         }
-        // the rows of a wave sit LPR lanes apart: a shuffle sum over them, then the waves through LDS
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-#pragma unroll
-            for (int off = LPR; off < 64; off <<= 1) cs[i] += __shfl_xor(cs[i], off, 64);
-        }
-        if (lane < LPR) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) part[w][8 * fr + i] = cs[i];
-        }
+        // every thread's partial column sums through LDS, then one thread per feature adds the RPP
+        // rows in order (no cross-lane shuffles)
+        *reinterpret_cast<float4 *>(&colp[rr][8 * fr]) = make_float4(cs[0], cs[1], cs[2], cs[3]);
+        *reinterpret_cast<float4 *>(&colp[rr][8 * fr + 4]) = make_float4(cs[4], cs[5], cs[6], cs[7]);
         __syncthreads();
         if (tid < D) {
             float su = 0.f;
 #pragma unroll
-            for (int g = 0; g < kEThreads / 64; ++g) su += part[g][tid];
+            for (int g = 0; g < RPP; ++g) su += colp[g][tid];
             ubar[tid] = (et * mu_t + su) / (et + static_cast<float>(N));
         }
         __syncthreads();
@@ -197,12 +234,7 @@ __global__ __launch_bounds__(kEThreads) void encoder_mfma_kernel(Problem p, floa
         }
     }
     // block reduction of (max, sum e^{s - max}, sum s): in each wave, then across the waves
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float m2 = __shfl_xor(mloc, off, 64), e2 = __shfl_xor(eloc, off, 64);
-        ploc += __shfl_xor(ploc, off, 64);
-        lse_merge(mloc, eloc, m2, e2);
-    }
+    wave_lse_merge(mloc, eloc, ploc);
     if (lane == 0) red[w] = make_float4(mloc, eloc, ploc, 0.f);
     __syncthreads();                           // also orders the logits (LDS or sg) before phase B
     float M = kNegInf, E = 0.f, P = 0.f;
@@ -328,19 +360,6 @@ __global__ __launch_bounds__(kEThreads) void encoder_mfma_kernel(Problem p, floa
         AY[ks] = *reinterpret_cast<const bf16x8 *>(&sxy[1][l16][32 * ks + 8 * g4]);
         if (G0) AH[ks] = *reinterpret_cast<const bf16x8 *>(&sxy[NS - 1][l16][32 * ks + 8 * g4]);
     }
-    uint4 qn[KS];
-    uint32_t g1n = 0, ghn = 0, g0n = 0;
-    auto load_q = [&](const int tb) __attribute__((always_inline)) {
-        const int t = min(16 * tb + l16, N - 1);   // in bounds; rows past N are never stored
-        const size_t tr = static_cast<size_t>(t) * D;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qn[ks] = *reinterpret_cast<const uint4 *>(q + tr + 32 * ks + 8 * g4);
-        g1n = g1[t];
-        ghn = gh[t];
-        if (G0) g0n = g0[t];
-    };
-    const int ntb = (N + 15) / 16;
-    if (w < ntb) load_q(w);
     for (int tb = w; tb < ntb; tb += kEThreads / 64) {
         const int t = 16 * tb + l16;
         const bool ok = t < N;
@@ -392,10 +411,344 @@ __global__ __launch_bounds__(kEThreads) void encoder_mfma_kernel(Problem p, floa
     }
 }
 
+// ---- Per-head variant for short sequences (N <= kEHeadMaxN, d = 64): one workgroup of 16 waves per
+// (batch, head) does the u sums, the logits and the unit k^ once for all column tiles (the tile
+// variant above repeats them per tile), reads all of u, k, v and the first q block of each wave at
+// its start (one memory round trip), stages all tokens at once for the states (128 at a time with
+// RoPE), and gives each
+// wave its own 16 x 16 tiles of X and Y (and H) and its own 16-token block of outputs.
+constexpr int kEHeadMaxN = 256;
+constexpr int kEHThreads = 1024;
+// tokens staged per round of the state pass: all of them, or 128 with RoPE (whose angle arithmetic
+// for two rows at once would spill)
+constexpr int kEHalf = 256;
+template <bool ROPE> constexpr int eh_round() { return ROPE ? 128 : kEHalf; }
+
+// Token column of row f in the transposed staging buffers of the per-head variant: bits 3-5 of the
+// token index XOR the row's 8-row group, so that the 8 feature groups of a staging write land in
+// different banks (rows 8 apart are 544 words apart, the same bank) while each 8-token group stays
+// contiguous for the 16-byte MFMA operand reads.
+__device__ __forceinline__ int eh_col(int f, int tok) { return tok ^ (((f >> 3) & 7) << 3); }
+
+template <int D, bool G0>
+union EHeadBuf {
+    float colp[kEHThreads / 16][D];                  // partial column sums of u, one per 16-lane row
+    struct {
+        uint16_t kt[D][kEHalf + kEPad];             // k^ of the round, transposed
+        uint16_t vxt[D][kEHalf + kEPad];            // v w_X of the round, transposed
+        uint16_t vyt[D][kEHalf + kEPad];            // v w_Y
+        uint16_t vht[G0 ? D : 1][kEHalf + kEPad];   // v (the H state of the zero-order gate)
+    } st;
+    uint16_t sxy[G0 ? 3 : 2][D][D + kEPad];         // X^T, Y^T (H^T) as bf16, for the outputs
+};
+
+template <int D, bool ROPE, bool G0>
+__global__ __launch_bounds__(kEHThreads) void encoder_head_kernel(Problem p) {
+    constexpr int NS = G0 ? 3 : 2;
+    constexpr int LPR = D / 8;                   // lanes per token row (8 features each)
+    constexpr int RPP = kEHThreads / LPR;        // token rows per pass
+    constexpr int UP = kEHeadMaxN / RPP;         // passes (rows per thread)
+    constexpr int ER = eh_round<ROPE>();         // tokens per staging round
+    constexpr int JPH = ER / RPP;                // passes per staging round
+    constexpr int NFT = D / 16;                  // 16-row (16-column) tiles of a d x d state
+    constexpr int TPW = NFT * NFT / 16;          // state tiles per wave
+    constexpr int KS = D / 32;                   // 32-feature steps of the output products
+    static_assert(UP * RPP == kEHeadMaxN && JPH * RPP == ER && TPW >= 1, "per-head shape");
+    __shared__ __align__(16) EHeadBuf<D, G0> buf;
+    __shared__ float ubar[D];
+    __shared__ float sl[kEHeadMaxN];
+    __shared__ float4 red[16];
+    __shared__ float red2[16];
+    __shared__ double rev[ROPE ? D / 2 : 1];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int bh = blockIdx.x, h = bh % p.H;
+    const int N = p.N;
+    const size_t row0 = static_cast<size_t>(bh) * N;
+    const uint16_t *q = static_cast<const uint16_t *>(p.q) + row0 * D;
+    const uint16_t *k = static_cast<const uint16_t *>(p.k) + row0 * D;
+    const uint16_t *v = static_cast<const uint16_t *>(p.v) + row0 * D;
+    const uint16_t *u = static_cast<const uint16_t *>(p.u) + row0 * D;
+    const uint16_t *g1 = static_cast<const uint16_t *>(p.g1) + row0;
+    const uint16_t *gh = static_cast<const uint16_t *>(p.gh) + row0;
+    const uint16_t *g0 = G0 ? static_cast<const uint16_t *>(p.g0) + row0 : nullptr;
+    uint16_t *o = static_cast<uint16_t *>(p.o) + row0 * D;
+    const int fr = tid % LPR, rr = tid / LPR;    // feature group and row of a pass
+    if (ROPE && tid < D / 2) rev[tid] = rope_rev_per_pos(tid, D, p.rope_base);   // ordered by the first barrier
+
+    // ---- every read up front: rows rr + RPP j of u, k, v (clamped into the sequence; rows past N
+    // are zeroed where used), and this wave's 16-token block of q with its gates
+    uint4 ur[UP], kr[UP], vr[UP];
+#pragma unroll
+    for (int j = 0; j < UP; ++j)       // u first: phase A waits for these only
+        ur[j] = *reinterpret_cast<const uint4 *>(u + static_cast<size_t>(min(rr + RPP * j, N - 1)) * D + 8 * fr);
+#pragma unroll
+    for (int j = 0; j < UP; ++j) {
+        const size_t off = static_cast<size_t>(min(rr + RPP * j, N - 1)) * D + 8 * fr;
+        kr[j] = *reinterpret_cast<const uint4 *>(k + off);
+        vr[j] = *reinterpret_cast<const uint4 *>(v + off);
+    }
+    // (the RoPE variant with the zero-order gate reads them at phase C: its registers are full)
+    constexpr bool EARLY_Q = !(ROPE && G0);
+    const int tq = min(16 * w + l16, N - 1);
+    uint4 qv[KS];
+    uint32_t g1v = 0, ghv = 0, g0v = 0;
+    auto load_q = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qv[ks] = *reinterpret_cast<const uint4 *>(q + static_cast<size_t>(tq) * D + 32 * ks + 8 * g4);
+        g1v = g1[tq];
+        ghv = gh[tq];
+        if (G0) g0v = g0[tq];
+    };
+    if (EARLY_Q) load_q();
+    const float et = expf(p.tau[h]);
+    const float mu_t = tid < 4 * D ? p.mu[h * D + (tid >> 2)] : 0.f;
+
+    // ---- A: ubar = (e^tau mu + sum u) / (e^tau + N). Per thread the column sums of its rows; for
+    // d = 64 the two token rows of a 16-lane row are added by DPP (row_ror 8); one partial per
+    // 16-lane row goes to LDS, and 4 d threads add them (16 each, then the 4 by DPP).
+    {
+        float cs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < UP; ++j) {
+            float x[8];
+            unpack8(ur[j], x);
+            const bool ok = rr + RPP * j < N;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) cs[i] += ok ? x[i] : 0.f;
+        }
+        if constexpr (LPR == 8) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) cs[i] += dpp_mov<kRowRor + 8>(cs[i]);
+        }
+        if ((lane & 15) < LPR) {
+            float *dst = &buf.colp[tid >> 4][8 * fr];
+            *reinterpret_cast<float4 *>(dst) = make_float4(cs[0], cs[1], cs[2], cs[3]);
+            *reinterpret_cast<float4 *>(dst + 4) = make_float4(cs[4], cs[5], cs[6], cs[7]);
+        }
+        __syncthreads();
+        if (tid < 4 * D) {
+            const int f = tid >> 2, qq = tid & 3;
+            float su = 0.f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) su += buf.colp[16 * qq + e][f];
+            su = group_sum<4>(su);
+            if (qq == 0) ubar[f] = (et * mu_t + su) / (et + static_cast<float>(N));
+        }
+        __syncthreads();
+    }
+    // logits s_r = -(u_r . ubar) / sqrt(d) and their (max, sum e^{s - max}, sum s): the maximum
+    // first (wave DPP max, then the 16 waves through LDS), then one exponential per row
+    float mx = kNegInf, ps = 0.f;
+    {
+        float ub[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ub[i] = ubar[8 * fr + i];
+        const float rs_du = 1.f / sqrtf(static_cast<float>(D));
+#pragma unroll
+        for (int j = 0; j < UP; ++j) {
+            const int r = rr + RPP * j;
+            float x[8];
+            unpack8(ur[j], x);
+            float dot = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) dot = fmaf(x[i], ub[i], dot);
+            dot = group_sum<LPR>(dot);
+            if (r < N && fr == 0) {
+                const float sv = -dot * rs_du;
+                sl[r] = sv;
+                mx = fmaxf(mx, sv);
+                ps += sv;
+            }
+        }
+    }
+    mx = lane_f(wave_scan_max(mx), 63);
+    ps = lane_f(wave_scan_add(ps), 63);
+    if (lane == 0) red[w] = make_float4(mx, ps, 0.f, 0.f);
+    __syncthreads();
+    float M = kNegInf, P = 0.f;
+    {
+        const float4 rv = red[l16];
+        float m = rv.x, q4 = rv.y;
+        m = fmaxf(m, dpp_mov<kQuadXor1>(m));
+        q4 += dpp_mov<kQuadXor1>(q4);
+        m = fmaxf(m, dpp_mov<kQuadXor2>(m));
+        q4 += dpp_mov<kQuadXor2>(q4);
+        m = fmaxf(m, dpp_mov<kRowHalfMirror>(m));
+        q4 += dpp_mov<kRowHalfMirror>(q4);
+        m = fmaxf(m, dpp_mov<kRowMirror>(m));
+        q4 += dpp_mov<kRowMirror>(q4);
+        M = lane_f(m, 0);
+        P = lane_f(q4, 0);
+    }
+    float es = 0.f;
+#pragma unroll
+    for (int j = 0; j < UP; ++j) {   // each lane reads back only the logits it wrote
+        const int r = rr + RPP * j;
+        if (r < N && fr == 0) es += __expf(sl[r] - M);
+    }
+    es = lane_f(wave_scan_add(es), 63);
+    if (lane == 0) red2[w] = es;
+    __syncthreads();                               // also orders sl before the state pass
+    float E;
+    {
+        float e4 = red2[l16];
+        e4 += dpp_mov<kQuadXor1>(e4);
+        e4 += dpp_mov<kQuadXor2>(e4);
+        e4 += dpp_mov<kRowHalfMirror>(e4);
+        e4 += dpp_mov<kRowMirror>(e4);
+        E = lane_f(e4, 0);
+    }
+    const float invN = 1.f / static_cast<float>(N);
+    const float invE = E > 0.f ? 1.f / E : 0.f;
+    const float PN = P * invN;
+
+    // ---- B: X = K^T diag(w_X) V, Y = K^T diag(w_Y) V (H = K^T V), 128 tokens per round; wave w
+    // owns state tiles w + 16 i (feature tile ft, column tile ct)
+    f32x4 X[TPW], Y[TPW], Hc[G0 ? TPW : 1];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) X[i] = Y[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < (G0 ? TPW : 1); ++i) Hc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int nrounds = (N + ER - 1) / ER;
+    for (int rd = 0; rd < nrounds; ++rd) {
+#pragma unroll
+        for (int j = 0; j < UP; ++j) {
+            if (j / JPH != rd) continue;           // uniform: this pass's rows belong to the round
+            const int r = rr + RPP * j, rl = r - ER * rd;
+            const bool ok = r < N;
+            float kv[8], vv[8];
+            unpack8(kr[j], kv);
+            unpack8(vr[j], vv);
+            float ss = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ss = fmaf(kv[i], kv[i], ss);
+            ss = group_sum<LPR>(ss);
+            const float ik = ok ? __frsqrt_rn(fmaxf(ss, 1e-24f)) : 0.f;
+            if (ROPE) {
+#pragma unroll
+                for (int j2 = 0; j2 < 4; ++j2) {
+                    float cs, sn;
+                    rope_cos_sin(rev[4 * fr + j2], r, cs, sn);
+                    const float a = kv[2 * j2], b = kv[2 * j2 + 1];
+                    kv[2 * j2] = a * cs - b * sn;
+                    kv[2 * j2 + 1] = a * sn + b * cs;
+                }
+            }
+            const float sv = ok ? sl[r] : 0.f;
+            const float wx = ok ? __expf(sv - M) * invE - invN : 0.f;
+            const float wy = ok ? sv - PN : 0.f;
+            const float wh = ok ? 1.f : 0.f;
+            const int cl = eh_col(8 * fr, rl);    // the same for the 8 rows 8 fr + i
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                buf.st.kt[8 * fr + i][cl] = bf16_bits(kv[i] * ik);
+                buf.st.vxt[8 * fr + i][cl] = bf16_bits(vv[i] * wx);
+                buf.st.vyt[8 * fr + i][cl] = bf16_bits(vv[i] * wy);
+                if (G0) buf.st.vht[8 * fr + i][cl] = bf16_bits(vv[i] * wh);
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int ti = 0; ti < TPW; ++ti) {
+            const int tile = w + 16 * ti, ft = tile / NFT, ct = tile % NFT;
+#pragma unroll
+            for (int ks = 0; ks < ER / 32; ++ks) {
+                if (ER * rd + 32 * ks >= N) break;        // steps past the sequence hold zeros only
+                const int kk0 = 32 * ks + 8 * g4;
+                const int fa = 16 * ft + l16, fb = 16 * ct + l16;
+                const bf16x8 A = *reinterpret_cast<const bf16x8 *>(&buf.st.kt[fa][eh_col(fa, kk0)]);
+                const bf16x8 BX = *reinterpret_cast<const bf16x8 *>(&buf.st.vxt[fb][eh_col(fb, kk0)]);
+                const bf16x8 BY = *reinterpret_cast<const bf16x8 *>(&buf.st.vyt[fb][eh_col(fb, kk0)]);
+                X[ti] = mfma(A, BX, X[ti]);
+                Y[ti] = mfma(A, BY, Y[ti]);
+                if (G0) {
+                    const bf16x8 BH = *reinterpret_cast<const bf16x8 *>(&buf.st.vht[fb][eh_col(fb, kk0)]);
+                    Hc[ti] = mfma(A, BH, Hc[ti]);
+                }
+            }
+        }
+        __syncthreads();
+    }
+    // X^T, Y^T (H^T) as bf16 A operands: accumulator lane (l16, g4) holds features 16 ft + 4 g4 + [0, 4)
+    // of column 16 ct + l16
+#pragma unroll
+    for (int ti = 0; ti < TPW; ++ti) {
+        const int tile = w + 16 * ti, ft = tile / NFT, ct = tile % NFT;
+        const int f = 16 * ft + 4 * g4, c = 16 * ct + l16;
+        *reinterpret_cast<uint2 *>(&buf.sxy[0][c][f]) = make_uint2(pack2(X[ti][0], X[ti][1]), pack2(X[ti][2], X[ti][3]));
+        *reinterpret_cast<uint2 *>(&buf.sxy[1][c][f]) = make_uint2(pack2(Y[ti][0], Y[ti][1]), pack2(Y[ti][2], Y[ti][3]));
+        if (G0)
+            *reinterpret_cast<uint2 *>(&buf.sxy[NS - 1][c][f]) =
+                make_uint2(pack2(Hc[ti][0], Hc[ti][1]), pack2(Hc[ti][2], Hc[ti][3]));
+    }
+    __syncthreads();
+
+    // ---- C: wave w forms the outputs of tokens 16 w + [0, 16), all column tiles:
+    // o_t = sigmah_t q^_t X + ((sigma1_t - sigmah_t)/N) q^_t Y (+ (sigma0_t/N) q^_t H)
+    if (16 * w >= N) return;
+    if (!EARLY_Q) load_q();
+    const int t = 16 * w + l16;
+    const bool ok = t < N;
+    float ss = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        uint32_t wv[4] = {qv[ks].x, qv[ks].y, qv[ks].z, qv[ks].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ss = dot2_bf16(wv[i], ss);
+        if (ROPE) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                // the pair (2j, 2j+1) sits in one 32-bit word: j = 16 ks + 4 g4 + i
+                float cs, sn;
+                rope_cos_sin(rev[16 * ks + 4 * g4 + i], t, cs, sn);
+                const float a = lo_f(wv[i]), b = hi_f(wv[i]);
+                wv[i] = pack2(a * cs - b * sn, a * sn + b * cs);
+            }
+            qv[ks] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+        }
+    }
+    ss += __shfl_xor(ss, 16, 64);
+    ss += __shfl_xor(ss, 32, 64);
+    const float iq = ok ? __frsqrt_rn(fmaxf(ss, 1e-24f)) : 0.f;
+    const float s1 = ok ? __fdividef(1.f, 1.f + __expf(-lo_f(g1v))) : 0.f;
+    const float sh = ok ? __fdividef(1.f, 1.f + __expf(-lo_f(ghv))) : 0.f;
+    const float ax = sh * iq, ay = (s1 - sh) * invN * iq;
+    const float ah = (G0 && ok) ? __fdividef(1.f, 1.f + __expf(-lo_f(g0v))) * invN * iq : 0.f;
+#pragma unroll
+    for (int ct = 0; ct < NFT; ++ct) {
+        f32x4 accX = {0.f, 0.f, 0.f, 0.f}, accY = accX, accH = accX;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 B = as_bf16x8(qv[ks].x, qv[ks].y, qv[ks].z, qv[ks].w);
+            const int f0 = 32 * ks + 8 * g4;
+            accX = mfma(*reinterpret_cast<const bf16x8 *>(&buf.sxy[0][16 * ct + l16][f0]), B, accX);
+            accY = mfma(*reinterpret_cast<const bf16x8 *>(&buf.sxy[1][16 * ct + l16][f0]), B, accY);
+            if (G0) accH = mfma(*reinterpret_cast<const bf16x8 *>(&buf.sxy[NS - 1][16 * ct + l16][f0]), B, accH);
+        }
+        if (ok) {
+            float r4[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) r4[i] = ax * accX[i] + ay * accY[i] + (G0 ? ah * accH[i] : 0.f);
+            *reinterpret_cast<uint2 *>(o + static_cast<size_t>(t) * D + 16 * ct + 4 * g4) =
+                make_uint2(pack2(r4[0], r4[1]), pack2(r4[2], r4[3]));
+        }
+    }
+}
+
 template <int D, bool ROPE, bool G0>
 hipError_t launch_g(const Problem &p, float *work, hipStream_t stream) {
     const dim3 grid((D / 16) * p.B * p.H);
-    // short sequences take the variant with a small logits buffer: less LDS, more workgroups per CU
+    // short sequences at d = 64: the per-head variant (N >= 1: the front end returns before a launch
+    // for N = 0). At d = 128 it would need more than the 128 registers a wave has at 16 waves per CU.
+    if constexpr (D == 64) {
+        if (p.N <= kEHeadMaxN) {
+            hipLaunchKernelGGL((encoder_head_kernel<D, ROPE, G0>), dim3(p.B * p.H), dim3(kEHThreads), 0, stream, p);
+            return hipGetLastError();
+        }
+    }
     if (p.N <= kEShortN) {
         hipLaunchKernelGGL((encoder_mfma_kernel<D, ROPE, kEShortN, G0>), grid, dim3(kEThreads), 0, stream, p, nullptr);
         return hipGetLastError();

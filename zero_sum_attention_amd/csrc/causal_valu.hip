@@ -17,6 +17,8 @@
 // this kernel); the scalar scans are recomputed by every tile of a head (O(C) per chunk).
 // A continued sequence (state in: the recurrence of the linear-time prefix scan paused after
 // t_in tokens) starts from that state's F, G, H, m, E, P, with positions shifted by t_in.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "mfma_common.hpp"
@@ -514,34 +516,39 @@ __global__ __launch_bounds__(256) void causal_valu_combine_kernel(Problem p, Val
     float f = cont ? p.sin.F[e] : 0.f, g = cont ? p.sin.G[e] : 0.f, h = cont ? p.sin.Hs[e] : 0.f;
     float m = cont ? p.sin.m[bh] : kNegInf;
     // segments whose sums are loaded together: the loads are unconditional (the index clamped to the
-    // last segment) so they issue back to back; a guard per load compiles to a branch and a wait each
-    constexpr int kBatch = 32;
-    for (int j0 = 0; j0 + 1 < w.nseg; j0 += kBatch) {
-        const int nj = min(kBatch, w.nseg - 1 - j0);
-        float lf[kBatch], lg[kBatch], lh[kBatch], lm[kBatch];
+    // last segment) so they issue back to back; a guard per load compiles to a branch and a wait each.
+    // Batches of 4 segments when there are few, of 32 when there are many.
+    auto chain = [&](auto batch) __attribute__((always_inline)) {
+        constexpr int kBatch = decltype(batch)::value;
+        for (int j0 = 0; j0 + 1 < w.nseg; j0 += kBatch) {
+            const int nj = min(kBatch, w.nseg - 1 - j0);
+            float lf[kBatch], lg[kBatch], lh[kBatch], lm[kBatch];
 #pragma unroll
-        for (int jj = 0; jj < kBatch; ++jj) {
-            const int j = min(j0 + jj, w.nseg - 2);
-            const float *st = w.segst + (static_cast<size_t>(bh) * (w.nseg - 1) + j) * 3 * D * D;
-            lf[jj] = st[x];
-            lg[jj] = st[D * D + x];
-            lh[jj] = st[2 * D * D + x];
-            lm[jj] = w.segm[static_cast<size_t>(bh) * w.nseg + j];
-        }
+            for (int jj = 0; jj < kBatch; ++jj) {
+                const int j = min(j0 + jj, w.nseg - 2);
+                const float *st = w.segst + (static_cast<size_t>(bh) * (w.nseg - 1) + j) * 3 * D * D;
+                lf[jj] = st[x];
+                lg[jj] = st[D * D + x];
+                lh[jj] = st[2 * D * D + x];
+                lm[jj] = w.segm[static_cast<size_t>(bh) * w.nseg + j];
+            }
 #pragma unroll
-        for (int jj = 0; jj < kBatch; ++jj) {
-            if (jj < nj) {
-                float *st = w.segst + (static_cast<size_t>(bh) * (w.nseg - 1) + j0 + jj) * 3 * D * D;
-                f = exp_diff(m, lm[jj]) * f + lf[jj];
-                g += lg[jj];
-                h += lh[jj];
-                st[x] = f;
-                st[D * D + x] = g;
-                st[2 * D * D + x] = h;
-                m = lm[jj];
+            for (int jj = 0; jj < kBatch; ++jj) {
+                if (jj < nj) {
+                    float *st = w.segst + (static_cast<size_t>(bh) * (w.nseg - 1) + j0 + jj) * 3 * D * D;
+                    f = exp_diff(m, lm[jj]) * f + lf[jj];
+                    g += lg[jj];
+                    h += lh[jj];
+                    st[x] = f;
+                    st[D * D + x] = g;
+                    st[2 * D * D + x] = h;
+                    m = lm[jj];
+                }
             }
         }
-    }
+    };
+    if (w.nseg <= 5) chain(std::integral_constant<int, 4>{});
+    else chain(std::integral_constant<int, 32>{});
 }
 
 template <int D, typename T, bool ROPE>

@@ -164,9 +164,10 @@ zeros_status zeros_fwd_causal_noalloc(const zeros_shape *shape,
  * N u's, and the coefficients use t = N with the gates of token t. Writes o [B, H, N, d].
  * workspace: device scratch of zeros_fwd_encoder_workspace_bytes(shape) bytes, 256-byte aligned,
  *   owned by the caller and used only while the call's work runs on `stream`. Only bfloat16
- *   calls with d 64/128 and N > 4096 need any (4 N d/16 bytes per (b, h): the logits of the
- *   sequence once per 16-column tile); for every other shape it may be NULL. NULL when scratch
- *   is needed is ZEROS_ERR_NULL; too small or not 256-byte aligned is ZEROS_ERR_SHAPE.
+ *   calls with d 64/128 and N > 4096 need any (per (b, h): the logits, u sums per 256 tokens,
+ *   and three float32 d x d partial states per block of 256 to 2048 tokens); for every other
+ *   shape it may be NULL. NULL when scratch is needed is ZEROS_ERR_NULL; too small or not
+ *   256-byte aligned is ZEROS_ERR_SHAPE.
  */
 zeros_status zeros_fwd_encoder(const zeros_shape *shape,
                                const void *q, const void *k, const void *v, const void *u,

@@ -168,19 +168,51 @@ def test_library_never_allocates_scratch(lib):
         assert "workspace is NULL" in lib.zeros_last_error().decode()
     long_bf = shape(B=1, H=1, N=4097, d=64, d_u=64, dtype=1)
     need = lib.zeros_fwd_encoder_workspace_bytes(ctypes.byref(long_bf))
-    assert need == 4 * 4097 * 64 // 16            # the logits per 16-column tile, as float32
+    assert need == long_encoder_ws(1, 1, 4097, 64)
     assert call_encoder(lib, long_bf) == L.ZEROS_ERR_NULL
     assert call_encoder(lib, long_bf, ws=0x7000000, ws_bytes=need - 1) == L.ZEROS_ERR_SHAPE
     assert call_encoder(lib, long_bf, ws=0x7000010, ws_bytes=need) == L.ZEROS_ERR_SHAPE   # misaligned
 
 
-@pytest.mark.parametrize("kw,need", [(dict(N=4096, d=128, d_u=128, dtype=1), 0),           # logits in LDS
-                                     (dict(N=4097, d=128, d_u=128, dtype=1), 4097 * 8 * 4 * 6),
-                                     (dict(N=9000, d=64, d_u=64, dtype=1), 9000 * 4 * 4 * 6),
-                                     (dict(N=9000, d=64, d_u=64, dtype=0), 0),             # float32 kernel
-                                     (dict(N=9000, d=32, d_u=32, dtype=1), 0)])            # VALU kernel
+def long_encoder_ws(B, H, N, d):
+    """Scratch of the token-parallel long encoder: per (b, h) the u sums of the 256-token blocks,
+    the logits, and per state block (256 spb tokens, spb a power of two <= 8 that keeps about 512
+    workgroups) its (max, sum, sum) and three float32 d x d partial states, then three bf16 states;
+    each region rounded up to 256 bytes."""
+    up = lambda x: (x + 255) // 256 * 256
+    bh, nblk = B * H, (N + 255) // 256
+    spb = 1
+    while spb < 8 and bh * ((nblk + 2 * spb - 1) // (2 * spb)) >= 512:
+        spb *= 2
+    nsb = (nblk + spb - 1) // spb
+    return (up(bh * nblk * d * 4) + up(bh * N * 4) + up(bh * nsb * 16) + up(bh * nsb * 3 * d * d * 4)
+            + up(bh * 3 * d * d * 2))
+
+
+def test_long_encoder_plan_sizes():
+    """The state blocks grow while the grid keeps about 512 workgroups: 64 heads of 8192 tokens
+    take 1024-token blocks (8 per head), one head keeps 256-token blocks."""
+    d = 64
+    part = 3 * d * d * 4
+    assert long_encoder_ws(8, 8, 8192, d) == 64 * 32 * d * 4 + 64 * 8192 * 4 + 64 * 8 * 16 + 64 * 8 * part + 64 * 3 * d * d * 2
+    assert long_encoder_ws(1, 1, 8192, d) == 32 * d * 4 + 8192 * 4 + 512 + 32 * part + 3 * d * d * 2
+
+
+@pytest.mark.parametrize("kw,need", [
+    (dict(B=2, H=3, N=767, d=128, d_u=128, dtype=1), 0),                     # one launch, logits in LDS
+    (dict(B=2, H=3, N=768, d=128, d_u=128, dtype=1), long_encoder_ws(2, 3, 768, 128)),
+    (dict(B=2, H=3, N=4097, d=128, d_u=128, dtype=1), long_encoder_ws(2, 3, 4097, 128)),
+    (dict(B=2, H=3, N=9000, d=64, d_u=64, dtype=1), long_encoder_ws(2, 3, 9000, 64)),
+    (dict(B=96, H=4, N=256, d=64, d_u=64, dtype=1), 0),                      # per-head variant
+    (dict(B=96, H=4, N=257, d=64, d_u=64, dtype=1), long_encoder_ws(96, 4, 257, 64)),   # B H N d >= 96 Ki x 64
+    (dict(B=64, H=4, N=300, d=64, d_u=64, dtype=1), 0),                      # B H N d < 96 Ki x 64
+    (dict(B=32, H=4, N=400, d=128, d_u=128, dtype=1), long_encoder_ws(32, 4, 400, 128)),
+    (dict(B=2, H=3, N=9000, d=64, d_u=64, dtype=0), 0),                      # float32 kernel
+    (dict(B=2, H=3, N=9000, d=32, d_u=32, dtype=1), 0)])                     # VALU kernel
 def test_encoder_workspace_bytes(lib, kw, need):
-    assert lib.zeros_fwd_encoder_workspace_bytes(ctypes.byref(shape(B=2, H=3, **kw))) == need
+    """bfloat16 d 64/128 encoders take the token-parallel pipeline (and need scratch) from 768
+    tokens, or from 257 tokens once q holds 96 Ki x 64 elements."""
+    assert lib.zeros_fwd_encoder_workspace_bytes(ctypes.byref(shape(**kw))) == need
 
 
 def test_noalloc_rejects_oversize_on_the_host(lib):

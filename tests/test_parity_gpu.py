@@ -303,7 +303,7 @@ def test_encoder_shapes(d, N, dtype, rope):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("N", [64, 65, 128, 129, 255, 300, 1000])
+@pytest.mark.parametrize("N", [64, 65, 128, 129, 255, 300, 700])
 @pytest.mark.parametrize("rope", [False, True])
 def test_encoder_mfma_chunks(d, N, rope):
     """bfloat16 encoder on the matrix cores: several 64-token state chunks and 16-token output
@@ -318,11 +318,11 @@ def test_encoder_mfma_chunks(d, N, rope):
     assert err <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("d,N", [(64, 256), (64, 257), (128, 4096), (128, 4097), (64, 9000)])
+@pytest.mark.parametrize("d,N", [(64, 256), (64, 257), (128, 767), (128, 768), (64, 9000)])
 def test_encoder_length_boundaries(d, N):
-    """Sequence lengths at the edges of the encoder's variants: 256 / 257 tokens (small and large
-    LDS logits buffer), 4096 (the longest with the logits in LDS), 4097 and 9000 (logits in global
-    scratch)."""
+    """Sequence lengths at the edges of the encoder's variants: 256 / 257 tokens (per-head variant
+    and the tile variant), 767 (the longest in one launch, logits in LDS), 768 and 9000 (the
+    token-parallel pipeline with its scratch)."""
     wl = CONFIGS[3].with_(B=1, H=2, N=N, d=d, d_u=d, dtype="bf16", seed=3100 + d + N)
     x = make_inputs(wl)
     o = to_f64(run_encoder(x, "bf16", rope=True))
@@ -330,6 +330,41 @@ def test_encoder_length_boundaries(d, N):
     err = rel_l2(o, ref)
     print(f"encoder d={d} N={N} rel_l2={err:.3e}", flush=True)
     assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("B,H,N,d,rope,gate0", [
+    (1, 2, 4097, 64, False, False),     # last 256-token block holds one token
+    (1, 2, 5000, 128, True, True),      # d = 128 with the zero-order gate (three states)
+    (8, 8, 4500, 64, False, True),      # 64 heads: 512-token state blocks, the last one ragged
+    (4, 8, 8192, 64, True, False),      # 32 heads: 512-token state blocks, 16 per head
+    (2, 3, 6001, 128, False, False),    # d = 128, ragged tail inside an output block
+    (96, 4, 300, 64, True, False),      # short sequences in a large batch: two 256-token blocks
+    (1, 2, 768, 128, False, True),      # the shortest sequence that takes the pipeline on its own
+])
+def test_encoder_long_blocks(B, H, N, d, rope, gate0):
+    """bfloat16 encoder on the token-parallel pipeline (u sums, logits per state block, partial
+    states, their reduction, outputs): one and several 256-token spans per state block, ragged state
+    and output blocks, RoPE and the zero-order gate."""
+    wl = CONFIGS[3].with_(B=B, H=H, N=N, d=d, d_u=d, dtype="bf16", seed=3200 + B * H + N + d)
+    x = make_inputs(wl, gate0=gate0)
+    t = to_device(x, "bf16")
+    o = Z.zeros_fwd_encoder(t["q"], t["k"], t["v"], t["u"], t["mu"], t["tau"], t["g1"], t["gh"],
+                            g0=t["g0"] if gate0 else None, rope=rope)
+    torch.cuda.synchronize()
+    err = rel_l2(to_f64(o), R.encoder_forward(**x, rope=rope))
+    print(f"encoder long B={B} H={H} N={N} d={d} rope={rope} gate0={gate0} rel_l2={err:.3e}", flush=True)
+    assert err <= TOL["bf16"]
+
+
+def test_encoder_long_large_logits():
+    """u scaled by 60 at N = 6000: the logits span about 300 (beyond the float32 exponent range of
+    e^{+-88}), so the state blocks' (max, sum e^{s - max}) must be merged by rescaling to the
+    global maximum, with the far-below blocks underflowing to zero weight."""
+    wl = CONFIGS[3].with_(B=1, H=2, N=6000, d=64, d_u=64, dtype="bf16", seed=3998)
+    x = make_inputs(wl, u_scale=60.0)
+    o = to_f64(run_encoder(x, "bf16"))
+    assert np.all(np.isfinite(o))
+    assert rel_l2(o, R.encoder_forward(**x)) <= TOL["bf16"]
 
 
 @pytest.mark.parametrize("N", [200, 300])

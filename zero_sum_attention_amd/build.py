@@ -23,6 +23,7 @@ SOURCES = [
     "zeros_api.cpp",
     "causal_valu.hip",
     "causal_f32.hip",
+    "encoder_long.hip",
     "causal_mfma.hip",
     "sm_causal.hip",
     "logits.hip",

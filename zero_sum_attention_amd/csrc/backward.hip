@@ -764,7 +764,7 @@ hipError_t launch_bwd(const Problem &p, const BwdGrads &g, const BwdWork &w, hip
     const int nls = (N + kLogitSeg - 1) / kLogitSeg;
     hipError_t err;
     if (N > 0) {
-        err = launch_logits(p, w.useg, w.s, w.agg, nullptr, stream);
+        err = launch_logits(p, w.useg, w.s, w.agg, stream);
         if (err != hipSuccess) return err;
         const int nblk = (N + 63) / 64;
         hipLaunchKernelGGL((bwd_scalar_kernel<T>), dim3(BH * nblk), dim3(64), 0, stream, p, w);

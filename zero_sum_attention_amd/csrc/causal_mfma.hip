@@ -212,16 +212,6 @@ __device__ __forceinline__ void piece_tb_pi(int piece, int &tb, int &pi) {
 __device__ __forceinline__ void st16(unsigned char *p, const bf16x8 &v) { *reinterpret_cast<bf16x8 *>(p) = v; }
 __device__ __forceinline__ bf16x8 ld16(const unsigned char *p) { return *reinterpret_cast<const bf16x8 *>(p); }
 
-// Transposing LDS read (ds_read_b64_tr_b16): every lane names 8 bytes (4 bfloat16), and within each
-// group of 16 lanes, lane i receives element i & 3 of the 8 bytes named by lanes 4 e + (i >> 2),
-// e = 0 .. 3 (measured layout). Four lanes naming 16 consecutive features of four rows thus give
-// each lane its feature of the four rows.
-__device__ __forceinline__ uint2 lds_tr16(const uint16_t *p) {
-    typedef short v4s __attribute__((ext_vector_type(4)));
-    const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(p));
-    return __builtin_bit_cast(uint2, r);
-}
-
 // ---- segment-parallel scan ----------------------------------------------------------------
 //
 // The chunks of a head are cut into nseg segments of seg_chunks chunks. One workgroup of D/16 waves
@@ -927,7 +917,7 @@ CausalWork causal_work_carve(void *base, int B, int H, int N, int du) {
 }
 
 hipError_t launch_causal_mfma(const Problem &p, const CausalWork &w, hipStream_t stream) {
-    hipError_t err = launch_logits(p, w.useg, w.s, w.agg, nullptr, stream);
+    hipError_t err = launch_logits(p, w.useg, w.s, w.agg, stream);
     if (err != hipSuccess) return err;
     if (p.d == 128) return p.rope ? launch_one<128, true>(p, w, stream) : launch_one<128, false>(p, w, stream);
     if (p.d == 64) return p.rope ? launch_one<64, true>(p, w, stream) : launch_one<64, false>(p, w, stream);

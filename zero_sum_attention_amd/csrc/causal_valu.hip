@@ -659,7 +659,7 @@ hipError_t launch_valu_combine(const Problem &p, const ValuWork &w, hipStream_t 
 }
 
 hipError_t launch_causal_valu(const Problem &p, const ValuWork &w, hipStream_t stream) {
-    hipError_t err = launch_logits(p, w.useg, w.s, w.agg, nullptr, stream);
+    hipError_t err = launch_logits(p, w.useg, w.s, w.agg, stream);
     if (err != hipSuccess) return err;
     // float32 with d 64 or 128: the per-head kernel (a bfloat16 call reaches this path only as a copy
     // of the state with N = 0, which the per-tile kernel does)

@@ -10,6 +10,9 @@
 // keep the uniform term) adds (sigma0_t/N) q^_t H with H = sum_i k^_i^T v_i, a third state
 // (the G0 instances).
 //
+// Sequences that encoder_long_path selects (from kEncoderTileMaxN tokens, or large batches) take the
+// token-parallel pipeline of encoder_long.hip instead; this file holds the single-launch variants.
+//
 // One workgroup of 4 waves per (batch, head, 16-column tile of the value dimension): d/16 workgroups
 // per head, each computing its tile's columns of X and Y and of the output.
 //   A: column sums of u -> ubar; logits s_i (lanes of a token row reduce their partial dots), each
@@ -22,6 +25,7 @@
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "mfma_common.hpp"
+#include "encoder_common.hpp"
 
 namespace zeros {
 namespace {
@@ -35,57 +39,9 @@ constexpr int kEPad = 8;           // bf16 elements of row padding in LDS
 template <int D>
 __device__ __forceinline__ float row_sum(float x) { return group_sum<D / 8>(x); }
 
-// (max, sum e^{s - max}) of two parts merged; a max of -inf marks an empty part.
-__device__ __forceinline__ void lse_merge(float &m, float &e, float m2, float e2) {
-    const float mm = fmaxf(m, m2);
-    e = (m == kNegInf ? 0.f : e * __expf(m - mm)) + (m2 == kNegInf ? 0.f : e2 * __expf(m2 - mm));
-    m = mm;
-}
-
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
-}
-
-// (max, sum e^{s - max}, sum s) merged over the 64 lanes of a wave; every lane gets the result.
-// Within a row of 16 lanes the partners come by DPP (the pairings of group_sum), then the four row
-// results by readlane.
-__device__ __forceinline__ void wave_lse_merge(float &m, float &e, float &ps) {
-    lse_merge(m, e, dpp_mov<kQuadXor1>(m), dpp_mov<kQuadXor1>(e));
-    ps += dpp_mov<kQuadXor1>(ps);
-    lse_merge(m, e, dpp_mov<kQuadXor2>(m), dpp_mov<kQuadXor2>(e));
-    ps += dpp_mov<kQuadXor2>(ps);
-    lse_merge(m, e, dpp_mov<kRowHalfMirror>(m), dpp_mov<kRowHalfMirror>(e));
-    ps += dpp_mov<kRowHalfMirror>(ps);
-    lse_merge(m, e, dpp_mov<kRowMirror>(m), dpp_mov<kRowMirror>(e));
-    ps += dpp_mov<kRowMirror>(ps);
-    float M = lane_f(m, 0), E = lane_f(e, 0), P = lane_f(ps, 0);
-#pragma unroll
-    for (int r = 16; r < 64; r += 16) {
-        lse_merge(M, E, lane_f(m, r), lane_f(e, r));
-        P += lane_f(ps, r);
-    }
-    m = M;
-    e = E;
-    ps = P;
-}
-
-// float -> bfloat16 bits (round to nearest even)
-__device__ __forceinline__ uint16_t bf16_bits(float x) { return static_cast<uint16_t>(pack2(x, 0.f) & 0xffffu); }
-
-__device__ __forceinline__ void unpack8(const uint4 &x, float (&f)[8]) {
-    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        f[2 * i] = lo_f(w[i]);
-        f[2 * i + 1] = hi_f(w[i]);
-    }
-}
-
-// NMAX > 0: the logits of the sequence stay in LDS (N <= NMAX); NMAX = 0: any N, the logits go to
-// sg, a global scratch region per (column tile, head) that only this workgroup writes and reads.
+// The logits of the sequence stay in LDS (N <= NMAX).
 template <int D, bool ROPE, int NMAX, bool G0>
-__global__ __launch_bounds__(kEThreads) void encoder_mfma_kernel(Problem p, float *sg) {
+__global__ __launch_bounds__(kEThreads) void encoder_mfma_kernel(Problem p) {
     constexpr int NS = G0 ? 3 : 2;     // states: X, Y (and H)
     constexpr int FT = D / 16;         // 16-row feature tiles of a state
     constexpr int FW = FT / 4;         // feature tiles per wave
@@ -94,7 +50,7 @@ __global__ __launch_bounds__(kEThreads) void encoder_mfma_kernel(Problem p, floa
     constexpr int RPP = kEThreads / LPR;   // token rows per pass
     __shared__ float ubar[D];
     __shared__ __align__(16) float colp[RPP][D];          // partial column sums of u, one row per token row of a pass
-    __shared__ float sl_lds[NMAX > 0 ? NMAX : 1];   // logits of the sequence (N <= NMAX)
+    __shared__ float sl[NMAX];                      // logits of the sequence (N <= NMAX)
     __shared__ float4 red[kEThreads / 64];
     __shared__ __align__(16) uint16_t kt[D][kEC + kEPad];    // k^ of the chunk, transposed
     __shared__ __align__(16) uint16_t vxt[16][kEC + kEPad];  // this tile's columns of v w_X, transposed
@@ -122,7 +78,6 @@ __global__ __launch_bounds__(kEThreads) void encoder_mfma_kernel(Problem p, floa
     const uint16_t *g0 = G0 ? static_cast<const uint16_t *>(p.g0) + row0 : nullptr;
     uint16_t *o = static_cast<uint16_t *>(p.o) + row0 * D;
     const float et = expf(p.tau[h]);
-    float *sl = NMAX > 0 ? sl_lds : sg + (static_cast<size_t>(ct) * bhn + bh) * N;
     const int fr = tid % LPR, rr = tid / LPR;       // feature group (8 features) and row of a pass
     if (ROPE && tid < D / 2) rev[tid] = rope_rev_per_pos(tid, D, p.rope_base);   // ordered by the first barrier
 
@@ -236,7 +191,7 @@ __global__ __launch_bounds__(kEThreads) void encoder_mfma_kernel(Problem p, floa
     // block reduction of (max, sum e^{s - max}, sum s): in each wave, then across the waves
     wave_lse_merge(mloc, eloc, ploc);
     if (lane == 0) red[w] = make_float4(mloc, eloc, ploc, 0.f);
-    __syncthreads();                           // also orders the logits (LDS or sg) before phase B
+    __syncthreads();                           // also orders the logits before phase B
     float M = kNegInf, E = 0.f, P = 0.f;
 #pragma unroll
     for (int i = 0; i < kEThreads / 64; ++i) {
@@ -423,12 +378,6 @@ constexpr int kEHThreads = 1024;
 // for two rows at once would spill)
 constexpr int kEHalf = 256;
 template <bool ROPE> constexpr int eh_round() { return ROPE ? 128 : kEHalf; }
-
-// Token column of row f in the transposed staging buffers of the per-head variant: bits 3-5 of the
-// token index XOR the row's 8-row group, so that the 8 feature groups of a staging write land in
-// different banks (rows 8 apart are 544 words apart, the same bank) while each 8-token group stays
-// contiguous for the 16-byte MFMA operand reads.
-__device__ __forceinline__ int eh_col(int f, int tok) { return tok ^ (((f >> 3) & 7) << 3); }
 
 template <int D, bool G0>
 union EHeadBuf {
@@ -739,7 +688,7 @@ __global__ __launch_bounds__(kEHThreads) void encoder_head_kernel(Problem p) {
 }
 
 template <int D, bool ROPE, bool G0>
-hipError_t launch_g(const Problem &p, float *work, hipStream_t stream) {
+hipError_t launch_g(const Problem &p, hipStream_t stream) {
     const dim3 grid((D / 16) * p.B * p.H);
     // short sequences at d = 64: the per-head variant (N >= 1: the front end returns before a launch
     // for N = 0). At d = 128 it would need more than the 128 registers a wave has at 16 waves per CU.
@@ -750,31 +699,25 @@ hipError_t launch_g(const Problem &p, float *work, hipStream_t stream) {
         }
     }
     if (p.N <= kEShortN) {
-        hipLaunchKernelGGL((encoder_mfma_kernel<D, ROPE, kEShortN, G0>), grid, dim3(kEThreads), 0, stream, p, nullptr);
+        hipLaunchKernelGGL((encoder_mfma_kernel<D, ROPE, kEShortN, G0>), grid, dim3(kEThreads), 0, stream, p);
         return hipGetLastError();
     }
-    if (p.N <= kEncoderMfmaMaxN) {
-        hipLaunchKernelGGL((encoder_mfma_kernel<D, ROPE, kEncoderMfmaMaxN, G0>), grid, dim3(kEThreads), 0, stream, p,
-                           nullptr);
-        return hipGetLastError();
-    }
-    // longer sequences: the logits in the caller's scratch, one region of N floats per workgroup
-    // (encoder_work_bytes; validated by the front end)
-    if (work == nullptr) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((encoder_mfma_kernel<D, ROPE, 0, G0>), grid, dim3(kEThreads), 0, stream, p, work);
+    // (longer sequences take encoder_long.hip: encoder_long_path)
+    if (p.N >= kEncoderTileMaxN) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((encoder_mfma_kernel<D, ROPE, kEncoderTileMaxN, G0>), grid, dim3(kEThreads), 0, stream, p);
     return hipGetLastError();
 }
 
 template <int D, bool ROPE>
-hipError_t launch_one(const Problem &p, float *work, hipStream_t stream) {
-    return p.g0 != nullptr ? launch_g<D, ROPE, true>(p, work, stream) : launch_g<D, ROPE, false>(p, work, stream);
+hipError_t launch_one(const Problem &p, hipStream_t stream) {
+    return p.g0 != nullptr ? launch_g<D, ROPE, true>(p, stream) : launch_g<D, ROPE, false>(p, stream);
 }
 
 }  // namespace
 
-hipError_t launch_encoder_mfma(const Problem &p, float *work, hipStream_t stream) {
-    if (p.d == 128) return p.rope ? launch_one<128, true>(p, work, stream) : launch_one<128, false>(p, work, stream);
-    if (p.d == 64) return p.rope ? launch_one<64, true>(p, work, stream) : launch_one<64, false>(p, work, stream);
+hipError_t launch_encoder_mfma(const Problem &p, hipStream_t stream) {
+    if (p.d == 128) return p.rope ? launch_one<128, true>(p, stream) : launch_one<128, false>(p, stream);
+    if (p.d == 64) return p.rope ? launch_one<64, true>(p, stream) : launch_one<64, false>(p, stream);
     return hipErrorInvalidValue;
 }
 

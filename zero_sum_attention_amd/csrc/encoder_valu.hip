@@ -269,12 +269,11 @@ static bool encoder_uses_mfma(const Problem &p) {
 }
 
 size_t encoder_work_bytes(const Problem &p) {
-    if (!encoder_uses_mfma(p) || p.N <= kEncoderMfmaMaxN) return 0;
-    return static_cast<size_t>(p.d / 16) * p.B * p.H * p.N * sizeof(float);
+    return encoder_uses_mfma(p) && encoder_long_path(p) ? encoder_long_work_bytes(p) : 0;
 }
 
 hipError_t launch_encoder(const Problem &p, void *work, hipStream_t stream) {
-    if (encoder_uses_mfma(p)) return launch_encoder_mfma(p, static_cast<float *>(work), stream);
+    if (encoder_uses_mfma(p)) return encoder_long_path(p) ? launch_encoder_long(p, work, stream) : launch_encoder_mfma(p, stream);
     switch (p.d) {
         case 16: return launch_d<16>(p, stream);
         case 32: return launch_d<32>(p, stream);

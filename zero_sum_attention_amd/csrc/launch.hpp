@@ -71,18 +71,31 @@ hipError_t launch_causal_valu(const Problem &p, const ValuWork &w, hipStream_t s
 hipError_t launch_valu_combine(const Problem &p, const ValuWork &w, hipStream_t stream);
 hipError_t launch_causal_f32(const Problem &p, const ValuWork &w, hipStream_t stream);
 
-// Logits of the causal paths; when rope_tab is not null it also fills the in-chunk RoPE angle
-// table [kCausalChunk, d/2] (cos, sin of r * theta_j) used by the prep kernel.
-hipError_t launch_logits(const Problem &p, float *useg, float *s_out, float4 *agg, float2 *rope_tab,
-                         hipStream_t stream);
+// Logits of the causal paths: s [B*H, N], the u sums per 256-token segment and the 64-token
+// (max, sum e^{s - max}, sum s) aggregates.
+hipError_t launch_logits(const Problem &p, float *useg, float *s_out, float4 *agg, hipStream_t stream);
+// Column sums of u per 256-token segment alone [B*H, ceil(N/256), d] (d 64 or 128).
+hipError_t launch_usum(const Problem &p, float *useg, hipStream_t stream);
 hipError_t launch_causal_mfma(const Problem &p, const CausalWork &w, hipStream_t stream);
 // Encoder: `work` is caller scratch of encoder_work_bytes(p) bytes (NULL when that is 0).
 hipError_t launch_encoder(const Problem &p, void *work, hipStream_t stream);
-// Matrix-core encoder for bfloat16, d in {64, 128}: the logits stay in LDS up to kEncoderMfmaMaxN
-// tokens, beyond that in the caller's scratch (4 N bytes per (b, h, 16-column tile)).
-constexpr int kEncoderMfmaMaxN = 4096;
+// Matrix-core encoder for bfloat16, d in {64, 128}. Sequences of up to 256 tokens, and those below
+// kEncoderTileMaxN tokens while q holds fewer than kEncoderLongElems elements, run in one launch
+// (encoder_mfma.hip: one workgroup per head, or per (head, 16-column tile) with the logits in LDS).
+// The others take the token-parallel pipeline of encoder_long.hip: five launches over (head, block
+// of tokens), whose scratch is encoder_long_work_bytes(p) bytes. (Measured crossover: the single
+// launch repeats its logits pass per column tile and has few workgroups per head, the pipeline
+// costs about 20 us of launches.)
+constexpr int kEncoderTileMaxN = 768;
+constexpr long kEncoderLongElems = 6291456;     // 96 Ki tokens at d = 64
+inline bool encoder_long_path(const Problem &p) {
+    return p.N > 256 &&
+           (p.N >= kEncoderTileMaxN || static_cast<long>(p.B) * p.H * p.N * p.d >= kEncoderLongElems);
+}
 size_t encoder_work_bytes(const Problem &p);
-hipError_t launch_encoder_mfma(const Problem &p, float *work, hipStream_t stream);
+size_t encoder_long_work_bytes(const Problem &p);
+hipError_t launch_encoder_long(const Problem &p, void *work, hipStream_t stream);
+hipError_t launch_encoder_mfma(const Problem &p, hipStream_t stream);
 hipError_t launch_decode(const Problem &p, hipStream_t stream);
 
 // ZeroS-SM, the zero-sum reweighting of standard causal softmax attention (sm_causal.hip):

@@ -58,8 +58,7 @@ __device__ __forceinline__ void load4<float>(const float *p, float (&x)[4]) {
 
 // Column sums of u over one segment: 8 consecutive features per thread, rows strided.
 template <int D, typename T>
-__global__ __launch_bounds__(kThreads) void useg_sum_kernel(const T *u, float *useg, int N, int nseg,
-                                                            float2 *rope_tab, float rope_base) {
+__global__ __launch_bounds__(kThreads) void useg_sum_kernel(const T *u, float *useg, int N, int nseg) {
     constexpr int VPR = D / 8;                 // threads per row
     constexpr int RPI = kThreads / VPR;        // rows per iteration
     __shared__ float part[RPI][D + 1];
@@ -69,29 +68,21 @@ __global__ __launch_bounds__(kThreads) void useg_sum_kernel(const T *u, float *u
     const int c0 = (tid % VPR) * 8, rg = tid / VPR;
     const int r0 = seg * kLogitSeg, r1 = min(N, r0 + kLogitSeg);
     const T *ub = u + static_cast<size_t>(bh) * N * D;
-    if (rope_tab != nullptr) {           // the RoPE angle table of the prep kernel, spread over the grid
-        for (int e = blockIdx.x * kThreads + tid; e < kCausalChunk * (D / 2); e += gridDim.x * kThreads) {
-            float c, sn;
-            rope_cos_sin(rope_rev_per_pos(e % (D / 2), D, rope_base), e / (D / 2), c, sn);
-            rope_tab[e] = make_float2(c, sn);
-        }
-    }
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    constexpr int U = 8;                       // rows in flight per thread
+    // rows in flight per thread: the whole segment in one pass where the registers allow it. The
+    // loads are unconditional (row index clamped, the extra rows not added): a load under a
+    // per-row condition would wait for each row on its own.
+    constexpr int U = kLogitSeg / RPI < (sizeof(T) == 2 ? 16 : 8) ? kLogitSeg / RPI : (sizeof(T) == 2 ? 16 : 8);
     for (int rb = r0 + rg; rb < r1; rb += U * RPI) {
         float x[U][8];
 #pragma unroll
+        for (int k = 0; k < U; ++k) load8(ub + static_cast<size_t>(min(rb + k * RPI, r1 - 1)) * D + c0, x[k]);
+#pragma unroll
         for (int k = 0; k < U; ++k) {
-            const int r = rb + k * RPI;
-            if (r < r1) load8(ub + static_cast<size_t>(r) * D + c0, x[k]);
-            else
+            const bool ok = rb + k * RPI < r1;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) x[k][i] = 0.f;
+            for (int i = 0; i < 8; ++i) acc[i] += ok ? x[k][i] : 0.f;
         }
-#pragma unroll
-        for (int k = 0; k < U; ++k)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] += x[k][i];
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) part[rg][c0 + i] = acc[i];
@@ -328,12 +319,149 @@ __global__ __launch_bounds__(kStreamThreads, 4) void logits_stream_kernel(const 
     }
 }
 
+// Logits of a short sequence (N <= lh_max_n<D>()) in one pass over u: one workgroup of 1024 threads
+// per head. Thread (feature group fg of 4 features, token block tb of TB tokens) reads its TB rows
+// once; the block totals go through LDS for an exclusive prefix over the blocks (each thread adds 4
+// block totals, then the parts before it), which gives every thread the running sum at its first
+// token; the per-token dots are summed over the FG lanes of a row by DPP. The 256-token segment sums
+// and the 64-token (max, sum e^{s - max}, sum s) aggregates come from the same data. The token
+// blocks are fixed (TB per d), so the grouping, and the rounding, do not depend on N.
+constexpr int kLHThreads = 1024;
+template <int D> __host__ __device__ constexpr int lh_tb() { return D == 16 ? 4 : D == 32 ? 8 : 16; }
+template <int D> __host__ __device__ constexpr int lh_max_n() { return kLHThreads / (D / 4) * lh_tb<D>(); }
+
 template <int D, typename T>
-hipError_t launch_t(const Problem &p, float *useg, float *s_out, float4 *agg, float2 *rope_tab, hipStream_t stream) {
+__global__ __launch_bounds__(kLHThreads) void logits_head_kernel(const T *u, const float *mu, const float *tau,
+                                                                 float *useg, float *s_out, float4 *agg, int N,
+                                                                 int H, int nseg, const float *su_in,
+                                                                 const int *t_in) {
+    constexpr int FG = D / 4;              // feature groups = threads per token row
+    constexpr int TBN = kLHThreads / FG;   // token blocks
+    constexpr int TB = lh_tb<D>();         // tokens per block
+    constexpr int P = kLHThreads / D;      // parts of the block prefix per feature (4 blocks each)
+    static_assert(TBN == 4 * P && 64 % TB == 0 && kLogitSeg % TB == 0, "per-head logits shape");
+    __shared__ float colp[TBN][D];         // block totals, then their exclusive prefix
+    __shared__ float psum[P][D];           // totals of 4 blocks
+    __shared__ float4 aggp[TBN];           // (max, sum e^{s - max}, sum s) of each block
+    // (the barriers order LDS only: a full barrier would also wait for the logit and u-sum stores)
+    const int bh = blockIdx.x, h = bh % H;
+    const int tid = threadIdx.x, fg = tid % FG, tb = tid / FG;
+    const T *ub = u + static_cast<size_t>(bh) * N * D;
+    const int t0 = tb * TB;
+    float x[TB][4];
+#pragma unroll
+    for (int k = 0; k < TB; ++k) {
+        const int t = t0 + k;
+        float y[4];
+        load4(ub + static_cast<size_t>(min(t, N - 1)) * D + 4 * fg, y);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[k][i] = t < N ? y[i] : 0.f;
+    }
+    float tot[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < TB; ++k)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tot[i] += x[k][i];
+    *reinterpret_cast<float4 *>(&colp[tb][4 * fg]) = make_float4(tot[0], tot[1], tot[2], tot[3]);
+    lds_barrier();
+    {
+        // thread (f, part): blocks 4 part .. 4 part + 3 of feature f
+        const int f = tid % D, part = tid / D;
+        float a[4], run = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            a[e] = colp[4 * part + e][f];
+            run += a[e];
+        }
+        psum[part][f] = run;
+        lds_barrier();
+        float pre = 0.f;
+        for (int q = 0; q < part; ++q) pre += psum[q][f];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            colp[4 * part + e][f] = pre;      // exclusive prefix of block 4 part + e
+            pre += a[e];
+        }
+        // u sums of the 256-token segments: the prefix difference at their block boundaries
+        lds_barrier();
+        if (part < nseg) {
+            constexpr int BPS = kLogitSeg / TB;            // blocks per segment
+            const int b0 = part * BPS, b1 = b0 + BPS;
+            float hi = 0.f;
+            if (b1 < TBN) hi = colp[b1][f];
+            else                                            // the prefix past the last block: all of it
+                for (int q = 0; q < P; ++q) hi += psum[q][f];
+            useg[(static_cast<size_t>(bh) * nseg + part) * D + f] = hi - colp[b0][f];
+        }
+    }
+    // logits of this thread's tokens
+    const float et = expf(tau[h]);
+    const float tprev = t_in != nullptr ? static_cast<float>(t_in[bh]) : 0.f;
+    float run[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int f = 4 * fg + i;
+        run[i] = et * mu[h * D + f] + (su_in != nullptr ? su_in[static_cast<size_t>(bh) * D + f] : 0.f) + colp[tb][f];
+    }
+    const float rs_du = 1.f / sqrtf(static_cast<float>(D));
+    float m = kNegInf, ps = 0.f;
+    float sv[TB];
+#pragma unroll
+    for (int k = 0; k < TB; ++k) {
+        const int t = t0 + k;
+        const float inv = 1.f / (et + tprev + static_cast<float>(t + 1));
+        float dot = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            run[i] += x[k][i];
+            dot += x[k][i] * (run[i] * inv);
+        }
+        dot = group_sum<FG>(dot);
+        sv[k] = -dot * rs_du;
+        if (t < N) {
+            if (fg == 0) s_out[static_cast<size_t>(bh) * N + t] = sv[k];
+            m = fmaxf(m, sv[k]);
+            ps += sv[k];
+        }
+    }
+    float e = 0.f;
+#pragma unroll
+    for (int k = 0; k < TB; ++k)
+        if (t0 + k < N) e += __expf(sv[k] - m);
+    if (fg == 0) aggp[tb] = make_float4(m, e, ps, 0.f);
+    lds_barrier();
+    // 64-token aggregates: 64 / TB blocks each
+    const int nb64 = (N + 63) / 64;
+    if (tid < nb64) {
+        float M = kNegInf, E = 0.f, Ps = 0.f;
+#pragma unroll
+        for (int j = 0; j < 64 / TB; ++j) {
+            const float4 a = aggp[tid * (64 / TB) + j];
+            const float mx = fmaxf(M, a.x);
+            E = (M == kNegInf ? 0.f : E * __expf(M - mx)) + (a.x == kNegInf ? 0.f : a.y * __expf(a.x - mx));
+            M = mx;
+            Ps += a.z;
+        }
+        agg[static_cast<size_t>(bh) * nb64 + tid] = make_float4(M, E, Ps, 0.f);
+    }
+}
+
+template <int D, typename T>
+hipError_t launch_t(const Problem &p, float *useg, float *s_out, float4 *agg, hipStream_t stream) {
     const int nseg = (p.N + kLogitSeg - 1) / kLogitSeg;
+    // short sequences in one pass per head (the float32 path; the bfloat16 matrix-core path keeps
+    // its stream kernel)
+    if constexpr (sizeof(T) == 4) {
+        if (p.N <= lh_max_n<D>()) {
+            hipLaunchKernelGGL((logits_head_kernel<D, T>), dim3(p.B * p.H), dim3(kLHThreads), 0, stream,
+                               static_cast<const T *>(p.u), p.mu, p.tau, useg, s_out, agg, p.N, p.H, nseg,
+                               p.sin.Su, p.sin.t);
+            return hipGetLastError();
+        }
+    }
     const int grid = p.B * p.H * nseg;
     hipLaunchKernelGGL((useg_sum_kernel<D, T>), dim3(grid), dim3(kThreads), 0, stream,
-                       static_cast<const T *>(p.u), useg, p.N, nseg, rope_tab, p.rope_base);
+                       static_cast<const T *>(p.u), useg, p.N, nseg);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     // (a continued sequence passes the state's u-sum and token count, which join the prior)
@@ -350,21 +478,39 @@ hipError_t launch_t(const Problem &p, float *useg, float *s_out, float4 *agg, fl
 }
 
 template <int D>
-hipError_t launch_d(const Problem &p, float *useg, float *s_out, float4 *agg, float2 *rope_tab, hipStream_t stream) {
-    return p.dtype == ZEROS_BF16 ? launch_t<D, bf16>(p, useg, s_out, agg, rope_tab, stream)
-                                 : launch_t<D, float>(p, useg, s_out, agg, rope_tab, stream);
+hipError_t launch_d(const Problem &p, float *useg, float *s_out, float4 *agg, hipStream_t stream) {
+    return p.dtype == ZEROS_BF16 ? launch_t<D, bf16>(p, useg, s_out, agg, stream)
+                                 : launch_t<D, float>(p, useg, s_out, agg, stream);
 }
 
 }  // namespace
 
-hipError_t launch_logits(const Problem &p, float *useg, float *s_out, float4 *agg, float2 *rope_tab,
-                         hipStream_t stream) {
+hipError_t launch_usum(const Problem &p, float *useg, hipStream_t stream) {
+    if (p.N == 0) return hipSuccess;
+    const int nseg = (p.N + kLogitSeg - 1) / kLogitSeg;
+    const dim3 grid(p.B * p.H * nseg);
+    const bool bf = p.dtype == ZEROS_BF16;
+    switch (p.d) {
+        case 64:
+            if (bf) hipLaunchKernelGGL((useg_sum_kernel<64, bf16>), grid, dim3(kThreads), 0, stream, static_cast<const bf16 *>(p.u), useg, p.N, nseg);
+            else hipLaunchKernelGGL((useg_sum_kernel<64, float>), grid, dim3(kThreads), 0, stream, static_cast<const float *>(p.u), useg, p.N, nseg);
+            break;
+        case 128:
+            if (bf) hipLaunchKernelGGL((useg_sum_kernel<128, bf16>), grid, dim3(kThreads), 0, stream, static_cast<const bf16 *>(p.u), useg, p.N, nseg);
+            else hipLaunchKernelGGL((useg_sum_kernel<128, float>), grid, dim3(kThreads), 0, stream, static_cast<const float *>(p.u), useg, p.N, nseg);
+            break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_logits(const Problem &p, float *useg, float *s_out, float4 *agg, hipStream_t stream) {
     if (p.N == 0) return hipSuccess;
     switch (p.d) {
-        case 16: return launch_d<16>(p, useg, s_out, agg, rope_tab, stream);
-        case 32: return launch_d<32>(p, useg, s_out, agg, rope_tab, stream);
-        case 64: return launch_d<64>(p, useg, s_out, agg, rope_tab, stream);
-        case 128: return launch_d<128>(p, useg, s_out, agg, rope_tab, stream);
+        case 16: return launch_d<16>(p, useg, s_out, agg, stream);
+        case 32: return launch_d<32>(p, useg, s_out, agg, stream);
+        case 64: return launch_d<64>(p, useg, s_out, agg, stream);
+        case 128: return launch_d<128>(p, useg, s_out, agg, stream);
         default: return hipErrorInvalidValue;
     }
 }

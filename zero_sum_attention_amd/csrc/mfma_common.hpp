@@ -39,4 +39,14 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, float acc) {
     return __builtin_amdgcn_fdot2_f32_bf16(v, v, acc, false);
 }
 
+// Transposing LDS read (ds_read_b64_tr_b16): every lane names 8 bytes (4 bfloat16), and within each
+// group of 16 lanes, lane i receives element i & 3 of the 8 bytes named by lanes 4 e + (i >> 2),
+// e = 0 .. 3 (measured layout). Four lanes naming 16 consecutive features of four rows thus give
+// each lane its feature of the four rows.
+__device__ __forceinline__ uint2 lds_tr16(const uint16_t *p) {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(p));
+    return __builtin_bit_cast(uint2, r);
+}
+
 }  // namespace zeros

@@ -197,9 +197,10 @@ def _f64(t) -> np.ndarray:
 def secondary(dev, oracle: dict, cores: int, steps: int = 20) -> list:
     """The other hot-path calls at their workload sizes, each with its parity against the oracle where
     one ran: the float32 LM-layer causal forward, a long float32 sequence on two heads (segmented
-    scan), the ViT-shaped encoder, one decode step of 256 sequences x 32 heads at t = 8192, the
-    headline with the zero-order gate, the headline as four chained calls of a quarter each (chunked
-    prefill through state_in / state_out) and the backward of the headline call."""
+    scan), the ViT-shaped encoder, a long encoder (64 heads x 8192 tokens), one decode step of 256
+    sequences x 32 heads at t = 8192, the headline with the zero-order gate, the headline as four
+    chained calls of a quarter each (chunked prefill through state_in / state_out) and the backward
+    of the headline call."""
     import torch
 
     import zero_sum_attention_amd as Z
@@ -277,6 +278,35 @@ def secondary(dev, oracle: dict, cores: int, steps: int = 20) -> list:
     out.append(ent)
     log(f"secondary {wl.name}: {ms:.4f} ms")
     del t, o, ws
+
+    # a long encoder sequence over many heads: the token-parallel encoder pipeline, parity sampled
+    # on two heads (the heads of an encoder are independent)
+    wl = CONFIGS[3].with_(B=8, H=8, N=8192, seed=23)
+    x = make_inputs(wl)
+    t = _dev_inputs(x, wl.dtype, dev)
+    o = torch.empty_like(t["v"])
+    ws = torch.empty(max(1, Z.zeros_fwd_encoder_workspace_bytes(wl.B, wl.H, wl.N, wl.d, wl.d_u, torch.bfloat16)),
+                     dtype=torch.uint8, device=dev)
+    ms_binding = _timed(dev, lambda st: Z.zeros_fwd_encoder(t["q"], t["k"], t["v"], t["u"], t["mu"], t["tau"],
+                                                            t["g1"], t["gh"], out=o, workspace=ws, stream=st), steps)
+    ms = _timed(dev, _c_call("zeros_fwd_encoder", t, o, ws, False, torch.cuda.current_stream(dev), wl.N), steps)
+    nbytes = algorithmic_bytes(wl)
+    ent = {"workload": "long-encoder-B8H8N8192d64", "call": "zeros_fwd_encoder", "dtype": "bf16", "ms": ms,
+           "ms_binding": ms_binding, "tokens_per_s": wl.B * wl.N / (ms * 1e-3), "algorithmic_bytes": nbytes,
+           "achieved_GBs": nbytes / (ms * 1e-3) / 1e9, "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    if oracle:
+        from oracle import zeros_ref as R
+        got = _f64(o)
+        errs = []
+        for (b, h) in ((0, 0), (wl.B - 1, wl.H - 1)):
+            ref = R.encoder_forward(x["q"][b:b + 1, h:h + 1], x["k"][b:b + 1, h:h + 1], x["v"][b:b + 1, h:h + 1],
+                                    x["u"][b:b + 1, h:h + 1], x["mu"][h:h + 1], x["tau"][h:h + 1],
+                                    x["g1"][b:b + 1, h:h + 1], x["gh"][b:b + 1, h:h + 1])
+            errs.append(rel_l2(got[b:b + 1, h:h + 1], ref))
+        ent["parity"] = {"heads": "(0, 0) and (B-1, H-1), the larger error", "rel_l2": max(errs), "bar": BAR["bf16"]}
+    out.append(ent)
+    log(f"secondary long encoder: {ms:.4f} ms")
+    del t, o, ws, x
 
     out.append(_decode_secondary(dev, steps, with_oracle=bool(oracle)))
     torch.cuda.empty_cache()

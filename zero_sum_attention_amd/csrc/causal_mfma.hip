@@ -32,6 +32,7 @@
 #include <hip/hip_bf16.h>
 
 #include "device_common.hpp"
+#include "kv_states.hpp"
 #include "launch.hpp"
 #include "mfma_common.hpp"
 
@@ -777,6 +778,71 @@ __global__ __launch_bounds__(kScanThreads<D>) void causal_scan_kernel(Problem p,
     }
 }
 
+// ---- pass 1, token-parallel: the segment-local state L of segments 0 .. nseg-2 (the recurrence run
+// from zero over the segment) in the centred basis at the segment end. Unrolled, the chunk maps
+// X <- rX X + cHX H + dX, Y <- Y + cHY H + dY, H <- H + dH of a segment give per token i
+//   L_X = sum_i (e^{s_i - m_n}/E_n - 1/t_n) k^_i^T v_i,   L_Y = sum_i (s_i - P_n/t_n) k^_i^T v_i,
+//   L_H = sum_i k^_i^T v_i,
+// with (m_n, E_n, P_n) the logit carry and t_n the token count at the segment end (the centred
+// weights of 关键设计 at t_n): one weighted contraction over the segment's tokens (kv_states.hpp),
+// with no chain of per-chunk steps. The composed scalar map of the segment (Rs, Hs, Ys: X <- Rs X +
+// Hs H, Y <- Y + Ys H) comes from the chunk maps of the coefficient records, in order.
+template <int D, bool ROPE>
+__global__ __launch_bounds__(kv_threads<D>()) void causal_seg_local_kernel(Problem p, CausalWork work) {
+    constexpr int JB = D / 16, NGT = D / 16;
+    __shared__ __align__(16) KvSmem<D, 3> sm;
+    __shared__ double rev[ROPE ? D / 2 : 1];
+    const int nseg = work.nseg;
+    const int seg = blockIdx.x % (nseg - 1), bh = blockIdx.x / (nseg - 1);
+    const int N = p.N, nch = (N + kC - 1) / kC;
+    const int c_begin = seg * work.seg_chunks, c_end = min(nch, c_begin + work.seg_chunks);
+    const int t0 = c_begin * kC, t1 = min(N, c_end * kC);
+    const int tin = p.sin.F != nullptr ? p.sin.t[bh] : 0;
+    const size_t row0 = static_cast<size_t>(bh) * N;
+    // the logit carry (m_n, E_n, P_n) at the segment end, before the rows are in flight (its wait then
+    // leaves them in flight)
+    const Coef *cf = work.coef + static_cast<size_t>(bh) * nch;
+    const float mn = cf[c_end - 1].chunk[0], En = cf[c_end - 1].chunk[1], Pn = cf[c_end - 1].chunk[2];
+    // tokens of this call are positions tin + r (RoPE phase as in the main pass)
+    KvStates<D, ROPE, 3> kv(sm, static_cast<const uint16_t *>(p.k) + row0 * D, static_cast<const uint16_t *>(p.v) + row0 * D,
+                            work.s + row0, rev, N, t0, t1, tin);
+    kv.start();
+    if (ROPE && kv.tid < D / 2) rev[kv.tid] = rope_rev_per_pos(kv.tid, D, p.rope_base);
+    lds_barrier();
+    const float iE = 1.f / En, itn = 1.f / static_cast<float>(tin + t1), pn = Pn * itn;
+    kv.run([&](float sv) __attribute__((always_inline)) { return make_float2(__expf(sv - mn) * iE - itn, sv - pn); });
+    if (kv.wv == 0) {
+        // composed map: per chunk (with tokens before it) Hs <- rX Hs + cHX, Ys <- Ys + cHY, Rs <- rX Rs;
+        // the first chunk of the sequence starts from nothing (Rs = 0)
+        float Rs = 1.f, hs = 0.f, ys = 0.f;
+        for (int cb = c_begin; cb < c_end; cb += 64) {
+            const int c = min(cb + kv.lane, c_end - 1);
+            const float rx = cf[c].chunk[3], hx = cf[c].chunk[4], hy = cf[c].chunk[5];
+            const int n = min(64, c_end - cb);
+            for (int j = 0; j < n; ++j) {
+                const float x = __shfl(rx, j, 64), y = __shfl(hx, j, 64), z = __shfl(hy, j, 64);
+                if (tin + (cb + j) * kC > 0) {
+                    hs = x * hs + y;
+                    ys += z;
+                    Rs *= x;
+                } else {
+                    Rs = 0.f;
+                }
+            }
+        }
+        if (kv.lane == 0) work.segsc[static_cast<size_t>(bh) * nseg + seg] = make_float4(Rs, hs, ys, 0.f);
+    }
+    // the segment state layout: float4 ((s JB + jb) NGT + gt) 64 + lane holds rows 16 jb + 4 g4 + [0, 4)
+    // of column 16 gt + l16 of state s
+    float4 *dst = reinterpret_cast<float4 *>(work.segst + (static_cast<size_t>(bh) * (nseg - 1) + seg) * kSegFloats<D>);
+#pragma unroll
+    for (int s = 0; s < 3; ++s)
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb)
+            dst[(size_t(s * JB + jb) * NGT + kv.wv) * 64 + kv.lane] =
+                make_float4(kv.acc[s][jb][0], kv.acc[s][jb][1], kv.acc[s][jb][2], kv.acc[s][jb][3]);
+}
+
 // Start states of segments 1 .. nseg-1 (in place over the segment-local sums), one float4 position
 // of the three state matrices per thread: S_{j+1} = M_j S_j + L_j with S_0 = 0, or the given state
 // in the centred basis for a continued sequence.
@@ -855,8 +921,8 @@ hipError_t launch_one(const Problem &p, const CausalWork &w, hipStream_t stream)
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if (w.nseg > 1) {
-        hipLaunchKernelGGL((causal_scan_kernel<D, ROPE, true>), dim3(bh * (w.nseg - 1)), dim3(kScanThreads<D>),
-                           0, stream, p, w);
+        hipLaunchKernelGGL((causal_seg_local_kernel<D, ROPE>), dim3(bh * (w.nseg - 1)), dim3(kv_threads<D>()), 0, stream,
+                           p, w);
         if ((err = hipGetLastError()) != hipSuccess) return err;
         hipLaunchKernelGGL((causal_seg_combine_kernel<D>), dim3(bh, (D * D / 4 + 255) / 256), dim3(256), 0,
                            stream, p, w);

@@ -18,6 +18,7 @@
 // Scratch: encoder_long_work_bytes(p).
 #include "device_common.hpp"
 #include "encoder_common.hpp"
+#include "kv_states.hpp"
 #include "launch.hpp"
 #include "mfma_common.hpp"
 
@@ -28,8 +29,6 @@ constexpr int kLB = kLogitSeg;     // tokens per u-sum block
 constexpr int kLPad = 8;           // bf16 elements of row padding in LDS (rows stay 4 mod 8 words)
 constexpr int kLThreads = 256;     // logits kernel
 
-template <int D> constexpr int st_threads() { return D == 64 ? 256 : 512; }
-template <int D> constexpr int st_round() { return D == 64 ? 128 : 64; }
 template <int D> constexpr int out_threads() { return D == 64 ? 256 : 512; }
 template <int D> constexpr int out_block() { return D == 64 ? 512 : 1024; }
 
@@ -159,60 +158,29 @@ __global__ __launch_bounds__(kLThreads) void enc_long_logits_kernel(Problem p, L
     }
 }
 
-// ---- 3: the partial states of a state block, in rounds of RND tokens (the rows of the next two
-// rounds are in flight while one is on the matrix cores). The round's k^ and v w_X, v w_Y (, v) rows
-// are staged token-major (one 16-byte store per row piece) and read as MFMA operands by transposing
-// LDS reads, which order the contraction over the tokens as 32 ks + 4 g4 + [0, 4), then + 16 (the
-// same for both operands). Wave w owns column tile w of every state, all its feature tiles.
+// ---- 3: the partial states of a state block (kv_states.hpp), with the weights of the whole head:
+// w_X = e^{s - m}/E - 1/N, w_Y = s - P/N, from the merged state-block aggregates.
 template <int D, bool ROPE, int NS>
-__global__ __launch_bounds__(st_threads<D>()) void enc_long_state_kernel(Problem p, LongWork w) {
-    constexpr int NT = st_threads<D>(), NW = NT / 64, RND = st_round<D>();
-    constexpr int LPR = D / 8, RPP = NT / LPR, PPR = RND / RPP;
-    constexpr int NFT = D / 16;
-    static_assert(PPR * RPP == RND && NW == NFT, "state kernel shape");
-    __shared__ __align__(16) uint16_t kh[RND][D + kLPad];         // k^ rows of the round
-    __shared__ __align__(16) uint16_t vw[NS][RND][D + kLPad];     // v w_X, v w_Y (, v) rows
+__global__ __launch_bounds__(kv_threads<D>()) void enc_long_state_kernel(Problem p, LongWork w) {
+    __shared__ __align__(16) KvSmem<D, NS> sm;
     __shared__ float scal[3];
     __shared__ double rev[ROPE ? D / 2 : 1];
     const int nsb = w.nsb, sb = blockIdx.x % nsb, bh = blockIdx.x / nsb;
-    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l16 = lane & 15, g4 = lane >> 4;
-    const int fr = tid % LPR, rr = tid / LPR;
     const int N = p.N, t0 = sb * w.sb_tokens, t1 = min(N, t0 + w.sb_tokens);
-    const int nrd = (t1 - t0 + RND - 1) / RND;
     const size_t row0 = static_cast<size_t>(bh) * N;
-    const uint16_t *k = static_cast<const uint16_t *>(p.k) + row0 * D;
-    const uint16_t *v = static_cast<const uint16_t *>(p.v) + row0 * D;
-    const float *srow = w.s + row0;
-    // the rows of one round in registers; loads of rounds past the block re-read its last round
-    // (from L2) so that every load is unconditional
-    struct Rows {
-        uint4 k[PPR], v[PPR];
-        float s[PPR];
-    };
-    auto load = [&](Rows &x, int rd) __attribute__((always_inline)) {
-        rd = min(rd, nrd - 1);
-#pragma unroll
-        for (int j = 0; j < PPR; ++j) {
-            const int r = min(t0 + rd * RND + rr + RPP * j, N - 1);
-            x.k[j] = *reinterpret_cast<const uint4 *>(k + static_cast<size_t>(r) * D + 8 * fr);
-            x.v[j] = *reinterpret_cast<const uint4 *>(v + static_cast<size_t>(r) * D + 8 * fr);
-            x.s[j] = srow[r];
-        }
-    };
-    Rows rows0, rows1;
-    load(rows0, 0);
-    load(rows1, 1);
-    if (ROPE && tid < D / 2) rev[tid] = rope_rev_per_pos(tid, D, p.rope_base);
-    if (wv == 0) {                     // (m, E, P) of the head from the state-block aggregates
+    KvStates<D, ROPE, NS> kv(sm, static_cast<const uint16_t *>(p.k) + row0 * D, static_cast<const uint16_t *>(p.v) + row0 * D,
+                             w.s + row0, rev, N, t0, t1, 0);
+    kv.start();
+    if (ROPE && kv.tid < D / 2) rev[kv.tid] = rope_rev_per_pos(kv.tid, D, p.rope_base);
+    if (kv.wv == 0) {                  // (m, E, P) of the head from the state-block aggregates
         float m = kNegInf, e = 0.f, ps = 0.f;
-        for (int j = lane; j < nsb; j += 64) {
+        for (int j = kv.lane; j < nsb; j += 64) {
             const float4 a = w.aggb[static_cast<size_t>(bh) * nsb + j];
             lse_merge(m, e, a.x, a.y);
             ps += a.z;
         }
         wave_lse_merge(m, e, ps);
-        if (lane == 0) {
+        if (kv.lane == 0) {
             scal[0] = m;
             scal[1] = e;
             scal[2] = ps;
@@ -221,87 +189,15 @@ __global__ __launch_bounds__(st_threads<D>()) void enc_long_state_kernel(Problem
     lds_barrier();
     const float M = scal[0], invE = scal[1] > 0.f ? 1.f / scal[1] : 0.f;
     const float invN = 1.f / static_cast<float>(N), PN = scal[2] * invN;
-
-    // transposing-read operand of 16-row tile `tile` of buffer b at 32-token step ks: lane (g4, l16)
-    // names features 16 tile + 4 (l16 & 3) + [0, 4) of token 32 ks + 4 g4 + (l16 >> 2) (and + 16)
-    auto operand = [&](const uint16_t (*b)[D + kLPad], int tile, int ks) __attribute__((always_inline)) {
-        const int f = 16 * tile + 4 * (l16 & 3), r = 32 * ks + 4 * g4 + (l16 >> 2);
-        const uint2 a = lds_tr16(&b[r][f]);
-        const uint2 c = lds_tr16(&b[r + 16][f]);
-        return as_bf16x8(a.x, a.y, c.x, c.y);
-    };
-
-    f32x4 acc[NS][NFT];
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-        for (int i = 0; i < NFT; ++i) acc[s][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // one round: stage the rows held in x, load round rd + 2 into x, then the products. A round past
-    // the block (rd >= nrd, when nrd is odd) stages zeros and skips its products.
-    auto round = [&](Rows &x, const int rd) __attribute__((always_inline)) {
-        const int rb = t0 + rd * RND;
-#pragma unroll
-        for (int j = 0; j < PPR; ++j) {
-            const int rl = rr + RPP * j, r = rb + rl;
-            const bool ok = r < t1;
-            float kv[8], vv[8];
-            unpack8(x.k[j], kv);
-            unpack8(x.v[j], vv);
-            float ss = 0.f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) ss = fmaf(kv[i], kv[i], ss);
-            ss = group_sum<LPR>(ss);
-            const float ik = ok ? __frsqrt_rn(fmaxf(ss, 1e-24f)) : 0.f;
-            if (ROPE) {
-#pragma unroll
-                for (int j2 = 0; j2 < 4; ++j2) {
-                    float cs, sn;
-                    rope_cos_sin(rev[4 * fr + j2], r, cs, sn);
-                    const float a = kv[2 * j2], b = kv[2 * j2 + 1];
-                    kv[2 * j2] = a * cs - b * sn;
-                    kv[2 * j2 + 1] = a * sn + b * cs;
-                }
-            }
-            const float wx = ok ? __expf(x.s[j] - M) * invE - invN : 0.f;
-            const float wy = ok ? x.s[j] - PN : 0.f;
-            *reinterpret_cast<uint4 *>(&kh[rl][8 * fr]) = make_uint4(pack2(kv[0] * ik, kv[1] * ik), pack2(kv[2] * ik, kv[3] * ik),
-                                                                     pack2(kv[4] * ik, kv[5] * ik), pack2(kv[6] * ik, kv[7] * ik));
-            *reinterpret_cast<uint4 *>(&vw[0][rl][8 * fr]) = make_uint4(pack2(vv[0] * wx, vv[1] * wx), pack2(vv[2] * wx, vv[3] * wx),
-                                                                        pack2(vv[4] * wx, vv[5] * wx), pack2(vv[6] * wx, vv[7] * wx));
-            *reinterpret_cast<uint4 *>(&vw[1][rl][8 * fr]) = make_uint4(pack2(vv[0] * wy, vv[1] * wy), pack2(vv[2] * wy, vv[3] * wy),
-                                                                        pack2(vv[4] * wy, vv[5] * wy), pack2(vv[6] * wy, vv[7] * wy));
-            if (NS == 3)   // v itself (zero past the block)
-                *reinterpret_cast<uint4 *>(&vw[NS - 1][rl][8 * fr]) = ok ? x.v[j] : make_uint4(0u, 0u, 0u, 0u);
-        }
-        load(x, rd + 2);
-        lds_barrier();
-#pragma unroll
-        for (int ks = 0; ks < RND / 32; ++ks) {
-            if (rb + 32 * ks >= t1) break;        // steps past the block hold zeros only
-            bf16x8 B[NS];
-#pragma unroll
-            for (int s = 0; s < NS; ++s) B[s] = operand(vw[s], wv, ks);
-#pragma unroll
-            for (int ft = 0; ft < NFT; ++ft) {
-                const bf16x8 A = operand(kh, ft, ks);
-#pragma unroll
-                for (int s = 0; s < NS; ++s) acc[s][ft] = mfma(A, B[s], acc[s][ft]);
-            }
-        }
-        lds_barrier();
-    };
-    for (int rd = 0; rd < nrd; rd += 2) {
-        round(rows0, rd);
-        round(rows1, rd + 1);
-    }
-    // accumulator lane (l16, g4) holds features 16 ft + 4 g4 + [0, 4) of column 16 wv + l16
+    kv.run([&](float sv) __attribute__((always_inline)) { return make_float2(__expf(sv - M) * invE - invN, sv - PN); });
+    // accumulator lane (l16, g4) of tile ft holds features 16 ft + 4 g4 + [0, 4) of column 16 wv + l16
     float *xp = w.xpart + (static_cast<size_t>(bh) * nsb + sb) * 3 * D * D;
 #pragma unroll
-    for (int ft = 0; ft < NFT; ++ft) {
+    for (int ft = 0; ft < D / 16; ++ft) {
 #pragma unroll
         for (int s = 0; s < NS; ++s)
-            *reinterpret_cast<float4 *>(xp + static_cast<size_t>(s) * D * D + static_cast<size_t>(16 * wv + l16) * D + 16 * ft +
-                                        4 * g4) = make_float4(acc[s][ft][0], acc[s][ft][1], acc[s][ft][2], acc[s][ft][3]);
+            *reinterpret_cast<float4 *>(xp + static_cast<size_t>(s) * D * D + static_cast<size_t>(16 * kv.wv + kv.l16) * D + 16 * ft +
+                                        4 * kv.g4) = make_float4(kv.acc[s][ft][0], kv.acc[s][ft][1], kv.acc[s][ft][2], kv.acc[s][ft][3]);
     }
 }
 
@@ -446,7 +342,7 @@ hipError_t launch_v(const Problem &p, const LongWork &w, hipStream_t stream) {
     hipLaunchKernelGGL((enc_long_logits_kernel<D>), dim3(bh * w.nsb), dim3(kLThreads), 0, stream, p, w);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((enc_long_state_kernel<D, ROPE, NS>), dim3(bh * w.nsb), dim3(st_threads<D>()), 0, stream, p, w);
+    hipLaunchKernelGGL((enc_long_state_kernel<D, ROPE, NS>), dim3(bh * w.nsb), dim3(kv_threads<D>()), 0, stream, p, w);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     hipLaunchKernelGGL(enc_long_reduce_kernel, dim3(bh, (NS * D * D / 4 + 255) / 256), dim3(256), 0, stream, w, D * D, NS);
     if ((err = hipGetLastError()) != hipSuccess) return err;

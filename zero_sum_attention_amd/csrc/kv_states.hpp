@@ -184,6 +184,8 @@ struct KvStates {
         for (int j = 0; j < PPR; ++j) {
             stage_row(x, rd + 1, j, nb, wfn, rbase, rrate);
             products(cb, j);
+            // (one step's operands and staging values live at a time)
+            if (j + 1 < PPR) asm volatile("" ::: "memory");
         }
         // (the next loads stay after this phase's work, so their registers are not held meanwhile)
         asm volatile("" ::: "memory");

@@ -149,6 +149,11 @@ def _dev_inputs(x: dict, dtype: str, dev):
             for k, v in x.items()}
 
 
+# timed calls for the prepared C calls of the short workloads (10-70 us each): 200 calls amortise the
+# first launch and the event packets, which 20 calls of a 10 us kernel do not
+SHORT_STEPS = 200
+
+
 def _timed(dev, fn, steps: int, warm_ms: float = 50.0) -> float:
     """Average ms of fn(stream) over `steps` back-to-back calls, HIP events on the launch stream,
     after back-to-back calls for warm_ms of wall time (at least 3): the GPU raises its clocks over
@@ -233,9 +238,9 @@ def secondary(dev, oracle: dict, cores: int, steps: int = 20) -> list:
                                         out=o, workspace=ws, stream=st)
     ms_binding = _timed(dev, run, steps)
     time.sleep(0.02)          # from near-idle clocks: three warm-up calls only
-    ms_short = _timed(dev, _c_call("zeros_fwd_causal", t, o, ws, False, torch.cuda.current_stream(dev), wl.N), steps,
+    ms_short = _timed(dev, _c_call("zeros_fwd_causal", t, o, ws, False, torch.cuda.current_stream(dev), wl.N), SHORT_STEPS,
                       warm_ms=0)
-    ms = _timed(dev, _c_call("zeros_fwd_causal", t, o, ws, False, torch.cuda.current_stream(dev), wl.N), steps)
+    ms = _timed(dev, _c_call("zeros_fwd_causal", t, o, ws, False, torch.cuda.current_stream(dev), wl.N), SHORT_STEPS)
     nbytes = algorithmic_bytes(wl)
     flops = 12 * wl.d * wl.d * wl.B * wl.H * wl.N
     ent = {"workload": wl.name, "call": "zeros_fwd_causal", "dtype": "f32", "ms": ms, "ms_short_warmup": ms_short,
@@ -265,9 +270,9 @@ def secondary(dev, oracle: dict, cores: int, steps: int = 20) -> list:
     ms_binding = _timed(dev, lambda st: Z.zeros_fwd_causal(t["q"], t["k"], t["v"], t["u"], t["mu"], t["tau"],
                                                            t["g1"], t["gh"], out=o, workspace=ws, stream=st), steps)
     time.sleep(0.02)          # from near-idle clocks: three warm-up calls only
-    ms_short = _timed(dev, _c_call("zeros_fwd_causal", t, o, ws, False, torch.cuda.current_stream(dev), wl.N), steps,
+    ms_short = _timed(dev, _c_call("zeros_fwd_causal", t, o, ws, False, torch.cuda.current_stream(dev), wl.N), SHORT_STEPS,
                       warm_ms=0)
-    ms = _timed(dev, _c_call("zeros_fwd_causal", t, o, ws, False, torch.cuda.current_stream(dev), wl.N), steps)
+    ms = _timed(dev, _c_call("zeros_fwd_causal", t, o, ws, False, torch.cuda.current_stream(dev), wl.N), SHORT_STEPS)
     flops = 12 * wl.d * wl.d * wl.B * wl.H * wl.N
     out.append({"workload": "long-f32-causal-B1H2N8192d64", "call": "zeros_fwd_causal", "dtype": "f32", "ms": ms,
                 "ms_short_warmup": ms_short, "ms_binding": ms_binding,
@@ -286,9 +291,9 @@ def secondary(dev, oracle: dict, cores: int, steps: int = 20) -> list:
     ms_binding = _timed(dev, lambda st: Z.zeros_fwd_encoder(t["q"], t["k"], t["v"], t["u"], t["mu"], t["tau"],
                                                             t["g1"], t["gh"], out=o, workspace=ws, stream=st), steps)
     time.sleep(0.02)          # from near-idle clocks: three warm-up calls only
-    ms_short = _timed(dev, _c_call("zeros_fwd_encoder", t, o, ws, False, torch.cuda.current_stream(dev), wl.N), steps,
+    ms_short = _timed(dev, _c_call("zeros_fwd_encoder", t, o, ws, False, torch.cuda.current_stream(dev), wl.N), SHORT_STEPS,
                       warm_ms=0)
-    ms = _timed(dev, _c_call("zeros_fwd_encoder", t, o, ws, False, torch.cuda.current_stream(dev), wl.N), steps)
+    ms = _timed(dev, _c_call("zeros_fwd_encoder", t, o, ws, False, torch.cuda.current_stream(dev), wl.N), SHORT_STEPS)
     nbytes = algorithmic_bytes(wl)
     ent = {"workload": wl.name, "call": "zeros_fwd_encoder", "ms": ms, "ms_short_warmup": ms_short,
            "ms_binding": ms_binding,
@@ -315,7 +320,7 @@ def secondary(dev, oracle: dict, cores: int, steps: int = 20) -> list:
                      dtype=torch.uint8, device=dev)
     ms_binding = _timed(dev, lambda st: Z.zeros_fwd_encoder(t["q"], t["k"], t["v"], t["u"], t["mu"], t["tau"],
                                                             t["g1"], t["gh"], out=o, workspace=ws, stream=st), steps)
-    ms = _timed(dev, _c_call("zeros_fwd_encoder", t, o, ws, False, torch.cuda.current_stream(dev), wl.N), steps)
+    ms = _timed(dev, _c_call("zeros_fwd_encoder", t, o, ws, False, torch.cuda.current_stream(dev), wl.N), SHORT_STEPS)
     nbytes = algorithmic_bytes(wl)
     ent = {"workload": "long-encoder-B8H8N8192d64", "call": "zeros_fwd_encoder", "dtype": "bf16", "ms": ms,
            "ms_binding": ms_binding, "tokens_per_s": wl.B * wl.N / (ms * 1e-3), "algorithmic_bytes": nbytes,

@@ -400,7 +400,14 @@ __global__ __launch_bounds__(kEHThreads) void encoder_head_kernel(Problem p) {
     constexpr int ER = eh_round<ROPE>();         // tokens per staging round
     constexpr int JPH = ER / RPP;                // passes per staging round
     constexpr int NFT = D / 16;                  // 16-row (16-column) tiles of a d x d state
-    constexpr int TPW = NFT * NFT / 16;          // state tiles per wave
+    // waves that form the states and the block of BF x BC 16 x 16 tiles each one owns: without RoPE
+    // eight waves of 1 x 2 tiles (each k^ operand read from LDS serves two tiles; sixteen waves of
+    // one tile read every operand four times over), with RoPE (fewer free registers) sixteen
+    static_assert(D == 64, "per-head variant: d = 64");
+    constexpr int PBW = ROPE ? 16 : 8;
+    constexpr int BF = 1, BC = ROPE ? 1 : 2;
+    constexpr int TPW = BF * BC;                 // state tiles per wave
+    static_assert(PBW * TPW == NFT * NFT, "state tiles");
     constexpr int KS = D / 32;                   // 32-feature steps of the output products
     static_assert(UP * RPP == kEHeadMaxN && JPH * RPP == ER && TPW >= 1, "per-head shape");
     __shared__ __align__(16) EHeadBuf<D, G0> buf;
@@ -554,8 +561,9 @@ __global__ __launch_bounds__(kEHThreads) void encoder_head_kernel(Problem p) {
     const float invE = E > 0.f ? 1.f / E : 0.f;
     const float PN = P * invN;
 
-    // ---- B: X = K^T diag(w_X) V, Y = K^T diag(w_Y) V (H = K^T V), 128 tokens per round; wave w
-    // owns state tiles w + 16 i (feature tile ft, column tile ct)
+    // ---- B: X = K^T diag(w_X) V, Y = K^T diag(w_Y) V (H = K^T V), ER tokens per round; wave w < PBW
+    // owns the feature tiles ftb + [0, BF) x column tiles ctb + [0, BC) of every state
+    const int ftb = (w / (NFT / BC)) * BF, ctb = (w % (NFT / BC)) * BC;   // this wave's first tiles (w < PBW)
     f32x4 X[TPW], Y[TPW], Hc[G0 ? TPW : 1];
 #pragma unroll
     for (int i = 0; i < TPW; ++i) X[i] = Y[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -600,23 +608,32 @@ __global__ __launch_bounds__(kEHThreads) void encoder_head_kernel(Problem p) {
             }
         }
         __syncthreads();
-#pragma unroll
-        for (int ti = 0; ti < TPW; ++ti) {
-            const int tile = w + 16 * ti, ft = tile / NFT, ct = tile % NFT;
+        if (w < PBW) {
 #pragma unroll
             for (int ks = 0; ks < ER / 32; ++ks) {
                 if (ER * rd + 32 * ks >= N) break;        // steps past the sequence hold zeros only
                 const int kk0 = 32 * ks + 8 * g4;
-                const int fa = 16 * ft + l16, fb = 16 * ct + l16;
-                const bf16x8 A = *reinterpret_cast<const bf16x8 *>(&buf.st.kt[fa][eh_col(fa, kk0)]);
-                const bf16x8 BX = *reinterpret_cast<const bf16x8 *>(&buf.st.vxt[fb][eh_col(fb, kk0)]);
-                const bf16x8 BY = *reinterpret_cast<const bf16x8 *>(&buf.st.vyt[fb][eh_col(fb, kk0)]);
-                X[ti] = mfma(A, BX, X[ti]);
-                Y[ti] = mfma(A, BY, Y[ti]);
-                if (G0) {
-                    const bf16x8 BH = *reinterpret_cast<const bf16x8 *>(&buf.st.vht[fb][eh_col(fb, kk0)]);
-                    Hc[ti] = mfma(A, BH, Hc[ti]);
+                bf16x8 A[BF], BX[BC], BY[BC], BH[G0 ? BC : 1];
+#pragma unroll
+                for (int i = 0; i < BF; ++i) {
+                    const int fa = 16 * (ftb + i) + l16;
+                    A[i] = *reinterpret_cast<const bf16x8 *>(&buf.st.kt[fa][eh_col(fa, kk0)]);
                 }
+#pragma unroll
+                for (int j = 0; j < BC; ++j) {
+                    const int fb = 16 * (ctb + j) + l16;
+                    BX[j] = *reinterpret_cast<const bf16x8 *>(&buf.st.vxt[fb][eh_col(fb, kk0)]);
+                    BY[j] = *reinterpret_cast<const bf16x8 *>(&buf.st.vyt[fb][eh_col(fb, kk0)]);
+                    if (G0) BH[j] = *reinterpret_cast<const bf16x8 *>(&buf.st.vht[fb][eh_col(fb, kk0)]);
+                }
+#pragma unroll
+                for (int i = 0; i < BF; ++i)
+#pragma unroll
+                    for (int j = 0; j < BC; ++j) {
+                        X[i * BC + j] = mfma(A[i], BX[j], X[i * BC + j]);
+                        Y[i * BC + j] = mfma(A[i], BY[j], Y[i * BC + j]);
+                        if (G0) Hc[i * BC + j] = mfma(A[i], BH[j], Hc[i * BC + j]);
+                    }
             }
         }
         __syncthreads();
@@ -625,8 +642,8 @@ __global__ __launch_bounds__(kEHThreads) void encoder_head_kernel(Problem p) {
     // of column 16 ct + l16
 #pragma unroll
     for (int ti = 0; ti < TPW; ++ti) {
-        const int tile = w + 16 * ti, ft = tile / NFT, ct = tile % NFT;
-        const int f = 16 * ft + 4 * g4, c = 16 * ct + l16;
+        if (w >= PBW) break;
+        const int f = 16 * (ftb + ti / BC) + 4 * g4, c = 16 * (ctb + ti % BC) + l16;
         *reinterpret_cast<uint2 *>(&buf.sxy[0][c][f]) = make_uint2(pack2(X[ti][0], X[ti][1]), pack2(X[ti][2], X[ti][3]));
         *reinterpret_cast<uint2 *>(&buf.sxy[1][c][f]) = make_uint2(pack2(Y[ti][0], Y[ti][1]), pack2(Y[ti][2], Y[ti][3]));
         if (G0)

@@ -158,19 +158,18 @@ __device__ __forceinline__ void chunk_scan(Coef &cf, int lane, int t0, int nval,
 // ---- per-chunk coefficients ---------------------------------------------------------------
 // One wave per (batch, head, chunk), all chunks in parallel: the logit carry at the chunk start
 // (the given state's (m, E, P) merged with the aggregates of the earlier chunks) and the chunk's
-// scalar scan. The record (sizeof(Coef) bytes) is read by both scan passes.
+// scalar scan. The record (sizeof(Coef) bytes) is read by the main scan pass. With scan segments the
+// records are formed in the pass 1 launch (causal_seg_local_kernel), else by causal_coef_kernel.
 constexpr int kCoefWaves = 4;
 static_assert(sizeof(Coef) % 16 == 0, "coefficient records are copied in 16-byte pieces");
 // LDS bytes of a coefficient record rounded up to whole 64-piece (1 KiB) wave copies
 constexpr int kCoefLds = int((sizeof(Coef) / 16 + 63) / 64 * 64 * 16);
 constexpr int kCoefStage = 8 * 64 * 16;   // one 64-piece direct copy per wave, up to 8 waves
 
-__global__ __launch_bounds__(64 * kCoefWaves) void causal_coef_kernel(Problem p, CausalWork work) {
-    const int lane = threadIdx.x & 63;
+// the record of chunk `item` (head item / nch, chunk item % nch), by one wave
+__device__ __forceinline__ void coef_item(const Problem &p, const CausalWork &work, const int item, const int lane) {
     const int N = p.N;
     const int nch = (N + kC - 1) / kC;
-    const int item = blockIdx.x * kCoefWaves + (threadIdx.x >> 6);
-    if (item >= p.B * p.H * nch) return;           // (wave-uniform)
     const int bh = item / nch, c = item % nch;
     const int t0 = c * kC, nval = min(kC, N - t0);
     const size_t row0 = static_cast<size_t>(bh) * N;
@@ -200,6 +199,13 @@ __global__ __launch_bounds__(64 * kCoefWaves) void causal_coef_kernel(Problem p,
                          ? __fdividef(1.f, 1.f + __expf(-lo_f(static_cast<const uint16_t *>(p.g0)[row0 + t0 + lane])))
                          : 0.f;
     chunk_scan(work.coef[item], lane, tin + t0, nval, sv, g1v, ghv, s0, m0, E0, P0);
+}
+
+__global__ __launch_bounds__(64 * kCoefWaves) void causal_coef_kernel(Problem p, CausalWork work) {
+    const int nch = (p.N + kC - 1) / kC;
+    const int item = blockIdx.x * kCoefWaves + (threadIdx.x >> 6);
+    if (item >= p.B * p.H * nch) return;           // (wave-uniform)
+    coef_item(p, work, item, threadIdx.x & 63);
 }
 
 // W piece of query block tb (0..3) and key-block pair pi (keys 32 pi .. 32 pi + 31), 2 pi <= tb:
@@ -785,53 +791,85 @@ __global__ __launch_bounds__(kScanThreads<D>) void causal_scan_kernel(Problem p,
 //   L_H = sum_i k^_i^T v_i,
 // with (m_n, E_n, P_n) the logit carry and t_n the token count at the segment end (the centred
 // weights of 关键设计 at t_n): one weighted contraction over the segment's tokens (kv_states.hpp),
-// with no chain of per-chunk steps. The composed scalar map of the segment (Rs, Hs, Ys: X <- Rs X +
-// Hs H, Y <- Y + Ys H) comes from the chunk maps of the coefficient records, in order.
+// with no chain of per-chunk steps. The segment's map of its start state (X <- Rs X + Hs H,
+// Y <- Y + Ys H) is the same re-centring between the carries at its two ends:
+//   Rs = E_s e^{m_s - m_n} / E_n,   Hs = Rs / t_s - 1 / t_n,   Ys = P_s / t_s - P_n / t_n.
+// Both carries come from the per-chunk logit aggregates, so pass 1 does not wait for the chunk
+// records: the same launch also forms them, in the workgroups past the segments (one wave per
+// chunk), which take the CUs the segments leave free.
 template <int D, bool ROPE>
 __global__ __launch_bounds__(kv_threads<D>()) void causal_seg_local_kernel(Problem p, CausalWork work) {
     constexpr int JB = D / 16, NGT = D / 16;
     __shared__ __align__(16) KvSmem<D, 3> sm;
     __shared__ double rev[ROPE ? D / 2 : 1];
+    __shared__ float scal[3];
     const int nseg = work.nseg;
-    const int seg = blockIdx.x % (nseg - 1), bh = blockIdx.x / (nseg - 1);
     const int N = p.N, nch = (N + kC - 1) / kC;
+    const int nloc = p.B * p.H * (nseg - 1);
+    if (static_cast<int>(blockIdx.x) >= nloc) {
+        // coefficient records (whole workgroup: no barrier below is reached)
+        const int item = (static_cast<int>(blockIdx.x) - nloc) * (kv_threads<D>() / 64) + static_cast<int>(threadIdx.x >> 6);
+        if (item < p.B * p.H * nch) coef_item(p, work, item, threadIdx.x & 63);
+        return;
+    }
+    const int seg = blockIdx.x % (nseg - 1), bh = blockIdx.x / (nseg - 1);
     const int c_begin = seg * work.seg_chunks, c_end = min(nch, c_begin + work.seg_chunks);
     const int t0 = c_begin * kC, t1 = min(N, c_end * kC);
-    const int tin = p.sin.F != nullptr ? p.sin.t[bh] : 0;
+    const bool cont = p.sin.F != nullptr;
+    const int tin = cont ? p.sin.t[bh] : 0;
     const size_t row0 = static_cast<size_t>(bh) * N;
-    // the logit carry (m_n, E_n, P_n) at the segment end, before the rows are in flight (its wait then
-    // leaves them in flight)
-    const Coef *cf = work.coef + static_cast<size_t>(bh) * nch;
-    const float mn = cf[c_end - 1].chunk[0], En = cf[c_end - 1].chunk[1], Pn = cf[c_end - 1].chunk[2];
     // tokens of this call are positions tin + r (RoPE phase as in the main pass)
     KvStates<D, ROPE, 3> kv(sm, static_cast<const uint16_t *>(p.k) + row0 * D, static_cast<const uint16_t *>(p.v) + row0 * D,
                             work.s + row0, rev, N, t0, t1, tin);
     kv.start();
     if (ROPE && kv.tid < D / 2) rev[kv.tid] = rope_rev_per_pos(kv.tid, D, p.rope_base);
-    lds_barrier();
-    const float iE = 1.f / En, itn = 1.f / static_cast<float>(tin + t1), pn = Pn * itn;
-    kv.run([&](float sv) __attribute__((always_inline)) { return make_float2(__expf(sv - mn) * iE - itn, sv - pn); });
     if (kv.wv == 0) {
-        // composed map: per chunk (with tokens before it) Hs <- rX Hs + cHX, Ys <- Ys + cHY, Rs <- rX Rs;
-        // the first chunk of the sequence starts from nothing (Rs = 0)
-        float Rs = 1.f, hs = 0.f, ys = 0.f;
-        for (int cb = c_begin; cb < c_end; cb += 64) {
-            const int c = min(cb + kv.lane, c_end - 1);
-            const float rx = cf[c].chunk[3], hx = cf[c].chunk[4], hy = cf[c].chunk[5];
-            const int n = min(64, c_end - cb);
-            for (int j = 0; j < n; ++j) {
-                const float x = __shfl(rx, j, 64), y = __shfl(hx, j, 64), z = __shfl(hy, j, 64);
-                if (tin + (cb + j) * kC > 0) {
-                    hs = x * hs + y;
-                    ys += z;
-                    Rs *= x;
-                } else {
-                    Rs = 0.f;
-                }
+        // carries at the segment start (chunks before c_begin) and end (before c_end), from the given
+        // state's (m, E, P) and the chunk aggregates
+        const bool from_state = cont && kv.lane == 0;
+        float ms = from_state ? p.sin.m[bh] : kNegInf, es = from_state ? p.sin.E[bh] : 0.f, ps = from_state ? p.sin.P[bh] : 0.f;
+        float me = kNegInf, ee = 0.f, pe = 0.f;
+        const float4 *ag = work.agg + static_cast<size_t>(bh) * nch;
+        for (int j = kv.lane; j < c_end; j += 64) {
+            const float4 g = ag[j];
+            if (j < c_begin) {
+                lse_combine(ms, es, g.x, g.y);
+                ps += g.z;
+            } else {
+                lse_combine(me, ee, g.x, g.y);
+                pe += g.z;
             }
         }
-        if (kv.lane == 0) work.segsc[static_cast<size_t>(bh) * nseg + seg] = make_float4(Rs, hs, ys, 0.f);
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            float m2 = __shfl_xor(ms, off, 64), e2 = __shfl_xor(es, off, 64), p2 = __shfl_xor(ps, off, 64);
+            lse_combine(ms, es, m2, e2);
+            ps += p2;
+            m2 = __shfl_xor(me, off, 64), e2 = __shfl_xor(ee, off, 64), p2 = __shfl_xor(pe, off, 64);
+            lse_combine(me, ee, m2, e2);
+            pe += p2;
+        }
+        // end carry = start carry merged with the segment's own chunks
+        float mn = ms, en = es;
+        lse_combine(mn, en, me, ee);
+        const float pn = ps + pe;
+        if (kv.lane == 0) {
+            scal[0] = mn;
+            scal[1] = en;
+            scal[2] = pn;
+            const float ts = static_cast<float>(tin + t0), tn = static_cast<float>(tin + t1);
+            float Rs = 0.f, hs = 0.f, ys = 0.f;          // from nothing: the start state is zero
+            if (tin + t0 > 0) {
+                Rs = es * __expf(ms - mn) / en;
+                hs = Rs / ts - 1.f / tn;
+                ys = ps / ts - pn / tn;
+            }
+            work.segsc[static_cast<size_t>(bh) * nseg + seg] = make_float4(Rs, hs, ys, 0.f);
+        }
     }
+    lds_barrier();
+    const float mn = scal[0], iE = 1.f / scal[1], itn = 1.f / static_cast<float>(tin + t1), pn = scal[2] * itn;
+    kv.run([&](float sv) __attribute__((always_inline)) { return make_float2(__expf(sv - mn) * iE - itn, sv - pn); });
     // the segment state layout: float4 ((s JB + jb) NGT + gt) 64 + lane holds rows 16 jb + 4 g4 + [0, 4)
     // of column 16 gt + l16 of state s
     float4 *dst = reinterpret_cast<float4 *>(work.segst + (static_cast<size_t>(bh) * (nseg - 1) + seg) * kSegFloats<D>);
@@ -915,16 +953,18 @@ hipError_t launch_one(const Problem &p, const CausalWork &w, hipStream_t stream)
     hipError_t err;
     const int bh = p.B * p.H;
     const int nch = (p.N + kC - 1) / kC;
-    if (nch > 0) {
-        hipLaunchKernelGGL(causal_coef_kernel, dim3((bh * nch + kCoefWaves - 1) / kCoefWaves), dim3(64 * kCoefWaves), 0,
+    if (w.nseg > 1) {
+        // pass 1, and the coefficient records in the workgroups past the segments
+        constexpr int kWaves = kv_threads<D>() / 64;
+        const int ncoef = (bh * nch + kWaves - 1) / kWaves;
+        hipLaunchKernelGGL((causal_seg_local_kernel<D, ROPE>), dim3(bh * (w.nseg - 1) + ncoef), dim3(kv_threads<D>()), 0,
                            stream, p, w);
         if ((err = hipGetLastError()) != hipSuccess) return err;
-    }
-    if (w.nseg > 1) {
-        hipLaunchKernelGGL((causal_seg_local_kernel<D, ROPE>), dim3(bh * (w.nseg - 1)), dim3(kv_threads<D>()), 0, stream,
-                           p, w);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
         hipLaunchKernelGGL((causal_seg_combine_kernel<D>), dim3(bh, (D * D / 4 + 255) / 256), dim3(256), 0,
+                           stream, p, w);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    } else if (nch > 0) {
+        hipLaunchKernelGGL(causal_coef_kernel, dim3((bh * nch + kCoefWaves - 1) / kCoefWaves), dim3(64 * kCoefWaves), 0,
                            stream, p, w);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }

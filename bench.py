@@ -684,10 +684,10 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": rec["hbm_bytes_per_call"] if rec else None,
                      "kernel": "zeros_fwd_causal call: useg_sum_kernel + logits_stream_kernel (logits and "
-                               "per-chunk aggregates) + causal_coef_kernel (per-chunk scalar coefficients) + "
-                               "causal_seg_local_kernel (pass 1: segments but the last, from zero, one weighted "
-                               "contraction each) + causal_seg_combine_kernel + causal_scan_kernel main (q^/k^ "
-                               "and the chunk weights formed in LDS, every segment)",
+                               "per-chunk aggregates) + causal_seg_local_kernel (pass 1: segments but the last, "
+                               "from zero, one weighted contraction each; its further workgroups form the "
+                               "per-chunk coefficient records) + causal_seg_combine_kernel + causal_scan_kernel "
+                               "main (q^/k^ and the chunk weights formed in LDS, every segment)",
                      "algorithmic_bytes_per_launch": nbytes,
                      "avg_kernel_ms": avg_kernel_ms,
                      "min_kernel_ms": float(np.min(kernel_ms)),

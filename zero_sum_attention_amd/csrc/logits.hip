@@ -206,32 +206,44 @@ __global__ __launch_bounds__(kStreamThreads, 4) void logits_stream_kernel(const 
     const int h = bh % H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int st = tid / LPT, fg = tid % LPT, l = lane % LPT;
+    // Loads in the order their values are needed, all before the first wait (loads complete in issue
+    // order): the prior, the first kBatch G sums of the earlier segments, then this thread's token rows,
+    // which stay in flight while the carry is summed. Every load is unconditional (index clamped,
+    // the extra values not added): a load under a per-load condition waits on its own.
+    const int f = tid % D, g = tid / D;        // carry sum: thread (feature f, phase g) adds segments g, g + G, ...
+    const float *us = useg + static_cast<size_t>(bh) * nseg * D + f;
     const float et = expf(tau[h]);
-    {
-        // prior (and the u-sum of a continued sequence's earlier tokens) plus the sums of u over
-        // the earlier segments: thread (feature f, phase g) adds segments g, g + G, ..., eight
-        // loads in flight at a time
-        const int f = tid % D, g = tid / D;
-        const float *us = useg + static_cast<size_t>(bh) * nseg * D + f;
-        const float pri = et * mu[h * D + f] + (su_in != nullptr ? su_in[static_cast<size_t>(bh) * D + f] : 0.f);
-        float a[8] = {g == 0 ? pri : 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int q0 = g; q0 < seg; q0 += 8 * G) {
+    const float mu_f = mu[h * D + f];
+    const float su_f = su_in != nullptr ? su_in[static_cast<size_t>(bh) * D + f] : 0.f;
+    constexpr int kBatch = D == 128 ? 8 : 32;     // (registers: the token rows take 4 TPS)
+    const int last = max(seg - 1, 0);
+    float v[kBatch];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int q = q0 + j * G;
-                a[j] += q < seg ? us[static_cast<size_t>(q) * D] : 0.f;
-            }
-        }
-        c0p[g][f] = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
-    }
+    for (int j = 0; j < kBatch; ++j) v[j] = us[static_cast<size_t>(min(g + j * G, last)) * D];
     const bf16 *ub = u + static_cast<size_t>(bh) * N * D;
     const int r0 = seg * kLogitSeg + st * TPS;
     uint4 x[TPS];
 #pragma unroll
-    for (int k = 0; k < TPS; ++k) {
-        const int r = r0 + k;
-        x[k] = r < N ? *reinterpret_cast<const uint4 *>(ub + static_cast<size_t>(r) * D + 8 * fg) : make_uint4(0, 0, 0, 0);
+    for (int k = 0; k < TPS; ++k)
+        x[k] = *reinterpret_cast<const uint4 *>(ub + static_cast<size_t>(min(r0 + k, N - 1)) * D + 8 * fg);
+    {
+        // prior (and the u-sum of a continued sequence's earlier tokens) plus the sums of u over the
+        // earlier segments
+        float a[8] = {g == 0 ? et * mu_f + su_f : 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) a[j % 8] += g + j * G < seg ? v[j] : 0.f;
+        for (int q0 = g + kBatch * G; q0 < seg; q0 += 8 * G) {      // (more than kBatch G earlier segments)
+            float v8[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v8[j] = us[static_cast<size_t>(min(q0 + j * G, last)) * D];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) a[j] += q0 + j * G < seg ? v8[j] : 0.f;
+        }
+        c0p[g][f] = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
     }
+#pragma unroll
+    for (int k = 0; k < TPS; ++k)
+        if (r0 + k >= N) x[k] = make_uint4(0, 0, 0, 0);
     float cs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < TPS; ++k) {
